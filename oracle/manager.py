@@ -1,0 +1,218 @@
+"""Block manager (oracle, test infrastructure only).
+
+The pages' manager, written out as a plain Python object:
+
+* state: a pool of ``num_blocks`` physical ids, an ordered free list and, per
+  live sequence, its length and block table ([MiniPaged-Qwen] §8.1, §8.2;
+  [mini-vLLM BM] "Block Manager 要维护哪些东西").
+* ``allocate_for_prefill`` takes ceil(n / block_size) blocks from the FRONT of
+  the free list, all or nothing ([mini-vLLM BM] "prefill 时如何分配 block";
+  [leetcode-22] Step 4 TODO 2, "Prefill 原子分配").
+* ``append_slot_for_decode`` allocates one front block exactly when the
+  position opens a new logical block (logical_block == len(block_table)),
+  returns the slot and increments the length ([MiniPaged-Qwen] §5.2 and §9;
+  [mini-vLLM BM] "decode 时如何追加 slot").  On an empty free list it fails
+  and changes nothing ([leetcode-22] Step 2 table, decode rollback test).
+* ``append_slots_for_decode`` is the batched form with the all-or-nothing
+  pre-check the scheduler needs ([mini-vLLM BM] "Block Manager 和 Scheduler
+  如何协作", can_append_slots).
+* ``free_sequence`` appends the table back onto the free list once
+  ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  With
+  ``sort_on_release`` the free list is sorted afterwards, which is what
+  [leetcode-22] reference answer ``release_request`` does.
+* ``check_invariants`` tests the invariants of [MiniPaged-Qwen] §15 and
+  [mini-vLLM BM] "正确性不变量".
+
+Readings taken where the pages are open (each listed in the design notes):
+allocation from the front of an ordered free list, release by appending in
+table order; the boundary rule of [MiniPaged-Qwen] §9 (not leetcode-22's
+``new_len % bs == 1``, which never allocates when block_size == 1); a prefill
+of 0 tokens creates a live empty sequence; sequence ids are non-negative.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+
+class ManagerError(Exception):
+    """Base of all manager errors.  Any error leaves the state unchanged."""
+
+
+class InvalidArgument(ManagerError, ValueError):
+    pass
+
+
+class OutOfBlocks(ManagerError, RuntimeError):
+    def __init__(self, msg: str = "OOM"):
+        super().__init__(msg)
+
+
+class NotLive(ManagerError, ValueError):
+    """Unknown or already-freed sequence (covers double free)."""
+
+
+class AlreadyPrefilled(ManagerError, ValueError):
+    pass
+
+
+def blocks_needed(num_tokens: int, block_size: int) -> int:
+    """ceil(num_tokens / block_size) ([MiniPaged-Qwen] §4.3;
+    [mini-vLLM BM] "prefill 时如何分配 block")."""
+    return -(-num_tokens // block_size)
+
+
+class _Seq:
+    __slots__ = ("length", "table")
+
+    def __init__(self):
+        self.length = 0          # tokens written so far == next write position
+        self.table: List[int] = []
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int,
+                 initial_free_order: Optional[Sequence[int]] = None,
+                 sort_on_release: bool = False):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidArgument("num_blocks and block_size must be positive")
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        if initial_free_order is None:
+            self.free: List[int] = list(range(self.num_blocks))
+        else:
+            order = [int(x) for x in initial_free_order]
+            if sorted(order) != list(range(self.num_blocks)):
+                raise InvalidArgument("initial free order must be a permutation of 0..N-1")
+            self.free = order
+        self.sort_on_release = bool(sort_on_release)
+        self.seqs: Dict[int, _Seq] = {}
+
+    # -- queries -----------------------------------------------------------
+    def num_free_blocks(self) -> int:
+        return len(self.free)
+
+    def can_allocate(self, num_tokens: int) -> bool:
+        """Enough free blocks for a prefill of ``num_tokens``
+        ([mini-vLLM BM] "prefill 时如何分配 block", can_allocate)."""
+        if num_tokens < 0:
+            raise InvalidArgument("num_tokens must be >= 0")
+        return blocks_needed(num_tokens, self.block_size) <= len(self.free)
+
+    def is_live(self, seq_id: int) -> bool:
+        return seq_id in self.seqs
+
+    def block_table(self, seq_id: int) -> List[int]:
+        return list(self._live(seq_id).table)
+
+    def context_len(self, seq_id: int) -> int:
+        return self._live(seq_id).length
+
+    def block_tables(self, seq_ids: Sequence[int], width: int, pad: int = -1) -> np.ndarray:
+        """Batch block-table tensor padded with ``pad`` ([MiniPaged-Qwen] §16.5)."""
+        out = np.full((len(seq_ids), width), pad, dtype=np.int32)
+        for row, sid in enumerate(seq_ids):
+            table = self._live(sid).table
+            if len(table) > width:
+                raise InvalidArgument("table wider than requested width")
+            out[row, :len(table)] = table
+        return out
+
+    def context_lens(self, seq_ids: Sequence[int]) -> np.ndarray:
+        """Per-sequence lengths ([MiniPaged-Qwen] §16.6)."""
+        return np.array([self._live(s).length for s in seq_ids], dtype=np.int32)
+
+    # -- operations --------------------------------------------------------
+    def allocate_for_prefill(self, seq_id: int, num_tokens: int) -> List[int]:
+        """Create ``seq_id`` with ``num_tokens`` prompt tokens and return their
+        slots, token t at block_table[t // bs], offset t % bs
+        ([mini-vLLM BM] "Block Manager 和 ModelRunner 如何协作")."""
+        if seq_id < 0 or num_tokens < 0:
+            raise InvalidArgument("seq_id and num_tokens must be >= 0")
+        if seq_id in self.seqs:
+            raise AlreadyPrefilled(f"sequence {seq_id} is already live")
+        need = blocks_needed(num_tokens, self.block_size)
+        if need > len(self.free):
+            raise OutOfBlocks()
+        seq = _Seq()
+        seq.table = self.free[:need]
+        del self.free[:need]
+        seq.length = num_tokens
+        self.seqs[seq_id] = seq
+        bs = self.block_size
+        return [seq.table[t // bs] * bs + t % bs for t in range(num_tokens)]
+
+    def append_slot_for_decode(self, seq_id: int) -> int:
+        """Slot of position len(seq); allocates one front block exactly when
+        that position opens a new logical block; then len += 1
+        ([MiniPaged-Qwen] §9, §9.1-§9.3)."""
+        seq = self._live(seq_id)
+        L = seq.length
+        logical_block = L // self.block_size
+        block_offset = L % self.block_size
+        if logical_block == len(seq.table):
+            if not self.free:
+                raise OutOfBlocks()
+            seq.table.append(self.free.pop(0))
+        physical_block = seq.table[logical_block]
+        seq.length = L + 1
+        return physical_block * self.block_size + block_offset
+
+    def append_slots_for_decode(self, seq_ids: Sequence[int]) -> List[int]:
+        """Batched append, all or nothing: the blocks this round needs are
+        counted first and the whole call fails with no change when the free
+        list is short ([mini-vLLM BM] "Block Manager 和 Scheduler 如何协作")."""
+        ids = [int(s) for s in seq_ids]
+        if len(set(ids)) != len(ids):
+            raise InvalidArgument("duplicate sequence ids in one append")
+        for s in ids:
+            self._live(s)
+        opening = sum(1 for s in ids
+                      if self.seqs[s].length // self.block_size == len(self.seqs[s].table))
+        if opening > len(self.free):
+            raise OutOfBlocks()
+        return [self.append_slot_for_decode(s) for s in ids]
+
+    def free_sequence(self, seq_id: int) -> None:
+        """Return every block of ``seq_id`` to the free list exactly once
+        ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block")."""
+        seq = self._live(seq_id)
+        self.free.extend(seq.table)
+        if self.sort_on_release:
+            self.free.sort()
+        del self.seqs[seq_id]
+
+    # -- invariants --------------------------------------------------------
+    def check_invariants(self) -> List[str]:
+        """Names of violated invariants (empty when all hold).
+
+        I1 no physical id in two tables / twice in one table; I2 tables and
+        free list disjoint; I3 |allocated| + |free| == N; I4 ids in [0, N);
+        I5 len(table) == ceil(len / bs); I6 free list has no duplicates
+        ([MiniPaged-Qwen] §15; [mini-vLLM BM] "正确性不变量";
+        [leetcode-22] Step 3 table).
+        """
+        bad = []
+        allocated = [pb for s in self.seqs.values() for pb in s.table]
+        if len(allocated) != len(set(allocated)):
+            bad.append("I1")
+        if set(allocated) & set(self.free):
+            bad.append("I2")
+        if len(allocated) + len(self.free) != self.num_blocks:
+            bad.append("I3")
+        if any(pb < 0 or pb >= self.num_blocks for pb in allocated + self.free):
+            bad.append("I4")
+        if any(len(s.table) != blocks_needed(s.length, self.block_size)
+               for s in self.seqs.values()):
+            bad.append("I5")
+        if len(self.free) != len(set(self.free)):
+            bad.append("I6")
+        return bad
+
+    # -- helpers -----------------------------------------------------------
+    def _live(self, seq_id: int) -> _Seq:
+        seq = self.seqs.get(int(seq_id))
+        if seq is None:
+            raise NotLive(f"sequence {seq_id} is not live")
+        return seq
