@@ -1,0 +1,270 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV cache write and paged decode attention
+ * for MI355X (gfx950), plus the host-side block manager that feeds them.
+ *
+ * Page shorthands used in the citations below:
+ *   [MiniPaged-Qwen] "MiniPaged-Qwen：Paged KV Cache 与 KV Block Manager"
+ *                    (blog.zsmgc.love), numbered sections.
+ *   [mini-vLLM BM]   "从零实现一个 mini vLLM — Block Manager" (yjxyzxyz.cn),
+ *                    section headings.
+ *   [leetcode-22]    "22. vLLM PagedAttention | vLLM 分页注意力"
+ *                    (datawhalechina llm-algo-leetcode), Step headings.
+ *
+ * Conventions for every entry point:
+ *   - Return value is a status code (PKV_OK or a negative PKV_ERR_*).  Any
+ *     error leaves all state unchanged ([leetcode-22] Step 2 table: a failed
+ *     growth rolls back; Step 4 TODO 2: OOM leaves no partial allocation).
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory (or managed memory) visible to the GPU that owns the
+ *     stream.  The caller owns every buffer and every stream; the library
+ *     allocates no device memory and keeps no pointer after a call returns.
+ *   - GPU entry points are asynchronous on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream).  Argument errors are reported
+ *     synchronously; a failed launch returns PKV_ERR_HIP.
+ *   - Manager objects are host-only and not thread-safe: one owner thread.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ status */
+#define PKV_OK                     0
+#define PKV_ERR_INVALID           (-1) /* bad argument (ValueError in the pages' Python) */
+#define PKV_ERR_OOM               (-2) /* not enough free blocks ("OOM", [leetcode-22] Step 4) */
+#define PKV_ERR_NOT_LIVE          (-3) /* unknown or already freed sequence (double free) */
+#define PKV_ERR_ALREADY_PREFILLED (-4) /* prefill of a live sequence */
+#define PKV_ERR_UNSUPPORTED       (-5) /* shape / dtype combination the kernels do not cover */
+#define PKV_ERR_HIP               (-6) /* a HIP runtime call or kernel launch failed */
+#define PKV_ERR_WORKSPACE         (-7) /* workspace missing or too small */
+#define PKV_ERR_INVARIANT         (-8) /* manager invariant violated */
+
+/* Static, NUL-terminated description of a status code. */
+const char* pkv_status_string(int status);
+
+/* ------------------------------------------------------------- cache layout */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+/*
+ * Where token `off` of KV head `h` of physical block `pb` lives:
+ *     base + pb * block_stride + h * head_stride + off * head_dim   (elements)
+ * with the head_dim elements of that token contiguous.  This is the
+ * [N, H_kv, block_size, D] indexing of [MiniPaged-Qwen] §11
+ * (KCache[physical_block, kvh, block_offset, :]) with free block and head
+ * strides, so that both layouts below are expressible:
+ *   - interleaved pool [N, 2, H_kv, bs, D]: key base = pool, value base =
+ *     pool + H_kv*bs*D elements, block_stride = 2*H_kv*bs*D,
+ *     head_stride = bs*D (one block holds its K half then its V half);
+ *   - split pools [N, H_kv, bs, D] each ([MiniPaged-Qwen] §11, §16.3):
+ *     block_stride = H_kv*bs*D, head_stride = bs*D.
+ * Requirements: head_stride >= block_size*head_dim, block_stride >=
+ * num_kv_heads*head_stride, all strides multiples of 8 elements.
+ */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  int32_t dtype;          /* pkv_dtype of K, V, q and the new key/value rows */
+  int32_t reserved;       /* must be 0 */
+  int64_t block_stride;   /* elements */
+  int64_t head_stride;    /* elements */
+} pkv_cache_layout;
+
+/* Bytes one pool tensor spans: (num_blocks-1)*block_stride +
+ * (num_kv_heads-1)*head_stride + block_size*head_dim elements.  Returns 0 on
+ * an invalid layout. */
+size_t pkv_pool_span_bytes(const pkv_cache_layout* layout);
+
+/* ---------------------------------------------------------- block manager */
+/*
+ * Host-side block manager ([MiniPaged-Qwen] §8, §9; [mini-vLLM BM]).
+ * State: `num_blocks` physical ids, an ordered free list and, per live
+ * sequence, its length (tokens written == next write position) and its block
+ * table (logical block i -> physical id, covering tokens [i*bs, (i+1)*bs)).
+ *
+ * Allocation takes ids from the FRONT of the free list; release appends a
+ * table to the BACK in logical order, then sorts the whole list when
+ * PKV_SORT_ON_RELEASE is set (the order [leetcode-22]'s reference answer
+ * keeps).  `initial_free_order` (host, [num_blocks], a permutation of
+ * 0..N-1) sets the starting order; NULL means 0, 1, ..., N-1
+ * ([MiniPaged-Qwen] §8.2).  The library copies it.
+ */
+typedef struct pkv_manager pkv_manager;
+#define PKV_SORT_ON_RELEASE 1u
+
+/* Returns NULL on invalid arguments (num_blocks <= 0, block_size <= 0, an
+ * order that is not a permutation, unknown flags) or allocation failure. */
+pkv_manager* pkv_manager_create(int32_t num_blocks, int32_t block_size,
+                                const int32_t* initial_free_order, uint32_t flags);
+void pkv_manager_destroy(pkv_manager* mgr);
+
+/* ceil(num_tokens / block_size) <= number of free blocks
+ * ([mini-vLLM BM] "prefill 时如何分配 block", can_allocate).
+ * Returns 1 (yes), 0 (no) or PKV_ERR_INVALID (num_tokens < 0, NULL mgr). */
+int pkv_can_allocate(const pkv_manager* mgr, int32_t num_tokens);
+int32_t pkv_num_free_blocks(const pkv_manager* mgr);
+int32_t pkv_num_live_sequences(const pkv_manager* mgr);
+
+/*
+ * Create live sequence `seq_id` (>= 0) holding `num_tokens` (>= 0) prompt
+ * tokens: ceil(num_tokens/bs) blocks from the front of the free list, all or
+ * nothing ([mini-vLLM BM] "prefill 时如何分配 block"; [leetcode-22] Step 4
+ * TODO 2).  When `slots_out` (host, [num_tokens]) is non-NULL it receives
+ * the flat slot of every prompt token, token t at
+ * table[t / bs] * bs + t % bs ([mini-vLLM BM] "Block Manager 和 ModelRunner
+ * 如何协作").  Errors: INVALID, ALREADY_PREFILLED (seq live), OOM.
+ */
+int pkv_allocate_for_prefill(pkv_manager* mgr, int64_t seq_id, int32_t num_tokens,
+                             int64_t* slots_out);
+
+/*
+ * Slot for the next token of `seq_id` ([MiniPaged-Qwen] §9): position
+ * L = len, logical_block = L / bs, offset = L % bs; when logical_block ==
+ * len(table) one block is taken from the front of the free list; slot =
+ * table[logical_block] * bs + offset; then len = L + 1.  `*slot_out` (host)
+ * receives the slot.  Errors: NOT_LIVE, OOM (no change), INVALID (NULL).
+ */
+int pkv_append_slot_for_decode(pkv_manager* mgr, int64_t seq_id, int64_t* slot_out);
+
+/*
+ * Batched append for `n` distinct live sequences, processed in array order,
+ * all or nothing: the number of sequences opening a new block is checked
+ * against the free list before anything changes ([mini-vLLM BM] "Block
+ * Manager 和 Scheduler 如何协作", can_append_slots).  Outputs (host, each
+ * [n], any may be NULL): slots_out[i] = slot of seq_ids[i]'s new token;
+ * lens_out[i] = its length after the append; new_block_out[i] = physical id
+ * appended to its table by this call, or -1 when none was.
+ * Errors: INVALID (n < 0, duplicate ids, NULL ids with n > 0), NOT_LIVE, OOM.
+ */
+int pkv_append_slots_for_decode(pkv_manager* mgr, const int64_t* seq_ids, int32_t n,
+                                int64_t* slots_out, int32_t* lens_out,
+                                int32_t* new_block_out);
+
+/* Return every block of `seq_id` to the free list exactly once
+ * ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  Errors: NOT_LIVE. */
+int pkv_free_sequence(pkv_manager* mgr, int64_t seq_id);
+
+/* Length of a live sequence, or PKV_ERR_NOT_LIVE. */
+int32_t pkv_context_len(const pkv_manager* mgr, int64_t seq_id);
+
+/* Copy the block table of `seq_id` into `out` (host, [cap]); `*len_out`
+ * receives its length.  INVALID when cap is too small. */
+int pkv_get_block_table(const pkv_manager* mgr, int64_t seq_id, int32_t* out,
+                        int32_t cap, int32_t* len_out);
+
+/* Batch block-table tensor ([MiniPaged-Qwen] §16.5): row i of `out` (host,
+ * [n, width] row-major) holds seq_ids[i]'s table, padded with `pad`.
+ * INVALID when a table is wider than `width`; NOT_LIVE for unknown ids. */
+int pkv_get_block_tables(const pkv_manager* mgr, const int64_t* seq_ids, int32_t n,
+                         int32_t width, int32_t pad, int32_t* out);
+
+/* Lengths of seq_ids into `out` (host, [n]) ([MiniPaged-Qwen] §16.6). */
+int pkv_get_context_lens(const pkv_manager* mgr, const int64_t* seq_ids, int32_t n,
+                         int32_t* out);
+
+/* Copy the free list, front first, into `out` (host, [cap]); `*count_out`
+ * receives its length.  INVALID when cap is too small. */
+int pkv_get_free_list(const pkv_manager* mgr, int32_t* out, int32_t cap, int32_t* count_out);
+
+/* Check the invariants of [MiniPaged-Qwen] §15 and [mini-vLLM BM]
+ * "正确性不变量": I1 no physical id twice across tables, I2 tables and free
+ * list disjoint, I3 |allocated| + |free| == N, I4 ids in [0, N),
+ * I5 len(table) == ceil(len / bs), I6 no duplicate in the free list.
+ * Returns PKV_OK or PKV_ERR_INVARIANT. */
+int pkv_check_invariants(const pkv_manager* mgr);
+
+/* ------------------------------------------------------------- cache write */
+/*
+ * Scatter the new tokens' K/V rows into the paged pool ([MiniPaged-Qwen]
+ * §12; address split of §11):  for every token t in [0, num_tokens)
+ *     pb = slot_mapping[t] / bs,  off = slot_mapping[t] % bs,
+ *     K[pb, h, off, :] = key[t, h, :],  V[pb, h, off, :] = value[t, h, :]
+ * for all heads h.  A bit-exact copy: key/value have the cache dtype.
+ *   key, value    device, [num_tokens, H_kv, D] contiguous, layout->dtype
+ *   slot_mapping  device, int64 [num_tokens]; entries outside
+ *                 [0, num_blocks*bs) are skipped (nothing written, no fault)
+ *   key_cache, value_cache  device pool bases as described by `layout`
+ * Slots must be distinct (two tokens with one slot race).  num_tokens == 0
+ * is a no-op.  Errors: INVALID, UNSUPPORTED (head_dim*elem_bytes not a
+ * multiple of 16), HIP.
+ */
+int paged_kv_write(const void* key, const void* value, const int64_t* slot_mapping,
+                   int32_t num_tokens, void* key_cache, void* value_cache,
+                   const pkv_cache_layout* layout, void* stream);
+
+/* -------------------------------------------------------- decode attention */
+/*
+ * Workspace bytes paged_decode_attention needs for split-K partial results:
+ * num_seqs * num_q_heads * P * (head_dim + 2) * 4, P = ceil(max_context_len /
+ * partition_tokens) (0 when P <= 1).  partition_tokens == 0 selects the
+ * library default (the same value paged_decode_attention picks for the same
+ * arguments).  Returns 0 for invalid arguments as well.
+ */
+size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len,
+                                             int32_t partition_tokens);
+
+/*
+ * Decode attention through block tables ([MiniPaged-Qwen] §13, §14, §17.3):
+ * for sequence b with L = context_lens[b] and query head qh,
+ *     kvh = qh / (H_q / H_kv),
+ *     K_pos = K[block_tables[b, pos / bs], kvh, pos % bs, :]  (pos < L),
+ *     out[b, qh, :] = softmax_pos(scale * q[b, qh, :] . K_pos) V_pos.
+ * No causal mask (one query per sequence at its last position).
+ *   out          device, [num_seqs, num_q_heads, D] contiguous, `out_dtype`
+ *                (PKV_F32, or the cache dtype)
+ *   q            device, [num_seqs, num_q_heads, D] contiguous, layout->dtype
+ *   key_cache, value_cache  device pool bases (see pkv_cache_layout)
+ *   block_tables device, int32 [num_seqs, block_table_stride] row-major;
+ *                entries j >= ceil(L/bs) are never read, so padding may hold
+ *                any value; ids outside [0, num_blocks) are skipped
+ *   context_lens device, int32 [num_seqs]; L is clamped to
+ *                [0, max_context_len]; L == 0 gives zeros
+ *   max_context_len  host upper bound of context_lens, and
+ *                max_context_len <= block_table_stride * block_size
+ *   partition_tokens split-K partition length in tokens (multiple of 16;
+ *                0 = library default); sequences longer than one partition
+ *                are reduced by a second kernel (max / sum rescaling)
+ *   workspace    device, >= paged_decode_attention_workspace_size(...)
+ *                bytes (may be NULL when that size is 0)
+ * Supported: block_size a multiple of 16, head_dim in {64, 128},
+ * H_q % H_kv == 0 with H_q / H_kv <= 16.  Softmax state and all sums are
+ * fp32.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
+                           const void* key_cache, const void* value_cache,
+                           const int32_t* block_tables, int32_t block_table_stride,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_q_heads, int32_t max_context_len, float scale,
+                           const pkv_cache_layout* layout, int32_t partition_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Apply the table growth of one batched append to a device-resident block
+ * table: for every i with new_block[i] >= 0,
+ *     block_tables[rows[i] * block_table_stride + (lens[i] - 1) / bs] = new_block[i]
+ * (the block a decode append opened holds the token at position lens[i]-1,
+ * [MiniPaged-Qwen] §9.2).  block_tables: device int32 [num_rows,
+ * block_table_stride]; rows, lens, new_block: device int32 [n]; rows may be
+ * NULL, meaning row i.  Entries whose target row or column falls outside the
+ * table are skipped.  Errors: INVALID, HIP.
+ */
+int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows,
+                            int32_t block_table_stride, const int32_t* rows,
+                            const int32_t* lens, const int32_t* new_block, int32_t n,
+                            int32_t block_size, void* stream);
+
+/* Library version string, e.g. "pkv 0.1.0 gfx950". */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,385 @@
+"""Python binding of libpkv: paged KV cache write, paged decode attention and
+the host block manager, for MI355X (gfx950).
+
+Argument marshalling only: every step runs in libpkv (HIP kernels and the C++
+manager).  PyTorch supplies device memory and the current stream.  There is
+no fallback: if the library is missing, importing the GPU entry points
+raises.
+
+Pool convention used by ``new_pool``: one tensor ``[N, 2, H_kv, bs, D]``
+per layer, K in ``[:, 0]`` and V in ``[:, 1]`` (each block holds its K half
+then its V half); the library also accepts separate ``[N, H_kv, bs, D]``
+tensors, or any views with contiguous ``[bs, D]`` tiles.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libpkv.so")
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+SORT_ON_RELEASE = 1
+
+STATUS = {0: "OK", -1: "INVALID", -2: "OOM", -3: "NOT_LIVE", -4: "ALREADY_PREFILLED",
+          -5: "UNSUPPORTED", -6: "HIP", -7: "WORKSPACE", -8: "INVARIANT"}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        msg = _lib_handle().pkv_status_string(status).decode() if _LIB is not None else self.name
+        super().__init__(f"{what}: {self.name} ({msg})" if what else f"{self.name} ({msg})")
+
+
+class InvalidArgumentError(PkvError, ValueError):
+    pass
+
+
+class OutOfBlocksError(PkvError):
+    pass
+
+
+class NotLiveError(PkvError, ValueError):
+    pass
+
+
+class AlreadyPrefilledError(PkvError, ValueError):
+    pass
+
+
+_ERRORS = {-1: InvalidArgumentError, -2: OutOfBlocksError, -3: NotLiveError,
+           -4: AlreadyPrefilledError}
+
+
+def _check(status: int, what: str) -> int:
+    if status < 0:
+        raise _ERRORS.get(status, PkvError)(status, what)
+    return status
+
+
+class CacheLayout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("block_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+
+
+_LIB = None
+_P = ctypes.c_void_p
+_I32, _I64, _U32, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
+_PI32, _PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+# name -> (restype, argtypes); the complete exported C ABI
+SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_pool_span_bytes": (_SZ, [ctypes.POINTER(CacheLayout)]),
+    "pkv_manager_create": (_P, [_I32, _I32, _PI32, _U32]),
+    "pkv_manager_destroy": (None, [_P]),
+    "pkv_can_allocate": (ctypes.c_int, [_P, _I32]),
+    "pkv_num_free_blocks": (_I32, [_P]),
+    "pkv_num_live_sequences": (_I32, [_P]),
+    "pkv_allocate_for_prefill": (ctypes.c_int, [_P, _I64, _I32, _PI64]),
+    "pkv_append_slot_for_decode": (ctypes.c_int, [_P, _I64, _PI64]),
+    "pkv_append_slots_for_decode": (ctypes.c_int, [_P, _PI64, _I32, _PI64, _PI32, _PI32]),
+    "pkv_free_sequence": (ctypes.c_int, [_P, _I64]),
+    "pkv_context_len": (_I32, [_P, _I64]),
+    "pkv_get_block_table": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
+    "pkv_get_block_tables": (ctypes.c_int, [_P, _PI64, _I32, _I32, _I32, _PI32]),
+    "pkv_get_context_lens": (ctypes.c_int, [_P, _PI64, _I32, _PI32]),
+    "pkv_get_free_list": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
+    "pkv_check_invariants": (ctypes.c_int, [_P]),
+    "paged_kv_write": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "paged_decode_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
+    "paged_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
+                                              _F32, ctypes.POINTER(CacheLayout), _I32, _P, _SZ, _P]),
+    "pkv_update_block_tables": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _I32, _I32, _P]),
+}
+
+
+def _lib_handle():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libpkv is not built ({LIB_PATH} missing): run "
+                               "`python -m paged_kv_cache_128_amd._build` first")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def load_library():
+    """Load libpkv (raises when it is missing) and return the ctypes handle."""
+    return _lib_handle()
+
+
+def version() -> str:
+    return _lib_handle().pkv_version().decode()
+
+
+def _np_i64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def _ptr(a: np.ndarray, ty):
+    return a.ctypes.data_as(ctypes.POINTER(ty))
+
+
+# --------------------------------------------------------------------------
+# Host block manager
+# --------------------------------------------------------------------------
+class KVBlockManager:
+    """Host block manager in libpkv (see ``pkv_manager_*`` in include/pkv.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int,
+                 initial_free_order: Optional[Sequence[int]] = None,
+                 sort_on_release: bool = False):
+        lib = _lib_handle()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise ValueError("initial_free_order must have num_blocks entries")
+        h = lib.pkv_manager_create(int(num_blocks), int(block_size),
+                                   None if order is None else _ptr(order, ctypes.c_int32),
+                                   SORT_ON_RELEASE if sort_on_release else 0)
+        if not h:
+            raise ValueError("invalid block manager arguments")
+        self._h = ctypes.c_void_p(h)
+        self._lib = lib
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_manager_destroy(h)
+            self._h = None
+
+    # queries
+    def can_allocate(self, num_tokens: int) -> bool:
+        return bool(_check(self._lib.pkv_can_allocate(self._h, int(num_tokens)), "can_allocate"))
+
+    def num_free_blocks(self) -> int:
+        return int(self._lib.pkv_num_free_blocks(self._h))
+
+    def num_live_sequences(self) -> int:
+        return int(self._lib.pkv_num_live_sequences(self._h))
+
+    def context_len(self, seq_id: int) -> int:
+        return _check(self._lib.pkv_context_len(self._h, int(seq_id)), "context_len")
+
+    def block_table(self, seq_id: int) -> list:
+        cap = self.num_blocks
+        out = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_get_block_table(self._h, int(seq_id), _ptr(out, ctypes.c_int32), cap,
+                                             ctypes.byref(n)), "block_table")
+        return out[:n.value].tolist()
+
+    def block_tables(self, seq_ids: Sequence[int], width: int, pad: int = -1,
+                     out: Optional[np.ndarray] = None) -> np.ndarray:
+        ids = _np_i64(seq_ids)
+        if out is None:
+            out = np.empty((len(ids), width), dtype=np.int32)
+        _check(self._lib.pkv_get_block_tables(self._h, _ptr(ids, ctypes.c_int64), len(ids), int(width),
+                                              int(pad), _ptr(out, ctypes.c_int32)), "block_tables")
+        return out
+
+    def context_lens(self, seq_ids: Sequence[int]) -> np.ndarray:
+        ids = _np_i64(seq_ids)
+        out = np.empty(len(ids), dtype=np.int32)
+        _check(self._lib.pkv_get_context_lens(self._h, _ptr(ids, ctypes.c_int64), len(ids),
+                                              _ptr(out, ctypes.c_int32)), "context_lens")
+        return out
+
+    def free_list(self) -> list:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_get_free_list(self._h, _ptr(out, ctypes.c_int32), self.num_blocks,
+                                           ctypes.byref(n)), "free_list")
+        return out[:n.value].tolist()
+
+    def check_invariants(self) -> bool:
+        return self._lib.pkv_check_invariants(self._h) == 0
+
+    # operations
+    def allocate_for_prefill(self, seq_id: int, num_tokens: int, want_slots: bool = True):
+        slots = np.empty(max(int(num_tokens), 0), dtype=np.int64) if want_slots else None
+        _check(self._lib.pkv_allocate_for_prefill(
+            self._h, int(seq_id), int(num_tokens),
+            None if slots is None else _ptr(slots, ctypes.c_int64)), "allocate_for_prefill")
+        return slots
+
+    def append_slot_for_decode(self, seq_id: int) -> int:
+        s = ctypes.c_int64(0)
+        _check(self._lib.pkv_append_slot_for_decode(self._h, int(seq_id), ctypes.byref(s)),
+               "append_slot_for_decode")
+        return s.value
+
+    def append_slots_for_decode(self, seq_ids, slots_out: Optional[np.ndarray] = None,
+                                lens_out: Optional[np.ndarray] = None,
+                                new_block_out: Optional[np.ndarray] = None):
+        """Batched all-or-nothing append.  Returns (slots int64, lens int32,
+        new_block int32); the optional outputs (e.g. numpy views of pinned
+        host tensors) are filled in place."""
+        ids = seq_ids if (isinstance(seq_ids, np.ndarray) and seq_ids.dtype == np.int64
+                          and seq_ids.flags.c_contiguous) else _np_i64(seq_ids)
+        n = len(ids)
+        slots = slots_out if slots_out is not None else np.empty(n, dtype=np.int64)
+        lens = lens_out if lens_out is not None else np.empty(n, dtype=np.int32)
+        newb = new_block_out if new_block_out is not None else np.empty(n, dtype=np.int32)
+        _check(self._lib.pkv_append_slots_for_decode(
+            self._h, _ptr(ids, ctypes.c_int64), n, _ptr(slots, ctypes.c_int64),
+            _ptr(lens, ctypes.c_int32), _ptr(newb, ctypes.c_int32)), "append_slots_for_decode")
+        return slots, lens, newb
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check(self._lib.pkv_free_sequence(self._h, int(seq_id)), "free_sequence")
+
+
+# --------------------------------------------------------------------------
+# Device entry points (torch tensors in, torch tensors out)
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> int:
+    torch = _torch()
+    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    if dtype not in codes:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return codes[dtype]
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_layout(key_cache, value_cache=None) -> CacheLayout:
+    """Layout of K/V cache tensors shaped [N, H_kv, bs, D] whose [bs, D]
+    tiles are contiguous (any block and head strides)."""
+    if key_cache.dim() != 4:
+        raise ValueError("key_cache must be [num_blocks, H_kv, block_size, head_dim]")
+    n, h, bs, d = key_cache.shape
+    st = key_cache.stride()
+    if st[3] != 1 or st[2] != d:
+        raise ValueError("each [block_size, head_dim] tile must be contiguous")
+    if value_cache is not None:
+        if value_cache.shape != key_cache.shape or value_cache.stride() != st \
+                or value_cache.dtype != key_cache.dtype:
+            raise ValueError("value_cache must match key_cache in shape, strides and dtype")
+    return CacheLayout(n, h, bs, d, dtype_code(key_cache.dtype), 0, st[0], st[1])
+
+
+def new_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype,
+             device="cuda", fill_bits: Optional[int] = None):
+    """Allocate one interleaved pool [N, 2, H_kv, bs, D] and return
+    (pool, key_cache view, value_cache view)."""
+    torch = _torch()
+    pool = torch.empty((num_blocks, 2, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+    if fill_bits is not None:
+        itype = torch.int16 if pool.element_size() == 2 else torch.int32
+        bits = fill_bits - (1 << 16) if itype is torch.int16 and fill_bits >= 1 << 15 else fill_bits
+        if itype is torch.int32 and bits >= 1 << 31:
+            bits -= 1 << 32
+        pool.view(itype).fill_(bits)
+    return pool, pool[:, 0], pool[:, 1]
+
+
+def paged_kv_write(key, value, slot_mapping, key_cache, value_cache, stream=None) -> None:
+    """Scatter key/value [T, H_kv, D] into the pool at slot_mapping [T]
+    (int64 device tensor)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    T = key.shape[0]
+    if key.shape != (T, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_tokens, H_kv, head_dim]")
+    if not (key.is_contiguous() and value.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("key, value and slot_mapping must be contiguous")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise ValueError("key/value dtype must equal the cache dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [num_tokens]")
+    st = _lib_handle().paged_kv_write(key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), T,
+                                      key_cache.data_ptr(), value_cache.data_ptr(),
+                                      ctypes.byref(lay), _stream_handle(stream))
+    _check(st, "paged_kv_write")
+
+
+def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, partition_tokens: int = 0) -> int:
+    return int(_lib_handle().paged_decode_attention_workspace_size(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_tokens))
+
+
+def paged_decode_attention(q, key_cache, value_cache, block_tables, context_lens, scale: float,
+                           out=None, out_dtype=None, partition_tokens: int = 0,
+                           max_context_len: Optional[int] = None, workspace=None, stream=None):
+    """Decode attention through block tables.  q [B, H_q, D]; block_tables
+    int32 [B, W]; context_lens int32 [B].  Returns out [B, H_q, D] (float32
+    unless ``out_dtype`` / ``out`` says otherwise)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    B, hq, d = q.shape
+    if d != lay.head_dim or q.dtype != key_cache.dtype or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, H_q, head_dim] in the cache dtype")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B \
+            or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [B, W] with unit column stride")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    W = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = W * lay.block_size
+    if out is None:
+        od = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty((B, hq, d), dtype=od, device=q.device)
+    if out.shape != (B, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be contiguous [B, H_q, head_dim]")
+    need = workspace_size(B, hq, lay.num_kv_heads, d, max_context_len, partition_tokens)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = _lib_handle().paged_decode_attention(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key_cache.data_ptr(),
+        value_cache.data_ptr(), block_tables.data_ptr(), block_tables.stride(0),
+        context_lens.data_ptr(), B, hq, int(max_context_len), float(scale), ctypes.byref(lay),
+        int(partition_tokens), ws_ptr, ws_bytes, _stream_handle(stream))
+    _check(st, "paged_decode_attention")
+    return out
+
+
+def update_block_tables(block_tables, lens, new_block, block_size: int, rows=None, stream=None) -> None:
+    """Apply one batched append's new blocks to a device block table."""
+    n = lens.shape[0]
+    if block_tables.dtype != _torch().int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [rows, W] with unit column stride")
+    st = _lib_handle().pkv_update_block_tables(
+        block_tables.data_ptr(), block_tables.shape[0], block_tables.stride(0),
+        None if rows is None else rows.data_ptr(),
+        lens.data_ptr(), new_block.data_ptr(), n, int(block_size), _stream_handle(stream))
+    _check(st, "update_block_tables")
+
+
+__all__ = [
+    "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
+    "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
+    "workspace_size", "update_block_tables", "new_pool", "cache_layout", "load_library",
+    "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
+]

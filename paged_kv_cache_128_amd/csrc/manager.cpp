@@ -1,0 +1,300 @@
+// Host-side KV block manager behind the C ABI (declared in include/pkv.h).
+//
+// The manager is the CPU metadata plane of [MiniPaged-Qwen] §8: an ordered
+// free list of physical block ids plus, per live sequence, its length and its
+// block table.  Semantics follow [MiniPaged-Qwen] §9 (append_token) and
+// [mini-vLLM BM] (allocate_for_prefill / append_slot_for_decode /
+// free_sequence / can_allocate).  Every operation validates first and mutates
+// only after all checks pass, so a failed call leaves the state unchanged.
+//
+// The free list is a ring buffer of capacity num_blocks: allocation pops the
+// front, release pushes at the back, and the list can never hold more than
+// num_blocks ids while the invariants hold.
+#include <algorithm>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pkv_internal.h"
+
+namespace {
+
+struct Sequence {
+  int32_t length = 0;            // tokens written == next write position
+  std::vector<int32_t> table;    // logical block -> physical block id
+};
+
+}  // namespace
+
+struct pkv_manager {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  bool sort_on_release = false;
+  // ring buffer holding the free list, front at `head`
+  std::vector<int32_t> ring;
+  int64_t head = 0;
+  int64_t count = 0;
+  std::unordered_map<int64_t, Sequence> seqs;
+
+  int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
+  int32_t pop_front() {
+    int32_t v = ring[head];
+    head = (head + 1) % num_blocks;
+    --count;
+    return v;
+  }
+  void push_back(int32_t v) {
+    ring[(head + count) % num_blocks] = v;
+    ++count;
+  }
+  void sort_free() {
+    std::vector<int32_t> tmp;
+    tmp.reserve(count);
+    for (int64_t i = 0; i < count; ++i) tmp.push_back(free_at(i));
+    std::sort(tmp.begin(), tmp.end());
+    head = 0;
+    for (int64_t i = 0; i < count; ++i) ring[i] = tmp[i];
+  }
+  int64_t blocks_for(int64_t tokens) const { return (tokens + block_size - 1) / block_size; }
+};
+
+extern "C" {
+
+pkv_manager* pkv_manager_create(int32_t num_blocks, int32_t block_size,
+                                const int32_t* initial_free_order, uint32_t flags) {
+  if (num_blocks <= 0 || block_size <= 0 || (flags & ~PKV_SORT_ON_RELEASE) != 0) return nullptr;
+  pkv_manager* m = new (std::nothrow) pkv_manager();
+  if (!m) return nullptr;
+  try {
+    m->num_blocks = num_blocks;
+    m->block_size = block_size;
+    m->sort_on_release = (flags & PKV_SORT_ON_RELEASE) != 0;
+    m->ring.resize(num_blocks);
+    if (initial_free_order) {
+      std::vector<char> seen(num_blocks, 0);
+      for (int32_t i = 0; i < num_blocks; ++i) {
+        int32_t v = initial_free_order[i];
+        if (v < 0 || v >= num_blocks || seen[v]) {
+          delete m;
+          return nullptr;
+        }
+        seen[v] = 1;
+        m->ring[i] = v;
+      }
+    } else {
+      for (int32_t i = 0; i < num_blocks; ++i) m->ring[i] = i;
+    }
+    m->head = 0;
+    m->count = num_blocks;
+  } catch (...) {
+    delete m;
+    return nullptr;
+  }
+  return m;
+}
+
+void pkv_manager_destroy(pkv_manager* mgr) { delete mgr; }
+
+int pkv_can_allocate(const pkv_manager* m, int32_t num_tokens) {
+  if (!m || num_tokens < 0) return PKV_ERR_INVALID;
+  return m->blocks_for(num_tokens) <= m->count ? 1 : 0;
+}
+
+int32_t pkv_num_free_blocks(const pkv_manager* m) {
+  return m ? static_cast<int32_t>(m->count) : PKV_ERR_INVALID;
+}
+
+int32_t pkv_num_live_sequences(const pkv_manager* m) {
+  return m ? static_cast<int32_t>(m->seqs.size()) : PKV_ERR_INVALID;
+}
+
+int pkv_allocate_for_prefill(pkv_manager* m, int64_t seq_id, int32_t num_tokens,
+                             int64_t* slots_out) {
+  if (!m || seq_id < 0 || num_tokens < 0) return PKV_ERR_INVALID;
+  if (m->seqs.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
+  const int64_t need = m->blocks_for(num_tokens);
+  if (need > m->count) return PKV_ERR_OOM;
+  Sequence s;
+  try {
+    s.table.reserve(need);
+    for (int64_t i = 0; i < need; ++i) s.table.push_back(m->free_at(i));
+    s.length = num_tokens;
+    m->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (int64_t i = 0; i < need; ++i) m->pop_front();
+  if (slots_out) {
+    const std::vector<int32_t>& t = m->seqs[seq_id].table;
+    const int64_t bs = m->block_size;
+    for (int64_t p = 0; p < num_tokens; ++p) slots_out[p] = t[p / bs] * bs + p % bs;
+  }
+  return PKV_OK;
+}
+
+// One append on a live sequence already checked to have a block available
+// when it needs one ([MiniPaged-Qwen] §9.1-§9.3).
+static int64_t append_one(pkv_manager* m, Sequence& s, int32_t* new_block) {
+  const int64_t bs = m->block_size;
+  const int64_t L = s.length;
+  const int64_t logical_block = L / bs;
+  const int64_t block_offset = L % bs;
+  *new_block = -1;
+  if (logical_block == static_cast<int64_t>(s.table.size())) {
+    int32_t pb = m->pop_front();
+    s.table.push_back(pb);
+    *new_block = pb;
+  }
+  s.length = static_cast<int32_t>(L + 1);
+  return static_cast<int64_t>(s.table[logical_block]) * bs + block_offset;
+}
+
+int pkv_append_slot_for_decode(pkv_manager* m, int64_t seq_id, int64_t* slot_out) {
+  if (!m || !slot_out) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  Sequence& s = it->second;
+  if (s.length == INT32_MAX) return PKV_ERR_INVALID;
+  const bool opens = (s.length / m->block_size) == static_cast<int64_t>(s.table.size());
+  if (opens && m->count == 0) return PKV_ERR_OOM;
+  try {
+    if (opens) s.table.reserve(s.table.size() + 1);
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  int32_t nb;
+  *slot_out = append_one(m, s, &nb);
+  return PKV_OK;
+}
+
+int pkv_append_slots_for_decode(pkv_manager* m, const int64_t* seq_ids, int32_t n,
+                                int64_t* slots_out, int32_t* lens_out, int32_t* new_block_out) {
+  if (!m || n < 0 || (n > 0 && !seq_ids)) return PKV_ERR_INVALID;
+  std::vector<Sequence*> seqs;
+  try {
+    seqs.reserve(n);
+    std::unordered_set<int64_t> seen;
+    seen.reserve(static_cast<size_t>(n) * 2);
+    for (int32_t i = 0; i < n; ++i)
+      if (!seen.insert(seq_ids[i]).second) return PKV_ERR_INVALID;
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  int64_t opening = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = m->seqs.find(seq_ids[i]);
+    if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+    Sequence& s = it->second;
+    if (s.length == INT32_MAX) return PKV_ERR_INVALID;
+    if (s.length / m->block_size == static_cast<int64_t>(s.table.size())) ++opening;
+    seqs.push_back(&s);
+  }
+  if (opening > m->count) return PKV_ERR_OOM;
+  try {
+    for (Sequence* s : seqs)
+      if (s->length / m->block_size == static_cast<int64_t>(s->table.size()))
+        s->table.reserve(s->table.size() + 1);
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t nb;
+    int64_t slot = append_one(m, *seqs[i], &nb);
+    if (slots_out) slots_out[i] = slot;
+    if (lens_out) lens_out[i] = seqs[i]->length;
+    if (new_block_out) new_block_out[i] = nb;
+  }
+  return PKV_OK;
+}
+
+int pkv_free_sequence(pkv_manager* m, int64_t seq_id) {
+  if (!m) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  for (int32_t pb : it->second.table) m->push_back(pb);
+  if (m->sort_on_release) m->sort_free();
+  m->seqs.erase(it);
+  return PKV_OK;
+}
+
+int32_t pkv_context_len(const pkv_manager* m, int64_t seq_id) {
+  if (!m) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  return it->second.length;
+}
+
+int pkv_get_block_table(const pkv_manager* m, int64_t seq_id, int32_t* out, int32_t cap,
+                        int32_t* len_out) {
+  if (!m || cap < 0 || (cap > 0 && !out)) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  const std::vector<int32_t>& t = it->second.table;
+  if (static_cast<int64_t>(t.size()) > cap) return PKV_ERR_INVALID;
+  std::copy(t.begin(), t.end(), out);
+  if (len_out) *len_out = static_cast<int32_t>(t.size());
+  return PKV_OK;
+}
+
+int pkv_get_block_tables(const pkv_manager* m, const int64_t* seq_ids, int32_t n, int32_t width,
+                         int32_t pad, int32_t* out) {
+  if (!m || n < 0 || width < 0 || (n > 0 && (!seq_ids || (width > 0 && !out))))
+    return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = m->seqs.find(seq_ids[i]);
+    if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+    if (static_cast<int64_t>(it->second.table.size()) > width) return PKV_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const std::vector<int32_t>& t = m->seqs.find(seq_ids[i])->second.table;
+    int32_t* row = out + static_cast<int64_t>(i) * width;
+    std::copy(t.begin(), t.end(), row);
+    std::fill(row + t.size(), row + width, pad);
+  }
+  return PKV_OK;
+}
+
+int pkv_get_context_lens(const pkv_manager* m, const int64_t* seq_ids, int32_t n, int32_t* out) {
+  if (!m || n < 0 || (n > 0 && (!seq_ids || !out))) return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i)
+    if (!m->seqs.count(seq_ids[i])) return PKV_ERR_NOT_LIVE;
+  for (int32_t i = 0; i < n; ++i) out[i] = m->seqs.find(seq_ids[i])->second.length;
+  return PKV_OK;
+}
+
+int pkv_get_free_list(const pkv_manager* m, int32_t* out, int32_t cap, int32_t* count_out) {
+  if (!m || cap < 0 || (cap > 0 && !out)) return PKV_ERR_INVALID;
+  if (m->count > cap) return PKV_ERR_INVALID;
+  for (int64_t i = 0; i < m->count; ++i) out[i] = m->free_at(i);
+  if (count_out) *count_out = static_cast<int32_t>(m->count);
+  return PKV_OK;
+}
+
+int pkv_check_invariants(const pkv_manager* m) {
+  if (!m) return PKV_ERR_INVALID;
+  const int64_t N = m->num_blocks;
+  std::vector<int32_t> owners(N, 0);
+  int64_t allocated = 0;
+  for (const auto& kv : m->seqs) {
+    const Sequence& s = kv.second;
+    if (static_cast<int64_t>(s.table.size()) != m->blocks_for(s.length)) return PKV_ERR_INVARIANT;  // I5
+    for (int32_t pb : s.table) {
+      if (pb < 0 || pb >= N) return PKV_ERR_INVARIANT;           // I4
+      if (++owners[pb] > 1) return PKV_ERR_INVARIANT;            // I1
+      ++allocated;
+    }
+  }
+  std::vector<char> in_free(N, 0);
+  for (int64_t i = 0; i < m->count; ++i) {
+    int32_t pb = m->free_at(i);
+    if (pb < 0 || pb >= N) return PKV_ERR_INVARIANT;             // I4
+    if (in_free[pb]) return PKV_ERR_INVARIANT;                   // I6
+    in_free[pb] = 1;
+    if (owners[pb]) return PKV_ERR_INVARIANT;                    // I2
+  }
+  if (allocated + m->count != N) return PKV_ERR_INVARIANT;       // I3
+  return PKV_OK;
+}
+
+}  // extern "C"

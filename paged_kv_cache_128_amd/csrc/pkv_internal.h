@@ -1,0 +1,21 @@
+// Internal declarations shared by the host sources of libpkv (not installed).
+#pragma once
+#include <stdint.h>
+#include <stddef.h>
+#include "pkv.h"
+
+namespace pkv {
+
+inline int elem_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// Validate a cache layout; returns PKV_OK or PKV_ERR_INVALID.
+int check_layout(const pkv_cache_layout* l);
+
+}  // namespace pkv

@@ -1,0 +1,738 @@
+// HIP kernels of libpkv for gfx950 (MI355X) and their C-ABI launchers.
+//
+//  * kv_write_kernel     -- slot-mapping scatter of new K/V rows into the pool
+//                           ([MiniPaged-Qwen] §11 slot split, §12 cache write).
+//  * attn_split_kernel   -- decode attention over one context partition of one
+//                           (sequence, KV head): block-table walk, GQA group
+//                           sharing each K/V tile, fp32 online softmax
+//                           ([MiniPaged-Qwen] §13, §14, §17.3).
+//  * attn_reduce_kernel  -- merges the partitions' (max, sum, accumulator)
+//                           triples into the final rows (split-K).
+//  * table_update_kernel -- applies the blocks a batched decode append opened
+//                           to a device-resident block table ([MiniPaged-Qwen] §9.2).
+//
+// Work mapping of attn_split_kernel (one 64-lane wavefront per workgroup):
+//  - The K/V pool is read in tiles of 16 consecutive logical tokens (a tile
+//    never straddles a physical block because block_size % 16 == 0).
+//  - Q.K^T runs on the matrix cores: A = the K tile (16 tokens x D), B = the
+//    query group transposed (D x 16 heads, heads >= G zero), one
+//    V_MFMA_F32_16x16x32_{BF16,F16} per 32 head-dims (16x16x4 F32 for fp32).
+//    Lane l supplies token (l % 16) of the K tile straight from HBM with
+//    16-byte loads; the result S^T lands with head = l % 16 and tokens
+//    4*(l/16) .. 4*(l/16)+3 in the lane's four accumulators.
+//  - P.V runs on the vector ALUs: lane l owns head-dim chunk (l % 16) and
+//    the same four tokens 4*(l/16).., so each V tile row is read by 16 lanes
+//    as one 256-byte (bf16, D = 128) coalesced segment.  The probabilities
+//    reach the P.V lanes through a 1 KiB LDS broadcast.
+//  - Softmax is online in fp32 and in log2 units (scores pre-multiplied by
+//    scale*log2(e), exponentials by v_exp_f32).  The running reference max
+//    only moves when a tile's max exceeds it by more than 8 (2^8 headroom),
+//    so the accumulator rescale is skipped on almost every tile.
+//  - The next tile's K and V are loaded before the current one is consumed
+//    (two register stages), so every wave keeps 8 KiB in flight.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "pkv_internal.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kSlack = 8.0f;     // allowed growth of exp2 arguments before a rescale
+constexpr int kTile = 16;          // tokens per tile == MFMA M dimension
+constexpr int kWave = 64;
+#ifndef PKV_SPLIT_WAVES_PER_SIMD
+#define PKV_SPLIT_WAVES_PER_SIMD 2
+#endif
+// Occupancy target of the split kernel (waves per SIMD).  The bf16 D = 128,
+// G = 7 instance needs about 180 VGPRs, which fits two waves without spills.
+template <int DT>
+constexpr int split_waves_per_simd() { return DT == PKV_F32 ? 2 : PKV_SPLIT_WAVES_PER_SIMD; }
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t u, float& a, float& b) {
+  if constexpr (DT == PKV_BF16) {
+    a = bf16lo(u);
+    b = bf16hi(u);
+  } else {
+    f16x2 h = __builtin_bit_cast(f16x2, u);
+    a = static_cast<float>(h.x);
+    b = static_cast<float>(h.y);
+  }
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int NDW>
+struct Dw { uint32_t w[NDW]; };
+
+template <int NDW>
+__device__ __forceinline__ Dw<NDW> load_dw(const void* p) {
+  Dw<NDW> r;
+  if constexpr (NDW % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < NDW / 4; ++i) {
+      uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      r.w[4 * i + 0] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (NDW == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = v.x; r.w[1] = v.y;
+  } else {
+    static_assert(NDW == 1, "unsupported load width");
+    r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+  return r;
+}
+
+// ------------------------------------------------------------ cache write
+// One thread moves one 16-byte chunk of one token's K row and the same chunk
+// of its V row.  Reads are fully coalesced; each (token, head) row lands as
+// one contiguous D*elem-byte segment of the pool.
+__global__ void __launch_bounds__(256)
+kv_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                const int64_t* __restrict__ slot_mapping, int64_t total_chunks,
+                int32_t chunks_per_head, int32_t chunks_per_token, int64_t capacity,
+                int32_t block_size, int64_t block_stride16, int64_t head_stride16,
+                int32_t token_stride16, uint4* __restrict__ key_cache,
+                uint4* __restrict__ value_cache) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total_chunks) return;
+  const int64_t t = idx / chunks_per_token;
+  const int32_t r = static_cast<int32_t>(idx - t * chunks_per_token);
+  const int32_t h = r / chunks_per_head;
+  const int32_t c = r - h * chunks_per_head;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= capacity) return;
+  const int64_t pb = slot / block_size;
+  const int64_t off = slot - pb * block_size;
+  const int64_t dst = pb * block_stride16 + h * head_stride16 + off * token_stride16 + c;
+  key_cache[dst] = key[idx];
+  value_cache[dst] = value[idx];
+}
+
+// ------------------------------------------------------------ table update
+__global__ void __launch_bounds__(256)
+table_update_kernel(int32_t* __restrict__ tables, int32_t num_rows, int32_t stride,
+                    const int32_t* __restrict__ rows,
+                    const int32_t* __restrict__ lens, const int32_t* __restrict__ new_block,
+                    int32_t n, int32_t block_size) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int32_t nb = new_block[i];
+  if (nb < 0) return;
+  const int32_t row = rows ? rows[i] : i;
+  const int32_t col = (lens[i] - 1) / block_size;
+  if (row < 0 || row >= num_rows || lens[i] <= 0 || col >= stride) return;
+  tables[static_cast<int64_t>(row) * stride + col] = nb;
+}
+
+// ------------------------------------------------------------ attention
+struct AttnArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_ml;      // [B, H_q, P, 2]  (m, l)
+  float* ws_acc;     // [B, H_q, P, D]
+  void* out;
+  int64_t block_stride;   // elements
+  int64_t head_stride;    // elements
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_seqs;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  int32_t max_len;
+  int32_t part_tokens;
+  int32_t max_parts;
+  int32_t out_dtype;
+  float scale_log2;       // scale * log2(e)
+};
+
+// Per-dtype / head-dim shape of the lane fragments.
+template <int DT, int D>
+struct Frag {
+  static constexpr int kBytes = (DT == PKV_F32) ? 4 : 2;
+  // K tile: lane supplies (D * kBytes / 4) bytes of its token = kDwK dwords.
+  static constexpr int kDwK = D * kBytes / 4 / 4;        // dwords per lane
+  static constexpr int kW = D / 16;                      // head-dim chunk per P.V lane
+  static constexpr int kDwV = kW * kBytes / 4;           // dwords per token row chunk
+};
+
+template <int DT, int D>
+struct Tile {
+  Dw<Frag<DT, D>::kDwK> k;
+  Dw<Frag<DT, D>::kDwV> v[4];
+};
+
+// Loads one 16-token tile.  `base` is the element offset of token 0 of the
+// tile inside K (and V) for this KV head.  Rows of tokens >= nvalid (the
+// unused tail of the last block, which may hold anything) are not read:
+// those lanes re-read token 0 instead, so every value that enters the sums
+// is finite; their scores are masked to -inf afterwards.
+template <int DT, int D>
+__device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kc, const char* vc,
+                                          int64_t base, int nvalid, int lane) {
+  using F = Frag<DT, D>;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int64_t kb = base * F::kBytes;
+  const int ktok = c16 < nvalid ? c16 : 0;
+  if constexpr (DT == PKV_F32) {
+    // token ktok, floats d = 16 j + 4 g4 .. +3 for j = 0 .. D/16-1
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      Dw<4> x = load_dw<4>(kc + kb + (static_cast<int64_t>(ktok) * D + 16 * j + 4 * g4) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.k.w[4 * j + e] = x.w[e];
+    }
+  } else {
+    // token ktok, halves d = 32 kk + 8 g4 .. +7 for kk = 0 .. D/32-1
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      Dw<4> x = load_dw<4>(kc + kb + (static_cast<int64_t>(ktok) * D + 32 * kk + 8 * g4) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t.k.w[4 * kk + e] = x.w[e];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int vtok = 4 * g4 + r < nvalid ? 4 * g4 + r : 0;
+    t.v[r] = load_dw<F::kDwV>(vc + kb + (static_cast<int64_t>(vtok) * D + c16 * F::kW) * F::kBytes);
+  }
+}
+
+// S^T[token 4*g4 + r][head c16] for the lane's 4 tokens.
+template <int DT, int D>
+__device__ __forceinline__ f32x4 qk_tile(const Tile<DT, D>& t, const Dw<Frag<DT, D>::kDwK>& qf) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT == PKV_F32) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k.w[i]),
+                                                 __uint_as_float(qf.w[i]), acc, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      uint4 a4 = make_uint4(t.k.w[4 * kk], t.k.w[4 * kk + 1], t.k.w[4 * kk + 2], t.k.w[4 * kk + 3]);
+      uint4 b4 = make_uint4(qf.w[4 * kk], qf.w[4 * kk + 1], qf.w[4 * kk + 2], qf.w[4 * kk + 3]);
+      if constexpr (DT == PKV_BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                      __builtin_bit_cast(bf16x8, b4), acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a4),
+                                                     __builtin_bit_cast(f16x8, b4), acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// Broadcast lane H of each 16-lane row to the whole row (DPP row_newbcast).
+template <int H>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x150 + H, 0xf, 0xf, false));
+}
+
+template <typename F, int... Hs>
+__device__ __forceinline__ void for_each_head_impl(F&& f, std::integer_sequence<int, Hs...>) {
+  (f(std::integral_constant<int, Hs>{}), ...);
+}
+// Calls f(std::integral_constant<int, h>) for h = 0 .. N-1.
+template <int N, typename F>
+__device__ __forceinline__ void for_each_head(F&& f) {
+  for_each_head_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One tile of online softmax + P.V.  Tokens >= nvalid of the tile get score
+// -inf, hence probability 0 (their K/V rows were replaced by token 0's).  The probability of (head h, token 4*g4+r)
+// sits in lane 16*g4 + h; the P.V lanes of row g4 pick it up with a DPP row
+// broadcast, so the loop needs neither LDS nor barriers.
+template <int DT, int D, int GP>
+__device__ __forceinline__ void consume_tile(const Tile<DT, D>& t, const Dw<Frag<DT, D>::kDwK>& qf,
+                                             int nvalid, float scale_log2, float& m, float& l,
+                                             float (&acc)[GP][Frag<DT, D>::kW], int lane) {
+  using F = Frag<DT, D>;
+  const int g4 = lane >> 4;
+  f32x4 s = qk_tile<DT, D>(t, qf);
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    x[r] = (4 * g4 + r < nvalid) ? s[r] * scale_log2 : -INFINITY;
+  }
+  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const bool grow = bm > m + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float m_new = fmaxf(m, bm);
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // 0 on the first tile (m = -inf)
+    l *= a;
+    m = m_new;
+    for_each_head<GP>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ah = row_bcast<h>(a);
+#pragma unroll
+      for (int e = 0; e < F::kW; ++e) acc[h][e] *= ah;
+    });
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(x[r] - m);   // masked tokens: exp2(-inf) = 0
+  }
+  l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float vf[F::kW];
+    if constexpr (DT == PKV_F32) {
+#pragma unroll
+      for (int e = 0; e < F::kW; ++e) vf[e] = __uint_as_float(t.v[r].w[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < F::kW / 2; ++e) unpack2<DT>(t.v[r].w[e], vf[2 * e], vf[2 * e + 1]);
+    }
+    for_each_head<GP>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ph = row_bcast<h>(p[r]);
+#pragma unroll
+      for (int e = 0; e < F::kW; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+    });
+  }
+}
+
+template <int DT, int D, int GP>
+__global__ void __launch_bounds__(kWave, split_waves_per_simd<DT>())
+attn_split_kernel(AttnArgs a) {
+  using F = Frag<DT, D>;
+  const int lane = threadIdx.x;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  // workgroup -> (partition, sequence, kv head), partition slowest
+  const int wg = blockIdx.x;
+  const int kvh = wg % a.hkv;
+  const int b = (wg / a.hkv) % a.num_seqs;
+  const int p = wg / (a.hkv * a.num_seqs);
+  int L = a.lens[b];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int G = a.group;
+  const int64_t out_row0 = static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(kvh) * G;
+  if (L == 0) {
+    if (p != 0) return;
+    for (int i = lane; i < G * D; i += kWave) {
+      const int64_t o = out_row0 * D + i;
+      if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = 0.f;
+      else static_cast<uint16_t*>(a.out)[o] = 0;
+    }
+    return;
+  }
+  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  if (p >= nparts) return;
+  const int t0 = p * a.part_tokens;
+  const int t1 = min(L, t0 + a.part_tokens);
+
+  // query group as the MFMA B operand: head c16, same head-dim map as K
+  Dw<F::kDwK> qf;
+  {
+    const int head = c16 < G ? c16 : 0;
+    const char* qrow = static_cast<const char*>(a.q) + (out_row0 + head) * D * F::kBytes;
+    if constexpr (DT == PKV_F32) {
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        Dw<4> x = load_dw<4>(qrow + (16 * j + 4 * g4) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf.w[4 * j + e] = x.w[e];
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        Dw<4> x = load_dw<4>(qrow + (32 * kk + 8 * g4) * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qf.w[4 * kk + e] = x.w[e];
+      }
+    }
+    if (c16 >= G) {
+#pragma unroll
+      for (int i = 0; i < F::kDwK; ++i) qf.w[i] = 0u;
+    }
+  }
+
+  const int bs = a.block_size;
+  const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.table_stride;
+  const int nblk = (L + bs - 1) / bs;   // table entries that may be read
+  const char* kc = static_cast<const char*>(a.kc);
+  const char* vc = static_cast<const char*>(a.vc);
+  const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
+
+  // Block-table slice cached in one VGPR (64 entries), read back per tile
+  // with v_readlane.
+  int tbl_base = (t0 / bs) & ~63;
+  int tbl = 0;
+  {
+    const int j = tbl_base + lane;
+    tbl = j < nblk ? trow[j] : 0;
+  }
+  // Element offset of tile i.  A table entry outside [0, num_blocks) is
+  // clamped into the pool: the kernel never leaves the pool, and the result
+  // for such a (caller-broken) table is unspecified.
+  auto tile_addr = [&](int i) -> int64_t {
+    const int tok = t0 + i * kTile;
+    const int lb = tok / bs;
+    if (lb >= tbl_base + 64) {
+      tbl_base = lb & ~63;
+      const int j = tbl_base + lane;
+      tbl = j < nblk ? trow[j] : 0;
+    }
+    int pb = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    const int off = tok - lb * bs;
+    return static_cast<int64_t>(pb) * a.block_stride + head_off + static_cast<int64_t>(off) * D;
+  };
+
+  float m = -INFINITY;
+  float l = 0.f;
+  float acc[GP][F::kW];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+
+  // Two register stages: tile i+1 is in flight while tile i is consumed.
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  auto nvalid_of = [&](int i) { return min(kTile, t1 - t0 - i * kTile); };
+  Tile<DT, D> ta, tb;
+  load_tile<DT, D>(ta, kc, vc, tile_addr(0), nvalid_of(0), lane);
+  for (int i = 0; i < ntiles; i += 2) {
+    const bool has_b = i + 1 < ntiles;
+    if (has_b) load_tile<DT, D>(tb, kc, vc, tile_addr(i + 1), nvalid_of(i + 1), lane);
+    consume_tile<DT, D, GP>(ta, qf, nvalid_of(i), a.scale_log2, m, l, acc, lane);
+    if (has_b) {
+      if (i + 2 < ntiles) load_tile<DT, D>(ta, kc, vc, tile_addr(i + 2), nvalid_of(i + 2), lane);
+      consume_tile<DT, D, GP>(tb, qf, nvalid_of(i + 1), a.scale_log2, m, l, acc, lane);
+    }
+  }
+
+  // reduce the four token groups
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < F::kW; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[h][e] = v;
+    }
+  // lane group g4 writes heads g4, g4 + 4, ...; lane c16 writes chunk c16
+  for_each_head<GP>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float lh = row_bcast<h>(l);
+    const float mh = row_bcast<h>(m);
+    if ((h & 3) != g4 || h >= G) return;
+    const int64_t row = out_row0 + h;
+    if (nparts == 1) {
+      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+      if (a.out_dtype == PKV_F32) {
+        float* o = static_cast<float*>(a.out) + row * D + c16 * F::kW;
+#pragma unroll
+        for (int e = 0; e < F::kW; ++e) o[e] = acc[h][e] * inv;
+      } else {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + row * D + c16 * F::kW;
+#pragma unroll
+        for (int e = 0; e < F::kW; ++e) {
+          const float y = acc[h][e] * inv;
+          o[e] = (a.out_dtype == PKV_BF16) ? f32_to_bf16_rne(y)
+                                           : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
+        }
+      }
+    } else {
+      const int64_t slot = row * a.max_parts + p;
+      float* w = a.ws_acc + slot * D + c16 * F::kW;
+#pragma unroll
+      for (int e = 0; e < F::kW; ++e) w[e] = acc[h][e];
+      if (c16 == 0) {
+        a.ws_ml[2 * slot + 0] = mh;
+        a.ws_ml[2 * slot + 1] = lh;
+      }
+    }
+  });
+}
+
+// Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with
+// M = max_p m_p.  One workgroup per (sequence, query head); sequences with a
+// single partition were finished by attn_split_kernel.
+template <int D>
+__global__ void __launch_bounds__(kWave)
+attn_reduce_kernel(AttnArgs a) {
+  const int qh = blockIdx.x % a.hq;
+  const int b = blockIdx.x / a.hq;
+  int L = a.lens[b];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
+  if (nparts <= 1) return;
+  const int64_t row = static_cast<int64_t>(b) * a.hq + qh;
+  const float* ml = a.ws_ml + row * a.max_parts * 2;
+  const float* acc = a.ws_acc + row * a.max_parts * D;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+  constexpr int kPer = D / kWave;
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  float den = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float mp = ml[2 * p];
+    const float w = (mp == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+    den = fmaf(w, ml[2 * p + 1], den);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] = fmaf(w, acc[p * D + e * kWave + threadIdx.x], num[e]);
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int64_t o = row * D + e * kWave + threadIdx.x;
+    const float y = num[e] * inv;
+    if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = y;
+    else if (a.out_dtype == PKV_BF16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(y);
+    else static_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
+  }
+}
+
+// ------------------------------------------------------------ dispatch
+constexpr int kDefaultPartition = 512;
+
+int pick_partition(int32_t partition_tokens) {
+  return partition_tokens > 0 ? partition_tokens : kDefaultPartition;
+}
+
+int padded_group(int g) {
+  if (g <= 1) return 1;
+  if (g <= 2) return 2;
+  if (g <= 4) return 4;
+  if (g <= 6) return 6;
+  if (g <= 7) return 7;
+  return 8;
+}
+
+template <int DT, int D, int GP>
+hipError_t launch_split_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_split_kernel<DT, D, GP>), grid, dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_split_d(const AttnArgs& a, int gp, dim3 grid, hipStream_t s) {
+  switch (gp) {
+    case 1: return launch_split_t<DT, D, 1>(a, grid, s);
+    case 2: return launch_split_t<DT, D, 2>(a, grid, s);
+    case 4: return launch_split_t<DT, D, 4>(a, grid, s);
+    case 6: return launch_split_t<DT, D, 6>(a, grid, s);
+    case 7: return launch_split_t<DT, D, 7>(a, grid, s);
+    default: return launch_split_t<DT, D, 8>(a, grid, s);
+  }
+}
+
+template <int DT>
+hipError_t launch_split_dt(const AttnArgs& a, int d, int gp, dim3 grid, hipStream_t s) {
+  if (d == 64) return launch_split_d<DT, 64>(a, gp, grid, s);
+  return launch_split_d<DT, 128>(a, gp, grid, s);
+}
+
+}  // namespace
+
+namespace pkv {
+
+int check_layout(const pkv_cache_layout* l) {
+  if (!l) return PKV_ERR_INVALID;
+  if (l->num_blocks <= 0 || l->num_kv_heads <= 0 || l->block_size <= 0 || l->head_dim <= 0)
+    return PKV_ERR_INVALID;
+  if (elem_bytes(l->dtype) == 0 || l->reserved != 0) return PKV_ERR_INVALID;
+  if (l->head_stride < static_cast<int64_t>(l->block_size) * l->head_dim) return PKV_ERR_INVALID;
+  if (l->block_stride < static_cast<int64_t>(l->num_kv_heads) * l->head_stride) return PKV_ERR_INVALID;
+  if (l->head_stride % 8 != 0 || l->block_stride % 8 != 0) return PKV_ERR_INVALID;
+  return PKV_OK;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID: return "invalid argument";
+    case PKV_ERR_OOM: return "OOM: not enough free KV blocks";
+    case PKV_ERR_NOT_LIVE: return "sequence is not live (unknown or already freed)";
+    case PKV_ERR_ALREADY_PREFILLED: return "sequence is already live";
+    case PKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_INVARIANT: return "block manager invariant violated";
+    default: return "unknown status";
+  }
+}
+
+const char* pkv_version(void) { return "pkv 0.1.0 gfx950"; }
+
+size_t pkv_pool_span_bytes(const pkv_cache_layout* l) {
+  if (pkv::check_layout(l) != PKV_OK) return 0;
+  const int64_t elems = static_cast<int64_t>(l->num_blocks - 1) * l->block_stride +
+                        static_cast<int64_t>(l->num_kv_heads - 1) * l->head_stride +
+                        static_cast<int64_t>(l->block_size) * l->head_dim;
+  return static_cast<size_t>(elems) * pkv::elem_bytes(l->dtype);
+}
+
+int paged_kv_write(const void* key, const void* value, const int64_t* slot_mapping,
+                   int32_t num_tokens, void* key_cache, void* value_cache,
+                   const pkv_cache_layout* l, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK || num_tokens < 0) return PKV_ERR_INVALID;
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping || !key_cache || !value_cache) return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const int64_t row_bytes = static_cast<int64_t>(l->head_dim) * eb;
+  if (row_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if ((l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+                          reinterpret_cast<uintptr_t>(key_cache) |
+                          reinterpret_cast<uintptr_t>(value_cache);
+  if (align % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const int32_t chunks_per_head = static_cast<int32_t>(row_bytes / 16);
+  const int32_t chunks_per_token = chunks_per_head * l->num_kv_heads;
+  const int64_t total = static_cast<int64_t>(num_tokens) * chunks_per_token;
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(kv_write_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(key),
+                     static_cast<const uint4*>(value), slot_mapping, total, chunks_per_head,
+                     chunks_per_token,
+                     static_cast<int64_t>(l->num_blocks) * l->block_size, l->block_size,
+                     l->block_stride * eb / 16, l->head_stride * eb / 16,
+                     static_cast<int32_t>(row_bytes / 16), static_cast<uint4*>(key_cache),
+                     static_cast<uint4*>(value_cache));
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || partition_tokens < 0)
+    return 0;
+  const int part = pick_partition(partition_tokens);
+  const int64_t P = (static_cast<int64_t>(max_context_len) + part - 1) / part;
+  if (P <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_q_heads * P * (head_dim + 2) * sizeof(float);
+}
+
+int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, const pkv_cache_layout* l, int32_t partition_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK) return PKV_ERR_INVALID;
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || block_table_stride < 0 ||
+      partition_tokens < 0)
+    return PKV_ERR_INVALID;
+  if (num_q_heads % l->num_kv_heads != 0) return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != l->dtype) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
+    return PKV_ERR_INVALID;
+  if (!(scale == scale)) return PKV_ERR_INVALID;
+  const int group = num_q_heads / l->num_kv_heads;
+  if (group > 8) return PKV_ERR_UNSUPPORTED;
+  if (l->head_dim != 64 && l->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (l->block_size % kTile != 0) return PKV_ERR_UNSUPPORTED;
+  const int part = pick_partition(partition_tokens);
+  if (part % kTile != 0) return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !key_cache || !value_cache || !context_lens ||
+      (max_context_len > 0 && !block_tables))
+    return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(key_cache) |
+                          reinterpret_cast<uintptr_t>(value_cache);
+  if (align % 16 != 0 || (l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  const int64_t P = max_context_len > 0 ? (static_cast<int64_t>(max_context_len) + part - 1) / part : 1;
+  const size_t need = paged_decode_attention_workspace_size(num_seqs, num_q_heads, l->num_kv_heads,
+                                                            l->head_dim, max_context_len, part);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PKV_ERR_WORKSPACE;
+  const int64_t wgs = P * num_seqs * l->num_kv_heads;
+  if (wgs > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+
+  AttnArgs a;
+  a.q = q;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  const int64_t acc_floats = static_cast<int64_t>(num_seqs) * num_q_heads * P * l->head_dim;
+  a.ws_acc = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need > 0 ? static_cast<float*>(workspace) + acc_floats : nullptr;
+  a.out = out;
+  a.block_stride = l->block_stride;
+  a.head_stride = l->head_stride;
+  a.table_stride = block_table_stride;
+  a.num_blocks = l->num_blocks;
+  a.block_size = l->block_size;
+  a.num_seqs = num_seqs;
+  a.hq = num_q_heads;
+  a.hkv = l->num_kv_heads;
+  a.group = group;
+  a.max_len = max_context_len;
+  a.part_tokens = part;
+  a.max_parts = static_cast<int32_t>(P);
+  a.out_dtype = out_dtype;
+  a.scale_log2 = scale * kLog2e;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(wgs));
+  const int gp = padded_group(group);
+  hipError_t e;
+  switch (l->dtype) {
+    case PKV_BF16: e = launch_split_dt<PKV_BF16>(a, l->head_dim, gp, grid, s); break;
+    case PKV_F16: e = launch_split_dt<PKV_F16>(a, l->head_dim, gp, grid, s); break;
+    default: e = launch_split_dt<PKV_F32>(a, l->head_dim, gp, grid, s); break;
+  }
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  if (P > 1) {
+    const dim3 rgrid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
+    if (l->head_dim == 64) hipLaunchKernelGGL(attn_reduce_kernel<64>, rgrid, dim3(kWave), 0, s, a);
+    else hipLaunchKernelGGL(attn_reduce_kernel<128>, rgrid, dim3(kWave), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,
+                            const int32_t* rows, const int32_t* lens, const int32_t* new_block,
+                            int32_t n, int32_t block_size, void* stream) {
+  if (n < 0 || num_rows < 0 || block_size <= 0 || block_table_stride <= 0) return PKV_ERR_INVALID;
+  if (n == 0) return PKV_OK;
+  if (!block_tables || !lens || !new_block) return PKV_ERR_INVALID;
+  hipLaunchKernelGGL(table_update_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), block_tables, num_rows, block_table_stride,
+                     rows, lens, new_block, n, block_size);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // extern "C"

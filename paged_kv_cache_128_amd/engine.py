@@ -1,0 +1,166 @@
+"""One layer's paged KV cache on one GPU: the pool, the host block manager,
+device-resident block tables and the decode step that ties them together.
+
+A decode step is the hot path of [MiniPaged-Qwen] §10 and §13 in order:
+
+  1. block manager append for every row (one batched C call; all or nothing,
+     [mini-vLLM BM] "Block Manager 和 Scheduler 如何协作"),
+  2. one host-to-device copy of the step's metadata (slots, lengths, opened
+     blocks) from a pinned staging buffer,
+  3. table update kernel (opened blocks -> device block table),
+  4. paged_kv_write of the new K/V rows ([MiniPaged-Qwen] §12),
+  5. paged_decode_attention over the updated cache ([MiniPaged-Qwen] §13),
+     so the new token attends to itself ([MiniPaged-Qwen] §1.1: append, then
+     attend over positions 0..L).
+
+Rows are batch positions; each live sequence occupies one row.  All device
+memory comes from torch; all work runs in libpkv on torch's current stream.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (KVBlockManager, new_pool, paged_decode_attention, paged_kv_write,
+               update_block_tables, workspace_size)
+
+
+class _Staging:
+    """Pinned host buffer + device mirror for one step's metadata, with an
+    event guarding reuse of the host side."""
+
+    def __init__(self, rows: int, device):
+        self.rows = rows
+        nbytes = 16 * rows
+        self.host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        self.dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = self.host.numpy()
+        self.slots = h[: 8 * rows].view(np.int64)
+        self.lens = h[8 * rows: 12 * rows].view(np.int32)
+        self.newb = h[12 * rows: 16 * rows].view(np.int32)
+        self.d_slots = self.dev[: 8 * rows].view(torch.int64)
+        self.d_lens = self.dev[8 * rows: 12 * rows].view(torch.int32)
+        self.d_newb = self.dev[12 * rows: 16 * rows].view(torch.int32)
+        self.event: Optional[torch.cuda.Event] = None
+
+    def wait_free(self):
+        if self.event is not None:
+            self.event.synchronize()
+
+    def upload(self, n: int):
+        if n == self.rows:
+            self.dev.copy_(self.host, non_blocking=True)
+        else:
+            self.d_slots[:n].copy_(self.host[: 8 * n].view(torch.int64), non_blocking=True)
+            self.d_lens[:n].copy_(self.host[8 * self.rows: 8 * self.rows + 4 * n].view(torch.int32),
+                                  non_blocking=True)
+            self.d_newb[:n].copy_(self.host[12 * self.rows: 12 * self.rows + 4 * n].view(torch.int32),
+                                  non_blocking=True)
+        self.event = torch.cuda.Event()
+        self.event.record()
+
+
+class PagedKVEngine:
+    def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                 dtype: torch.dtype, max_rows: int, max_blocks_per_seq: int,
+                 initial_free_order: Optional[Sequence[int]] = None, device="cuda",
+                 fill_bits: Optional[int] = None, partition_tokens: int = 0,
+                 num_q_heads: Optional[int] = None):
+        self.device = torch.device(device)
+        self.num_blocks = num_blocks
+        self.num_kv_heads = num_kv_heads
+        self.block_size = block_size
+        self.head_dim = head_dim
+        self.dtype = dtype
+        self.max_rows = max_rows
+        self.width = max_blocks_per_seq
+        self.partition_tokens = partition_tokens
+        self.manager = KVBlockManager(num_blocks, block_size, initial_free_order)
+        self.pool, self.key_cache, self.value_cache = new_pool(
+            num_blocks, num_kv_heads, block_size, head_dim, dtype, self.device, fill_bits)
+        self.tables = torch.full((max_rows, self.width), -1, dtype=torch.int32, device=self.device)
+        self.row_seq: Dict[int, int] = {}
+        self._staging = [_Staging(max_rows, self.device), _Staging(max_rows, self.device)]
+        self._turn = 0
+        self._ws = None
+        self._nq = num_q_heads
+
+    # -- admission / release ------------------------------------------------
+    def prefill(self, seq_id: int, row: int, key: torch.Tensor, value: torch.Tensor,
+                num_tokens: Optional[int] = None) -> np.ndarray:
+        """Admit ``seq_id`` into ``row`` with its prompt K/V ([n, H_kv, D]
+        device tensors, n may be 0): allocate, write, publish the table row."""
+        n = key.shape[0] if num_tokens is None else num_tokens
+        slots = self.manager.allocate_for_prefill(seq_id, n)
+        if n > 0:
+            d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
+            paged_kv_write(key, value, d_slots, self.key_cache, self.value_cache)
+        self._publish_row(seq_id, row)
+        return slots
+
+    def prefill_many(self, seq_ids: Sequence[int], rows: Sequence[int], lengths: Sequence[int],
+                     key: torch.Tensor, value: torch.Tensor) -> np.ndarray:
+        """Admit several sequences whose prompt rows are concatenated in
+        ``key``/``value`` ([sum(lengths), H_kv, D]) with one write launch."""
+        all_slots = []
+        for sid, n in zip(seq_ids, lengths):
+            all_slots.append(self.manager.allocate_for_prefill(int(sid), int(n)))
+        slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
+        if slots.size:
+            d_slots = torch.from_numpy(slots).to(self.device)
+            paged_kv_write(key, value, d_slots, self.key_cache, self.value_cache)
+        for sid, row in zip(seq_ids, rows):
+            self._publish_row(int(sid), int(row))
+        return slots
+
+    def _publish_row(self, seq_id: int, row: int):
+        tab = self.manager.block_tables([seq_id], self.width, -1)
+        self.tables[row].copy_(torch.from_numpy(tab[0]), non_blocking=False)
+        self.row_seq[row] = seq_id
+
+    def free(self, seq_id: int) -> None:
+        self.manager.free_sequence(seq_id)
+        for r, s in list(self.row_seq.items()):
+            if s == seq_id:
+                del self.row_seq[r]
+
+    # -- decode ---------------------------------------------------------------
+    def workspace(self, num_seqs: int, num_q_heads: int, max_context_len: int) -> Optional[torch.Tensor]:
+        need = workspace_size(num_seqs, num_q_heads, self.num_kv_heads, self.head_dim,
+                              max_context_len, self.partition_tokens)
+        if need == 0:
+            return None
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def append(self, seq_ids: np.ndarray):
+        """Host part of a step: batched append into the next staging buffer
+        and its upload.  Returns the staging object (device views inside)."""
+        st = self._staging[self._turn]
+        self._turn ^= 1
+        st.wait_free()
+        n = len(seq_ids)
+        self.manager.append_slots_for_decode(seq_ids, st.slots[:n], st.lens[:n], st.newb[:n])
+        st.upload(n)
+        return st
+
+    def decode_step(self, seq_ids: np.ndarray, new_k: torch.Tensor, new_v: torch.Tensor,
+                    q: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """One decode step for rows 0..n-1 holding ``seq_ids`` (int64).
+        ``max_context_len`` defaults to the longest length after the append
+        (known on the host from the manager, no device sync)."""
+        n = len(seq_ids)
+        st = self.append(seq_ids)
+        if max_context_len is None:
+            max_context_len = int(st.lens[:n].max()) if n else 0
+        update_block_tables(self.tables, st.d_lens[:n], st.d_newb[:n], self.block_size)
+        paged_kv_write(new_k, new_v, st.d_slots[:n], self.key_cache, self.value_cache)
+        ws = self.workspace(n, q.shape[1], max_context_len)
+        return paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n],
+                                      st.d_lens[:n], scale, out=out,
+                                      partition_tokens=self.partition_tokens,
+                                      max_context_len=max_context_len, workspace=ws)

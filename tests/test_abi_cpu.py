@@ -1,0 +1,106 @@
+"""The C-ABI library loads on a CPU-only host and exports every entry point
+include/pkv.h declares; host-side argument checks of the GPU entry points
+reject bad input before anything reaches the GPU.  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_128_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = "\n".join(line for line in text.splitlines() if not line.lstrip().startswith("#"))
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{()]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = pkv.load_library()
+    names = _declared_functions()
+    assert len(names) >= 20, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in pkv.h but not exported"
+    # the binding wraps exactly the declared ABI
+    assert set(pkv.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version():
+    lib = pkv.load_library()
+    for code in range(-8, 1):
+        assert lib.pkv_status_string(code)
+    assert b"unknown" in lib.pkv_status_string(-99)
+    assert pkv.version().startswith("pkv ")
+
+
+def _layout(**kw):
+    base = dict(num_blocks=64, num_kv_heads=4, block_size=16, head_dim=64, dtype=pkv.PKV_F32,
+                reserved=0, block_stride=2 * 4 * 16 * 64, head_stride=16 * 64)
+    base.update(kw)
+    return pkv.CacheLayout(**base)
+
+
+def test_pool_span_and_layout_validation():
+    lib = pkv.load_library()
+    lay = _layout()
+    span = lib.pkv_pool_span_bytes(ctypes.byref(lay))
+    assert span == ((64 - 1) * 2 * 4 * 16 * 64 + 3 * 16 * 64 + 16 * 64) * 4
+    for bad in (dict(num_blocks=0), dict(head_stride=10), dict(block_stride=16 * 64),
+                dict(dtype=7), dict(reserved=1)):
+        assert lib.pkv_pool_span_bytes(ctypes.byref(_layout(**bad))) == 0
+
+
+def test_attention_argument_checks_need_no_gpu():
+    lib = pkv.load_library()
+    lay = _layout()
+    fake = ctypes.c_void_p(0x1000)
+    def call(**kw):
+        a = dict(out=fake, out_dtype=pkv.PKV_F32, q=fake, kc=fake, vc=fake, tables=fake, stride=4,
+                 lens=fake, B=4, hq=4, max_len=64, scale=0.125, lay=lay, part=0, ws=None, wsb=0)
+        a.update(kw)
+        return lib.paged_decode_attention(a["out"], a["out_dtype"], a["q"], a["kc"], a["vc"],
+                                          a["tables"], a["stride"], a["lens"], a["B"], a["hq"],
+                                          a["max_len"], a["scale"], ctypes.byref(a["lay"]),
+                                          a["part"], a["ws"], a["wsb"], None)
+    assert call(hq=6) == -1                          # H_q % H_kv != 0
+    assert call(max_len=65) == -1                    # beyond table width * bs
+    assert call(out_dtype=pkv.PKV_BF16) == -1        # out dtype neither f32 nor cache dtype
+    assert call(hq=4 * 9) == -5                      # group 9 > 8
+    assert call(lay=_layout(head_dim=96, head_stride=16 * 96, block_stride=8 * 16 * 96)) == -5
+    assert call(lay=_layout(block_size=8, head_stride=8 * 64, block_stride=8 * 8 * 64), max_len=32) == -5
+    assert call(part=24) == -1                       # partition not a multiple of 16
+    assert call(max_len=64, stride=4, part=16) == -7 # needs workspace, none given
+    assert call(B=0) == 0                            # nothing to do
+    assert call(scale=float("nan")) == -1
+
+
+def test_workspace_size_formula():
+    assert pkv.workspace_size(8, 32, 8, 128, 32768, 512) == 8 * 32 * 64 * 130 * 4
+    assert pkv.workspace_size(4, 4, 4, 64, 512, 512) == 0
+    assert pkv.workspace_size(4, 4, 4, 64, 513, 512) == 4 * 4 * 2 * 66 * 4
+
+
+def test_write_argument_checks_need_no_gpu():
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    lay = _layout()
+    assert lib.paged_kv_write(fake, fake, fake, -1, fake, fake, ctypes.byref(lay), None) == -1
+    assert lib.paged_kv_write(fake, fake, fake, 0, fake, fake, ctypes.byref(lay), None) == 0
+    odd = _layout(dtype=pkv.PKV_BF16, head_dim=4, head_stride=16 * 8, block_stride=4 * 16 * 8)
+    assert lib.paged_kv_write(fake, fake, fake, 3, fake, fake, ctypes.byref(odd), None) == -5
+    assert lib.pkv_update_block_tables(fake, 4, 0, None, fake, fake, 3, 16, None) == -1
+    assert lib.pkv_update_block_tables(fake, -1, 4, None, fake, fake, 3, 16, None) == -1
+
+
+def test_manager_create_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        pkv.KVBlockManager(0, 16)
+    with pytest.raises(ValueError):
+        pkv.KVBlockManager(4, 16, [0, 1, 1, 2])
+    with pytest.raises(ValueError):
+        pkv.KVBlockManager(4, 0)

@@ -1,0 +1,219 @@
+"""GPU parity: the HIP write and attention (through the C ABI binding) against
+the CPU oracle on the same seeded inputs.
+
+Bars: the cache write is bit-exact over the whole pool (poison included);
+attention is within 2e-3 (fp16/bf16 KV) or 1e-5 (fp32 KV) max abs error of
+the float64 oracle, with fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.replay import decode_state
+
+from gpu_harness import bits_u, engine_for, run_step, to_device, TORCH_DTYPE
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+
+
+def _banner(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _pool_bits(eng):
+    pool = eng.pool
+    return bits_u(pool[:, 0]), bits_u(pool[:, 1])
+
+
+def _oracle_bits(a, dtype):
+    if dtype == "bf16":
+        return a
+    if dtype == "f16":
+        return a.view(np.uint16)
+    return a.view(np.uint32)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen2_1p5b_b32"])
+def test_write_and_attention_full_compare(name):
+    cfg = synth.CONFIGS[name]
+    _banner(f"config {cfg.index} {name}: full write + attention compare")
+    wl = synth.decode_workload(cfg)
+    st = decode_state(wl)
+    eng = engine_for(wl)
+    out = run_step(eng, wl)
+    # manager parity: the C++ manager produced the same tables and lengths
+    ids = list(range(cfg.batch))
+    assert np.array_equal(eng.manager.context_lens(ids), st.context_lens)
+    assert eng.manager.free_list() == st.manager.free
+    width = eng.width
+    assert np.array_equal(eng.tables.cpu().numpy(), st.manager.block_tables(ids, width, -1))
+    # write: whole pool bit-exact, poison included
+    kb, vb = _pool_bits(eng)
+    assert np.array_equal(kb, _oracle_bits(st.key_cache, cfg.dtype))
+    assert np.array_equal(vb, _oracle_bits(st.value_cache, cfg.dtype))
+    # attention
+    ref = oracle.decode_attention(wl.q, st.key_cache, st.value_cache, st.block_tables,
+                                  st.context_lens, cfg.scale, cfg.dtype)
+    got = out.double().cpu().numpy()
+    err = np.abs(got - ref).max()
+    _banner(f"config {cfg.index}: max abs err {err:.3e}")
+    assert err <= TOL[cfg.dtype], err
+
+
+def test_single_token_is_exact():
+    """L = 1: the only weight is exactly 1, so the output equals the new
+    token's V row bit for bit (fp32 output, fp32 KV)."""
+    cfg = synth.CONFIGS["tiny"]
+    wl = synth.decode_workload(cfg)
+    eng = engine_for(wl)
+    out = run_step(eng, wl).cpu().numpy()
+    b = int(np.nonzero(wl.context_lens == 1)[0][0])
+    for qh in range(cfg.num_q_heads):
+        assert np.array_equal(out[b, qh], wl.new_v[b, qh // (cfg.num_q_heads // cfg.num_kv_heads)])
+
+
+def _small_case(dtype, h_q, h_kv, d, bs, lens, num_blocks, seed, pad=-1):
+    """Direct (engine-free) inputs: random pool contents, a random placement,
+    tables padded with `pad`."""
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    perm = rng.permutation(num_blocks)
+    width = max(1, max(-(-L // bs) for L in lens))
+    tables = np.full((B, width), pad, dtype=np.int32)
+    used = 0
+    for b, L in enumerate(lens):
+        nb = -(-L // bs)
+        tables[b, :nb] = perm[used:used + nb]
+        used += nb
+    assert used <= num_blocks
+    kc = synth.normal(rng, (num_blocks, h_kv, bs, d), dtype)
+    vc = synth.normal(rng, (num_blocks, h_kv, bs, d), dtype)
+    # poison every slot past each sequence's length
+    poison = synth.poison_array((), dtype)
+    for b, L in enumerate(lens):
+        nb = -(-L // bs)
+        if nb and L % bs:
+            kc[tables[b, nb - 1], :, L % bs:, :] = poison
+            vc[tables[b, nb - 1], :, L % bs:, :] = poison
+    q = synth.normal(rng, (B, h_q, d), dtype)
+    return dict(kc=kc, vc=vc, tables=tables, lens=np.array(lens, dtype=np.int32), q=q,
+                scale=float(np.float32(1.0) / np.sqrt(np.float32(d))), dtype=dtype, bs=bs)
+
+
+def _gpu_attend(case, partition_tokens=0, out_dtype=torch.float32, split_layout=False, tables=None):
+    import paged_kv_cache_128_amd as pkv
+    dt = case["dtype"]
+    N, h_kv, bs, d = case["kc"].shape
+    if split_layout:
+        kc = to_device(case["kc"], dt)
+        vc = to_device(case["vc"], dt)
+    else:
+        pool, kc, vc = pkv.new_pool(N, h_kv, bs, d, TORCH_DTYPE[dt])
+        kc.copy_(to_device(case["kc"], dt))
+        vc.copy_(to_device(case["vc"], dt))
+    t = torch.from_numpy(case["tables"] if tables is None else tables).cuda()
+    lens = torch.from_numpy(case["lens"]).cuda()
+    q = to_device(case["q"], dt)
+    out = pkv.paged_decode_attention(q, kc, vc, t, lens, case["scale"], out_dtype=out_dtype,
+                                     partition_tokens=partition_tokens,
+                                     max_context_len=max(int(case["lens"].max()), 0))
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_attend(case):
+    return oracle.decode_attention(case["q"], case["kc"], case["vc"], case["tables"], case["lens"],
+                                   case["scale"], case["dtype"])
+
+
+@pytest.mark.parametrize("dtype,h_q,h_kv,d", [("bf16", 28, 4, 128), ("f16", 12, 2, 128),
+                                              ("f32", 4, 4, 64), ("bf16", 8, 8, 64),
+                                              ("f16", 6, 2, 64), ("f32", 16, 2, 128),
+                                              ("bf16", 10, 2, 128), ("bf16", 8, 1, 128),
+                                              ("f16", 4, 2, 128)])
+def test_edge_lengths_and_groups(dtype, h_q, h_kv, d):
+    bs = 16
+    lens = [1, bs - 1, bs, bs + 1, 2 * bs + 5, 3 * bs, 100, 37]
+    _banner(f"edge lengths {dtype} Hq={h_q} Hkv={h_kv} D={d}")
+    case = _small_case(dtype, h_q, h_kv, d, bs, lens, 64, seed=h_q * 1000 + d)
+    ref = _oracle_attend(case)
+    for part in (0, 16, 48):
+        got = _gpu_attend(case, partition_tokens=part).double().cpu().numpy()
+        err = np.abs(got - ref).max()
+        assert err <= TOL[dtype], (part, err)
+
+
+def test_block_size_32_and_split_layout():
+    case = _small_case("bf16", 32, 8, 128, 32, [1, 31, 32, 33, 700, 513], 96, seed=5)
+    ref = _oracle_attend(case)
+    for split in (False, True):
+        for part in (0, 32, 512):
+            got = _gpu_attend(case, partition_tokens=part, split_layout=split).double().cpu().numpy()
+            assert np.abs(got - ref).max() <= 2e-3
+
+
+def test_padding_value_does_not_matter_and_relabelling_is_bitwise():
+    case = _small_case("bf16", 28, 4, 128, 16, [5, 16, 17, 300, 1000], 200, seed=9)
+    a = _gpu_attend(case).cpu().numpy()
+    t2 = case["tables"].copy()
+    t2[t2 == -1] = np.iinfo(np.int32).max
+    b = _gpu_attend(case, tables=t2).cpu().numpy()
+    assert np.array_equal(a, b)
+    # physical relabelling: move every block, fix the tables; bitwise equal
+    perm = np.random.default_rng(1).permutation(200)
+    inv = np.argsort(perm)
+    moved = dict(case)
+    moved["kc"] = case["kc"][inv]
+    moved["vc"] = case["vc"][inv]
+    moved["tables"] = np.where(case["tables"] >= 0, perm[np.maximum(case["tables"], 0)], -1).astype(np.int32)
+    c = _gpu_attend(moved).cpu().numpy()
+    assert np.array_equal(a, c)
+    # paged == contiguous: identity placement of the same logical K/V
+    ident = dict(case)
+    B = len(case["lens"])
+    W = case["tables"].shape[1]
+    kc = np.empty((B * W,) + case["kc"].shape[1:], dtype=case["kc"].dtype)
+    vc = np.empty_like(kc)
+    for b in range(B):
+        for j in range(W):
+            src = case["tables"][b, j]
+            kc[b * W + j] = case["kc"][src] if src >= 0 else case["kc"][0]
+            vc[b * W + j] = case["vc"][src] if src >= 0 else case["vc"][0]
+    ident["kc"], ident["vc"] = kc, vc
+    ident["tables"] = np.arange(B * W, dtype=np.int32).reshape(B, W)
+    d = _gpu_attend(ident).cpu().numpy()
+    assert np.array_equal(a, d)
+
+
+def test_empty_context_and_half_outputs():
+    case = _small_case("bf16", 8, 2, 128, 16, [0, 1, 40], 16, seed=3)
+    got = _gpu_attend(case).cpu().numpy()
+    assert np.all(got[0] == 0)
+    ref = _oracle_attend(case)
+    assert np.abs(got[1:] - ref[1:]).max() <= 2e-3
+    for od in (torch.bfloat16,):
+        h = _gpu_attend(case, out_dtype=od).float().cpu().numpy()
+        half_ulp = np.abs(ref[1:]) * 2.0 ** -8
+        assert np.all(np.abs(h[1:] - ref[1:]) <= 2e-3 + half_ulp)
+    case16 = _small_case("f16", 8, 2, 128, 16, [0, 3, 40], 16, seed=4)
+    h = _gpu_attend(case16, out_dtype=torch.float16).float().cpu().numpy()
+    ref = _oracle_attend(case16)
+    assert np.all(h[0] == 0)
+    assert np.all(np.abs(h[1:] - ref[1:]) <= 2e-3 + np.abs(ref[1:]) * 2.0 ** -11)
+
+
+def test_write_skips_out_of_range_slots():
+    import paged_kv_cache_128_amd as pkv
+    pool, kc, vc = pkv.new_pool(4, 2, 16, 64, torch.bfloat16, fill_bits=0x7FC5)
+    key = torch.ones((3, 2, 64), dtype=torch.bfloat16, device="cuda")
+    slots = torch.tensor([-1, 4 * 16, 17], dtype=torch.int64, device="cuda")
+    pkv.paged_kv_write(key, key * 2, slots, kc, vc)
+    torch.cuda.synchronize()
+    kb = bits_u(kc)
+    assert np.count_nonzero(kb != 0x7FC5) == 2 * 64          # only slot 17 (block 1, offset 1)
+    assert np.all(kc[1, :, 1].float().cpu().numpy() == 1.0)
+    assert np.all(vc[1, :, 1].float().cpu().numpy() == 2.0)

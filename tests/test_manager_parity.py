@@ -1,0 +1,125 @@
+"""The C++ block manager (through the C ABI) against the oracle manager on
+the pages' worked examples and on seeded random op traces: identical slots,
+tables, lengths, free-list order and error kinds after every op.  CPU only
+(host logic)."""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_cache_128_amd as pkv
+import synth
+
+ERR = {oracle.InvalidArgument: pkv.InvalidArgumentError, oracle.OutOfBlocks: pkv.OutOfBlocksError,
+       oracle.NotLive: pkv.NotLiveError, oracle.AlreadyPrefilled: pkv.AlreadyPrefilledError}
+
+
+def _run(mgr, op, impl):
+    """Apply op; returns ("ok", result) or ("err", kind)."""
+    try:
+        if op[0] == "prefill":
+            r = mgr.allocate_for_prefill(op[1], op[2])
+            return "ok", [int(x) for x in r]
+        if op[0] == "append":
+            return "ok", int(mgr.append_slot_for_decode(op[1]))
+        if op[0] == "append_batch":
+            r = mgr.append_slots_for_decode(list(op[1]))
+            if impl == "c":
+                slots, lens, newb = r
+                return "ok", [int(x) for x in slots]
+            return "ok", [int(x) for x in r]
+        if op[0] == "free":
+            mgr.free_sequence(op[1])
+            return "ok", None
+        return "ok", bool(mgr.can_allocate(op[1]))
+    except (oracle.ManagerError, pkv.PkvError) as e:
+        for o, c in ERR.items():
+            if isinstance(e, o) or isinstance(e, c):
+                return "err", o.__name__
+        raise
+
+
+def _same_state(o, c, ids):
+    assert c.free_list() == o.free
+    assert c.num_live_sequences() == len(o.seqs)
+    for s in ids:
+        if o.is_live(s):
+            assert c.block_table(s) == o.block_table(s)
+            assert c.context_len(s) == o.context_len(s)
+        else:
+            with pytest.raises(pkv.NotLiveError):
+                c.context_len(s)
+    assert c.check_invariants()
+
+
+@pytest.mark.parametrize("seed,n_blocks,bs,sort", [(11, 48, 4, False), (12, 9, 1, True),
+                                                   (13, 20, 16, False), (14, 100, 3, True),
+                                                   (15, 33, 7, False)])
+def test_random_traces_match_oracle(seed, n_blocks, bs, sort):
+    order = np.random.default_rng(seed).permutation(n_blocks)
+    o = oracle.BlockManager(n_blocks, bs, order, sort_on_release=sort)
+    c = pkv.KVBlockManager(n_blocks, bs, order, sort_on_release=sort)
+    ids = list(range(30))
+    kinds = set()
+    for op in synth.manager_op_trace(seed, 3000, max_id=30, max_prefill=50):
+        ro = _run(o, op, "o")
+        rc = _run(c, op, "c")
+        assert ro == rc, (op, ro, rc)
+        kinds.add(ro[1] if ro[0] == "err" else "ok")
+        _same_state(o, c, ids)
+    assert {"ok", "OutOfBlocks", "NotLive", "AlreadyPrefilled", "InvalidArgument"} <= kinds
+
+
+def test_worked_examples_through_c_abi(golden):
+    g = golden["address_translation"]
+    m = pkv.KVBlockManager(16, 4, [5, 2, 9, 1] + [i for i in range(16) if i not in (5, 2, 9, 1)])
+    slots = m.allocate_for_prefill(0, 16)
+    assert slots[g["token_pos"]] == g["slot"]
+    g = golden["lifecycle"]
+    m = pkv.KVBlockManager(16, 4, g["free_front"] + [i for i in range(16) if i not in g["free_front"]])
+    slots = m.allocate_for_prefill(0, g["prompt"])
+    assert [[s // 4, s % 4] for s in slots] == g["prompt_block_offsets"]
+    for tok in "GHI":
+        s = m.append_slot_for_decode(0)
+        assert [s // 4, s % 4] == [g[tok]["block"], g[tok]["offset"]]
+    assert m.block_table(0) == g["table_final"]
+    g = golden["leetcode22_tests"]["report"]
+    m = pkv.KVBlockManager(g["num_blocks"], g["block_size"], sort_on_release=True)
+    m.allocate_for_prefill(5, g["prompt"])
+    m.free_sequence(5)
+    assert m.free_list() == g["free_after_release"]
+    with pytest.raises(pkv.NotLiveError):
+        m.free_sequence(5)
+
+
+def test_batched_append_outputs_new_blocks():
+    m = pkv.KVBlockManager(16, 4)
+    m.allocate_for_prefill(0, 4)
+    m.allocate_for_prefill(1, 3)
+    slots, lens, newb = m.append_slots_for_decode([0, 1])
+    assert lens.tolist() == [5, 4]
+    assert newb[0] == m.block_table(0)[1] and newb[1] == -1
+    assert slots.tolist() == [m.block_table(0)[1] * 4, m.block_table(1)[0] * 4 + 3]
+    tabs = m.block_tables([0, 1], 3, -1)
+    assert tabs.tolist() == [m.block_table(0) + [-1], m.block_table(1) + [-1, -1]]
+    with pytest.raises(pkv.InvalidArgumentError):
+        m.block_tables([0, 1], 1, -1)
+
+
+def test_churn_replay_matches_oracle():
+    cfg = synth.CONFIGS["qwen2_7b_b64"]
+    rng = np.random.default_rng(cfg.seed)
+    rng.integers(512, 8193, size=cfg.batch)
+    events = synth.churn_events(rng, 120)
+    o = oracle.BlockManager(cfg.num_blocks, cfg.block_size)
+    c = pkv.KVBlockManager(cfg.num_blocks, cfg.block_size)
+    from oracle.replay import replay_churn
+    replay_churn(o, events)
+    for ev in events:
+        if ev[0] == "prefill":
+            c.allocate_for_prefill(ev[1], ev[2], want_slots=False)
+        elif ev[0] == "grow":
+            for _ in range(ev[2]):
+                c.append_slots_for_decode(list(ev[1]))
+        else:
+            c.free_sequence(ev[1])
+    assert c.free_list() == o.free
