@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV cache decode hot path on one MI355X.
+
+One step = the whole hot path over one batch: host block-manager append for
+every sequence, metadata upload, block-table update, paged_kv_write of the
+new K/V rows, and paged decode attention (partition kernel + split-K merge)
+over the updated cache.  Default workload: the Qwen2-7B-shaped batch-64
+decode (H_q 28, H_kv 4, D 128, bf16, block_size 16, context lengths
+U[512, 8192], pool of 65,536 blocks fragmented by a seeded churn of 500
+prior sequences).  Inputs are seeded synthetic tensors (``synth``), resident
+in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is the KV bytes the steps' attention must
+read (sum over sequences of L * H_kv * 2 * D * elem_bytes) divided by the
+wall time of the timed steps.  ``roofline`` is for the attention partition
+kernel (the dominant kernel): KV bytes per launch over its mean duration
+from HIP events recorded on the launch stream during the timed steps.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME]
+    python bench.py --calibrate-copy      # plain 1 GiB copy, for PMC scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_kernel_qwen2_7b_b64_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc", "pkv_kernels.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    from the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, None
+    text = open(TRAFFIC_FILE).read()
+    sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
+    if not sha or not tb or sha.group(1) != kernel_source_sha():
+        return None, None
+    return float(tb.group(1)), sha.group(1)
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(cfg, wl, budget_s: float):
+    """The CPU oracle, untuned, on a bounded sample of the same workload: the
+    first few sequences (churned pool state, history prefill, the measured
+    append and write, gather-then-contiguous float64 attention).  Only the
+    step's write and attention are timed."""
+    import oracle
+    from oracle.replay import replay_churn
+    import synth
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_baseline(cfg, wl, budget_s, oracle, replay_churn, synth)
+
+
+def _cpu_baseline(cfg, wl, budget_s, oracle, replay_churn, synth):
+    t_setup = time.perf_counter()
+    mgr = oracle.BlockManager(cfg.num_blocks, cfg.block_size, wl.initial_free_order)
+    replay_churn(mgr, wl.churn)
+    fill = synth.poison_array((), cfg.dtype)
+    kc, vc = oracle.new_pool(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, fill)
+    elem = synth.ELEM_BYTES[cfg.dtype]
+    done_bytes = 0
+    done_seqs = 0
+    elapsed = 0.0
+    for b in range(len(wl.context_lens)):
+        slots = mgr.allocate_for_prefill(b, int(wl.context_lens[b]) - 1)
+        oracle.write_kv(wl.hist_k[b], wl.hist_v[b], slots, kc, vc, cfg.block_size)
+        t0 = time.perf_counter()
+        step = [mgr.append_slot_for_decode(b)]
+        oracle.write_kv(wl.new_k[b:b + 1], wl.new_v[b:b + 1], step, kc, vc, cfg.block_size)
+        L = mgr.context_len(b)
+        table = np.array([mgr.block_table(b)], dtype=np.int32)
+        oracle.decode_attention(wl.q[b:b + 1], kc, vc, table, [L], cfg.scale, cfg.dtype)
+        elapsed += time.perf_counter() - t0
+        done_bytes += L * cfg.num_kv_heads * 2 * cfg.head_dim * elem
+        done_seqs += 1
+        if elapsed >= budget_s:
+            break
+    log(f"cpu baseline: {done_seqs} sequences in {elapsed:.2f}s "
+        f"(setup {time.perf_counter() - t_setup - elapsed:.1f}s)")
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done_seqs} of {len(wl.context_lens)} sequences of the same workload: "
+                      f"append + write + float64 gather-then-contiguous attention, "
+                      f"{done_bytes} KV bytes in {elapsed:.2f} s on one host thread",
+            "decode_tokens_per_s": done_seqs / elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen2_7b_b64")
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="split-K partition length (-1: the workload's own, else library default)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-iters", type=int, default=20)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import torch
+    import synth
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.steps:
+        raise SystemExit("the serving-trace workload is driven by its own test, not by bench.py")
+    tdtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cfg.dtype]
+    t_gen = time.perf_counter()
+    wl = synth.decode_workload(cfg)
+    B = len(wl.context_lens)
+    log(f"workload {cfg.name}: B={B} sum(L)={int(wl.context_lens.sum())} "
+        f"(generated in {time.perf_counter() - t_gen:.1f}s)")
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    total_steps = args.warmup + args.steps
+    width = int(-(-(int(wl.context_lens.max()) + total_steps) // cfg.block_size))
+    part = cfg.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
+    eng = PagedKVEngine(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, tdtype, B,
+                        width, wl.initial_free_order, partition_tokens=part,
+                        num_q_heads=cfg.num_q_heads)
+    for ev in wl.churn:
+        if ev[0] == "prefill":
+            eng.manager.allocate_for_prefill(ev[1], ev[2], want_slots=False)
+        elif ev[0] == "grow":
+            for _ in range(ev[2]):
+                eng.manager.append_slots_for_decode(list(ev[1]))
+        else:
+            eng.manager.free_sequence(ev[1])
+    eng.prefill_many(list(range(B)), list(range(B)), [int(L) - 1 for L in wl.context_lens],
+                     dev(np.concatenate(wl.hist_k)), dev(np.concatenate(wl.hist_v)))
+    tabs = eng.tables.cpu().numpy()
+    adj = sum(int(np.count_nonzero(np.diff(r[r >= 0]) == 1)) for r in tabs)
+    pairs = sum(max(int((r >= 0).sum()) - 1, 0) for r in tabs)
+    frag = adj / pairs if pairs else 0.0
+    del tabs
+
+    ring = [(dev(wl.new_k), dev(wl.new_v), dev(wl.q))]
+    for k, v, q in synth.extra_step_tensors(cfg, B, 7):
+        ring.append((dev(k), dev(v), dev(q)))
+    ids = np.arange(B, dtype=np.int64)
+    out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    elem = synth.ELEM_BYTES[cfg.dtype]
+    base = wl.context_lens.astype(np.int64)          # lengths after the first decode step
+
+    def kv_bytes(step):
+        return int((base + step).sum()) * cfg.num_kv_heads * 2 * cfg.head_dim * elem
+
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        k, v, q = ring[s % len(ring)]
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = args.warmup + i
+        k, v, q = ring[s % len(ring)]
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_bytes = np.array([kv_bytes(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
+    total_kv = float(step_bytes.sum())
+    value = total_kv / wall / 1e9
+    tokens_per_s = B * args.steps / wall
+    split_avg_s = float(split_ms.mean()) / 1e3
+    achieved = float(step_bytes.mean()) / split_avg_s / 1e9
+    attn_gbps = float(step_bytes.mean()) / (float((split_ms + merge_ms).mean()) / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {wall * 1e6 / args.steps:.1f} us/step, split kernel "
+        f"{split_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us, "
+        f"KV {step_bytes.mean() / 1e6:.1f} MB/step")
+
+    # attention only, with a 1 GiB read before each launch pair (cold caches;
+    # a read leaves no dirty lines behind to be written back during the launch)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    lens_dev = torch.from_numpy(eng.manager.context_lens(list(range(B)))).cuda()
+    maxlen = int(lens_dev.max().item())
+    cold_bytes = int(lens_dev.sum().item()) * cfg.num_kv_heads * 2 * cfg.head_dim * elem
+    q = ring[0][2]
+    cold = []
+    for _ in range(args.cold_iters):
+        flush.sum()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        eng.attend(q, lens_dev, cfg.scale, maxlen, out=out, events=e)
+        torch.cuda.synchronize()
+        cold.append((e[0].elapsed_time(e[1]), e[0].elapsed_time(e[2])))
+    cold = np.array(cold)
+    del flush
+
+    traffic, _ = recorded_traffic()
+    result = {
+        "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: one decode step (append, write, attention) of B={B} sequences, "
+                        f"H_q={cfg.num_q_heads} H_kv={cfg.num_kv_heads} D={cfg.head_dim} "
+                        f"{cfg.dtype} block_size={cfg.block_size}, pool {cfg.num_blocks} blocks",
+            "batch": B,
+            "context_lens": f"U[{cfg.len_range[0]}, {cfg.len_range[1]}]" if cfg.len_range else
+                            list(map(int, cfg.fixed_lens)),
+            "sum_context_first_step": int(base.sum()),
+            "partition_tokens": part if part else "library default",
+            "placement": cfg.placement,
+            "adjacent_logical_neighbours_fraction": round(frag, 4),
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(tokens_per_s, 1),
+        "attention_kv_gbps": round(attn_gbps, 2),
+        "attention_cold_us": {"partition_kernel": round(float(np.median(cold[:, 0])) * 1e3, 2),
+                              "partition_plus_merge": round(float(np.median(cold[:, 1])) * 1e3, 2),
+                              "kv_bytes": cold_bytes,
+                              "kv_gbps": round(cold_bytes / (float(np.median(cold[:, 1])) / 1e3) / 1e9, 2),
+                              "note": "1 GiB device read before each launch pair"},
+        "roofline": {
+            "kernel": f"attn_split_kernel<{cfg.dtype}, D={cfg.head_dim}, "
+                      f"G={cfg.num_q_heads // cfg.num_kv_heads}> (partition kernel)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "mean_launch_us": round(split_avg_s * 1e6, 3),
+            "algorithmic_bytes_per_launch": round(float(step_bytes.mean())),
+        },
+        "kernel_source_sha256_16": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -247,6 +247,30 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two launches of paged_decode_attention, callable separately with the
+ * same arguments (for instance to time or overlap them): _partial runs the
+ * partition kernel, which finishes every sequence that fits in one partition
+ * and leaves (max, sum, accumulator) partials in `workspace` for the others;
+ * _merge then reduces those partials into `out` (a no-op when no sequence
+ * spans two partitions).  The pair, in this order on one stream, equals one
+ * paged_decode_attention call.
+ */
+int paged_decode_attention_partial(void* out, int32_t out_dtype, const void* q,
+                                   const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len, float scale,
+                                   const pkv_cache_layout* layout, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
+                                 const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, int32_t block_table_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len, float scale,
+                                 const pkv_cache_layout* layout, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Apply the table growth of one batched append to a device-resident block
  * table: for every i with new_block[i] >= 0,
  *     block_tables[rows[i] * block_table_stride + (lens[i] - 1) / bs] = new_block[i]

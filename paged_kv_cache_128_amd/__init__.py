@@ -99,6 +99,12 @@ SIGNATURES = {
     "paged_decode_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               _F32, ctypes.POINTER(CacheLayout), _I32, _P, _SZ, _P]),
+    "paged_decode_attention_partial": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                                      _I32, _F32, ctypes.POINTER(CacheLayout), _I32,
+                                                      _P, _SZ, _P]),
+    "paged_decode_attention_merge": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
+                                                    _I32, _F32, ctypes.POINTER(CacheLayout), _I32,
+                                                    _P, _SZ, _P]),
     "pkv_update_block_tables": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _I32, _I32, _P]),
 }
 
@@ -329,10 +335,12 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
 
 def paged_decode_attention(q, key_cache, value_cache, block_tables, context_lens, scale: float,
                            out=None, out_dtype=None, partition_tokens: int = 0,
-                           max_context_len: Optional[int] = None, workspace=None, stream=None):
+                           max_context_len: Optional[int] = None, workspace=None, stream=None,
+                           phase: str = "both"):
     """Decode attention through block tables.  q [B, H_q, D]; block_tables
     int32 [B, W]; context_lens int32 [B].  Returns out [B, H_q, D] (float32
-    unless ``out_dtype`` / ``out`` says otherwise)."""
+    unless ``out_dtype`` / ``out`` says otherwise).  ``phase`` = "partial" or
+    "merge" runs one of the two launches (same arguments, same workspace)."""
     torch = _torch()
     lay = cache_layout(key_cache, value_cache)
     B, hq, d = q.shape
@@ -353,10 +361,14 @@ def paged_decode_attention(q, key_cache, value_cache, block_tables, context_lens
         raise ValueError("out must be contiguous [B, H_q, head_dim]")
     need = workspace_size(B, hq, lay.num_kv_heads, d, max_context_len, partition_tokens)
     if need > 0 and workspace is None:
+        if phase != "both":
+            raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = _lib_handle().paged_decode_attention(
+    fn = {"both": "paged_decode_attention", "partial": "paged_decode_attention_partial",
+          "merge": "paged_decode_attention_merge"}[phase]
+    st = getattr(_lib_handle(), fn)(
         out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key_cache.data_ptr(),
         value_cache.data_ptr(), block_tables.data_ptr(), block_tables.stride(0),
         context_lens.data_ptr(), B, hq, int(max_context_len), float(scale), ctypes.byref(lay),

@@ -49,10 +49,10 @@ constexpr float kSlack = 8.0f;     // allowed growth of exp2 arguments before a 
 constexpr int kTile = 16;          // tokens per tile == MFMA M dimension
 constexpr int kWave = 64;
 #ifndef PKV_SPLIT_WAVES_PER_SIMD
-#define PKV_SPLIT_WAVES_PER_SIMD 2
+#define PKV_SPLIT_WAVES_PER_SIMD 3
 #endif
-// Occupancy target of the split kernel (waves per SIMD).  The bf16 D = 128,
-// G = 7 instance needs about 180 VGPRs, which fits two waves without spills.
+// Occupancy target of the split kernel (waves per SIMD).  The 16-bit D = 128
+// instances fit three waves (<= 168 VGPRs) without spills; fp32 takes two.
 template <int DT>
 constexpr int split_waves_per_simd() { return DT == PKV_F32 ? 2 : PKV_SPLIT_WAVES_PER_SIMD; }
 
@@ -177,63 +177,128 @@ struct Frag {
   static constexpr int kDwK = D * kBytes / 4 / 4;        // dwords per lane
   static constexpr int kW = D / 16;                      // head-dim chunk per P.V lane
   static constexpr int kDwV = kW * kBytes / 4;           // dwords per token row chunk
+  // 16-bit, D = 128: K is fetched as whole 256-byte rows (like V) and
+  // regrouped into the MFMA operand layout through LDS; every load
+  // instruction then covers complete cache lines and can stream past the
+  // caches (non-temporal).
+  static constexpr bool kRowK = (DT != PKV_F32) && (D == 128);
 };
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ Dw<4> load_nt16(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  Dw<4> r;
+  r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+  return r;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void global_void;
+
+// V rows of one tile as the P.V lanes hold them: lane (g4, c16) has the
+// head-dim chunk c16 of tokens 4*g4 .. 4*g4+3.
 template <int DT, int D>
-struct Tile {
-  Dw<Frag<DT, D>::kDwK> k;
+struct VTile {
   Dw<Frag<DT, D>::kDwV> v[4];
 };
 
-// Loads one 16-token tile.  `base` is the element offset of token 0 of the
-// tile inside K (and V) for this KV head.  Rows of tokens >= nvalid (the
-// unused tail of the last block, which may hold anything) are not read:
-// those lanes re-read token 0 instead, so every value that enters the sums
-// is finite; their scores are masked to -inf afterwards.
+// K tile as the MFMA A operand (direct path): lane (g4, c16) has token c16.
 template <int DT, int D>
-__device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kc, const char* vc,
-                                          int64_t base, int nvalid, int lane) {
+struct KFrag {
+  Dw<Frag<DT, D>::kDwK> k;
+};
+
+// In every loader, rows of tokens >= nvalid (the unused tail of the last
+// block, which may hold anything) are not read: those lanes re-read token 0
+// instead, so every value that enters the sums is finite; their scores are
+// masked to -inf afterwards.
+
+template <int DT, int D>
+__device__ __forceinline__ void load_v(VTile<DT, D>& t, const char* vtile, int nvalid, int lane) {
   using F = Frag<DT, D>;
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int64_t kb = base * F::kBytes;
-  const int ktok = c16 < nvalid ? c16 : 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int tok = 4 * g4 + r < nvalid ? 4 * g4 + r : 0;
+    const char* src = vtile + (static_cast<int64_t>(tok) * D + c16 * F::kW) * F::kBytes;
+    if constexpr (F::kRowK) t.v[r] = load_nt16(src);
+    else t.v[r] = load_dw<F::kDwV>(src);
+  }
+}
+
+// Direct path: lane (g4, c16) loads its MFMA operand, token c16.
+template <int DT, int D>
+__device__ __forceinline__ void load_k_direct(KFrag<DT, D>& t, const char* ktile, int nvalid, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int tok = c16 < nvalid ? c16 : 0;
   if constexpr (DT == PKV_F32) {
-    // token ktok, floats d = 16 j + 4 g4 .. +3 for j = 0 .. D/16-1
+    // floats d = 16 j + 4 g4 .. +3 for j = 0 .. D/16-1
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) {
-      Dw<4> x = load_dw<4>(kc + kb + (static_cast<int64_t>(ktok) * D + 16 * j + 4 * g4) * 4);
+      Dw<4> x = load_dw<4>(ktile + (static_cast<int64_t>(tok) * D + 16 * j + 4 * g4) * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) t.k.w[4 * j + e] = x.w[e];
     }
   } else {
-    // token ktok, halves d = 32 kk + 8 g4 .. +7 for kk = 0 .. D/32-1
+    // halves d = 32 kk + 8 g4 .. +7 for kk = 0 .. D/32-1
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      Dw<4> x = load_dw<4>(kc + kb + (static_cast<int64_t>(ktok) * D + 32 * kk + 8 * g4) * 2);
+      Dw<4> x = load_dw<4>(ktile + (static_cast<int64_t>(tok) * D + 32 * kk + 8 * g4) * 2);
 #pragma unroll
       for (int e = 0; e < 4; ++e) t.k.w[4 * kk + e] = x.w[e];
     }
   }
+}
+
+// Row path (16-bit, D = 128): the K tile (16 rows of 256 bytes) goes from
+// HBM straight into LDS with four global_load_lds_dwordx4, each filling one
+// KiB: lane l of instruction rr writes slot (l % 16) of row 4 rr + l / 16.
+// The lane fetches chunk (slot ^ row) of that row, so chunk c of row r sits
+// at slot c ^ r; each instruction still reads four whole rows from HBM.
+template <int DT, int D>
+__device__ __forceinline__ void issue_k_rows(const char* ktile, uint4* sk, int nvalid, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int vtok = 4 * g4 + r < nvalid ? 4 * g4 + r : 0;
-    t.v[r] = load_dw<F::kDwV>(vc + kb + (static_cast<int64_t>(vtok) * D + c16 * F::kW) * F::kBytes);
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = 4 * rr + g4;
+    const int src_row = row < nvalid ? row : 0;
+    const char* src = ktile + static_cast<int64_t>(src_row) * D * 2 + ((c16 ^ row) * 16);
+    __builtin_amdgcn_global_load_lds((global_void*)(src),
+                                     (lds_void*)(sk + rr * 64), 16, 0, 0);
   }
 }
 
-// S^T[token 4*g4 + r][head c16] for the lane's 4 tokens.
+// Reads the staged K rows back in the MFMA operand layout: lane (g4, c16)
+// takes chunk 4 kk + g4 (head-dims 32 kk + 8 g4 ..) of row c16.  The 16
+// lanes of a group hit 16 different slots, so no two share an LDS bank.
 template <int DT, int D>
-__device__ __forceinline__ f32x4 qk_tile(const Tile<DT, D>& t, const Dw<Frag<DT, D>::kDwK>& qf) {
+__device__ __forceinline__ Dw<Frag<DT, D>::kDwK> read_k_rows(const uint4* sk, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  Dw<Frag<DT, D>::kDwK> r;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const uint4 x = sk[c16 * 16 + ((4 * kk + g4) ^ c16)];
+    r.w[4 * kk] = x.x; r.w[4 * kk + 1] = x.y; r.w[4 * kk + 2] = x.z; r.w[4 * kk + 3] = x.w;
+  }
+  return r;
+}
+
+// S^T[token 4*g4 + r][head c16] for the lane's 4 tokens from the K operand
+// and the query group operand (same head-dim map).
+template <int DT, int D>
+__device__ __forceinline__ f32x4 qk_mfma(const Dw<Frag<DT, D>::kDwK>& kf,
+                                         const Dw<Frag<DT, D>::kDwK>& qf) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if constexpr (DT == PKV_F32) {
 #pragma unroll
     for (int i = 0; i < D / 4; ++i)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(t.k.w[i]),
-                                                 __uint_as_float(qf.w[i]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf.w[i]), __uint_as_float(qf.w[i]),
+                                                 acc, 0, 0, 0);
   } else {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      uint4 a4 = make_uint4(t.k.w[4 * kk], t.k.w[4 * kk + 1], t.k.w[4 * kk + 2], t.k.w[4 * kk + 3]);
+      uint4 a4 = make_uint4(kf.w[4 * kk], kf.w[4 * kk + 1], kf.w[4 * kk + 2], kf.w[4 * kk + 3]);
       uint4 b4 = make_uint4(qf.w[4 * kk], qf.w[4 * kk + 1], qf.w[4 * kk + 2], qf.w[4 * kk + 3]);
       if constexpr (DT == PKV_BF16)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a4),
@@ -262,17 +327,17 @@ __device__ __forceinline__ void for_each_head(F&& f) {
   for_each_head_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// One tile of online softmax + P.V.  Tokens >= nvalid of the tile get score
-// -inf, hence probability 0 (their K/V rows were replaced by token 0's).  The probability of (head h, token 4*g4+r)
+// Online softmax + P.V for one tile whose scores are `s`.  Tokens >= nvalid
+// of the tile get score -inf, hence probability 0 (their K/V rows were
+// replaced by token 0's).  The probability of (head h, token 4*g4+r)
 // sits in lane 16*g4 + h; the P.V lanes of row g4 pick it up with a DPP row
 // broadcast, so the loop needs neither LDS nor barriers.
 template <int DT, int D, int GP>
-__device__ __forceinline__ void consume_tile(const Tile<DT, D>& t, const Dw<Frag<DT, D>::kDwK>& qf,
-                                             int nvalid, float scale_log2, float& m, float& l,
-                                             float (&acc)[GP][Frag<DT, D>::kW], int lane) {
+__device__ __forceinline__ void softmax_pv(const f32x4 s, const VTile<DT, D>& t, int nvalid,
+                                           float scale_log2, float& m, float& l,
+                                           float (&acc)[GP][Frag<DT, D>::kW], int lane) {
   using F = Frag<DT, D>;
   const int g4 = lane >> 4;
-  f32x4 s = qk_tile<DT, D>(t, qf);
   float x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -343,10 +408,14 @@ attn_split_kernel(AttnArgs a) {
     }
     return;
   }
+  // The sequence's ceil(L / part_tokens) partitions split its 16-token tiles
+  // evenly (they differ by at most one tile), so partitions of one launch
+  // carry nearly equal work.
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
   if (p >= nparts) return;
-  const int t0 = p * a.part_tokens;
-  const int t1 = min(L, t0 + a.part_tokens);
+  const int ntiles_seq = (L + kTile - 1) / kTile;
+  const int t0 = kTile * static_cast<int>((static_cast<int64_t>(p) * ntiles_seq) / nparts);
+  const int t1 = min(L, kTile * static_cast<int>((static_cast<int64_t>(p + 1) * ntiles_seq) / nparts));
 
   // query group as the MFMA B operand: head c16, same head-dim map as K
   Dw<F::kDwK> qf;
@@ -376,31 +445,27 @@ attn_split_kernel(AttnArgs a) {
 
   const int bs = a.block_size;
   const int32_t* trow = a.tables + static_cast<int64_t>(b) * a.table_stride;
-  const int nblk = (L + bs - 1) / bs;   // table entries that may be read
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
   const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
 
-  // Block-table slice cached in one VGPR (64 entries), read back per tile
-  // with v_readlane.
-  int tbl_base = (t0 / bs) & ~63;
-  int tbl = 0;
-  {
-    const int j = tbl_base + lane;
-    tbl = j < nblk ? trow[j] : 0;
-  }
+  // The partition's slice of the block table is staged in LDS once, so the
+  // tile loop reads it with LDS loads (counted apart from the K/V loads and
+  // never forcing them to drain).
+  extern __shared__ int32_t sh_tbl[];
+  __shared__ uint4 sk_buf[F::kRowK ? 256 : 1];
+  uint4* sk = sk_buf;
+  const int lb0 = t0 / bs;
+  const int lb1 = (t1 - 1) / bs;
+  for (int j = lane; j <= lb1 - lb0; j += kWave) sh_tbl[j] = trow[lb0 + j];
+  __syncthreads();
   // Element offset of tile i.  A table entry outside [0, num_blocks) is
   // clamped into the pool: the kernel never leaves the pool, and the result
   // for such a (caller-broken) table is unspecified.
   auto tile_addr = [&](int i) -> int64_t {
     const int tok = t0 + i * kTile;
     const int lb = tok / bs;
-    if (lb >= tbl_base + 64) {
-      tbl_base = lb & ~63;
-      const int j = tbl_base + lane;
-      tbl = j < nblk ? trow[j] : 0;
-    }
-    int pb = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
+    int pb = __builtin_amdgcn_readfirstlane(sh_tbl[lb - lb0]);
     pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
     const int off = tok - lb * bs;
     return static_cast<int64_t>(pb) * a.block_stride + head_off + static_cast<int64_t>(off) * D;
@@ -414,18 +479,68 @@ attn_split_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
 
-  // Two register stages: tile i+1 is in flight while tile i is consumed.
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+  const int last = ntiles - 1;
   auto nvalid_of = [&](int i) { return min(kTile, t1 - t0 - i * kTile); };
-  Tile<DT, D> ta, tb;
-  load_tile<DT, D>(ta, kc, vc, tile_addr(0), nvalid_of(0), lane);
-  for (int i = 0; i < ntiles; i += 2) {
-    const bool has_b = i + 1 < ntiles;
-    if (has_b) load_tile<DT, D>(tb, kc, vc, tile_addr(i + 1), nvalid_of(i + 1), lane);
-    consume_tile<DT, D, GP>(ta, qf, nvalid_of(i), a.scale_log2, m, l, acc, lane);
-    if (has_b) {
-      if (i + 2 < ntiles) load_tile<DT, D>(ta, kc, vc, tile_addr(i + 2), nvalid_of(i + 2), lane);
-      consume_tile<DT, D, GP>(tb, qf, nvalid_of(i + 1), a.scale_log2, m, l, acc, lane);
+  // Loads past the last tile are issued with the index clamped (re-reading
+  // the tile just fetched, which the caches hold), so the loop has no
+  // conditional loads and the waits stay exact.
+  if constexpr (F::kRowK) {
+    // Tile i+1 (K into LDS, V into registers) is fetched while tile i's
+    // softmax and P.V run; the K operand of tile i is read out of LDS first.
+    VTile<DT, D> va, vb;
+    {
+      const int64_t e0 = tile_addr(0) * F::kBytes;
+      issue_k_rows<DT, D>(kc + e0, sk, nvalid_of(0), lane);
+      load_v<DT, D>(va, vc + e0, nvalid_of(0), lane);
+    }
+    for (int i = 0; i < ntiles; i += 2) {
+      const int ib = min(i + 1, last);
+      const int ia = min(i + 2, last);
+      f32x4 sc = qk_mfma<DT, D>(read_k_rows<DT, D>(sk, lane), qf);
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of tile i done before it is refilled
+      {
+        const int64_t eb = tile_addr(ib) * F::kBytes;
+        issue_k_rows<DT, D>(kc + eb, sk, nvalid_of(ib), lane);
+        load_v<DT, D>(vb, vc + eb, nvalid_of(ib), lane);
+      }
+      softmax_pv<DT, D, GP>(sc, va, nvalid_of(i), a.scale_log2, m, l, acc, lane);
+      if (i + 1 < ntiles) {
+        sc = qk_mfma<DT, D>(read_k_rows<DT, D>(sk, lane), qf);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        const int64_t ea = tile_addr(ia) * F::kBytes;
+        issue_k_rows<DT, D>(kc + ea, sk, nvalid_of(ia), lane);
+        load_v<DT, D>(va, vc + ea, nvalid_of(ia), lane);
+        softmax_pv<DT, D, GP>(sc, vb, nvalid_of(i + 1), a.scale_log2, m, l, acc, lane);
+      }
+    }
+  } else {
+    // Direct path: two register stages, tile i+1 in flight while tile i is
+    // consumed.
+    KFrag<DT, D> ka, kb;
+    VTile<DT, D> va, vb;
+    {
+      const int64_t e0 = tile_addr(0) * F::kBytes;
+      load_k_direct<DT, D>(ka, kc + e0, nvalid_of(0), lane);
+      load_v<DT, D>(va, vc + e0, nvalid_of(0), lane);
+    }
+    for (int i = 0; i < ntiles; i += 2) {
+      const int ib = min(i + 1, last);
+      const int ia = min(i + 2, last);
+      {
+        const int64_t eb = tile_addr(ib) * F::kBytes;
+        load_k_direct<DT, D>(kb, kc + eb, nvalid_of(ib), lane);
+        load_v<DT, D>(vb, vc + eb, nvalid_of(ib), lane);
+      }
+      softmax_pv<DT, D, GP>(qk_mfma<DT, D>(ka.k, qf), va, nvalid_of(i), a.scale_log2, m, l, acc, lane);
+      {
+        const int64_t ea = tile_addr(ia) * F::kBytes;
+        load_k_direct<DT, D>(ka, kc + ea, nvalid_of(ia), lane);
+        load_v<DT, D>(va, vc + ea, nvalid_of(ia), lane);
+      }
+      if (i + 1 < ntiles)
+        softmax_pv<DT, D, GP>(qk_mfma<DT, D>(kb.k, qf), vb, nvalid_of(i + 1), a.scale_log2, m, l,
+                              acc, lane);
     }
   }
 
@@ -532,9 +647,16 @@ int padded_group(int g) {
   return 8;
 }
 
+// Dynamic LDS of the partition kernel: the block-table entries one
+// partition can touch.
+size_t table_lds_bytes(int part_tokens, int block_size) {
+  return static_cast<size_t>((part_tokens + kTile) / block_size + 2) * sizeof(int32_t);
+}
+
 template <int DT, int D, int GP>
 hipError_t launch_split_t(const AttnArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_split_kernel<DT, D, GP>), grid, dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL((attn_split_kernel<DT, D, GP>), grid, dim3(kWave),
+                     table_lds_bytes(a.part_tokens, a.block_size), s, a);
   return hipGetLastError();
 }
 
@@ -642,12 +764,22 @@ size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_hea
   return static_cast<size_t>(num_seqs) * num_q_heads * P * (head_dim + 2) * sizeof(float);
 }
 
-int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const void* key_cache,
-                           const void* value_cache, const int32_t* block_tables,
-                           int32_t block_table_stride, const int32_t* context_lens,
-                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
-                           float scale, const pkv_cache_layout* l, int32_t partition_tokens,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kPhasePartial = 1;
+constexpr int kPhaseMerge = 2;
+
+// Validates the arguments, then launches the partition kernel (phase 1)
+// and/or the split-K merge kernel (phase 2, only when some sequence spans
+// more than one partition).
+int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, const void* key_cache,
+                   const void* value_cache, const int32_t* block_tables,
+                   int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_context_len, float scale,
+                   const pkv_cache_layout* l, int32_t partition_tokens, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (pkv::check_layout(l) != PKV_OK) return PKV_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || block_table_stride < 0 ||
       partition_tokens < 0)
@@ -663,6 +795,7 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const vo
   if (l->block_size % kTile != 0) return PKV_ERR_UNSUPPORTED;
   const int part = pick_partition(partition_tokens);
   if (part % kTile != 0) return PKV_ERR_INVALID;
+  if (table_lds_bytes(part, l->block_size) > 32768) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !key_cache || !value_cache || !context_lens ||
       (max_context_len > 0 && !block_tables))
@@ -705,22 +838,64 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const vo
   a.scale_log2 = scale * kLog2e;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<uint32_t>(wgs));
-  const int gp = padded_group(group);
-  hipError_t e;
-  switch (l->dtype) {
-    case PKV_BF16: e = launch_split_dt<PKV_BF16>(a, l->head_dim, gp, grid, s); break;
-    case PKV_F16: e = launch_split_dt<PKV_F16>(a, l->head_dim, gp, grid, s); break;
-    default: e = launch_split_dt<PKV_F32>(a, l->head_dim, gp, grid, s); break;
+  if (phases & kPhasePartial) {
+    const dim3 grid(static_cast<uint32_t>(wgs));
+    const int gp = padded_group(group);
+    hipError_t e;
+    switch (l->dtype) {
+      case PKV_BF16: e = launch_split_dt<PKV_BF16>(a, l->head_dim, gp, grid, s); break;
+      case PKV_F16: e = launch_split_dt<PKV_F16>(a, l->head_dim, gp, grid, s); break;
+      default: e = launch_split_dt<PKV_F32>(a, l->head_dim, gp, grid, s); break;
+    }
+    if (e != hipSuccess) return PKV_ERR_HIP;
   }
-  if (e != hipSuccess) return PKV_ERR_HIP;
-  if (P > 1) {
+  if ((phases & kPhaseMerge) && P > 1) {
     const dim3 rgrid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
     if (l->head_dim == 64) hipLaunchKernelGGL(attn_reduce_kernel<64>, rgrid, dim3(kWave), 0, s, a);
     else hipLaunchKernelGGL(attn_reduce_kernel<128>, rgrid, dim3(kWave), 0, s, a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int32_t block_table_stride, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                           float scale, const pkv_cache_layout* l, int32_t partition_tokens,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(kPhasePartial | kPhaseMerge, out, out_dtype, q, key_cache, value_cache,
+                        block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
+                        max_context_len, scale, l, partition_tokens, workspace, workspace_bytes,
+                        stream);
+}
+
+int paged_decode_attention_partial(void* out, int32_t out_dtype, const void* q,
+                                   const void* key_cache, const void* value_cache,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len, float scale,
+                                   const pkv_cache_layout* l, int32_t partition_tokens,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(kPhasePartial, out, out_dtype, q, key_cache, value_cache, block_tables,
+                        block_table_stride, context_lens, num_seqs, num_q_heads, max_context_len,
+                        scale, l, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
+                                 const void* key_cache, const void* value_cache,
+                                 const int32_t* block_tables, int32_t block_table_stride,
+                                 const int32_t* context_lens, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len, float scale,
+                                 const pkv_cache_layout* l, int32_t partition_tokens,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return attention_impl(kPhaseMerge, out, out_dtype, q, key_cache, value_cache, block_tables,
+                        block_table_stride, context_lens, num_seqs, num_q_heads, max_context_len,
+                        scale, l, partition_tokens, workspace, workspace_bytes, stream);
 }
 
 int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,

@@ -149,18 +149,37 @@ class PagedKVEngine:
 
     def decode_step(self, seq_ids: np.ndarray, new_k: torch.Tensor, new_v: torch.Tensor,
                     q: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
         """One decode step for rows 0..n-1 holding ``seq_ids`` (int64).
         ``max_context_len`` defaults to the longest length after the append
-        (known on the host from the manager, no device sync)."""
+        (known on the host from the manager, no device sync).  ``events``
+        (three torch.cuda.Event) are recorded before the attention partition
+        kernel, between it and the split-K merge, and after the merge."""
         n = len(seq_ids)
         st = self.append(seq_ids)
         if max_context_len is None:
             max_context_len = int(st.lens[:n].max()) if n else 0
         update_block_tables(self.tables, st.d_lens[:n], st.d_newb[:n], self.block_size)
         paged_kv_write(new_k, new_v, st.d_slots[:n], self.key_cache, self.value_cache)
+        return self.attend(q, st.d_lens[:n], scale, max_context_len, out=out, events=events)
+
+    def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
+               out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
+        """Attention of rows 0..B-1 over the current cache (no append/write)."""
+        n = q.shape[0]
         ws = self.workspace(n, q.shape[1], max_context_len)
-        return paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n],
-                                      st.d_lens[:n], scale, out=out,
-                                      partition_tokens=self.partition_tokens,
-                                      max_context_len=max_context_len, workspace=ws)
+        kw = dict(partition_tokens=self.partition_tokens, max_context_len=max_context_len,
+                  workspace=ws)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        if events is None:
+            return paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n],
+                                          lens, scale, out=out, **kw)
+        events[0].record()
+        paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], lens, scale,
+                               out=out, phase="partial", **kw)
+        events[1].record()
+        paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], lens, scale,
+                               out=out, phase="merge", **kw)
+        events[2].record()
+        return out
