@@ -384,6 +384,63 @@ __device__ __forceinline__ void softmax_pv(const f32x4 s, const VTile<DT, D>& t,
   }
 }
 
+// End of a wave's run over one (sequence, KV head) segment: sums the four
+// token groups' (l, acc), then for each of the G query heads writes either
+// the normalised output row (`final`) or the raw (m, l, acc) partial to
+// workspace slot ws_row0 + h * ws_row_stride.  Lane group g4 writes heads
+// g4, g4 + 4, ...; lane c16 writes head-dim chunk c16.
+template <int DT, int D, int GP>
+__device__ __forceinline__ void wave_epilogue(float m, float l, float (&acc)[GP][Frag<DT, D>::kW],
+                                              int lane, int G, bool final, void* out, int out_dtype,
+                                              int64_t out_row0, float* ws_acc, float* ws_ml,
+                                              int64_t ws_row0, int64_t ws_row_stride) {
+  using F = Frag<DT, D>;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < F::kW; ++e) {
+      float v = acc[h][e];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[h][e] = v;
+    }
+  for_each_head<GP>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    const float lh = row_bcast<h>(l);
+    const float mh = row_bcast<h>(m);
+    if ((h & 3) != g4 || h >= G) return;
+    if (final) {
+      const int64_t row = out_row0 + h;
+      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
+      if (out_dtype == PKV_F32) {
+        float* o = static_cast<float*>(out) + row * D + c16 * F::kW;
+#pragma unroll
+        for (int e = 0; e < F::kW; ++e) o[e] = acc[h][e] * inv;
+      } else {
+        uint16_t* o = static_cast<uint16_t*>(out) + row * D + c16 * F::kW;
+#pragma unroll
+        for (int e = 0; e < F::kW; ++e) {
+          const float y = acc[h][e] * inv;
+          o[e] = (out_dtype == PKV_BF16) ? f32_to_bf16_rne(y)
+                                         : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
+        }
+      }
+    } else {
+      const int64_t slot = ws_row0 + h * ws_row_stride;
+      float* w = ws_acc + slot * D + c16 * F::kW;
+#pragma unroll
+      for (int e = 0; e < F::kW; ++e) w[e] = acc[h][e];
+      if (c16 == 0) {
+        ws_ml[2 * slot + 0] = mh;
+        ws_ml[2 * slot + 1] = lh;
+      }
+    }
+  });
+}
+
 template <int DT, int D, int GP>
 __global__ void __launch_bounds__(kWave, split_waves_per_simd<DT>())
 attn_split_kernel(AttnArgs a) {
@@ -514,6 +571,8 @@ attn_split_kernel(AttnArgs a) {
         softmax_pv<DT, D, GP>(sc, vb, nvalid_of(i + 1), a.scale_log2, m, l, acc, lane);
       }
     }
+    // the last (clamped) K fetch into LDS must land before the wave can exit
+    __builtin_amdgcn_s_waitcnt(0);
   } else {
     // Direct path: two register stages, tile i+1 in flight while tile i is
     // consumed.
@@ -544,51 +603,8 @@ attn_split_kernel(AttnArgs a) {
     }
   }
 
-  // reduce the four token groups
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < F::kW; ++e) {
-      float v = acc[h][e];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[h][e] = v;
-    }
-  // lane group g4 writes heads g4, g4 + 4, ...; lane c16 writes chunk c16
-  for_each_head<GP>([&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const float lh = row_bcast<h>(l);
-    const float mh = row_bcast<h>(m);
-    if ((h & 3) != g4 || h >= G) return;
-    const int64_t row = out_row0 + h;
-    if (nparts == 1) {
-      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
-      if (a.out_dtype == PKV_F32) {
-        float* o = static_cast<float*>(a.out) + row * D + c16 * F::kW;
-#pragma unroll
-        for (int e = 0; e < F::kW; ++e) o[e] = acc[h][e] * inv;
-      } else {
-        uint16_t* o = static_cast<uint16_t*>(a.out) + row * D + c16 * F::kW;
-#pragma unroll
-        for (int e = 0; e < F::kW; ++e) {
-          const float y = acc[h][e] * inv;
-          o[e] = (a.out_dtype == PKV_BF16) ? f32_to_bf16_rne(y)
-                                           : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
-        }
-      }
-    } else {
-      const int64_t slot = row * a.max_parts + p;
-      float* w = a.ws_acc + slot * D + c16 * F::kW;
-#pragma unroll
-      for (int e = 0; e < F::kW; ++e) w[e] = acc[h][e];
-      if (c16 == 0) {
-        a.ws_ml[2 * slot + 0] = mh;
-        a.ws_ml[2 * slot + 1] = lh;
-      }
-    }
-  });
+  wave_epilogue<DT, D, GP>(m, l, acc, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc,
+                           a.ws_ml, out_row0 * a.max_parts + p, a.max_parts);
 }
 
 // Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with
@@ -631,8 +647,356 @@ attn_reduce_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------ stream-K attention
+// One workgroup per contiguous range of the launch's 16-token tiles, with
+// the tiles of all sequences laid end to end (sequence b owns tiles
+// [S_b, S_b + T_b), T_b = ceil(L_b / 16)).  Workgroup w takes tiles
+// [w*T/W, (w+1)*T/W) and runs one wave per KV head, so it streams every
+// physical block of its range as one contiguous region (K half then V half
+// of the block), and all workgroups carry the same number of tiles whatever
+// the mix of context lengths.  A sequence cut by a range boundary leaves a
+// (max, sum, accumulator) partial per piece in the workspace; the merge
+// kernel combines the pieces.  16-bit KV, D = 128, H_kv <= 8, G <= 8.
+struct StreamArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* ws_ml;      // [W, 2, H_q, 2]
+  float* ws_acc;     // [W, 2, H_q, D]
+  void* out;
+  int64_t block_stride;
+  int64_t head_stride;
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_seqs;
+  int32_t hq;
+  int32_t hkv;
+  int32_t group;
+  int32_t max_len;
+  int32_t out_dtype;
+  int32_t range_cap;     // table entries one workgroup may stage
+  int32_t num_wgs;       // W, workgroups of the stream kernel
+  float scale_log2;
+};
+
+constexpr int kStreamMaxHeads = 8;
+
+__device__ __forceinline__ int clamp_len(int L, int max_len) {
+  return L < 0 ? 0 : (L > max_len ? max_len : L);
+}
+
+// Largest b in [0, B) with S[b] <= g (S non-decreasing, S[0] = 0 <= g < S[B]);
+// that b has T_b > 0 and owns tile g.
+__device__ __forceinline__ int seq_of_tile(const int32_t* S, int B, int g) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S[mid] <= g) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Exclusive prefix sums of T_b into S[0..B] by one wave.
+__device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_len, int32_t* S,
+                                            int lane) {
+  const int per = (B + kWave - 1) / kWave;
+  const int b0 = min(B, lane * per), b1 = min(B, b0 + per);
+  int part = 0;
+  for (int b = b0; b < b1; ++b) part += (clamp_len(lens[b], max_len) + kTile - 1) / kTile;
+  int incl = part;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int run = incl - part;
+  for (int b = b0; b < b1; ++b) {
+    S[b] = run;
+    run += (clamp_len(lens[b], max_len) + kTile - 1) / kTile;
+  }
+  if (lane == kWave - 1) S[B] = incl;
+}
+
+template <int DT, int GP>
+__global__ void __launch_bounds__(kWave * kStreamMaxHeads, 2)
+attn_stream_kernel(StreamArgs a) {
+  constexpr int D = 128;
+  using F = Frag<DT, D>;
+  static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
+  extern __shared__ int32_t sh_stream[];
+  __shared__ uint4 sk_all[kStreamMaxHeads][256];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int B = a.num_seqs;
+  int32_t* S = sh_stream;              // [B + 1]
+  int32_t* tbl = sh_stream + B + 1;    // [range_cap]
+  if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, lane);
+  __syncthreads();
+  const int T = S[B];
+  const int W = gridDim.x;
+  const int g0 = static_cast<int>((static_cast<int64_t>(blockIdx.x) * T) / W);
+  const int g1 = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * T) / W);
+  if (g0 >= g1) return;                // whole workgroup: empty range
+  const int bs = a.block_size;
+  for (int t = threadIdx.x; t < g1 - g0; t += blockDim.x) {
+    const int g = g0 + t;
+    const int b = seq_of_tile(S, B, g);
+    const int lb = ((g - S[b]) * kTile) / bs;
+    int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
+    tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+  }
+  __syncthreads();
+
+  const int kvh = wave;
+  const int G = a.group;
+  uint4* sk = sk_all[wave];
+  const char* kc = static_cast<const char*>(a.kc);
+  const char* vc = static_cast<const char*>(a.vc);
+  const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
+  // element offset of tile g (inside the workgroup's range)
+  auto tile_elem = [&](int g, int b_of_g) -> int64_t {
+    const int ti = g - S[b_of_g];
+    const int off = (ti * kTile) % bs;
+    return static_cast<int64_t>(tbl[g - g0]) * a.block_stride + head_off +
+           static_cast<int64_t>(off) * D;
+  };
+  auto load_q = [&](Dw<F::kDwK>& qf, int b) {
+    const int head = c16 < G ? c16 : 0;
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(kvh) * G + head) * D) * 2;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      Dw<4> x = load_dw<4>(qrow + (32 * kk + 8 * g4) * 2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qf.w[4 * kk + e] = (c16 < G) ? x.w[e] : 0u;
+    }
+  };
+
+  // consume cursor (sequence of the tile being computed)
+  int bc = seq_of_tile(S, B, g0);
+  int sc0 = S[bc], sc1 = S[bc + 1];          // tile range of sequence bc
+  int Lc = clamp_len(a.lens[bc], a.max_len);
+  int seg0 = g0;                              // first tile of the current segment
+  // prefetch cursor (sequence of the next tile to load)
+  int bn = bc, sn0 = sc0, sn1 = sc1, Ln = Lc;
+  Dw<F::kDwK> qf;
+  load_q(qf, bc);
+  float m = -INFINITY, l = 0.f;
+  float acc[GP][F::kW];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+
+  auto nvalid_at = [&](int g, int s0, int L) { return min(kTile, L - kTile * (g - s0)); };
+  VTile<DT, D> vcur, vnext;
+  {
+    const int64_t e0 = tile_elem(g0, bc) * 2;
+    const int nv = nvalid_at(g0, sc0, Lc);
+    issue_k_rows<DT, D>(kc + e0, sk, nv, lane);
+    load_v<DT, D>(vcur, vc + e0, nv, lane);
+  }
+  // Per tile g: scores from the K rows in LDS; then the fetch of tile g + 1
+  // (clamped to the range) and, when g + 1 opens the next sequence, that
+  // sequence's query group straight into qf (the scores of g no longer
+  // need it); then softmax + P.V of g; then the segment end if g closes one.
+  for (int g = g0; g < g1; ++g) {
+    const f32x4 scr = qk_mfma<DT, D>(read_k_rows<DT, D>(sk, lane), qf);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of tile g done before it is refilled
+    const int gn = min(g + 1, g1 - 1);
+    if (gn >= sn1) {
+      bn = seq_of_tile(S, B, gn);
+      sn0 = S[bn];
+      sn1 = S[bn + 1];
+      Ln = clamp_len(a.lens[bn], a.max_len);
+      load_q(qf, bn);
+    }
+    {
+      const int64_t en = tile_elem(gn, bn) * 2;
+      const int nv = nvalid_at(gn, sn0, Ln);
+      issue_k_rows<DT, D>(kc + en, sk, nv, lane);
+      load_v<DT, D>(vnext, vc + en, nv, lane);
+    }
+    softmax_pv<DT, D, GP>(scr, vcur, nvalid_at(g, sc0, Lc), a.scale_log2, m, l, acc, lane);
+    vcur = vnext;
+    if (g == g1 - 1 || g == sc1 - 1) {
+      const bool complete = (seg0 == sc0) && (g == sc1 - 1);
+      const int slot = (seg0 == g0) ? 0 : 1;
+      wave_epilogue<DT, D, GP>(m, l, acc, lane, G, complete, a.out, a.out_dtype,
+                               static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G,
+                               a.ws_acc, a.ws_ml,
+                               (static_cast<int64_t>(blockIdx.x) * 2 + slot) * a.hq +
+                                   static_cast<int64_t>(kvh) * G,
+                               1);
+      bc = bn;
+      sc0 = sn0;
+      sc1 = sn1;
+      Lc = Ln;
+      seg0 = g + 1;
+      m = -INFINITY;
+      l = 0.f;
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+    }
+  }
+  // the last (clamped) K fetch into LDS must land before the wave can exit
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Merge of the stream kernel's partials.  One 64-lane workgroup per
+// (sequence, query head).  A sequence with L = 0 gets zeros; one that a
+// single workgroup covered was finished already; otherwise its pieces are
+// combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// The pieces of sequence b are the non-empty ranges over its tiles: with at
+// least as many tiles as workgroups every range is non-empty and the pieces
+// are the consecutive workgroups w_first .. w_last; with fewer tiles each
+// non-empty range holds exactly one tile and piece j is the owner of tile
+// S_b + j.
+template <int D>
+__global__ void __launch_bounds__(kWave)
+attn_stream_merge_kernel(StreamArgs a) {
+  const int lane = threadIdx.x;
+  const int qh = blockIdx.x % a.hq;
+  const int b = blockIdx.x / a.hq;
+  const int W = a.num_wgs;
+  int before = 0, total = 0;
+  for (int j = lane; j < a.num_seqs; j += kWave) {
+    const int t = (clamp_len(a.lens[j], a.max_len) + kTile - 1) / kTile;
+    total += t;
+    if (j < b) before += t;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    before += __shfl_xor(before, o);
+    total += __shfl_xor(total, o);
+  }
+  const int L = clamp_len(a.lens[b], a.max_len);
+  const int64_t orow = (static_cast<int64_t>(b) * a.hq + qh) * D;
+  constexpr int kPer = D / kWave;
+  if (L == 0) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int64_t o = orow + lane * kPer + e;
+      if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = 0.f;
+      else static_cast<uint16_t*>(a.out)[o] = 0;
+    }
+    return;
+  }
+  const int Tb = (L + kTile - 1) / kTile;
+  auto owner = [&](int g) {
+    return static_cast<int>((static_cast<int64_t>(g + 1) * W - 1) / total);
+  };
+  const int w_first = owner(before);
+  const int w_last = owner(before + Tb - 1);
+  if (w_first == w_last) return;
+  const bool dense = total >= W;
+  const int npieces = dense ? (w_last - w_first + 1) : Tb;
+  const int g0_first = static_cast<int>((static_cast<int64_t>(w_first) * total) / W);
+  const int first_slot = (g0_first < before) ? 1 : 0;
+  auto slot_of = [&](int j) -> int64_t {
+    const int w = dense ? (w_first + j) : owner(before + j);
+    return (static_cast<int64_t>(w) * 2 + (j == 0 ? first_slot : 0)) * a.hq + qh;
+  };
+  // Pieces in chunks of 8: every lane loads each piece's (m, l) and its own
+  // accumulator slice, all loads of a chunk in flight together, then folds
+  // the chunk into a running (M, den, num) with one rescale.
+  constexpr int kChunk = 8;
+  float M = -INFINITY, den = 0.f;
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  for (int j0 = 0; j0 < npieces; j0 += kChunk) {
+    float mp[kChunk], lp[kChunk], v[kChunk][kPer];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int j = min(j0 + u, npieces - 1);
+      const int64_t sl = slot_of(j);
+      const float2 ml2 = *reinterpret_cast<const float2*>(a.ws_ml + 2 * sl);
+      mp[u] = (j0 + u < npieces) ? ml2.x : -INFINITY;
+      lp[u] = ml2.y;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) v[u][e] = a.ws_acc[sl * D + lane * kPer + e];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) Mc = fmaxf(Mc, mp[u]);
+    const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] *= r;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float wt = (mp[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp[u] - Mc);
+      den = fmaf(wt, lp[u], den);
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) num[e] = fmaf(wt, v[u][e], num[e]);
+    }
+    M = Mc;
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int64_t o = orow + lane * kPer + e;
+    const float y = num[e] * inv;
+    if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = y;
+    else if (a.out_dtype == PKV_BF16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(y);
+    else static_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
+  }
+}
+
 // ------------------------------------------------------------ dispatch
 constexpr int kDefaultPartition = 512;
+constexpr int kStreamWavesPerCu = 8;      // stream kernel: resident waves per CU aimed at
+constexpr size_t kStreamDynLdsMax = 32768;
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+// Launch plan of the stream kernel, or ok = false when the shape is not one
+// it covers (the partition kernel then runs with the default partition).
+struct StreamPlan {
+  bool ok = false;
+  int wgs = 0;
+  int range_cap = 0;
+  size_t dyn_lds = 0;
+  size_t workspace = 0;
+};
+
+StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t max_context_len, int dtype_or_neg) {
+  StreamPlan pl;
+  if (head_dim != 128 || num_kv_heads > kStreamMaxHeads || num_kv_heads <= 0) return pl;
+  if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8) return pl;
+  if (dtype_or_neg == PKV_F32) return pl;
+  const int per_cu = kStreamWavesPerCu / num_kv_heads > 0 ? kStreamWavesPerCu / num_kv_heads : 1;
+  const int64_t wgs = static_cast<int64_t>(device_cu_count()) * per_cu;
+  const int64_t tiles_max = static_cast<int64_t>(num_seqs) * ((max_context_len + kTile - 1) / kTile);
+  if (tiles_max >= (1LL << 30)) return pl;
+  const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
+  const size_t dyn = static_cast<size_t>(num_seqs + 1 + cap) * sizeof(int32_t);
+  if (dyn > kStreamDynLdsMax) return pl;
+  pl.ok = true;
+  pl.wgs = static_cast<int>(wgs);
+  pl.range_cap = static_cast<int>(cap);
+  pl.dyn_lds = dyn;
+  pl.workspace = static_cast<size_t>(wgs) * 2 * num_q_heads * (head_dim + 2) * sizeof(float);
+  return pl;
+}
 
 int pick_partition(int32_t partition_tokens) {
   return partition_tokens > 0 ? partition_tokens : kDefaultPartition;
@@ -669,6 +1033,25 @@ hipError_t launch_split_d(const AttnArgs& a, int gp, dim3 grid, hipStream_t s) {
     case 6: return launch_split_t<DT, D, 6>(a, grid, s);
     case 7: return launch_split_t<DT, D, 7>(a, grid, s);
     default: return launch_split_t<DT, D, 8>(a, grid, s);
+  }
+}
+
+template <int DT, int GP>
+hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, hipStream_t s) {
+  hipLaunchKernelGGL((attn_stream_kernel<DT, GP>), dim3(static_cast<uint32_t>(pl.wgs)),
+                     dim3(kWave * a.hkv), pl.dyn_lds, s, a);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, hipStream_t s) {
+  switch (gp) {
+    case 1: return launch_stream_t<DT, 1>(a, pl, s);
+    case 2: return launch_stream_t<DT, 2>(a, pl, s);
+    case 4: return launch_stream_t<DT, 4>(a, pl, s);
+    case 6: return launch_stream_t<DT, 6>(a, pl, s);
+    case 7: return launch_stream_t<DT, 7>(a, pl, s);
+    default: return launch_stream_t<DT, 8>(a, pl, s);
   }
 }
 
@@ -760,8 +1143,12 @@ size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_hea
     return 0;
   const int part = pick_partition(partition_tokens);
   const int64_t P = (static_cast<int64_t>(max_context_len) + part - 1) / part;
-  if (P <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  size_t need = P <= 1 ? 0 : static_cast<size_t>(num_seqs) * num_q_heads * P * (head_dim + 2) * sizeof(float);
+  if (partition_tokens == 0) {
+    const StreamPlan pl = plan_stream(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, -1);
+    if (pl.ok && pl.workspace > need) need = pl.workspace;
+  }
+  return need;
 }
 
 }  // extern "C"
@@ -805,6 +1192,51 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
                           reinterpret_cast<uintptr_t>(value_cache);
   if (align % 16 != 0 || (l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0)
     return PKV_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (partition_tokens == 0) {
+    const StreamPlan pl = plan_stream(num_seqs, num_q_heads, l->num_kv_heads, l->head_dim,
+                                      max_context_len, l->dtype);
+    if (pl.ok) {
+      if (!workspace || workspace_bytes < pl.workspace) return PKV_ERR_WORKSPACE;
+      StreamArgs sa;
+      sa.q = q;
+      sa.kc = key_cache;
+      sa.vc = value_cache;
+      sa.tables = block_tables;
+      sa.lens = context_lens;
+      const int64_t acc_floats = static_cast<int64_t>(pl.wgs) * 2 * num_q_heads * l->head_dim;
+      sa.ws_acc = static_cast<float*>(workspace);
+      sa.ws_ml = static_cast<float*>(workspace) + acc_floats;
+      sa.out = out;
+      sa.block_stride = l->block_stride;
+      sa.head_stride = l->head_stride;
+      sa.table_stride = block_table_stride;
+      sa.num_blocks = l->num_blocks;
+      sa.block_size = l->block_size;
+      sa.num_seqs = num_seqs;
+      sa.hq = num_q_heads;
+      sa.hkv = l->num_kv_heads;
+      sa.group = group;
+      sa.max_len = max_context_len;
+      sa.out_dtype = out_dtype;
+      sa.range_cap = pl.range_cap;
+      sa.num_wgs = pl.wgs;
+      sa.scale_log2 = scale * kLog2e;
+      if (phases & kPhasePartial) {
+        const int gp = padded_group(group);
+        hipError_t e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, s)
+                                              : launch_stream_dt<PKV_F16>(sa, gp, pl, s);
+        if (e != hipSuccess) return PKV_ERR_HIP;
+      }
+      if (phases & kPhaseMerge) {
+        hipLaunchKernelGGL(attn_stream_merge_kernel<128>,
+                           dim3(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads)),
+                           dim3(kWave), 0, s, sa);
+        if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+      }
+      return PKV_OK;
+    }
+  }
   const int64_t P = max_context_len > 0 ? (static_cast<int64_t>(max_context_len) + part - 1) / part : 1;
   const size_t need = paged_decode_attention_workspace_size(num_seqs, num_q_heads, l->num_kv_heads,
                                                             l->head_dim, max_context_len, part);
@@ -837,7 +1269,6 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * kLog2e;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (phases & kPhasePartial) {
     const dim3 grid(static_cast<uint32_t>(wgs));
     const int gp = padded_group(group);

@@ -217,3 +217,43 @@ def test_write_skips_out_of_range_slots():
     assert np.count_nonzero(kb != 0x7FC5) == 2 * 64          # only slot 17 (block 1, offset 1)
     assert np.all(kc[1, :, 1].float().cpu().numpy() == 1.0)
     assert np.all(vc[1, :, 1].float().cpu().numpy() == 2.0)
+
+
+def _ragged_case(dtype, h_q, h_kv, lens, seed, bs=16):
+    nb = sum(-(-L // bs) for L in lens) + 8
+    return _small_case(dtype, h_q, h_kv, 128, bs, lens, nb, seed=seed)
+
+
+def test_stream_many_short_sequences_with_empty_ones():
+    """Hundreds of short sequences (some empty): the stream kernel's ranges
+    cut through sequences at arbitrary tiles, several sequences share a
+    workgroup, and many workgroups are empty."""
+    rng = np.random.default_rng(21)
+    lens = [int(x) for x in rng.integers(0, 90, size=300)]
+    lens[0] = 0
+    lens[7] = 1
+    lens[-1] = 0
+    case = _ragged_case("bf16", 28, 4, lens, seed=22)
+    ref = _oracle_attend(case)
+    got = _gpu_attend(case, partition_tokens=0).double().cpu().numpy()
+    assert np.abs(got - ref).max() <= 2e-3
+    split = _gpu_attend(case, partition_tokens=32).double().cpu().numpy()
+    assert np.abs(split - ref).max() <= 2e-3
+    assert np.all(got[0] == 0) and np.all(got[-1] == 0)
+
+
+def test_stream_one_long_sequence_split_everywhere():
+    case = _ragged_case("f16", 8, 8, [12345], seed=23)
+    ref = _oracle_attend(case)
+    got = _gpu_attend(case, partition_tokens=0).double().cpu().numpy()
+    assert np.abs(got - ref).max() <= 2e-3
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(2, 2), (7, 1), (24, 8), (12, 2)])
+def test_stream_head_layouts(h_q, h_kv):
+    rng = np.random.default_rng(h_q * 31 + h_kv)
+    lens = [int(x) for x in rng.integers(1, 700, size=23)]
+    case = _ragged_case("bf16", h_q, h_kv, lens, seed=h_q + 100 * h_kv)
+    ref = _oracle_attend(case)
+    got = _gpu_attend(case, partition_tokens=0).double().cpu().numpy()
+    assert np.abs(got - ref).max() <= 2e-3
