@@ -33,7 +33,6 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_kernel_qwen2_7b_b64_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc", "pkv_kernels.hip")
 
 
@@ -46,12 +45,14 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed PMC summary, if it was taken
-    from the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded_traffic(kernel_name: str, workload: str):
+    """HBM bytes per launch from the committed PMC summary
+    profiles/<kernel>_<workload>.md, if it was taken from the current kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_{workload}.md")
+    if not os.path.exists(path):
         return None, None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
     if not sha or not tb or sha.group(1) != kernel_source_sha():
@@ -241,7 +242,10 @@ def main():
     cold = np.array(cold)
     del flush
 
-    traffic, _ = recorded_traffic()
+    import paged_kv_cache_128_amd as pkv
+    path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
+    kernel_name = {"stream": "attn_stream_kernel", "partition": "attn_split_kernel"}[path]
+    traffic, _ = recorded_traffic(kernel_name, cfg.name)
     result = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s",
         "value": round(value, 2),
@@ -276,8 +280,8 @@ def main():
                               "kv_gbps": round(cold_bytes / (float(np.median(cold[:, 1])) / 1e3) / 1e9, 2),
                               "note": "1 GiB device read before each launch pair"},
         "roofline": {
-            "kernel": f"attn_split_kernel<{cfg.dtype}, D={cfg.head_dim}, "
-                      f"G={cfg.num_q_heads // cfg.num_kv_heads}> (partition kernel)",
+            "kernel": f"{kernel_name}<{cfg.dtype}, D={cfg.head_dim}, "
+                      f"G={cfg.num_q_heads // cfg.num_kv_heads}>",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

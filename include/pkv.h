@@ -247,6 +247,20 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Which attention kernel paged_decode_attention runs for these arguments:
+ * PKV_PATH_STREAM (1): one workgroup per equal share of all tiles of the
+ * launch, all KV heads of a tile together (16-bit KV, head_dim 128,
+ * H_kv <= 8, H_q / H_kv <= 8, partition_tokens == 0); PKV_PATH_PARTITION (2):
+ * one workgroup per (sequence, KV head, context partition of
+ * partition_tokens tokens, default 512).  Negative status on invalid
+ * arguments.  Host-only; the workspace size matches the path.
+ */
+#define PKV_PATH_STREAM 1
+#define PKV_PATH_PARTITION 2
+int paged_decode_attention_path(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                const pkv_cache_layout* layout, int32_t partition_tokens);
+
+/*
  * The two launches of paged_decode_attention, callable separately with the
  * same arguments (for instance to time or overlap them): _partial runs the
  * partition kernel, which finishes every sequence that fits in one partition

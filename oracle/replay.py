@@ -60,3 +60,29 @@ def decode_state(wl: "synth.DecodeWorkload", width: Optional[int] = None,
         width = max(len(mgr.block_table(b)) for b in ids)
     return OracleDecodeState(mgr, kc, vc, step, mgr.block_tables(ids, width, pad),
                              mgr.context_lens(ids), prefill_slots)
+
+
+def serving_replay(trace: "synth.ServingTrace"):
+    """Oracle replay of the serving trace: initial prefill of every row, then
+    per step the batched append, the write of the step's K/V rows, a yield
+    (the caller may run the oracle attention on the state), and the finishes
+    with their refills.  Yields (step, manager, key_cache, value_cache,
+    row_ids, step_slots)."""
+    cfg = trace.cfg
+    mgr = BlockManager(cfg.num_blocks, cfg.block_size)
+    fill = synth.poison_array((), cfg.dtype)
+    kc, vc = new_pool(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, fill)
+    B = len(trace.prompt_lens)
+    row_ids = list(range(B))
+    for b in range(B):
+        slots = mgr.allocate_for_prefill(b, int(trace.prompt_lens[b]))
+        write_kv(trace.hist_k[b], trace.hist_v[b], slots, kc, vc, cfg.block_size)
+    for st in trace.steps:
+        slots = mgr.append_slots_for_decode(row_ids)
+        write_kv(st.new_k, st.new_v, slots, kc, vc, cfg.block_size)
+        yield st, mgr, kc, vc, row_ids, slots
+        for r in st.refills:
+            mgr.free_sequence(r.old_id)
+            s = mgr.allocate_for_prefill(r.new_id, r.prompt_len)
+            write_kv(r.k, r.v, s, kc, vc, cfg.block_size)
+            row_ids[r.row] = r.new_id

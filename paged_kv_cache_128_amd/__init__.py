@@ -105,6 +105,7 @@ SIGNATURES = {
     "paged_decode_attention_merge": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32,
                                                     _I32, _F32, ctypes.POINTER(CacheLayout), _I32,
                                                     _P, _SZ, _P]),
+    "paged_decode_attention_path": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(CacheLayout), _I32]),
     "pkv_update_block_tables": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _I32, _I32, _P]),
 }
 
@@ -377,6 +378,16 @@ def paged_decode_attention(q, key_cache, value_cache, block_tables, context_lens
     return out
 
 
+def attention_path(num_seqs: int, num_q_heads: int, max_context_len: int, key_cache,
+                   partition_tokens: int = 0) -> str:
+    """"stream" or "partition": the attention kernel the library picks."""
+    lay = cache_layout(key_cache)
+    st = _check(_lib_handle().paged_decode_attention_path(num_seqs, num_q_heads, max_context_len,
+                                                          ctypes.byref(lay), partition_tokens),
+                "paged_decode_attention_path")
+    return {1: "stream", 2: "partition"}[st]
+
+
 def update_block_tables(block_tables, lens, new_block, block_size: int, rows=None, stream=None) -> None:
     """Apply one batched append's new blocks to a device block table."""
     n = lens.shape[0]
@@ -392,6 +403,6 @@ def update_block_tables(block_tables, lens, new_block, block_size: int, rows=Non
 __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
-    "workspace_size", "update_block_tables", "new_pool", "cache_layout", "load_library",
+    "workspace_size", "update_block_tables", "attention_path", "new_pool", "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

@@ -1293,6 +1293,17 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
 
 extern "C" {
 
+int paged_decode_attention_path(int32_t num_seqs, int32_t num_q_heads, int32_t max_context_len,
+                                const pkv_cache_layout* l, int32_t partition_tokens) {
+  if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
+      partition_tokens < 0 || num_q_heads % l->num_kv_heads != 0)
+    return PKV_ERR_INVALID;
+  if (partition_tokens == 0 &&
+      plan_stream(num_seqs, num_q_heads, l->num_kv_heads, l->head_dim, max_context_len, l->dtype).ok)
+    return PKV_PATH_STREAM;
+  return PKV_PATH_PARTITION;
+}
+
 int paged_decode_attention(void* out, int32_t out_dtype, const void* q, const void* key_cache,
                            const void* value_cache, const int32_t* block_tables,
                            int32_t block_table_stride, const int32_t* context_lens,
