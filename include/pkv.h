@@ -198,6 +198,29 @@ int paged_kv_write(const void* key, const void* value, const int64_t* slot_mappi
                    int32_t num_tokens, void* key_cache, void* value_cache,
                    const pkv_cache_layout* layout, void* stream);
 
+/*
+ * The write of one decode step, with the step's metadata taken from HOST
+ * memory and carried into the launch as kernel arguments (no separate
+ * host-to-device copy; the caller may reuse `slots` and `lens` as soon as
+ * the call returns).  For every row i in [0, num_rows):
+ *   - key/value row i (device, [num_rows, H_kv, D] contiguous) is written at
+ *     slots[i] exactly as paged_kv_write does ([MiniPaged-Qwen] §12);
+ *   - when block_tables (device, int32 [table_rows, block_table_stride]) is
+ *     not NULL and the token is the first of its block ((lens[i] - 1) % bs
+ *     == 0, i.e. the append opened a block, [MiniPaged-Qwen] §9.2), the
+ *     table entry [i, (lens[i] - 1) / bs] is set to slots[i] / bs;
+ *   - when lens_out (device, int32 [num_rows]) is not NULL, lens_out[i] =
+ *     lens[i].
+ *   slots (host, int64 [num_rows]) and lens (host, int32 [num_rows]) are the
+ *   outputs of pkv_append_slots_for_decode for the rows in order.
+ * Slots outside [0, num_blocks*bs) write nothing.  Errors: INVALID,
+ * UNSUPPORTED, HIP.
+ */
+int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
+                     const int32_t* lens, int32_t num_rows, void* key_cache, void* value_cache,
+                     const pkv_cache_layout* layout, int32_t* block_tables, int32_t table_rows,
+                     int32_t block_table_stride, int32_t* lens_out, void* stream);
+
 /* -------------------------------------------------------- decode attention */
 /*
  * Workspace bytes paged_decode_attention needs for split-K partial results:

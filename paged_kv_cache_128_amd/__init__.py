@@ -96,6 +96,8 @@ SIGNATURES = {
     "pkv_get_free_list": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
     "pkv_check_invariants": (ctypes.c_int, [_P]),
     "paged_kv_write": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "pkv_decode_write": (ctypes.c_int, [_P, _P, _PI64, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout),
+                                        _P, _I32, _I32, _P, _P]),
     "paged_decode_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               _F32, ctypes.POINTER(CacheLayout), _I32, _P, _SZ, _P]),
@@ -328,6 +330,40 @@ def paged_kv_write(key, value, slot_mapping, key_cache, value_cache, stream=None
     _check(st, "paged_kv_write")
 
 
+def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
+                 block_tables=None, lens_out=None, stream=None) -> None:
+    """One decode step's write with host metadata (see pkv_decode_write):
+    key/value [n, H_kv, D] device; slots int64 [n] and lens int32 [n] host
+    (numpy); optional device block table [rows, W] and lens_out int32 [n]."""
+    lay = cache_layout(key_cache, value_cache)
+    n = key.shape[0]
+    if key.shape != (n, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_rows, H_kv, head_dim]")
+    if not (key.is_contiguous() and value.is_contiguous()):
+        raise ValueError("key and value must be contiguous")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype:
+        raise ValueError("key/value dtype must equal the cache dtype")
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if slots.shape != (n,) or lens.shape != (n,):
+        raise ValueError("slots and lens must have one entry per row")
+    torch = _torch()
+    if block_tables is not None and (block_tables.dtype != torch.int32 or block_tables.dim() != 2
+                                     or block_tables.stride(1) != 1):
+        raise ValueError("block_tables must be int32 [rows, W] with unit column stride")
+    if lens_out is not None and (lens_out.dtype != torch.int32 or lens_out.numel() < n
+                                 or not lens_out.is_contiguous()):
+        raise ValueError("lens_out must be a contiguous int32 tensor of at least n entries")
+    st = _lib_handle().pkv_decode_write(
+        key.data_ptr(), value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n,
+        key_cache.data_ptr(), value_cache.data_ptr(), ctypes.byref(lay),
+        None if block_tables is None else block_tables.data_ptr(),
+        0 if block_tables is None else block_tables.shape[0],
+        0 if block_tables is None else block_tables.stride(0),
+        None if lens_out is None else lens_out.data_ptr(), _stream_handle(stream))
+    _check(st, "pkv_decode_write")
+
+
 def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                    max_context_len: int, partition_tokens: int = 0) -> int:
     return int(_lib_handle().paged_decode_attention_workspace_size(
@@ -403,6 +439,6 @@ def update_block_tables(block_tables, lens, new_block, block_size: int, rows=Non
 __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
-    "workspace_size", "update_block_tables", "attention_path", "new_pool", "cache_layout", "load_library",
+    "workspace_size", "update_block_tables", "attention_path", "decode_write", "new_pool", "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

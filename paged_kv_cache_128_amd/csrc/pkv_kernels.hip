@@ -127,6 +127,55 @@ kv_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
   value_cache[dst] = value[idx];
 }
 
+// ------------------------------------------------------------ decode-step write
+// One decode step's metadata travels in the kernel arguments (no separate
+// host-to-device copy): per row i the new token's slot and the row's length
+// after the append.  The kernel writes the K/V rows like kv_write_kernel,
+// publishes the block a row opened (a token at offset 0 of its block opened
+// that block at logical index (len - 1) / bs, [MiniPaged-Qwen] §9.2) into the
+// device block table, and copies the lengths to `lens_out` for the
+// attention launch that follows.
+constexpr int kStepRows = 256;
+struct StepMeta {
+  int64_t slots[kStepRows];
+  int32_t lens[kStepRows];
+};
+
+__global__ void __launch_bounds__(256)
+decode_write_kernel(StepMeta meta, int32_t n, int32_t row0, const uint4* __restrict__ key,
+                    const uint4* __restrict__ value, int32_t chunks_per_head,
+                    int32_t chunks_per_token, int64_t capacity, int32_t block_size,
+                    int64_t block_stride16, int64_t head_stride16, int32_t token_stride16,
+                    uint4* __restrict__ key_cache, uint4* __restrict__ value_cache,
+                    int32_t* __restrict__ tables, int32_t table_rows, int32_t table_stride,
+                    int32_t* __restrict__ lens_out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(n) * chunks_per_token) return;
+  const int32_t t = static_cast<int32_t>(idx / chunks_per_token);
+  const int32_t r = static_cast<int32_t>(idx - static_cast<int64_t>(t) * chunks_per_token);
+  const int64_t slot = meta.slots[t];
+  if (r == 0) {
+    const int32_t len = meta.lens[t];
+    const int32_t row = row0 + t;
+    if (lens_out) lens_out[row] = len;
+    if (tables && row < table_rows && len > 0 && slot >= 0 && slot < capacity &&
+        (len - 1) % block_size == 0) {
+      const int32_t col = (len - 1) / block_size;
+      if (col < table_stride) tables[static_cast<int64_t>(row) * table_stride + col] =
+          static_cast<int32_t>(slot / block_size);
+    }
+  }
+  if (slot < 0 || slot >= capacity) return;
+  const int32_t h = r / chunks_per_head;
+  const int32_t c = r - h * chunks_per_head;
+  const int64_t pb = slot / block_size;
+  const int64_t off = slot - pb * block_size;
+  const int64_t dst = pb * block_stride16 + h * head_stride16 + off * token_stride16 + c;
+  const int64_t src = static_cast<int64_t>(row0 + t) * chunks_per_token + r;
+  key_cache[dst] = key[src];
+  value_cache[dst] = value[src];
+}
+
 // ------------------------------------------------------------ table update
 __global__ void __launch_bounds__(256)
 table_update_kernel(int32_t* __restrict__ tables, int32_t num_rows, int32_t stride,
@@ -256,9 +305,13 @@ __device__ __forceinline__ void load_k_direct(KFrag<DT, D>& t, const char* ktile
 // KiB: lane l of instruction rr writes slot (l % 16) of row 4 rr + l / 16.
 // The lane fetches chunk (slot ^ row) of that row, so chunk c of row r sits
 // at slot c ^ r; each instruction still reads four whole rows from HBM.
+// The asm statements are compiler-only memory barriers: the LDS writes of the
+// DMA are not ordered against ordinary LDS reads by the optimiser, so reads
+// of `sk` must not be moved across the issue point in either direction.
 template <int DT, int D>
 __device__ __forceinline__ void issue_k_rows(const char* ktile, uint4* sk, int nvalid, int lane) {
   const int g4 = lane >> 4, c16 = lane & 15;
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const int row = 4 * rr + g4;
@@ -267,6 +320,7 @@ __device__ __forceinline__ void issue_k_rows(const char* ktile, uint4* sk, int n
     __builtin_amdgcn_global_load_lds((global_void*)(src),
                                      (lds_void*)(sk + rr * 64), 16, 0, 0);
   }
+  asm volatile("" ::: "memory");
 }
 
 // Reads the staged K rows back in the MFMA operand layout: lane (g4, c16)
@@ -720,20 +774,28 @@ __device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_
   if (lane == kWave - 1) S[B] = incl;
 }
 
+// Tiles are taken in chunks of up to kStreamChunk consecutive tiles of one
+// sequence: the chunk's K rows sit in LDS and its V rows in registers while
+// the next chunk is being fetched, so each wave keeps up to
+// kStreamChunk * 8 KiB in flight during its compute.
+constexpr int kStreamChunk = 2;
+
 template <int DT, int GP>
 __global__ void __launch_bounds__(kWave * kStreamMaxHeads, 2)
 attn_stream_kernel(StreamArgs a) {
   constexpr int D = 128;
+  constexpr int CH = kStreamChunk;
   using F = Frag<DT, D>;
   static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
-  extern __shared__ int32_t sh_stream[];
-  __shared__ uint4 sk_all[kStreamMaxHeads][256];
+  // dynamic LDS: [K staging: H_kv waves x CH tiles x 4 KiB][S: B + 1][tbl: range_cap]
+  extern __shared__ uint4 sh_stream[];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & (kWave - 1);
   const int g4 = lane >> 4, c16 = lane & 15;
   const int B = a.num_seqs;
-  int32_t* S = sh_stream;              // [B + 1]
-  int32_t* tbl = sh_stream + B + 1;    // [range_cap]
+  uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * 256;
+  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(a.hkv) * CH * 256);
+  int32_t* tbl = S + B + 1;
   if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, lane);
   __syncthreads();
   const int T = S[B];
@@ -753,16 +815,15 @@ attn_stream_kernel(StreamArgs a) {
 
   const int kvh = wave;
   const int G = a.group;
-  uint4* sk = sk_all[wave];
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
   const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
-  // element offset of tile g (inside the workgroup's range)
-  auto tile_elem = [&](int g, int b_of_g) -> int64_t {
+  // byte offset of tile g of sequence b (inside the workgroup's range)
+  auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
     const int ti = g - S[b_of_g];
     const int off = (ti * kTile) % bs;
-    return static_cast<int64_t>(tbl[g - g0]) * a.block_stride + head_off +
-           static_cast<int64_t>(off) * D;
+    return (static_cast<int64_t>(tbl[g - g0]) * a.block_stride + head_off +
+            static_cast<int64_t>(off) * D) * 2;
   };
   auto load_q = [&](Dw<F::kDwK>& qf, int b) {
     const int head = c16 < G ? c16 : 0;
@@ -775,14 +836,16 @@ attn_stream_kernel(StreamArgs a) {
       for (int e = 0; e < 4; ++e) qf.w[4 * kk + e] = (c16 < G) ? x.w[e] : 0u;
     }
   };
+  auto nvalid_at = [&](int g, int s0, int L) { return min(kTile, L - kTile * (g - s0)); };
+  // tiles in the chunk starting at g of a sequence ending before tile s_end
+  auto chunk_len = [&](int g, int s_end) { return min(CH, min(g1, s_end) - g); };
 
-  // consume cursor (sequence of the tile being computed)
+  // current chunk: tiles [cg, cg + cn) of sequence bc, whose tiles are [sc0, sc1)
   int bc = seq_of_tile(S, B, g0);
-  int sc0 = S[bc], sc1 = S[bc + 1];          // tile range of sequence bc
+  int sc0 = S[bc], sc1 = S[bc + 1];
   int Lc = clamp_len(a.lens[bc], a.max_len);
   int seg0 = g0;                              // first tile of the current segment
-  // prefetch cursor (sequence of the next tile to load)
-  int bn = bc, sn0 = sc0, sn1 = sc1, Ln = Lc;
+  int cg = g0, cn = chunk_len(g0, sc1);
   Dw<F::kDwK> qf;
   load_q(qf, bc);
   float m = -INFINITY, l = 0.f;
@@ -792,39 +855,56 @@ attn_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
 
-  auto nvalid_at = [&](int g, int s0, int L) { return min(kTile, L - kTile * (g - s0)); };
-  VTile<DT, D> vcur, vnext;
-  {
-    const int64_t e0 = tile_elem(g0, bc) * 2;
-    const int nv = nvalid_at(g0, sc0, Lc);
-    issue_k_rows<DT, D>(kc + e0, sk, nv, lane);
-    load_v<DT, D>(vcur, vc + e0, nv, lane);
+  VTile<DT, D> vcur[CH], vnext[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if (j < cn) {
+      const int64_t e = tile_bytes(cg + j, bc);
+      const int nv = nvalid_at(cg + j, sc0, Lc);
+      issue_k_rows<DT, D>(kc + e, sk + j * 256, nv, lane);
+      load_v<DT, D>(vcur[j], vc + e, nv, lane);
+    }
   }
-  // Per tile g: scores from the K rows in LDS; then the fetch of tile g + 1
-  // (clamped to the range) and, when g + 1 opens the next sequence, that
-  // sequence's query group straight into qf (the scores of g no longer
-  // need it); then softmax + P.V of g; then the segment end if g closes one.
-  for (int g = g0; g < g1; ++g) {
-    const f32x4 scr = qk_mfma<DT, D>(read_k_rows<DT, D>(sk, lane), qf);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads of tile g done before it is refilled
-    const int gn = min(g + 1, g1 - 1);
-    if (gn >= sn1) {
-      bn = seq_of_tile(S, B, gn);
-      sn0 = S[bn];
-      sn1 = S[bn + 1];
-      Ln = clamp_len(a.lens[bn], a.max_len);
-      load_q(qf, bn);
+  // Per chunk: scores of its tiles from the K rows in LDS; then the fetch of
+  // the next chunk and, when that chunk opens the next sequence, its query
+  // group straight into qf (this chunk's scores no longer need it); then
+  // softmax + P.V of the chunk's tiles; then the segment end if the chunk
+  // closes one.
+  while (cg < g1) {
+    f32x4 scr[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads done before the buffers are refilled
+    const int ng = cg + cn;
+    int bn = bc, sn0 = sc0, sn1 = sc1, Ln = Lc, nn = 0;
+    if (ng < g1) {
+      if (ng >= sc1) {
+        bn = seq_of_tile(S, B, ng);
+        sn0 = S[bn];
+        sn1 = S[bn + 1];
+        Ln = clamp_len(a.lens[bn], a.max_len);
+        load_q(qf, bn);
+      }
+      nn = chunk_len(ng, sn1);
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (j < nn) {
+          const int64_t e = tile_bytes(ng + j, bn);
+          const int nv = nvalid_at(ng + j, sn0, Ln);
+          issue_k_rows<DT, D>(kc + e, sk + j * 256, nv, lane);
+          load_v<DT, D>(vnext[j], vc + e, nv, lane);
+        }
+      }
     }
-    {
-      const int64_t en = tile_elem(gn, bn) * 2;
-      const int nv = nvalid_at(gn, sn0, Ln);
-      issue_k_rows<DT, D>(kc + en, sk, nv, lane);
-      load_v<DT, D>(vnext, vc + en, nv, lane);
-    }
-    softmax_pv<DT, D, GP>(scr, vcur, nvalid_at(g, sc0, Lc), a.scale_log2, m, l, acc, lane);
-    vcur = vnext;
-    if (g == g1 - 1 || g == sc1 - 1) {
-      const bool complete = (seg0 == sc0) && (g == sc1 - 1);
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (j < cn)
+        softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cg + j, sc0, Lc), a.scale_log2, m, l, acc,
+                              lane);
+    const int last = cg + cn - 1;
+    if (last == g1 - 1 || last == sc1 - 1) {
+      const bool complete = (seg0 == sc0) && (last == sc1 - 1);
       const int slot = (seg0 == g0) ? 0 : 1;
       wave_epilogue<DT, D, GP>(m, l, acc, lane, G, complete, a.out, a.out_dtype,
                                static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G,
@@ -836,7 +916,7 @@ attn_stream_kernel(StreamArgs a) {
       sc0 = sn0;
       sc1 = sn1;
       Lc = Ln;
-      seg0 = g + 1;
+      seg0 = ng;
       m = -INFINITY;
       l = 0.f;
 #pragma unroll
@@ -844,9 +924,11 @@ attn_stream_kernel(StreamArgs a) {
 #pragma unroll
         for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
     }
+#pragma unroll
+    for (int j = 0; j < CH; ++j) vcur[j] = vnext[j];
+    cg = ng;
+    cn = nn;
   }
-  // the last (clamped) K fetch into LDS must land before the wave can exit
-  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // Merge of the stream kernel's partials.  One 64-lane workgroup per
@@ -953,7 +1035,7 @@ attn_stream_merge_kernel(StreamArgs a) {
 // ------------------------------------------------------------ dispatch
 constexpr int kDefaultPartition = 512;
 constexpr int kStreamWavesPerCu = 8;      // stream kernel: resident waves per CU aimed at
-constexpr size_t kStreamDynLdsMax = 32768;
+constexpr size_t kStreamDynLdsMax = 65536;
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -988,7 +1070,8 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   const int64_t tiles_max = static_cast<int64_t>(num_seqs) * ((max_context_len + kTile - 1) / kTile);
   if (tiles_max >= (1LL << 30)) return pl;
   const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
-  const size_t dyn = static_cast<size_t>(num_seqs + 1 + cap) * sizeof(int32_t);
+  const size_t dyn = static_cast<size_t>(num_kv_heads) * kStreamChunk * 4096 +
+                     static_cast<size_t>(num_seqs + 1 + cap) * sizeof(int32_t);
   if (dyn > kStreamDynLdsMax) return pl;
   pl.ok = true;
   pl.wgs = static_cast<int>(wgs);
@@ -1133,6 +1216,47 @@ int paged_kv_write(const void* key, const void* value, const int64_t* slot_mappi
                      static_cast<int32_t>(row_bytes / 16), static_cast<uint4*>(key_cache),
                      static_cast<uint4*>(value_cache));
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_decode_write(const void* key, const void* value, const int64_t* slots, const int32_t* lens,
+                     int32_t num_rows, void* key_cache, void* value_cache,
+                     const pkv_cache_layout* l, int32_t* block_tables, int32_t table_rows,
+                     int32_t block_table_stride, int32_t* lens_out, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK || num_rows < 0 || table_rows < 0 || block_table_stride < 0)
+    return PKV_ERR_INVALID;
+  if (num_rows == 0) return PKV_OK;
+  if (!key || !value || !slots || !lens || !key_cache || !value_cache) return PKV_ERR_INVALID;
+  if (block_tables && block_table_stride <= 0) return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const int64_t row_bytes = static_cast<int64_t>(l->head_dim) * eb;
+  if (row_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  if ((l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value) |
+                          reinterpret_cast<uintptr_t>(key_cache) |
+                          reinterpret_cast<uintptr_t>(value_cache);
+  if (align % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  const int32_t chunks_per_head = static_cast<int32_t>(row_bytes / 16);
+  const int32_t chunks_per_token = chunks_per_head * l->num_kv_heads;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t row0 = 0; row0 < num_rows; row0 += kStepRows) {
+    const int32_t n = num_rows - row0 < kStepRows ? num_rows - row0 : kStepRows;
+    StepMeta meta;
+    for (int32_t i = 0; i < n; ++i) {
+      meta.slots[i] = slots[row0 + i];
+      meta.lens[i] = lens[row0 + i];
+    }
+    const int64_t total = static_cast<int64_t>(n) * chunks_per_token;
+    hipLaunchKernelGGL(decode_write_kernel, dim3(static_cast<uint32_t>((total + 255) / 256)),
+                       dim3(256), 0, s, meta, n, row0, static_cast<const uint4*>(key),
+                       static_cast<const uint4*>(value), chunks_per_head, chunks_per_token,
+                       static_cast<int64_t>(l->num_blocks) * l->block_size, l->block_size,
+                       l->block_stride * eb / 16, l->head_stride * eb / 16,
+                       static_cast<int32_t>(row_bytes / 16), static_cast<uint4*>(key_cache),
+                       static_cast<uint4*>(value_cache), block_tables, table_rows,
+                       block_table_stride, lens_out);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
 }
 
 size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,

@@ -5,11 +5,11 @@ A decode step is the hot path of [MiniPaged-Qwen] §10 and §13 in order:
 
   1. block manager append for every row (one batched C call; all or nothing,
      [mini-vLLM BM] "Block Manager 和 Scheduler 如何协作"),
-  2. one host-to-device copy of the step's metadata (slots, lengths, opened
-     blocks) from a pinned staging buffer,
-  3. table update kernel (opened blocks -> device block table),
-  4. paged_kv_write of the new K/V rows ([MiniPaged-Qwen] §12),
-  5. paged_decode_attention over the updated cache ([MiniPaged-Qwen] §13),
+  2. one write launch that carries the step's slots and lengths in its kernel
+     arguments: it writes the new K/V rows ([MiniPaged-Qwen] §12), publishes
+     the blocks the append opened into the device block table and stores the
+     lengths on the device,
+  3. paged_decode_attention over the updated cache ([MiniPaged-Qwen] §13),
      so the new token attends to itself ([MiniPaged-Qwen] §1.1: append, then
      attend over positions 0..L).
 
@@ -23,43 +23,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, new_pool, paged_decode_attention, paged_kv_write,
-               update_block_tables, workspace_size)
-
-
-class _Staging:
-    """Pinned host buffer + device mirror for one step's metadata, with an
-    event guarding reuse of the host side."""
-
-    def __init__(self, rows: int, device):
-        self.rows = rows
-        nbytes = 16 * rows
-        self.host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
-        self.dev = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        h = self.host.numpy()
-        self.slots = h[: 8 * rows].view(np.int64)
-        self.lens = h[8 * rows: 12 * rows].view(np.int32)
-        self.newb = h[12 * rows: 16 * rows].view(np.int32)
-        self.d_slots = self.dev[: 8 * rows].view(torch.int64)
-        self.d_lens = self.dev[8 * rows: 12 * rows].view(torch.int32)
-        self.d_newb = self.dev[12 * rows: 16 * rows].view(torch.int32)
-        self.event: Optional[torch.cuda.Event] = None
-
-    def wait_free(self):
-        if self.event is not None:
-            self.event.synchronize()
-
-    def upload(self, n: int):
-        if n == self.rows:
-            self.dev.copy_(self.host, non_blocking=True)
-        else:
-            self.d_slots[:n].copy_(self.host[: 8 * n].view(torch.int64), non_blocking=True)
-            self.d_lens[:n].copy_(self.host[8 * self.rows: 8 * self.rows + 4 * n].view(torch.int32),
-                                  non_blocking=True)
-            self.d_newb[:n].copy_(self.host[12 * self.rows: 12 * self.rows + 4 * n].view(torch.int32),
-                                  non_blocking=True)
-        self.event = torch.cuda.Event()
-        self.event.record()
+from . import (KVBlockManager, decode_write, new_pool, paged_decode_attention, paged_kv_write,
+               workspace_size)
 
 
 class PagedKVEngine:
@@ -82,8 +47,10 @@ class PagedKVEngine:
             num_blocks, num_kv_heads, block_size, head_dim, dtype, self.device, fill_bits)
         self.tables = torch.full((max_rows, self.width), -1, dtype=torch.int32, device=self.device)
         self.row_seq: Dict[int, int] = {}
-        self._staging = [_Staging(max_rows, self.device), _Staging(max_rows, self.device)]
-        self._turn = 0
+        self.d_lens = torch.zeros(max_rows, dtype=torch.int32, device=self.device)
+        self.slots = np.empty(max_rows, dtype=np.int64)      # last step's slots (host)
+        self.lens = np.empty(max_rows, dtype=np.int32)       # last step's lengths (host)
+        self._newb = np.empty(max_rows, dtype=np.int32)
         self._ws = None
         self._nq = num_q_heads
 
@@ -136,32 +103,21 @@ class PagedKVEngine:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return self._ws
 
-    def append(self, seq_ids: np.ndarray):
-        """Host part of a step: batched append into the next staging buffer
-        and its upload.  Returns the staging object (device views inside)."""
-        st = self._staging[self._turn]
-        self._turn ^= 1
-        st.wait_free()
-        n = len(seq_ids)
-        self.manager.append_slots_for_decode(seq_ids, st.slots[:n], st.lens[:n], st.newb[:n])
-        st.upload(n)
-        return st
-
     def decode_step(self, seq_ids: np.ndarray, new_k: torch.Tensor, new_v: torch.Tensor,
                     q: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
         """One decode step for rows 0..n-1 holding ``seq_ids`` (int64).
         ``max_context_len`` defaults to the longest length after the append
         (known on the host from the manager, no device sync).  ``events``
-        (three torch.cuda.Event) are recorded before the attention partition
-        kernel, between it and the split-K merge, and after the merge."""
+        (three torch.cuda.Event) are recorded before the attention kernel,
+        between it and the merge, and after the merge."""
         n = len(seq_ids)
-        st = self.append(seq_ids)
+        self.manager.append_slots_for_decode(seq_ids, self.slots[:n], self.lens[:n], self._newb[:n])
         if max_context_len is None:
-            max_context_len = int(st.lens[:n].max()) if n else 0
-        update_block_tables(self.tables, st.d_lens[:n], st.d_newb[:n], self.block_size)
-        paged_kv_write(new_k, new_v, st.d_slots[:n], self.key_cache, self.value_cache)
-        return self.attend(q, st.d_lens[:n], scale, max_context_len, out=out, events=events)
+            max_context_len = int(self.lens[:n].max()) if n else 0
+        decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
+                     block_tables=self.tables, lens_out=self.d_lens)
+        return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
 
     def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
                out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:

@@ -83,8 +83,7 @@ def test_serving_trace_200_steps():
     for st_g, (st_o, mgr, kc, vc, o_rows, o_slots) in zip(tr_gpu.steps, serving_replay(tr_ora)):
         out = eng.decode_step(row_ids, to_device(st_g.new_k, cfg.dtype), to_device(st_g.new_v, cfg.dtype),
                               to_device(st_g.q, cfg.dtype), cfg.scale)
-        staged = eng._staging[eng._turn ^ 1]
-        assert staged.slots[:B].tolist() == list(o_slots), f"slots differ at step {st_g.step}"
+        assert eng.slots[:B].tolist() == list(o_slots), f"slots differ at step {st_g.step}"
         if st_g.step % 25 == 0 or st_g.step == cfg.steps - 1:
             torch.cuda.synchronize()
             rows = _sample(np.array([mgr.context_len(s) for s in o_rows]), 8, st_g.step)

@@ -257,3 +257,32 @@ def test_stream_head_layouts(h_q, h_kv):
     ref = _oracle_attend(case)
     got = _gpu_attend(case, partition_tokens=0).double().cpu().numpy()
     assert np.abs(got - ref).max() <= 2e-3
+
+
+def test_decode_write_matches_write_plus_table_update():
+    """pkv_decode_write (metadata in kernel arguments) equals paged_kv_write
+    followed by pkv_update_block_tables, over 300 rows (two launches)."""
+    import paged_kv_cache_128_amd as pkv
+    rng = np.random.default_rng(77)
+    n, N, bs = 300, 2048, 16
+    mgr = pkv.KVBlockManager(N, bs, rng.permutation(N))
+    for i in range(n):
+        mgr.allocate_for_prefill(i, int(rng.integers(0, 40)))
+    ids = np.arange(n, dtype=np.int64)
+    W = 8
+    tabs0 = torch.from_numpy(mgr.block_tables(ids, W, -1)).cuda()
+    slots, lens, newb = mgr.append_slots_for_decode(ids)
+    key = torch.randn((n, 4, 128), device="cuda").to(torch.bfloat16)
+    val = torch.randn((n, 4, 128), device="cuda").to(torch.bfloat16)
+    pa, ka, va = pkv.new_pool(N, 4, bs, 128, torch.bfloat16, fill_bits=0x7FC5)
+    pb_, kb, vb = pkv.new_pool(N, 4, bs, 128, torch.bfloat16, fill_bits=0x7FC5)
+    ta, tb = tabs0.clone(), tabs0.clone()
+    d_lens = torch.zeros(n, dtype=torch.int32, device="cuda")
+    pkv.decode_write(key, val, slots, lens, ka, va, block_tables=ta, lens_out=d_lens)
+    pkv.paged_kv_write(key, val, torch.from_numpy(slots).cuda(), kb, vb)
+    pkv.update_block_tables(tb, torch.from_numpy(lens).cuda(), torch.from_numpy(newb).cuda(), bs)
+    torch.cuda.synchronize()
+    assert torch.equal(pa.view(torch.int16), pb_.view(torch.int16))
+    assert torch.equal(ta, tb)
+    assert np.array_equal(ta.cpu().numpy(), mgr.block_tables(ids, W, -1))
+    assert np.array_equal(d_lens.cpu().numpy(), lens)
