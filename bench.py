@@ -276,8 +276,8 @@ def main():
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(tokens_per_s, 1),
         "attention_kv_gbps": round(attn_gbps, 2),
-        "attention_cold_us": {"partition_kernel": round(float(np.median(cold[:, 0])) * 1e3, 2),
-                              "partition_plus_merge": round(float(np.median(cold[:, 1])) * 1e3, 2),
+        "attention_cold_us": {"attention_kernel": round(float(np.median(cold[:, 0])) * 1e3, 2),
+                              "attention_plus_merge": round(float(np.median(cold[:, 1])) * 1e3, 2),
                               "kv_bytes": cold_bytes,
                               "kv_gbps": round(cold_bytes / (float(np.median(cold[:, 1])) / 1e3) / 1e9, 2),
                               "note": "1 GiB device read before each launch pair"},
