@@ -31,6 +31,8 @@
 //  - The next tile's K and V are loaded before the current one is consumed
 //    (two register stages), so every wave keeps 8 KiB in flight.
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include <utility>
@@ -270,7 +272,9 @@ __device__ __forceinline__ void load_v(VTile<DT, D>& t, const char* vtile, int n
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int tok = 4 * g4 + r < nvalid ? 4 * g4 + r : 0;
-    const char* src = vtile + (static_cast<int64_t>(tok) * D + c16 * F::kW) * F::kBytes;
+    // 32-bit lane offset on a wave-uniform tile base
+    const uint32_t off = static_cast<uint32_t>((tok * D + c16 * F::kW) * F::kBytes);
+    const char* src = vtile + off;
     if constexpr (F::kRowK) t.v[r] = load_nt16(src);
     else t.v[r] = load_dw<F::kDwV>(src);
   }
@@ -316,8 +320,8 @@ __device__ __forceinline__ void issue_k_rows(const char* ktile, uint4* sk, int n
   for (int rr = 0; rr < 4; ++rr) {
     const int row = 4 * rr + g4;
     const int src_row = row < nvalid ? row : 0;
-    const char* src = ktile + static_cast<int64_t>(src_row) * D * 2 + ((c16 ^ row) * 16);
-    __builtin_amdgcn_global_load_lds((global_void*)(src),
+    const uint32_t off = static_cast<uint32_t>(src_row * D * 2 + ((c16 ^ row) * 16));
+    __builtin_amdgcn_global_load_lds((global_void*)(ktile + off),
                                      (lds_void*)(sk + rr * 64), 16, 0, 0);
   }
   asm volatile("" ::: "memory");
@@ -442,57 +446,90 @@ __device__ __forceinline__ void softmax_pv(const f32x4 s, const VTile<DT, D>& t,
 // token groups' (l, acc), then for each of the G query heads writes either
 // the normalised output row (`final`) or the raw (m, l, acc) partial to
 // workspace slot ws_row0 + h * ws_row_stride.  Lane group g4 writes heads
-// g4, g4 + 4, ...; lane c16 writes head-dim chunk c16.
+// g4 and g4 + 4; lane c16 writes head-dim chunk c16.  The accumulator sum
+// over the four groups is a reduce-scatter in two exchanges (lanes 32 apart,
+// then 16 apart), each lane keeping half of the heads per exchange, so it
+// ends with just the two heads it writes: half the lane exchanges of an
+// all-reduce and a quarter of its registers.
 template <int DT, int D, int GP>
 __device__ __forceinline__ void wave_epilogue(float m, float l, float (&acc)[GP][Frag<DT, D>::kW],
                                               int lane, int G, bool final, void* out, int out_dtype,
                                               int64_t out_row0, float* ws_acc, float* ws_ml,
                                               int64_t ws_row0, int64_t ws_row_stride) {
   using F = Frag<DT, D>;
+  constexpr int kW = F::kW;
+  static_assert(GP <= 8, "two heads per lane group");
   const int g4 = lane >> 4, c16 = lane & 15;
+  const bool b1 = (g4 & 2) != 0, b0 = (g4 & 1) != 0;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
+  auto A = [&](int h, int e) -> float { return h < GP ? acc[h][e] : 0.f; };
+  // exchange 1 (g4 bit 1): pair p holds heads h0 = p + (p & 2) and h0 + 2;
+  // the lane keeps the one whose bit 1 matches its own
+  float k1[4][kW];
 #pragma unroll
-  for (int h = 0; h < GP; ++h)
+  for (int p = 0; p < 4; ++p) {
+    const int h0 = p + (p & 2), h1 = h0 + 2;
 #pragma unroll
-    for (int e = 0; e < F::kW; ++e) {
-      float v = acc[h][e];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[h][e] = v;
+    for (int e = 0; e < kW; ++e) {
+      if (h0 >= GP) {
+        k1[p][e] = 0.f;
+        continue;
+      }
+      const float send = b1 ? A(h0, e) : A(h1, e);
+      const float keep = b1 ? A(h1, e) : A(h0, e);
+      k1[p][e] = keep + __shfl_xor(send, 32);
     }
-  for_each_head<GP>([&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const float lh = row_bcast<h>(l);
-    const float mh = row_bcast<h>(m);
-    if ((h & 3) != g4 || h >= G) return;
+  }
+  // exchange 2 (g4 bit 0): k2[j] ends as head 4 j + g4
+  float k2[2][kW];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+#pragma unroll
+    for (int e = 0; e < kW; ++e) {
+      if (4 * j >= GP) {
+        k2[j][e] = 0.f;
+        continue;
+      }
+      const float send = b0 ? k1[2 * j][e] : k1[2 * j + 1][e];
+      const float keep = b0 ? k1[2 * j + 1][e] : k1[2 * j][e];
+      k2[j][e] = keep + __shfl_xor(send, 16);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (4 * j >= GP) continue;
+    const int h = 4 * j + g4;
+    const float lh = __shfl(l, h);     // lane h holds head h's (m, l)
+    const float mh = __shfl(m, h);
+    if (h >= G) continue;
     if (final) {
       const int64_t row = out_row0 + h;
       const float inv = lh > 0.f ? 1.0f / lh : 0.f;
       if (out_dtype == PKV_F32) {
-        float* o = static_cast<float*>(out) + row * D + c16 * F::kW;
+        float* o = static_cast<float*>(out) + row * D + c16 * kW;
 #pragma unroll
-        for (int e = 0; e < F::kW; ++e) o[e] = acc[h][e] * inv;
+        for (int e = 0; e < kW; ++e) o[e] = k2[j][e] * inv;
       } else {
-        uint16_t* o = static_cast<uint16_t*>(out) + row * D + c16 * F::kW;
+        uint16_t* o = static_cast<uint16_t*>(out) + row * D + c16 * kW;
 #pragma unroll
-        for (int e = 0; e < F::kW; ++e) {
-          const float y = acc[h][e] * inv;
+        for (int e = 0; e < kW; ++e) {
+          const float y = k2[j][e] * inv;
           o[e] = (out_dtype == PKV_BF16) ? f32_to_bf16_rne(y)
                                          : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
         }
       }
     } else {
       const int64_t slot = ws_row0 + h * ws_row_stride;
-      float* w = ws_acc + slot * D + c16 * F::kW;
+      float* w = ws_acc + slot * D + c16 * kW;
 #pragma unroll
-      for (int e = 0; e < F::kW; ++e) w[e] = acc[h][e];
+      for (int e = 0; e < kW; ++e) w[e] = k2[j][e];
       if (c16 == 0) {
         ws_ml[2 * slot + 0] = mh;
         ws_ml[2 * slot + 1] = lh;
       }
     }
-  });
+  }
 }
 
 template <int DT, int D, int GP>
@@ -702,23 +739,40 @@ attn_reduce_kernel(AttnArgs a) {
 }
 
 // ------------------------------------------------------------ stream-K attention
-// One workgroup per contiguous range of the launch's 16-token tiles, with
-// the tiles of all sequences laid end to end (sequence b owns tiles
-// [S_b, S_b + T_b), T_b = ceil(L_b / 16)).  Workgroup w takes tiles
-// [w*T/W, (w+1)*T/W) and runs one wave per KV head, so it streams every
-// physical block of its range as one contiguous region (K half then V half
-// of the block), and all workgroups carry the same number of tiles whatever
-// the mix of context lengths.  A sequence cut by a range boundary leaves a
-// (max, sum, accumulator) partial per piece in the workspace; the merge
-// kernel combines the pieces.  16-bit KV, D = 128, H_kv <= 8, G <= 8.
+// The launch's 16-token tiles, with the tiles of all sequences laid end to
+// end (sequence b owns tiles [S_b, S_b + T_b), T_b = ceil(L_b / 16)), are
+// cut into W equal contiguous ranges: range r takes tiles [r*T/W, (r+1)*T/W),
+// so every range carries the same number of tiles whatever the mix of
+// context lengths.  One workgroup per CU holds R consecutive ranges.  A job
+// is one (range, KV head); its tiles are cut into chunks of up to
+// kStreamChunk tiles of one sequence, and two waves share the job: the
+// front worker claims chunks from the start of the range, the back worker
+// from its end, one LDS atomic per claim, until the claims meet.  The two
+// waves on one SIMD do not progress at the same rate (the one in the
+// second wave slot runs markedly slower under this load), so the meeting
+// point, not a fixed split, decides who reads what.  When every KV head has
+// two waves (2 * R * H_kv <= 8) each job has its own pair; otherwise
+// (H_kv > 4) each wave is the front worker of job j and then the back
+// worker of job (j + 4) mod H_kv.
+//
+// Every maximal run of one worker's chunks in one sequence is a segment; a
+// segment that covers its whole sequence writes the normalised output,
+// other segments leave a (max, sum, accumulator) partial in one of four
+// slots of their job: 0 = the front worker's segment starting at the range
+// start, 1 = its segment ending at the meeting point, 2 = the back worker's
+// segment ending at the range end, 3 = its segment starting at the meeting
+// point.  The front worker records the meeting point; the merge kernel
+// finds the pieces of each sequence from the range bounds and the meeting
+// points.  16-bit KV, D = 128, H_kv <= 8, G <= 8.
 struct StreamArgs {
   const void* q;
   const void* kc;
   const void* vc;
   const int32_t* tables;
   const int32_t* lens;
-  float* ws_ml;      // [W, 2, H_q, 2]
-  float* ws_acc;     // [W, 2, H_q, D]
+  float* ws_acc;     // [W, 4, H_q, D]   (W = num_ranges)
+  float* ws_ml;      // [W, 4, H_q, 2]
+  int32_t* ws_x;     // [W, H_kv] meeting tile of each job
   void* out;
   int64_t block_stride;
   int64_t head_stride;
@@ -731,12 +785,16 @@ struct StreamArgs {
   int32_t group;
   int32_t max_len;
   int32_t out_dtype;
-  int32_t range_cap;     // table entries one workgroup may stage
-  int32_t num_wgs;       // W, workgroups of the stream kernel
+  int32_t range_cap;     // tiles one workgroup may hold
+  int32_t num_ranges;    // W
+  int32_t ranges_per_wg; // R
   float scale_log2;
 };
 
 constexpr int kStreamMaxHeads = 8;
+constexpr int kStreamMaxWaves = 8;
+constexpr int kStreamSlots = 4;          // partial slots per job
+constexpr int kStreamMaxRanges = 1024;   // W bound (merge kernel's piece list)
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
   return L < 0 ? 0 : (L > max_len ? max_len : L);
@@ -753,9 +811,10 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* S, int B, int g) {
   return lo;
 }
 
-// Exclusive prefix sums of T_b into S[0..B] by one wave.
+// Exclusive prefix sums of T_b into S[0..B], and the clamped context
+// lengths into Ls[0..B), by one wave.
 __device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_len, int32_t* S,
-                                            int lane) {
+                                            int32_t* Ls, int lane) {
   const int per = (B + kWave - 1) / kWave;
   const int b0 = min(B, lane * per), b1 = min(B, b0 + per);
   int part = 0;
@@ -768,185 +827,335 @@ __device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_
   }
   int run = incl - part;
   for (int b = b0; b < b1; ++b) {
+    const int L = clamp_len(lens[b], max_len);
     S[b] = run;
-    run += (clamp_len(lens[b], max_len) + kTile - 1) / kTile;
+    Ls[b] = L;
+    run += (L + kTile - 1) / kTile;
   }
   if (lane == kWave - 1) S[B] = incl;
 }
 
-// Tiles are taken in chunks of up to kStreamChunk consecutive tiles of one
-// sequence: the chunk's K rows sit in LDS and its V rows in registers while
-// the next chunk is being fetched, so each wave keeps up to
-// kStreamChunk * 8 KiB in flight during its compute.
+// A value every lane of the wave holds alike, moved to a scalar register.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Tile ranges: range r starts at tile r*T/W; tile g lies in range owner(g).
+__device__ __forceinline__ int range_start(int64_t r, int T, int W) {
+  return static_cast<int>((r * T) / W);
+}
+__device__ __forceinline__ int range_owner(int g, int T, int W) {
+  return static_cast<int>((static_cast<int64_t>(g + 1) * W - 1) / T);
+}
+
+// Buffer-resource loads of one 16-row tile (16-bit, D = 128: rows of 256
+// bytes).  The resource covers only the tile's first `nvalid` rows, so the
+// hardware range check returns zeros for the rows past the context instead
+// of whatever the block's unused tail holds; every lane's offset is then a
+// constant of its lane, with the tile base in scalar registers.
+constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer, 32-bit data format
+constexpr int kCacheNT = 2;              // non-temporal cache policy
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* tile, int nvalid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(tile), static_cast<short>(0),
+                                           nvalid * 256, kRsrcWord3);
+}
+
+// K rows into LDS, swizzled as issue_k_rows lays them out: lane l of
+// instruction rr fetches chunk ((l % 16) ^ row) of row 4 rr + l / 16.
+__device__ __forceinline__ void issue_k_rows_buf(const char* ktile, uint4* sk, int nvalid, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(ktile, nvalid);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int row = 4 * rr + g4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sk + rr * 64), 16,
+                                             row * 256 + ((c16 ^ row) << 4), 0, 0, 0);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// V rows as the P.V lanes hold them: lane (g4, c16) takes chunk c16 of rows
+// 4 g4 .. 4 g4 + 3 (each instruction reads four whole rows).
+template <int DT>
+__device__ __forceinline__ void load_v_buf(VTile<DT, 128>& t, const char* vtile, int nvalid, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = tile_rsrc(vtile, nvalid);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, (4 * g4 + r) * 256 + (c16 << 4), 0, kCacheNT);
+    t.v[r].w[0] = v.x; t.v[r].w[1] = v.y; t.v[r].w[2] = v.z; t.v[r].w[3] = v.w;
+  }
+}
+
+// A chunk's K rows sit in LDS and its V rows in registers while the next
+// chunk is being fetched, so each wave keeps up to kStreamChunk * 8 KiB in
+// flight during its compute.
 constexpr int kStreamChunk = 2;
 
-template <int DT, int GP>
-__global__ void __launch_bounds__(kWave * kStreamMaxHeads, 2)
+// s_waitcnt immediates (gfx9 encoding): wait for every vector memory
+// operation, or for every LDS operation, the other counters left alone.
+constexpr int kWaitVm0 = 0x0f70;
+constexpr int kWaitLgkm0 = 0xc07f;
+
+template <int DT, int GP, bool PAIRED>
+__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
 attn_stream_kernel(StreamArgs a) {
   constexpr int D = 128;
   constexpr int CH = kStreamChunk;
   using F = Frag<DT, D>;
   static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
-  // dynamic LDS: [K staging: H_kv waves x CH tiles x 4 KiB][S: B + 1][tbl: range_cap]
+  // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
+  //              [tbl: cap][cstart: cap + 1][cseq: cap][kr: R + 1][claim: R * H_kv]
   extern __shared__ uint4 sh_stream[];
-  const int wave = threadIdx.x >> 6;
+  const int wave = uni(threadIdx.x >> 6);    // wave-uniform: keeps all per-job values scalar
   const int lane = threadIdx.x & (kWave - 1);
   const int g4 = lane >> 4, c16 = lane & 15;
+  const int nwaves = blockDim.x >> 6;
   const int B = a.num_seqs;
+  const int R = a.ranges_per_wg;
+  const int H = a.hkv;
+  const int J = R * H;
+  const int cap = a.range_cap;
   uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * 256;
-  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(a.hkv) * CH * 256);
-  int32_t* tbl = S + B + 1;
-  if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, lane);
+  uint4* sq = sh_stream + static_cast<int64_t>(nwaves) * CH * 256 + static_cast<int64_t>(wave) * 256;
+  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(nwaves) * (CH + 1) * 256);
+  int32_t* Ls = S + B + 1;
+  int32_t* tbl = Ls + B;
+  int32_t* cstart = tbl + cap;
+  int32_t* cseq = cstart + cap + 1;
+  int32_t* kr = cseq + cap;
+  uint32_t* claim = reinterpret_cast<uint32_t*>(kr + R + 1);
+  if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, Ls, lane);
   __syncthreads();
   const int T = S[B];
-  const int W = gridDim.x;
-  const int g0 = static_cast<int>((static_cast<int64_t>(blockIdx.x) * T) / W);
-  const int g1 = static_cast<int>((static_cast<int64_t>(blockIdx.x + 1) * T) / W);
-  if (g0 >= g1) return;                // whole workgroup: empty range
+  const int W = a.num_ranges;
+  const int64_t r_base = static_cast<int64_t>(blockIdx.x) * R;
+  // the workgroup's tiles [w0, w1): ranges r_base .. r_base + R - 1
+  const int w0 = range_start(r_base, T, W);
+  const int w1 = range_start(r_base + R, T, W);
+  if (w0 >= w1) return;                // whole workgroup: empty ranges
   const int bs = a.block_size;
-  for (int t = threadIdx.x; t < g1 - g0; t += blockDim.x) {
-    const int g = g0 + t;
+  for (int t = threadIdx.x; t < w1 - w0; t += blockDim.x) {
+    const int g = w0 + t;
     const int b = seq_of_tile(S, B, g);
     const int lb = ((g - S[b]) * kTile) / bs;
     int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
     tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
   }
+  if (static_cast<int>(threadIdx.x) < J) claim[threadIdx.x] = 0u;
+  if (wave == nwaves - 1) {
+    // Chunk list: a chunk starts at every range start and sequence start and
+    // every CH tiles after either; cstart[k] is the first tile of chunk k
+    // and cseq[k] its sequence, cstart[nc] = w1, kr[r] the first chunk of
+    // range r_base + r.
+    int nc = 0;
+    for (int t0 = w0; t0 < w1; t0 += kWave) {
+      const int t = t0 + lane;
+      bool first = false;
+      int b = 0;
+      if (t < w1) {
+        b = seq_of_tile(S, B, t);
+        const int from = max(S[b], range_start(range_owner(t, T, W), T, W));
+        first = ((t - from) % CH) == 0;
+      }
+      const uint64_t m = __builtin_amdgcn_ballot_w64(first);
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+      if (first) {
+        cstart[nc + below] = t;
+        cseq[nc + below] = b;
+      }
+      nc += __builtin_popcountll(m);
+    }
+    if (lane == 0) cstart[nc] = w1;
+    if (lane <= R) {
+      // first chunk starting at or after the range's first tile
+      const int rs = range_start(r_base + lane, T, W);
+      int lo = 0, hi = nc;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (cstart[mid] < rs) lo = mid + 1; else hi = mid;
+      }
+      kr[lane] = lo;
+    }
+  }
   __syncthreads();
 
-  const int kvh = wave;
   const int G = a.group;
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
-  const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
-  // byte offset of tile g of sequence b (inside the workgroup's range)
-  auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
-    const int ti = g - S[b_of_g];
-    const int off = (ti * kTile) % bs;
-    return (static_cast<int64_t>(tbl[g - g0]) * a.block_stride + head_off +
-            static_cast<int64_t>(off) * D) * 2;
-  };
-  auto load_q = [&](Dw<F::kDwK>& qf, int b) {
-    const int head = c16 < G ? c16 : 0;
-    const char* qrow = static_cast<const char*>(a.q) +
-                       ((static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(kvh) * G + head) * D) * 2;
+  // PAIRED: nwaves == 2 * J, one task per wave; else nwaves == J, two.
+  constexpr int ntasks = PAIRED ? 1 : 2;
+  for (int task = 0; task < ntasks; ++task) {
+    const int job = PAIRED ? (wave % J) : (task == 0 ? wave : (wave + 4) % J);
+    const bool back = PAIRED ? (wave >= J) : (task == 1);
+    const int r = job / H;
+    const int kvh = job - r * H;
+    const int64_t rng = r_base + r;
+    const int g0 = range_start(rng, T, W);
+    const int g1 = range_start(rng + 1, T, W);
+    const int k0 = uni(kr[r]), k1 = uni(kr[r + 1]);
+    const int nc = k1 - k0;
+    const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
+    int nf = 0;                           // chunks this front worker claimed
+    // One claim (one lane's LDS atomic for the wave): the chunk index, or
+    // -1 once the two workers have met.
+    auto claim_next = [&]() -> int {
+      uint32_t old = 0;
+      if (lane == 0) old = atomicAdd(&claim[job], back ? 0x10000u : 1u);
+      old = __builtin_amdgcn_readfirstlane(old);
+      const int f = static_cast<int>(old & 0xffffu), bk = static_cast<int>(old >> 16);
+      if (f + bk >= nc) return -1;
+      if (!back) ++nf;
+      return back ? k1 - 1 - bk : k0 + f;
+    };
+    // byte offset of tile g of sequence b (inside the workgroup's tiles)
+    auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
+      const int ti = g - uni(S[b_of_g]);
+      const int off = (ti * kTile) % bs;
+      return (static_cast<int64_t>(uni(tbl[g - w0])) * a.block_stride + head_off +
+              static_cast<int64_t>(off) * D) * 2;
+    };
+    // The query group of sequence b, as the MFMA B operand, into the wave's
+    // LDS slot by DMA: instruction kk gives lane (g4, c16) head-dims
+    // 32 kk + 8 g4 .. + 7 of head c16.  Lanes of the padding heads
+    // (c16 >= G) take a copy of the group's first head: their scores track
+    // that head's exactly (so they never cause an extra rescale) and are
+    // never written.  Kept in LDS, the operand costs no registers while the
+    // P.V products run.
+    auto load_q = [&](int b) {
+      const int head = c16 < G ? c16 : 0;
+      const char* qgrp = static_cast<const char*>(a.q) +
+                         (static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(kvh) * G) * D * 2;
+      asm volatile("" ::: "memory");
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      Dw<4> x = load_dw<4>(qrow + (32 * kk + 8 * g4) * 2);
+      for (int kk = 0; kk < D / 32; ++kk)
+        __builtin_amdgcn_global_load_lds((global_void*)(qgrp + (head * D + 32 * kk + 8 * g4) * 2),
+                                         (lds_void*)(sq + kk * 64), 16, 0, 0);
+      asm volatile("" ::: "memory");
+    };
+    auto read_q = [&]() {
+      Dw<F::kDwK> qf;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf.w[4 * kk + e] = (c16 < G) ? x.w[e] : 0u;
-    }
-  };
-  auto nvalid_at = [&](int g, int s0, int L) { return min(kTile, L - kTile * (g - s0)); };
-  // tiles in the chunk starting at g of a sequence ending before tile s_end
-  auto chunk_len = [&](int g, int s_end) { return min(CH, min(g1, s_end) - g); };
-
-  // current chunk: tiles [cg, cg + cn) of sequence bc, whose tiles are [sc0, sc1)
-  int bc = seq_of_tile(S, B, g0);
-  int sc0 = S[bc], sc1 = S[bc + 1];
-  int Lc = clamp_len(a.lens[bc], a.max_len);
-  int seg0 = g0;                              // first tile of the current segment
-  int cg = g0, cn = chunk_len(g0, sc1);
-  Dw<F::kDwK> qf;
-  load_q(qf, bc);
-  float m = -INFINITY, l = 0.f;
-  float acc[GP][F::kW];
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
-
-  VTile<DT, D> vcur[CH], vnext[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    if (j < cn) {
-      const int64_t e = tile_bytes(cg + j, bc);
-      const int nv = nvalid_at(cg + j, sc0, Lc);
-      issue_k_rows<DT, D>(kc + e, sk + j * 256, nv, lane);
-      load_v<DT, D>(vcur[j], vc + e, nv, lane);
-    }
-  }
-  // Per chunk: scores of its tiles from the K rows in LDS; then the fetch of
-  // the next chunk and, when that chunk opens the next sequence, its query
-  // group straight into qf (this chunk's scores no longer need it); then
-  // softmax + P.V of the chunk's tiles; then the segment end if the chunk
-  // closes one.
-  while (cg < g1) {
-    f32x4 scr[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // LDS reads done before the buffers are refilled
-    const int ng = cg + cn;
-    int bn = bc, sn0 = sc0, sn1 = sc1, Ln = Lc, nn = 0;
-    if (ng < g1) {
-      if (ng >= sc1) {
-        bn = seq_of_tile(S, B, ng);
-        sn0 = S[bn];
-        sn1 = S[bn + 1];
-        Ln = clamp_len(a.lens[bn], a.max_len);
-        load_q(qf, bn);
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const uint4 x = sq[kk * 64 + lane];
+        qf.w[4 * kk] = x.x; qf.w[4 * kk + 1] = x.y; qf.w[4 * kk + 2] = x.z; qf.w[4 * kk + 3] = x.w;
       }
-      nn = chunk_len(ng, sn1);
+      return qf;
+    };
+    auto nvalid_at = [&](int g, int b) { return min(kTile, uni(Ls[b]) - kTile * (g - uni(S[b]))); };
+    // K rows of the n tiles from g on of sequence b into LDS, V rows into
+    // `v`; the LDS reads for the addresses all come before the first DMA.
+    auto issue_chunk = [&](VTile<DT, D> (&v)[CH], int g, int n, int b) {
+      int64_t e[CH];
+      int nv[CH];
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
-        if (j < nn) {
-          const int64_t e = tile_bytes(ng + j, bn);
-          const int nv = nvalid_at(ng + j, sn0, Ln);
-          issue_k_rows<DT, D>(kc + e, sk + j * 256, nv, lane);
-          load_v<DT, D>(vnext[j], vc + e, nv, lane);
+        e[j] = j < n ? tile_bytes(g + j, b) : 0;
+        nv[j] = nvalid_at(g + j, b);
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (j < n) {
+          issue_k_rows_buf(kc + e[j], sk + j * 256, nv[j], lane);
+          load_v_buf<DT>(v[j], vc + e[j], nv[j], lane);
         }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-      if (j < cn)
-        softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cg + j, sc0, Lc), a.scale_log2, m, l, acc,
-                              lane);
-    const int last = cg + cn - 1;
-    if (last == g1 - 1 || last == sc1 - 1) {
-      const bool complete = (seg0 == sc0) && (last == sc1 - 1);
-      const int slot = (seg0 == g0) ? 0 : 1;
-      wave_epilogue<DT, D, GP>(m, l, acc, lane, G, complete, a.out, a.out_dtype,
-                               static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G,
-                               a.ws_acc, a.ws_ml,
-                               (static_cast<int64_t>(blockIdx.x) * 2 + slot) * a.hq +
-                                   static_cast<int64_t>(kvh) * G,
-                               1);
-      bc = bn;
-      sc0 = sn0;
-      sc1 = sn1;
-      Lc = Ln;
-      seg0 = ng;
-      m = -INFINITY;
-      l = 0.f;
+    };
+
+    int cur = claim_next();
+    if (cur >= 0) {
+      // current chunk: tiles [cs, cs + cn) of sequence bc
+      int cs = uni(cstart[cur]);
+      int cn = uni(cstart[cur + 1]) - cs;
+      int bc = uni(cseq[cur]);
+      load_q(bc);
+      VTile<DT, D> vcur[CH], vnext[CH];
+      issue_chunk(vcur, cs, cn, bc);
+      int seg_lo = cs, seg_hi = cs + cn;    // tiles of the current segment
+      float m = -INFINITY, l = 0.f;
+      float acc[GP][F::kW];
 #pragma unroll
       for (int h = 0; h < GP; ++h)
 #pragma unroll
         for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
-    }
+      // Per chunk: wait for its DMA (and its query group); scores from the K
+      // rows in LDS; then the next chunk's fetch (V into `vnext`) and, when
+      // that chunk is in another sequence, its query group straight into qf;
+      // then the claim after it; then softmax + P.V of this chunk; then the
+      // segment end if the next chunk leaves this sequence.
+      while (true) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        f32x4 scr[CH];
+        {
+          const Dw<F::kDwK> qf = read_q();
 #pragma unroll
-    for (int j = 0; j < CH; ++j) vcur[j] = vnext[j];
-    cg = ng;
-    cn = nn;
+          for (int j = 0; j < CH; ++j)
+            if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
+        }
+        const int nxt = claim_next();
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS reads done before the buffer is refilled
+        int ns = 0, nn = 0, bn = -1;
+        if (nxt >= 0) {
+          ns = uni(cstart[nxt]);
+          nn = uni(cstart[nxt + 1]) - ns;
+          bn = uni(cseq[nxt]);
+          issue_chunk(vnext, ns, nn, bn);
+          if (bn != bc) load_q(bn);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          if (j < cn)
+            softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+        if (bn != bc) {
+          const bool complete = seg_lo == uni(S[bc]) && seg_hi == uni(S[bc + 1]);
+          const int slot = back ? (seg_hi == g1 ? 2 : 3) : (seg_lo == g0 ? 0 : 1);
+          wave_epilogue<DT, D, GP>(m, l, acc, lane, G, complete, a.out, a.out_dtype,
+                                   static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G,
+                                   a.ws_acc, a.ws_ml,
+                                   (rng * kStreamSlots + slot) * a.hq + static_cast<int64_t>(kvh) * G, 1);
+          m = -INFINITY;
+          l = 0.f;
+#pragma unroll
+          for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+          seg_lo = ns;
+          seg_hi = ns + nn;
+        } else if (back) {
+          seg_lo = ns;
+        } else {
+          seg_hi = ns + nn;
+        }
+        if (nxt < 0) break;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) vcur[j] = vnext[j];
+        cs = ns;
+        cn = nn;
+        bc = bn;
+      }
+    }
+    if (!back && lane == 0)
+      a.ws_x[rng * H + kvh] = nf == nc ? g1 : uni(cstart[k0 + nf]);
   }
 }
 
 // Merge of the stream kernel's partials.  One 64-lane workgroup per
 // (sequence, query head).  A sequence with L = 0 gets zeros; one that a
-// single workgroup covered was finished already; otherwise its pieces are
-// combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// The pieces of sequence b are the non-empty ranges over its tiles: with at
-// least as many tiles as workgroups every range is non-empty and the pieces
-// are the consecutive workgroups w_first .. w_last; with fewer tiles each
-// non-empty range holds exactly one tile and piece j is the owner of tile
-// S_b + j.
+// single segment covered was finished already; otherwise its pieces are
+// combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The
+// pieces of sequence b are, in every range that holds some of its tiles,
+// the part before the range's meeting point x (front worker) and the part
+// from x on (back worker), where not empty.
 template <int D>
 __global__ void __launch_bounds__(kWave)
 attn_stream_merge_kernel(StreamArgs a) {
+  __shared__ int32_t plist[2 * kStreamMaxRanges];
   const int lane = threadIdx.x;
   const int qh = blockIdx.x % a.hq;
   const int b = blockIdx.x / a.hq;
-  const int W = a.num_wgs;
+  const int kvh = qh / a.group;
+  const int W = a.num_ranges;
   int before = 0, total = 0;
   for (int j = lane; j < a.num_seqs; j += kWave) {
     const int t = (clamp_len(a.lens[j], a.max_len) + kTile - 1) / kTile;
@@ -970,21 +1179,37 @@ attn_stream_merge_kernel(StreamArgs a) {
     }
     return;
   }
-  const int Tb = (L + kTile - 1) / kTile;
-  auto owner = [&](int g) {
-    return static_cast<int>((static_cast<int64_t>(g + 1) * W - 1) / total);
-  };
-  const int w_first = owner(before);
-  const int w_last = owner(before + Tb - 1);
-  if (w_first == w_last) return;
-  const bool dense = total >= W;
-  const int npieces = dense ? (w_last - w_first + 1) : Tb;
-  const int g0_first = static_cast<int>((static_cast<int64_t>(w_first) * total) / W);
-  const int first_slot = (g0_first < before) ? 1 : 0;
-  auto slot_of = [&](int j) -> int64_t {
-    const int w = dense ? (w_first + j) : owner(before + j);
-    return (static_cast<int64_t>(w) * 2 + (j == 0 ? first_slot : 0)) * a.hq + qh;
-  };
+  const int Sb = before, Se = before + (L + kTile - 1) / kTile;
+  const int r_first = range_owner(Sb, total, W);
+  const int r_last = range_owner(Se - 1, total, W);
+  // Piece list: lane i looks at ranges r_first + i, r_first + i + 64, ...
+  int npieces = 0;
+  for (int r0 = r_first; r0 <= r_last; r0 += kWave) {
+    const int r = r0 + lane;
+    int sl[2];
+    int n = 0;
+    if (r <= r_last) {
+      const int g0 = range_start(r, total, W), g1 = range_start(r + 1, total, W);
+      if (g0 < g1) {
+        const int x = a.ws_x[static_cast<int64_t>(r) * a.hkv + kvh];
+        const int lo = max(g0, Sb), hi = min(g1, Se);
+        if (lo < min(x, hi)) sl[n++] = r * kStreamSlots + (lo == g0 ? 0 : 1);
+        if (max(x, lo) < hi) sl[n++] = r * kStreamSlots + (hi == g1 ? 2 : 3);
+      }
+    }
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int at = npieces + incl - n;
+    if (n > 0) plist[at] = sl[0];
+    if (n > 1) plist[at + 1] = sl[1];
+    npieces += __shfl(incl, kWave - 1);
+  }
+  __syncthreads();
+  if (npieces <= 1) return;            // one segment covered the sequence
   // Pieces in chunks of 8: every lane loads each piece's (m, l) and its own
   // accumulator slice, all loads of a chunk in flight together, then folds
   // the chunk into a running (M, den, num) with one rescale.
@@ -998,7 +1223,7 @@ attn_stream_merge_kernel(StreamArgs a) {
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       const int j = min(j0 + u, npieces - 1);
-      const int64_t sl = slot_of(j);
+      const int64_t sl = static_cast<int64_t>(plist[j]) * a.hq + qh;
       const float2 ml2 = *reinterpret_cast<const float2*>(a.ws_ml + 2 * sl);
       mp[u] = (j0 + u < npieces) ? ml2.x : -INFINITY;
       lp[u] = ml2.y;
@@ -1034,8 +1259,22 @@ attn_stream_merge_kernel(StreamArgs a) {
 
 // ------------------------------------------------------------ dispatch
 constexpr int kDefaultPartition = 512;
-constexpr int kStreamWavesPerCu = 8;      // stream kernel: resident waves per CU aimed at
-constexpr size_t kStreamDynLdsMax = 65536;
+
+int device_attr_cached(hipDeviceAttribute_t attr, int (&cache)[64], int fallback) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fallback;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess || n <= 0) n = fallback;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+// LDS one workgroup may allocate (160 KiB on gfx950).
+size_t device_lds_per_block() {
+  static int cached[64] = {0};
+  return static_cast<size_t>(device_attr_cached(hipDeviceAttributeMaxSharedMemoryPerBlock, cached, 65536));
+}
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -1053,9 +1292,14 @@ int device_cu_count() {
 // it covers (the partition kernel then runs with the default partition).
 struct StreamPlan {
   bool ok = false;
-  int wgs = 0;
+  int wgs = 0;            // workgroups, one per CU
+  int waves = 0;          // per workgroup
+  int ranges_per_wg = 0;  // R
+  int ranges = 0;         // W = wgs * R
   int range_cap = 0;
   size_t dyn_lds = 0;
+  size_t acc_floats = 0;  // workspace: accumulators, then (m, l), then meeting points
+  size_t ml_floats = 0;
   size_t workspace = 0;
 };
 
@@ -1065,19 +1309,32 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (head_dim != 128 || num_kv_heads > kStreamMaxHeads || num_kv_heads <= 0) return pl;
   if (num_q_heads % num_kv_heads != 0 || num_q_heads / num_kv_heads > 8) return pl;
   if (dtype_or_neg == PKV_F32) return pl;
-  const int per_cu = kStreamWavesPerCu / num_kv_heads > 0 ? kStreamWavesPerCu / num_kv_heads : 1;
-  const int64_t wgs = static_cast<int64_t>(device_cu_count()) * per_cu;
+  // two waves per job when they fit in kStreamMaxWaves, else one wave per
+  // job that also works the back of another job
+  const int R = 2 * num_kv_heads <= kStreamMaxWaves ? kStreamMaxWaves / (2 * num_kv_heads) : 1;
+  const int waves = 2 * num_kv_heads <= kStreamMaxWaves ? 2 * R * num_kv_heads : num_kv_heads;
+  const int64_t wgs = device_cu_count();
+  const int64_t ranges = wgs * R;
+  if (ranges > kStreamMaxRanges) return pl;
   const int64_t tiles_max = static_cast<int64_t>(num_seqs) * ((max_context_len + kTile - 1) / kTile);
   if (tiles_max >= (1LL << 30)) return pl;
   const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
-  const size_t dyn = static_cast<size_t>(num_kv_heads) * kStreamChunk * 4096 +
-                     static_cast<size_t>(num_seqs + 1 + cap) * sizeof(int32_t);
-  if (dyn > kStreamDynLdsMax) return pl;
+  if (cap > 32767) return pl;          // claim counters are 16-bit
+  const size_t dyn = static_cast<size_t>(waves) * (kStreamChunk + 1) * 4096 +
+                     static_cast<size_t>(2 * num_seqs + 1 + 3 * cap + 1 + R + 1 + R * num_kv_heads) *
+                         sizeof(int32_t);
+  if (dyn > device_lds_per_block()) return pl;
   pl.ok = true;
   pl.wgs = static_cast<int>(wgs);
+  pl.waves = waves;
+  pl.ranges_per_wg = R;
+  pl.ranges = static_cast<int>(ranges);
   pl.range_cap = static_cast<int>(cap);
   pl.dyn_lds = dyn;
-  pl.workspace = static_cast<size_t>(wgs) * 2 * num_q_heads * (head_dim + 2) * sizeof(float);
+  pl.acc_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * head_dim;
+  pl.ml_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * 2;
+  pl.workspace = (pl.acc_floats + pl.ml_floats) * sizeof(float) +
+                 static_cast<size_t>(ranges) * num_kv_heads * sizeof(int32_t);
   return pl;
 }
 
@@ -1119,11 +1376,31 @@ hipError_t launch_split_d(const AttnArgs& a, int gp, dim3 grid, hipStream_t s) {
   }
 }
 
+template <int DT, int GP, bool PAIRED>
+hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, hipStream_t s) {
+  // Raise the kernel's dynamic-LDS limit to what this launch asks for
+  // (plan_stream already checked it against the device's per-block LDS),
+  // once per device and size.
+  static std::atomic<int> raised[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::atomic<int>& done = raised[dev & 63];
+  if (pl.dyn_lds > 65536 && static_cast<int>(pl.dyn_lds) > done.load()) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DT, GP, PAIRED>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(pl.dyn_lds));
+    if (e != hipSuccess) return e;
+    done.store(static_cast<int>(pl.dyn_lds));
+  }
+  hipLaunchKernelGGL((attn_stream_kernel<DT, GP, PAIRED>), dim3(static_cast<uint32_t>(pl.wgs)),
+                     dim3(kWave * pl.waves), pl.dyn_lds, s, a);
+  return hipGetLastError();
+}
+
 template <int DT, int GP>
 hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, hipStream_t s) {
-  hipLaunchKernelGGL((attn_stream_kernel<DT, GP>), dim3(static_cast<uint32_t>(pl.wgs)),
-                     dim3(kWave * a.hkv), pl.dyn_lds, s, a);
-  return hipGetLastError();
+  return pl.waves == 2 * pl.ranges_per_wg * a.hkv ? launch_stream_p<DT, GP, true>(a, pl, s)
+                                                  : launch_stream_p<DT, GP, false>(a, pl, s);
 }
 
 template <int DT>
@@ -1328,9 +1605,9 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.vc = value_cache;
       sa.tables = block_tables;
       sa.lens = context_lens;
-      const int64_t acc_floats = static_cast<int64_t>(pl.wgs) * 2 * num_q_heads * l->head_dim;
       sa.ws_acc = static_cast<float*>(workspace);
-      sa.ws_ml = static_cast<float*>(workspace) + acc_floats;
+      sa.ws_ml = sa.ws_acc + pl.acc_floats;
+      sa.ws_x = reinterpret_cast<int32_t*>(sa.ws_ml + pl.ml_floats);
       sa.out = out;
       sa.block_stride = l->block_stride;
       sa.head_stride = l->head_stride;
@@ -1344,7 +1621,8 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.max_len = max_context_len;
       sa.out_dtype = out_dtype;
       sa.range_cap = pl.range_cap;
-      sa.num_wgs = pl.wgs;
+      sa.num_ranges = pl.ranges;
+      sa.ranges_per_wg = pl.ranges_per_wg;
       sa.scale_log2 = scale * kLog2e;
       if (phases & kPhasePartial) {
         const int gp = padded_group(group);
