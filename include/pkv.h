@@ -223,11 +223,16 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
 
 /* -------------------------------------------------------- decode attention */
 /*
- * Workspace bytes paged_decode_attention needs for split-K partial results:
- * num_seqs * num_q_heads * P * (head_dim + 2) * 4, P = ceil(max_context_len /
- * partition_tokens) (0 when P <= 1).  partition_tokens == 0 selects the
- * library default (the same value paged_decode_attention picks for the same
- * arguments).  Returns 0 for invalid arguments as well.
+ * Workspace bytes paged_decode_attention needs for the path it takes with
+ * these arguments (see paged_decode_attention_path).  Partition path:
+ * num_seqs * num_q_heads * P * (head_dim + 2) * 4 bytes of split-K partials,
+ * P = ceil(max_context_len / partition_tokens) (0 when P <= 1; a
+ * partition_tokens of 0 that cannot take the stream path means 512).  Stream
+ * path (partition_tokens == 0): W * 4 * num_q_heads * (head_dim + 2) * 4
+ * bytes of partials and W * num_kv_heads meeting tiles, with
+ * W = CUs * max(1, 4 / num_kv_heads) tile ranges (integer division; 256 CUs
+ * on MI355X).  The contents need no initialisation.  Returns 0 for invalid
+ * arguments as well.
  */
 size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,
@@ -258,7 +263,7 @@ size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_hea
  *   workspace    device, >= paged_decode_attention_workspace_size(...)
  *                bytes (may be NULL when that size is 0)
  * Supported: block_size a multiple of 16, head_dim in {64, 128},
- * H_q % H_kv == 0 with H_q / H_kv <= 16.  Softmax state and all sums are
+ * H_q % H_kv == 0 with H_q / H_kv <= 8.  Softmax state and all sums are
  * fp32.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
  */
 int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
@@ -271,9 +276,10 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
 
 /*
  * Which attention kernel paged_decode_attention runs for these arguments:
- * PKV_PATH_STREAM (1): one workgroup per equal share of all tiles of the
- * launch, all KV heads of a tile together (16-bit KV, head_dim 128,
- * H_kv <= 8, H_q / H_kv <= 8, partition_tokens == 0); PKV_PATH_PARTITION (2):
+ * PKV_PATH_STREAM (1): the launch's 16-token tiles cut into equal ranges,
+ * one workgroup per CU, each (range, KV head) shared by two waves that
+ * claim chunks from its two ends (16-bit KV, head_dim 128, H_kv <= 8,
+ * H_q / H_kv <= 8, partition_tokens == 0); PKV_PATH_PARTITION (2):
  * one workgroup per (sequence, KV head, context partition of
  * partition_tokens tokens, default 512).  Negative status on invalid
  * arguments.  Host-only; the workspace size matches the path.
@@ -286,11 +292,11 @@ int paged_decode_attention_path(int32_t num_seqs, int32_t num_q_heads, int32_t m
 /*
  * The two launches of paged_decode_attention, callable separately with the
  * same arguments (for instance to time or overlap them): _partial runs the
- * partition kernel, which finishes every sequence that fits in one partition
- * and leaves (max, sum, accumulator) partials in `workspace` for the others;
- * _merge then reduces those partials into `out` (a no-op when no sequence
- * spans two partitions).  The pair, in this order on one stream, equals one
- * paged_decode_attention call.
+ * attention kernel (stream or partition path), which finishes every
+ * sequence one segment covers and leaves (max, sum, accumulator) partials in
+ * `workspace` for the others; _merge then reduces those partials into `out`.
+ * The pair, in this order on one stream, equals one paged_decode_attention
+ * call.
  */
 int paged_decode_attention_partial(void* out, int32_t out_dtype, const void* q,
                                    const void* key_cache, const void* value_cache,
