@@ -229,7 +229,7 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
  * P = ceil(max_context_len / partition_tokens) (0 when P <= 1; a
  * partition_tokens of 0 that cannot take the stream path means 512).  Stream
  * path (partition_tokens == 0): W * 4 * num_q_heads * (head_dim + 2) * 4
- * bytes of partials and W * num_kv_heads meeting tiles, with
+ * bytes of partials and W * num_kv_heads split tiles, with
  * W = CUs * max(1, 4 / num_kv_heads) tile ranges (integer division; 256 CUs
  * on MI355X).  The contents need no initialisation.  Returns 0 for invalid
  * arguments as well.
@@ -278,7 +278,7 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
  * Which attention kernel paged_decode_attention runs for these arguments:
  * PKV_PATH_STREAM (1): the launch's 16-token tiles cut into equal ranges,
  * one workgroup per CU, each (range, KV head) shared by two waves that
- * claim chunks from its two ends (16-bit KV, head_dim 128, H_kv <= 8,
+ * split its chunks at a fixed point (16-bit KV, head_dim 128, H_kv <= 8,
  * H_q / H_kv <= 8, partition_tokens == 0); PKV_PATH_PARTITION (2):
  * one workgroup per (sequence, KV head, context partition of
  * partition_tokens tokens, default 512).  Negative status on invalid

@@ -746,24 +746,24 @@ attn_reduce_kernel(AttnArgs a) {
 // context lengths.  One workgroup per CU holds R consecutive ranges.  A job
 // is one (range, KV head); its tiles are cut into chunks of up to
 // kStreamChunk tiles of one sequence, and two waves share the job: the
-// front worker claims chunks from the start of the range, the back worker
-// from its end, one LDS atomic per claim, until the claims meet.  The two
-// waves on one SIMD do not progress at the same rate (the one in the
-// second wave slot runs markedly slower under this load), so the meeting
-// point, not a fixed split, decides who reads what.  When every KV head has
-// two waves (2 * R * H_kv <= 8) each job has its own pair; otherwise
-// (H_kv > 4) each wave is the front worker of job j and then the back
-// worker of job (j + 4) mod H_kv.
+// front worker takes the chunks before a split point, the back worker the
+// rest.  The two waves on one SIMD do not progress at the same rate (the
+// one in the second wave slot runs markedly slower under this load), so the
+// split gives the slot-0 wave the larger share (job_split).  The split is
+// fixed, so results are bitwise reproducible.  When every KV head has two
+// waves (2 * R * H_kv <= 8) each job has its own pair; otherwise (H_kv > 4)
+// each wave is the front worker of job j and then the back worker of job
+// (j + 4) mod H_kv.
 //
 // Every maximal run of one worker's chunks in one sequence is a segment; a
 // segment that covers its whole sequence writes the normalised output,
 // other segments leave a (max, sum, accumulator) partial in one of four
 // slots of their job: 0 = the front worker's segment starting at the range
-// start, 1 = its segment ending at the meeting point, 2 = the back worker's
-// segment ending at the range end, 3 = its segment starting at the meeting
-// point.  The front worker records the meeting point; the merge kernel
-// finds the pieces of each sequence from the range bounds and the meeting
-// points.  16-bit KV, D = 128, H_kv <= 8, G <= 8.
+// start, 1 = its segment ending at the split point, 2 = the back worker's
+// segment ending at the range end, 3 = its segment starting at the split
+// point.  The front worker records the split tile; the merge kernel finds
+// the pieces of each sequence from the range bounds and the split tiles.
+// 16-bit KV, D = 128, H_kv <= 8, G <= 8.
 struct StreamArgs {
   const void* q;
   const void* kc;
@@ -772,7 +772,7 @@ struct StreamArgs {
   const int32_t* lens;
   float* ws_acc;     // [W, 4, H_q, D]   (W = num_ranges)
   float* ws_ml;      // [W, 4, H_q, 2]
-  int32_t* ws_x;     // [W, H_kv] meeting tile of each job
+  int32_t* ws_x;     // [W, H_kv] split tile of each job
   void* out;
   int64_t block_stride;
   int64_t head_stride;
@@ -794,6 +794,25 @@ struct StreamArgs {
 constexpr int kStreamMaxHeads = 8;
 constexpr int kStreamMaxWaves = 8;
 constexpr int kStreamSlots = 4;          // partial slots per job
+// Percent of a job's chunks taken by the worker in SIMD wave slot 0 when its
+// partner is in slot 1: under this load the second slot's wave takes ~26%
+// longer per chunk (measured per wave with the real-time counter), and a
+// balanced pair splits about 56 : 44.
+constexpr int kSlot0Share = 56;
+
+// Where a job's nc chunks split between its two workers: the front worker
+// is wave `job` of the workgroup, the back worker wave J + job (two waves
+// per job) or the wave that runs job's back after its own front (one wave
+// per job).  Waves 0-3 sit in SIMD wave slot 0, waves 4-7 in slot 1; the
+// slot-0 worker takes kSlot0Share percent of the chunks when its partner is
+// in slot 1, else the split is even.
+template <bool PAIRED>
+__device__ __forceinline__ int job_split(int nc, int job, int J) {
+  const int fw = job;
+  const int bw = PAIRED ? J + job : (job + J - 4 % J) % J;
+  if ((fw >> 2) == (bw >> 2)) return (nc + 1) / 2;
+  return (fw >> 2) == 0 ? (nc * kSlot0Share + 50) / 100 : (nc * (100 - kSlot0Share) + 50) / 100;
+}
 constexpr int kStreamMaxRanges = 1024;   // W bound (merge kernel's piece list)
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
@@ -905,7 +924,7 @@ attn_stream_kernel(StreamArgs a) {
   using F = Frag<DT, D>;
   static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
   // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
-  //              [tbl: cap][cstart: cap + 1][cseq: cap][kr: R + 1][claim: R * H_kv]
+  //              [tbl: cap][cstart: cap + 1][cseq: cap][kr: R + 1]
   extern __shared__ uint4 sh_stream[];
   const int wave = uni(threadIdx.x >> 6);    // wave-uniform: keeps all per-job values scalar
   const int lane = threadIdx.x & (kWave - 1);
@@ -924,7 +943,6 @@ attn_stream_kernel(StreamArgs a) {
   int32_t* cstart = tbl + cap;
   int32_t* cseq = cstart + cap + 1;
   int32_t* kr = cseq + cap;
-  uint32_t* claim = reinterpret_cast<uint32_t*>(kr + R + 1);
   if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, Ls, lane);
   __syncthreads();
   const int T = S[B];
@@ -942,7 +960,6 @@ attn_stream_kernel(StreamArgs a) {
     int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
     tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
   }
-  if (static_cast<int>(threadIdx.x) < J) claim[threadIdx.x] = 0u;
   if (wave == nwaves - 1) {
     // Chunk list: a chunk starts at every range start and sequence start and
     // every CH tiles after either; cstart[k] is the first tile of chunk k
@@ -997,18 +1014,10 @@ attn_stream_kernel(StreamArgs a) {
     const int k0 = uni(kr[r]), k1 = uni(kr[r + 1]);
     const int nc = k1 - k0;
     const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
-    int nf = 0;                           // chunks this front worker claimed
-    // One claim (one lane's LDS atomic for the wave): the chunk index, or
-    // -1 once the two workers have met.
-    auto claim_next = [&]() -> int {
-      uint32_t old = 0;
-      if (lane == 0) old = atomicAdd(&claim[job], back ? 0x10000u : 1u);
-      old = __builtin_amdgcn_readfirstlane(old);
-      const int f = static_cast<int>(old & 0xffffu), bk = static_cast<int>(old >> 16);
-      if (f + bk >= nc) return -1;
-      if (!back) ++nf;
-      return back ? k1 - 1 - bk : k0 + f;
-    };
+    // The job's chunks [k0, k1) split at k0 + ks: the front worker takes
+    // those before, the back worker those from there on; both walk forward.
+    const int ks = job_split<PAIRED>(nc, job, J);
+    const int my0 = back ? k0 + ks : k0, my1 = back ? k1 : k0 + ks;
     // byte offset of tile g of sequence b (inside the workgroup's tiles)
     auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
       const int ti = g - uni(S[b_of_g]);
@@ -1063,12 +1072,12 @@ attn_stream_kernel(StreamArgs a) {
       }
     };
 
-    int cur = claim_next();
-    if (cur >= 0) {
-      // current chunk: tiles [cs, cs + cn) of sequence bc
-      int cs = uni(cstart[cur]);
-      int cn = uni(cstart[cur + 1]) - cs;
-      int bc = uni(cseq[cur]);
+    if (my0 < my1) {
+      // current chunk ck: tiles [cs, cs + cn) of sequence bc
+      int ck = my0;
+      int cs = uni(cstart[ck]);
+      int cn = uni(cstart[ck + 1]) - cs;
+      int bc = uni(cseq[ck]);
       load_q(bc);
       VTile<DT, D> vcur[CH], vnext[CH];
       issue_chunk(vcur, cs, cn, bc);
@@ -1081,9 +1090,9 @@ attn_stream_kernel(StreamArgs a) {
         for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
       // Per chunk: wait for its DMA (and its query group); scores from the K
       // rows in LDS; then the next chunk's fetch (V into `vnext`) and, when
-      // that chunk is in another sequence, its query group straight into qf;
-      // then the claim after it; then softmax + P.V of this chunk; then the
-      // segment end if the next chunk leaves this sequence.
+      // that chunk is in another sequence, its query group into LDS; then
+      // softmax + P.V of this chunk; then the segment end if the next chunk
+      // leaves this sequence.
       while (true) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         f32x4 scr[CH];
@@ -1093,7 +1102,7 @@ attn_stream_kernel(StreamArgs a) {
           for (int j = 0; j < CH; ++j)
             if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
         }
-        const int nxt = claim_next();
+        const int nxt = ck + 1 < my1 ? ck + 1 : -1;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS reads done before the buffer is refilled
         int ns = 0, nn = 0, bn = -1;
         if (nxt >= 0) {
@@ -1122,21 +1131,19 @@ attn_stream_kernel(StreamArgs a) {
             for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
           seg_lo = ns;
           seg_hi = ns + nn;
-        } else if (back) {
-          seg_lo = ns;
         } else {
           seg_hi = ns + nn;
         }
         if (nxt < 0) break;
 #pragma unroll
         for (int j = 0; j < CH; ++j) vcur[j] = vnext[j];
+        ck = nxt;
         cs = ns;
         cn = nn;
         bc = bn;
       }
     }
-    if (!back && lane == 0)
-      a.ws_x[rng * H + kvh] = nf == nc ? g1 : uni(cstart[k0 + nf]);
+    if (!back && lane == 0) a.ws_x[rng * H + kvh] = uni(cstart[k0 + ks]);
   }
 }
 
@@ -1145,7 +1152,7 @@ attn_stream_kernel(StreamArgs a) {
 // single segment covered was finished already; otherwise its pieces are
 // combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The
 // pieces of sequence b are, in every range that holds some of its tiles,
-// the part before the range's meeting point x (front worker) and the part
+// the part before the range's split tile x (front worker) and the part
 // from x on (back worker), where not empty.
 template <int D>
 __global__ void __launch_bounds__(kWave)
@@ -1298,7 +1305,7 @@ struct StreamPlan {
   int ranges = 0;         // W = wgs * R
   int range_cap = 0;
   size_t dyn_lds = 0;
-  size_t acc_floats = 0;  // workspace: accumulators, then (m, l), then meeting points
+  size_t acc_floats = 0;  // workspace: accumulators, then (m, l), then split tiles
   size_t ml_floats = 0;
   size_t workspace = 0;
 };
@@ -1319,9 +1326,8 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   const int64_t tiles_max = static_cast<int64_t>(num_seqs) * ((max_context_len + kTile - 1) / kTile);
   if (tiles_max >= (1LL << 30)) return pl;
   const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
-  if (cap > 32767) return pl;          // claim counters are 16-bit
   const size_t dyn = static_cast<size_t>(waves) * (kStreamChunk + 1) * 4096 +
-                     static_cast<size_t>(2 * num_seqs + 1 + 3 * cap + 1 + R + 1 + R * num_kv_heads) *
+                     static_cast<size_t>(2 * num_seqs + 1 + 3 * cap + 1 + R + 1) *
                          sizeof(int32_t);
   if (dyn > device_lds_per_block()) return pl;
   pl.ok = true;
