@@ -2,19 +2,23 @@
 """Benchmark of the paged KV cache decode hot path on one MI355X.
 
 One step = the whole hot path over one batch: host block-manager append for
-every sequence, metadata upload, block-table update, paged_kv_write of the
-new K/V rows, and paged decode attention (partition kernel + split-K merge)
-over the updated cache.  Default workload: the Qwen2-7B-shaped batch-64
-decode (H_q 28, H_kv 4, D 128, bf16, block_size 16, context lengths
-U[512, 8192], pool of 65,536 blocks fragmented by a seeded churn of 500
-prior sequences).  Inputs are seeded synthetic tensors (``synth``), resident
-in HBM before timing starts.
+every sequence, then the write of the new K/V rows (with the blocks the
+append opened published into the device block table) and paged decode
+attention over the updated cache.  With the stream attention path the write
+runs inside the attention launch (pkv_decode_step), followed by the split-K
+merge launch; ``--separate-write`` runs it as its own launch instead.
+Default workload: the Qwen2-7B-shaped batch-64 decode (H_q 28, H_kv 4,
+D 128, bf16, block_size 16, context lengths U[512, 8192], pool of 65,536
+blocks fragmented by a seeded churn of 500 prior sequences).  Inputs are
+seeded synthetic tensors (``synth``), resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is the KV bytes the steps' attention must
 read (sum over sequences of L * H_kv * 2 * D * elem_bytes) divided by the
-wall time of the timed steps.  ``roofline`` is for the attention partition
-kernel (the dominant kernel): KV bytes per launch over its mean duration
-from HIP events recorded on the launch stream during the timed steps.
+wall time of the timed steps.  ``roofline`` is for the step's first launch
+(the dominant kernel): its algorithmic bytes (the KV bytes read, plus the
+new rows written when the write runs inside it) over its mean duration from
+HIP events recorded on the launch stream around it on every fifth timed
+step.
 
     python bench.py [--steps K] [--warmup W] [--config NAME]
     python bench.py --calibrate-copy      # plain 1 GiB copy, for PMC scaling
@@ -134,6 +138,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="record the kernel-timing events on every n-th timed step")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="run the step's write as its own launch instead of inside the attention")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -199,10 +207,14 @@ def main():
     torch.cuda.synchronize()
     for s in range(args.warmup):
         k, v, q = ring[s % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out)
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=not args.separate_write)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Kernel timing: HIP events around the step's kernels on every
+    # --event-every-th timed step (each recorded event costs a few us of GPU
+    # time, so events on every step would slow the very steps being timed).
+    timed = [i for i in range(args.steps) if i % max(1, args.event_every) == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
     if torch.distributed.is_available() and torch.distributed.is_initialized():
         torch.distributed.barrier()
     torch.cuda.synchronize()
@@ -210,19 +222,21 @@ def main():
     for i in range(args.steps):
         s = args.warmup + i
         k, v, q = ring[s % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs[i])
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i), fused=not args.separate_write)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    split_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
+    merge_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in timed])
     step_bytes = np.array([kv_bytes(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
+    timed_bytes = step_bytes[timed]
     total_kv = float(step_bytes.sum())
     value = total_kv / wall / 1e9
     tokens_per_s = B * args.steps / wall
     split_avg_s = float(split_ms.mean()) / 1e3
-    achieved = float(step_bytes.mean()) / split_avg_s / 1e9
-    attn_gbps = float(step_bytes.mean()) / (float((split_ms + merge_ms).mean()) / 1e3) / 1e9
+    # the first launch of a step also writes the step's new K/V rows when fused
+    new_row_bytes = B * cfg.num_kv_heads * 2 * cfg.head_dim * elem
+    attn_gbps = float(timed_bytes.mean()) / (float((split_ms + merge_ms).mean()) / 1e3) / 1e9
     log(f"timed {args.steps} steps: {wall * 1e6 / args.steps:.1f} us/step, split kernel "
         f"{split_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us, "
         f"KV {step_bytes.mean() / 1e6:.1f} MB/step")
@@ -246,8 +260,14 @@ def main():
 
     import paged_kv_cache_128_amd as pkv
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
-    kernel_name = {"stream": "attn_stream_kernel", "partition": "attn_split_kernel"}[path]
+    # the engine's step: the write runs inside the stream launch (pkv_decode_step)
+    # when the stream path applies and the batch has at most 256 rows
+    fused = path == "stream" and B <= 256 and not args.separate_write
+    kernel_name = ("attn_stream_step_kernel" if fused else
+                   {"stream": "attn_stream_kernel", "partition": "attn_split_kernel"}[path])
     traffic, _ = recorded_traffic(kernel_name, cfg.name)
+    alg_bytes = float(timed_bytes.mean()) + (new_row_bytes if fused else 0)
+    achieved = alg_bytes / split_avg_s / 1e9
     result = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s",
         "value": round(value, 2),
@@ -291,7 +311,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "mean_launch_us": round(split_avg_s * 1e6, 3),
-            "algorithmic_bytes_per_launch": round(float(step_bytes.mean())),
+            "algorithmic_bytes_per_launch": round(alg_bytes),
         },
         "kernel_source_sha256_16": kernel_source_sha(),
     }

@@ -314,6 +314,52 @@ int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step after the host-side append ([MiniPaged-Qwen] §1.1: write
+ * the step's K/V, then attend over the whole context including it):
+ * exactly pkv_decode_write(key, value, slots, lens, num_seqs, key_cache,
+ * value_cache, layout, block_tables, num_seqs, block_table_stride, lens_out)
+ * followed by paged_decode_attention(out, out_dtype, q, key_cache,
+ * value_cache, block_tables, block_table_stride, lens_out, num_seqs,
+ * num_q_heads, max_context_len, scale, layout, 0, workspace, ...), with
+ * the same results bit for bit.  When the stream path applies, at most 256
+ * rows are given, every slots[i] lies in [0, num_blocks * bs) and every
+ * lens[i] in [1, max_context_len], the write runs inside the attention
+ * launch: the one wave per KV head that reads a sequence's last tile takes
+ * the new row from `key`/`value` and stores it into the pool, and the new
+ * lengths and opened blocks are published by the same launch.  Otherwise
+ * the two calls run one after the other.
+ *   key, value   device, [num_seqs, H_kv, D] contiguous, 16-byte aligned
+ *   slots, lens  host, the outputs of pkv_append_slots_for_decode in row
+ *                order (lens = context lengths after the append)
+ *   block_tables device, int32 [num_seqs, block_table_stride]; entries of
+ *                blocks the append opened are written
+ *   lens_out     device, int32 [num_seqs], receives lens
+ *   workspace    as for paged_decode_attention with partition_tokens 0
+ * Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int pkv_decode_step(void* out, int32_t out_dtype, const void* q, const void* key,
+                    const void* value, const int64_t* slots, const int32_t* lens,
+                    int32_t num_seqs, void* key_cache, void* value_cache,
+                    const pkv_cache_layout* layout, int32_t* block_tables,
+                    int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                    int32_t max_context_len, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * The first launch of pkv_decode_step alone (the write and the attention
+ * kernel, leaving partials of split sequences in `workspace`);
+ * paged_decode_attention_merge with context_lens = lens_out and the same
+ * other arguments completes it.
+ */
+int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const void* key,
+                            const void* value, const int64_t* slots, const int32_t* lens,
+                            int32_t num_seqs, void* key_cache, void* value_cache,
+                            const pkv_cache_layout* layout, int32_t* block_tables,
+                            int32_t block_table_stride, int32_t* lens_out,
+                            int32_t num_q_heads, int32_t max_context_len, float scale,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Apply the table growth of one batched append to a device-resident block
  * table: for every i with new_block[i] >= 0,
  *     block_tables[rows[i] * block_table_stride + (lens[i] - 1) / bs] = new_block[i]

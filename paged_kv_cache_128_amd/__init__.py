@@ -98,6 +98,12 @@ SIGNATURES = {
     "paged_kv_write": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
     "pkv_decode_write": (ctypes.c_int, [_P, _P, _PI64, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout),
                                         _P, _I32, _I32, _P, _P]),
+    "pkv_decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
+                                       ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
+                                       ctypes.c_float, _P, _SZ, _P]),
+    "pkv_decode_step_partial": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
+                                               ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
+                                               ctypes.c_float, _P, _SZ, _P]),
     "paged_decode_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               _F32, ctypes.POINTER(CacheLayout), _I32, _P, _SZ, _P]),
@@ -364,6 +370,55 @@ def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, val
     _check(st, "pkv_decode_write")
 
 
+def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
+                block_tables, lens_out, scale: float, max_context_len: int, out=None,
+                out_dtype=None, workspace=None, stream=None, phase: str = "both"):
+    """One decode step after the host-side append (see pkv_decode_step): the
+    write of key/value [n, H_kv, D] at `slots` (host int64) and the attention
+    of q [n, H_q, D] over the updated cache, with lens (host int32, lengths
+    after the append) published to lens_out (device int32 [n]) and opened
+    blocks to block_tables.  ``phase`` "partial" runs only the first launch;
+    paged_decode_attention(..., phase="merge") with context_lens=lens_out
+    completes it."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    n, hq, d = q.shape
+    if key.shape != (n, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_rows, H_kv, head_dim]")
+    if not (key.is_contiguous() and value.is_contiguous() and q.is_contiguous()):
+        raise ValueError("q, key and value must be contiguous")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype or q.dtype != key_cache.dtype:
+        raise ValueError("q/key/value dtype must equal the cache dtype")
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if slots.shape != (n,) or lens.shape != (n,):
+        raise ValueError("slots and lens must have one entry per row")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1 \
+            or block_tables.shape[0] < n:
+        raise ValueError("block_tables must be int32 [>= n, W] with unit column stride")
+    if lens_out.dtype != torch.int32 or lens_out.numel() < n or not lens_out.is_contiguous():
+        raise ValueError("lens_out must be a contiguous int32 tensor of at least n entries")
+    if out is None:
+        od = torch.float32 if out_dtype is None else out_dtype
+        out = torch.empty((n, hq, d), dtype=od, device=q.device)
+    need = workspace_size(n, hq, lay.num_kv_heads, d, max_context_len, 0)
+    if need > 0 and workspace is None:
+        if phase != "both":
+            raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    fn = {"both": "pkv_decode_step", "partial": "pkv_decode_step_partial"}[phase]
+    st = getattr(_lib_handle(), fn)(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
+        _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
+        value_cache.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(), block_tables.stride(0),
+        lens_out.data_ptr(), hq, int(max_context_len), float(scale),
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    _check(st, fn)
+    return out
+
+
 def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                    max_context_len: int, partition_tokens: int = 0) -> int:
     return int(_lib_handle().paged_decode_attention_workspace_size(
@@ -439,6 +494,7 @@ def update_block_tables(block_tables, lens, new_block, block_size: int, rows=Non
 __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
-    "workspace_size", "update_block_tables", "attention_path", "decode_write", "new_pool", "cache_layout", "load_library",
+    "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
+    "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

@@ -789,6 +789,15 @@ struct StreamArgs {
   int32_t num_ranges;    // W
   int32_t ranges_per_wg; // R
   float scale_log2;
+  // decode-step form only: the step's new rows [B, H_kv, D] and where the
+  // step's write goes (pool, table of table_rows rows, device lengths)
+  const void* new_k;
+  const void* new_v;
+  void* kc_w;
+  void* vc_w;
+  int32_t* tables_w;
+  int32_t table_rows;
+  int32_t* lens_out;
 };
 
 constexpr int kStreamMaxHeads = 8;
@@ -832,12 +841,13 @@ __device__ __forceinline__ int seq_of_tile(const int32_t* S, int B, int g) {
 
 // Exclusive prefix sums of T_b into S[0..B], and the clamped context
 // lengths into Ls[0..B), by one wave.
-__device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_len, int32_t* S,
+template <typename LenOf>
+__device__ __forceinline__ void tile_prefix(LenOf lens, int B, int max_len, int32_t* S,
                                             int32_t* Ls, int lane) {
   const int per = (B + kWave - 1) / kWave;
   const int b0 = min(B, lane * per), b1 = min(B, b0 + per);
   int part = 0;
-  for (int b = b0; b < b1; ++b) part += (clamp_len(lens[b], max_len) + kTile - 1) / kTile;
+  for (int b = b0; b < b1; ++b) part += (clamp_len(lens(b), max_len) + kTile - 1) / kTile;
   int incl = part;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -846,7 +856,7 @@ __device__ __forceinline__ void tile_prefix(const int32_t* lens, int B, int max_
   }
   int run = incl - part;
   for (int b = b0; b < b1; ++b) {
-    const int L = clamp_len(lens[b], max_len);
+    const int L = clamp_len(lens(b), max_len);
     S[b] = run;
     Ls[b] = L;
     run += (L + kTile - 1) / kTile;
@@ -916,9 +926,15 @@ constexpr int kStreamChunk = 2;
 constexpr int kWaitVm0 = 0x0f70;
 constexpr int kWaitLgkm0 = 0xc07f;
 
-template <int DT, int GP, bool PAIRED>
-__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
-attn_stream_kernel(StreamArgs a) {
+// The stream kernel's body.  FUSED: the decode-step form, which also does
+// the step's write: the lengths (after the append) and the new tokens'
+// slots come in `meta`; workgroup 0 publishes the lengths and the blocks
+// the step opened; the tile holding a sequence's new token takes its block
+// from the slot, and the one wave per KV head that reads that tile
+// replaces the token's row (stale in the pool until then) with the new K/V
+// row and stores that row into the pool.
+template <int DT, int GP, bool PAIRED, bool FUSED>
+__device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta* meta) {
   constexpr int D = 128;
   constexpr int CH = kStreamChunk;
   using F = Frag<DT, D>;
@@ -943,7 +959,22 @@ attn_stream_kernel(StreamArgs a) {
   int32_t* cstart = tbl + cap;
   int32_t* cseq = cstart + cap + 1;
   int32_t* kr = cseq + cap;
-  if (wave == 0) tile_prefix(a.lens, B, a.max_len, S, Ls, lane);
+  if (wave == 0) {
+    if constexpr (FUSED) tile_prefix([&](int b) { return meta->lens[b]; }, B, a.max_len, S, Ls, lane);
+    else tile_prefix([&](int b) { return a.lens[b]; }, B, a.max_len, S, Ls, lane);
+  }
+  if constexpr (FUSED) {
+    if (blockIdx.x == 0) {
+      for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int L = meta->lens[b];
+        if (a.lens_out) a.lens_out[b] = L;
+        if (a.tables_w && b < a.table_rows && L > 0 && (L - 1) % a.block_size == 0 &&
+            (L - 1) / a.block_size < a.table_stride)
+          a.tables_w[static_cast<int64_t>(b) * a.table_stride + (L - 1) / a.block_size] =
+              static_cast<int32_t>(meta->slots[b] / a.block_size);
+      }
+    }
+  }
   __syncthreads();
   const int T = S[B];
   const int W = a.num_ranges;
@@ -957,7 +988,11 @@ attn_stream_kernel(StreamArgs a) {
     const int g = w0 + t;
     const int b = seq_of_tile(S, B, g);
     const int lb = ((g - S[b]) * kTile) / bs;
-    int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
+    int pb;
+    if (FUSED && lb == (Ls[b] - 1) / bs)
+      pb = static_cast<int>(meta->slots[b] / bs);   // the new token's block (maybe opened now)
+    else
+      pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
     tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
   }
   if (wave == nwaves - 1) {
@@ -1055,6 +1090,50 @@ attn_stream_kernel(StreamArgs a) {
     auto nvalid_at = [&](int g, int b) { return min(kTile, uni(Ls[b]) - kTile * (g - uni(S[b]))); };
     // K rows of the n tiles from g on of sequence b into LDS, V rows into
     // `v`; the LDS reads for the addresses all come before the first DMA.
+    // New-token row of the chunk in flight (decode-step form): held when the
+    // chunk holds its sequence's last tile, as tile jn's row rn; lane
+    // (g4, c16) has 16-byte chunk c16 of the K and V rows.
+    bool hn = false;
+    int jn = 0, rn = 0;
+    u32x4 nk = {0u, 0u, 0u, 0u}, nvr = {0u, 0u, 0u, 0u};
+    auto fetch_new = [&](int g, int n, int b) {
+      hn = false;
+      if constexpr (FUSED) {
+        const int tl = uni(S[b + 1]) - 1;
+        if (g <= tl && tl < g + n) {
+          hn = true;
+          jn = tl - g;
+          rn = (uni(Ls[b]) - 1) & (kTile - 1);
+          const int64_t off = ((static_cast<int64_t>(b) * H + kvh) * D + c16 * 8) * 2;
+          nk = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_k) + off));
+          nvr = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(static_cast<const char*>(a.new_v) + off));
+        }
+      }
+    };
+    // At the head of the chunk holding a new token: its K row into the
+    // staged tile, its V row into the P.V registers, both rows into the pool.
+    auto place_new = [&](VTile<DT, D> (&v)[CH], int b) {
+      if constexpr (FUSED) {
+        if (g4 == 0) sk[jn * 256 + rn * 16 + (c16 ^ rn)] = make_uint4(nk.x, nk.y, nk.z, nk.w);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j == jn && r == (rn & 3) && g4 == (rn >> 2)) {
+              v[j].v[r].w[0] = nvr.x; v[j].v[r].w[1] = nvr.y;
+              v[j].v[r].w[2] = nvr.z; v[j].v[r].w[3] = nvr.w;
+            }
+        if (g4 == 0) {
+          const int64_t slot = meta->slots[b];
+          const int64_t pb = slot / bs, off = slot - pb * bs;
+          const int64_t dst = ((pb * a.block_stride + head_off + off * D) + c16 * 8) * 2;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.kc_w) + dst) = nk;
+          *reinterpret_cast<u32x4*>(static_cast<char*>(a.vc_w) + dst) = nvr;
+        }
+      }
+    };
     auto issue_chunk = [&](VTile<DT, D> (&v)[CH], int g, int n, int b) {
       int64_t e[CH];
       int nv[CH];
@@ -1081,6 +1160,7 @@ attn_stream_kernel(StreamArgs a) {
       load_q(bc);
       VTile<DT, D> vcur[CH], vnext[CH];
       issue_chunk(vcur, cs, cn, bc);
+      fetch_new(cs, cn, bc);
       int seg_lo = cs, seg_hi = cs + cn;    // tiles of the current segment
       float m = -INFINITY, l = 0.f;
       float acc[GP][F::kW];
@@ -1095,6 +1175,7 @@ attn_stream_kernel(StreamArgs a) {
       // leaves this sequence.
       while (true) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        if (FUSED && hn) place_new(vcur, bc);
         f32x4 scr[CH];
         {
           const Dw<F::kDwK> qf = read_q();
@@ -1110,6 +1191,7 @@ attn_stream_kernel(StreamArgs a) {
           nn = uni(cstart[nxt + 1]) - ns;
           bn = uni(cseq[nxt]);
           issue_chunk(vnext, ns, nn, bn);
+          fetch_new(ns, nn, bn);
           if (bn != bc) load_q(bn);
         }
 #pragma unroll
@@ -1145,6 +1227,20 @@ attn_stream_kernel(StreamArgs a) {
     }
     if (!back && lane == 0) a.ws_x[rng * H + kvh] = uni(cstart[k0 + ks]);
   }
+}
+
+template <int DT, int GP, bool PAIRED>
+__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
+attn_stream_kernel(StreamArgs a) {
+  stream_body<DT, GP, PAIRED, false>(a, nullptr);
+}
+
+// The decode step in one launch: the write of the step's new rows (taken
+// from `meta` and a.new_k / a.new_v) fused into the attention.
+template <int DT, int GP, bool PAIRED>
+__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
+attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
+  stream_body<DT, GP, PAIRED, true>(a, &meta);
 }
 
 // Merge of the stream kernel's partials.  One 64-lane workgroup per
@@ -1382,42 +1478,58 @@ hipError_t launch_split_d(const AttnArgs& a, int gp, dim3 grid, hipStream_t s) {
   }
 }
 
-template <int DT, int GP, bool PAIRED>
-hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, hipStream_t s) {
-  // Raise the kernel's dynamic-LDS limit to what this launch asks for
-  // (plan_stream already checked it against the device's per-block LDS),
-  // once per device and size.
+// Raises a kernel's dynamic-LDS limit to what a launch asks for (the plan
+// already checked it against the device's per-block LDS), once per device
+// and size.
+template <typename K>
+hipError_t raise_lds(K kernel, size_t bytes) {
   static std::atomic<int> raised[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   std::atomic<int>& done = raised[dev & 63];
-  if (pl.dyn_lds > 65536 && static_cast<int>(pl.dyn_lds) > done.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_stream_kernel<DT, GP, PAIRED>),
+  if (bytes > 65536 && static_cast<int>(bytes) > done.load()) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(pl.dyn_lds));
+                                             static_cast<int>(bytes));
     if (e != hipSuccess) return e;
-    done.store(static_cast<int>(pl.dyn_lds));
+    done.store(static_cast<int>(bytes));
   }
-  hipLaunchKernelGGL((attn_stream_kernel<DT, GP, PAIRED>), dim3(static_cast<uint32_t>(pl.wgs)),
-                     dim3(kWave * pl.waves), pl.dyn_lds, s, a);
+  return hipSuccess;
+}
+
+template <int DT, int GP, bool PAIRED>
+hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, const StepMeta* meta,
+                           hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(pl.wgs)), block(kWave * pl.waves);
+  if (meta) {
+    const hipError_t e = raise_lds(&attn_stream_step_kernel<DT, GP, PAIRED>, pl.dyn_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_stream_step_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a, *meta);
+  } else {
+    const hipError_t e = raise_lds(&attn_stream_kernel<DT, GP, PAIRED>, pl.dyn_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_stream_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a);
+  }
   return hipGetLastError();
 }
 
 template <int DT, int GP>
-hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, hipStream_t s) {
-  return pl.waves == 2 * pl.ranges_per_wg * a.hkv ? launch_stream_p<DT, GP, true>(a, pl, s)
-                                                  : launch_stream_p<DT, GP, false>(a, pl, s);
+hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, const StepMeta* meta,
+                           hipStream_t s) {
+  return pl.waves == 2 * pl.ranges_per_wg * a.hkv ? launch_stream_p<DT, GP, true>(a, pl, meta, s)
+                                                  : launch_stream_p<DT, GP, false>(a, pl, meta, s);
 }
 
 template <int DT>
-hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, hipStream_t s) {
+hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, const StepMeta* meta,
+                            hipStream_t s) {
   switch (gp) {
-    case 1: return launch_stream_t<DT, 1>(a, pl, s);
-    case 2: return launch_stream_t<DT, 2>(a, pl, s);
-    case 4: return launch_stream_t<DT, 4>(a, pl, s);
-    case 6: return launch_stream_t<DT, 6>(a, pl, s);
-    case 7: return launch_stream_t<DT, 7>(a, pl, s);
-    default: return launch_stream_t<DT, 8>(a, pl, s);
+    case 1: return launch_stream_t<DT, 1>(a, pl, meta, s);
+    case 2: return launch_stream_t<DT, 2>(a, pl, meta, s);
+    case 4: return launch_stream_t<DT, 4>(a, pl, meta, s);
+    case 6: return launch_stream_t<DT, 6>(a, pl, meta, s);
+    case 7: return launch_stream_t<DT, 7>(a, pl, meta, s);
+    default: return launch_stream_t<DT, 8>(a, pl, meta, s);
   }
 }
 
@@ -1565,15 +1677,28 @@ namespace {
 constexpr int kPhasePartial = 1;
 constexpr int kPhaseMerge = 2;
 
-// Validates the arguments, then launches the partition kernel (phase 1)
-// and/or the split-K merge kernel (phase 2, only when some sequence spans
-// more than one partition).
+// The decode-step form of the stream launch: the step's new rows, its
+// metadata, and where its write goes.
+struct StepArgs {
+  const void* key;
+  const void* value;
+  const StepMeta* meta;
+  void* key_cache;
+  void* value_cache;
+  int32_t* block_tables;
+  int32_t table_rows;
+  int32_t* lens_out;
+};
+
+// Validates the arguments, then launches the attention kernel (phase 1)
+// and/or the split-K merge kernel (phase 2).  With `step` (stream path
+// only), phase 1 is the decode-step kernel that also does the step's write.
 int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, const void* key_cache,
                    const void* value_cache, const int32_t* block_tables,
                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
                    int32_t num_q_heads, int32_t max_context_len, float scale,
                    const pkv_cache_layout* l, int32_t partition_tokens, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   size_t workspace_bytes, void* stream, const StepArgs* step = nullptr) {
   if (pkv::check_layout(l) != PKV_OK) return PKV_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || block_table_stride < 0 ||
       partition_tokens < 0)
@@ -1630,10 +1755,18 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.num_ranges = pl.ranges;
       sa.ranges_per_wg = pl.ranges_per_wg;
       sa.scale_log2 = scale * kLog2e;
+      sa.new_k = step ? step->key : nullptr;
+      sa.new_v = step ? step->value : nullptr;
+      sa.kc_w = step ? step->key_cache : nullptr;
+      sa.vc_w = step ? step->value_cache : nullptr;
+      sa.tables_w = step ? step->block_tables : nullptr;
+      sa.table_rows = step ? step->table_rows : 0;
+      sa.lens_out = step ? step->lens_out : nullptr;
       if (phases & kPhasePartial) {
         const int gp = padded_group(group);
-        hipError_t e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, s)
-                                              : launch_stream_dt<PKV_F16>(sa, gp, pl, s);
+        const StepMeta* meta = step ? step->meta : nullptr;
+        hipError_t e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, meta, s)
+                                              : launch_stream_dt<PKV_F16>(sa, gp, pl, meta, s);
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
@@ -1746,6 +1879,78 @@ int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
   return attention_impl(kPhaseMerge, out, out_dtype, q, key_cache, value_cache, block_tables,
                         block_table_stride, context_lens, num_seqs, num_q_heads, max_context_len,
                         scale, l, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+// The decode step (append already done on the host): the write of the
+// step's new rows and the attention over the updated cache.  One launch
+// (plus the merge) when the stream path applies, at most 256 rows are
+// given and every slot and length is in range; otherwise pkv_decode_write
+// then paged_decode_attention.
+namespace {
+int decode_step_impl(int phases, void* out, int32_t out_dtype, const void* q, const void* key,
+                     const void* value, const int64_t* slots, const int32_t* lens, int32_t num_seqs,
+                     void* key_cache, void* value_cache, const pkv_cache_layout* l,
+                     int32_t* block_tables, int32_t block_table_stride, int32_t* lens_out,
+                     int32_t num_q_heads, int32_t max_context_len, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
+      block_table_stride <= 0)
+    return PKV_ERR_INVALID;
+  if (num_seqs == 0) return PKV_OK;
+  if (!key || !value || !slots || !lens || !lens_out || !block_tables) return PKV_ERR_INVALID;
+  const int64_t capacity = static_cast<int64_t>(l->num_blocks) * l->block_size;
+  bool fused = num_seqs <= kStepRows &&
+               (reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value)) % 16 == 0 &&
+               plan_stream(num_seqs, num_q_heads, l->num_kv_heads, l->head_dim, max_context_len,
+                           l->dtype).ok;
+  for (int32_t i = 0; fused && i < num_seqs; ++i)
+    fused = slots[i] >= 0 && slots[i] < capacity && lens[i] >= 1 && lens[i] <= max_context_len &&
+            (lens[i] - 1) / l->block_size < block_table_stride;
+  if (!fused) {
+    if (phases & kPhasePartial) {
+      const int r = pkv_decode_write(key, value, slots, lens, num_seqs, key_cache, value_cache, l,
+                                     block_tables, num_seqs, block_table_stride, lens_out, stream);
+      if (r != PKV_OK) return r;
+    }
+    return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
+                          block_table_stride, lens_out, num_seqs, num_q_heads, max_context_len,
+                          scale, l, 0, workspace, workspace_bytes, stream);
+  }
+  StepMeta meta;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    meta.slots[i] = slots[i];
+    meta.lens[i] = lens[i];
+  }
+  const StepArgs st{key, value, &meta, key_cache, value_cache, block_tables, num_seqs, lens_out};
+  return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
+                        block_table_stride, lens_out, num_seqs, num_q_heads, max_context_len,
+                        scale, l, 0, workspace, workspace_bytes, stream, &st);
+}
+}  // namespace
+
+int pkv_decode_step(void* out, int32_t out_dtype, const void* q, const void* key,
+                    const void* value, const int64_t* slots, const int32_t* lens, int32_t num_seqs,
+                    void* key_cache, void* value_cache, const pkv_cache_layout* layout,
+                    int32_t* block_tables, int32_t block_table_stride, int32_t* lens_out,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return decode_step_impl(kPhasePartial | kPhaseMerge, out, out_dtype, q, key, value, slots, lens,
+                          num_seqs, key_cache, value_cache, layout, block_tables,
+                          block_table_stride, lens_out, num_q_heads, max_context_len, scale,
+                          workspace, workspace_bytes, stream);
+}
+
+int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const void* key,
+                            const void* value, const int64_t* slots, const int32_t* lens,
+                            int32_t num_seqs, void* key_cache, void* value_cache,
+                            const pkv_cache_layout* layout, int32_t* block_tables,
+                            int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return decode_step_impl(kPhasePartial, out, out_dtype, q, key, value, slots, lens, num_seqs,
+                          key_cache, value_cache, layout, block_tables, block_table_stride,
+                          lens_out, num_q_heads, max_context_len, scale, workspace,
+                          workspace_bytes, stream);
 }
 
 int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,

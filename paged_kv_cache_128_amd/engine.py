@@ -5,13 +5,17 @@ A decode step is the hot path of [MiniPaged-Qwen] §10 and §13 in order:
 
   1. block manager append for every row (one batched C call; all or nothing,
      [mini-vLLM BM] "Block Manager 和 Scheduler 如何协作"),
-  2. one write launch that carries the step's slots and lengths in its kernel
-     arguments: it writes the new K/V rows ([MiniPaged-Qwen] §12), publishes
-     the blocks the append opened into the device block table and stores the
-     lengths on the device,
+  2. the write of the new K/V rows ([MiniPaged-Qwen] §12), with the blocks
+     the append opened published into the device block table and the
+     lengths stored on the device, the step's slots and lengths travelling
+     in kernel arguments,
   3. paged_decode_attention over the updated cache ([MiniPaged-Qwen] §13),
      so the new token attends to itself ([MiniPaged-Qwen] §1.1: append, then
      attend over positions 0..L).
+
+With the stream attention path (partition_tokens 0), steps 2 and 3 are one
+launch (pkv_decode_step) plus the merge; otherwise they are a write launch
+and the attention.
 
 Rows are batch positions; each live sequence occupies one row.  All device
 memory comes from torch; all work runs in libpkv on torch's current stream.
@@ -23,8 +27,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, decode_write, new_pool, paged_decode_attention, paged_kv_write,
-               workspace_size)
+from . import (KVBlockManager, decode_step, decode_write, new_pool, paged_decode_attention,
+               paged_kv_write, workspace_size)
 
 
 class PagedKVEngine:
@@ -105,19 +109,38 @@ class PagedKVEngine:
 
     def decode_step(self, seq_ids: np.ndarray, new_k: torch.Tensor, new_v: torch.Tensor,
                     q: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
-                    out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, events=None,
+                    fused: bool = True) -> torch.Tensor:
         """One decode step for rows 0..n-1 holding ``seq_ids`` (int64).
         ``max_context_len`` defaults to the longest length after the append
         (known on the host from the manager, no device sync).  ``events``
-        (three torch.cuda.Event) are recorded before the attention kernel,
-        between it and the merge, and after the merge."""
+        (three torch.cuda.Event) are recorded before the attention kernel
+        (with the fused step: the write-and-attention kernel), between it and
+        the merge, and after the merge.  ``fused`` = False forces the
+        separate write launch."""
         n = len(seq_ids)
         self.manager.append_slots_for_decode(seq_ids, self.slots[:n], self.lens[:n], self._newb[:n])
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
-        decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
-                     block_tables=self.tables, lens_out=self.d_lens)
-        return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
+        if not (fused and self.partition_tokens == 0 and n > 0):
+            decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
+                         block_tables=self.tables, lens_out=self.d_lens)
+            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
+        ws = self.workspace(n, q.shape[1], max_context_len)
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        args = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
+                self.tables, self.d_lens, scale, max_context_len)
+        if events is None:
+            return decode_step(*args, out=out, workspace=ws)
+        events[0].record()
+        decode_step(*args, out=out, workspace=ws, phase="partial")
+        events[1].record()
+        paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], self.d_lens[:n],
+                               scale, out=out, partition_tokens=0, max_context_len=max_context_len,
+                               workspace=ws, phase="merge")
+        events[2].record()
+        return out
 
     def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
                out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:

@@ -286,3 +286,44 @@ def test_decode_write_matches_write_plus_table_update():
     assert torch.equal(ta, tb)
     assert np.array_equal(ta.cpu().numpy(), mgr.block_tables(ids, W, -1))
     assert np.array_equal(d_lens.cpu().numpy(), lens)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,hq,hkv,B", [("bf16", 28, 4, 64), ("f16", 12, 2, 40),
+                                            ("bf16", 32, 8, 250), ("bf16", 8, 8, 300),
+                                            ("f16", 4, 1, 9)])
+def test_fused_decode_step_equals_separate_launches(dtype, hq, hkv, B):
+    """pkv_decode_step (the write inside the attention launch; at most 256
+    rows, else the two launches) gives bit for bit the pool, tables, device
+    lengths and outputs of pkv_decode_write followed by the attention, over
+    three steps that open new blocks (prompt lengths at block multiples)."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    rng = np.random.default_rng(31 + B)
+    bs, D = 16, 128
+    lens = rng.integers(1, 400, size=B)
+    lens[::5] = 16 * rng.integers(1, 20, size=len(lens[::5]))     # next append opens a block
+    N = int(np.ceil((lens + 8) / bs).sum()) + 64
+    order = rng.permutation(N)
+    width = int(np.ceil((lens.max() + 8) / bs))
+    td = TORCH_DTYPE[dtype]
+    engs = [PagedKVEngine(N, hkv, bs, D, td, B, width, order, fill_bits=0x7E05, partition_tokens=0,
+                          num_q_heads=hq) for _ in range(2)]
+    tot = int(lens.sum())
+    k0 = torch.randn((tot, hkv, D), device="cuda").to(td)
+    v0 = torch.randn((tot, hkv, D), device="cuda").to(td)
+    for e in engs:
+        e.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], k0, v0)
+    ids = np.arange(B, dtype=np.int64)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    for step in range(3):
+        k = torch.randn((B, hkv, D), device="cuda").to(td)
+        v = torch.randn((B, hkv, D), device="cuda").to(td)
+        q = torch.randn((B, hq, D), device="cuda").to(td)
+        oa = engs[0].decode_step(ids, k, v, q, scale, fused=True)
+        ob = engs[1].decode_step(ids, k, v, q, scale, fused=False)
+        torch.cuda.synchronize()
+        assert torch.equal(engs[0].pool.view(torch.int16), engs[1].pool.view(torch.int16)), step
+        assert torch.equal(engs[0].tables, engs[1].tables), step
+        assert torch.equal(engs[0].d_lens[:B], engs[1].d_lens[:B]), step
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), step
+        assert bool(torch.isfinite(oa).all())
