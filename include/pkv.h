@@ -229,9 +229,8 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
  * P = ceil(max_context_len / partition_tokens) (0 when P <= 1; a
  * partition_tokens of 0 that cannot take the stream path means 512).  Stream
  * path (partition_tokens == 0): W * 4 * num_q_heads * (head_dim + 2) * 4
- * bytes of partials and W * num_kv_heads split tiles, with
- * W = CUs * max(1, 4 / num_kv_heads) tile ranges (integer division; 256 CUs
- * on MI355X).  The contents need no initialisation.  Returns 0 for invalid
+ * bytes of partials, with W = CUs * max(1, 4 / num_kv_heads) tile ranges
+ * (integer division; 256 CUs on MI355X).  The contents need no initialisation.  Returns 0 for invalid
  * arguments as well.
  */
 size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
@@ -278,7 +277,7 @@ int paged_decode_attention(void* out, int32_t out_dtype, const void* q,
  * Which attention kernel paged_decode_attention runs for these arguments:
  * PKV_PATH_STREAM (1): the launch's 16-token tiles cut into equal ranges,
  * one workgroup per CU, each (range, KV head) shared by two waves that
- * split its chunks at a fixed point (16-bit KV, head_dim 128, H_kv <= 8,
+ * split its tiles at a fixed point (16-bit KV, head_dim 128, H_kv <= 8,
  * H_q / H_kv <= 8, partition_tokens == 0); PKV_PATH_PARTITION (2):
  * one workgroup per (sequence, KV head, context partition of
  * partition_tokens tokens, default 512).  Negative status on invalid
@@ -346,10 +345,13 @@ int pkv_decode_step(void* out, int32_t out_dtype, const void* q, const void* key
                     size_t workspace_bytes, void* stream);
 
 /*
- * The first launch of pkv_decode_step alone (the write and the attention
- * kernel, leaving partials of split sequences in `workspace`);
- * paged_decode_attention_merge with context_lens = lens_out and the same
- * other arguments completes it.
+ * The two launches of pkv_decode_step, callable separately with the same
+ * arguments: _partial runs the write and the attention kernel, leaving
+ * partials of split sequences in `workspace`; _merge reduces them into
+ * `out` (in the one-launch form it takes the lengths from `lens`, host,
+ * as kernel arguments).  paged_decode_attention_merge with context_lens =
+ * lens_out and the same other arguments may stand in for _merge.  The pair,
+ * in this order on one stream, equals one pkv_decode_step call.
  */
 int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const void* key,
                             const void* value, const int64_t* slots, const int32_t* lens,
@@ -358,6 +360,13 @@ int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const v
                             int32_t block_table_stride, int32_t* lens_out,
                             int32_t num_q_heads, int32_t max_context_len, float scale,
                             void* workspace, size_t workspace_bytes, void* stream);
+int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const void* key,
+                          const void* value, const int64_t* slots, const int32_t* lens,
+                          int32_t num_seqs, void* key_cache, void* value_cache,
+                          const pkv_cache_layout* layout, int32_t* block_tables,
+                          int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Apply the table growth of one batched append to a device-resident block

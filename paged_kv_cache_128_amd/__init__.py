@@ -104,6 +104,9 @@ SIGNATURES = {
     "pkv_decode_step_partial": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
                                                ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
                                                ctypes.c_float, _P, _SZ, _P]),
+    "pkv_decode_step_merge": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
+                                             ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
+                                             ctypes.c_float, _P, _SZ, _P]),
     "paged_decode_attention_workspace_size": (_SZ, [_I32, _I32, _I32, _I32, _I32, _I32]),
     "paged_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32,
                                               _F32, ctypes.POINTER(CacheLayout), _I32, _P, _SZ, _P]),
@@ -377,9 +380,8 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
     write of key/value [n, H_kv, D] at `slots` (host int64) and the attention
     of q [n, H_q, D] over the updated cache, with lens (host int32, lengths
     after the append) published to lens_out (device int32 [n]) and opened
-    blocks to block_tables.  ``phase`` "partial" runs only the first launch;
-    paged_decode_attention(..., phase="merge") with context_lens=lens_out
-    completes it."""
+    blocks to block_tables.  ``phase`` "partial" runs only the first launch
+    and "merge" (same arguments and workspace) only the second."""
     torch = _torch()
     lay = cache_layout(key_cache, value_cache)
     n, hq, d = q.shape
@@ -406,7 +408,8 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
         if phase != "both":
             raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    fn = {"both": "pkv_decode_step", "partial": "pkv_decode_step_partial"}[phase]
+    fn = {"both": "pkv_decode_step", "partial": "pkv_decode_step_partial",
+          "merge": "pkv_decode_step_merge"}[phase]
     st = getattr(_lib_handle(), fn)(
         out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
         _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),

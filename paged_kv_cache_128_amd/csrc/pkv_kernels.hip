@@ -744,26 +744,26 @@ attn_reduce_kernel(AttnArgs a) {
 // cut into W equal contiguous ranges: range r takes tiles [r*T/W, (r+1)*T/W),
 // so every range carries the same number of tiles whatever the mix of
 // context lengths.  One workgroup per CU holds R consecutive ranges.  A job
-// is one (range, KV head); its tiles are cut into chunks of up to
-// kStreamChunk tiles of one sequence, and two waves share the job: the
-// front worker takes the chunks before a split point, the back worker the
-// rest.  The two waves on one SIMD do not progress at the same rate (the
-// one in the second wave slot runs markedly slower under this load), so the
-// split gives the slot-0 wave the larger share (job_split).  The split is
-// fixed, so results are bitwise reproducible.  When every KV head has two
-// waves (2 * R * H_kv <= 8) each job has its own pair; otherwise (H_kv > 4)
-// each wave is the front worker of job j and then the back worker of job
-// (j + 4) mod H_kv.
+// is one (range, KV head), and two waves share it: the front worker takes
+// the tiles before a split tile x, the back worker those from x on.  The
+// two waves on one SIMD do not progress at the same rate (the one in the
+// second wave slot runs markedly slower under this load), so the split
+// gives the slot-0 wave the larger share (part_split).  x depends only on
+// the range and the job, so results are bitwise reproducible and the merge
+// kernel recomputes it.  Each worker walks its part in chunks of up to
+// kStreamChunk tiles of one sequence (a chunk ends at a sequence end or at
+// the part's end).  When every KV head has two waves (2 * R * H_kv <= 8)
+// each job has its own pair; otherwise (H_kv > 4) each wave is the front
+// worker of job j and then the back worker of job (j + 4) mod H_kv.
 //
-// Every maximal run of one worker's chunks in one sequence is a segment; a
+// Every maximal run of one worker's tiles in one sequence is a segment; a
 // segment that covers its whole sequence writes the normalised output,
 // other segments leave a (max, sum, accumulator) partial in one of four
 // slots of their job: 0 = the front worker's segment starting at the range
-// start, 1 = its segment ending at the split point, 2 = the back worker's
+// start, 1 = its segment ending at the split tile, 2 = the back worker's
 // segment ending at the range end, 3 = its segment starting at the split
-// point.  The front worker records the split tile; the merge kernel finds
-// the pieces of each sequence from the range bounds and the split tiles.
-// 16-bit KV, D = 128, H_kv <= 8, G <= 8.
+// tile.  The merge kernel finds the pieces of each sequence from the range
+// bounds and the split tiles.  16-bit KV, D = 128, H_kv <= 8, G <= 8.
 struct StreamArgs {
   const void* q;
   const void* kc;
@@ -772,7 +772,6 @@ struct StreamArgs {
   const int32_t* lens;
   float* ws_acc;     // [W, 4, H_q, D]   (W = num_ranges)
   float* ws_ml;      // [W, 4, H_q, 2]
-  int32_t* ws_x;     // [W, H_kv] split tile of each job
   void* out;
   int64_t block_stride;
   int64_t head_stride;
@@ -809,18 +808,17 @@ constexpr int kStreamSlots = 4;          // partial slots per job
 // balanced pair splits about 56 : 44.
 constexpr int kSlot0Share = 56;
 
-// Where a job's nc chunks split between its two workers: the front worker
-// is wave `job` of the workgroup, the back worker wave J + job (two waves
-// per job) or the wave that runs job's back after its own front (one wave
-// per job).  Waves 0-3 sit in SIMD wave slot 0, waves 4-7 in slot 1; the
-// slot-0 worker takes kSlot0Share percent of the chunks when its partner is
-// in slot 1, else the split is even.
-template <bool PAIRED>
-__device__ __forceinline__ int job_split(int nc, int job, int J) {
+// How many of a job's n tiles its front worker takes.  The front worker is
+// wave `job` of the workgroup, the back worker wave J + job (paired: two
+// waves per job) or the wave that runs job's back after its own front
+// (J - 4 + job) mod J.  Waves 0-3 sit in SIMD wave slot 0, waves 4-7 in
+// slot 1; the slot-0 worker takes kSlot0Share percent of the tiles when
+// its partner is in slot 1, else the split is even.
+__device__ __forceinline__ int part_split(int n, int job, int J, bool paired) {
   const int fw = job;
-  const int bw = PAIRED ? J + job : (job + J - 4 % J) % J;
-  if ((fw >> 2) == (bw >> 2)) return (nc + 1) / 2;
-  return (fw >> 2) == 0 ? (nc * kSlot0Share + 50) / 100 : (nc * (100 - kSlot0Share) + 50) / 100;
+  const int bw = paired ? J + job : (job + J - 4 % J) % J;
+  if ((fw >> 2) == (bw >> 2)) return (n + 1) / 2;
+  return (fw >> 2) == 0 ? (n * kSlot0Share + 50) / 100 : (n * (100 - kSlot0Share) + 50) / 100;
 }
 constexpr int kStreamMaxRanges = 1024;   // W bound (merge kernel's piece list)
 
@@ -940,7 +938,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   using F = Frag<DT, D>;
   static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
   // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
-  //              [tbl: cap][cstart: cap + 1][cseq: cap][kr: R + 1]
+  //              [tbl: cap]
   extern __shared__ uint4 sh_stream[];
   const int wave = uni(threadIdx.x >> 6);    // wave-uniform: keeps all per-job values scalar
   const int lane = threadIdx.x & (kWave - 1);
@@ -950,15 +948,11 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   const int R = a.ranges_per_wg;
   const int H = a.hkv;
   const int J = R * H;
-  const int cap = a.range_cap;
   uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * 256;
   uint4* sq = sh_stream + static_cast<int64_t>(nwaves) * CH * 256 + static_cast<int64_t>(wave) * 256;
   int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(nwaves) * (CH + 1) * 256);
   int32_t* Ls = S + B + 1;
   int32_t* tbl = Ls + B;
-  int32_t* cstart = tbl + cap;
-  int32_t* cseq = cstart + cap + 1;
-  int32_t* kr = cseq + cap;
   if (wave == 0) {
     if constexpr (FUSED) tile_prefix([&](int b) { return meta->lens[b]; }, B, a.max_len, S, Ls, lane);
     else tile_prefix([&](int b) { return a.lens[b]; }, B, a.max_len, S, Ls, lane);
@@ -995,42 +989,6 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
     tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
   }
-  if (wave == nwaves - 1) {
-    // Chunk list: a chunk starts at every range start and sequence start and
-    // every CH tiles after either; cstart[k] is the first tile of chunk k
-    // and cseq[k] its sequence, cstart[nc] = w1, kr[r] the first chunk of
-    // range r_base + r.
-    int nc = 0;
-    for (int t0 = w0; t0 < w1; t0 += kWave) {
-      const int t = t0 + lane;
-      bool first = false;
-      int b = 0;
-      if (t < w1) {
-        b = seq_of_tile(S, B, t);
-        const int from = max(S[b], range_start(range_owner(t, T, W), T, W));
-        first = ((t - from) % CH) == 0;
-      }
-      const uint64_t m = __builtin_amdgcn_ballot_w64(first);
-      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
-      if (first) {
-        cstart[nc + below] = t;
-        cseq[nc + below] = b;
-      }
-      nc += __builtin_popcountll(m);
-    }
-    if (lane == 0) cstart[nc] = w1;
-    if (lane <= R) {
-      // first chunk starting at or after the range's first tile
-      const int rs = range_start(r_base + lane, T, W);
-      int lo = 0, hi = nc;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (cstart[mid] < rs) lo = mid + 1; else hi = mid;
-      }
-      kr[lane] = lo;
-    }
-  }
   __syncthreads();
 
   const int G = a.group;
@@ -1046,13 +1004,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     const int64_t rng = r_base + r;
     const int g0 = range_start(rng, T, W);
     const int g1 = range_start(rng + 1, T, W);
-    const int k0 = uni(kr[r]), k1 = uni(kr[r + 1]);
-    const int nc = k1 - k0;
     const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
-    // The job's chunks [k0, k1) split at k0 + ks: the front worker takes
-    // those before, the back worker those from there on; both walk forward.
-    const int ks = job_split<PAIRED>(nc, job, J);
-    const int my0 = back ? k0 + ks : k0, my1 = back ? k1 : k0 + ks;
+    // The job's tiles [g0, g1) split at x: the front worker takes those
+    // before, the back worker those from x on; both walk forward.
+    const int x = g0 + part_split(g1 - g0, job, J, PAIRED);
+    const int p0 = back ? x : g0, p1 = back ? g1 : x;
+    // the chunk from tile g of sequence b: up to CH tiles, within b and the part
+    auto chunk_len = [&](int g, int b) { return min(CH, min(uni(S[b + 1]), p1) - g); };
     // byte offset of tile g of sequence b (inside the workgroup's tiles)
     auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
       const int ti = g - uni(S[b_of_g]);
@@ -1151,12 +1109,11 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       }
     };
 
-    if (my0 < my1) {
-      // current chunk ck: tiles [cs, cs + cn) of sequence bc
-      int ck = my0;
-      int cs = uni(cstart[ck]);
-      int cn = uni(cstart[ck + 1]) - cs;
-      int bc = uni(cseq[ck]);
+    if (p0 < p1) {
+      // current chunk: tiles [cs, cs + cn) of sequence bc
+      int cs = p0;
+      int bc = uni(seq_of_tile(S, B, cs));
+      int cn = chunk_len(cs, bc);
       load_q(bc);
       VTile<DT, D> vcur[CH], vnext[CH];
       issue_chunk(vcur, cs, cn, bc);
@@ -1183,13 +1140,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
           for (int j = 0; j < CH; ++j)
             if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
         }
-        const int nxt = ck + 1 < my1 ? ck + 1 : -1;
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS reads done before the buffer is refilled
+        const bool more = cs + cn < p1;
         int ns = 0, nn = 0, bn = -1;
-        if (nxt >= 0) {
-          ns = uni(cstart[nxt]);
-          nn = uni(cstart[nxt + 1]) - ns;
-          bn = uni(cseq[nxt]);
+        if (more) {
+          ns = cs + cn;
+          bn = bc;
+          while (uni(S[bn + 1]) <= ns) ++bn;       // skips sequences with no tiles
+          nn = chunk_len(ns, bn);
           issue_chunk(vnext, ns, nn, bn);
           fetch_new(ns, nn, bn);
           if (bn != bc) load_q(bn);
@@ -1216,16 +1174,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
         } else {
           seg_hi = ns + nn;
         }
-        if (nxt < 0) break;
+        if (!more) break;
 #pragma unroll
         for (int j = 0; j < CH; ++j) vcur[j] = vnext[j];
-        ck = nxt;
         cs = ns;
         cn = nn;
         bc = bn;
       }
     }
-    if (!back && lane == 0) a.ws_x[rng * H + kvh] = uni(cstart[k0 + ks]);
   }
 }
 
@@ -1243,25 +1199,35 @@ attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
   stream_body<DT, GP, PAIRED, true>(a, &meta);
 }
 
+// Lengths of at most kStepRows sequences carried in the kernel arguments.
+struct LensMeta {
+  int32_t lens[kStepRows];
+};
+
 // Merge of the stream kernel's partials.  One 64-lane workgroup per
 // (sequence, query head).  A sequence with L = 0 gets zeros; one that a
 // single segment covered was finished already; otherwise its pieces are
 // combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The
 // pieces of sequence b are, in every range that holds some of its tiles,
 // the part before the range's split tile x (front worker) and the part
-// from x on (back worker), where not empty.
-template <int D>
+// from x on (back worker), where not empty.  The lengths come from
+// `meta` (ARG_LENS) or from a.lens.
+template <int D, bool ARG_LENS>
 __global__ void __launch_bounds__(kWave)
-attn_stream_merge_kernel(StreamArgs a) {
+attn_stream_merge_kernel(StreamArgs a, LensMeta meta) {
   __shared__ int32_t plist[2 * kStreamMaxRanges];
   const int lane = threadIdx.x;
   const int qh = blockIdx.x % a.hq;
   const int b = blockIdx.x / a.hq;
   const int kvh = qh / a.group;
   const int W = a.num_ranges;
+  const int R = a.ranges_per_wg;
+  const int J = R * a.hkv;
+  const bool paired = 2 * a.hkv <= kStreamMaxWaves;
+  auto len_of = [&](int j) { return clamp_len(ARG_LENS ? meta.lens[j] : a.lens[j], a.max_len); };
   int before = 0, total = 0;
   for (int j = lane; j < a.num_seqs; j += kWave) {
-    const int t = (clamp_len(a.lens[j], a.max_len) + kTile - 1) / kTile;
+    const int t = (len_of(j) + kTile - 1) / kTile;
     total += t;
     if (j < b) before += t;
   }
@@ -1270,7 +1236,7 @@ attn_stream_merge_kernel(StreamArgs a) {
     before += __shfl_xor(before, o);
     total += __shfl_xor(total, o);
   }
-  const int L = clamp_len(a.lens[b], a.max_len);
+  const int L = len_of(b);
   const int64_t orow = (static_cast<int64_t>(b) * a.hq + qh) * D;
   constexpr int kPer = D / kWave;
   if (L == 0) {
@@ -1294,7 +1260,7 @@ attn_stream_merge_kernel(StreamArgs a) {
     if (r <= r_last) {
       const int g0 = range_start(r, total, W), g1 = range_start(r + 1, total, W);
       if (g0 < g1) {
-        const int x = a.ws_x[static_cast<int64_t>(r) * a.hkv + kvh];
+        const int x = g0 + part_split(g1 - g0, (r % R) * a.hkv + kvh, J, paired);
         const int lo = max(g0, Sb), hi = min(g1, Se);
         if (lo < min(x, hi)) sl[n++] = r * kStreamSlots + (lo == g0 ? 0 : 1);
         if (max(x, lo) < hi) sl[n++] = r * kStreamSlots + (hi == g1 ? 2 : 3);
@@ -1401,7 +1367,7 @@ struct StreamPlan {
   int ranges = 0;         // W = wgs * R
   int range_cap = 0;
   size_t dyn_lds = 0;
-  size_t acc_floats = 0;  // workspace: accumulators, then (m, l), then split tiles
+  size_t acc_floats = 0;  // workspace: accumulators, then (m, l)
   size_t ml_floats = 0;
   size_t workspace = 0;
 };
@@ -1423,8 +1389,7 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (tiles_max >= (1LL << 30)) return pl;
   const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
   const size_t dyn = static_cast<size_t>(waves) * (kStreamChunk + 1) * 4096 +
-                     static_cast<size_t>(2 * num_seqs + 1 + 3 * cap + 1 + R + 1) *
-                         sizeof(int32_t);
+                     static_cast<size_t>(2 * num_seqs + 1 + cap) * sizeof(int32_t);
   if (dyn > device_lds_per_block()) return pl;
   pl.ok = true;
   pl.wgs = static_cast<int>(wgs);
@@ -1435,8 +1400,7 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   pl.dyn_lds = dyn;
   pl.acc_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * head_dim;
   pl.ml_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * 2;
-  pl.workspace = (pl.acc_floats + pl.ml_floats) * sizeof(float) +
-                 static_cast<size_t>(ranges) * num_kv_heads * sizeof(int32_t);
+  pl.workspace = (pl.acc_floats + pl.ml_floats) * sizeof(float);
   return pl;
 }
 
@@ -1738,7 +1702,6 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.lens = context_lens;
       sa.ws_acc = static_cast<float*>(workspace);
       sa.ws_ml = sa.ws_acc + pl.acc_floats;
-      sa.ws_x = reinterpret_cast<int32_t*>(sa.ws_ml + pl.ml_floats);
       sa.out = out;
       sa.block_stride = l->block_stride;
       sa.head_stride = l->head_stride;
@@ -1770,9 +1733,14 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
-        hipLaunchKernelGGL(attn_stream_merge_kernel<128>,
-                           dim3(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads)),
-                           dim3(kWave), 0, s, sa);
+        const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
+        LensMeta lm;
+        if (step) {
+          for (int32_t i = 0; i < num_seqs; ++i) lm.lens[i] = step->meta->lens[i];
+          hipLaunchKernelGGL((attn_stream_merge_kernel<128, true>), grid, dim3(kWave), 0, s, sa, lm);
+        } else {
+          hipLaunchKernelGGL((attn_stream_merge_kernel<128, false>), grid, dim3(kWave), 0, s, sa, lm);
+        }
         if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
       }
       return PKV_OK;
@@ -1948,6 +1916,19 @@ int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const v
                             int32_t max_context_len, float scale, void* workspace,
                             size_t workspace_bytes, void* stream) {
   return decode_step_impl(kPhasePartial, out, out_dtype, q, key, value, slots, lens, num_seqs,
+                          key_cache, value_cache, layout, block_tables, block_table_stride,
+                          lens_out, num_q_heads, max_context_len, scale, workspace,
+                          workspace_bytes, stream);
+}
+
+int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const void* key,
+                          const void* value, const int64_t* slots, const int32_t* lens,
+                          int32_t num_seqs, void* key_cache, void* value_cache,
+                          const pkv_cache_layout* layout, int32_t* block_tables,
+                          int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_step_impl(kPhaseMerge, out, out_dtype, q, key, value, slots, lens, num_seqs,
                           key_cache, value_cache, layout, block_tables, block_table_stride,
                           lens_out, num_q_heads, max_context_len, scale, workspace,
                           workspace_bytes, stream);

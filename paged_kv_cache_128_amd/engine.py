@@ -136,9 +136,7 @@ class PagedKVEngine:
         events[0].record()
         decode_step(*args, out=out, workspace=ws, phase="partial")
         events[1].record()
-        paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], self.d_lens[:n],
-                               scale, out=out, partition_tokens=0, max_context_len=max_context_len,
-                               workspace=ws, phase="merge")
+        decode_step(*args, out=out, workspace=ws, phase="merge")
         events[2].record()
         return out
 
