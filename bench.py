@@ -126,6 +126,42 @@ def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
     return done_bytes, done_seqs, elapsed
 
 
+def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
+    """Copy-on-write block copies (pkv_copy_blocks) on the workload's pool:
+    ``pairs`` allocated blocks copied into free ones per launch, timed with
+    HIP events around ``iters`` back-to-back launches.  Algorithmic bytes:
+    every copied block is read once and written once."""
+    import torch
+    import paged_kv_cache_128_amd as pkv
+    free = np.array(eng.manager.free_list()[:pairs], dtype=np.int32)
+    tabs = eng.tables.cpu().numpy()
+    used = tabs[tabs >= 0][:pairs].astype(np.int32)
+    n = min(len(free), len(used))
+    if n == 0:
+        return None
+    src, dst = used[:n], free[:n]
+    block_bytes = 2 * eng.num_kv_heads * eng.block_size * eng.head_dim * eng.pool.element_size()
+    for _ in range(5):
+        pkv.copy_blocks(src, dst, eng.key_cache, eng.value_cache)
+    torch.cuda.synchronize()
+    # back-to-back launches between one event pair, as copies arrive in a
+    # serving loop (an isolated launch would time mostly the launch itself)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        pkv.copy_blocks(src, dst, eng.key_cache, eng.value_cache)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    moved = 2 * n * block_bytes
+    gbps = moved / (us * 1e-6) / 1e9
+    log(f"block copy: {n} blocks of {block_bytes} B in {us:.2f} us per launch ({gbps:.0f} GB/s)")
+    return {"kernel": "block_copy_kernel", "blocks_per_launch": n, "block_bytes": block_bytes,
+            "algorithmic_bytes_per_launch": moved, "mean_launch_us": round(us, 3),
+            "achieved_gbps": round(gbps, 2), "peak_gbps": HBM_PEAK_GBPS,
+            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,6 +293,7 @@ def main():
         cold.append((e[0].elapsed_time(e[1]), e[0].elapsed_time(e[2])))
     cold = np.array(cold)
     del flush
+    block_copy = measure_block_copy(eng)
 
     import paged_kv_cache_128_amd as pkv
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
@@ -314,6 +351,7 @@ def main():
             "algorithmic_bytes_per_launch": round(alg_bytes),
         },
         "kernel_source_sha256_16": kernel_source_sha(),
+        "copy_on_write": block_copy,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)

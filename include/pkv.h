@@ -94,6 +94,17 @@ size_t pkv_pool_span_bytes(const pkv_cache_layout* layout);
  * keeps).  `initial_free_order` (host, [num_blocks], a permutation of
  * 0..N-1) sets the starting order; NULL means 0, 1, ..., N-1
  * ([MiniPaged-Qwen] §8.2).  The library copies it.
+ *
+ * Prefix sharing and copy-on-write ([impl-detail] "Copy-on-Write共享"):
+ * every block has a reference count, the number of tables holding it
+ * (pkv_share_prefix lets several tables hold one block).  Release drops one
+ * reference per table entry and appends a block to the free list when its
+ * count reaches 0.  An append whose token lands in a block held by more than
+ * one table first takes a free block (front of the list), drops one
+ * reference from the shared block, puts the new block in the table and
+ * queues the pair (shared block, new block); the caller drains the queue
+ * with pkv_take_block_copies and runs pkv_copy_blocks on the device before
+ * it writes the step's rows.  Without sharing nothing is ever queued.
  */
 typedef struct pkv_manager pkv_manager;
 #define PKV_SORT_ON_RELEASE 1u
@@ -134,21 +145,47 @@ int pkv_append_slot_for_decode(pkv_manager* mgr, int64_t seq_id, int64_t* slot_o
 
 /*
  * Batched append for `n` distinct live sequences, processed in array order,
- * all or nothing: the number of sequences opening a new block is checked
- * against the free list before anything changes ([mini-vLLM BM] "Block
- * Manager 和 Scheduler 如何协作", can_append_slots).  Outputs (host, each
- * [n], any may be NULL): slots_out[i] = slot of seq_ids[i]'s new token;
- * lens_out[i] = its length after the append; new_block_out[i] = physical id
- * appended to its table by this call, or -1 when none was.
+ * all or nothing: the blocks the call takes (one per sequence opening a
+ * block, one per copy-on-write, counted in array order) are checked against
+ * the free list before anything changes ([mini-vLLM BM] "Block Manager 和
+ * Scheduler 如何协作", can_append_slots).  Outputs (host, each [n], any may
+ * be NULL): slots_out[i] = slot of seq_ids[i]'s new token; lens_out[i] = its
+ * length after the append; new_block_out[i] = physical id this call put in
+ * its table (an opened block, or a copy-on-write block at the same logical
+ * index), or -1 when none.
  * Errors: INVALID (n < 0, duplicate ids, NULL ids with n > 0), NOT_LIVE, OOM.
  */
 int pkv_append_slots_for_decode(pkv_manager* mgr, const int64_t* seq_ids, int32_t n,
                                 int64_t* slots_out, int32_t* lens_out,
                                 int32_t* new_block_out);
 
-/* Return every block of `seq_id` to the free list exactly once
+/* Release `seq_id`: each block of its table loses one reference, and those
+ * whose count reaches 0 are appended to the free list in table order
  * ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  Errors: NOT_LIVE. */
 int pkv_free_sequence(pkv_manager* mgr, int64_t seq_id);
+
+/*
+ * Create live sequence `seq_id` (>= 0) holding the first `num_tokens`
+ * (0 <= num_tokens <= donor length) tokens of live sequence `donor_id`
+ * without copying: its table is the donor's first ceil(num_tokens / bs)
+ * blocks, the partial last block included, each gaining one reference
+ * ([impl-detail] "前缀共享", share_prefix_blocks).  Its length is
+ * num_tokens; its next append copies the last block first when that block is
+ * still shared.  With num_tokens equal to the donor's length this forks the
+ * donor.  Errors: INVALID, NOT_LIVE (donor), ALREADY_PREFILLED (seq_id
+ * live).
+ */
+int pkv_share_prefix(pkv_manager* mgr, int64_t donor_id, int64_t seq_id, int32_t num_tokens);
+
+/* Reference count of physical block `block` (0 when free), or INVALID. */
+int32_t pkv_block_ref_count(const pkv_manager* mgr, int32_t block);
+
+/* Drain the copy-on-write queue, oldest first: src[i] (shared block) and
+ * dst[i] (the new block that replaced it in one table) for i < *count_out
+ * (host arrays of `cap` entries).  INVALID when more than `cap` are queued
+ * (nothing is drained then). */
+int pkv_take_block_copies(pkv_manager* mgr, int32_t* src, int32_t* dst, int32_t cap,
+                          int32_t* count_out);
 
 /* Length of a live sequence, or PKV_ERR_NOT_LIVE. */
 int32_t pkv_context_len(const pkv_manager* mgr, int64_t seq_id);
@@ -173,8 +210,10 @@ int pkv_get_context_lens(const pkv_manager* mgr, const int64_t* seq_ids, int32_t
 int pkv_get_free_list(const pkv_manager* mgr, int32_t* out, int32_t cap, int32_t* count_out);
 
 /* Check the invariants of [MiniPaged-Qwen] §15 and [mini-vLLM BM]
- * "正确性不变量": I1 no physical id twice across tables, I2 tables and free
- * list disjoint, I3 |allocated| + |free| == N, I4 ids in [0, N),
+ * "正确性不变量": I1 no physical id twice in one table and each block's
+ * reference count equals the number of tables holding it (without sharing:
+ * no id in two tables), I2 tables and free list disjoint (free blocks count
+ * 0), I3 |distinct allocated| + |free| == N, I4 ids in [0, N),
  * I5 len(table) == ceil(len / bs), I6 no duplicate in the free list.
  * Returns PKV_OK or PKV_ERR_INVARIANT. */
 int pkv_check_invariants(const pkv_manager* mgr);
@@ -206,9 +245,9 @@ int paged_kv_write(const void* key, const void* value, const int64_t* slot_mappi
  *   - key/value row i (device, [num_rows, H_kv, D] contiguous) is written at
  *     slots[i] exactly as paged_kv_write does ([MiniPaged-Qwen] §12);
  *   - when block_tables (device, int32 [table_rows, block_table_stride]) is
- *     not NULL and the token is the first of its block ((lens[i] - 1) % bs
- *     == 0, i.e. the append opened a block, [MiniPaged-Qwen] §9.2), the
- *     table entry [i, (lens[i] - 1) / bs] is set to slots[i] / bs;
+ *     not NULL, the table entry [i, (lens[i] - 1) / bs] is set to
+ *     slots[i] / bs: the block holding the new token, which the append may
+ *     have opened ([MiniPaged-Qwen] §9.2) or copied on write;
  *   - when lens_out (device, int32 [num_rows]) is not NULL, lens_out[i] =
  *     lens[i].
  *   slots (host, int64 [num_rows]) and lens (host, int32 [num_rows]) are the
@@ -220,6 +259,20 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
                      const int32_t* lens, int32_t num_rows, void* key_cache, void* value_cache,
                      const pkv_cache_layout* layout, int32_t* block_tables, int32_t table_rows,
                      int32_t block_table_stride, int32_t* lens_out, void* stream);
+
+/*
+ * Whole-block copies for copy-on-write ([impl-detail] "Copy-on-Write机制":
+ * the new block receives the shared block's K and V): for i < n, every
+ * token row of every KV head of block src[i] is copied to block dst[i], in
+ * key_cache and in value_cache.  src, dst: host int32 [n], carried into the
+ * launches as kernel arguments (256 pairs per launch).  Pairs with an id
+ * outside [0, num_blocks) are skipped.  No dst may equal any pair's src or
+ * another pair's dst (the pairs run concurrently); pkv_take_block_copies
+ * output meets this.  n == 0 is a no-op.  Errors: INVALID, UNSUPPORTED
+ * (a head's block_size*head_dim*elem_bytes not a multiple of 16), HIP.
+ */
+int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
+                    void* value_cache, const pkv_cache_layout* layout, void* stream);
 
 /* -------------------------------------------------------- decode attention */
 /*
@@ -325,13 +378,15 @@ int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
  * lens[i] in [1, max_context_len], the write runs inside the attention
  * launch: the one wave per KV head that reads a sequence's last tile takes
  * the new row from `key`/`value` and stores it into the pool, and the new
- * lengths and opened blocks are published by the same launch.  Otherwise
+ * lengths and table entries are published by the same launch.  Otherwise
  * the two calls run one after the other.
  *   key, value   device, [num_seqs, H_kv, D] contiguous, 16-byte aligned
  *   slots, lens  host, the outputs of pkv_append_slots_for_decode in row
  *                order (lens = context lengths after the append)
- *   block_tables device, int32 [num_seqs, block_table_stride]; entries of
- *                blocks the append opened are written
+ *   block_tables device, int32 [num_seqs, block_table_stride]; entry
+ *                [i, (lens[i] - 1) / bs] is set to slots[i] / bs (blocks
+ *                the append opened or copied on write; the copies
+ *                themselves, pkv_copy_blocks, must run before this call)
  *   lens_out     device, int32 [num_seqs], receives lens
  *   workspace    as for paged_decode_attention with partition_tokens 0
  * Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.

@@ -45,6 +45,22 @@ def write_kv(key: np.ndarray, value: np.ndarray, slot_mapping: Sequence[int],
         value_cache[pb, :, off, :] = value[i]
 
 
+def copy_blocks(pairs: Sequence[Tuple[int, int]], key_cache: np.ndarray,
+                value_cache: np.ndarray) -> None:
+    """Copy-on-write copies ([impl-detail] "Copy-on-Write机制": the new block
+    takes the shared block's k and v): for each (src, dst) in order,
+    key_cache[dst] = key_cache[src] and value_cache[dst] = value_cache[src],
+    every head and token row.  Pairs with an id outside [0, num_blocks) are
+    skipped."""
+    n = key_cache.shape[0]
+    for src, dst in pairs:
+        src, dst = int(src), int(dst)
+        if not (0 <= src < n and 0 <= dst < n):
+            continue
+        key_cache[dst] = key_cache[src]
+        value_cache[dst] = value_cache[src]
+
+
 def gather_logical(cache: np.ndarray, block_table: Sequence[int], seq_len: int) -> np.ndarray:
     """Logically contiguous [H_kv, seq_len, D] view of one sequence: blocks in
     TABLE order (never sorted by physical id), concatenated along the token

@@ -16,22 +16,37 @@ The pages' manager, written out as a plain Python object:
 * ``append_slots_for_decode`` is the batched form with the all-or-nothing
   pre-check the scheduler needs ([mini-vLLM BM] "Block Manager 和 Scheduler
   如何协作", can_append_slots).
-* ``free_sequence`` appends the table back onto the free list once
-  ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  With
-  ``sort_on_release`` the free list is sorted afterwards, which is what
-  [leetcode-22] reference answer ``release_request`` does.
+* ``free_sequence`` drops the sequence's reference to each block of its
+  table and appends the blocks no table holds any more onto the free list,
+  in table order ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block";
+  [impl-detail] "块池" ref_count).  With ``sort_on_release`` the free list
+  is sorted afterwards, which is what [leetcode-22] reference answer
+  ``release_request`` does.
+* Prefix sharing and copy-on-write ([impl-detail] "Copy-on-Write共享"):
+  every block carries a reference count, the number of tables holding it.
+  ``share_prefix`` starts a sequence on the first ceil(n / bs) blocks of a
+  live donor (count + 1 each, "前缀共享").  An append whose token lands in a
+  block held by more than one table first takes a free block, queues a
+  copy of the shared block into it, drops one reference from the shared
+  block and puts the new block in the table ("Copy-on-Write机制").  The
+  queued (source, destination) pairs are drained by ``take_copies``; the
+  caller copies those blocks before it writes the step's rows.
 * ``check_invariants`` tests the invariants of [MiniPaged-Qwen] §15 and
-  [mini-vLLM BM] "正确性不变量".
+  [mini-vLLM BM] "正确性不变量", with I1 read for shared blocks as "each
+  block's count equals the number of tables holding it".
 
 Readings taken where the pages are open (each listed in the design notes):
 allocation from the front of an ordered free list, release by appending in
 table order; the boundary rule of [MiniPaged-Qwen] §9 (not leetcode-22's
 ``new_len % bs == 1``, which never allocates when block_size == 1); a prefill
-of 0 tokens creates a live empty sequence; sequence ids are non-negative.
+of 0 tokens creates a live empty sequence; sequence ids are non-negative;
+a shared prefix shares ceil(n / bs) blocks, its partial last block
+included, as [impl-detail]'s ``share_prefix_blocks`` does; the copy takes
+the whole block.
 """
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -88,6 +103,8 @@ class BlockManager:
             self.free = order
         self.sort_on_release = bool(sort_on_release)
         self.seqs: Dict[int, _Seq] = {}
+        self.ref: List[int] = [0] * self.num_blocks      # tables holding each block
+        self.copies: List[Tuple[int, int]] = []          # queued (source, destination)
 
     # -- queries -----------------------------------------------------------
     def num_free_blocks(self) -> int:
@@ -123,6 +140,18 @@ class BlockManager:
         """Per-sequence lengths ([MiniPaged-Qwen] §16.6)."""
         return np.array([self._live(s).length for s in seq_ids], dtype=np.int32)
 
+    def ref_count(self, block: int) -> int:
+        """Number of tables holding ``block`` ([impl-detail] "块池" ref_count)."""
+        if block < 0 or block >= self.num_blocks:
+            raise InvalidArgument("block id out of range")
+        return self.ref[block]
+
+    def take_copies(self) -> List[Tuple[int, int]]:
+        """The queued copy-on-write pairs (source, destination), oldest first;
+        the queue is left empty."""
+        out, self.copies = self.copies, []
+        return out
+
     # -- operations --------------------------------------------------------
     def allocate_for_prefill(self, seq_id: int, num_tokens: int) -> List[int]:
         """Create ``seq_id`` with ``num_tokens`` prompt tokens and return their
@@ -138,10 +167,31 @@ class BlockManager:
         seq = _Seq()
         seq.table = self.free[:need]
         del self.free[:need]
+        for pb in seq.table:
+            self.ref[pb] = 1
         seq.length = num_tokens
         self.seqs[seq_id] = seq
         bs = self.block_size
         return [seq.table[t // bs] * bs + t % bs for t in range(num_tokens)]
+
+    def share_prefix(self, donor_id: int, seq_id: int, num_tokens: int) -> None:
+        """Create ``seq_id`` holding the first ``num_tokens`` tokens of live
+        ``donor_id`` without copying: its table is the donor's first
+        ceil(num_tokens / bs) blocks, each block's count + 1
+        ([impl-detail] "前缀共享", share_prefix_blocks)."""
+        if seq_id < 0 or num_tokens < 0:
+            raise InvalidArgument("seq_id and num_tokens must be >= 0")
+        donor = self._live(donor_id)
+        if seq_id in self.seqs:
+            raise AlreadyPrefilled(f"sequence {seq_id} is already live")
+        if num_tokens > donor.length:
+            raise InvalidArgument("shared prefix longer than the donor")
+        seq = _Seq()
+        seq.table = donor.table[:blocks_needed(num_tokens, self.block_size)]
+        for pb in seq.table:
+            self.ref[pb] += 1
+        seq.length = num_tokens
+        self.seqs[seq_id] = seq
 
     def append_slot_for_decode(self, seq_id: int) -> int:
         """Slot of position len(seq); allocates one front block exactly when
@@ -154,7 +204,19 @@ class BlockManager:
         if logical_block == len(seq.table):
             if not self.free:
                 raise OutOfBlocks()
-            seq.table.append(self.free.pop(0))
+            new = self.free.pop(0)
+            self.ref[new] = 1
+            seq.table.append(new)
+        elif self.ref[seq.table[logical_block]] > 1:
+            # the token lands in a block other tables hold: copy on write
+            if not self.free:
+                raise OutOfBlocks()
+            old = seq.table[logical_block]
+            new = self.free.pop(0)
+            self.ref[old] -= 1
+            self.ref[new] = 1
+            seq.table[logical_block] = new
+            self.copies.append((old, new))
         physical_block = seq.table[logical_block]
         seq.length = L + 1
         return physical_block * self.block_size + block_offset
@@ -168,9 +230,21 @@ class BlockManager:
             raise InvalidArgument("duplicate sequence ids in one append")
         for s in ids:
             self._live(s)
-        opening = sum(1 for s in ids
-                      if self.seqs[s].length // self.block_size == len(self.seqs[s].table))
-        if opening > len(self.free):
+        # blocks this call takes: one per opened block, one per copy on
+        # write, counting the references earlier copies in the call drop
+        need = 0
+        dropped: Dict[int, int] = {}
+        for s in ids:
+            seq = self.seqs[s]
+            lb = seq.length // self.block_size
+            if lb == len(seq.table):
+                need += 1
+            else:
+                pb = seq.table[lb]
+                if self.ref[pb] - dropped.get(pb, 0) > 1:
+                    need += 1
+                    dropped[pb] = dropped.get(pb, 0) + 1
+        if need > len(self.free):
             raise OutOfBlocks()
         return [self.append_slot_for_decode(s) for s in ids]
 
@@ -178,7 +252,10 @@ class BlockManager:
         """Return every block of ``seq_id`` to the free list exactly once
         ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block")."""
         seq = self._live(seq_id)
-        self.free.extend(seq.table)
+        for pb in seq.table:
+            self.ref[pb] -= 1
+            if self.ref[pb] == 0:
+                self.free.append(pb)
         if self.sort_on_release:
             self.free.sort()
         del self.seqs[seq_id]
@@ -187,19 +264,27 @@ class BlockManager:
     def check_invariants(self) -> List[str]:
         """Names of violated invariants (empty when all hold).
 
-        I1 no physical id in two tables / twice in one table; I2 tables and
-        free list disjoint; I3 |allocated| + |free| == N; I4 ids in [0, N);
+        I1 no physical id twice in one table, and each block's count equals
+        the number of tables holding it (without sharing: no id in two
+        tables); I2 tables and free list disjoint, free blocks count 0;
+        I3 |distinct allocated| + |free| == N; I4 ids in [0, N);
         I5 len(table) == ceil(len / bs); I6 free list has no duplicates
         ([MiniPaged-Qwen] §15; [mini-vLLM BM] "正确性不变量";
-        [leetcode-22] Step 3 table).
+        [leetcode-22] Step 3 table; [impl-detail] "Copy-on-Write共享").
         """
         bad = []
         allocated = [pb for s in self.seqs.values() for pb in s.table]
-        if len(allocated) != len(set(allocated)):
+        holders: Dict[int, int] = {}
+        for pb in allocated:
+            holders[pb] = holders.get(pb, 0) + 1
+        if any(len(s.table) != len(set(s.table)) for s in self.seqs.values()) or \
+                any(self.ref[pb] != n for pb, n in holders.items()
+                    if 0 <= pb < self.num_blocks):
             bad.append("I1")
-        if set(allocated) & set(self.free):
+        if set(allocated) & set(self.free) or \
+                any(self.ref[pb] != 0 for pb in self.free if 0 <= pb < self.num_blocks):
             bad.append("I2")
-        if len(allocated) + len(self.free) != self.num_blocks:
+        if len(holders) + len(self.free) != self.num_blocks:
             bad.append("I3")
         if any(pb < 0 or pb >= self.num_blocks for pb in allocated + self.free):
             bad.append("I4")

@@ -89,6 +89,10 @@ SIGNATURES = {
     "pkv_append_slot_for_decode": (ctypes.c_int, [_P, _I64, _PI64]),
     "pkv_append_slots_for_decode": (ctypes.c_int, [_P, _PI64, _I32, _PI64, _PI32, _PI32]),
     "pkv_free_sequence": (ctypes.c_int, [_P, _I64]),
+    "pkv_share_prefix": (ctypes.c_int, [_P, _I64, _I64, _I32]),
+    "pkv_block_ref_count": (_I32, [_P, _I32]),
+    "pkv_take_block_copies": (ctypes.c_int, [_P, _PI32, _PI32, _I32, _PI32]),
+    "pkv_copy_blocks": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
     "pkv_context_len": (_I32, [_P, _I64]),
     "pkv_get_block_table": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
     "pkv_get_block_tables": (ctypes.c_int, [_P, _PI64, _I32, _I32, _I32, _PI32]),
@@ -265,6 +269,26 @@ class KVBlockManager:
     def free_sequence(self, seq_id: int) -> None:
         _check(self._lib.pkv_free_sequence(self._h, int(seq_id)), "free_sequence")
 
+    def share_prefix(self, donor_id: int, seq_id: int, num_tokens: int) -> None:
+        """New sequence on the donor's first ceil(num_tokens / bs) blocks
+        (see pkv_share_prefix)."""
+        _check(self._lib.pkv_share_prefix(self._h, int(donor_id), int(seq_id), int(num_tokens)),
+               "share_prefix")
+
+    def ref_count(self, block: int) -> int:
+        return _check(self._lib.pkv_block_ref_count(self._h, int(block)), "ref_count")
+
+    def take_copies(self):
+        """Drain the copy-on-write queue: (src int32, dst int32) numpy arrays."""
+        cap = self.num_blocks
+        src = np.empty(cap, dtype=np.int32)
+        dst = np.empty(cap, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_take_block_copies(self._h, _ptr(src, ctypes.c_int32),
+                                               _ptr(dst, ctypes.c_int32), cap, ctypes.byref(n)),
+               "take_copies")
+        return src[:n.value].copy(), dst[:n.value].copy()
+
 
 # --------------------------------------------------------------------------
 # Device entry points (torch tensors in, torch tensors out)
@@ -337,6 +361,20 @@ def paged_kv_write(key, value, slot_mapping, key_cache, value_cache, stream=None
                                       key_cache.data_ptr(), value_cache.data_ptr(),
                                       ctypes.byref(lay), _stream_handle(stream))
     _check(st, "paged_kv_write")
+
+
+def copy_blocks(src, dst, key_cache, value_cache, stream=None) -> None:
+    """Copy whole blocks src[i] -> dst[i] (host int32 arrays) in both pools
+    (see pkv_copy_blocks)."""
+    lay = cache_layout(key_cache, value_cache)
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    if src.shape != dst.shape or src.ndim != 1:
+        raise ValueError("src and dst must be 1-D arrays of one length")
+    st = _lib_handle().pkv_copy_blocks(_ptr(src, ctypes.c_int32), _ptr(dst, ctypes.c_int32),
+                                       len(src), key_cache.data_ptr(), value_cache.data_ptr(),
+                                       ctypes.byref(lay), _stream_handle(stream))
+    _check(st, "copy_blocks")
 
 
 def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
@@ -498,6 +536,7 @@ __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
+    "copy_blocks",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

@@ -10,6 +10,13 @@
 // The free list is a ring buffer of capacity num_blocks: allocation pops the
 // front, release pushes at the back, and the list can never hold more than
 // num_blocks ids while the invariants hold.
+//
+// Prefix sharing and copy-on-write ([impl-detail] "Copy-on-Write共享"): each
+// block has a reference count, the number of tables holding it; a block
+// returns to the free list when its count drops to 0.  An append whose
+// token lands in a block other tables also hold takes a free block for the
+// sequence and queues a (source, destination) copy that the caller runs on
+// the device before the step's write.
 #include <algorithm>
 #include <new>
 #include <unordered_map>
@@ -36,6 +43,8 @@ struct pkv_manager {
   int64_t head = 0;
   int64_t count = 0;
   std::unordered_map<int64_t, Sequence> seqs;
+  std::vector<int32_t> ref;                            // tables holding each block
+  std::vector<std::pair<int32_t, int32_t>> copies;     // queued (source, destination)
 
   int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
   int32_t pop_front() {
@@ -71,6 +80,7 @@ pkv_manager* pkv_manager_create(int32_t num_blocks, int32_t block_size,
     m->block_size = block_size;
     m->sort_on_release = (flags & PKV_SORT_ON_RELEASE) != 0;
     m->ring.resize(num_blocks);
+    m->ref.assign(num_blocks, 0);
     if (initial_free_order) {
       std::vector<char> seen(num_blocks, 0);
       for (int32_t i = 0; i < num_blocks; ++i) {
@@ -124,7 +134,7 @@ int pkv_allocate_for_prefill(pkv_manager* m, int64_t seq_id, int32_t num_tokens,
   } catch (...) {
     return PKV_ERR_INVALID;
   }
-  for (int64_t i = 0; i < need; ++i) m->pop_front();
+  for (int64_t i = 0; i < need; ++i) m->ref[m->pop_front()] = 1;
   if (slots_out) {
     const std::vector<int32_t>& t = m->seqs[seq_id].table;
     const int64_t bs = m->block_size;
@@ -133,8 +143,37 @@ int pkv_allocate_for_prefill(pkv_manager* m, int64_t seq_id, int32_t num_tokens,
   return PKV_OK;
 }
 
+int pkv_share_prefix(pkv_manager* m, int64_t donor_id, int64_t seq_id, int32_t num_tokens) {
+  if (!m || seq_id < 0 || num_tokens < 0) return PKV_ERR_INVALID;
+  auto d = m->seqs.find(donor_id);
+  if (d == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  if (m->seqs.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
+  if (num_tokens > d->second.length) return PKV_ERR_INVALID;
+  const int64_t n = m->blocks_for(num_tokens);
+  Sequence s;
+  try {
+    s.table.assign(d->second.table.begin(), d->second.table.begin() + n);
+    s.length = num_tokens;
+    m->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (int32_t pb : m->seqs[seq_id].table) ++m->ref[pb];
+  return PKV_OK;
+}
+
+// Does the next append of `s` take a block: one it opens, or a copy of a
+// block other tables hold (`dropped` = references earlier appends of the
+// same call release from that block)?
+static bool append_takes_block(const pkv_manager* m, const Sequence& s, int32_t dropped) {
+  const int64_t lb = s.length / m->block_size;
+  if (lb == static_cast<int64_t>(s.table.size())) return true;
+  return m->ref[s.table[lb]] - dropped > 1;
+}
+
 // One append on a live sequence already checked to have a block available
-// when it needs one ([MiniPaged-Qwen] §9.1-§9.3).
+// when it needs one and room in the copy queue ([MiniPaged-Qwen] §9.1-§9.3;
+// copy-on-write of [impl-detail] "Copy-on-Write机制").
 static int64_t append_one(pkv_manager* m, Sequence& s, int32_t* new_block) {
   const int64_t bs = m->block_size;
   const int64_t L = s.length;
@@ -143,7 +182,16 @@ static int64_t append_one(pkv_manager* m, Sequence& s, int32_t* new_block) {
   *new_block = -1;
   if (logical_block == static_cast<int64_t>(s.table.size())) {
     int32_t pb = m->pop_front();
+    m->ref[pb] = 1;
     s.table.push_back(pb);
+    *new_block = pb;
+  } else if (m->ref[s.table[logical_block]] > 1) {
+    const int32_t old = s.table[logical_block];
+    const int32_t pb = m->pop_front();
+    --m->ref[old];
+    m->ref[pb] = 1;
+    s.table[logical_block] = pb;
+    m->copies.emplace_back(old, pb);
     *new_block = pb;
   }
   s.length = static_cast<int32_t>(L + 1);
@@ -157,9 +205,10 @@ int pkv_append_slot_for_decode(pkv_manager* m, int64_t seq_id, int64_t* slot_out
   Sequence& s = it->second;
   if (s.length == INT32_MAX) return PKV_ERR_INVALID;
   const bool opens = (s.length / m->block_size) == static_cast<int64_t>(s.table.size());
-  if (opens && m->count == 0) return PKV_ERR_OOM;
+  if (append_takes_block(m, s, 0) && m->count == 0) return PKV_ERR_OOM;
   try {
     if (opens) s.table.reserve(s.table.size() + 1);
+    m->copies.reserve(m->copies.size() + 1);
   } catch (...) {
     return PKV_ERR_INVALID;
   }
@@ -181,20 +230,33 @@ int pkv_append_slots_for_decode(pkv_manager* m, const int64_t* seq_ids, int32_t 
   } catch (...) {
     return PKV_ERR_INVALID;
   }
-  int64_t opening = 0;
   for (int32_t i = 0; i < n; ++i) {
     auto it = m->seqs.find(seq_ids[i]);
     if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
     Sequence& s = it->second;
     if (s.length == INT32_MAX) return PKV_ERR_INVALID;
-    if (s.length / m->block_size == static_cast<int64_t>(s.table.size())) ++opening;
     seqs.push_back(&s);
   }
-  if (opening > m->count) return PKV_ERR_OOM;
+  // blocks the call takes, in array order: opened blocks and copies on write
+  // (a copy drops one reference from the shared block for later rows)
+  int64_t need = 0;
   try {
+    std::unordered_map<int32_t, int32_t> dropped;
+    for (Sequence* s : seqs) {
+      const int64_t lb = s->length / m->block_size;
+      const bool opens = lb == static_cast<int64_t>(s->table.size());
+      const int32_t pb = opens ? -1 : s->table[lb];
+      const int32_t d = opens ? 0 : (dropped.count(pb) ? dropped[pb] : 0);
+      if (append_takes_block(m, *s, d)) {
+        ++need;
+        if (!opens) dropped[pb] = d + 1;
+      }
+    }
+    if (need > m->count) return PKV_ERR_OOM;
     for (Sequence* s : seqs)
       if (s->length / m->block_size == static_cast<int64_t>(s->table.size()))
         s->table.reserve(s->table.size() + 1);
+    m->copies.reserve(m->copies.size() + need);
   } catch (...) {
     return PKV_ERR_INVALID;
   }
@@ -212,7 +274,8 @@ int pkv_free_sequence(pkv_manager* m, int64_t seq_id) {
   if (!m) return PKV_ERR_INVALID;
   auto it = m->seqs.find(seq_id);
   if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
-  for (int32_t pb : it->second.table) m->push_back(pb);
+  for (int32_t pb : it->second.table)
+    if (--m->ref[pb] == 0) m->push_back(pb);
   if (m->sort_on_release) m->sort_free();
   m->seqs.erase(it);
   return PKV_OK;
@@ -271,29 +334,51 @@ int pkv_get_free_list(const pkv_manager* m, int32_t* out, int32_t cap, int32_t* 
   return PKV_OK;
 }
 
+int32_t pkv_block_ref_count(const pkv_manager* m, int32_t block) {
+  if (!m || block < 0 || block >= m->num_blocks) return PKV_ERR_INVALID;
+  return m->ref[block];
+}
+
+int pkv_take_block_copies(pkv_manager* m, int32_t* src, int32_t* dst, int32_t cap,
+                          int32_t* count_out) {
+  if (!m || cap < 0 || !count_out || (cap > 0 && (!src || !dst))) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(m->copies.size()) > cap) return PKV_ERR_INVALID;
+  for (size_t i = 0; i < m->copies.size(); ++i) {
+    src[i] = m->copies[i].first;
+    dst[i] = m->copies[i].second;
+  }
+  *count_out = static_cast<int32_t>(m->copies.size());
+  m->copies.clear();
+  return PKV_OK;
+}
+
 int pkv_check_invariants(const pkv_manager* m) {
   if (!m) return PKV_ERR_INVALID;
   const int64_t N = m->num_blocks;
-  std::vector<int32_t> owners(N, 0);
-  int64_t allocated = 0;
+  std::vector<int32_t> holders(N, 0);
+  int64_t distinct = 0;
   for (const auto& kv : m->seqs) {
     const Sequence& s = kv.second;
     if (static_cast<int64_t>(s.table.size()) != m->blocks_for(s.length)) return PKV_ERR_INVARIANT;  // I5
-    for (int32_t pb : s.table) {
+    for (size_t i = 0; i < s.table.size(); ++i) {
+      const int32_t pb = s.table[i];
       if (pb < 0 || pb >= N) return PKV_ERR_INVARIANT;           // I4
-      if (++owners[pb] > 1) return PKV_ERR_INVARIANT;            // I1
-      ++allocated;
+      for (size_t j = 0; j < i; ++j)
+        if (s.table[j] == pb) return PKV_ERR_INVARIANT;          // I1: twice in one table
+      if (holders[pb]++ == 0) ++distinct;
     }
   }
+  for (int64_t pb = 0; pb < N; ++pb)
+    if (holders[pb] > 0 && m->ref[pb] != holders[pb]) return PKV_ERR_INVARIANT;  // I1: counts
   std::vector<char> in_free(N, 0);
   for (int64_t i = 0; i < m->count; ++i) {
     int32_t pb = m->free_at(i);
     if (pb < 0 || pb >= N) return PKV_ERR_INVARIANT;             // I4
     if (in_free[pb]) return PKV_ERR_INVARIANT;                   // I6
     in_free[pb] = 1;
-    if (owners[pb]) return PKV_ERR_INVARIANT;                    // I2
+    if (holders[pb] || m->ref[pb] != 0) return PKV_ERR_INVARIANT;  // I2
   }
-  if (allocated + m->count != N) return PKV_ERR_INVARIANT;       // I3
+  if (distinct + m->count != N) return PKV_ERR_INVARIANT;        // I3
   return PKV_OK;
 }
 

@@ -1,0 +1,70 @@
+// Whole-block copies for copy-on-write ([impl-detail] "Copy-on-Write机制":
+// when a sequence writes into a block other tables still hold, it gets a new
+// block that first receives the shared block's K and V).
+//
+// One workgroup per (pair, K or V, KV head) moves that head's block_size
+// token rows, which sit contiguously (head_stride >= block_size * head_dim),
+// in 16-byte lanes: a plain HBM-bound copy, coalesced on both sides.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int kCopyPairs = 256;   // pairs carried by one launch's arguments
+constexpr int kCopyThreads = 256;
+
+struct CopyMeta {
+  int32_t src[kCopyPairs];
+  int32_t dst[kCopyPairs];
+};
+
+__global__ void __launch_bounds__(kCopyThreads)
+block_copy_kernel(CopyMeta meta, int32_t num_blocks, int32_t heads, int64_t block_stride16,
+                  int64_t head_stride16, int32_t head_chunks, uint4* __restrict__ key_cache,
+                  uint4* __restrict__ value_cache) {
+  const int32_t item = blockIdx.x;
+  const int32_t pair = item / (2 * heads);
+  const int32_t rem = item - pair * 2 * heads;
+  const int32_t half = rem / heads;          // 0: key cache, 1: value cache
+  const int32_t h = rem - half * heads;
+  const int32_t s = meta.src[pair], d = meta.dst[pair];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  uint4* base = half == 0 ? key_cache : value_cache;
+  const uint4* from = base + s * block_stride16 + h * head_stride16;
+  uint4* to = base + d * block_stride16 + h * head_stride16;
+  for (int32_t i = threadIdx.x; i < head_chunks; i += kCopyThreads) to[i] = from[i];
+}
+
+}  // namespace
+
+extern "C" int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
+                               void* value_cache, const pkv_cache_layout* l, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK || n < 0) return PKV_ERR_INVALID;
+  if (n == 0) return PKV_OK;
+  if (!src || !dst || !key_cache || !value_cache) return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const int64_t head_bytes = static_cast<int64_t>(l->block_size) * l->head_dim * eb;
+  if (head_bytes % 16 != 0 || (l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) % 16) != 0)
+    return PKV_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t p0 = 0; p0 < n; p0 += kCopyPairs) {
+    const int32_t m = n - p0 < kCopyPairs ? n - p0 : kCopyPairs;
+    CopyMeta meta;
+    for (int32_t i = 0; i < m; ++i) {
+      meta.src[i] = src[p0 + i];
+      meta.dst[i] = dst[p0 + i];
+    }
+    const int64_t grid = static_cast<int64_t>(m) * 2 * l->num_kv_heads;
+    hipLaunchKernelGGL(block_copy_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kCopyThreads), 0, s,
+                       meta, l->num_blocks, l->num_kv_heads, l->block_stride * eb / 16,
+                       l->head_stride * eb / 16, static_cast<int32_t>(head_bytes / 16),
+                       static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache));
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}

@@ -133,10 +133,10 @@ kv_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
 // One decode step's metadata travels in the kernel arguments (no separate
 // host-to-device copy): per row i the new token's slot and the row's length
 // after the append.  The kernel writes the K/V rows like kv_write_kernel,
-// publishes the block a row opened (a token at offset 0 of its block opened
-// that block at logical index (len - 1) / bs, [MiniPaged-Qwen] §9.2) into the
-// device block table, and copies the lengths to `lens_out` for the
-// attention launch that follows.
+// publishes the block holding each row's new token (table entry
+// (len - 1) / bs: a block the append opened, [MiniPaged-Qwen] §9.2, or one
+// it copied on write) into the device block table, and copies the lengths
+// to `lens_out` for the attention launch that follows.
 constexpr int kStepRows = 256;
 struct StepMeta {
   int64_t slots[kStepRows];
@@ -160,8 +160,7 @@ decode_write_kernel(StepMeta meta, int32_t n, int32_t row0, const uint4* __restr
     const int32_t len = meta.lens[t];
     const int32_t row = row0 + t;
     if (lens_out) lens_out[row] = len;
-    if (tables && row < table_rows && len > 0 && slot >= 0 && slot < capacity &&
-        (len - 1) % block_size == 0) {
+    if (tables && row < table_rows && len > 0 && slot >= 0 && slot < capacity) {
       const int32_t col = (len - 1) / block_size;
       if (col < table_stride) tables[static_cast<int64_t>(row) * table_stride + col] =
           static_cast<int32_t>(slot / block_size);
@@ -926,8 +925,8 @@ constexpr int kWaitLgkm0 = 0xc07f;
 
 // The stream kernel's body.  FUSED: the decode-step form, which also does
 // the step's write: the lengths (after the append) and the new tokens'
-// slots come in `meta`; workgroup 0 publishes the lengths and the blocks
-// the step opened; the tile holding a sequence's new token takes its block
+// slots come in `meta`; workgroup 0 publishes the lengths and the table
+// entry of each new token's block; the tile holding a sequence's new token takes its block
 // from the slot, and the one wave per KV head that reads that tile
 // replaces the token's row (stale in the pool until then) with the new K/V
 // row and stores that row into the pool.
@@ -962,8 +961,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       for (int b = threadIdx.x; b < B; b += blockDim.x) {
         const int L = meta->lens[b];
         if (a.lens_out) a.lens_out[b] = L;
-        if (a.tables_w && b < a.table_rows && L > 0 && (L - 1) % a.block_size == 0 &&
-            (L - 1) / a.block_size < a.table_stride)
+        if (a.tables_w && b < a.table_rows && L > 0 && (L - 1) / a.block_size < a.table_stride)
           a.tables_w[static_cast<int64_t>(b) * a.table_stride + (L - 1) / a.block_size] =
               static_cast<int32_t>(meta->slots[b] / a.block_size);
       }

@@ -4,7 +4,9 @@ device-resident block tables and the decode step that ties them together.
 A decode step is the hot path of [MiniPaged-Qwen] §10 and §13 in order:
 
   1. block manager append for every row (one batched C call; all or nothing,
-     [mini-vLLM BM] "Block Manager 和 Scheduler 如何协作"),
+     [mini-vLLM BM] "Block Manager 和 Scheduler 如何协作"), then, when
+     sequences share blocks, the copies of the blocks the append copied on
+     write ([impl-detail] "Copy-on-Write机制"),
   2. the write of the new K/V rows ([MiniPaged-Qwen] §12), with the blocks
      the append opened published into the device block table and the
      lengths stored on the device, the step's slots and lengths travelling
@@ -27,8 +29,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, decode_step, decode_write, new_pool, paged_decode_attention,
-               paged_kv_write, workspace_size)
+from . import (KVBlockManager, copy_blocks, decode_step, decode_write, new_pool,
+               paged_decode_attention, paged_kv_write, workspace_size)
 
 
 class PagedKVEngine:
@@ -57,6 +59,7 @@ class PagedKVEngine:
         self._newb = np.empty(max_rows, dtype=np.int32)
         self._ws = None
         self._nq = num_q_heads
+        self._sharing = False      # set once any table shares a block
 
     # -- admission / release ------------------------------------------------
     def prefill(self, seq_id: int, row: int, key: torch.Tensor, value: torch.Tensor,
@@ -85,6 +88,14 @@ class PagedKVEngine:
         for sid, row in zip(seq_ids, rows):
             self._publish_row(int(sid), int(row))
         return slots
+
+    def share_prefix(self, donor_id: int, seq_id: int, row: int, num_tokens: int) -> None:
+        """Admit ``seq_id`` into ``row`` holding the first ``num_tokens`` tokens
+        of live ``donor_id`` on the donor's blocks, no copy
+        ([impl-detail] "前缀共享"); its appends copy a shared block first."""
+        self.manager.share_prefix(donor_id, seq_id, num_tokens)
+        self._sharing = True
+        self._publish_row(seq_id, row)
 
     def _publish_row(self, seq_id: int, row: int):
         tab = self.manager.block_tables([seq_id], self.width, -1)
@@ -120,6 +131,10 @@ class PagedKVEngine:
         separate write launch."""
         n = len(seq_ids)
         self.manager.append_slots_for_decode(seq_ids, self.slots[:n], self.lens[:n], self._newb[:n])
+        if self._sharing:
+            src, dst = self.manager.take_copies()
+            if len(src):
+                copy_blocks(src, dst, self.key_cache, self.value_cache)
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
         if not (fused and self.partition_tokens == 0 and n > 0):

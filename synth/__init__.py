@@ -323,7 +323,35 @@ def manager_op_trace(seed: int, n_ops: int, max_id: int = 40, max_prefill: int =
     return ops
 
 
+def manager_share_trace(seed: int, n_ops: int, max_id: int = 24, max_prefill: int = 40):
+    """Random ops with prefix sharing: prefills, shares of a (random-length)
+    prefix of a donor, single and batched appends, frees and capacity
+    queries, including ones that must fail (unknown donors, live targets,
+    prefixes longer than the donor, OOM, duplicate ids)."""
+    rng = np.random.default_rng(seed)
+    ops = []
+    for _ in range(n_ops):
+        u = rng.random()
+        if u < 0.2:
+            ops.append(("prefill", int(rng.integers(max_id)), int(rng.integers(0, max_prefill + 1))))
+        elif u < 0.4:
+            ops.append(("share", int(rng.integers(max_id)), int(rng.integers(max_id)),
+                        int(rng.integers(0, max_prefill + 8))))
+        elif u < 0.6:
+            ops.append(("append", int(rng.integers(max_id))))
+        elif u < 0.8:
+            k = int(rng.integers(1, 9))
+            ids = [int(x) for x in rng.integers(max_id, size=k)]
+            ops.append(("append_batch", tuple(ids)))
+        elif u < 0.97:
+            ops.append(("free", int(rng.integers(max_id))))
+        else:
+            ops.append(("can_allocate", int(rng.integers(0, 4 * max_prefill))))
+    return ops
+
+
 __all__ = [
+    "manager_share_trace",
     "CONFIGS", "CONFIG_BY_INDEX", "Config", "DecodeWorkload", "decode_workload",
     "serving_trace", "ServingTrace", "ServingStep", "Refill", "churn_events",
     "manager_op_trace", "extra_step_tensors", "to_storage", "poison_array", "normal",

@@ -123,3 +123,60 @@ def test_churn_replay_matches_oracle():
         else:
             c.free_sequence(ev[1])
     assert c.free_list() == o.free
+
+
+def _run_share(mgr, op, impl):
+    """Apply a sharing-trace op; returns (outcome, result, queued copies)."""
+    try:
+        if op[0] == "share":
+            mgr.share_prefix(op[1], op[2], op[3])
+            r = ("ok", None)
+        else:
+            r = _run(mgr, op, impl)
+    except (oracle.ManagerError, pkv.PkvError) as e:
+        r = None
+        for o, c in ERR.items():
+            if isinstance(e, o) or isinstance(e, c):
+                r = ("err", o.__name__)
+        if r is None:
+            raise
+    if impl == "c":
+        src, dst = mgr.take_copies()
+        copies = list(zip(src.tolist(), dst.tolist()))
+    else:
+        copies = mgr.take_copies()
+    return r, copies
+
+
+@pytest.mark.parametrize("seed,n_blocks,bs,sort", [(41, 40, 4, False), (42, 12, 1, True),
+                                                   (43, 20, 16, False), (44, 25, 3, True)])
+def test_random_share_traces_match_oracle(seed, n_blocks, bs, sort):
+    """Prefix sharing and copy-on-write: identical outcomes, slots, tables,
+    reference counts, copy queues and free-list order after every op."""
+    order = np.random.default_rng(seed).permutation(n_blocks)
+    o = oracle.BlockManager(n_blocks, bs, order, sort_on_release=sort)
+    c = pkv.KVBlockManager(n_blocks, bs, order, sort_on_release=sort)
+    ids = list(range(24))
+    kinds, n_copies = set(), 0
+    for op in synth.manager_share_trace(seed, 2000):
+        ro = _run_share(o, op, "o")
+        rc = _run_share(c, op, "c")
+        assert ro == rc, (op, ro, rc)
+        kinds.add(ro[0][1] if ro[0][0] == "err" else "ok")
+        n_copies += len(ro[1])
+        _same_state(o, c, ids)
+        assert [c.ref_count(b) for b in range(n_blocks)] == o.ref
+    assert {"ok", "OutOfBlocks", "NotLive", "AlreadyPrefilled", "InvalidArgument"} <= kinds
+    assert n_copies > 0 or bs == 1       # with bs == 1 no block is ever partly filled
+
+
+def test_batched_append_reports_copy_on_write_blocks():
+    m = pkv.KVBlockManager(8, 4)
+    m.allocate_for_prefill(0, 6)
+    m.share_prefix(0, 1, 6)
+    slots, lens, newb = m.append_slots_for_decode([1, 0])
+    assert newb.tolist() == [2, -1] and lens.tolist() == [7, 7]
+    assert slots.tolist() == [2 * 4 + 2, 1 * 4 + 2]
+    src, dst = m.take_copies()
+    assert src.tolist() == [1] and dst.tolist() == [2]
+    assert m.block_table(1) == [0, 2] and m.ref_count(1) == 1
