@@ -1,0 +1,112 @@
+"""Pins of the oracle's FP8 KV rows (oracle/quant.py): the E4M3 code table
+against the OCP 8-bit floating point definition (closed forms and the
+format's named values), round-to-nearest-even against brute force over every
+code, the per-row power-of-two scale against its defining inequality, the
+quantisation error against the format's half-ulp bound, and FP8 paged
+attention against the online-softmax oracle run on the read-back values.
+CPU only."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quant
+
+
+def test_named_e4m3_values():
+    # OCP FP8 E4M3: bias 7, largest finite S.1111.110 = 448, NaN S.1111.111,
+    # smallest normal 2^-6, smallest subnormal 2^-9, no infinities.
+    named = {0x00: 0.0, 0x38: 1.0, 0x3F: 1.875, 0x40: 2.0, 0xC0: -2.0, 0x7E: 448.0,
+             0xFE: -448.0, 0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x01: 2.0 ** -9,
+             0x30: 0.5, 0x77: 240.0}
+    for code, val in named.items():
+        assert quant.e4m3_decode(code) == val, hex(code)
+        assert quant.e4m3_encode(val) == code, hex(code)
+    assert math.isnan(quant.e4m3_decode(0x7F)) and math.isnan(quant.e4m3_decode(0xFF))
+    assert quant.e4m3_encode(-0.0) == 0x80 and quant.e4m3_encode(0.0) == 0x00
+    finite = [quant.e4m3_decode(c) for c in range(256) if c not in (0x7F, 0xFF)]
+    assert len(set(finite)) == 253            # +0 and -0 compare equal
+    assert max(finite) == 448.0 and min(finite) == -448.0
+
+
+def test_every_code_round_trips():
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        assert quant.e4m3_encode(quant.e4m3_decode(c)) == c
+
+
+def _brute_force(x):
+    best, best_d = None, None
+    for c in range(0x7F):                     # non-negative finite codes
+        d = abs(quant.e4m3_decode(c) - abs(x))
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return best | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+
+def test_round_to_nearest_even_against_brute_force():
+    rng = np.random.default_rng(3)
+    xs = list(rng.uniform(-448, 448, 300)) + list(rng.uniform(-0.02, 0.02, 300))
+    # exact midpoints between neighbouring codes (the ties)
+    for c in range(0x7D):
+        xs.append((quant.e4m3_decode(c) + quant.e4m3_decode(c + 1)) / 2)
+    for x in xs:
+        x = float(np.float32(x))
+        assert quant.e4m3_encode(x) == _brute_force(x), x
+    assert quant.e4m3_encode(1.0625) == 0x38 and quant.e4m3_encode(1.1875) == 0x3A
+    assert quant.e4m3_encode(1.5 * 2.0 ** -9) == 0x02 and quant.e4m3_encode(0.5 * 2.0 ** -9) == 0x00
+
+
+def test_row_scale_is_the_smallest_fitting_power_of_two():
+    rng = np.random.default_rng(4)
+    for _ in range(500):
+        row = (rng.standard_normal(128) * 10.0 ** rng.uniform(-6, 6)).astype(np.float32)
+        e = quant.row_scale_exponent(row)
+        amax = float(np.abs(row).max())
+        assert amax <= 448.0 * 2.0 ** e
+        assert amax > 448.0 * 2.0 ** (e - 1)
+    for k in (-20, 0, 3, 40):
+        assert quant.row_scale_exponent(np.array([448.0 * 2.0 ** k], np.float32)) == k
+        assert quant.row_scale_exponent(np.array([449.0 * 2.0 ** k], np.float32)) == k + 1
+    assert quant.row_scale_exponent(np.zeros(8, np.float32)) == 0
+
+
+def test_quantisation_error_within_half_ulp():
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        row = (rng.standard_normal(128) * rng.uniform(0.01, 100)).astype(np.float32)
+        codes, sb = quant.quantize_row(row)
+        back = quant.dequantize(codes[None], np.array([sb]))[0]
+        e = sb - 127
+        y = np.abs(row.astype(np.float64)) / 2.0 ** e
+        ulp = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 1e-300))) - 3), 2.0 ** -9)
+        assert np.all(np.abs(back - row) <= 0.5 * ulp * 2.0 ** e + 0.0)
+        assert np.abs(row).max() / 2.0 ** e > 224.0      # the top code range is used
+
+
+def test_fp8_attention_matches_online_oracle_on_read_back_values():
+    rng = np.random.default_rng(6)
+    N, H, bs, D, hq = 12, 2, 4, 16, 4
+    kc, vc, ks, vs = quant.new_fp8_pool(N, H, bs, D)
+    m = oracle.BlockManager(N, bs, rng.permutation(N))
+    lens = [7, 1, 12]
+    for b, L in enumerate(lens):
+        slots = m.allocate_for_prefill(b, L)
+        k = (rng.standard_normal((L, H, D)) * 3).astype(np.float32)
+        v = rng.standard_normal((L, H, D)).astype(np.float32)
+        quant.write_kv_fp8(k, v, slots, kc, vc, ks, vs, bs)
+    q = rng.standard_normal((3, hq, D)).astype(np.float32)
+    tabs = m.block_tables([0, 1, 2], 3, -1)
+    got = quant.decode_attention_fp8(q, "f32", kc, vc, ks, vs, tabs, lens, 0.25)
+    # the read-back values as a float32 pool (exact: E4M3 * 2^e fits float32)
+    kf = quant.dequantize(kc, ks).astype(np.float32)
+    vf = quant.dequantize(vc, vs).astype(np.float32)
+    for b, L in enumerate(lens):
+        ref = oracle.decode_attention_online(q[b], kf, vf, m.block_table(b), L, 0.25, "f32")
+        assert np.abs(got[b] - ref).max() < 1e-12
+    # untouched rows keep the poison pattern
+    used = {pb for b in range(3) for pb in m.block_table(b)}
+    for pb in set(range(N)) - used:
+        assert np.all(kc[pb] == 0x7F) and np.all(ks[pb] == 0xFF)
