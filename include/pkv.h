@@ -48,7 +48,9 @@ extern "C" {
 const char* pkv_status_string(int status);
 
 /* ------------------------------------------------------------- cache layout */
-typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3: 8-bit KV codes (OCP E4M3, largest finite 448) with one
+ * power-of-two scale byte per token row; see the FP8 section below. */
+typedef enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 /*
  * Where token `off` of KV head `h` of physical block `pb` lives:
@@ -422,6 +424,70 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
                           int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
                           int32_t max_context_len, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------- FP8 KV */
+/*
+ * 8-bit KV blocks ([impl-detail] "实践建议": the KV inside a block can be
+ * quantised on its own).  A cache with layout->dtype == PKV_FP8_E4M3 holds
+ * one byte per element: an OCP E4M3 code (bias 7, largest finite 448, no
+ * infinities).  Every token row of every KV head is quantised on its own
+ * when it is written, with a power-of-two scale 2^e stored as one OCP E8M0
+ * byte (e + 127) per row:
+ *     e    = smallest integer with max|x| <= 448 * 2^e, clamped to
+ *            [-126, 127] (0 for an all-zero row),
+ *     code = E4M3(x * 2^-e), round to nearest, ties to even; a negative-zero
+ *            code is stored as 0x00,
+ * and the row reads back as E4M3(code) * 2^e.  Scale bytes mirror the code
+ * layout with one byte per row: the scale of row (pb, h, off) is at
+ *     scales + pb * (block_stride / head_dim) + h * (head_stride / head_dim) + off
+ * (an interleaved scale pool [N, 2, H_kv, bs] next to a code pool
+ * [N, 2, H_kv, bs, D]: key scales = pool, value scales = pool + H_kv * bs).
+ * Inputs must be finite.  The write calls accept head_dim 64 or 128; the
+ * attention takes the stream path shapes (head_dim 128, H_kv <= 8,
+ * H_q / H_kv <= 8, block_size a multiple of 16).
+ */
+
+/*
+ * paged_kv_write into 8-bit blocks: key/value (device, [num_tokens, H_kv,
+ * D] contiguous, 16-byte aligned) in src_dtype (PKV_F32, PKV_F16 or
+ * PKV_BF16) are quantised row by row as above and stored at slot_mapping
+ * (device int64 [num_tokens]; slots outside the pool are skipped) with their
+ * scale bytes in key_scales / value_scales (device).  Errors: INVALID,
+ * UNSUPPORTED, HIP.
+ */
+int paged_kv_write_fp8(const void* key, const void* value, int32_t src_dtype,
+                       const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                       void* value_cache, uint8_t* key_scales, uint8_t* value_scales,
+                       const pkv_cache_layout* layout, void* stream);
+
+/* pkv_decode_write into 8-bit blocks: the same quantised write with the
+ * step's slots and lengths from host memory (kernel arguments), the block
+ * table entries and lens_out as pkv_decode_write sets them. */
+int pkv_decode_write_fp8(const void* key, const void* value, int32_t src_dtype,
+                         const int64_t* slots, const int32_t* lens, int32_t num_rows,
+                         void* key_cache, void* value_cache, uint8_t* key_scales,
+                         uint8_t* value_scales, const pkv_cache_layout* layout,
+                         int32_t* block_tables, int32_t table_rows, int32_t block_table_stride,
+                         int32_t* lens_out, void* stream);
+
+/*
+ * paged_decode_attention over 8-bit blocks: the same quantity, with each
+ * cached row read back as E4M3(code) * 2^e.  q (device, [num_seqs,
+ * num_q_heads, 128]) is q_dtype (PKV_BF16 or PKV_F16); out is PKV_F32 or
+ * q_dtype.  phases: 1 = the attention kernel only, 2 = the merge only, 3 =
+ * both (the pair 1 then 2 on one stream equals 3).  The workspace is that of
+ * paged_decode_attention with partition_tokens 0.  Scale pointers must be
+ * 4-byte aligned.  Errors: INVALID, UNSUPPORTED (shapes outside the stream
+ * path), WORKSPACE, HIP.
+ */
+int paged_decode_attention_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                               const void* key_cache, const void* value_cache,
+                               const uint8_t* key_scales, const uint8_t* value_scales,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_context_len, float scale, const pkv_cache_layout* layout,
+                               int32_t phases, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /*
  * Apply the table growth of one batched append to a device-resident block

@@ -11,7 +11,9 @@ block's rows never need re-quantising as the block fills:
 * scale: one power of two per row, stored as an OCP E8M0 byte (value
   2^(byte - 127)): the smallest 2^e with max|x| / 2^e <= 448, e clamped to
   [-126, 127]; an all-zero row takes e = 0;
-* code = E4M3(x * 2^-e), and the row reads back as decode(code) * 2^e.
+* code = E4M3(x * 2^-e), and the row reads back as decode(code) * 2^e; a
+  code of negative zero (0x80) is stored as 0x00, so stored codes never use
+  0x80, which the other 8-bit E4M3 variant (no negative zero) reads as NaN.
 
 Multiplying by 2^-e is exact in float32 (the inputs are float32-widened
 16-bit or float32 values), so the only rounding is the E4M3 one.  Pins:
@@ -76,6 +78,7 @@ def quantize_row(row: np.ndarray) -> Tuple[np.ndarray, int]:
     e = row_scale_exponent(row)
     scaled = row.astype(np.float32) * np.float32(2.0 ** -e)
     codes = np.array([e4m3_encode(v) for v in scaled], dtype=np.uint8)
+    codes[codes == 0x80] = 0x00
     return codes, e + 127
 
 
@@ -83,6 +86,30 @@ def dequantize(codes: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
     """float64 values of codes [..., D] with per-row scale bytes [...]."""
     table = np.array([e4m3_decode(c) for c in range(256)], dtype=np.float64)
     return table[codes] * np.exp2(scale_bytes.astype(np.float64) - 127.0)[..., None]
+
+
+def quantize_rows(rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """quantize_row over the last axis of float32 ``rows`` [..., D], in
+    numpy array form (same steps: the scale exponent from frexp of the row
+    max, the exact power-of-two scaling, then E4M3 round to nearest even);
+    returns (codes uint8 [..., D], scale bytes uint8 [...])."""
+    x = rows.astype(np.float32)
+    amax = np.abs(x).max(axis=-1).astype(np.float64)
+    m, k = np.frexp(amax)
+    e = (k - 1) - 8 + (2.0 * m > 1.75)
+    e = np.where(amax == 0.0, 0, np.clip(e, -126, 127)).astype(np.int64)
+    y = (x.astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None])   # exact
+    a = np.abs(y)
+    sign = np.where(np.signbit(y), 0x80, 0)
+    sub = a < 2.0 ** -6
+    E = np.floor(np.log2(np.where(sub, 1.0, a))).astype(np.int64)
+    E = np.where(np.exp2(E.astype(np.float64)) > a, E - 1, E)                   # guard log2 rounding
+    E = np.where(np.exp2(E.astype(np.float64) + 1) <= a, E + 1, E)
+    r = np.rint(a * np.exp2((3 - E).astype(np.float64))).astype(np.int64)
+    normal = ((E + 7) << 3) + (r - 8)
+    code = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), normal)
+    code = np.where(code == 0, 0, code | sign)
+    return code.astype(np.uint8), (e + 127).astype(np.uint8)
 
 
 def new_fp8_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int):
@@ -108,9 +135,8 @@ def write_kv_fp8(key: np.ndarray, value: np.ndarray, slot_mapping: Sequence[int]
         if slot < 0 or slot >= capacity:
             continue
         pb, off = split_slot(slot, block_size)
-        for h in range(key.shape[1]):
-            key_cache[pb, h, off], key_scales[pb, h, off] = quantize_row(key[i, h])
-            value_cache[pb, h, off], value_scales[pb, h, off] = quantize_row(value[i, h])
+        key_cache[pb, :, off], key_scales[pb, :, off] = quantize_rows(key[i])
+        value_cache[pb, :, off], value_scales[pb, :, off] = quantize_rows(value[i])
 
 
 def decode_attention_fp8(q: np.ndarray, q_dtype: str, key_cache: np.ndarray,

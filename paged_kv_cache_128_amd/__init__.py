@@ -22,7 +22,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_lib", "libpkv.so")
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 SORT_ON_RELEASE = 1
 
 STATUS = {0: "OK", -1: "INVALID", -2: "OOM", -3: "NOT_LIVE", -4: "ALREADY_PREFILLED",
@@ -93,6 +93,13 @@ SIGNATURES = {
     "pkv_block_ref_count": (_I32, [_P, _I32]),
     "pkv_take_block_copies": (ctypes.c_int, [_P, _PI32, _PI32, _I32, _PI32]),
     "pkv_copy_blocks": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "paged_kv_write_fp8": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _P, _P, _P, _P,
+                                          ctypes.POINTER(CacheLayout), _P]),
+    "pkv_decode_write_fp8": (ctypes.c_int, [_P, _P, _I32, _PI64, _PI32, _I32, _P, _P, _P, _P,
+                                            ctypes.POINTER(CacheLayout), _P, _I32, _I32, _P, _P]),
+    "paged_decode_attention_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _I32, _P,
+                                                  _I32, _I32, _I32, _F32, ctypes.POINTER(CacheLayout),
+                                                  _I32, _P, _SZ, _P]),
     "pkv_context_len": (_I32, [_P, _I64]),
     "pkv_get_block_table": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
     "pkv_get_block_tables": (ctypes.c_int, [_P, _PI64, _I32, _I32, _I32, _PI32]),
@@ -300,7 +307,8 @@ def _torch():
 
 def dtype_code(dtype) -> int:
     torch = _torch()
-    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+    codes = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+             torch.float8_e4m3fn: PKV_FP8_E4M3}
     if dtype not in codes:
         raise ValueError(f"unsupported dtype {dtype}")
     return codes[dtype]
@@ -326,6 +334,117 @@ def cache_layout(key_cache, value_cache=None) -> CacheLayout:
                 or value_cache.dtype != key_cache.dtype:
             raise ValueError("value_cache must match key_cache in shape, strides and dtype")
     return CacheLayout(n, h, bs, d, dtype_code(key_cache.dtype), 0, st[0], st[1])
+
+
+def new_fp8_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
+                 device="cuda", poison: bool = False):
+    """8-bit KV pool: codes [N, 2, H_kv, bs, D] (torch.float8_e4m3fn) and scale
+    bytes [N, 2, H_kv, bs] (uint8).  Returns (codes, key view, value view,
+    scales, key-scale view, value-scale view).  ``poison`` fills codes with
+    0x7F (NaN) and scales with 0xFF so reads of unwritten rows show."""
+    torch = _torch()
+    codes = torch.empty((num_blocks, 2, num_kv_heads, block_size, head_dim), dtype=torch.float8_e4m3fn,
+                        device=device)
+    scales = torch.empty((num_blocks, 2, num_kv_heads, block_size), dtype=torch.uint8, device=device)
+    if poison:
+        codes.view(torch.uint8).fill_(0x7F)
+        scales.fill_(0xFF)
+    return codes, codes[:, 0], codes[:, 1], scales, scales[:, 0], scales[:, 1]
+
+
+def _check_scales(key_cache, key_scales, value_scales):
+    torch = _torch()
+    n, h, bs, d = key_cache.shape
+    st = key_cache.stride()
+    for t in (key_scales, value_scales):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (n, h, bs) or \
+                tuple(t.stride()) != (st[0] // d, st[1] // d, 1):
+            raise ValueError("scales must be uint8 [N, H_kv, bs] mirroring the code layout")
+
+
+def paged_kv_write_fp8(key, value, slot_mapping, key_cache, value_cache, key_scales, value_scales,
+                       stream=None) -> None:
+    """paged_kv_write into 8-bit blocks: key/value [T, H_kv, D] (bf16, f16 or
+    f32) quantised row by row (see paged_kv_write_fp8 in pkv.h)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    T = key.shape[0]
+    if key.shape != (T, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape \
+            or value.dtype != key.dtype or not (key.is_contiguous() and value.is_contiguous()):
+        raise ValueError("key/value must be contiguous [num_tokens, H_kv, head_dim] of one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int64 [num_tokens]")
+    st = _lib_handle().paged_kv_write_fp8(key.data_ptr(), value.data_ptr(), dtype_code(key.dtype),
+                                          slot_mapping.data_ptr(), T, key_cache.data_ptr(),
+                                          value_cache.data_ptr(), key_scales.data_ptr(),
+                                          value_scales.data_ptr(), ctypes.byref(lay),
+                                          _stream_handle(stream))
+    _check(st, "paged_kv_write_fp8")
+
+
+def decode_write_fp8(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
+                     key_scales, value_scales, block_tables=None, lens_out=None, stream=None) -> None:
+    """pkv_decode_write into 8-bit blocks (host slots int64 and lens int32)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    n = key.shape[0]
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if key.shape != (n, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape \
+            or slots.shape != (n,) or lens.shape != (n,):
+        raise ValueError("key/value [n, H_kv, D] with n slots and lens")
+    tab_ptr, rows, stride = None, 0, 0
+    if block_tables is not None:
+        if block_tables.dtype != torch.int32 or block_tables.stride(1) != 1:
+            raise ValueError("block_tables must be int32 with unit column stride")
+        tab_ptr, rows, stride = block_tables.data_ptr(), block_tables.shape[0], block_tables.stride(0)
+    st = _lib_handle().pkv_decode_write_fp8(
+        key.data_ptr(), value.data_ptr(), dtype_code(key.dtype), _ptr(slots, ctypes.c_int64),
+        _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(), value_cache.data_ptr(),
+        key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay), tab_ptr, rows, stride,
+        None if lens_out is None else lens_out.data_ptr(), _stream_handle(stream))
+    _check(st, "pkv_decode_write_fp8")
+
+
+def paged_decode_attention_fp8(q, key_cache, value_cache, key_scales, value_scales, block_tables,
+                               context_lens, scale: float, out=None, out_dtype=None,
+                               max_context_len: Optional[int] = None, workspace=None, stream=None,
+                               phase: str = "both"):
+    """Decode attention over 8-bit blocks (see paged_decode_attention_fp8 in
+    pkv.h); q [B, H_q, 128] bf16 or f16."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    B, hq, d = q.shape
+    if d != lay.head_dim or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, H_q, head_dim]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != B \
+            or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [B, W] with unit column stride")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (B,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * lay.block_size
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.float32 if out_dtype is None else out_dtype,
+                          device=q.device)
+    need = workspace_size(B, hq, lay.num_kv_heads, d, max_context_len, 0)
+    if need > 0 and workspace is None:
+        if phase != "both":
+            raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    phases = {"partial": 1, "merge": 2, "both": 3}[phase]
+    st = _lib_handle().paged_decode_attention_fp8(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), key_cache.data_ptr(),
+        value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(), block_tables.data_ptr(),
+        block_tables.stride(0), context_lens.data_ptr(), B, hq, int(max_context_len), float(scale),
+        ctypes.byref(lay), phases, None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    _check(st, "paged_decode_attention_fp8")
+    return out
 
 
 def new_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype,
@@ -536,7 +655,8 @@ __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
-    "copy_blocks",
+    "copy_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
+    "paged_decode_attention_fp8", "PKV_FP8_E4M3",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

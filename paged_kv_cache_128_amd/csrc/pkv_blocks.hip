@@ -43,6 +43,7 @@ block_copy_kernel(CopyMeta meta, int32_t num_blocks, int32_t heads, int64_t bloc
 extern "C" int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
                                void* value_cache, const pkv_cache_layout* l, void* stream) {
   if (pkv::check_layout(l) != PKV_OK || n < 0) return PKV_ERR_INVALID;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // codes without their scales
   if (n == 0) return PKV_OK;
   if (!src || !dst || !key_cache || !value_cache) return PKV_ERR_INVALID;
   const int eb = pkv::elem_bytes(l->dtype);

@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <stdint.h>
 
 #include <utility>
@@ -137,11 +138,8 @@ kv_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
 // (len - 1) / bs: a block the append opened, [MiniPaged-Qwen] §9.2, or one
 // it copied on write) into the device block table, and copies the lengths
 // to `lens_out` for the attention launch that follows.
-constexpr int kStepRows = 256;
-struct StepMeta {
-  int64_t slots[kStepRows];
-  int32_t lens[kStepRows];
-};
+using pkv::kStepRows;
+using pkv::StepMeta;
 
 __global__ void __launch_bounds__(256)
 decode_write_kernel(StepMeta meta, int32_t n, int32_t row0, const uint4* __restrict__ key,
@@ -235,6 +233,7 @@ struct Frag {
 };
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ Dw<4> load_nt16(const char* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -796,6 +795,12 @@ struct StreamArgs {
   int32_t* tables_w;
   int32_t table_rows;
   int32_t* lens_out;
+  // 8-bit KV only: scale bytes of K and V rows, at ks + pb * sblock_stride
+  // + h * shead_stride + off
+  const uint8_t* ks;
+  const uint8_t* vs;
+  int64_t sblock_stride;
+  int64_t shead_stride;
 };
 
 constexpr int kStreamMaxHeads = 8;
@@ -918,6 +923,155 @@ __device__ __forceinline__ void load_v_buf(VTile<DT, 128>& t, const char* vtile,
 // flight during its compute.
 constexpr int kStreamChunk = 2;
 
+// ---- 8-bit KV blocks (PKV_FP8_E4M3): D = 128 one-byte E4M3 codes per row
+// and one E8M0 scale byte per row (value 2^(byte - 127); the encoding is in
+// pkv_fp8.hip).  A tile is 2 KiB of codes, so a chunk takes twice the tiles
+// for the same bytes in flight.  The hardware conversion reads the codes as
+// OCP E4M3; stored codes never use 0x80 or 0x7F/0xFF, so the value of every
+// code read from a written row is the same in both 8-bit E4M3 variants up
+// to the factor kFp8Decode (the OCP variant: 1).
+constexpr int kStreamChunk8 = 4;
+constexpr float kFp8Decode = 1.0f;
+
+struct VTile8 {
+  uint32_t w[4][2];   // lane (g4, c16): codes 8 c16 .. 8 c16 + 7 of rows 4 g4 + r
+  uint32_t ks;        // K scale bytes of rows 4 g4 .. 4 g4 + 3
+  uint32_t vs;        // V scale bytes of the same rows
+};
+
+// K rows (128 bytes each) into LDS: instruction rr covers rows 8 rr .. 8 rr
+// + 7; lane l fetches chunk (l % 8) ^ (row % 8) of row 8 rr + l / 8, so
+// chunk c of row r sits at slot c ^ (r % 8).  Rows past nvalid read zeros.
+__device__ __forceinline__ void issue_k_rows8(const char* ktile, uint4* sk, int nvalid, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(ktile), static_cast<short>(0), nvalid * 128, kRsrcWord3);
+  const int r8 = lane >> 3, c8 = lane & 7;
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int row = 8 * rr + r8;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(sk + rr * 64), 16,
+                                             row * 128 + ((c8 ^ (row & 7)) << 4), 0, 0, 0);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// V codes as the P.V lanes hold them, and the tile's scale bytes (the 16
+// bytes of a tile are always inside the block, written or not).
+__device__ __forceinline__ void load_v_buf8(VTile8& t, const char* vtile, const uint8_t* ksc,
+                                            const uint8_t* vsc, int nvalid, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(vtile), static_cast<short>(0), nvalid * 128, kRsrcWord3);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (4 * g4 + r) * 128 + (c16 << 3), 0, kCacheNT);
+    t.w[r][0] = v.x;
+    t.w[r][1] = v.y;
+  }
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(ksc), static_cast<short>(0), 16, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(vsc), static_cast<short>(0), 16, kRsrcWord3);
+  t.ks = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * g4, 0, 0);
+  t.vs = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * g4, 0, 0);
+}
+
+// Four codes of a dword as float32 (hardware E4M3 conversion).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+  f[0] = lo.x * kFp8Decode; f[1] = lo.y * kFp8Decode;
+  f[2] = hi.x * kFp8Decode; f[3] = hi.y * kFp8Decode;
+}
+
+// Two float32 of code values (exact in 16 bits) packed as the MFMA's 16-bit type.
+template <int DT>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (DT == PKV_BF16)
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+// The staged K codes of row c16 as the MFMA operand: lane (g4, c16) takes
+// bytes 32 g4 .. 32 g4 + 31 of its row; step kk uses bytes 32 g4 + 8 kk ..
+// + 7 (the query operand is staged with the same head-dim map).
+template <int DT>
+__device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const uint4 A = sk[c16 * 8 + ((2 * g4) ^ (c16 & 7))];
+  const uint4 Bv = sk[c16 * 8 + ((2 * g4 + 1) ^ (c16 & 7))];
+  const uint32_t w[8] = {A.x, A.y, A.z, A.w, Bv.x, Bv.y, Bv.z, Bv.w};
+  Dw<16> r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float f[4];
+    fp8x4_to_f32(w[i], f);
+    r.w[2 * i] = pack16<DT>(f[0], f[1]);
+    r.w[2 * i + 1] = pack16<DT>(f[2], f[3]);
+  }
+  return r;
+}
+
+// softmax_pv for 8-bit tiles: the score of token t is the code dot product
+// times 2^ek(t), the V row of t is its codes times 2^ev(t).  The K scale
+// goes into the exp2 argument's factor, the V scale into the probability
+// the P.V lanes receive (the sum l keeps the unscaled probability).
+template <int GP>
+__device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int nvalid,
+                                            float scale_log2, float& m, float& l,
+                                            float (&acc)[GP][8], int lane) {
+  const int g4 = lane >> 4;
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ek = static_cast<int>((t.ks >> (8 * r)) & 0xffu) - 127;
+    x[r] = (4 * g4 + r < nvalid) ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
+  }
+  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const bool grow = bm > m + kSlack;
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    const float m_new = fmaxf(m, bm);
+    const float a = __builtin_amdgcn_exp2f(m - m_new);
+    l *= a;
+    m = m_new;
+    for_each_head<GP>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ah = row_bcast<h>(a);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
+    });
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);
+  l += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ev = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
+    const float pr = __builtin_amdgcn_ldexpf(p[r], ev);
+    float vf[8];
+    float f0[4], f1[4];
+    fp8x4_to_f32(t.w[r][0], f0);
+    fp8x4_to_f32(t.w[r][1], f1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vf[e] = f0[e];
+      vf[4 + e] = f1[e];
+    }
+    for_each_head<GP>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ph = row_bcast<h>(pr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+    });
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding): wait for every vector memory
 // operation, or for every LDS operation, the other counters left alone.
 constexpr int kWaitVm0 = 0x0f70;
@@ -929,13 +1083,18 @@ constexpr int kWaitLgkm0 = 0xc07f;
 // entry of each new token's block; the tile holding a sequence's new token takes its block
 // from the slot, and the one wave per KV head that reads that tile
 // replaces the token's row (stale in the pool until then) with the new K/V
-// row and stores that row into the pool.
-template <int DT, int GP, bool PAIRED, bool FUSED>
+// row and stores that row into the pool.  KV8: the cache holds 8-bit rows
+// (DT is then the query's type, which the K codes are converted to).
+template <int DT, int GP, bool PAIRED, bool FUSED, bool KV8>
 __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta* meta) {
   constexpr int D = 128;
-  constexpr int CH = kStreamChunk;
+  constexpr int CH = KV8 ? kStreamChunk8 : kStreamChunk;
+  constexpr int KT = KV8 ? 128 : 256;     // LDS uint4 slots of one staged K tile
+  constexpr int EB = KV8 ? 1 : 2;         // bytes per cached element
   using F = Frag<DT, D>;
-  static_assert(F::kRowK, "stream kernel is for 16-bit KV with D = 128");
+  using VT = std::conditional_t<KV8, VTile8, VTile<DT, D>>;
+  static_assert(F::kRowK, "stream kernel is for 16-bit queries with D = 128");
+  static_assert(!(FUSED && KV8), "the decode-step form writes 16-bit rows");
   // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
   //              [tbl: cap]
   extern __shared__ uint4 sh_stream[];
@@ -947,9 +1106,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   const int R = a.ranges_per_wg;
   const int H = a.hkv;
   const int J = R * H;
-  uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * 256;
-  uint4* sq = sh_stream + static_cast<int64_t>(nwaves) * CH * 256 + static_cast<int64_t>(wave) * 256;
-  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(nwaves) * (CH + 1) * 256);
+  uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * KT;
+  uint4* sq = sh_stream + static_cast<int64_t>(nwaves) * CH * KT + static_cast<int64_t>(wave) * 256;
+  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(nwaves) * (CH * KT + 256));
   int32_t* Ls = S + B + 1;
   int32_t* tbl = Ls + B;
   if (wave == 0) {
@@ -1014,7 +1173,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       const int ti = g - uni(S[b_of_g]);
       const int off = (ti * kTile) % bs;
       return (static_cast<int64_t>(uni(tbl[g - w0])) * a.block_stride + head_off +
-              static_cast<int64_t>(off) * D) * 2;
+              static_cast<int64_t>(off) * D) * EB;
+    };
+    // 8-bit KV: byte offset of the tile's first scale byte
+    auto tile_scale = [&](int g, int b_of_g) -> int64_t {
+      const int ti = g - uni(S[b_of_g]);
+      return static_cast<int64_t>(uni(tbl[g - w0])) * a.sblock_stride +
+             static_cast<int64_t>(kvh) * a.shead_stride + (ti * kTile) % bs;
     };
     // The query group of sequence b, as the MFMA B operand, into the wave's
     // LDS slot by DMA: instruction kk gives lane (g4, c16) head-dims
@@ -1029,9 +1194,11 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
                          (static_cast<int64_t>(b) * a.hq + static_cast<int64_t>(kvh) * G) * D * 2;
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        __builtin_amdgcn_global_load_lds((global_void*)(qgrp + (head * D + 32 * kk + 8 * g4) * 2),
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int d0 = KV8 ? 32 * g4 + 8 * kk : 32 * kk + 8 * g4;   // the K operand's head-dim map
+        __builtin_amdgcn_global_load_lds((global_void*)(qgrp + (head * D + d0) * 2),
                                          (lds_void*)(sq + kk * 64), 16, 0, 0);
+      }
       asm volatile("" ::: "memory");
     };
     auto read_q = [&]() {
@@ -1070,7 +1237,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     };
     // At the head of the chunk holding a new token: its K row into the
     // staged tile, its V row into the P.V registers, both rows into the pool.
-    auto place_new = [&](VTile<DT, D> (&v)[CH], int b) {
+    auto place_new = [&](VT (&v)[CH], int b) {
       if constexpr (FUSED) {
         if (g4 == 0) sk[jn * 256 + rn * 16 + (c16 ^ rn)] = make_uint4(nk.x, nk.y, nk.z, nk.w);
 #pragma unroll
@@ -1090,19 +1257,25 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
         }
       }
     };
-    auto issue_chunk = [&](VTile<DT, D> (&v)[CH], int g, int n, int b) {
-      int64_t e[CH];
+    auto issue_chunk = [&](VT (&v)[CH], int g, int n, int b) {
+      int64_t e[CH], so[CH];
       int nv[CH];
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         e[j] = j < n ? tile_bytes(g + j, b) : 0;
+        so[j] = (KV8 && j < n) ? tile_scale(g + j, b) : 0;
         nv[j] = nvalid_at(g + j, b);
       }
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
         if (j < n) {
-          issue_k_rows_buf(kc + e[j], sk + j * 256, nv[j], lane);
-          load_v_buf<DT>(v[j], vc + e[j], nv[j], lane);
+          if constexpr (KV8) {
+            issue_k_rows8(kc + e[j], sk + j * KT, nv[j], lane);
+            load_v_buf8(v[j], vc + e[j], a.ks + so[j], a.vs + so[j], nv[j], lane);
+          } else {
+            issue_k_rows_buf(kc + e[j], sk + j * KT, nv[j], lane);
+            load_v_buf<DT>(v[j], vc + e[j], nv[j], lane);
+          }
         }
       }
     };
@@ -1113,7 +1286,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       int bc = uni(seq_of_tile(S, B, cs));
       int cn = chunk_len(cs, bc);
       load_q(bc);
-      VTile<DT, D> vcur[CH], vnext[CH];
+      VT vcur[CH], vnext[CH];
       issue_chunk(vcur, cs, cn, bc);
       fetch_new(cs, cn, bc);
       int seg_lo = cs, seg_hi = cs + cn;    // tiles of the current segment
@@ -1135,8 +1308,12 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
         {
           const Dw<F::kDwK> qf = read_q();
 #pragma unroll
-          for (int j = 0; j < CH; ++j)
-            if (j < cn) scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * 256, lane), qf);
+          for (int j = 0; j < CH; ++j) {
+            if (j < cn) {
+              if constexpr (KV8) scr[j] = qk_mfma<DT, D>(read_k_rows8<DT>(sk + j * KT, lane), qf);
+              else scr[j] = qk_mfma<DT, D>(read_k_rows<DT, D>(sk + j * KT, lane), qf);
+            }
+          }
         }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // LDS reads done before the buffer is refilled
         const bool more = cs + cn < p1;
@@ -1151,9 +1328,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
           if (bn != bc) load_q(bn);
         }
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
-          if (j < cn)
-            softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+        for (int j = 0; j < CH; ++j) {
+          if (j < cn) {
+            if constexpr (KV8)
+              softmax_pv8<GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+            else
+              softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+          }
+        }
         if (bn != bc) {
           const bool complete = seg_lo == uni(S[bc]) && seg_hi == uni(S[bc + 1]);
           const int slot = back ? (seg_hi == g1 ? 2 : 3) : (seg_lo == g0 ? 0 : 1);
@@ -1186,7 +1368,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
 template <int DT, int GP, bool PAIRED>
 __global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
 attn_stream_kernel(StreamArgs a) {
-  stream_body<DT, GP, PAIRED, false>(a, nullptr);
+  stream_body<DT, GP, PAIRED, false, false>(a, nullptr);
+}
+
+// Attention over 8-bit KV blocks (DT: the query's type).
+template <int DT, int GP, bool PAIRED>
+__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
+attn_stream8_kernel(StreamArgs a) {
+  stream_body<DT, GP, PAIRED, false, true>(a, nullptr);
 }
 
 // The decode step in one launch: the write of the step's new rows (taken
@@ -1194,7 +1383,7 @@ attn_stream_kernel(StreamArgs a) {
 template <int DT, int GP, bool PAIRED>
 __global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
 attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
-  stream_body<DT, GP, PAIRED, true>(a, &meta);
+  stream_body<DT, GP, PAIRED, true, false>(a, &meta);
 }
 
 // Lengths of at most kStepRows sequences carried in the kernel arguments.
@@ -1459,10 +1648,16 @@ hipError_t raise_lds(K kernel, size_t bytes) {
   return hipSuccess;
 }
 
-template <int DT, int GP, bool PAIRED>
+template <int DT, int GP, bool PAIRED, bool KV8>
 hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, const StepMeta* meta,
                            hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(pl.wgs)), block(kWave * pl.waves);
+  if constexpr (KV8) {
+    const hipError_t e = raise_lds(&attn_stream8_kernel<DT, GP, PAIRED>, pl.dyn_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_stream8_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a);
+    return hipGetLastError();
+  }
   if (meta) {
     const hipError_t e = raise_lds(&attn_stream_step_kernel<DT, GP, PAIRED>, pl.dyn_lds);
     if (e != hipSuccess) return e;
@@ -1475,23 +1670,23 @@ hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, const Step
   return hipGetLastError();
 }
 
-template <int DT, int GP>
+template <int DT, int GP, bool KV8>
 hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, const StepMeta* meta,
                            hipStream_t s) {
-  return pl.waves == 2 * pl.ranges_per_wg * a.hkv ? launch_stream_p<DT, GP, true>(a, pl, meta, s)
-                                                  : launch_stream_p<DT, GP, false>(a, pl, meta, s);
+  return pl.waves == 2 * pl.ranges_per_wg * a.hkv ? launch_stream_p<DT, GP, true, KV8>(a, pl, meta, s)
+                                                  : launch_stream_p<DT, GP, false, KV8>(a, pl, meta, s);
 }
 
-template <int DT>
+template <int DT, bool KV8 = false>
 hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, const StepMeta* meta,
                             hipStream_t s) {
   switch (gp) {
-    case 1: return launch_stream_t<DT, 1>(a, pl, meta, s);
-    case 2: return launch_stream_t<DT, 2>(a, pl, meta, s);
-    case 4: return launch_stream_t<DT, 4>(a, pl, meta, s);
-    case 6: return launch_stream_t<DT, 6>(a, pl, meta, s);
-    case 7: return launch_stream_t<DT, 7>(a, pl, meta, s);
-    default: return launch_stream_t<DT, 8>(a, pl, meta, s);
+    case 1: return launch_stream_t<DT, 1, KV8>(a, pl, meta, s);
+    case 2: return launch_stream_t<DT, 2, KV8>(a, pl, meta, s);
+    case 4: return launch_stream_t<DT, 4, KV8>(a, pl, meta, s);
+    case 6: return launch_stream_t<DT, 6, KV8>(a, pl, meta, s);
+    case 7: return launch_stream_t<DT, 7, KV8>(a, pl, meta, s);
+    default: return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
   }
 }
 
@@ -1549,6 +1744,7 @@ int paged_kv_write(const void* key, const void* value, const int64_t* slot_mappi
                    int32_t num_tokens, void* key_cache, void* value_cache,
                    const pkv_cache_layout* l, void* stream) {
   if (pkv::check_layout(l) != PKV_OK || num_tokens < 0) return PKV_ERR_INVALID;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // paged_kv_write_fp8
   if (num_tokens == 0) return PKV_OK;
   if (!key || !value || !slot_mapping || !key_cache || !value_cache) return PKV_ERR_INVALID;
   const int eb = pkv::elem_bytes(l->dtype);
@@ -1581,6 +1777,7 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots, c
                      int32_t block_table_stride, int32_t* lens_out, void* stream) {
   if (pkv::check_layout(l) != PKV_OK || num_rows < 0 || table_rows < 0 || block_table_stride < 0)
     return PKV_ERR_INVALID;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // pkv_decode_write_fp8
   if (num_rows == 0) return PKV_OK;
   if (!key || !value || !slots || !lens || !key_cache || !value_cache) return PKV_ERR_INVALID;
   if (block_tables && block_table_stride <= 0) return PKV_ERR_INVALID;
@@ -1639,6 +1836,13 @@ namespace {
 constexpr int kPhasePartial = 1;
 constexpr int kPhaseMerge = 2;
 
+// 8-bit KV attention: the rows' scale bytes and the query's type.
+struct Fp8Args {
+  const uint8_t* key_scales;
+  const uint8_t* value_scales;
+  int32_t q_dtype;
+};
+
 // The decode-step form of the stream launch: the step's new rows, its
 // metadata, and where its write goes.
 struct StepArgs {
@@ -1660,13 +1864,20 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
                    int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
                    int32_t num_q_heads, int32_t max_context_len, float scale,
                    const pkv_cache_layout* l, int32_t partition_tokens, void* workspace,
-                   size_t workspace_bytes, void* stream, const StepArgs* step = nullptr) {
+                   size_t workspace_bytes, void* stream, const StepArgs* step = nullptr,
+                   const Fp8Args* f8 = nullptr) {
   if (pkv::check_layout(l) != PKV_OK) return PKV_ERR_INVALID;
   if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || block_table_stride < 0 ||
       partition_tokens < 0)
     return PKV_ERR_INVALID;
+  if ((l->dtype == PKV_FP8_E4M3) != (f8 != nullptr)) return PKV_ERR_UNSUPPORTED;
+  // the type of q (and of a non-fp32 output): the cache's, or for 8-bit KV the given one
+  const int qt = f8 ? f8->q_dtype : l->dtype;
+  if (f8 && ((qt != PKV_BF16 && qt != PKV_F16) || !f8->key_scales || !f8->value_scales))
+    return PKV_ERR_INVALID;
+  if (f8 && (partition_tokens != 0 || step)) return PKV_ERR_UNSUPPORTED;
   if (num_q_heads % l->num_kv_heads != 0) return PKV_ERR_INVALID;
-  if (out_dtype != PKV_F32 && out_dtype != l->dtype) return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != qt) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
     return PKV_ERR_INVALID;
   if (!(scale == scale)) return PKV_ERR_INVALID;
@@ -1686,6 +1897,14 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
                           reinterpret_cast<uintptr_t>(value_cache);
   if (align % 16 != 0 || (l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0)
     return PKV_ERR_UNSUPPORTED;
+  if (f8) {
+    // scale bytes mirror the code layout with one byte per row; a tile's 16
+    // scale bytes are read as dwords
+    if (l->head_stride % l->head_dim != 0 || l->block_stride % l->head_dim != 0 ||
+        (l->head_stride / l->head_dim) % 4 != 0 || (l->block_stride / l->head_dim) % 4 != 0 ||
+        ((reinterpret_cast<uintptr_t>(f8->key_scales) | reinterpret_cast<uintptr_t>(f8->value_scales)) % 4) != 0)
+      return PKV_ERR_UNSUPPORTED;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (partition_tokens == 0) {
     const StreamPlan pl = plan_stream(num_seqs, num_q_heads, l->num_kv_heads, l->head_dim,
@@ -1723,11 +1942,18 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.tables_w = step ? step->block_tables : nullptr;
       sa.table_rows = step ? step->table_rows : 0;
       sa.lens_out = step ? step->lens_out : nullptr;
+      sa.ks = f8 ? f8->key_scales : nullptr;
+      sa.vs = f8 ? f8->value_scales : nullptr;
+      sa.sblock_stride = l->block_stride / l->head_dim;
+      sa.shead_stride = l->head_stride / l->head_dim;
       if (phases & kPhasePartial) {
         const int gp = padded_group(group);
         const StepMeta* meta = step ? step->meta : nullptr;
-        hipError_t e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, meta, s)
-                                              : launch_stream_dt<PKV_F16>(sa, gp, pl, meta, s);
+        hipError_t e;
+        if (f8) e = (qt == PKV_BF16) ? launch_stream_dt<PKV_BF16, true>(sa, gp, pl, nullptr, s)
+                                     : launch_stream_dt<PKV_F16, true>(sa, gp, pl, nullptr, s);
+        else e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, meta, s)
+                                        : launch_stream_dt<PKV_F16>(sa, gp, pl, meta, s);
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
@@ -1744,6 +1970,7 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       return PKV_OK;
     }
   }
+  if (f8) return PKV_ERR_UNSUPPORTED;     // 8-bit KV: stream path shapes only
   const int64_t P = max_context_len > 0 ? (static_cast<int64_t>(max_context_len) + part - 1) / part : 1;
   const size_t need = paged_decode_attention_workspace_size(num_seqs, num_q_heads, l->num_kv_heads,
                                                             l->head_dim, max_context_len, part);
@@ -1808,6 +2035,7 @@ int paged_decode_attention_path(int32_t num_seqs, int32_t num_q_heads, int32_t m
   if (partition_tokens == 0 &&
       plan_stream(num_seqs, num_q_heads, l->num_kv_heads, l->head_dim, max_context_len, l->dtype).ok)
     return PKV_PATH_STREAM;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // 8-bit KV: stream path only
   return PKV_PATH_PARTITION;
 }
 
@@ -1862,6 +2090,7 @@ int decode_step_impl(int phases, void* out, int32_t out_dtype, const void* q, co
   if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
       block_table_stride <= 0)
     return PKV_ERR_INVALID;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PKV_OK;
   if (!key || !value || !slots || !lens || !lens_out || !block_tables) return PKV_ERR_INVALID;
   const int64_t capacity = static_cast<int64_t>(l->num_blocks) * l->block_size;
@@ -1930,6 +2159,21 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
                           key_cache, value_cache, layout, block_tables, block_table_stride,
                           lens_out, num_q_heads, max_context_len, scale, workspace,
                           workspace_bytes, stream);
+}
+
+int paged_decode_attention_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                               const void* key_cache, const void* value_cache,
+                               const uint8_t* key_scales, const uint8_t* value_scales,
+                               const int32_t* block_tables, int32_t block_table_stride,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t max_context_len, float scale, const pkv_cache_layout* layout,
+                               int32_t phases, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (phases < 1 || phases > 3) return PKV_ERR_INVALID;
+  const Fp8Args f8{key_scales, value_scales, q_dtype};
+  return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
+                        block_table_stride, context_lens, num_seqs, num_q_heads, max_context_len,
+                        scale, layout, 0, workspace, workspace_bytes, stream, nullptr, &f8);
 }
 
 int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,

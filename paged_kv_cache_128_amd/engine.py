@@ -17,7 +17,10 @@ A decode step is the hot path of [MiniPaged-Qwen] §10 and §13 in order:
 
 With the stream attention path (partition_tokens 0), steps 2 and 3 are one
 launch (pkv_decode_step) plus the merge; otherwise they are a write launch
-and the attention.
+and the attention.  With dtype torch.float8_e4m3fn the pool holds 8-bit
+rows with one scale byte each ([impl-detail] "实践建议"): writes quantise
+(paged_kv_write_fp8 / pkv_decode_write_fp8) and attention reads them back
+(paged_decode_attention_fp8); the query keeps its 16-bit type.
 
 Rows are batch positions; each live sequence occupies one row.  All device
 memory comes from torch; all work runs in libpkv on torch's current stream.
@@ -29,8 +32,9 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, copy_blocks, decode_step, decode_write, new_pool,
-               paged_decode_attention, paged_kv_write, workspace_size)
+from . import (KVBlockManager, copy_blocks, decode_step, decode_write, decode_write_fp8, new_fp8_pool,
+               new_pool, paged_decode_attention, paged_decode_attention_fp8, paged_kv_write,
+               paged_kv_write_fp8, workspace_size)
 
 
 class PagedKVEngine:
@@ -49,8 +53,14 @@ class PagedKVEngine:
         self.width = max_blocks_per_seq
         self.partition_tokens = partition_tokens
         self.manager = KVBlockManager(num_blocks, block_size, initial_free_order)
-        self.pool, self.key_cache, self.value_cache = new_pool(
-            num_blocks, num_kv_heads, block_size, head_dim, dtype, self.device, fill_bits)
+        self.fp8 = dtype == torch.float8_e4m3fn
+        if self.fp8:
+            (self.pool, self.key_cache, self.value_cache, self.scales, self.key_scales,
+             self.value_scales) = new_fp8_pool(num_blocks, num_kv_heads, block_size, head_dim,
+                                               self.device, poison=fill_bits is not None)
+        else:
+            self.pool, self.key_cache, self.value_cache = new_pool(
+                num_blocks, num_kv_heads, block_size, head_dim, dtype, self.device, fill_bits)
         self.tables = torch.full((max_rows, self.width), -1, dtype=torch.int32, device=self.device)
         self.row_seq: Dict[int, int] = {}
         self.d_lens = torch.zeros(max_rows, dtype=torch.int32, device=self.device)
@@ -70,9 +80,16 @@ class PagedKVEngine:
         slots = self.manager.allocate_for_prefill(seq_id, n)
         if n > 0:
             d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
-            paged_kv_write(key, value, d_slots, self.key_cache, self.value_cache)
+            self._write(key, value, d_slots)
         self._publish_row(seq_id, row)
         return slots
+
+    def _write(self, key, value, d_slots):
+        if self.fp8:
+            paged_kv_write_fp8(key, value, d_slots, self.key_cache, self.value_cache,
+                               self.key_scales, self.value_scales)
+        else:
+            paged_kv_write(key, value, d_slots, self.key_cache, self.value_cache)
 
     def prefill_many(self, seq_ids: Sequence[int], rows: Sequence[int], lengths: Sequence[int],
                      key: torch.Tensor, value: torch.Tensor) -> np.ndarray:
@@ -84,7 +101,7 @@ class PagedKVEngine:
         slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
             d_slots = torch.from_numpy(slots).to(self.device)
-            paged_kv_write(key, value, d_slots, self.key_cache, self.value_cache)
+            self._write(key, value, d_slots)
         for sid, row in zip(seq_ids, rows):
             self._publish_row(int(sid), int(row))
         return slots
@@ -93,6 +110,8 @@ class PagedKVEngine:
         """Admit ``seq_id`` into ``row`` holding the first ``num_tokens`` tokens
         of live ``donor_id`` on the donor's blocks, no copy
         ([impl-detail] "前缀共享"); its appends copy a shared block first."""
+        if self.fp8:
+            raise NotImplementedError("copy-on-write of 8-bit blocks (codes and scales) is not built")
         self.manager.share_prefix(donor_id, seq_id, num_tokens)
         self._sharing = True
         self._publish_row(seq_id, row)
@@ -137,6 +156,11 @@ class PagedKVEngine:
                 copy_blocks(src, dst, self.key_cache, self.value_cache)
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
+        if self.fp8:
+            decode_write_fp8(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache,
+                             self.value_cache, self.key_scales, self.value_scales,
+                             block_tables=self.tables, lens_out=self.d_lens)
+            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
         if not (fused and self.partition_tokens == 0 and n > 0):
             decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                          block_tables=self.tables, lens_out=self.d_lens)
@@ -160,10 +184,22 @@ class PagedKVEngine:
         """Attention of rows 0..B-1 over the current cache (no append/write)."""
         n = q.shape[0]
         ws = self.workspace(n, q.shape[1], max_context_len)
-        kw = dict(partition_tokens=self.partition_tokens, max_context_len=max_context_len,
-                  workspace=ws)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        if self.fp8:
+            args = (q, self.key_cache, self.value_cache, self.key_scales, self.value_scales,
+                    self.tables[:n], lens, scale)
+            kw8 = dict(out=out, max_context_len=max_context_len, workspace=ws)
+            if events is None:
+                return paged_decode_attention_fp8(*args, **kw8)
+            events[0].record()
+            paged_decode_attention_fp8(*args, phase="partial", **kw8)
+            events[1].record()
+            paged_decode_attention_fp8(*args, phase="merge", **kw8)
+            events[2].record()
+            return out
+        kw = dict(partition_tokens=self.partition_tokens, max_context_len=max_context_len,
+                  workspace=ws)
         if events is None:
             return paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n],
                                           lens, scale, out=out, **kw)

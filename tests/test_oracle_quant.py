@@ -84,6 +84,13 @@ def test_quantisation_error_within_half_ulp():
         ulp = np.where(y >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(y, 1e-300))) - 3), 2.0 ** -9)
         assert np.all(np.abs(back - row) <= 0.5 * ulp * 2.0 ** e + 0.0)
         assert np.abs(row).max() / 2.0 ** e > 224.0      # the top code range is used
+        assert not np.any(codes == 0x80)
+
+
+def test_negative_zero_codes_are_stored_as_zero():
+    row = np.array([-0.0, -1e-9, 3.0, -5.0], dtype=np.float32)
+    codes, sb = quant.quantize_row(row)
+    assert codes[0] == 0x00 and codes[1] == 0x00 and sb == 127 - 6
 
 
 def test_fp8_attention_matches_online_oracle_on_read_back_values():
@@ -110,3 +117,19 @@ def test_fp8_attention_matches_online_oracle_on_read_back_values():
     used = {pb for b in range(3) for pb in m.block_table(b)}
     for pb in set(range(N)) - used:
         assert np.all(kc[pb] == 0x7F) and np.all(ks[pb] == 0xFF)
+
+
+def test_array_quantiser_equals_the_scalar_definition():
+    rng = np.random.default_rng(8)
+    rows = [(rng.standard_normal(64) * 10.0 ** rng.uniform(-8, 8)).astype(np.float32) for _ in range(60)]
+    rows.append(np.zeros(64, np.float32))
+    rows.append(np.array([-0.0] * 32 + [1.0] * 32, np.float32))
+    ties = np.array([(quant.e4m3_decode(c) + quant.e4m3_decode(c + 1)) / 2 for c in range(0x70, 0x7D)],
+                    np.float32)
+    rows.append(np.concatenate([ties, -ties, np.full(64 - 2 * len(ties), 448.0, np.float32)]))
+    rows.append(np.array([2.0 ** -140, -(2.0 ** -135)] + [0.0] * 62, np.float32))   # float32 subnormals
+    arr = np.stack(rows)
+    codes, sbytes = quant.quantize_rows(arr)
+    for i, r in enumerate(rows):
+        c, sb = quant.quantize_row(r)
+        assert np.array_equal(codes[i], c) and sbytes[i] == sb, i
