@@ -162,6 +162,81 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
             "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
+    """The same workload with an 8-bit KV pool (E4M3 codes + one scale byte
+    per row; the history quantised by the prefill write): decode steps of
+    append, quantising step write and 8-bit attention + merge.  Reported
+    beside the 16-bit headline: KV bytes actually read (codes and scale
+    bytes) per second, decode tokens/s, and the 8-bit attention kernel's
+    roofline from HIP events on every --event-every-th step."""
+    import torch
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    B = len(wl.context_lens)
+    eng = PagedKVEngine(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim,
+                        torch.float8_e4m3fn, B, width, wl.initial_free_order, partition_tokens=0,
+                        num_q_heads=cfg.num_q_heads)
+    for ev in wl.churn:
+        if ev[0] == "prefill":
+            eng.manager.allocate_for_prefill(ev[1], ev[2], want_slots=False)
+        elif ev[0] == "grow":
+            for _ in range(ev[2]):
+                eng.manager.append_slots_for_decode(list(ev[1]))
+        else:
+            eng.manager.free_sequence(ev[1])
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    hk, hv = dev(np.concatenate(wl.hist_k)), dev(np.concatenate(wl.hist_v))
+    eng.prefill_many(list(range(B)), list(range(B)), [int(L) - 1 for L in wl.context_lens], hk, hv)
+    del hk, hv
+    ids = np.arange(B, dtype=np.int64)
+    out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
+    row_bytes = cfg.num_kv_heads * 2 * (cfg.head_dim + 1)       # K and V codes + scale bytes per token
+
+    def kv8(step):
+        return int((base + step).sum()) * row_bytes
+
+    for s_ in range(args.warmup):
+        k, v, q = ring[s_ % len(ring)]
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out)
+    timed = [i for i in range(args.steps) if i % max(1, args.event_every) == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        k, v, q = ring[(args.warmup + i) % len(ring)]
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
+    merge_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in timed])
+    step_bytes = np.array([kv8(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
+    alg = float(step_bytes[timed].mean())
+    achieved = alg / (float(kern_ms.mean()) / 1e3) / 1e9
+    tps = B * args.steps / wall
+    log(f"fp8 KV: {wall * 1e6 / args.steps:.1f} us/step, attention kernel {kern_ms.mean() * 1e3:.1f} us, "
+        f"merge {merge_ms.mean() * 1e3:.1f} us, KV {step_bytes.mean() / 1e6:.1f} MB/step")
+    return {
+        "kv_dtype": "fp8_e4m3 codes + e8m0 row scales",
+        "value": round(float(step_bytes.sum()) / wall / 1e9, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "kv_bytes_per_step": round(float(step_bytes.mean())),
+        "decode_tokens_per_s": round(tps, 1),
+        "tokens_per_s_vs_16bit": round(tps / tokens_per_s_16, 3),
+        "roofline": {
+            "kernel": f"attn_stream8_kernel<{cfg.dtype} q, D={cfg.head_dim}, "
+                      f"G={cfg.num_q_heads // cfg.num_kv_heads}>",
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "mean_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
+            "algorithmic_bytes_per_launch": round(alg),
+        },
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -178,6 +253,7 @@ def main():
                     help="record the kernel-timing events on every n-th timed step")
     ap.add_argument("--separate-write", action="store_true",
                     help="run the step's write as its own launch instead of inside the attention")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -294,6 +370,9 @@ def main():
     cold = np.array(cold)
     del flush
     block_copy = measure_block_copy(eng)
+    fp8 = None
+    if not args.no_fp8 and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
+        fp8 = measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s)
 
     import paged_kv_cache_128_amd as pkv
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
@@ -352,6 +431,7 @@ def main():
         },
         "kernel_source_sha256_16": kernel_source_sha(),
         "copy_on_write": block_copy,
+        "fp8_kv": fp8,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)

@@ -926,12 +926,9 @@ constexpr int kStreamChunk = 2;
 // ---- 8-bit KV blocks (PKV_FP8_E4M3): D = 128 one-byte E4M3 codes per row
 // and one E8M0 scale byte per row (value 2^(byte - 127); the encoding is in
 // pkv_fp8.hip).  A tile is 2 KiB of codes, so a chunk takes twice the tiles
-// for the same bytes in flight.  The hardware conversion reads the codes as
-// OCP E4M3; stored codes never use 0x80 or 0x7F/0xFF, so the value of every
-// code read from a written row is the same in both 8-bit E4M3 variants up
-// to the factor kFp8Decode (the OCP variant: 1).
+// for the same bytes in flight.  The hardware conversion on gfx950 reads the
+// codes as OCP E4M3 (checked code by code against the definition).
 constexpr int kStreamChunk8 = 4;
-constexpr float kFp8Decode = 1.0f;
 
 struct VTile8 {
   uint32_t w[4][2];   // lane (g4, c16): codes 8 c16 .. 8 c16 + 7 of rows 4 g4 + r
@@ -969,12 +966,8 @@ __device__ __forceinline__ void load_v_buf8(VTile8& t, const char* vtile, const 
     t.w[r][0] = v.x;
     t.w[r][1] = v.y;
   }
-  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(ksc), static_cast<short>(0), 16, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(vsc), static_cast<short>(0), 16, kRsrcWord3);
-  t.ks = __builtin_amdgcn_raw_buffer_load_b32(rk, 4 * g4, 0, 0);
-  t.vs = __builtin_amdgcn_raw_buffer_load_b32(rv, 4 * g4, 0, 0);
+  t.ks = *reinterpret_cast<const uint32_t*>(ksc + 4 * g4);
+  t.vs = *reinterpret_cast<const uint32_t*>(vsc + 4 * g4);
 }
 
 // Four codes of a dword as float32 (hardware E4M3 conversion).
@@ -982,8 +975,8 @@ __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
   const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-  f[0] = lo.x * kFp8Decode; f[1] = lo.y * kFp8Decode;
-  f[2] = hi.x * kFp8Decode; f[3] = hi.y * kFp8Decode;
+  f[0] = lo.x; f[1] = lo.y;
+  f[2] = hi.x; f[3] = hi.y;
 }
 
 // Two float32 of code values (exact in 16 bits) packed as the MFMA's 16-bit type.
@@ -1015,60 +1008,168 @@ __device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
   return r;
 }
 
-// softmax_pv for 8-bit tiles: the score of token t is the code dot product
-// times 2^ek(t), the V row of t is its codes times 2^ev(t).  The K scale
-// goes into the exp2 argument's factor, the V scale into the probability
-// the P.V lanes receive (the sum l keeps the unscaled probability).
+// P.V accumulator of the 8-bit path, computed on the matrix cores:
+// O^T[d][h] += sum_t V^T[d][t] P^T[t][h], one 16x16x16 f16 MFMA per eighth
+// of the head dims.  MFMA j maps its row index c to head-dim 8 c + j, so its
+// A operand (lane (g4, c16): rows 4 g4 .. 4 g4 + 3 at head-dim 8 c16 + j) is
+// byte j of the lane's V codes, and its B operand (lane (g4, c16): head c16,
+// tokens 4 g4 ..) is the score layout as it comes out of the Q.K MFMA.
+// Lane (g4, c16) ends up with head c16's head-dims 32 g4 .. 32 g4 + 31:
+// c[j][i] is head-dim 32 g4 + 8 i + j.  The V codes enter the MFMA as exact
+// f16 values and P as f16 (round to nearest) scaled by 2^(ev(t) - eref),
+// where eref, the largest V scale exponent seen in the segment, keeps the
+// products in f16 range; c holds the accumulator times 2^-eref.
+struct Acc8 {
+  f32x4 c[8];
+  int eref;
+};
+constexpr int kNoRef = -100000;
+
 template <int GP>
+struct AccV {
+  float a[GP][8];
+};
+
+template <int GP>
+__device__ __forceinline__ void acc_zero(AccV<GP>& x) {
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x.a[h][e] = 0.f;
+}
+__device__ __forceinline__ void acc_zero(Acc8& x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x.c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  x.eref = kNoRef;
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Online softmax + P.V for one 8-bit tile: the score of token t is the code
+// dot product times 2^ek(t) (into the exp2 argument's factor), the V row of
+// t its codes times 2^ev(t) (into the probability the MFMA takes; the sum l
+// keeps the unscaled probability).
 __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int nvalid,
-                                            float scale_log2, float& m, float& l,
-                                            float (&acc)[GP][8], int lane) {
+                                            float scale_log2, float& m, float& l, Acc8& acc,
+                                            int lane) {
   const int g4 = lane >> 4;
   float x[4];
+  int ev[4];
+  int evm = kNoRef;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
+    const bool valid = 4 * g4 + r < nvalid;
     const int ek = static_cast<int>((t.ks >> (8 * r)) & 0xffu) - 127;
-    x[r] = (4 * g4 + r < nvalid) ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
+    ev[r] = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
+    x[r] = valid ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
+    if (valid) evm = max(evm, ev[r]);
   }
   float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
   bm = fmaxf(bm, __shfl_xor(bm, 16));
   bm = fmaxf(bm, __shfl_xor(bm, 32));
+  evm = max(evm, __shfl_xor(evm, 16));
+  evm = max(evm, __shfl_xor(evm, 32));
+  evm = uni(evm);                                  // the same in every lane
   const bool grow = bm > m + kSlack;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float m_new = fmaxf(m, bm);
-    const float a = __builtin_amdgcn_exp2f(m - m_new);
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head
     l *= a;
     m = m_new;
-    for_each_head<GP>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      const float ah = row_bcast<h>(a);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= ah;
-    });
+    for (int j = 0; j < 8; ++j) acc.c[j] *= a;
+  }
+  if (evm > acc.eref) {
+    if (acc.eref != kNoRef) {
+      const int sh = acc.eref - evm;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc.c[j][i] = __builtin_amdgcn_ldexpf(acc.c[j][i], sh);
+    }
+    acc.eref = evm;
   }
   float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);
   l += (p[0] + p[1]) + (p[2] + p[3]);
+  const f16x4 b = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[0], ev[0] - acc.eref)),
+                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[1], ev[1] - acc.eref)),
+                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[2], ev[2] - acc.eref)),
+                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[3], ev[3] - acc.eref))};
+  // 4x4 byte transposes: X[4 q + k] = byte k of t.w[0..3][q] (rows 0..3)
+  uint32_t X[8];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int ev = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
-    const float pr = __builtin_amdgcn_ldexpf(p[r], ev);
-    float vf[8];
-    float f0[4], f1[4];
-    fp8x4_to_f32(t.w[r][0], f0);
-    fp8x4_to_f32(t.w[r][1], f1);
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t A = __builtin_amdgcn_perm(t.w[1][q], t.w[0][q], 0x05010400u);
+    const uint32_t Bq = __builtin_amdgcn_perm(t.w[1][q], t.w[0][q], 0x07030602u);
+    const uint32_t C = __builtin_amdgcn_perm(t.w[3][q], t.w[2][q], 0x05010400u);
+    const uint32_t Dq = __builtin_amdgcn_perm(t.w[3][q], t.w[2][q], 0x07030602u);
+    X[4 * q + 0] = __builtin_amdgcn_perm(C, A, 0x05040100u);
+    X[4 * q + 1] = __builtin_amdgcn_perm(C, A, 0x07060302u);
+    X[4 * q + 2] = __builtin_amdgcn_perm(Dq, Bq, 0x05040100u);
+    X[4 * q + 3] = __builtin_amdgcn_perm(Dq, Bq, 0x07060302u);
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vf[e] = f0[e];
-      vf[4 + e] = f1[e];
+  for (int j = 0; j < 8; ++j) {
+    float f[4];
+    fp8x4_to_f32(X[j], f);
+    const u32x2 av = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1])),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3]))};
+    acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av), b, acc.c[j], 0, 0, 0);
+  }
+}
+
+// End of a segment on the 8-bit path: lane (g4, c16) holds head c16's
+// head-dims 32 g4 .. + 31; the four token groups' sums l are added, and each
+// lane of a real head (c16 < G) writes its 32 values (normalised output, or
+// the partial with its (m, l)).
+__device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc, int lane, int G,
+                                               bool final, void* out, int out_dtype,
+                                               int64_t out_row0, float* ws_acc, float* ws_ml,
+                                               int64_t ws_row0) {
+  constexpr int D = 128;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (c16 >= G) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i], acc.eref);
+  if (final) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t o = (out_row0 + c16) * D + 32 * g4;
+    if (out_dtype == PKV_F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        dst[k] = make_float4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+    } else {
+      uint32_t w[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float y0 = v[2 * k] * inv, y1 = v[2 * k + 1] * inv;
+        const uint32_t h0 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y0)
+                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y0));
+        const uint32_t h1 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y1)
+                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y1));
+        w[k] = h0 | (h1 << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
     }
-    for_each_head<GP>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      const float ph = row_bcast<h>(pr);
+  } else {
+    const int64_t slot = ws_row0 + c16;
+    float4* dst = reinterpret_cast<float4*>(ws_acc + slot * D + 32 * g4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
-    });
+    for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    if (g4 == 0) {
+      ws_ml[2 * slot + 0] = m;
+      ws_ml[2 * slot + 1] = l;
+    }
   }
 }
 
@@ -1291,11 +1392,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       fetch_new(cs, cn, bc);
       int seg_lo = cs, seg_hi = cs + cn;    // tiles of the current segment
       float m = -INFINITY, l = 0.f;
-      float acc[GP][F::kW];
-#pragma unroll
-      for (int h = 0; h < GP; ++h)
-#pragma unroll
-        for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+      std::conditional_t<KV8, Acc8, AccV<GP>> acc;
+      acc_zero(acc);
       // Per chunk: wait for its DMA (and its query group); scores from the K
       // rows in LDS; then the next chunk's fetch (V into `vnext`) and, when
       // that chunk is in another sequence, its query group into LDS; then
@@ -1331,24 +1429,24 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
         for (int j = 0; j < CH; ++j) {
           if (j < cn) {
             if constexpr (KV8)
-              softmax_pv8<GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+              softmax_pv8(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
             else
-              softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+              softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc.a, lane);
           }
         }
         if (bn != bc) {
           const bool complete = seg_lo == uni(S[bc]) && seg_hi == uni(S[bc + 1]);
           const int slot = back ? (seg_hi == g1 ? 2 : 3) : (seg_lo == g0 ? 0 : 1);
-          wave_epilogue<DT, D, GP>(m, l, acc, lane, G, complete, a.out, a.out_dtype,
-                                   static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G,
-                                   a.ws_acc, a.ws_ml,
-                                   (rng * kStreamSlots + slot) * a.hq + static_cast<int64_t>(kvh) * G, 1);
+          const int64_t orow = static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G;
+          const int64_t wrow = (rng * kStreamSlots + slot) * a.hq + static_cast<int64_t>(kvh) * G;
+          if constexpr (KV8)
+            wave_epilogue8(m, l, acc, lane, G, complete, a.out, a.out_dtype, orow, a.ws_acc, a.ws_ml, wrow);
+          else
+            wave_epilogue<DT, D, GP>(m, l, acc.a, lane, G, complete, a.out, a.out_dtype, orow,
+                                     a.ws_acc, a.ws_ml, wrow, 1);
           m = -INFINITY;
           l = 0.f;
-#pragma unroll
-          for (int h = 0; h < GP; ++h)
-#pragma unroll
-            for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+          acc_zero(acc);
           seg_lo = ns;
           seg_hi = ns + nn;
         } else {
@@ -1680,6 +1778,8 @@ hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, const Step
 template <int DT, bool KV8 = false>
 hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, const StepMeta* meta,
                             hipStream_t s) {
+  // the 8-bit path's P.V covers 16 heads on the matrix cores whatever G is
+  if constexpr (KV8) return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
   switch (gp) {
     case 1: return launch_stream_t<DT, 1, KV8>(a, pl, meta, s);
     case 2: return launch_stream_t<DT, 2, KV8>(a, pl, meta, s);
