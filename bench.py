@@ -230,7 +230,8 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
             "kernel": f"attn_stream8_kernel<{cfg.dtype} q, D={cfg.head_dim}, "
                       f"G={cfg.num_q_heads // cfg.num_kv_heads}>",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": recorded_traffic("attn_stream8_kernel", cfg.name)[0],
             "mean_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
             "algorithmic_bytes_per_launch": round(alg),
         },

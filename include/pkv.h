@@ -405,9 +405,9 @@ int pkv_decode_step(void* out, int32_t out_dtype, const void* q, const void* key
  * The two launches of pkv_decode_step, callable separately with the same
  * arguments: _partial runs the write and the attention kernel, leaving
  * partials of split sequences in `workspace`; _merge reduces them into
- * `out` (in the one-launch form it takes the lengths from `lens`, host,
- * as kernel arguments).  paged_decode_attention_merge with context_lens =
- * lens_out and the same other arguments may stand in for _merge.  The pair,
+ * `out` (reading the lengths from lens_out).  paged_decode_attention_merge
+ * with context_lens = lens_out and the same other arguments may stand in
+ * for _merge.  The pair,
  * in this order on one stream, equals one pkv_decode_step call.
  */
 int pkv_decode_step_partial(void* out, int32_t out_dtype, const void* q, const void* key,

@@ -925,10 +925,11 @@ constexpr int kStreamChunk = 2;
 
 // ---- 8-bit KV blocks (PKV_FP8_E4M3): D = 128 one-byte E4M3 codes per row
 // and one E8M0 scale byte per row (value 2^(byte - 127); the encoding is in
-// pkv_fp8.hip).  A tile is 2 KiB of codes, so a chunk takes twice the tiles
-// for the same bytes in flight.  The hardware conversion on gfx950 reads the
+// pkv_fp8.hip).  A tile is 2 KiB of codes; chunks stay at two tiles (four
+// measured slower: the extra per-tile addresses and buffer descriptors
+// spill scalar registers).  The hardware conversion on gfx950 reads the
 // codes as OCP E4M3 (checked code by code against the definition).
-constexpr int kStreamChunk8 = 4;
+constexpr int kStreamChunk8 = 2;
 
 struct VTile8 {
   uint32_t w[4][2];   // lane (g4, c16): codes 8 c16 .. 8 c16 + 7 of rows 4 g4 + r
@@ -1484,22 +1485,16 @@ attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
   stream_body<DT, GP, PAIRED, true, false>(a, &meta);
 }
 
-// Lengths of at most kStepRows sequences carried in the kernel arguments.
-struct LensMeta {
-  int32_t lens[kStepRows];
-};
-
 // Merge of the stream kernel's partials.  One 64-lane workgroup per
 // (sequence, query head).  A sequence with L = 0 gets zeros; one that a
 // single segment covered was finished already; otherwise its pieces are
 // combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The
 // pieces of sequence b are, in every range that holds some of its tiles,
 // the part before the range's split tile x (front worker) and the part
-// from x on (back worker), where not empty.  The lengths come from
-// `meta` (ARG_LENS) or from a.lens.
-template <int D, bool ARG_LENS>
+// from x on (back worker), where not empty.
+template <int D>
 __global__ void __launch_bounds__(kWave)
-attn_stream_merge_kernel(StreamArgs a, LensMeta meta) {
+attn_stream_merge_kernel(StreamArgs a) {
   __shared__ int32_t plist[2 * kStreamMaxRanges];
   const int lane = threadIdx.x;
   const int qh = blockIdx.x % a.hq;
@@ -1509,7 +1504,7 @@ attn_stream_merge_kernel(StreamArgs a, LensMeta meta) {
   const int R = a.ranges_per_wg;
   const int J = R * a.hkv;
   const bool paired = 2 * a.hkv <= kStreamMaxWaves;
-  auto len_of = [&](int j) { return clamp_len(ARG_LENS ? meta.lens[j] : a.lens[j], a.max_len); };
+  auto len_of = [&](int j) { return clamp_len(a.lens[j], a.max_len); };
   int before = 0, total = 0;
   for (int j = lane; j < a.num_seqs; j += kWave) {
     const int t = (len_of(j) + kTile - 1) / kTile;
@@ -2057,14 +2052,10 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
+        // lengths from device memory (for the decode step: lens_out, written by
+        // the first launch); a copy in the kernel arguments measured slower
         const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
-        LensMeta lm;
-        if (step) {
-          for (int32_t i = 0; i < num_seqs; ++i) lm.lens[i] = step->meta->lens[i];
-          hipLaunchKernelGGL((attn_stream_merge_kernel<128, true>), grid, dim3(kWave), 0, s, sa, lm);
-        } else {
-          hipLaunchKernelGGL((attn_stream_merge_kernel<128, false>), grid, dim3(kWave), 0, s, sa, lm);
-        }
+        hipLaunchKernelGGL(attn_stream_merge_kernel<128>, grid, dim3(kWave), 0, s, sa);
         if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
       }
       return PKV_OK;
