@@ -1,4 +1,4 @@
-"""Decode attention (oracle, test infrastructure only).
+"""Decode and chunked-prefill attention (oracle, test infrastructure only).
 
 The quantity is [MiniPaged-Qwen] §1.1 / §13:
     O = softmax(scale * q K^T) V
@@ -16,6 +16,10 @@ whole blocks, to apply the GQA map and to drop the causal mask).
 block table with a running max / sum / accumulator, the "online softmax"
 CPU reference [MiniPaged-Qwen] §17.3 names; it is the second route used to
 check the first.
+
+``prefill_attention`` is the multi-query form: a chunk of query rows at the
+last positions of a sequence, each under the causal mask of [impl-detail]
+"分块注意力".  Pins: ``tests/test_oracle_prefill.py``.
 """
 from __future__ import annotations
 
@@ -112,4 +116,46 @@ def decode_attention_online(q_b: np.ndarray, key_cache: np.ndarray, value_cache:
             l = l * a + e
             m = m_new
         out[qh] = acc / l
+    return out
+
+
+def prefill_attention(q: np.ndarray, q_start: Sequence[int], key_cache: np.ndarray,
+                      value_cache: np.ndarray, block_tables: np.ndarray,
+                      context_lens: Sequence[int], scale: float, dtype: str) -> np.ndarray:
+    """Chunked-prefill attention through block tables, float64.
+
+    Sequence b holds L_b = context_lens[b] cached tokens (the chunk's own K/V
+    already written, [MiniPaged-Qwen] §1.1 and §12); its n_b query rows are
+    q[q_start[b] : q_start[b + 1]], the last n_b positions: row i sits at
+    p = L_b - n_b + i and attends to positions 0 .. p with the causal mask of
+    [impl-detail] "分块注意力" (``create_causal_mask``), the GQA map of
+    [MiniPaged-Qwen] §14 and the gather of [MiniPaged-Qwen] §13.  A full
+    prefill is n_b = L_b; decode is n_b = 1.  Rows with p < 0 get zeros.
+    Returns float64 [T, H_q, D].
+    """
+    T, h_q, d = q.shape
+    h_kv = key_cache.shape[1]
+    out = np.zeros((T, h_q, d), dtype=np.float64)
+    for b in range(len(context_lens)):
+        L = int(context_lens[b])
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n = r1 - r0
+        if n == 0 or L == 0:
+            continue
+        table = [int(x) for x in block_tables[b]]
+        k = widen(gather_logical(key_cache, table, L), dtype)      # [H_kv, L, D]
+        v = widen(gather_logical(value_cache, table, L), dtype)
+        qb = widen(q[r0:r1], dtype)                                 # [n, H_q, D]
+        pos = L - n + np.arange(n)                                  # query positions
+        mask = np.arange(L)[None, :] <= pos[:, None]                # [n, L] causal
+        for qh in range(h_q):
+            kvh = kv_head_of(qh, h_q, h_kv)
+            s = float(scale) * (qb[:, qh, :] @ k[kvh].T)            # [n, L]
+            s = np.where(mask, s, -np.inf)
+            smax = s.max(axis=1, keepdims=True)
+            live = np.isfinite(smax[:, 0])
+            e = np.where(mask, np.exp(s - np.where(live[:, None], smax, 0.0)), 0.0)
+            den = e.sum(axis=1, keepdims=True)
+            o = (e @ v[kvh]) / np.where(den > 0, den, 1.0)
+            out[r0:r1, qh, :] = np.where(live[:, None], o, 0.0)
     return out
