@@ -37,6 +37,7 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc", "pkv_kernels.hip")
 
 
@@ -162,6 +163,51 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
             "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, seed: int = 2024):
+    """Full-prompt prefill attention (paged_prefill_attention) with the
+    workload's head shape: ``seqs`` prompts of ``prompt`` tokens admitted and
+    written through the engine, then the attention launch timed with HIP
+    events around ``iters`` back-to-back launches.  Useful FLOPs: row i of a
+    prompt sees i + 1 keys, 4 * D FLOPs per key and query head (Q.K and P.V)."""
+    import torch
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    import paged_kv_cache_128_amd as pkv
+    tdtype = {"bf16": torch.bfloat16, "f16": torch.float16}[cfg.dtype]
+    bs, D, hq, hkv = cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    per = -(-prompt // bs)
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    eng = PagedKVEngine(seqs * per + 8, hkv, bs, D, tdtype, seqs, per,
+                        np.random.default_rng(seed).permutation(seqs * per + 8), num_q_heads=hq)
+    T = seqs * prompt
+    k = torch.randn((T, hkv, D), device="cuda", generator=g).to(tdtype)
+    v = torch.randn((T, hkv, D), device="cuda", generator=g).to(tdtype)
+    q = torch.randn((T, hq, D), device="cuda", generator=g).to(tdtype)
+    scale = 1.0 / float(np.sqrt(D))
+    out = eng.prefill_chunk(list(range(seqs)), list(range(seqs)), [prompt] * seqs, k, v, q, scale)
+    qs = torch.arange(0, T + 1, prompt, dtype=torch.int32, device="cuda")
+    lens = torch.full((seqs,), prompt, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
+                                    max_q_len=prompt, max_context_len=prompt, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
+                                    max_q_len=prompt, max_context_len=prompt, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    flops = seqs * (prompt * (prompt + 1) // 2) * hq * 4 * D
+    tflops = flops / (us * 1e-6) / 1e12
+    log(f"prefill: {seqs} x {prompt} tokens in {us:.1f} us per launch ({tflops:.0f} TFLOP/s)")
+    return {"kernel": f"prefill_kernel<{cfg.dtype}, D={D}>", "workload": f"{seqs} prompts of {prompt} "
+            f"tokens, H_q={hq} H_kv={hkv}, causal, full prefill", "mean_launch_us": round(us, 2),
+            "useful_flops_per_launch": flops, "achieved_tflops": round(tflops, 1),
+            "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "prefill_tokens_per_s": round(seqs * prompt / (us * 1e-6), 1)}
+
+
 def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
     """The same workload with an 8-bit KV pool (E4M3 codes + one scale byte
     per row; the history quantised by the prefill write): decode steps of
@@ -255,6 +301,7 @@ def main():
     ap.add_argument("--separate-write", action="store_true",
                     help="run the step's write as its own launch instead of inside the attention")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill attention measurement")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -374,6 +421,9 @@ def main():
     fp8 = None
     if not args.no_fp8 and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
         fp8 = measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s)
+    prefill = None
+    if not args.no_prefill and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
+        prefill = measure_prefill(cfg)
 
     import paged_kv_cache_128_amd as pkv
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
@@ -433,6 +483,7 @@ def main():
         "kernel_source_sha256_16": kernel_source_sha(),
         "copy_on_write": block_copy,
         "fp8_kv": fp8,
+        "prefill": prefill,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)

@@ -161,6 +161,17 @@ int pkv_append_slots_for_decode(pkv_manager* mgr, const int64_t* seq_ids, int32_
                                 int64_t* slots_out, int32_t* lens_out,
                                 int32_t* new_block_out);
 
+/*
+ * Append `num_tokens` (>= 0) tokens to live `seq_id` (a prefill chunk):
+ * slots_out (host, [num_tokens], nullable) receives the slots of positions
+ * len .. len + num_tokens - 1, each as pkv_append_slot_for_decode computes
+ * it (opening blocks, and copying a shared tail block on write), all or
+ * nothing: the blocks the call takes are checked against the free list
+ * first ([MiniPaged-Qwen] §9; [mini-vLLM BM] "prefill 时如何分配 block").
+ * Errors: INVALID, NOT_LIVE, OOM.
+ */
+int pkv_append_tokens(pkv_manager* mgr, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
+
 /* Release `seq_id`: each block of its table loses one reference, and those
  * whose count reaches 0 are appended to the free list in table order
  * ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  Errors: NOT_LIVE. */
@@ -424,6 +435,34 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
                           int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
                           int32_t max_context_len, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------- prefill attention */
+/*
+ * Chunked-prefill attention through block tables: sequence b holds
+ * L = context_lens[b] cached tokens (the chunk's own K/V already written,
+ * e.g. by paged_kv_write; [MiniPaged-Qwen] §1.1, §12); its query rows are
+ * q[q_start[b] .. q_start[b + 1] - 1], the last n_b positions, row i at
+ * p = L - n_b + i attending to positions 0 .. p only (the causal mask of
+ * [impl-detail] "分块注意力"), with the GQA map kvh = qh / (H_q / H_kv)
+ * ([MiniPaged-Qwen] §14) and the table addressing of §13.  A full prefill
+ * is n_b = L; rows with p < 0 get zeros.
+ *   out          device, [T, num_q_heads, D], T = q_start[num_seqs];
+ *                PKV_F32 or the cache dtype
+ *   q            device, [T, num_q_heads, D] contiguous, cache dtype
+ *   q_start      device int32 [num_seqs + 1], non-decreasing from 0
+ *   context_lens device int32 [num_seqs], clamped to [0, max_context_len]
+ *   max_q_len    host, >= every n_b (sizes the grid)
+ * Products run on the matrix cores in the cache's 16-bit type with fp32
+ * accumulation; P enters P.V as a 16-bit value plus a 16-bit remainder.
+ * Supported: 16-bit KV, head_dim 128, block_size a multiple of 16.
+ * Errors: INVALID, UNSUPPORTED, HIP.
+ */
+int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const int32_t* q_start,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
+                            const void* key_cache, const void* value_cache,
+                            const pkv_cache_layout* layout, const int32_t* block_tables,
+                            int32_t block_table_stride, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* stream);
 
 /* ------------------------------------------------------------- FP8 KV */
 /*

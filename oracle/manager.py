@@ -248,6 +248,23 @@ class BlockManager:
             raise OutOfBlocks()
         return [self.append_slot_for_decode(s) for s in ids]
 
+    def append_tokens(self, seq_id: int, num_tokens: int) -> List[int]:
+        """Slots of ``num_tokens`` new tokens at positions len .. len + n - 1
+        (a prefill chunk of a live sequence), all or nothing: the blocks the
+        n appends take (opened blocks, and a copy of a shared tail block) are
+        counted first; then each token is appended as append_slot_for_decode
+        does ([MiniPaged-Qwen] §9; [mini-vLLM BM] "prefill 时如何分配 block")."""
+        seq = self._live(seq_id)
+        if num_tokens < 0:
+            raise InvalidArgument("num_tokens must be >= 0")
+        L, bs = seq.length, self.block_size
+        need = blocks_needed(L + num_tokens, bs) - len(seq.table)
+        if num_tokens > 0 and L // bs < len(seq.table) and self.ref[seq.table[L // bs]] > 1:
+            need += 1
+        if need > len(self.free):
+            raise OutOfBlocks()
+        return [self.append_slot_for_decode(seq_id) for _ in range(num_tokens)]
+
     def free_sequence(self, seq_id: int) -> None:
         """Return every block of ``seq_id`` to the free list exactly once
         ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block")."""

@@ -90,6 +90,9 @@ SIGNATURES = {
     "pkv_append_slots_for_decode": (ctypes.c_int, [_P, _PI64, _I32, _PI64, _PI32, _PI32]),
     "pkv_free_sequence": (ctypes.c_int, [_P, _I64]),
     "pkv_share_prefix": (ctypes.c_int, [_P, _I64, _I64, _I32]),
+    "pkv_append_tokens": (ctypes.c_int, [_P, _I64, _I32, _PI64]),
+    "paged_prefill_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
+                                               ctypes.POINTER(CacheLayout), _P, _I32, _I32, _I32, _F32, _P]),
     "pkv_block_ref_count": (_I32, [_P, _I32]),
     "pkv_take_block_copies": (ctypes.c_int, [_P, _PI32, _PI32, _I32, _PI32]),
     "pkv_copy_blocks": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
@@ -276,6 +279,14 @@ class KVBlockManager:
     def free_sequence(self, seq_id: int) -> None:
         _check(self._lib.pkv_free_sequence(self._h, int(seq_id)), "free_sequence")
 
+    def append_tokens(self, seq_id: int, num_tokens: int) -> np.ndarray:
+        """Slots of num_tokens new tokens of a live sequence, all or nothing
+        (see pkv_append_tokens)."""
+        slots = np.empty(max(int(num_tokens), 0), dtype=np.int64)
+        _check(self._lib.pkv_append_tokens(self._h, int(seq_id), int(num_tokens),
+                                           _ptr(slots, ctypes.c_int64)), "append_tokens")
+        return slots
+
     def share_prefix(self, donor_id: int, seq_id: int, num_tokens: int) -> None:
         """New sequence on the donor's first ceil(num_tokens / bs) blocks
         (see pkv_share_prefix)."""
@@ -444,6 +455,39 @@ def paged_decode_attention_fp8(q, key_cache, value_cache, key_scales, value_scal
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream_handle(stream))
     _check(st, "paged_decode_attention_fp8")
+    return out
+
+
+def paged_prefill_attention(q, q_start, key_cache, value_cache, block_tables, context_lens,
+                            scale: float, max_q_len: int, max_context_len: Optional[int] = None,
+                            out=None, out_dtype=None, stream=None):
+    """Chunked-prefill causal attention (see paged_prefill_attention in
+    pkv.h): q [T, H_q, D]; q_start int32 [B + 1] and context_lens int32 [B]
+    device tensors; max_q_len (host) bounds the rows of one sequence."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    T, hq, d = q.shape
+    B = context_lens.shape[0]
+    if d != lay.head_dim or q.dtype != key_cache.dtype or not q.is_contiguous():
+        raise ValueError("q must be contiguous [T, H_q, head_dim] in the cache dtype")
+    if q_start.dtype != torch.int32 or q_start.shape != (B + 1,) or not q_start.is_contiguous():
+        raise ValueError("q_start must be contiguous int32 [B + 1]")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] < B \
+            or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [>= B, W] with unit column stride")
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * lay.block_size
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32 if out_dtype is None else out_dtype,
+                          device=q.device)
+    st = _lib_handle().paged_prefill_attention(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), q_start.data_ptr(), context_lens.data_ptr(),
+        B, int(max_q_len), key_cache.data_ptr(), value_cache.data_ptr(), ctypes.byref(lay),
+        block_tables.data_ptr(), block_tables.stride(0), hq, int(max_context_len), float(scale),
+        _stream_handle(stream))
+    _check(st, "paged_prefill_attention")
     return out
 
 
@@ -656,7 +700,7 @@ __all__ = [
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
     "copy_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
-    "paged_decode_attention_fp8", "PKV_FP8_E4M3",
+    "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

@@ -23,7 +23,7 @@ LIB = os.path.join(LIBDIR, "libpkv.so")
 OBJDIR = os.path.join(ROOT, "_build", "pkv")
 
 ARCH = "gfx950"
-SOURCES = ["pkv_kernels.hip", "pkv_blocks.hip", "pkv_fp8.hip", "manager.cpp"]
+SOURCES = ["pkv_kernels.hip", "pkv_blocks.hip", "pkv_fp8.hip", "pkv_prefill.hip", "manager.cpp"]
 # Packed fp32 ops (v_pk_*_f32) are switched off for every device pass.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall",

@@ -270,6 +270,32 @@ int pkv_append_slots_for_decode(pkv_manager* m, const int64_t* seq_ids, int32_t 
   return PKV_OK;
 }
 
+int pkv_append_tokens(pkv_manager* m, int64_t seq_id, int32_t num_tokens, int64_t* slots_out) {
+  if (!m || num_tokens < 0) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  Sequence& s = it->second;
+  if (static_cast<int64_t>(s.length) + num_tokens > INT32_MAX) return PKV_ERR_INVALID;
+  const int64_t bs = m->block_size;
+  int64_t need = m->blocks_for(static_cast<int64_t>(s.length) + num_tokens) - static_cast<int64_t>(s.table.size());
+  if (num_tokens > 0 && s.length / bs < static_cast<int64_t>(s.table.size()) &&
+      m->ref[s.table[s.length / bs]] > 1)
+    ++need;
+  if (need > m->count) return PKV_ERR_OOM;
+  try {
+    s.table.reserve(m->blocks_for(static_cast<int64_t>(s.length) + num_tokens));
+    m->copies.reserve(m->copies.size() + 1);
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    int32_t nb;
+    const int64_t slot = append_one(m, s, &nb);
+    if (slots_out) slots_out[i] = slot;
+  }
+  return PKV_OK;
+}
+
 int pkv_free_sequence(pkv_manager* m, int64_t seq_id) {
   if (!m) return PKV_ERR_INVALID;
   auto it = m->seqs.find(seq_id);

@@ -32,9 +32,9 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, copy_blocks, decode_step, decode_write, decode_write_fp8, new_fp8_pool,
-               new_pool, paged_decode_attention, paged_decode_attention_fp8, paged_kv_write,
-               paged_kv_write_fp8, workspace_size)
+from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_write, decode_write_fp8,
+               new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
+               paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, workspace_size)
 
 
 class PagedKVEngine:
@@ -83,6 +83,44 @@ class PagedKVEngine:
             self._write(key, value, d_slots)
         self._publish_row(seq_id, row)
         return slots
+
+    def prefill_chunk(self, seq_ids: Sequence[int], rows: Sequence[int], chunk_lens: Sequence[int],
+                      key: torch.Tensor, value: torch.Tensor, q: torch.Tensor, scale: float,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """One prefill chunk per sequence: a sequence not yet live is admitted
+        with its chunk as its prompt, a live one is extended by it
+        (pkv_append_tokens); the chunks' K/V rows ([sum(chunk_lens), H_kv, D],
+        concatenated in order) are written, then every chunk's query rows
+        (q [sum(chunk_lens), H_q, D]) attend causally over their sequence
+        (paged_prefill_attention).  Returns out [sum(chunk_lens), H_q, D]."""
+        if self.fp8:
+            raise NotImplementedError("prefill attention reads 16-bit KV blocks")
+        all_slots, lens = [], []
+        for sid, row, n in zip(seq_ids, rows, chunk_lens):
+            sid, n = int(sid), int(n)
+            try:
+                self.manager.context_len(sid)
+                all_slots.append(self.manager.append_tokens(sid, n))
+            except NotLiveError:
+                all_slots.append(self.manager.allocate_for_prefill(sid, n))
+            lens.append(self.manager.context_len(sid))
+        if self._sharing:
+            src, dst = self.manager.take_copies()
+            if len(src):
+                copy_blocks(src, dst, self.key_cache, self.value_cache)
+        slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
+        if slots.size:
+            self._write(key, value, torch.from_numpy(slots).to(self.device))
+        for sid, row in zip(seq_ids, rows):
+            self._publish_row(int(sid), int(row))
+        B = len(seq_ids)
+        q_start = np.concatenate([[0], np.cumsum(np.asarray(chunk_lens, dtype=np.int64))]).astype(np.int32)
+        d_qs = torch.from_numpy(q_start).to(self.device)
+        d_lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(self.device)
+        tables = self.tables[torch.as_tensor(list(rows), dtype=torch.long, device=self.device)]
+        return paged_prefill_attention(q, d_qs, self.key_cache, self.value_cache, tables, d_lens, scale,
+                                       max_q_len=int(max(chunk_lens)) if B else 0,
+                                       max_context_len=int(max(lens)) if B else 0, out=out)
 
     def _write(self, key, value, d_slots):
         if self.fp8:

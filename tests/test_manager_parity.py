@@ -180,3 +180,42 @@ def test_batched_append_reports_copy_on_write_blocks():
     src, dst = m.take_copies()
     assert src.tolist() == [1] and dst.tolist() == [2]
     assert m.block_table(1) == [0, 2] and m.ref_count(1) == 1
+
+
+@pytest.mark.parametrize("seed,n_blocks,bs", [(51, 30, 4), (52, 16, 16), (53, 9, 1)])
+def test_append_tokens_matches_oracle(seed, n_blocks, bs):
+    """Multi-token appends (prefill chunks), with sharing so that a chunk can
+    start in a shared tail block: identical slots, errors, tables, copies
+    and free lists."""
+    rng = np.random.default_rng(seed)
+    o = oracle.BlockManager(n_blocks, bs)
+    c = pkv.KVBlockManager(n_blocks, bs)
+    kinds = set()
+    for _ in range(600):
+        u = rng.random()
+        sid = int(rng.integers(8))
+        if u < 0.2:
+            op = ("prefill", sid, int(rng.integers(0, 12)))
+        elif u < 0.35:
+            op = ("share", int(rng.integers(8)), sid, int(rng.integers(0, 12)))
+        elif u < 0.8:
+            op = ("append_tokens", sid, int(rng.integers(0, 20)))
+        else:
+            op = ("free", sid)
+        res = []
+        for mgr, impl in ((o, "o"), (c, "c")):
+            try:
+                if op[0] == "append_tokens":
+                    r = ("ok", [int(x) for x in mgr.append_tokens(op[1], op[2])])
+                else:
+                    r = _run_share(mgr, op, impl)[0]
+            except (oracle.ManagerError, pkv.PkvError) as e:
+                r = ("err", next(o_.__name__ for o_, c_ in ERR.items() if isinstance(e, (o_, c_))))
+            copies = mgr.take_copies()
+            if impl == "c":
+                copies = list(zip(copies[0].tolist(), copies[1].tolist()))
+            res.append((r, copies))
+        assert res[0] == res[1], (op, res)
+        kinds.add(res[0][0][0] if res[0][0][0] == "ok" else res[0][0][1])
+        assert c.free_list() == o.free and c.check_invariants() and o.check_invariants() == []
+    assert {"ok", "OutOfBlocks"} <= kinds
