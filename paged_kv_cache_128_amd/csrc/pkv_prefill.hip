@@ -7,23 +7,27 @@
 // full prefill is n_b = L_b.
 //
 // Unlike decode, each K/V tile meets many query rows, so both products are
-// dense contractions and run on the matrix cores.  One wave takes 16 query
-// rows of one head; a workgroup four waves (64 rows) of one (sequence, head),
-// and it stages the sequence's block-table entries in LDS once.  Per tile of
-// 16 keys:
-//   - scores S^T[key][row] = K Q^T by four 16x16x32 MFMAs (A = K rows as
-//     loaded, B = the query rows), so lane (g4, c16) holds row c16's scores
-//     for keys 4 g4 .. 4 g4 + 3 -- which is the B operand layout of P.V;
-//   - online softmax per row (exp2 with the scale folded in, fp32 state);
-//   - O^T[d][row] += V^T P^T by 16x16x16 MFMAs: MFMA j maps its row index c
-//     to head-dim 8 c + j, so its A operand is element j of the lane's V
-//     rows 4 g4 .. 4 g4 + 3 at head-dims 8 c16 .. 8 c16 + 7 (as loaded), and
-//     P enters as a 16-bit high part plus a 16-bit remainder (two MFMAs),
-//     which keeps P to about 2^-17 of its value.
-// Lane (g4, c16) ends with row c16's head-dims 32 g4 .. 32 g4 + 31.  The next
-// tile's K and V are fetched while the current one's P.V runs.  Keys past L
-// read zeros (buffer range check) and are masked like every key past the
-// row's position.  16-bit KV, head_dim 128.
+// dense contractions and run on the matrix cores.  A workgroup takes 128
+// query rows of one (sequence, head): four waves of 32 rows, each as two
+// 16-column MFMA blocks.  Per tile of 64 keys (four 16-key sub-tiles, each
+// inside one block) the workgroup stages K and V once in LDS (double-
+// buffered, filled by LDS-DMA while the previous tile is being used; K rows
+// XOR-swizzled so the operand reads hit distinct banks), then for each
+// sub-tile every wave
+//   - forms scores S^T[key][row] = K Q^T with 16x16x32 MFMAs (A = K rows,
+//     B = the query rows), so lane (g4, c16) holds row c16's scores for
+//     keys 4 g4 .. 4 g4 + 3 -- the B operand layout of P.V;
+//   - runs the online softmax per row (exp2 with the scale folded in, fp32
+//     state);
+//   - adds O^T[d][row] += V^T P^T with 16x16x16 MFMAs: MFMA j maps its row
+//     index c to head-dim 8 c + j, so its A operand is element j of V rows
+//     4 g4 .. 4 g4 + 3 at head-dims 8 c16 .. 8 c16 + 7, and P enters as a
+//     16-bit value plus its 16-bit remainder (two MFMAs; P to about 2^-17).
+// Lane (g4, c16) ends with its rows' head-dims 32 g4 .. 32 g4 + 31.  A wave
+// skips the products of tiles wholly past its rows' positions (it still
+// takes part in the staging).  Keys past L read zeros (buffer range check)
+// and are masked like every key past a row's position.  16-bit KV, head_dim
+// 128.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -33,15 +37,19 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kRowsPerWave = 16;
 constexpr int kWavesPF = 4;
+constexpr int kBlocksPerWave = 2;                     // 16-row MFMA column blocks per wave
+constexpr int kRowsPerWave = 16 * kBlocksPerWave;
 constexpr int kRowsPerWG = kRowsPerWave * kWavesPF;
-constexpr int kKeys = 16;
+constexpr int kKeys = 16;                             // keys per MFMA sub-tile
+constexpr int kSub = 4;                               // sub-tiles per staged tile
 constexpr int kD = 128;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kSlack = 8.0f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kWaitVm0 = 0x0f70;
+constexpr int kSubSlots = kKeys * kD * 2 / 16;        // 16-byte LDS slots of one K or V sub-tile
+constexpr int kTileSlots = kSub * kSubSlots;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +58,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct PrefillArgs {
   const void* q;             // [T, H_q, D]
@@ -73,15 +82,9 @@ struct PrefillArgs {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
 template <int DT>
 __device__ __forceinline__ uint16_t to16(float f) {
-  if constexpr (DT == PKV_BF16) return f32_to_bf16_rne(f);
+  if constexpr (DT == PKV_BF16) return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
   else return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
 }
 template <int DT>
@@ -115,150 +118,219 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c
                                                  c, 0, 0, 0);
 }
 
-struct KV {
-  u32x4 k[4];   // K operand: key c16, head-dims 32 kk + 8 g4 .. + 7
-  u32x4 v[4];   // V rows 4 g4 + r, head-dims 8 c16 .. + 7
-};
-
 template <int DT>
 __global__ void __launch_bounds__(kWave * kWavesPF)
 prefill_kernel(PrefillArgs a) {
-  extern __shared__ int32_t sh_tbl[];
+  // dynamic LDS: [K tile x 2][V tile x 2] (16-byte slots), then the table entries
+  extern __shared__ uint4 sh_pf[];
+  uint4* sk = sh_pf;                                  // 2 x kTileSlots
+  uint4* sv = sh_pf + 2 * kTileSlots;                 // 2 x kTileSlots
+  int32_t* tbl = reinterpret_cast<int32_t*>(sh_pf + 4 * kTileSlots);
   const int wave = uni(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & (kWave - 1);
   const int g4 = lane >> 4, c16 = lane & 15;
   const int b = blockIdx.z, qh = blockIdx.y;
+  const int qblk = gridDim.x - 1 - blockIdx.x;        // the longest blocks start first
   const int r0 = uni(a.q_start[b]);
   const int n = uni(a.q_start[b + 1]) - r0;
   const int Lraw = uni(a.lens[b]);
   const int L = Lraw < 0 ? 0 : (Lraw > a.max_len ? a.max_len : Lraw);
   const int bs = a.block_size;
-  // keys the workgroup's rows can see: up to the last of its rows' positions
-  const int wg_last = min(static_cast<int>(blockIdx.x) * kRowsPerWG + kRowsPerWG, n) - 1;
-  const int wg_keys = wg_last < 0 ? 0 : max(0, min(L, L - n + wg_last + 1));
+  const int wg_first = qblk * kRowsPerWG;
+  if (wg_first >= n) return;                          // whole workgroup: no rows
+  const int wg_last = min(wg_first + kRowsPerWG, n) - 1;
+  const int wg_keys = max(0, min(L, L - n + wg_last + 1));
+  const int ntiles = (wg_keys + kSub * kKeys - 1) / (kSub * kKeys);
   const int nblk = (wg_keys + bs - 1) / bs;
   for (int e = threadIdx.x; e < nblk; e += blockDim.x) {
     const int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + e];
-    sh_tbl[e] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    tbl[e] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
   }
   __syncthreads();
-  const int q0 = blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
-  if (q0 >= n) return;
   const int kvh = qh / a.group;
-  const int my_row = q0 + c16;
-  const bool row_ok = my_row < n;
-  const int my_pos = row_ok ? L - n + my_row : -1;       // keys 0 .. my_pos
-  const int last_row = min(q0 + kRowsPerWave, n) - 1;
-  const int nkeys = max(0, min(L, L - n + last_row + 1));
-  const int ntiles = (nkeys + kKeys - 1) / kKeys;
-  // query operand: row c16, head-dims 32 kk + 8 g4 .. + 7
-  u32x4 qf[4];
-  {
+  const int q0 = wg_first + wave * kRowsPerWave;      // this wave's first row
+  // the last key any of this wave's rows sees (-1: none)
+  const int w_last = min(q0 + kRowsPerWave, n) - 1;
+  const int w_maxkey = q0 < n ? min(L - 1, L - n + w_last) : -1;
+  int row[kBlocksPerWave], pos[kBlocksPerWave];
+  bool ok[kBlocksPerWave];
+#pragma unroll
+  for (int c = 0; c < kBlocksPerWave; ++c) {
+    row[c] = q0 + 16 * c + c16;
+    ok[c] = row[c] < n;
+    pos[c] = ok[c] ? L - n + row[c] : -1;             // keys 0 .. pos
+  }
+  // query operands: row c16 of block c, head-dims 32 kk + 8 g4 .. + 7
+  u32x4 qf[kBlocksPerWave][4];
+#pragma unroll
+  for (int c = 0; c < kBlocksPerWave; ++c) {
     const char* qrow = static_cast<const char*>(a.q) +
-                       ((static_cast<int64_t>(r0) + (row_ok ? my_row : 0)) * a.hq + qh) * kD * 2;
+                       ((static_cast<int64_t>(r0) + (ok[c] ? row[c] : 0)) * a.hq + qh) * kD * 2;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + (32 * kk + 8 * g4) * 2);
-      qf[kk] = row_ok ? x : u32x4{0u, 0u, 0u, 0u};
+      qf[c][kk] = ok[c] ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
   const char* kc = static_cast<const char*>(a.kc);
   const char* vc = static_cast<const char*>(a.vc);
   const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
-  auto fetch = [&](KV& t, int kt) {
-    const int key0 = kt * kKeys;
-    const int pb = uni(sh_tbl[key0 / bs]);
-    const int64_t base = (static_cast<int64_t>(pb) * a.block_stride + head_off +
-                          static_cast<int64_t>(key0 % bs) * kD) * 2;
-    const int nvalid = min(kKeys, L - key0);
+  // Stage tile kt into buffer kt % 2: wave w moves sub-tile w, K rows
+  // (chunk c of row r to slot c ^ r) and V rows (plain), four rows per
+  // 16-byte-per-lane DMA.  Rows past the workgroup's last key (a sub-tile
+  // wholly past it included) read zeros, so every V value that meets a zero
+  // probability is finite and only staged table entries are used.
+  auto stage = [&](int kt) {
+    const int key0 = (kt * kSub + wave) * kKeys;
+    const int nvalid = max(0, min(kKeys, wg_keys - key0));
+    const int pb = nvalid > 0 ? uni(tbl[key0 / bs]) : 0;
+    const int64_t base = nvalid > 0 ? (static_cast<int64_t>(pb) * a.block_stride + head_off +
+                                       static_cast<int64_t>(key0 % bs) * kD) * 2 : 0;
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kc + base, nvalid);
     const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vc + base, nvalid);
+    uint4* dk = sk + (kt & 1) * kTileSlots + wave * kSubSlots;
+    uint4* dv = sv + (kt & 1) * kTileSlots + wave * kSubSlots;
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      t.k[kk] = __builtin_amdgcn_raw_buffer_load_b128(rk, c16 * kD * 2 + (32 * kk + 8 * g4) * 2, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      t.v[r] = __builtin_amdgcn_raw_buffer_load_b128(rv, (4 * g4 + r) * kD * 2 + c16 * 16, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + g4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dk + 64 * i), 16,
+                                               r * kD * 2 + ((c16 ^ r) << 4), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dv + 64 * i), 16, r * kD * 2 + (c16 << 4), 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
   };
-  float m = -INFINITY, l = 0.f;
-  f32x4 acc[8];
+  float m[kBlocksPerWave], l[kBlocksPerWave];
+  f32x4 acc[kBlocksPerWave][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  KV cur, nxt;
-  if (ntiles > 0) fetch(cur, 0);
+  for (int c = 0; c < kBlocksPerWave; ++c) {
+    m[c] = -INFINITY;
+    l[c] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[c][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (ntiles > 0) stage(0);
   for (int kt = 0; kt < ntiles; ++kt) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();                  // tile kt staged by every wave; tile kt - 1 no longer read
+    if (kt + 1 < ntiles) stage(kt + 1);
+#pragma unroll 1
+    for (int sub = 0; sub < kSub; ++sub) {
+    const int key0 = (kt * kSub + sub) * kKeys;
+    if (key0 > w_maxkey) break;                       // every key from here on is past this wave's rows
+    const uint4* tk = sk + (kt & 1) * kTileSlots + sub * kSubSlots;
+    const uint4* tv = sv + (kt & 1) * kTileSlots + sub * kSubSlots;
+    // K operand: key c16, chunk 4 kk + g4 (slot (4 kk + g4) ^ c16)
+    u32x4 kf[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s = mfma_qk<DT>(cur.k[kk], qf[kk], s);
-    if (kt + 1 < ntiles) fetch(nxt, kt + 1);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt * kKeys + 4 * g4 + i;
-      x[i] = key <= my_pos ? s[i] * a.scale_log2 : -INFINITY;
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint4 x = tk[c16 * 16 + ((4 * kk + g4) ^ c16)];
+      kf[kk] = u32x4{x.x, x.y, x.z, x.w};
     }
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
-      const float m_new = fmaxf(m, bm);
-      const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-      l *= f;
-      m = m_new;
+    // V rows 4 g4 + r, head-dims 8 c16 .. + 7
+    uint4 vr[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= f;
-    }
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    // P as a 16-bit high part and remainder (B operand: keys 4 g4 + i, row c16)
-    uint16_t hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hi[i] = to16<DT>(p[i]);
-      lo[i] = to16<DT>(p[i] - from16<DT>(hi[i]));
-    }
-    const u32x2 bh = {static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
-                      static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
-    const u32x2 bl = {static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
-                      static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
+    for (int r = 0; r < 4; ++r) vr[r] = tv[(4 * g4 + r) * 16 + c16];
+    u32x2 av[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      // element j of V rows 4 g4 + r: half (j % 2) of dword j / 2
       const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const u32x2 av = {__builtin_amdgcn_perm(cur.v[1][j >> 1], cur.v[0][j >> 1], sel),
-                        __builtin_amdgcn_perm(cur.v[3][j >> 1], cur.v[2][j >> 1], sel)};
-      acc[j] = mfma_pv<DT>(av, bh, acc[j]);
-      acc[j] = mfma_pv<DT>(av, bl, acc[j]);
+      const int w = j >> 1;
+      const uint32_t v0 = w == 0 ? vr[0].x : w == 1 ? vr[0].y : w == 2 ? vr[0].z : vr[0].w;
+      const uint32_t v1 = w == 0 ? vr[1].x : w == 1 ? vr[1].y : w == 2 ? vr[1].z : vr[1].w;
+      const uint32_t v2 = w == 0 ? vr[2].x : w == 1 ? vr[2].y : w == 2 ? vr[2].z : vr[2].w;
+      const uint32_t v3 = w == 0 ? vr[3].x : w == 1 ? vr[3].y : w == 2 ? vr[3].z : vr[3].w;
+      av[j] = u32x2{__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v3, v2, sel)};
     }
-    if (kt + 1 < ntiles) cur = nxt;
+    // scores of both column blocks, each as two independent MFMA chains
+    f32x4 sa[kBlocksPerWave], sb[kBlocksPerWave];
+#pragma unroll
+    for (int c = 0; c < kBlocksPerWave; ++c) {
+      sa[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; kk += 2)
+#pragma unroll
+      for (int c = 0; c < kBlocksPerWave; ++c) {
+        sa[c] = mfma_qk<DT>(kf[kk], qf[c][kk], sa[c]);
+        sb[c] = mfma_qk<DT>(kf[kk + 1], qf[c][kk + 1], sb[c]);
+      }
+    u32x2 bh[kBlocksPerWave], bl[kBlocksPerWave];
+#pragma unroll
+    for (int c = 0; c < kBlocksPerWave; ++c) {
+      const f32x4 s = sa[c] + sb[c];
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 4 * g4 + i;
+        x[i] = key <= pos[c] ? s[i] * a.scale_log2 : -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      if (__builtin_amdgcn_ballot_w64(bm > m[c] + kSlack) != 0) {
+        const float m_new = fmaxf(m[c], bm);
+        const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
+        l[c] *= f;
+        m[c] = m_new;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[c][j] *= f;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m[c]);
+      l[c] += (p[0] + p[1]) + (p[2] + p[3]);
+      uint16_t hi[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = to16<DT>(p[i]);
+        lo[i] = to16<DT>(p[i] - from16<DT>(hi[i]));
+      }
+      bh[c] = u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
+                    static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
+      bl[c] = u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
+                    static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
+    }
+    // P.V: sixteen independent accumulators per pass (high part, then remainder)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int c = 0; c < kBlocksPerWave; ++c) acc[c][j] = mfma_pv<DT>(av[j], bh[c], acc[c][j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int c = 0; c < kBlocksPerWave; ++c) acc[c][j] = mfma_pv<DT>(av[j], bl[c], acc[c][j]);
+    }
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (!row_ok) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  const int64_t o = ((static_cast<int64_t>(r0) + my_row) * a.hq + qh) * kD + 32 * g4;
-  float v[32];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int c = 0; c < kBlocksPerWave; ++c) {
+    float lc = l[c];
+    lc += __shfl_xor(lc, 16);
+    lc += __shfl_xor(lc, 32);
+    if (!ok[c]) continue;
+    const float inv = lc > 0.f ? 1.0f / lc : 0.f;
+    const int64_t o = ((static_cast<int64_t>(r0) + row[c]) * a.hq + qh) * kD + 32 * g4;
+    float v[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[8 * i + j] = acc[j][i] * inv;
-  if (a.out_dtype == PKV_F32) {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + o);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-  } else {
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + o);
+      for (int j = 0; j < 8; ++j) v[8 * i + j] = acc[c][j][i] * inv;
+    if (a.out_dtype == PKV_F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + o);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t w[4];
+      for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    } else {
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + o);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e])) |
-               (static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e + 1])) << 16);
-      dst[k] = make_uint4(w[0], w[1], w[2], w[3]);
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e])) |
+                 (static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e + 1])) << 16);
+        dst[k] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 }
@@ -289,8 +361,13 @@ extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void*
                           reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache);
   if (align % 16 != 0 || (l->head_stride * 2) % 16 != 0 || (l->block_stride * 2) % 16 != 0)
     return PKV_ERR_UNSUPPORTED;
-  const size_t lds = static_cast<size_t>((max_context_len + l->block_size - 1) / l->block_size + 1) * 4;
-  if (lds > 65536) return PKV_ERR_UNSUPPORTED;
+  const size_t lds = static_cast<size_t>(4 * kTileSlots) * 16 +
+                    static_cast<size_t>((max_context_len + l->block_size - 1) / l->block_size + 1) * 4;
+  int dev = 0, lds_max = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return PKV_ERR_HIP;
+  if (lds > static_cast<size_t>(lds_max)) return PKV_ERR_UNSUPPORTED;
   const int64_t gx = (static_cast<int64_t>(max_q_len) + kRowsPerWG - 1) / kRowsPerWG;
   if (gx > 0x7fffffffLL || num_q_heads > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
   PrefillArgs a;
@@ -314,6 +391,11 @@ extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void*
   const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(num_q_heads),
                   static_cast<uint32_t>(num_seqs));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* fn = l->dtype == PKV_BF16 ? reinterpret_cast<const void*>(&prefill_kernel<PKV_BF16>)
+                                        : reinterpret_cast<const void*>(&prefill_kernel<PKV_F16>);
+  if (lds > 65536 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         static_cast<int>(lds)) != hipSuccess)
+    return PKV_ERR_HIP;
   if (l->dtype == PKV_BF16)
     hipLaunchKernelGGL(prefill_kernel<PKV_BF16>, grid, dim3(kWave * kWavesPF), lds, s, a);
   else
