@@ -163,6 +163,39 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
             "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def measure_swap(eng, seqs: int = 8, iters: int = 5):
+    """Swap to host on the workload's pool: the first ``seqs`` sequences'
+    blocks gathered into a staging array (pkv_gather_blocks, HBM-bound) and
+    copied to pinned host memory, timed separately with HIP events; the
+    sequences are then swapped back in.  Reported: staging GB/s (read + write
+    of the blocks) and device-to-host GB/s."""
+    import torch
+    import paged_kv_cache_128_amd as pkv
+    ids = np.concatenate([np.array(eng.manager.block_table(s), dtype=np.int32) for s in range(seqs)])
+    block_bytes = 2 * eng.num_kv_heads * eng.block_size * eng.head_dim * eng.pool.element_size()
+    staged = pkv.gather_blocks(ids, eng.key_cache, eng.value_cache)
+    host = torch.empty(staged.shape, dtype=staged.dtype, pin_memory=True)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(iters):
+        pkv.gather_blocks(ids, eng.key_cache, eng.value_cache, staging=staged)
+    ev[1].record()
+    for _ in range(iters):
+        host.copy_(staged, non_blocking=True)
+    ev[2].record()
+    torch.cuda.synchronize()
+    g_us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+    c_us = ev[1].elapsed_time(ev[2]) * 1e3 / iters
+    nbytes = len(ids) * block_bytes
+    log(f"swap: {len(ids)} blocks ({nbytes / 1e6:.1f} MB): gather {g_us:.1f} us, device-to-host {c_us:.1f} us")
+    return {"kernel": "block_stage_kernel<gather>", "blocks": int(len(ids)), "bytes": int(nbytes),
+            "gather_us": round(g_us, 2), "gather_gbps": round(2 * nbytes / (g_us * 1e-6) / 1e9, 1),
+            "gather_frac_hbm": round(2 * nbytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "device_to_host_us": round(c_us, 2),
+            "device_to_host_gbps": round(nbytes / (c_us * 1e-6) / 1e9, 1)}
+
+
 def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, seed: int = 2024):
     """Full-prompt prefill attention (paged_prefill_attention) with the
     workload's head shape: ``seqs`` prompts of ``prompt`` tokens admitted and
@@ -418,6 +451,7 @@ def main():
     cold = np.array(cold)
     del flush
     block_copy = measure_block_copy(eng)
+    swap = measure_swap(eng)
     fp8 = None
     if not args.no_fp8 and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
         fp8 = measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s)
@@ -482,6 +516,7 @@ def main():
         },
         "kernel_source_sha256_16": kernel_source_sha(),
         "copy_on_write": block_copy,
+        "swap_to_host": swap,
         "fp8_kv": fp8,
         "prefill": prefill,
     }

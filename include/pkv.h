@@ -190,6 +190,27 @@ int pkv_free_sequence(pkv_manager* mgr, int64_t seq_id);
  */
 int pkv_share_prefix(pkv_manager* mgr, int64_t donor_id, int64_t seq_id, int32_t num_tokens);
 
+/*
+ * Swap to host ([impl-detail] "异构内存支持" evict_to_cpu /
+ * prefetch_to_gpu).  pkv_swap_out releases every block of live `seq_id` to
+ * the free list (table order, then the sort of PKV_SORT_ON_RELEASE) and
+ * keeps its length; ids_out (host, [cap]) receives the released blocks in
+ * table order and *count_out their number, so the caller can copy them out
+ * (pkv_gather_blocks) before anything reuses them.  The sequence is then
+ * swapped: not live (appends give NOT_LIVE; prefill and share onto its id
+ * give ALREADY_PREFILLED), and pkv_free_sequence forgets it.  A sequence
+ * holding a block another table shares cannot be swapped out (INVALID).
+ * pkv_swap_in gives a swapped sequence ceil(len / bs) blocks from the front
+ * of the free list, all or nothing (OOM leaves it swapped), returns its new
+ * table in ids_out, and makes it live with the same length; the caller then
+ * copies the contents back (pkv_scatter_blocks).  Errors: INVALID (cap too
+ * small, shared blocks), NOT_LIVE, ALREADY_PREFILLED, OOM.
+ */
+int pkv_swap_out(pkv_manager* mgr, int64_t seq_id, int32_t* ids_out, int32_t cap, int32_t* count_out);
+int pkv_swap_in(pkv_manager* mgr, int64_t seq_id, int32_t* ids_out, int32_t cap, int32_t* count_out);
+/* 1 when `seq_id` is swapped out, 0 otherwise, or INVALID. */
+int pkv_is_swapped(const pkv_manager* mgr, int64_t seq_id);
+
 /* Reference count of physical block `block` (0 when free), or INVALID. */
 int32_t pkv_block_ref_count(const pkv_manager* mgr, int32_t block);
 
@@ -286,6 +307,20 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
  */
 int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
                     void* value_cache, const pkv_cache_layout* layout, void* stream);
+
+/*
+ * Swap staging ([impl-detail] "异构内存支持"): pkv_gather_blocks copies
+ * blocks ids[0 .. n-1] (host int32) of both pools into `staging` (device,
+ * 16-byte aligned, n * 2 * H_kv * bs * D elements: entry j is block ids[j]'s
+ * K half then V half, [n, 2, H_kv, bs, D]); pkv_scatter_blocks copies entry
+ * j back into block ids[j].  The caller moves the staging array to and from
+ * host memory (a plain device-host copy).  Ids outside [0, num_blocks) are
+ * skipped.  16-bit and fp32 layouts.  Errors: INVALID, UNSUPPORTED, HIP.
+ */
+int pkv_gather_blocks(const int32_t* ids, int32_t n, const void* key_cache, const void* value_cache,
+                      void* staging, const pkv_cache_layout* layout, void* stream);
+int pkv_scatter_blocks(const void* staging, const int32_t* ids, int32_t n, void* key_cache,
+                       void* value_cache, const pkv_cache_layout* layout, void* stream);
 
 /* -------------------------------------------------------- decode attention */
 /*

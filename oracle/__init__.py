@@ -26,7 +26,7 @@ pin say "parity unpinned" in their docstring.
 from .manager import (BlockManager, ManagerError, InvalidArgument, OutOfBlocks,
                       NotLive, AlreadyPrefilled, blocks_needed)
 from .slots import slot_of, split_slot, kv_head_of
-from .cache import new_pool, write_kv, gather_logical, copy_blocks
+from .cache import new_pool, write_kv, gather_logical, copy_blocks, gather_blocks, scatter_blocks
 from .attention import (widen, decode_attention, decode_attention_online,
                         contiguous_attention, prefill_attention)
 from .ledger import estimate_kv_cache_bytes, allocation_report, tail_waste
@@ -34,7 +34,7 @@ from .ledger import estimate_kv_cache_bytes, allocation_report, tail_waste
 __all__ = [
     "BlockManager", "ManagerError", "InvalidArgument", "OutOfBlocks", "NotLive",
     "AlreadyPrefilled", "blocks_needed", "slot_of", "split_slot", "kv_head_of",
-    "new_pool", "write_kv", "gather_logical", "copy_blocks", "widen", "decode_attention",
+    "new_pool", "write_kv", "gather_logical", "copy_blocks", "gather_blocks", "scatter_blocks", "widen", "decode_attention",
     "decode_attention_online", "contiguous_attention", "prefill_attention", "estimate_kv_cache_bytes",
     "allocation_report", "tail_waste",
 ]

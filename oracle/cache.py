@@ -61,6 +61,22 @@ def copy_blocks(pairs: Sequence[Tuple[int, int]], key_cache: np.ndarray,
         value_cache[dst] = value_cache[src]
 
 
+def gather_blocks(ids: Sequence[int], key_cache: np.ndarray, value_cache: np.ndarray) -> np.ndarray:
+    """Swap-out staging ([impl-detail] "异构内存支持": a block's k and v go to
+    host memory): blocks ``ids`` in order as one array [n, 2, H, bs, D]
+    (K half, then V half)."""
+    return np.stack([np.stack([key_cache[int(i)], value_cache[int(i)]]) for i in ids]) \
+        if len(ids) else np.empty((0, 2) + key_cache.shape[1:], key_cache.dtype)
+
+
+def scatter_blocks(staged: np.ndarray, ids: Sequence[int], key_cache: np.ndarray,
+                   value_cache: np.ndarray) -> None:
+    """Swap-in: staged block j back into block ids[j] of both pools."""
+    for j, i in enumerate(ids):
+        key_cache[int(i)] = staged[j, 0]
+        value_cache[int(i)] = staged[j, 1]
+
+
 def gather_logical(cache: np.ndarray, block_table: Sequence[int], seq_len: int) -> np.ndarray:
     """Logically contiguous [H_kv, seq_len, D] view of one sequence: blocks in
     TABLE order (never sorted by physical id), concatenated along the token

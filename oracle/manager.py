@@ -31,6 +31,13 @@ The pages' manager, written out as a plain Python object:
   block and puts the new block in the table ("Copy-on-Write机制").  The
   queued (source, destination) pairs are drained by ``take_copies``; the
   caller copies those blocks before it writes the step's rows.
+* Swap to host ([impl-detail] "异构内存支持" evict_to_cpu / prefetch_to_gpu):
+  ``swap_out`` gives a live sequence's blocks back to the free list (in
+  table order) and keeps its length, so the caller can copy those blocks to
+  host memory first; ``swap_in`` takes ceil(len / bs) blocks from the front
+  of the free list, all or nothing, for the caller to copy back into.  A
+  sequence holding a shared block cannot be swapped out (its blocks would
+  stay in other tables).
 * ``check_invariants`` tests the invariants of [MiniPaged-Qwen] §15 and
   [mini-vLLM BM] "正确性不变量", with I1 read for shared blocks as "each
   block's count equals the number of tables holding it".
@@ -104,6 +111,7 @@ class BlockManager:
         self.sort_on_release = bool(sort_on_release)
         self.seqs: Dict[int, _Seq] = {}
         self.ref: List[int] = [0] * self.num_blocks      # tables holding each block
+        self.swapped: Dict[int, int] = {}                # swapped-out sequence -> length
         self.copies: List[Tuple[int, int]] = []          # queued (source, destination)
 
     # -- queries -----------------------------------------------------------
@@ -159,7 +167,7 @@ class BlockManager:
         ([mini-vLLM BM] "Block Manager 和 ModelRunner 如何协作")."""
         if seq_id < 0 or num_tokens < 0:
             raise InvalidArgument("seq_id and num_tokens must be >= 0")
-        if seq_id in self.seqs:
+        if seq_id in self.seqs or seq_id in self.swapped:
             raise AlreadyPrefilled(f"sequence {seq_id} is already live")
         need = blocks_needed(num_tokens, self.block_size)
         if need > len(self.free):
@@ -182,7 +190,7 @@ class BlockManager:
         if seq_id < 0 or num_tokens < 0:
             raise InvalidArgument("seq_id and num_tokens must be >= 0")
         donor = self._live(donor_id)
-        if seq_id in self.seqs:
+        if seq_id in self.seqs or seq_id in self.swapped:
             raise AlreadyPrefilled(f"sequence {seq_id} is already live")
         if num_tokens > donor.length:
             raise InvalidArgument("shared prefix longer than the donor")
@@ -265,9 +273,53 @@ class BlockManager:
             raise OutOfBlocks()
         return [self.append_slot_for_decode(seq_id) for _ in range(num_tokens)]
 
+    def swap_out(self, seq_id: int) -> List[int]:
+        """Release the blocks of live ``seq_id`` (returned in table order, for
+        the caller to copy out first) and keep its length; the sequence is
+        then swapped, not live ([impl-detail] "异构内存支持" evict_to_cpu)."""
+        seq = self._live(seq_id)
+        if any(self.ref[pb] > 1 for pb in seq.table):
+            raise InvalidArgument("a sequence holding a shared block cannot be swapped out")
+        table = list(seq.table)
+        for pb in table:
+            self.ref[pb] = 0
+            self.free.append(pb)
+        if self.sort_on_release:
+            self.free.sort()
+        self.swapped[int(seq_id)] = seq.length
+        del self.seqs[int(seq_id)]
+        return table
+
+    def swap_in(self, seq_id: int) -> List[int]:
+        """Make swapped ``seq_id`` live again on ceil(len / bs) blocks from the
+        front of the free list, all or nothing; returns its new table (for the
+        caller to copy back into, [impl-detail] "异构内存支持" prefetch_to_gpu)."""
+        seq_id = int(seq_id)
+        if seq_id in self.seqs:
+            raise AlreadyPrefilled(f"sequence {seq_id} is live")
+        if seq_id not in self.swapped:
+            raise NotLive(f"sequence {seq_id} is not swapped out")
+        L = self.swapped[seq_id]
+        need = blocks_needed(L, self.block_size)
+        if need > len(self.free):
+            raise OutOfBlocks()
+        seq = _Seq()
+        seq.table = self.free[:need]
+        del self.free[:need]
+        for pb in seq.table:
+            self.ref[pb] = 1
+        seq.length = L
+        self.seqs[seq_id] = seq
+        del self.swapped[seq_id]
+        return list(seq.table)
+
     def free_sequence(self, seq_id: int) -> None:
         """Return every block of ``seq_id`` to the free list exactly once
-        ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block")."""
+        ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  A swapped-out
+        sequence holds no blocks and is just forgotten."""
+        if int(seq_id) in self.swapped:
+            del self.swapped[int(seq_id)]
+            return
         seq = self._live(seq_id)
         for pb in seq.table:
             self.ref[pb] -= 1

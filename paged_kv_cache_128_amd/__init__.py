@@ -91,6 +91,11 @@ SIGNATURES = {
     "pkv_free_sequence": (ctypes.c_int, [_P, _I64]),
     "pkv_share_prefix": (ctypes.c_int, [_P, _I64, _I64, _I32]),
     "pkv_append_tokens": (ctypes.c_int, [_P, _I64, _I32, _PI64]),
+    "pkv_swap_out": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
+    "pkv_swap_in": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
+    "pkv_is_swapped": (ctypes.c_int, [_P, _I64]),
+    "pkv_gather_blocks": (ctypes.c_int, [_PI32, _I32, _P, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "pkv_scatter_blocks": (ctypes.c_int, [_P, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
     "paged_prefill_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
                                                ctypes.POINTER(CacheLayout), _P, _I32, _I32, _I32, _F32, _P]),
     "pkv_block_ref_count": (_I32, [_P, _I32]),
@@ -286,6 +291,26 @@ class KVBlockManager:
         _check(self._lib.pkv_append_tokens(self._h, int(seq_id), int(num_tokens),
                                            _ptr(slots, ctypes.c_int64)), "append_tokens")
         return slots
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """Release a live sequence's blocks, keeping its length; returns the
+        released ids in table order (see pkv_swap_out)."""
+        ids = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_swap_out(self._h, int(seq_id), _ptr(ids, ctypes.c_int32), self.num_blocks,
+                                      ctypes.byref(n)), "swap_out")
+        return ids[:n.value].copy()
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """Fresh blocks for a swapped sequence; returns its new table."""
+        ids = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(self._lib.pkv_swap_in(self._h, int(seq_id), _ptr(ids, ctypes.c_int32), self.num_blocks,
+                                     ctypes.byref(n)), "swap_in")
+        return ids[:n.value].copy()
+
+    def is_swapped(self, seq_id: int) -> bool:
+        return bool(_check(self._lib.pkv_is_swapped(self._h, int(seq_id)), "is_swapped"))
 
     def share_prefix(self, donor_id: int, seq_id: int, num_tokens: int) -> None:
         """New sequence on the donor's first ceil(num_tokens / bs) blocks
@@ -526,6 +551,38 @@ def paged_kv_write(key, value, slot_mapping, key_cache, value_cache, stream=None
     _check(st, "paged_kv_write")
 
 
+def gather_blocks(ids, key_cache, value_cache, staging=None, stream=None):
+    """Blocks ids (host int32) of both pools into a staging tensor
+    [n, 2, H_kv, bs, D] (see pkv_gather_blocks); returns it."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    shape = (len(ids), 2, lay.num_kv_heads, lay.block_size, lay.head_dim)
+    if staging is None:
+        staging = torch.empty(shape, dtype=key_cache.dtype, device=key_cache.device)
+    if tuple(staging.shape) != shape or not staging.is_contiguous() or staging.dtype != key_cache.dtype:
+        raise ValueError("staging must be contiguous [n, 2, H_kv, bs, D] in the cache dtype")
+    st = _lib_handle().pkv_gather_blocks(_ptr(ids, ctypes.c_int32), len(ids), key_cache.data_ptr(),
+                                         value_cache.data_ptr(), staging.data_ptr(), ctypes.byref(lay),
+                                         _stream_handle(stream))
+    _check(st, "gather_blocks")
+    return staging
+
+
+def scatter_blocks(staging, ids, key_cache, value_cache, stream=None) -> None:
+    """Staging entry j back into block ids[j] of both pools (see pkv_scatter_blocks)."""
+    lay = cache_layout(key_cache, value_cache)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    shape = (len(ids), 2, lay.num_kv_heads, lay.block_size, lay.head_dim)
+    if tuple(staging.shape) != shape or not staging.is_contiguous() or staging.dtype != key_cache.dtype \
+            or staging.device != key_cache.device:
+        raise ValueError("staging must be a contiguous device tensor [n, 2, H_kv, bs, D] in the cache dtype")
+    st = _lib_handle().pkv_scatter_blocks(staging.data_ptr(), _ptr(ids, ctypes.c_int32), len(ids),
+                                          key_cache.data_ptr(), value_cache.data_ptr(), ctypes.byref(lay),
+                                          _stream_handle(stream))
+    _check(st, "scatter_blocks")
+
+
 def copy_blocks(src, dst, key_cache, value_cache, stream=None) -> None:
     """Copy whole blocks src[i] -> dst[i] (host int32 arrays) in both pools
     (see pkv_copy_blocks)."""
@@ -699,7 +756,7 @@ __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
-    "copy_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
+    "copy_blocks", "gather_blocks", "scatter_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
     "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",

@@ -17,6 +17,11 @@
 // token lands in a block other tables also hold takes a free block for the
 // sequence and queues a (source, destination) copy that the caller runs on
 // the device before the step's write.
+//
+// Swap to host ([impl-detail] "异构内存支持"): swap-out releases a sequence's
+// blocks and keeps its length; swap-in gives it fresh blocks, all or nothing.
+// The caller copies the block contents out before the blocks are reused and
+// back after swap-in.
 #include <algorithm>
 #include <new>
 #include <unordered_map>
@@ -45,6 +50,7 @@ struct pkv_manager {
   std::unordered_map<int64_t, Sequence> seqs;
   std::vector<int32_t> ref;                            // tables holding each block
   std::vector<std::pair<int32_t, int32_t>> copies;     // queued (source, destination)
+  std::unordered_map<int64_t, int32_t> swapped;        // swapped-out sequence -> length
 
   int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
   int32_t pop_front() {
@@ -122,7 +128,7 @@ int32_t pkv_num_live_sequences(const pkv_manager* m) {
 int pkv_allocate_for_prefill(pkv_manager* m, int64_t seq_id, int32_t num_tokens,
                              int64_t* slots_out) {
   if (!m || seq_id < 0 || num_tokens < 0) return PKV_ERR_INVALID;
-  if (m->seqs.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
+  if (m->seqs.count(seq_id) || m->swapped.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
   const int64_t need = m->blocks_for(num_tokens);
   if (need > m->count) return PKV_ERR_OOM;
   Sequence s;
@@ -147,7 +153,7 @@ int pkv_share_prefix(pkv_manager* m, int64_t donor_id, int64_t seq_id, int32_t n
   if (!m || seq_id < 0 || num_tokens < 0) return PKV_ERR_INVALID;
   auto d = m->seqs.find(donor_id);
   if (d == m->seqs.end()) return PKV_ERR_NOT_LIVE;
-  if (m->seqs.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
+  if (m->seqs.count(seq_id) || m->swapped.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
   if (num_tokens > d->second.length) return PKV_ERR_INVALID;
   const int64_t n = m->blocks_for(num_tokens);
   Sequence s;
@@ -296,8 +302,65 @@ int pkv_append_tokens(pkv_manager* m, int64_t seq_id, int32_t num_tokens, int64_
   return PKV_OK;
 }
 
+int pkv_swap_out(pkv_manager* m, int64_t seq_id, int32_t* ids_out, int32_t cap, int32_t* count_out) {
+  if (!m || cap < 0 || !count_out || (cap > 0 && !ids_out)) return PKV_ERR_INVALID;
+  auto it = m->seqs.find(seq_id);
+  if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
+  const std::vector<int32_t>& t = it->second.table;
+  if (static_cast<int64_t>(t.size()) > cap) return PKV_ERR_INVALID;
+  for (int32_t pb : t)
+    if (m->ref[pb] > 1) return PKV_ERR_INVALID;    // a shared block stays in other tables
+  try {
+    m->swapped.emplace(seq_id, it->second.length);
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (size_t i = 0; i < t.size(); ++i) {
+    ids_out[i] = t[i];
+    m->ref[t[i]] = 0;
+    m->push_back(t[i]);
+  }
+  *count_out = static_cast<int32_t>(t.size());
+  if (m->sort_on_release) m->sort_free();
+  m->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_swap_in(pkv_manager* m, int64_t seq_id, int32_t* ids_out, int32_t cap, int32_t* count_out) {
+  if (!m || cap < 0 || !count_out || (cap > 0 && !ids_out)) return PKV_ERR_INVALID;
+  if (m->seqs.count(seq_id)) return PKV_ERR_ALREADY_PREFILLED;
+  auto it = m->swapped.find(seq_id);
+  if (it == m->swapped.end()) return PKV_ERR_NOT_LIVE;
+  const int64_t need = m->blocks_for(it->second);
+  if (need > cap) return PKV_ERR_INVALID;
+  if (need > m->count) return PKV_ERR_OOM;
+  Sequence s;
+  try {
+    s.table.reserve(need);
+    for (int64_t i = 0; i < need; ++i) s.table.push_back(m->free_at(i));
+    s.length = it->second;
+    m->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  for (int64_t i = 0; i < need; ++i) {
+    const int32_t pb = m->pop_front();
+    m->ref[pb] = 1;
+    ids_out[i] = pb;
+  }
+  *count_out = static_cast<int32_t>(need);
+  m->swapped.erase(it);
+  return PKV_OK;
+}
+
+int pkv_is_swapped(const pkv_manager* m, int64_t seq_id) {
+  if (!m) return PKV_ERR_INVALID;
+  return m->swapped.count(seq_id) ? 1 : 0;
+}
+
 int pkv_free_sequence(pkv_manager* m, int64_t seq_id) {
   if (!m) return PKV_ERR_INVALID;
+  if (m->swapped.erase(seq_id)) return PKV_OK;     // a swapped-out sequence holds no blocks
   auto it = m->seqs.find(seq_id);
   if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
   for (int32_t pb : it->second.table)

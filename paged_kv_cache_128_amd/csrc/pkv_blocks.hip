@@ -38,7 +38,85 @@ block_copy_kernel(CopyMeta meta, int32_t num_blocks, int32_t heads, int64_t bloc
   for (int32_t i = threadIdx.x; i < head_chunks; i += kCopyThreads) to[i] = from[i];
 }
 
+// Swap staging ([impl-detail] "异构内存支持"): block ids[j] of the pool <->
+// entry j of a contiguous staging array [n, 2, H_kv, bs, D] (K half, then V
+// half), one workgroup per (entry, K or V, head) as in the copy.
+template <bool TO_STAGING>
+__global__ void __launch_bounds__(kCopyThreads)
+block_stage_kernel(CopyMeta meta, int32_t num_blocks, int32_t heads, int64_t block_stride16,
+                   int64_t head_stride16, int32_t head_chunks, uint4* __restrict__ key_cache,
+                   uint4* __restrict__ value_cache, uint4* __restrict__ staging) {
+  const int32_t item = blockIdx.x;
+  const int32_t j = item / (2 * heads);
+  const int32_t rem = item - j * 2 * heads;
+  const int32_t half = rem / heads;
+  const int32_t h = rem - half * heads;
+  const int32_t id = meta.src[j];
+  if (id < 0 || id >= num_blocks) return;
+  uint4* pool = (half == 0 ? key_cache : value_cache) + id * block_stride16 + h * head_stride16;
+  uint4* st = staging + ((static_cast<int64_t>(meta.dst[j]) * 2 + half) * heads + h) * head_chunks;
+  for (int32_t i = threadIdx.x; i < head_chunks; i += kCopyThreads) {
+    if (TO_STAGING) st[i] = pool[i];
+    else pool[i] = st[i];
+  }
+}
+
+// Shared checks of the copy and staging entry points.
+int block_layout_ok(const pkv_cache_layout* l, const void* key_cache, const void* value_cache) {
+  if (pkv::check_layout(l) != PKV_OK) return PKV_ERR_INVALID;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;   // codes without their scales
+  if (!key_cache || !value_cache) return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const int64_t head_bytes = static_cast<int64_t>(l->block_size) * l->head_dim * eb;
+  if (head_bytes % 16 != 0 || (l->head_stride * eb) % 16 != 0 || (l->block_stride * eb) % 16 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) % 16) != 0)
+    return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+template <bool TO_STAGING>
+int stage_blocks(const int32_t* ids, int32_t n, void* key_cache, void* value_cache, void* staging,
+                 const pkv_cache_layout* l, void* stream) {
+  if (n < 0) return PKV_ERR_INVALID;
+  const int st = block_layout_ok(l, key_cache, value_cache);
+  if (st != PKV_OK) return st;
+  if (n == 0) return PKV_OK;
+  if (!ids || !staging || reinterpret_cast<uintptr_t>(staging) % 16 != 0) return PKV_ERR_INVALID;
+  const int eb = pkv::elem_bytes(l->dtype);
+  const int64_t head_bytes = static_cast<int64_t>(l->block_size) * l->head_dim * eb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t p0 = 0; p0 < n; p0 += kCopyPairs) {
+    const int32_t m = n - p0 < kCopyPairs ? n - p0 : kCopyPairs;
+    CopyMeta meta;
+    for (int32_t i = 0; i < m; ++i) {
+      meta.src[i] = ids[p0 + i];
+      meta.dst[i] = p0 + i;                    // staging entry
+    }
+    const int64_t grid = static_cast<int64_t>(m) * 2 * l->num_kv_heads;
+    hipLaunchKernelGGL(block_stage_kernel<TO_STAGING>, dim3(static_cast<uint32_t>(grid)), dim3(kCopyThreads), 0,
+                       s, meta, l->num_blocks, l->num_kv_heads, l->block_stride * eb / 16,
+                       l->head_stride * eb / 16, static_cast<int32_t>(head_bytes / 16),
+                       static_cast<uint4*>(key_cache), static_cast<uint4*>(value_cache),
+                       static_cast<uint4*>(staging));
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
 }  // namespace
+
+extern "C" int pkv_gather_blocks(const int32_t* ids, int32_t n, const void* key_cache,
+                                 const void* value_cache, void* staging, const pkv_cache_layout* l,
+                                 void* stream) {
+  return stage_blocks<true>(ids, n, const_cast<void*>(key_cache), const_cast<void*>(value_cache), staging,
+                            l, stream);
+}
+
+extern "C" int pkv_scatter_blocks(const void* staging, const int32_t* ids, int32_t n, void* key_cache,
+                                  void* value_cache, const pkv_cache_layout* l, void* stream) {
+  return stage_blocks<false>(ids, n, key_cache, value_cache, const_cast<void*>(staging), l, stream);
+}
 
 extern "C" int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
                                void* value_cache, const pkv_cache_layout* l, void* stream) {

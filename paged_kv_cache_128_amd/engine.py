@@ -33,6 +33,7 @@ import numpy as np
 import torch
 
 from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_write, decode_write_fp8,
+               gather_blocks, scatter_blocks,
                new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
                paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, workspace_size)
 
@@ -152,6 +153,33 @@ class PagedKVEngine:
             raise NotImplementedError("copy-on-write of 8-bit blocks (codes and scales) is not built")
         self.manager.share_prefix(donor_id, seq_id, num_tokens)
         self._sharing = True
+        self._publish_row(seq_id, row)
+
+    def swap_out(self, seq_id: int) -> torch.Tensor:
+        """Move a live sequence's blocks to pinned host memory and release
+        them ([impl-detail] "异构内存支持" evict_to_cpu): gather on the device,
+        then one device-to-host copy on the current stream (the host tensor
+        holds the data once the stream has passed it).  Returns the host
+        copy, which swap_in takes back.  The sequence's row is left to the
+        caller."""
+        if self.fp8:
+            raise NotImplementedError("swap of 8-bit blocks (codes and scales) is not built")
+        ids = self.manager.swap_out(seq_id)
+        staged = gather_blocks(ids, self.key_cache, self.value_cache)
+        host = torch.empty(staged.shape, dtype=staged.dtype, pin_memory=True)
+        host.copy_(staged, non_blocking=True)
+        for r, s in list(self.row_seq.items()):
+            if s == seq_id:
+                del self.row_seq[r]
+        return host
+
+    def swap_in(self, seq_id: int, row: int, host: torch.Tensor) -> None:
+        """Bring a swapped sequence back into ``row`` on fresh blocks
+        ([impl-detail] "异构内存支持" prefetch_to_gpu): one host-to-device
+        copy, a scatter, and the table row published."""
+        ids = self.manager.swap_in(seq_id)
+        staged = host.to(self.device, non_blocking=True)
+        scatter_blocks(staged, ids, self.key_cache, self.value_cache)
         self._publish_row(seq_id, row)
 
     def _publish_row(self, seq_id: int, row: int):
