@@ -38,7 +38,10 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc", "pkv_kernels.hip")
+CSRC = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc")
+# the decode attention kernels are built from this file and the headers it includes
+KERNEL_SOURCES = [os.path.join(CSRC, "pkv_kernels.hip"), os.path.join(CSRC, "pkv_internal.h"),
+                  os.path.join(CSRC, "pkv_fp8_codec.h"), os.path.join(ROOT, "include", "pkv.h")]
 
 
 def log(msg):
@@ -46,8 +49,11 @@ def log(msg):
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic(kernel_name: str, workload: str):
@@ -279,14 +285,14 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
 
     for s_ in range(args.warmup):
         k, v, q = ring[s_ % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out)
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=not args.separate_write)
     timed = [i for i in range(args.steps) if i % max(1, args.event_every) == 0]
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         k, v, q = ring[(args.warmup + i) % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i))
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i), fused=not args.separate_write)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])

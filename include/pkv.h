@@ -564,6 +564,25 @@ int paged_decode_attention_fp8(void* out, int32_t out_dtype, const void* q, int3
                                void* stream);
 
 /*
+ * pkv_decode_step over 8-bit blocks: key/value (device, [num_seqs, H_kv, D],
+ * q_dtype) are quantised as paged_kv_write_fp8 quantises them, then the
+ * 8-bit attention runs, with the same results, bit for bit, as
+ * pkv_decode_write_fp8 followed by paged_decode_attention_fp8.  Under the
+ * conditions of pkv_decode_step the write runs inside the attention launch:
+ * the one wave per KV head that reads a sequence's last tile quantises the
+ * new rows (the same encoding) and stores codes and scale bytes.  phases as
+ * for paged_decode_attention_fp8.  Errors: INVALID, UNSUPPORTED, WORKSPACE,
+ * HIP.
+ */
+int pkv_decode_step_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype, const void* key,
+                        const void* value, const int64_t* slots, const int32_t* lens, int32_t num_seqs,
+                        void* key_cache, void* value_cache, uint8_t* key_scales, uint8_t* value_scales,
+                        const pkv_cache_layout* layout, int32_t* block_tables,
+                        int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                        int32_t max_context_len, float scale, int32_t phases, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
  * Apply the table growth of one batched append to a device-resident block
  * table: for every i with new_block[i] >= 0,
  *     block_tables[rows[i] * block_table_stride + (lens[i] - 1) / bs] = new_block[i]

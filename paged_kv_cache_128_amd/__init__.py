@@ -105,6 +105,9 @@ SIGNATURES = {
                                           ctypes.POINTER(CacheLayout), _P]),
     "pkv_decode_write_fp8": (ctypes.c_int, [_P, _P, _I32, _PI64, _PI32, _I32, _P, _P, _P, _P,
                                             ctypes.POINTER(CacheLayout), _P, _I32, _I32, _P, _P]),
+    "pkv_decode_step_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _PI64, _PI32, _I32, _P, _P, _P, _P,
+                                           ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32, _F32, _I32,
+                                           _P, _SZ, _P]),
     "paged_decode_attention_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _P, _P, _P, _I32, _P,
                                                   _I32, _I32, _I32, _F32, ctypes.POINTER(CacheLayout),
                                                   _I32, _P, _SZ, _P]),
@@ -444,6 +447,39 @@ def decode_write_fp8(key, value, slots: np.ndarray, lens: np.ndarray, key_cache,
     _check(st, "pkv_decode_write_fp8")
 
 
+def decode_step_fp8(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
+                    key_scales, value_scales, block_tables, lens_out, scale: float, max_context_len: int,
+                    out=None, workspace=None, stream=None, phase: str = "both"):
+    """pkv_decode_step over 8-bit blocks: key/value [n, H_kv, D] and q
+    [n, H_q, D] in one 16-bit type; slots int64 / lens int32 host arrays."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    n, hq, d = q.shape
+    if key.shape != (n, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape \
+            or key.dtype != q.dtype or value.dtype != q.dtype:
+        raise ValueError("key/value must be [n, H_kv, head_dim] in q's dtype")
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if out is None:
+        out = torch.empty((n, hq, d), dtype=torch.float32, device=q.device)
+    need = workspace_size(n, hq, lay.num_kv_heads, d, max_context_len, 0)
+    if need > 0 and workspace is None:
+        if phase != "both":
+            raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib_handle().pkv_decode_step_fp8(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), key.data_ptr(),
+        value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
+        value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay),
+        block_tables.data_ptr(), block_tables.stride(0), lens_out.data_ptr(), hq, int(max_context_len),
+        float(scale), {"partial": 1, "merge": 2, "both": 3}[phase],
+        None if workspace is None else workspace.data_ptr(),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(st, "pkv_decode_step_fp8")
+    return out
+
+
 def paged_decode_attention_fp8(q, key_cache, value_cache, key_scales, value_scales, block_tables,
                                context_lens, scale: float, out=None, out_dtype=None,
                                max_context_len: Optional[int] = None, workspace=None, stream=None,
@@ -757,7 +793,7 @@ __all__ = [
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
     "copy_blocks", "gather_blocks", "scatter_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
-    "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention",
+    "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention", "decode_step_fp8",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

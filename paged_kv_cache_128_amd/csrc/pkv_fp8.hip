@@ -20,45 +20,12 @@
 
 #include <cstdint>
 
+#include "pkv_fp8_codec.h"
 #include "pkv_internal.h"
 
 namespace {
 
 constexpr int kThreads = 256;
-
-// E4M3 byte of a finite y with |y| <= 448, ties to an even mantissa.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t c;
-  if (a < 0x1p-6f) {
-    c = static_cast<uint32_t>(rintf(a * 512.0f));                 // subnormal: m * 2^-9, m = 0..8
-  } else {
-    const int E = static_cast<int>((__float_as_uint(a) >> 23) & 0xffu) - 127;
-    const float r = rintf(__builtin_amdgcn_ldexpf(a, 3 - E));      // 8 .. 16
-    c = static_cast<uint32_t>(((E + 7) << 3) + static_cast<int>(r) - 8);
-  }
-  return c == 0 ? 0u : (sign | c);
-}
-
-// e of the row scale 2^e for a row whose largest magnitude is amax (>= 0).
-__device__ __forceinline__ int row_exponent(float amax) {
-  const uint32_t ab = __float_as_uint(amax);
-  if (ab == 0) return 0;
-  int E;
-  uint32_t man;
-  const uint32_t ef = ab >> 23;
-  if (ef == 0) {                                  // float32 subnormal
-    const int lz = __clz(ab);
-    E = (31 - lz) - 149;
-    man = (ab << (lz - 8)) & 0x7fffffu;
-  } else {
-    E = static_cast<int>(ef) - 127;
-    man = ab & 0x7fffffu;
-  }
-  const int e = E - 8 + (man > 0x600000u ? 1 : 0);  // 448 = 1.75 * 2^8
-  return e < -126 ? -126 : (e > 127 ? 127 : e);
-}
 
 // Eight source values of one row, widened to float32.
 __device__ __forceinline__ void load8(const void* src, int dtype, int64_t elem, float (&x)[8]) {
@@ -93,12 +60,12 @@ __device__ __forceinline__ void quantize_store(const float (&x)[8], int lpr, int
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
   for (int o = lpr / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  const int e = row_exponent(amax);
+  const int e = pkv::row_exponent(amax);
   uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    w0 |= e4m3_code(__builtin_amdgcn_ldexpf(x[i], -e)) << (8 * i);
-    w1 |= e4m3_code(__builtin_amdgcn_ldexpf(x[4 + i], -e)) << (8 * i);
+    w0 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(x[i], -e)) << (8 * i);
+    w1 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(x[4 + i], -e)) << (8 * i);
   }
   *reinterpret_cast<uint2*>(code_row + 8 * sub) = make_uint2(w0, w1);
   if (sub == 0) *scale = static_cast<uint8_t>(e + 127);

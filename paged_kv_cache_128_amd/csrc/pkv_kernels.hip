@@ -38,6 +38,7 @@
 
 #include <utility>
 
+#include "pkv_fp8_codec.h"
 #include "pkv_internal.h"
 
 namespace {
@@ -801,6 +802,8 @@ struct StreamArgs {
   const uint8_t* vs;
   int64_t sblock_stride;
   int64_t shead_stride;
+  uint8_t* ks_w;     // decode-step form of the 8-bit path: where the new rows' scale bytes go
+  uint8_t* vs_w;
 };
 
 constexpr int kStreamMaxHeads = 8;
@@ -1196,7 +1199,6 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   using F = Frag<DT, D>;
   using VT = std::conditional_t<KV8, VTile8, VTile<DT, D>>;
   static_assert(F::kRowK, "stream kernel is for 16-bit queries with D = 128");
-  static_assert(!(FUSED && KV8), "the decode-step form writes 16-bit rows");
   // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
   //              [tbl: cap]
   extern __shared__ uint4 sh_stream[];
@@ -1340,7 +1342,65 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     // At the head of the chunk holding a new token: its K row into the
     // staged tile, its V row into the P.V registers, both rows into the pool.
     auto place_new = [&](VT (&v)[CH], int b) {
-      if constexpr (FUSED) {
+      if constexpr (FUSED && KV8) {
+        // the new rows (the query's 16-bit type) quantised here exactly as
+        // the 8-bit cache writes do it: each 16-lane group holds the whole
+        // row, lane c16 elements 8 c16 .. 8 c16 + 7
+        float xk[8], xv[8];
+        const uint32_t wk[4] = {nk.x, nk.y, nk.z, nk.w}, wv[4] = {nvr.x, nvr.y, nvr.z, nvr.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unpack2<DT>(wk[i], xk[2 * i], xk[2 * i + 1]);
+          unpack2<DT>(wv[i], xv[2 * i], xv[2 * i + 1]);
+        }
+        float ak = 0.f, av = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ak = fmaxf(ak, fabsf(xk[i]));
+          av = fmaxf(av, fabsf(xv[i]));
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          ak = fmaxf(ak, __shfl_xor(ak, o));
+          av = fmaxf(av, __shfl_xor(av, o));
+        }
+        const int ek = pkv::row_exponent(ak), evx = pkv::row_exponent(av);
+        uint32_t k0 = 0, k1 = 0, v0 = 0, v1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k0 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(xk[i], -ek)) << (8 * i);
+          k1 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(xk[4 + i], -ek)) << (8 * i);
+          v0 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(xv[i], -evx)) << (8 * i);
+          v1 |= pkv::e4m3_code(__builtin_amdgcn_ldexpf(xv[4 + i], -evx)) << (8 * i);
+        }
+        // K codes into the staged tile (chunk c of row rn at slot c ^ (rn % 8)),
+        // V codes and both scale bytes into the P.V registers
+        if (g4 == 0)
+          reinterpret_cast<uint2*>(sk + jn * KT + rn * 8 + ((c16 >> 1) ^ (rn & 7)))[c16 & 1] = make_uint2(k0, k1);
+        const int sh = 8 * (rn & 3);
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (j == jn && r == (rn & 3) && g4 == (rn >> 2)) {
+              v[j].w[r][0] = v0;
+              v[j].w[r][1] = v1;
+              v[j].ks = (v[j].ks & ~(0xffu << sh)) | (static_cast<uint32_t>(ek + 127) << sh);
+              v[j].vs = (v[j].vs & ~(0xffu << sh)) | (static_cast<uint32_t>(evx + 127) << sh);
+            }
+        if (g4 == 0) {
+          const int64_t slot = meta->slots[b];
+          const int64_t pb = slot / bs, off = slot - pb * bs;
+          const int64_t dst = pb * a.block_stride + head_off + off * D + c16 * 8;
+          *reinterpret_cast<uint2*>(static_cast<char*>(a.kc_w) + dst) = make_uint2(k0, k1);
+          *reinterpret_cast<uint2*>(static_cast<char*>(a.vc_w) + dst) = make_uint2(v0, v1);
+          if (c16 == 0) {
+            const int64_t so = pb * a.sblock_stride + static_cast<int64_t>(kvh) * a.shead_stride + off;
+            a.ks_w[so] = static_cast<uint8_t>(ek + 127);
+            a.vs_w[so] = static_cast<uint8_t>(evx + 127);
+          }
+        }
+      } else if constexpr (FUSED) {
         if (g4 == 0) sk[jn * 256 + rn * 16 + (c16 ^ rn)] = make_uint4(nk.x, nk.y, nk.z, nk.w);
 #pragma unroll
         for (int j = 0; j < CH; ++j)
@@ -1475,6 +1535,14 @@ template <int DT, int GP, bool PAIRED>
 __global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
 attn_stream8_kernel(StreamArgs a) {
   stream_body<DT, GP, PAIRED, false, true>(a, nullptr);
+}
+
+// The 8-bit decode step in one launch: the new rows (the query's type) are
+// quantised and written by the wave that reads their tile.
+template <int DT, int GP, bool PAIRED>
+__global__ void __launch_bounds__(kWave * kStreamMaxWaves, 2)
+attn_stream8_step_kernel(StreamArgs a, StepMeta meta) {
+  stream_body<DT, GP, PAIRED, true, true>(a, &meta);
 }
 
 // The decode step in one launch: the write of the step's new rows (taken
@@ -1746,9 +1814,15 @@ hipError_t launch_stream_p(const StreamArgs& a, const StreamPlan& pl, const Step
                            hipStream_t s) {
   const dim3 grid(static_cast<uint32_t>(pl.wgs)), block(kWave * pl.waves);
   if constexpr (KV8) {
-    const hipError_t e = raise_lds(&attn_stream8_kernel<DT, GP, PAIRED>, pl.dyn_lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_stream8_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a);
+    if (meta) {
+      const hipError_t e = raise_lds(&attn_stream8_step_kernel<DT, GP, PAIRED>, pl.dyn_lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_stream8_step_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a, *meta);
+    } else {
+      const hipError_t e = raise_lds(&attn_stream8_kernel<DT, GP, PAIRED>, pl.dyn_lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((attn_stream8_kernel<DT, GP, PAIRED>), grid, block, pl.dyn_lds, s, a);
+    }
     return hipGetLastError();
   }
   if (meta) {
@@ -1774,14 +1848,17 @@ template <int DT, bool KV8 = false>
 hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, const StepMeta* meta,
                             hipStream_t s) {
   // the 8-bit path's P.V covers 16 heads on the matrix cores whatever G is
-  if constexpr (KV8) return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
-  switch (gp) {
-    case 1: return launch_stream_t<DT, 1, KV8>(a, pl, meta, s);
-    case 2: return launch_stream_t<DT, 2, KV8>(a, pl, meta, s);
-    case 4: return launch_stream_t<DT, 4, KV8>(a, pl, meta, s);
-    case 6: return launch_stream_t<DT, 6, KV8>(a, pl, meta, s);
-    case 7: return launch_stream_t<DT, 7, KV8>(a, pl, meta, s);
-    default: return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
+  if constexpr (KV8) {
+    return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
+  } else {
+    switch (gp) {
+      case 1: return launch_stream_t<DT, 1, KV8>(a, pl, meta, s);
+      case 2: return launch_stream_t<DT, 2, KV8>(a, pl, meta, s);
+      case 4: return launch_stream_t<DT, 4, KV8>(a, pl, meta, s);
+      case 6: return launch_stream_t<DT, 6, KV8>(a, pl, meta, s);
+      case 7: return launch_stream_t<DT, 7, KV8>(a, pl, meta, s);
+      default: return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
+    }
   }
 }
 
@@ -1949,6 +2026,8 @@ struct StepArgs {
   int32_t* block_tables;
   int32_t table_rows;
   int32_t* lens_out;
+  uint8_t* key_scales = nullptr;     // 8-bit path: where the new rows' scale bytes go
+  uint8_t* value_scales = nullptr;
 };
 
 // Validates the arguments, then launches the attention kernel (phase 1)
@@ -1970,7 +2049,7 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
   const int qt = f8 ? f8->q_dtype : l->dtype;
   if (f8 && ((qt != PKV_BF16 && qt != PKV_F16) || !f8->key_scales || !f8->value_scales))
     return PKV_ERR_INVALID;
-  if (f8 && (partition_tokens != 0 || step)) return PKV_ERR_UNSUPPORTED;
+  if (f8 && partition_tokens != 0) return PKV_ERR_UNSUPPORTED;
   if (num_q_heads % l->num_kv_heads != 0) return PKV_ERR_INVALID;
   if (out_dtype != PKV_F32 && out_dtype != qt) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
@@ -2039,14 +2118,16 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.lens_out = step ? step->lens_out : nullptr;
       sa.ks = f8 ? f8->key_scales : nullptr;
       sa.vs = f8 ? f8->value_scales : nullptr;
+      sa.ks_w = step ? step->key_scales : nullptr;
+      sa.vs_w = step ? step->value_scales : nullptr;
       sa.sblock_stride = l->block_stride / l->head_dim;
       sa.shead_stride = l->head_stride / l->head_dim;
       if (phases & kPhasePartial) {
         const int gp = padded_group(group);
         const StepMeta* meta = step ? step->meta : nullptr;
         hipError_t e;
-        if (f8) e = (qt == PKV_BF16) ? launch_stream_dt<PKV_BF16, true>(sa, gp, pl, nullptr, s)
-                                     : launch_stream_dt<PKV_F16, true>(sa, gp, pl, nullptr, s);
+        if (f8) e = (qt == PKV_BF16) ? launch_stream_dt<PKV_BF16, true>(sa, gp, pl, meta, s)
+                                     : launch_stream_dt<PKV_F16, true>(sa, gp, pl, meta, s);
         else e = (l->dtype == PKV_BF16) ? launch_stream_dt<PKV_BF16>(sa, gp, pl, meta, s)
                                         : launch_stream_dt<PKV_F16>(sa, gp, pl, meta, s);
         if (e != hipSuccess) return PKV_ERR_HIP;
@@ -2172,16 +2253,24 @@ int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
 // given and every slot and length is in range; otherwise pkv_decode_write
 // then paged_decode_attention.
 namespace {
+// 8-bit decode step: the scale pools (written and read) and the query's type.
+struct Fp8Step {
+  uint8_t* key_scales;
+  uint8_t* value_scales;
+  int32_t q_dtype;
+};
+
 int decode_step_impl(int phases, void* out, int32_t out_dtype, const void* q, const void* key,
                      const void* value, const int64_t* slots, const int32_t* lens, int32_t num_seqs,
                      void* key_cache, void* value_cache, const pkv_cache_layout* l,
                      int32_t* block_tables, int32_t block_table_stride, int32_t* lens_out,
                      int32_t num_q_heads, int32_t max_context_len, float scale, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     size_t workspace_bytes, void* stream, const Fp8Step* f8s = nullptr) {
   if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 ||
       block_table_stride <= 0)
     return PKV_ERR_INVALID;
-  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if ((l->dtype == PKV_FP8_E4M3) != (f8s != nullptr)) return PKV_ERR_UNSUPPORTED;
+  if (f8s && (!f8s->key_scales || !f8s->value_scales)) return PKV_ERR_INVALID;
   if (num_seqs == 0) return PKV_OK;
   if (!key || !value || !slots || !lens || !lens_out || !block_tables) return PKV_ERR_INVALID;
   const int64_t capacity = static_cast<int64_t>(l->num_blocks) * l->block_size;
@@ -2192,25 +2281,33 @@ int decode_step_impl(int phases, void* out, int32_t out_dtype, const void* q, co
   for (int32_t i = 0; fused && i < num_seqs; ++i)
     fused = slots[i] >= 0 && slots[i] < capacity && lens[i] >= 1 && lens[i] <= max_context_len &&
             (lens[i] - 1) / l->block_size < block_table_stride;
+  const Fp8Args f8a = f8s ? Fp8Args{f8s->key_scales, f8s->value_scales, f8s->q_dtype} : Fp8Args{};
   if (!fused) {
     if (phases & kPhasePartial) {
-      const int r = pkv_decode_write(key, value, slots, lens, num_seqs, key_cache, value_cache, l,
-                                     block_tables, num_seqs, block_table_stride, lens_out, stream);
+      const int r = f8s ? pkv_decode_write_fp8(key, value, f8s->q_dtype, slots, lens, num_seqs, key_cache,
+                                               value_cache, f8s->key_scales, f8s->value_scales, l,
+                                               block_tables, num_seqs, block_table_stride, lens_out, stream)
+                        : pkv_decode_write(key, value, slots, lens, num_seqs, key_cache, value_cache, l,
+                                           block_tables, num_seqs, block_table_stride, lens_out, stream);
       if (r != PKV_OK) return r;
     }
     return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
                           block_table_stride, lens_out, num_seqs, num_q_heads, max_context_len,
-                          scale, l, 0, workspace, workspace_bytes, stream);
+                          scale, l, 0, workspace, workspace_bytes, stream, nullptr, f8s ? &f8a : nullptr);
   }
   StepMeta meta;
   for (int32_t i = 0; i < num_seqs; ++i) {
     meta.slots[i] = slots[i];
     meta.lens[i] = lens[i];
   }
-  const StepArgs st{key, value, &meta, key_cache, value_cache, block_tables, num_seqs, lens_out};
+  StepArgs st{key, value, &meta, key_cache, value_cache, block_tables, num_seqs, lens_out};
+  if (f8s) {
+    st.key_scales = f8s->key_scales;
+    st.value_scales = f8s->value_scales;
+  }
   return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
                         block_table_stride, lens_out, num_seqs, num_q_heads, max_context_len,
-                        scale, l, 0, workspace, workspace_bytes, stream, &st);
+                        scale, l, 0, workspace, workspace_bytes, stream, &st, f8s ? &f8a : nullptr);
 }
 }  // namespace
 
@@ -2265,6 +2362,21 @@ int paged_decode_attention_fp8(void* out, int32_t out_dtype, const void* q, int3
   return attention_impl(phases, out, out_dtype, q, key_cache, value_cache, block_tables,
                         block_table_stride, context_lens, num_seqs, num_q_heads, max_context_len,
                         scale, layout, 0, workspace, workspace_bytes, stream, nullptr, &f8);
+}
+
+int pkv_decode_step_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype, const void* key,
+                        const void* value, const int64_t* slots, const int32_t* lens, int32_t num_seqs,
+                        void* key_cache, void* value_cache, uint8_t* key_scales, uint8_t* value_scales,
+                        const pkv_cache_layout* layout, int32_t* block_tables,
+                        int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                        int32_t max_context_len, float scale, int32_t phases, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (phases < 1 || phases > 3) return PKV_ERR_INVALID;
+  if (q_dtype != PKV_BF16 && q_dtype != PKV_F16) return PKV_ERR_INVALID;
+  const Fp8Step f8s{key_scales, value_scales, q_dtype};
+  return decode_step_impl(phases, out, out_dtype, q, key, value, slots, lens, num_seqs, key_cache,
+                          value_cache, layout, block_tables, block_table_stride, lens_out, num_q_heads,
+                          max_context_len, scale, workspace, workspace_bytes, stream, &f8s);
 }
 
 int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,

@@ -154,6 +154,8 @@ prefill_kernel(PrefillArgs a) {
   const int w_maxkey = q0 < n ? min(L - 1, L - n + w_last) : -1;
   int row[kBlocksPerWave], pos[kBlocksPerWave];
   bool ok[kBlocksPerWave];
+  // the first key some row of this wave does not see: keys below it need no mask
+  const int w_minpos = min(q0, n - 1) < 0 ? -1 : L - n + q0;
 #pragma unroll
   for (int c = 0; c < kBlocksPerWave; ++c) {
     row[c] = q0 + 16 * c + c16;
@@ -261,10 +263,15 @@ prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < kBlocksPerWave; ++c) {
       const f32x4 s = sa[c] + sb[c];
       float x[4];
+      if (key0 + kKeys - 1 <= w_minpos) {             // below every row's diagonal: no mask
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * g4 + i;
-        x[i] = key <= pos[c] ? s[i] * a.scale_log2 : -INFINITY;
+        for (int i = 0; i < 4; ++i) x[i] = ok[c] ? s[i] * a.scale_log2 : -INFINITY;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 4 * g4 + i;
+          x[i] = key <= pos[c] ? s[i] * a.scale_log2 : -INFINITY;
+        }
       }
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -277,9 +284,12 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[c][j] *= f;
       }
+      // exp2(-inf - m) is 0 for a finite m; a row with no visible key yet
+      // (m = -inf) subtracts 0 instead, so its masked scores give 0 too
+      const float msub = m[c] == -INFINITY ? 0.f : m[c];
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = x[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[i] - m[c]);
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - msub);
       l[c] += (p[0] + p[1]) + (p[2] + p[3]);
       uint16_t hi[4], lo[4];
 #pragma unroll

@@ -32,7 +32,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_write, decode_write_fp8,
+from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_step_fp8, decode_write,
+               decode_write_fp8,
                gather_blocks, scatter_blocks,
                new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
                paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, workspace_size)
@@ -222,11 +223,25 @@ class PagedKVEngine:
                 copy_blocks(src, dst, self.key_cache, self.value_cache)
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
-        if self.fp8:
+        if self.fp8 and not fused:
             decode_write_fp8(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache,
                              self.value_cache, self.key_scales, self.value_scales,
                              block_tables=self.tables, lens_out=self.d_lens)
             return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
+        if self.fp8:
+            ws = self.workspace(n, q.shape[1], max_context_len)
+            if out is None:
+                out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+            args8 = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
+                     self.key_scales, self.value_scales, self.tables, self.d_lens, scale, max_context_len)
+            if events is None:
+                return decode_step_fp8(*args8, out=out, workspace=ws)
+            events[0].record()
+            decode_step_fp8(*args8, out=out, workspace=ws, phase="partial")
+            events[1].record()
+            decode_step_fp8(*args8, out=out, workspace=ws, phase="merge")
+            events[2].record()
+            return out
         if not (fused and self.partition_tokens == 0 and n > 0):
             decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                          block_tables=self.tables, lens_out=self.d_lens)

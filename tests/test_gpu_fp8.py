@@ -218,3 +218,57 @@ def test_fp8_engine_decode_steps_match_oracle():
         err = np.abs(out.double().cpu().numpy() - ref).max()
         _banner(f"fp8 engine step {step}: max abs err {err:.3e}")
         assert err <= 2e-3, (step, err)
+
+
+@pytest.mark.parametrize("hq,hkv,B", [(28, 4, 24), (32, 8, 9), (12, 2, 40)])
+def test_fp8_fused_step_equals_separate_launches_and_oracle(hq, hkv, B):
+    """pkv_decode_step_fp8 (the quantising write inside the 8-bit attention
+    launch) gives bit for bit the pool, scales, tables, lengths and outputs
+    of pkv_decode_write_fp8 followed by the 8-bit attention, over three
+    steps that open blocks, and stays within 2e-3 of the oracle."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    print(f"[gpu] fp8 fused step hq={hq} hkv={hkv} B={B}", flush=True)
+    rng = np.random.default_rng(40 + B)
+    bs, D = 16, 128
+    lens = rng.integers(1, 300, size=B)
+    lens[::4] = 16 * rng.integers(1, 12, size=len(lens[::4]))
+    N = int(np.ceil((lens + 4) / bs).sum()) + 16
+    order = rng.permutation(N)
+    width = int(np.ceil((lens.max() + 4) / bs))
+    engs = [PagedKVEngine(N, hkv, bs, D, torch.float8_e4m3fn, B, width, order, fill_bits=0,
+                          partition_tokens=0, num_q_heads=hq) for _ in range(2)]
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc, oks, ovs = quant.new_fp8_pool(N, hkv, bs, D)
+    k0 = synth.normal(rng, (int(lens.sum()), hkv, D), "bf16")
+    v0 = synth.normal(rng, (int(lens.sum()), hkv, D), "bf16")
+    at = 0
+    for b, L in enumerate(lens):
+        sl = om.allocate_for_prefill(b, int(L))
+        quant.write_kv_fp8(_f32(k0[at:at + L], "bf16"), _f32(v0[at:at + L], "bf16"), sl, okc, ovc, oks, ovs, bs)
+        at += L
+    for e in engs:
+        e.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], to_device(k0, "bf16"),
+                       to_device(v0, "bf16"))
+    ids = np.arange(B, dtype=np.int64)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    for step in range(3):
+        nk = synth.normal(rng, (B, hkv, D), "bf16")
+        nv = synth.normal(rng, (B, hkv, D), "bf16")
+        q = synth.normal(rng, (B, hq, D), "bf16")
+        slots = om.append_slots_for_decode(list(range(B)))
+        quant.write_kv_fp8(_f32(nk, "bf16"), _f32(nv, "bf16"), slots, okc, ovc, oks, ovs, bs)
+        ref = quant.decode_attention_fp8(q, "bf16", okc, ovc, oks, ovs, om.block_tables(list(range(B)), width, -1),
+                                         om.context_lens(list(range(B))), scale)
+        oa = engs[0].decode_step(ids, to_device(nk, "bf16"), to_device(nv, "bf16"), to_device(q, "bf16"), scale,
+                                 fused=True)
+        ob = engs[1].decode_step(ids, to_device(nk, "bf16"), to_device(nv, "bf16"), to_device(q, "bf16"), scale,
+                                 fused=False)
+        torch.cuda.synchronize()
+        for x, y in ((engs[0].pool, engs[1].pool), (engs[0].scales, engs[1].scales)):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), step
+        assert np.array_equal(_u8(engs[0].key_cache), okc) and np.array_equal(_u8(engs[0].value_scales), ovs)
+        assert torch.equal(engs[0].tables, engs[1].tables) and torch.equal(engs[0].d_lens, engs[1].d_lens)
+        assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), step
+        err = np.abs(oa.double().cpu().numpy() - ref).max()
+        print(f"[gpu] fp8 fused step {step}: max abs err {err:.3e}", flush=True)
+        assert err <= 2e-3, err
