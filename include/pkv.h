@@ -303,7 +303,8 @@ int pkv_decode_write(const void* key, const void* value, const int64_t* slots,
  * outside [0, num_blocks) are skipped.  No dst may equal any pair's src or
  * another pair's dst (the pairs run concurrently); pkv_take_block_copies
  * output meets this.  n == 0 is a no-op.  Errors: INVALID, UNSUPPORTED
- * (a head's block_size*head_dim*elem_bytes not a multiple of 16), HIP.
+ * (an 8-bit layout: pkv_copy_blocks_fp8; a head's block_size*head_dim*elem_bytes
+ * not a multiple of 16), HIP.
  */
 int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
                     void* value_cache, const pkv_cache_layout* layout, void* stream);
@@ -315,12 +316,36 @@ int pkv_copy_blocks(const int32_t* src, const int32_t* dst, int32_t n, void* key
  * K half then V half, [n, 2, H_kv, bs, D]); pkv_scatter_blocks copies entry
  * j back into block ids[j].  The caller moves the staging array to and from
  * host memory (a plain device-host copy).  Ids outside [0, num_blocks) are
- * skipped.  16-bit and fp32 layouts.  Errors: INVALID, UNSUPPORTED, HIP.
+ * skipped.  16-bit and fp32 layouts (8-bit ones: the _fp8 forms below).
+ * Errors: INVALID, UNSUPPORTED, HIP.
  */
 int pkv_gather_blocks(const int32_t* ids, int32_t n, const void* key_cache, const void* value_cache,
                       void* staging, const pkv_cache_layout* layout, void* stream);
 int pkv_scatter_blocks(const void* staging, const int32_t* ids, int32_t n, void* key_cache,
                        void* value_cache, const pkv_cache_layout* layout, void* stream);
+
+/*
+ * The copy and the swap staging for 8-bit blocks (layout->dtype ==
+ * PKV_FP8_E4M3): a block's rows are its codes together with their scale
+ * bytes, so each of these moves both ([impl-detail] "Copy-on-Write机制",
+ * "异构内存支持"; the scale addresses are those of the FP8 section below).
+ * key_scales / value_scales (device) are the scale views matching
+ * key_cache / value_cache.  staging holds the codes as for
+ * pkv_gather_blocks (one byte per element); staging_scales (device,
+ * n * 2 * H_kv * bs bytes, no alignment needed) holds entry j's scale bytes,
+ * [n, 2, H_kv, bs] (K half, then V half).  Otherwise as pkv_copy_blocks,
+ * pkv_gather_blocks and pkv_scatter_blocks.  Errors: INVALID (a NULL scale
+ * pointer), UNSUPPORTED (a 16-bit or fp32 layout), HIP.
+ */
+int pkv_copy_blocks_fp8(const int32_t* src, const int32_t* dst, int32_t n, void* key_cache,
+                        void* value_cache, uint8_t* key_scales, uint8_t* value_scales,
+                        const pkv_cache_layout* layout, void* stream);
+int pkv_gather_blocks_fp8(const int32_t* ids, int32_t n, const void* key_cache, const void* value_cache,
+                          const uint8_t* key_scales, const uint8_t* value_scales, void* staging,
+                          uint8_t* staging_scales, const pkv_cache_layout* layout, void* stream);
+int pkv_scatter_blocks_fp8(const void* staging, const uint8_t* staging_scales, const int32_t* ids,
+                           int32_t n, void* key_cache, void* value_cache, uint8_t* key_scales,
+                           uint8_t* value_scales, const pkv_cache_layout* layout, void* stream);
 
 /* -------------------------------------------------------- decode attention */
 /*

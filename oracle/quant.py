@@ -25,6 +25,7 @@ from typing import Sequence, Tuple
 
 import numpy as np
 
+from .cache import copy_blocks, gather_blocks, scatter_blocks
 from .slots import split_slot
 
 E4M3_MAX = 448.0
@@ -137,6 +138,33 @@ def write_kv_fp8(key: np.ndarray, value: np.ndarray, slot_mapping: Sequence[int]
         pb, off = split_slot(slot, block_size)
         key_cache[pb, :, off], key_scales[pb, :, off] = quantize_rows(key[i])
         value_cache[pb, :, off], value_scales[pb, :, off] = quantize_rows(value[i])
+
+
+def copy_blocks_fp8(pairs: Sequence[Tuple[int, int]], key_cache: np.ndarray, value_cache: np.ndarray,
+                    key_scales: np.ndarray, value_scales: np.ndarray) -> None:
+    """Copy-on-write copies of 8-bit blocks ([impl-detail]
+    "Copy-on-Write机制": the new block takes the shared block's k and v).
+    A stored row is its codes together with its scale byte, so the whole-block
+    copy of cache.copy_blocks is applied to the code arrays [N, H, bs, D] and
+    to the scale arrays [N, H, bs] alike."""
+    copy_blocks(pairs, key_cache, value_cache)
+    copy_blocks(pairs, key_scales, value_scales)
+
+
+def gather_blocks_fp8(ids: Sequence[int], key_cache: np.ndarray, value_cache: np.ndarray,
+                      key_scales: np.ndarray, value_scales: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Swap-out staging of 8-bit blocks ([impl-detail] "异构内存支持"):
+    (codes [n, 2, H, bs, D], scale bytes [n, 2, H, bs]) of blocks ``ids`` in
+    order, K half then V half, as cache.gather_blocks stages them."""
+    return gather_blocks(ids, key_cache, value_cache), gather_blocks(ids, key_scales, value_scales)
+
+
+def scatter_blocks_fp8(codes: np.ndarray, scales: np.ndarray, ids: Sequence[int], key_cache: np.ndarray,
+                       value_cache: np.ndarray, key_scales: np.ndarray, value_scales: np.ndarray) -> None:
+    """Swap-in of 8-bit blocks: staged entry j (codes and scale bytes) back
+    into block ids[j]."""
+    scatter_blocks(codes, ids, key_cache, value_cache)
+    scatter_blocks(scales, ids, key_scales, value_scales)
 
 
 def decode_attention_fp8(q: np.ndarray, q_dtype: str, key_cache: np.ndarray,

@@ -101,6 +101,11 @@ SIGNATURES = {
     "pkv_block_ref_count": (_I32, [_P, _I32]),
     "pkv_take_block_copies": (ctypes.c_int, [_P, _PI32, _PI32, _I32, _PI32]),
     "pkv_copy_blocks": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "pkv_copy_blocks_fp8": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, _P, _P, ctypes.POINTER(CacheLayout), _P]),
+    "pkv_gather_blocks_fp8": (ctypes.c_int, [_PI32, _I32, _P, _P, _P, _P, _P, _P,
+                                             ctypes.POINTER(CacheLayout), _P]),
+    "pkv_scatter_blocks_fp8": (ctypes.c_int, [_P, _P, _PI32, _I32, _P, _P, _P, _P,
+                                              ctypes.POINTER(CacheLayout), _P]),
     "paged_kv_write_fp8": (ctypes.c_int, [_P, _P, _I32, _P, _I32, _P, _P, _P, _P,
                                           ctypes.POINTER(CacheLayout), _P]),
     "pkv_decode_write_fp8": (ctypes.c_int, [_P, _P, _I32, _PI64, _PI32, _I32, _P, _P, _P, _P,
@@ -633,6 +638,65 @@ def copy_blocks(src, dst, key_cache, value_cache, stream=None) -> None:
     _check(st, "copy_blocks")
 
 
+def copy_blocks_fp8(src, dst, key_cache, value_cache, key_scales, value_scales, stream=None) -> None:
+    """copy_blocks for an 8-bit pool: codes and scale bytes (see
+    pkv_copy_blocks_fp8)."""
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    dst = np.ascontiguousarray(dst, dtype=np.int32)
+    if src.shape != dst.shape or src.ndim != 1:
+        raise ValueError("src and dst must be 1-D arrays of one length")
+    st = _lib_handle().pkv_copy_blocks_fp8(_ptr(src, ctypes.c_int32), _ptr(dst, ctypes.c_int32), len(src),
+                                           key_cache.data_ptr(), value_cache.data_ptr(), key_scales.data_ptr(),
+                                           value_scales.data_ptr(), ctypes.byref(lay), _stream_handle(stream))
+    _check(st, "copy_blocks_fp8")
+
+
+def _fp8_staging_shapes(lay, n):
+    return ((n, 2, lay.num_kv_heads, lay.block_size, lay.head_dim), (n, 2, lay.num_kv_heads, lay.block_size))
+
+
+def gather_blocks_fp8(ids, key_cache, value_cache, key_scales, value_scales, stream=None):
+    """gather_blocks for an 8-bit pool: returns (codes [n, 2, H_kv, bs, D],
+    scale bytes [n, 2, H_kv, bs]) (see pkv_gather_blocks_fp8)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    cshape, sshape = _fp8_staging_shapes(lay, len(ids))
+    codes = torch.empty(cshape, dtype=key_cache.dtype, device=key_cache.device)
+    scales = torch.empty(sshape, dtype=torch.uint8, device=key_cache.device)
+    st = _lib_handle().pkv_gather_blocks_fp8(_ptr(ids, ctypes.c_int32), len(ids), key_cache.data_ptr(),
+                                             value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(),
+                                             codes.data_ptr(), scales.data_ptr(), ctypes.byref(lay),
+                                             _stream_handle(stream))
+    _check(st, "gather_blocks_fp8")
+    return codes, scales
+
+
+def scatter_blocks_fp8(codes, scales, ids, key_cache, value_cache, key_scales, value_scales, stream=None) -> None:
+    """scatter_blocks for an 8-bit pool: staged codes and scale bytes (as
+    gather_blocks_fp8 returns them) back into blocks ids (see
+    pkv_scatter_blocks_fp8)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    cshape, sshape = _fp8_staging_shapes(lay, len(ids))
+    if tuple(codes.shape) != cshape or codes.dtype != key_cache.dtype or not codes.is_contiguous() \
+            or codes.device != key_cache.device:
+        raise ValueError("codes must be a contiguous device tensor [n, 2, H_kv, bs, D] in the cache dtype")
+    if tuple(scales.shape) != sshape or scales.dtype != torch.uint8 or not scales.is_contiguous() \
+            or scales.device != key_cache.device:
+        raise ValueError("scales must be a contiguous device uint8 tensor [n, 2, H_kv, bs]")
+    st = _lib_handle().pkv_scatter_blocks_fp8(codes.data_ptr(), scales.data_ptr(), _ptr(ids, ctypes.c_int32),
+                                              len(ids), key_cache.data_ptr(), value_cache.data_ptr(),
+                                              key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay),
+                                              _stream_handle(stream))
+    _check(st, "scatter_blocks_fp8")
+
+
 def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
                  block_tables=None, lens_out=None, stream=None) -> None:
     """One decode step's write with host metadata (see pkv_decode_write):
@@ -792,7 +856,8 @@ __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
-    "copy_blocks", "gather_blocks", "scatter_blocks", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
+    "copy_blocks", "gather_blocks", "scatter_blocks", "copy_blocks_fp8", "gather_blocks_fp8",
+    "scatter_blocks_fp8", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
     "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention", "decode_step_fp8",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",

@@ -34,7 +34,7 @@ import torch
 
 from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_step_fp8, decode_write,
                decode_write_fp8,
-               gather_blocks, scatter_blocks,
+               gather_blocks, scatter_blocks, copy_blocks_fp8, gather_blocks_fp8, scatter_blocks_fp8,
                new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
                paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, workspace_size)
 
@@ -106,10 +106,7 @@ class PagedKVEngine:
             except NotLiveError:
                 all_slots.append(self.manager.allocate_for_prefill(sid, n))
             lens.append(self.manager.context_len(sid))
-        if self._sharing:
-            src, dst = self.manager.take_copies()
-            if len(src):
-                copy_blocks(src, dst, self.key_cache, self.value_cache)
+        self._run_copies()
         slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
             self._write(key, value, torch.from_numpy(slots).to(self.device))
@@ -123,6 +120,19 @@ class PagedKVEngine:
         return paged_prefill_attention(q, d_qs, self.key_cache, self.value_cache, tables, d_lens, scale,
                                        max_q_len=int(max(chunk_lens)) if B else 0,
                                        max_context_len=int(max(lens)) if B else 0, out=out)
+
+    def _run_copies(self):
+        """Copy-on-write: the block copies the manager queued, on the stream,
+        before anything writes into the new blocks."""
+        if not self._sharing:
+            return
+        src, dst = self.manager.take_copies()
+        if not len(src):
+            return
+        if self.fp8:
+            copy_blocks_fp8(src, dst, self.key_cache, self.value_cache, self.key_scales, self.value_scales)
+        else:
+            copy_blocks(src, dst, self.key_cache, self.value_cache)
 
     def _write(self, key, value, d_slots):
         if self.fp8:
@@ -150,8 +160,6 @@ class PagedKVEngine:
         """Admit ``seq_id`` into ``row`` holding the first ``num_tokens`` tokens
         of live ``donor_id`` on the donor's blocks, no copy
         ([impl-detail] "前缀共享"); its appends copy a shared block first."""
-        if self.fp8:
-            raise NotImplementedError("copy-on-write of 8-bit blocks (codes and scales) is not built")
         self.manager.share_prefix(donor_id, seq_id, num_tokens)
         self._sharing = True
         self._publish_row(seq_id, row)
@@ -161,26 +169,33 @@ class PagedKVEngine:
         them ([impl-detail] "异构内存支持" evict_to_cpu): gather on the device,
         then one device-to-host copy on the current stream (the host tensor
         holds the data once the stream has passed it).  Returns the host
-        copy, which swap_in takes back.  The sequence's row is left to the
+        copy, which swap_in takes back: one pinned tensor [n, 2, H_kv, bs, D],
+        or for an 8-bit pool the pair (codes, scale bytes [n, 2, H_kv, bs]).  The sequence's row is left to the
         caller."""
-        if self.fp8:
-            raise NotImplementedError("swap of 8-bit blocks (codes and scales) is not built")
         ids = self.manager.swap_out(seq_id)
-        staged = gather_blocks(ids, self.key_cache, self.value_cache)
-        host = torch.empty(staged.shape, dtype=staged.dtype, pin_memory=True)
-        host.copy_(staged, non_blocking=True)
+        if self.fp8:
+            staged = gather_blocks_fp8(ids, self.key_cache, self.value_cache, self.key_scales, self.value_scales)
+        else:
+            staged = (gather_blocks(ids, self.key_cache, self.value_cache),)
+        host = tuple(torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in staged)
+        for h, t in zip(host, staged):
+            h.copy_(t, non_blocking=True)
         for r, s in list(self.row_seq.items()):
             if s == seq_id:
                 del self.row_seq[r]
-        return host
+        return host if self.fp8 else host[0]
 
     def swap_in(self, seq_id: int, row: int, host: torch.Tensor) -> None:
         """Bring a swapped sequence back into ``row`` on fresh blocks
         ([impl-detail] "异构内存支持" prefetch_to_gpu): one host-to-device
         copy, a scatter, and the table row published."""
         ids = self.manager.swap_in(seq_id)
-        staged = host.to(self.device, non_blocking=True)
-        scatter_blocks(staged, ids, self.key_cache, self.value_cache)
+        if self.fp8:
+            codes, scales = (t.to(self.device, non_blocking=True) for t in host)
+            scatter_blocks_fp8(codes, scales, ids, self.key_cache, self.value_cache, self.key_scales,
+                               self.value_scales)
+        else:
+            scatter_blocks(host.to(self.device, non_blocking=True), ids, self.key_cache, self.value_cache)
         self._publish_row(seq_id, row)
 
     def _publish_row(self, seq_id: int, row: int):
@@ -217,10 +232,7 @@ class PagedKVEngine:
         separate write launch."""
         n = len(seq_ids)
         self.manager.append_slots_for_decode(seq_ids, self.slots[:n], self.lens[:n], self._newb[:n])
-        if self._sharing:
-            src, dst = self.manager.take_copies()
-            if len(src):
-                copy_blocks(src, dst, self.key_cache, self.value_cache)
+        self._run_copies()
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
         if self.fp8 and not fused:

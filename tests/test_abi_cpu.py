@@ -104,3 +104,26 @@ def test_manager_create_rejects_bad_arguments():
         pkv.KVBlockManager(4, 16, [0, 1, 1, 2])
     with pytest.raises(ValueError):
         pkv.KVBlockManager(4, 0)
+
+
+def test_block_copy_and_staging_dtype_checks_need_no_gpu():
+    """The 16-bit block entry points refuse an 8-bit layout (its codes would
+    move without their scales) and the 8-bit ones refuse a 16-bit layout or
+    a missing scale array, before any launch; n == 0 is a no-op."""
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    l16 = _layout(dtype=pkv.PKV_BF16, head_dim=128, head_stride=16 * 128, block_stride=2 * 4 * 16 * 128)
+    l8 = _layout(dtype=pkv.PKV_FP8_E4M3, head_dim=128, head_stride=16 * 128, block_stride=2 * 4 * 16 * 128)
+    assert lib.pkv_copy_blocks(ids, ids, 2, fake, fake, ctypes.byref(l8), None) == -5
+    assert lib.pkv_gather_blocks(ids, 2, fake, fake, fake, ctypes.byref(l8), None) == -5
+    assert lib.pkv_scatter_blocks(fake, ids, 2, fake, fake, ctypes.byref(l8), None) == -5
+    assert lib.pkv_copy_blocks_fp8(ids, ids, 2, fake, fake, fake, fake, ctypes.byref(l16), None) == -5
+    assert lib.pkv_gather_blocks_fp8(ids, 2, fake, fake, fake, fake, fake, fake, ctypes.byref(l16), None) == -5
+    assert lib.pkv_scatter_blocks_fp8(fake, fake, ids, 2, fake, fake, fake, fake, ctypes.byref(l16), None) == -5
+    assert lib.pkv_copy_blocks_fp8(ids, ids, 2, fake, fake, None, fake, ctypes.byref(l8), None) == -1
+    assert lib.pkv_gather_blocks_fp8(ids, 2, fake, fake, fake, fake, fake, None, ctypes.byref(l8), None) == -1
+    assert lib.pkv_scatter_blocks_fp8(fake, fake, ids, 2, fake, fake, fake, None, ctypes.byref(l8), None) == -1
+    assert lib.pkv_copy_blocks_fp8(ids, ids, -1, fake, fake, fake, fake, ctypes.byref(l8), None) == -1
+    assert lib.pkv_copy_blocks_fp8(ids, ids, 0, fake, fake, fake, fake, ctypes.byref(l8), None) == 0
+    assert lib.pkv_gather_blocks_fp8(ids, 0, fake, fake, fake, fake, fake, fake, ctypes.byref(l8), None) == 0

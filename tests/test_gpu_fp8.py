@@ -272,3 +272,153 @@ def test_fp8_fused_step_equals_separate_launches_and_oracle(hq, hkv, B):
         err = np.abs(oa.double().cpu().numpy() - ref).max()
         print(f"[gpu] fp8 fused step {step}: max abs err {err:.3e}", flush=True)
         assert err <= 2e-3, err
+
+
+def _fp8_pools(rng, N, H, bs, D, T):
+    """Oracle and GPU 8-bit pools, poisoned, then T random rows written at
+    random slots by each side's quantising write (bit-exact, tested above)."""
+    okc, ovc, oks, ovs = quant.new_fp8_pool(N, H, bs, D)
+    g = pkv.new_fp8_pool(N, H, bs, D, "cuda", poison=True)
+    k = synth.normal(rng, (T, H, D), "bf16")
+    v = synth.normal(rng, (T, H, D), "bf16")
+    slots = rng.permutation(N * bs)[:T].astype(np.int64)
+    quant.write_kv_fp8(_f32(k, "bf16"), _f32(v, "bf16"), slots, okc, ovc, oks, ovs, bs)
+    pkv.paged_kv_write_fp8(to_device(k, "bf16"), to_device(v, "bf16"), torch.from_numpy(slots).cuda(),
+                           g[1], g[2], g[4], g[5])
+    return (okc, ovc, oks, ovs), g
+
+
+def _same_pool(g, o):
+    okc, ovc, oks, ovs = o
+    return (np.array_equal(_u8(g[1]), okc) and np.array_equal(_u8(g[2]), ovc)
+            and np.array_equal(_u8(g[4]), oks) and np.array_equal(_u8(g[5]), ovs))
+
+
+@pytest.mark.parametrize("H,bs,D,npairs", [(4, 16, 128, 300), (2, 32, 64, 3), (8, 8, 128, 1)])
+def test_fp8_copy_blocks_bit_exact(H, bs, D, npairs):
+    """pkv_copy_blocks_fp8 against the oracle's copy of codes and scale
+    bytes, over the whole pool (poison included); an out-of-range pair is
+    skipped."""
+    _banner(f"fp8 copy_blocks H={H} bs={bs} D={D} pairs={npairs}")
+    rng = np.random.default_rng(300 + npairs)
+    N = 2 * npairs + 8
+    o, g = _fp8_pools(rng, N, H, bs, D, (N * bs * 3) // 4)
+    perm = rng.permutation(N)
+    src = np.append(perm[:npairs], [N + 5]).astype(np.int32)
+    dst = np.append(perm[npairs:2 * npairs], [perm[-1]]).astype(np.int32)
+    pkv.copy_blocks_fp8(src, dst, g[1], g[2], g[4], g[5])
+    torch.cuda.synchronize()
+    quant.copy_blocks_fp8(list(zip(src.tolist(), dst.tolist())), *o)
+    assert _same_pool(g, o)
+
+
+@pytest.mark.parametrize("H,bs,D,n", [(4, 16, 128, 300), (2, 8, 64, 5)])
+def test_fp8_gather_scatter_bit_exact(H, bs, D, n):
+    """pkv_gather_blocks_fp8 / pkv_scatter_blocks_fp8 against the oracle's
+    staging of codes and scale bytes."""
+    _banner(f"fp8 gather/scatter H={H} bs={bs} D={D} n={n}")
+    rng = np.random.default_rng(400 + n)
+    N = n + 20
+    o, g = _fp8_pools(rng, N, H, bs, D, N * bs - 7)
+    ids = rng.permutation(N)[:n].astype(np.int32)
+    codes, scales = pkv.gather_blocks_fp8(ids, g[1], g[2], g[4], g[5])
+    torch.cuda.synchronize()
+    rc, rs = quant.gather_blocks_fp8(ids, *o)
+    assert np.array_equal(_u8(codes), rc) and np.array_equal(scales.cpu().numpy(), rs)
+    dst = rng.permutation(N)[:n].astype(np.int32)
+    pkv.scatter_blocks_fp8(codes, scales, dst, g[1], g[2], g[4], g[5])
+    torch.cuda.synchronize()
+    quant.scatter_blocks_fp8(rc, rs, dst, *o)
+    assert _same_pool(g, o)
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_fp8_shared_prefix_decode_matches_oracle(fused):
+    """Prefix sharing on an 8-bit pool through the engine: forks and shorter
+    shares, then decode steps whose appends copy shared blocks (codes and
+    scales) first; against the oracle replay: the whole pool bit for bit,
+    tables, reference counts, and attention within 2e-3."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    _banner(f"fp8 sharing decode fused={fused}")
+    rng = np.random.default_rng(61 + int(fused))
+    hq, hkv, bs, D = 28, 4, 16, 128
+    donors = [int(x) for x in rng.integers(1, 300, size=5)]
+    donors[1] = 6 * bs
+    shares = [(0, donors[0]), (1, donors[1]), (2, max(1, donors[2] // 2)), (3, (donors[3] // bs) * bs),
+              (4, donors[4] - 1), (0, 0)]
+    steps = 3
+    ids = list(range(len(donors) + len(shares)))
+    width = int(np.ceil((max(donors) + steps + 1) / bs))
+    N = sum(int(np.ceil((L + steps) / bs)) for L in donors) + len(shares) * 2 + 16
+    order = rng.permutation(N)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    om = oracle.BlockManager(N, bs, order)
+    o = quant.new_fp8_pool(N, hkv, bs, D)
+    eng = PagedKVEngine(N, hkv, bs, D, torch.float8_e4m3fn, len(ids), width, order, fill_bits=0,
+                        partition_tokens=0, num_q_heads=hq)
+    pk = [synth.normal(rng, (L, hkv, D), "bf16") for L in donors]
+    pv = [synth.normal(rng, (L, hkv, D), "bf16") for L in donors]
+    for sid, L in enumerate(donors):
+        quant.write_kv_fp8(_f32(pk[sid], "bf16"), _f32(pv[sid], "bf16"), om.allocate_for_prefill(sid, L), *o, bs)
+    eng.prefill_many(list(range(len(donors))), list(range(len(donors))), donors,
+                     to_device(np.concatenate(pk), "bf16"), to_device(np.concatenate(pv), "bf16"))
+    for j, (donor, n) in enumerate(shares):
+        sid = len(donors) + j
+        om.share_prefix(donor, sid, n)
+        eng.share_prefix(donor, sid, sid, n)
+    copies_seen = 0
+    for step in range(steps):
+        nk = synth.normal(rng, (len(ids), hkv, D), "bf16")
+        nv = synth.normal(rng, (len(ids), hkv, D), "bf16")
+        q = synth.normal(rng, (len(ids), hq, D), "bf16")
+        slots = om.append_slots_for_decode(ids)
+        pairs = om.take_copies()
+        copies_seen += len(pairs)
+        quant.copy_blocks_fp8(pairs, *o)
+        quant.write_kv_fp8(_f32(nk, "bf16"), _f32(nv, "bf16"), slots, *o, bs)
+        tabs = om.block_tables(ids, width, -1)
+        ref = quant.decode_attention_fp8(q, "bf16", *o, tabs, om.context_lens(ids), scale)
+        out = eng.decode_step(np.array(ids, np.int64), to_device(nk, "bf16"), to_device(nv, "bf16"),
+                              to_device(q, "bf16"), scale, fused=fused)
+        torch.cuda.synchronize()
+        assert [eng.manager.ref_count(b) for b in range(N)] == om.ref, step
+        assert np.array_equal(eng.tables.cpu().numpy(), tabs), step
+        assert _same_pool((eng.pool, eng.key_cache, eng.value_cache, eng.scales, eng.key_scales,
+                           eng.value_scales), o), step
+        err = np.abs(out.double().cpu().numpy() - ref).max()
+        _banner(f"fp8 sharing step {step}: copies {len(pairs)}, max abs err {err:.3e}")
+        assert err <= 2e-3, (step, err)
+    assert copies_seen > 0
+
+
+def test_fp8_engine_swap_round_trip_is_bit_exact():
+    """Swap of an 8-bit sequence through pinned host memory: after its
+    blocks are reused by another sequence and it comes back on other
+    blocks, its attention output is bit for bit what it was."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    _banner("fp8 engine swap round trip")
+    rng = np.random.default_rng(72)
+    B, hq, hkv, bs, D = 6, 28, 4, 16, 128
+    lens = rng.integers(20, 400, B)
+    N = int(np.ceil(lens / bs).sum()) + 40
+    eng = PagedKVEngine(N, hkv, bs, D, torch.float8_e4m3fn, B + 1, N, rng.permutation(N), num_q_heads=hq)
+    k = to_device(synth.normal(rng, (int(lens.sum()), hkv, D), "bf16"), "bf16")
+    v = to_device(synth.normal(rng, (int(lens.sum()), hkv, D), "bf16"), "bf16")
+    eng.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], k, v)
+    q = to_device(synth.normal(rng, (B, hq, D), "bf16"), "bf16")
+    d_lens = torch.from_numpy(lens.astype(np.int32)).cuda()
+    before = eng.attend(q, d_lens, 0.088, int(lens.max())).clone()
+    old_table = eng.manager.block_table(2)
+    host = eng.swap_out(2)
+    assert isinstance(host, tuple) and host[0].is_pinned() and host[1].is_pinned()
+    n_other = eng.manager.num_free_blocks() * bs
+    eng.prefill(99, B, to_device(synth.normal(rng, (n_other, hkv, D), "bf16"), "bf16"),
+                to_device(synth.normal(rng, (n_other, hkv, D), "bf16"), "bf16"))
+    assert set(eng.manager.block_table(99)) & set(old_table)
+    eng.free(99)
+    eng.manager.allocate_for_prefill(100, 5 * bs)
+    eng.swap_in(2, 2, host)
+    assert eng.manager.block_table(2) != old_table
+    after = eng.attend(q, d_lens, 0.088, int(lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int32), after.view(torch.int32))

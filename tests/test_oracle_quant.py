@@ -133,3 +133,62 @@ def test_array_quantiser_equals_the_scalar_definition():
     for i, r in enumerate(rows):
         c, sb = quant.quantize_row(r)
         assert np.array_equal(codes[i], c) and sbytes[i] == sb, i
+
+
+def _fp8_pool_with_spread_scales(rng, N, H, bs, D):
+    """An 8-bit pool whose blocks hold rows of very different magnitudes, so
+    that codes read with another block's scale bytes give other values."""
+    kc, vc, ks, vs = quant.new_fp8_pool(N, H, bs, D)
+    for b in range(N):
+        mag = 2.0 ** (3 * b - 12)
+        k = (rng.standard_normal((bs, H, D)) * mag).astype(np.float32)
+        v = (rng.standard_normal((bs, H, D)) * mag * 0.5).astype(np.float32)
+        quant.write_kv_fp8(k, v, [b * bs + o for o in range(bs)], kc, vc, ks, vs, bs)
+    return kc, vc, ks, vs
+
+
+def test_fp8_block_copy_keeps_every_read_back_value():
+    """Copy-on-write of an 8-bit block ([impl-detail] "Copy-on-Write机制"):
+    the new block reads back exactly the shared block's values, the
+    attention of a table through it is unchanged, and no other block moves.
+    Copying codes without their scale bytes fails the first check."""
+    rng = np.random.default_rng(9)
+    N, H, bs, D = 8, 2, 4, 16
+    kc, vc, ks, vs = _fp8_pool_with_spread_scales(rng, N, H, bs, D)
+    before = [(kc[b].copy(), vc[b].copy(), ks[b].copy(), vs[b].copy()) for b in range(N)]
+    pairs = [(1, 6), (4, 2)]
+    q = np.asarray(rng.standard_normal((1, 2 * H, D)), dtype=np.float32).astype(np.float16)
+    ref = quant.decode_attention_fp8(q, "f16", kc, vc, ks, vs, np.array([[1, 4]]), [2 * bs - 1], 0.25)
+    quant.copy_blocks_fp8(pairs, kc, vc, ks, vs)
+    for s, d in pairs:
+        assert not np.array_equal(quant.dequantize(before[d][0], before[d][2]),
+                                  quant.dequantize(kc[s], ks[s]))     # the copy changes something
+        assert np.array_equal(quant.dequantize(kc[d], ks[d]), quant.dequantize(kc[s], ks[s]))
+        assert np.array_equal(quant.dequantize(vc[d], vs[d]), quant.dequantize(vc[s], vs[s]))
+        assert np.array_equal(kc[d], kc[s]) and np.array_equal(vs[d], vs[s])
+    for b in set(range(N)) - {d for _, d in pairs}:
+        assert all(np.array_equal(x, y) for x, y in zip((kc[b], vc[b], ks[b], vs[b]), before[b]))
+    out = quant.decode_attention_fp8(q, "f16", kc, vc, ks, vs, np.array([[6, 2]]), [2 * bs - 1], 0.25)
+    assert np.array_equal(out, ref)
+
+
+def test_fp8_swap_staging_round_trip():
+    """Swap of 8-bit blocks ([impl-detail] "异构内存支持"): staged entry j
+    holds block ids[j]'s codes and scale bytes (K half, then V half), reads
+    back as that block's values, and scattering it onto other blocks
+    reproduces every value there."""
+    rng = np.random.default_rng(10)
+    N, H, bs, D = 9, 3, 4, 8
+    kc, vc, ks, vs = _fp8_pool_with_spread_scales(rng, N, H, bs, D)
+    ids = [7, 0, 3]
+    codes, scales = quant.gather_blocks_fp8(ids, kc, vc, ks, vs)
+    assert codes.shape == (3, 2, H, bs, D) and scales.shape == (3, 2, H, bs)
+    for j, b in enumerate(ids):
+        assert np.array_equal(quant.dequantize(codes[j, 0], scales[j, 0]), quant.dequantize(kc[b], ks[b]))
+        assert np.array_equal(quant.dequantize(codes[j, 1], scales[j, 1]), quant.dequantize(vc[b], vs[b]))
+    want = [(quant.dequantize(kc[b], ks[b]), quant.dequantize(vc[b], vs[b])) for b in ids]
+    dst = [2, 8, 5]
+    quant.scatter_blocks_fp8(codes, scales, dst, kc, vc, ks, vs)
+    for (wk, wv), b in zip(want, dst):
+        assert np.array_equal(quant.dequantize(kc[b], ks[b]), wk)
+        assert np.array_equal(quant.dequantize(vc[b], vs[b]), wv)
