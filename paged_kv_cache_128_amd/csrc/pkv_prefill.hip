@@ -9,22 +9,25 @@
 // Unlike decode, each K/V tile meets many query rows, so both products are
 // dense contractions and run on the matrix cores.  A workgroup takes 128
 // query rows of one (sequence, head): four waves of 32 rows, each as two
-// 16-column MFMA blocks.  Per tile of 64 keys (four 16-key sub-tiles, each
-// inside one block) the workgroup stages K and V once in LDS (double-
+// 16-column MFMA blocks.  Per tile of 64 keys (four 16-key quarters, one
+// staged by each wave) the workgroup stages K and V once in LDS (double-
 // buffered, filled by LDS-DMA while the previous tile is being used; K rows
 // XOR-swizzled so the operand reads hit distinct banks), then for each
-// sub-tile every wave
+// 32-key half of the tile every wave
 //   - forms scores S^T[key][row] = K Q^T with 16x16x32 MFMAs (A = K rows,
 //     B = the query rows), so lane (g4, c16) holds row c16's scores for
-//     keys 4 g4 .. 4 g4 + 3 -- the B operand layout of P.V;
-//   - runs the online softmax per row (exp2 with the scale folded in, fp32
-//     state);
-//   - adds O^T[d][row] += V^T P^T with 16x16x16 MFMAs: MFMA j maps its row
-//     index c to head-dim 8 c + j, so its A operand is element j of V rows
-//     4 g4 .. 4 g4 + 3 at head-dims 8 c16 .. 8 c16 + 7, and P enters as a
-//     16-bit value plus its 16-bit remainder (two MFMAs; P to about 2^-17).
+//     keys 4 g4 .. 4 g4 + 3 of each 16-key quarter;
+//   - runs the online softmax per row over those eight scores (exp2 with
+//     the scale folded in, fp32 state; the max and sum across the four lanes
+//     of a row by lane swaps on the vector ALU);
+//   - adds O^T[d][row] += V^T P^T with 16x16x32 MFMAs whose k index 8 g4 + e
+//     stands for key 16 (e / 4) + 4 g4 + e % 4, so a lane's own eight
+//     probabilities are its B operand; MFMA j maps its row index c to
+//     head-dim 8 c + j, so its A operand is element j of the lane's V rows
+//     (head-dims 8 c16 .. 8 c16 + 7); P enters as a 16-bit value plus its
+//     16-bit remainder (two MFMAs; P to about 2^-17).
 // Lane (g4, c16) ends with its rows' head-dims 32 g4 .. 32 g4 + 31.  A wave
-// skips the products of tiles wholly past its rows' positions (it still
+// skips the products of key ranges wholly past its rows' positions (it still
 // takes part in the staging).  Keys past L read zeros (buffer range check)
 // and are masked like every key past a row's position.  16-bit KV, head_dim
 // 128.
@@ -99,7 +102,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
 }
 
 template <int DT>
-__device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_k32(const u32x4& a, const u32x4& b, f32x4 c) {
   if constexpr (DT == PKV_BF16)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                    c, 0, 0, 0);
@@ -108,18 +111,24 @@ __device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, f32x4 c
                                                   c, 0, 0, 0);
 }
 
-template <int DT>
-__device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, f32x4 c) {
-  if constexpr (DT == PKV_BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
-                                                     c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b),
-                                                 c, 0, 0, 0);
+// Max and sum over the lanes c16, c16 + 16, c16 + 32, c16 + 48 (every lane
+// gets the result), on the vector ALU: the 16-lane row swap pairs rows
+// (0, 1) and (2, 3), the 32-lane half swap pairs the halves.
+__device__ __forceinline__ float max_over_g4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_g4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int DT>
-__global__ void __launch_bounds__(kWave * kWavesPF)
+__global__ void __launch_bounds__(kWave * kWavesPF) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_kernel(PrefillArgs a) {
   // dynamic LDS: [K tile x 2][V tile x 2] (16-byte slots), then the table entries
   extern __shared__ uint4 sh_pf[];
@@ -184,7 +193,7 @@ prefill_kernel(PrefillArgs a) {
   // probability is finite and only staged table entries are used.
   auto stage = [&](int kt) {
     const int key0 = (kt * kSub + wave) * kKeys;
-    const int nvalid = max(0, min(kKeys, wg_keys - key0));
+    const int nvalid = uni(max(0, min(kKeys, wg_keys - key0)));   // uniform: keeps the DMA descriptor scalar
     const int pb = nvalid > 0 ? uni(tbl[key0 / bs]) : 0;
     const int64_t base = nvalid > 0 ? (static_cast<int64_t>(pb) * a.block_stride + head_off +
                                        static_cast<int64_t>(key0 % bs) * kD) * 2 : 0;
@@ -217,107 +226,110 @@ prefill_kernel(PrefillArgs a) {
     __syncthreads();                  // tile kt staged by every wave; tile kt - 1 no longer read
     if (kt + 1 < ntiles) stage(kt + 1);
 #pragma unroll 1
-    for (int sub = 0; sub < kSub; ++sub) {
-    const int key0 = (kt * kSub + sub) * kKeys;
-    if (key0 > w_maxkey) break;                       // every key from here on is past this wave's rows
-    const uint4* tk = sk + (kt & 1) * kTileSlots + sub * kSubSlots;
-    const uint4* tv = sv + (kt & 1) * kTileSlots + sub * kSubSlots;
-    // K operand: key c16, chunk 4 kk + g4 (slot (4 kk + g4) ^ c16)
-    u32x4 kf[4];
+    for (int sub = 0; sub < kSub; sub += 2) {
+      // keys key0 .. key0 + 31: staged sub-tiles sub (half 0) and sub + 1 (half 1)
+      const int key0 = (kt * kSub + sub) * kKeys;
+      if (key0 > w_maxkey) break;                     // every key from here on is past this wave's rows
+      const uint4* tk = sk + (kt & 1) * kTileSlots + sub * kSubSlots;
+      const uint4* tv = sv + (kt & 1) * kTileSlots + sub * kSubSlots;
+      // K operands: key c16 of half h, chunk 4 kk + g4 (slot (4 kk + g4) ^ c16)
+      u32x4 kf[2][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint4 x = tk[c16 * 16 + ((4 * kk + g4) ^ c16)];
-      kf[kk] = u32x4{x.x, x.y, x.z, x.w};
-    }
-    // V rows 4 g4 + r, head-dims 8 c16 .. + 7
-    uint4 vr[4];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = tv[(4 * g4 + r) * 16 + c16];
-    u32x2 av[8];
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint4 x = tk[h * kSubSlots + c16 * 16 + ((4 * kk + g4) ^ c16)];
+          kf[h][kk] = u32x4{x.x, x.y, x.z, x.w};
+        }
+      // scores of both halves and both column blocks: four MFMA chains
+      f32x4 sa[2][kBlocksPerWave];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const int w = j >> 1;
-      const uint32_t v0 = w == 0 ? vr[0].x : w == 1 ? vr[0].y : w == 2 ? vr[0].z : vr[0].w;
-      const uint32_t v1 = w == 0 ? vr[1].x : w == 1 ? vr[1].y : w == 2 ? vr[1].z : vr[1].w;
-      const uint32_t v2 = w == 0 ? vr[2].x : w == 1 ? vr[2].y : w == 2 ? vr[2].z : vr[2].w;
-      const uint32_t v3 = w == 0 ? vr[3].x : w == 1 ? vr[3].y : w == 2 ? vr[3].z : vr[3].w;
-      av[j] = u32x2{__builtin_amdgcn_perm(v1, v0, sel), __builtin_amdgcn_perm(v3, v2, sel)};
-    }
-    // scores of both column blocks, each as two independent MFMA chains
-    f32x4 sa[kBlocksPerWave], sb[kBlocksPerWave];
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int c = 0; c < kBlocksPerWave; ++c) {
-      sa[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sb[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+        for (int c = 0; c < kBlocksPerWave; ++c) sa[h][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; kk += 2)
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c = 0; c < kBlocksPerWave; ++c) sa[h][c] = mfma_k32<DT>(kf[h][kk], qf[c][kk], sa[h][c]);
+      // V rows 4 g4 + r of each half, head-dims 8 c16 .. + 7 (read while the
+      // softmax runs)
+      uint4 vr[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vr[h][r] = tv[h * kSubSlots + (4 * g4 + r) * 16 + c16];
+      // P as the B operand of the 32-key P.V: lane (g4, c16) gives row c16's
+      // probabilities for k = 8 g4 + e, which stands for key 16 (e / 4) +
+      // 4 g4 + e % 4 -- the lane's own scores, in order
+      u32x4 bh[kBlocksPerWave], bl[kBlocksPerWave];
+      const bool below = key0 + 2 * kKeys - 1 <= w_minpos;   // below every row's diagonal: no mask
 #pragma unroll
       for (int c = 0; c < kBlocksPerWave; ++c) {
-        sa[c] = mfma_qk<DT>(kf[kk], qf[c][kk], sa[c]);
-        sb[c] = mfma_qk<DT>(kf[kk + 1], qf[c][kk + 1], sb[c]);
+        // the row's last visible key: keys above it are masked (a select, no branch)
+        const int lim = below ? (ok[c] ? key0 + 2 * kKeys : -1) : pos[c];
+        float x[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = sa[h][c][i] * a.scale_log2;
+            x[4 * h + i] = key0 + 16 * h + 4 * g4 + i <= lim ? sc : -INFINITY;
+          }
+        float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        bm = max_over_g4(bm);
+        if (__builtin_amdgcn_ballot_w64(bm > m[c] + kSlack) != 0) {
+          const float m_new = fmaxf(m[c], bm);
+          const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
+          l[c] *= f;
+          m[c] = m_new;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[c][j] *= f;
+        }
+        // exp2(-inf - m) is 0 for a finite m; a row with no visible key yet
+        // (m = -inf) subtracts 0 instead, so its masked scores give 0 too
+        const float msub = m[c] == -INFINITY ? 0.f : m[c];
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - msub);
+        l[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t h0 = to16<DT>(p[2 * e]), h1 = to16<DT>(p[2 * e + 1]);
+          hw[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+          lw[e] = static_cast<uint32_t>(to16<DT>(p[2 * e] - from16<DT>(h0))) |
+                  (static_cast<uint32_t>(to16<DT>(p[2 * e + 1] - from16<DT>(h1))) << 16);
+        }
+        bh[c] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        bl[c] = u32x4{lw[0], lw[1], lw[2], lw[3]};
       }
-    u32x2 bh[kBlocksPerWave], bl[kBlocksPerWave];
+      // P.V: MFMA j maps its row index c to head-dim 8 c + j; its A operand is
+      // element j of V rows 4 g4 .. 4 g4 + 3 of half 0, then of half 1
 #pragma unroll
-    for (int c = 0; c < kBlocksPerWave; ++c) {
-      const f32x4 s = sa[c] + sb[c];
-      float x[4];
-      if (key0 + kKeys - 1 <= w_minpos) {             // below every row's diagonal: no mask
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        const int w = j >> 1;
+        uint32_t e[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = ok[c] ? s[i] * a.scale_log2 : -INFINITY;
-      } else {
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 4 * g4 + i;
-          x[i] = key <= pos[c] ? s[i] * a.scale_log2 : -INFINITY;
+          for (int r = 0; r < 4; ++r)
+            e[h][r] = w == 0 ? vr[h][r].x : w == 1 ? vr[h][r].y : w == 2 ? vr[h][r].z : vr[h][r].w;
+        const u32x4 av{__builtin_amdgcn_perm(e[0][1], e[0][0], sel), __builtin_amdgcn_perm(e[0][3], e[0][2], sel),
+                       __builtin_amdgcn_perm(e[1][1], e[1][0], sel), __builtin_amdgcn_perm(e[1][3], e[1][2], sel)};
+#pragma unroll
+        for (int c = 0; c < kBlocksPerWave; ++c) {
+          acc[c][j] = mfma_k32<DT>(av, bh[c], acc[c][j]);
+          acc[c][j] = mfma_k32<DT>(av, bl[c], acc[c][j]);
         }
       }
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      if (__builtin_amdgcn_ballot_w64(bm > m[c] + kSlack) != 0) {
-        const float m_new = fmaxf(m[c], bm);
-        const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
-        l[c] *= f;
-        m[c] = m_new;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[c][j] *= f;
-      }
-      // exp2(-inf - m) is 0 for a finite m; a row with no visible key yet
-      // (m = -inf) subtracts 0 instead, so its masked scores give 0 too
-      const float msub = m[c] == -INFINITY ? 0.f : m[c];
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - msub);
-      l[c] += (p[0] + p[1]) + (p[2] + p[3]);
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[i] = to16<DT>(p[i]);
-        lo[i] = to16<DT>(p[i] - from16<DT>(hi[i]));
-      }
-      bh[c] = u32x2{static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16),
-                    static_cast<uint32_t>(hi[2]) | (static_cast<uint32_t>(hi[3]) << 16)};
-      bl[c] = u32x2{static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16),
-                    static_cast<uint32_t>(lo[2]) | (static_cast<uint32_t>(lo[3]) << 16)};
-    }
-    // P.V: sixteen independent accumulators per pass (high part, then remainder)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int c = 0; c < kBlocksPerWave; ++c) acc[c][j] = mfma_pv<DT>(av[j], bh[c], acc[c][j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int c = 0; c < kBlocksPerWave; ++c) acc[c][j] = mfma_pv<DT>(av[j], bl[c], acc[c][j]);
     }
   }
 #pragma unroll
   for (int c = 0; c < kBlocksPerWave; ++c) {
-    float lc = l[c];
-    lc += __shfl_xor(lc, 16);
-    lc += __shfl_xor(lc, 32);
+    const float lc = sum_over_g4(l[c]);
     if (!ok[c]) continue;
     const float inv = lc > 0.f ? 1.0f / lc : 0.f;
     const int64_t o = ((static_cast<int64_t>(r0) + row[c]) * a.hq + qh) * kD + 32 * g4;
