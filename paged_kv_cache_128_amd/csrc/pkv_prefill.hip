@@ -58,6 +58,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -94,6 +96,26 @@ template <int DT>
 __device__ __forceinline__ float from16(uint16_t h) {
   if constexpr (DT == PKV_BF16) return __uint_as_float(static_cast<uint32_t>(h) << 16);
   else return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Two floats to a packed pair of 16-bit values (element 0 in the low half),
+// rounded to nearest even; and back.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float x0, float x1) {
+  if constexpr (DT == PKV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  else
+    return static_cast<uint32_t>(to16<DT>(x0)) | (static_cast<uint32_t>(to16<DT>(x1)) << 16);
+}
+template <int DT>
+__device__ __forceinline__ void unpack2f(uint32_t w, float& x0, float& x1) {
+  if constexpr (DT == PKV_BF16) {
+    x0 = __uint_as_float(w << 16);
+    x1 = __uint_as_float(w & 0xffff0000u);
+  } else {
+    x0 = from16<DT>(static_cast<uint16_t>(w));
+    x1 = from16<DT>(static_cast<uint16_t>(w >> 16));
+  }
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int nrows) {
@@ -264,21 +286,26 @@ prefill_kernel(PrefillArgs a) {
       // probabilities for k = 8 g4 + e, which stands for key 16 (e / 4) +
       // 4 g4 + e % 4 -- the lane's own scores, in order
       u32x4 bh[kBlocksPerWave], bl[kBlocksPerWave];
-      const bool below = key0 + 2 * kKeys - 1 <= w_minpos;   // below every row's diagonal: no mask
+      const bool below = key0 + 2 * kKeys - 1 <= w_minpos;   // below every row's diagonal
 #pragma unroll
       for (int c = 0; c < kBlocksPerWave; ++c) {
-        // the row's last visible key: keys above it are masked (a select, no branch)
-        const int lim = below ? (ok[c] ? key0 + 2 * kKeys : -1) : pos[c];
+        // raw scores, masked: the scale is positive, so the row max can be
+        // taken before scaling and the scale folded into the exponent's fma
         float x[8];
+        if (below) {                                  // no key past any row's position (rows past n
+#pragma unroll                                        // have zero queries: finite, never written)
+          for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int i = 0; i < 4; ++i) x[4 * h + i] = sa[h][c][i];
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sc = sa[h][c][i] * a.scale_log2;
-            x[4 * h + i] = key0 + 16 * h + 4 * g4 + i <= lim ? sc : -INFINITY;
-          }
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              x[4 * h + i] = key0 + 16 * h + 4 * g4 + i <= pos[c] ? sa[h][c][i] : -INFINITY;
+        }
         float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        bm = max_over_g4(bm);
+        bm = max_over_g4(bm) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(bm > m[c] + kSlack) != 0) {
           const float m_new = fmaxf(m[c], bm);
           const float f = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
@@ -292,15 +319,15 @@ prefill_kernel(PrefillArgs a) {
         const float msub = m[c] == -INFINITY ? 0.f : m[c];
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(x[e] - msub);
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], a.scale_log2, -msub));
         l[c] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint16_t h0 = to16<DT>(p[2 * e]), h1 = to16<DT>(p[2 * e + 1]);
-          hw[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-          lw[e] = static_cast<uint32_t>(to16<DT>(p[2 * e] - from16<DT>(h0))) |
-                  (static_cast<uint32_t>(to16<DT>(p[2 * e + 1] - from16<DT>(h1))) << 16);
+          hw[e] = pack2<DT>(p[2 * e], p[2 * e + 1]);
+          float h0, h1;
+          unpack2f<DT>(hw[e], h0, h1);
+          lw[e] = pack2<DT>(p[2 * e] - h0, p[2 * e + 1] - h1);
         }
         bh[c] = u32x4{hw[0], hw[1], hw[2], hw[3]};
         bl[c] = u32x4{lw[0], lw[1], lw[2], lw[3]};
