@@ -871,6 +871,15 @@ __device__ __forceinline__ void tile_prefix(LenOf lens, int B, int max_len, int3
 
 // A value every lane of the wave holds alike, moved to a scalar register.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni64(int64_t x) {
+  const uint64_t u = static_cast<uint64_t>(x);
+  return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(uni(static_cast<int>(u)))) |
+                              (static_cast<uint64_t>(static_cast<uint32_t>(uni(static_cast<int>(u >> 32)))) << 32));
+}
+struct TileOff8 {
+  int64_t e;   // element (byte) offset of the tile's first code row
+  int64_t s;   // offset of its first scale byte
+};
 
 // Tile ranges: range r starts at tile r*T/W; tile g lies in range owner(g).
 __device__ __forceinline__ int range_start(int64_t r, int T, int W) {
@@ -1199,8 +1208,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   using F = Frag<DT, D>;
   using VT = std::conditional_t<KV8, VTile8, VTile<DT, D>>;
   static_assert(F::kRowK, "stream kernel is for 16-bit queries with D = 128");
-  // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB][S: B + 1][Ls: B]
-  //              [tbl: cap]
+  // dynamic LDS: [K staging: waves x CH tiles x 4 KiB][q: waves x 4 KiB]
+  //              [tile offsets: cap][S: B + 1][Ls: B]
   extern __shared__ uint4 sh_stream[];
   const int wave = uni(threadIdx.x >> 6);    // wave-uniform: keeps all per-job values scalar
   const int lane = threadIdx.x & (kWave - 1);
@@ -1212,9 +1221,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   const int J = R * H;
   uint4* sk = sh_stream + static_cast<int64_t>(wave) * CH * KT;
   uint4* sq = sh_stream + static_cast<int64_t>(nwaves) * CH * KT + static_cast<int64_t>(wave) * 256;
-  int32_t* S = reinterpret_cast<int32_t*>(sh_stream + static_cast<int64_t>(nwaves) * (CH * KT + 256));
+  // per tile of the workgroup: element offset of its first row in the pool
+  // (block * block_stride + row-in-block * D, head offset excluded) and, for
+  // 8-bit KV, the offset of its first scale byte (head excluded)
+  using TileOff = std::conditional_t<KV8, TileOff8, int64_t>;
+  TileOff* tbl = reinterpret_cast<TileOff*>(sh_stream + static_cast<int64_t>(nwaves) * (CH * KT + 256));
+  int32_t* S = reinterpret_cast<int32_t*>(tbl + a.range_cap);
   int32_t* Ls = S + B + 1;
-  int32_t* tbl = Ls + B;
   if (wave == 0) {
     if constexpr (FUSED) tile_prefix([&](int b) { return meta->lens[b]; }, B, a.max_len, S, Ls, lane);
     else tile_prefix([&](int b) { return a.lens[b]; }, B, a.max_len, S, Ls, lane);
@@ -1242,13 +1255,18 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
   for (int t = threadIdx.x; t < w1 - w0; t += blockDim.x) {
     const int g = w0 + t;
     const int b = seq_of_tile(S, B, g);
-    const int lb = ((g - S[b]) * kTile) / bs;
+    const int tok = (g - S[b]) * kTile;
+    const int lb = tok / bs;
     int pb;
     if (FUSED && lb == (Ls[b] - 1) / bs)
       pb = static_cast<int>(meta->slots[b] / bs);   // the new token's block (maybe opened now)
     else
       pb = a.tables[static_cast<int64_t>(b) * a.table_stride + lb];
-    tbl[t] = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+    const int off = tok - lb * bs;
+    const int64_t e = static_cast<int64_t>(pb) * a.block_stride + static_cast<int64_t>(off) * D;
+    if constexpr (KV8) tbl[t] = TileOff8{e, static_cast<int64_t>(pb) * a.sblock_stride + off};
+    else tbl[t] = e;
   }
   __syncthreads();
 
@@ -1272,18 +1290,15 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     const int p0 = back ? x : g0, p1 = back ? g1 : x;
     // the chunk from tile g of sequence b: up to CH tiles, within b and the part
     auto chunk_len = [&](int g, int b) { return min(CH, min(uni(S[b + 1]), p1) - g); };
-    // byte offset of tile g of sequence b (inside the workgroup's tiles)
-    auto tile_bytes = [&](int g, int b_of_g) -> int64_t {
-      const int ti = g - uni(S[b_of_g]);
-      const int off = (ti * kTile) % bs;
-      return (static_cast<int64_t>(uni(tbl[g - w0])) * a.block_stride + head_off +
-              static_cast<int64_t>(off) * D) * EB;
+    // byte offset of tile g (inside the workgroup's tiles) and, for 8-bit
+    // KV, of its first scale byte, from the staged offsets
+    auto tile_bytes = [&](int g) -> int64_t {
+      if constexpr (KV8) return uni64(tbl[g - w0].e) + head_off;
+      else return (uni64(tbl[g - w0]) + head_off) * EB;
     };
-    // 8-bit KV: byte offset of the tile's first scale byte
-    auto tile_scale = [&](int g, int b_of_g) -> int64_t {
-      const int ti = g - uni(S[b_of_g]);
-      return static_cast<int64_t>(uni(tbl[g - w0])) * a.sblock_stride +
-             static_cast<int64_t>(kvh) * a.shead_stride + (ti * kTile) % bs;
+    auto tile_scale = [&](int g) -> int64_t {
+      if constexpr (KV8) return uni64(tbl[g - w0].s) + static_cast<int64_t>(kvh) * a.shead_stride;
+      else return 0;
     };
     // The query group of sequence b, as the MFMA B operand, into the wave's
     // LDS slot by DMA: instruction kk gives lane (g4, c16) head-dims
@@ -1424,8 +1439,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       int nv[CH];
 #pragma unroll
       for (int j = 0; j < CH; ++j) {
-        e[j] = j < n ? tile_bytes(g + j, b) : 0;
-        so[j] = (KV8 && j < n) ? tile_scale(g + j, b) : 0;
+        e[j] = j < n ? tile_bytes(g + j) : 0;
+        so[j] = (KV8 && j < n) ? tile_scale(g + j) : 0;
         nv[j] = nvalid_at(g + j, b);
       }
 #pragma unroll
@@ -1737,7 +1752,8 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   if (tiles_max >= (1LL << 30)) return pl;
   const int64_t cap = (tiles_max + wgs - 1) / wgs + 1;
   const size_t dyn = static_cast<size_t>(waves) * (kStreamChunk + 1) * 4096 +
-                     static_cast<size_t>(2 * num_seqs + 1 + cap) * sizeof(int32_t);
+                     static_cast<size_t>(cap) * sizeof(TileOff8) +   // either entry size fits
+                     static_cast<size_t>(2 * num_seqs + 1) * sizeof(int32_t);
   if (dyn > device_lds_per_block()) return pl;
   pl.ok = true;
   pl.wgs = static_cast<int>(wgs);
