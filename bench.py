@@ -298,8 +298,11 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
     kern_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
     merge_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in timed])
     step_bytes = np.array([kv8(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
-    alg = float(step_bytes[timed].mean())
+    fused = not args.separate_write
+    # the fused launch also writes the B new rows (codes and scale bytes)
+    alg = float(step_bytes[timed].mean()) + (B * row_bytes if fused else 0)
     achieved = alg / (float(kern_ms.mean()) / 1e3) / 1e9
+    kname = "attn_stream8_step_kernel" if fused else "attn_stream8_kernel"
     tps = B * args.steps / wall
     log(f"fp8 KV: {wall * 1e6 / args.steps:.1f} us/step, attention kernel {kern_ms.mean() * 1e3:.1f} us, "
         f"merge {merge_ms.mean() * 1e3:.1f} us, KV {step_bytes.mean() / 1e6:.1f} MB/step")
@@ -312,11 +315,11 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
         "decode_tokens_per_s": round(tps, 1),
         "tokens_per_s_vs_16bit": round(tps / tokens_per_s_16, 3),
         "roofline": {
-            "kernel": f"attn_stream8_kernel<{cfg.dtype} q, D={cfg.head_dim}, "
+            "kernel": f"{kname}<{cfg.dtype} q, D={cfg.head_dim}, "
                       f"G={cfg.num_q_heads // cfg.num_kv_heads}>",
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": recorded_traffic("attn_stream8_kernel", cfg.name)[0],
+            "traffic": recorded_traffic(kname, cfg.name)[0],
             "mean_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
             "algorithmic_bytes_per_launch": round(alg),
         },

@@ -454,9 +454,10 @@ def decode_write_fp8(key, value, slots: np.ndarray, lens: np.ndarray, key_cache,
 
 def decode_step_fp8(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
                     key_scales, value_scales, block_tables, lens_out, scale: float, max_context_len: int,
-                    out=None, workspace=None, stream=None, phase: str = "both"):
+                    out=None, workspace=None, stream=None, phase: str = "both", events=None):
     """pkv_decode_step over 8-bit blocks: key/value [n, H_kv, D] and q
-    [n, H_q, D] in one 16-bit type; slots int64 / lens int32 host arrays."""
+    [n, H_q, D] in one 16-bit type; slots int64 / lens int32 host arrays.
+    ``phase`` and ``events`` as for decode_step."""
     torch = _torch()
     lay = cache_layout(key_cache, value_cache)
     _check_scales(key_cache, key_scales, value_scales)
@@ -473,15 +474,24 @@ def decode_step_fp8(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cach
         if phase != "both":
             raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    st = _lib_handle().pkv_decode_step_fp8(
-        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), key.data_ptr(),
-        value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
-        value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay),
-        block_tables.data_ptr(), block_tables.stride(0), lens_out.data_ptr(), hq, int(max_context_len),
-        float(scale), {"partial": 1, "merge": 2, "both": 3}[phase],
-        None if workspace is None else workspace.data_ptr(),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle(stream))
-    _check(st, "pkv_decode_step_fp8")
+    head = (out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), key.data_ptr(),
+            value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
+            value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay),
+            block_tables.data_ptr(), block_tables.stride(0), lens_out.data_ptr(), hq, int(max_context_len),
+            float(scale))
+    tail = (None if workspace is None else workspace.data_ptr(),
+            0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    fn = _lib_handle().pkv_decode_step_fp8
+    if events is not None:
+        if phase != "both":
+            raise ValueError("events time both phases of one call")
+        _record(events[0], stream)
+        _check(fn(*head, 1, *tail), "pkv_decode_step_fp8")
+        _record(events[1], stream)
+        _check(fn(*head, 2, *tail), "pkv_decode_step_fp8")
+        _record(events[2], stream)
+        return out
+    _check(fn(*head, {"partial": 1, "merge": 2, "both": 3}[phase], *tail), "pkv_decode_step_fp8")
     return out
 
 
@@ -733,13 +743,16 @@ def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, val
 
 def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
                 block_tables, lens_out, scale: float, max_context_len: int, out=None,
-                out_dtype=None, workspace=None, stream=None, phase: str = "both"):
+                out_dtype=None, workspace=None, stream=None, phase: str = "both", events=None):
     """One decode step after the host-side append (see pkv_decode_step): the
     write of key/value [n, H_kv, D] at `slots` (host int64) and the attention
     of q [n, H_q, D] over the updated cache, with lens (host int32, lengths
     after the append) published to lens_out (device int32 [n]) and opened
     blocks to block_tables.  ``phase`` "partial" runs only the first launch
-    and "merge" (same arguments and workspace) only the second."""
+    and "merge" (same arguments and workspace) only the second.  ``events``
+    (three torch.cuda.Event, with phase "both") are recorded on the stream
+    before the first launch, between the two and after the second; the
+    arguments are checked and marshalled once for both launches."""
     torch = _torch()
     lay = cache_layout(key_cache, value_cache)
     n, hq, d = q.shape
@@ -766,18 +779,34 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
         if phase != "both":
             raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
+            _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
+            value_cache.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(), block_tables.stride(0),
+            lens_out.data_ptr(), hq, int(max_context_len), float(scale),
+            None if workspace is None else workspace.data_ptr(),
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            _stream_handle(stream))
+    lib = _lib_handle()
+    if events is not None:
+        if phase != "both":
+            raise ValueError("events time both phases of one call")
+        _record(events[0], stream)
+        _check(lib.pkv_decode_step_partial(*args), "pkv_decode_step_partial")
+        _record(events[1], stream)
+        _check(lib.pkv_decode_step_merge(*args), "pkv_decode_step_merge")
+        _record(events[2], stream)
+        return out
     fn = {"both": "pkv_decode_step", "partial": "pkv_decode_step_partial",
           "merge": "pkv_decode_step_merge"}[phase]
-    st = getattr(_lib_handle(), fn)(
-        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
-        _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
-        value_cache.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(), block_tables.stride(0),
-        lens_out.data_ptr(), hq, int(max_context_len), float(scale),
-        None if workspace is None else workspace.data_ptr(),
-        0 if workspace is None else workspace.numel() * workspace.element_size(),
-        _stream_handle(stream))
-    _check(st, fn)
+    _check(getattr(lib, fn)(*args), fn)
     return out
+
+
+def _record(event, stream):
+    if stream is None:
+        event.record()
+    else:
+        event.record(stream)
 
 
 def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,

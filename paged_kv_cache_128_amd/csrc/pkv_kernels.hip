@@ -32,7 +32,8 @@
 //    (two register stages), so every wave keeps 8 KiB in flight.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
+#include <mutex>
+#include <vector>
 #include <type_traits>
 #include <stdint.h>
 
@@ -1807,21 +1808,27 @@ hipError_t launch_split_d(const AttnArgs& a, int gp, dim3 grid, hipStream_t s) {
 }
 
 // Raises a kernel's dynamic-LDS limit to what a launch asks for (the plan
-// already checked it against the device's per-block LDS), once per device
-// and size.
+// already checked it against the device's per-block LDS), once per kernel,
+// device and size.
 template <typename K>
 hipError_t raise_lds(K kernel, size_t bytes) {
-  static std::atomic<int> raised[64];
+  if (bytes <= 65536) return hipSuccess;
+  struct Raised {
+    const void* fn;
+    int dev;
+    int bytes;
+  };
+  static std::mutex mu;
+  static std::vector<Raised> done;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  std::atomic<int>& done = raised[dev & 63];
-  if (bytes > 65536 && static_cast<int>(bytes) > done.load()) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(bytes));
-    if (e != hipSuccess) return e;
-    done.store(static_cast<int>(bytes));
-  }
+  const void* fn = reinterpret_cast<const void*>(kernel);
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Raised& r : done)
+    if (r.fn == fn && r.dev == dev && r.bytes >= static_cast<int>(bytes)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+  if (e != hipSuccess) return e;
+  done.push_back(Raised{fn, dev, static_cast<int>(bytes)});
   return hipSuccess;
 }
 

@@ -246,14 +246,7 @@ class PagedKVEngine:
                 out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
             args8 = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                      self.key_scales, self.value_scales, self.tables, self.d_lens, scale, max_context_len)
-            if events is None:
-                return decode_step_fp8(*args8, out=out, workspace=ws)
-            events[0].record()
-            decode_step_fp8(*args8, out=out, workspace=ws, phase="partial")
-            events[1].record()
-            decode_step_fp8(*args8, out=out, workspace=ws, phase="merge")
-            events[2].record()
-            return out
+            return decode_step_fp8(*args8, out=out, workspace=ws, events=events)
         if not (fused and self.partition_tokens == 0 and n > 0):
             decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                          block_tables=self.tables, lens_out=self.d_lens)
@@ -263,14 +256,7 @@ class PagedKVEngine:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         args = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                 self.tables, self.d_lens, scale, max_context_len)
-        if events is None:
-            return decode_step(*args, out=out, workspace=ws)
-        events[0].record()
-        decode_step(*args, out=out, workspace=ws, phase="partial")
-        events[1].record()
-        decode_step(*args, out=out, workspace=ws, phase="merge")
-        events[2].record()
-        return out
+        return decode_step(*args, out=out, workspace=ws, events=events)
 
     def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
                out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
