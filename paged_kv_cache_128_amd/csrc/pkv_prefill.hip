@@ -80,6 +80,8 @@ struct PrefillArgs {
   int32_t block_size;
   int32_t hq;
   int32_t group;
+  int32_t num_seqs;
+  int32_t num_qblk;          // 128-row query blocks per sequence (the longest chunk's)
   int32_t max_len;
   int32_t out_dtype;
   float scale_log2;
@@ -160,8 +162,20 @@ prefill_kernel(PrefillArgs a) {
   const int wave = uni(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & (kWave - 1);
   const int g4 = lane >> 4, c16 = lane & 15;
-  const int b = blockIdx.z, qh = blockIdx.y;
-  const int qblk = gridDim.x - 1 - blockIdx.x;        // the longest blocks start first
+  // Workgroup order: the longest query blocks first over the whole launch;
+  // within one block index, consecutive workgroups cycle through the
+  // (sequence, KV head) pairs, and workgroups are handed to the XCDs in
+  // turn, so each pair's query heads share one XCD's L2 (exactly when the
+  // pair count is a multiple of the XCD count) and its K/V tiles, staged by
+  // every one of them, are fetched from HBM about once.
+  const int per_level = a.hq * a.num_seqs;
+  const int qblk = a.num_qblk - 1 - static_cast<int>(blockIdx.x) / per_level;
+  const int rem = static_cast<int>(blockIdx.x) % per_level;
+  const int hkv = a.hq / a.group;
+  const int npairs = a.num_seqs * hkv;
+  const int pair = rem % npairs;
+  const int b = pair / hkv;
+  const int qh = (pair - b * hkv) * a.group + rem / npairs;
   const int r0 = uni(a.q_start[b]);
   const int n = uni(a.q_start[b + 1]) - r0;
   const int Lraw = uni(a.lens[b]);
@@ -418,7 +432,7 @@ extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void*
     return PKV_ERR_HIP;
   if (lds > static_cast<size_t>(lds_max)) return PKV_ERR_UNSUPPORTED;
   const int64_t gx = (static_cast<int64_t>(max_q_len) + kRowsPerWG - 1) / kRowsPerWG;
-  if (gx > 0x7fffffffLL || num_q_heads > 65535 || num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  if (gx * num_q_heads * num_seqs > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
   PrefillArgs a;
   a.q = q;
   a.q_start = q_start;
@@ -437,8 +451,9 @@ extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void*
   a.max_len = max_context_len;
   a.out_dtype = out_dtype;
   a.scale_log2 = scale * kLog2e;
-  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>(num_q_heads),
-                  static_cast<uint32_t>(num_seqs));
+  a.num_seqs = num_seqs;
+  a.num_qblk = static_cast<int32_t>(gx);
+  const dim3 grid(static_cast<uint32_t>(gx * num_q_heads * num_seqs));
   hipStream_t s = static_cast<hipStream_t>(stream);
   const void* fn = l->dtype == PKV_BF16 ? reinterpret_cast<const void*>(&prefill_kernel<PKV_BF16>)
                                         : reinterpret_cast<const void*>(&prefill_kernel<PKV_F16>);
