@@ -9,9 +9,10 @@ import torch
 
 import oracle
 import synth
-from oracle.replay import decode_state, serving_replay
+from oracle import quant
+from oracle.replay import decode_state, replay_churn, serving_replay
 
-from gpu_harness import TORCH_DTYPE, bits_u, engine_for, run_step, to_device
+from gpu_harness import TORCH_DTYPE, bits_u, engine_for, replay_churn_device, run_step, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +105,103 @@ def test_serving_trace_200_steps():
     assert eng.manager.free_list() == mgr.free
     _check_pool(eng, kc, vc)
     _banner(f"serving trace ok, worst sampled err {worst:.2e}")
+
+
+def test_full_size_fp8_decode_step():
+    """The batch-64 workload with an 8-bit pool, in the launch configuration
+    of the bench's 8-bit leg (one fused step: quantising write inside the
+    attention launch, then the merge): tables and lengths as the oracle's
+    manager replay; every stored row of six sampled sequences (codes and
+    scale bytes, the step's new row included) bit for bit as the oracle's
+    quantiser; their attention within 2e-3 of the float64 oracle."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    cfg = synth.CONFIGS["qwen2_7b_b64"]
+    _banner("fp8 batch-64: generating")
+    wl = synth.decode_workload(cfg)
+    B, H, bs, D = len(wl.context_lens), cfg.num_kv_heads, cfg.block_size, cfg.head_dim
+    width = int(-(-int(wl.context_lens.max()) // bs))
+    eng = PagedKVEngine(cfg.num_blocks, H, bs, D, torch.float8_e4m3fn, B, width, wl.initial_free_order,
+                        fill_bits=0, partition_tokens=0, num_q_heads=cfg.num_q_heads)
+    replay_churn_device(eng.manager, wl.churn)
+    eng.prefill_many(list(range(B)), list(range(B)), [int(L) - 1 for L in wl.context_lens],
+                     to_device(np.concatenate(wl.hist_k), cfg.dtype), to_device(np.concatenate(wl.hist_v), cfg.dtype))
+    out = run_step(eng, wl).double().cpu().numpy()
+    _banner("fp8 batch-64: oracle manager replay")
+    om = oracle.BlockManager(cfg.num_blocks, bs, wl.initial_free_order)
+    replay_churn(om, wl.churn)
+    for b in range(B):
+        om.allocate_for_prefill(b, int(wl.context_lens[b]) - 1)
+    om.append_slots_for_decode(list(range(B)))
+    tabs = om.block_tables(list(range(B)), width, -1)
+    assert np.array_equal(eng.tables.cpu().numpy(), tabs)
+    assert np.array_equal(eng.d_lens[:B].cpu().numpy(), om.context_lens(list(range(B))))
+    worst = 0.0
+    for b in _sample(wl.context_lens, 6, cfg.seed):
+        L = int(wl.context_lens[b])
+        nb = -(-L // bs)
+        ids = torch.from_numpy(tabs[b, :nb].astype(np.int64)).cuda()
+        got = []
+        for codes, scales in ((eng.key_cache, eng.key_scales), (eng.value_cache, eng.value_scales)):
+            c = codes[ids].view(torch.uint8).cpu().numpy()                 # [nb, H, bs, D]
+            sc = scales[ids].cpu().numpy()                                  # [nb, H, bs]
+            got.append((c.transpose(1, 0, 2, 3).reshape(H, nb * bs, D)[:, :L],
+                        sc.transpose(1, 0, 2).reshape(H, nb * bs)[:, :L]))
+        want = []
+        for hist, new in ((wl.hist_k[b], wl.new_k[b]), (wl.hist_v[b], wl.new_v[b])):
+            rows = oracle.widen(np.concatenate([hist, new[None]]), cfg.dtype).astype(np.float32)   # [L, H, D]
+            c, sc = quant.quantize_rows(rows)
+            want.append((c.transpose(1, 0, 2), sc.T))
+        for (gc, gs), (wc, ws) in zip(got, want):
+            assert np.array_equal(gc, wc) and np.array_equal(gs, ws), b
+        ref = oracle.contiguous_attention(oracle.widen(wl.q[b], cfg.dtype), quant.dequantize(*want[0]),
+                                          quant.dequantize(*want[1]), cfg.scale)
+        err = float(np.abs(out[b] - ref).max())
+        worst = max(worst, err)
+        assert err <= 2e-3, (b, err)
+    _banner(f"fp8 batch-64: max abs err {worst:.3e}")
+
+
+def test_full_size_prefill():
+    """The bench's prefill launch shape: 8 prompts of 2048 tokens, H 28/4,
+    bf16, each admitted as one chunk through the engine (the kernel's full
+    grid); the pool bit for bit as the oracle write; sampled rows (tile and
+    block edges, seeded picks; all query heads) within 2e-3 of the oracle's
+    prefill attention of that row over its sequence cut at the row."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    cfg = synth.CONFIGS["qwen2_7b_b64"]
+    seqs, prompt = 8, 2048
+    bs, D, hq, hkv = cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
+    per = prompt // bs
+    N = seqs * per + 8
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(N)
+    _banner("prefill 8 x 2048: generating")
+    T = seqs * prompt
+    k = synth.normal(rng, (T, hkv, D), "bf16")
+    v = synth.normal(rng, (T, hkv, D), "bf16")
+    q = synth.normal(rng, (T, hq, D), "bf16")
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    eng = PagedKVEngine(N, hkv, bs, D, torch.bfloat16, seqs, per, order, fill_bits=synth.POISON_BITS["bf16"],
+                        num_q_heads=hq)
+    out = eng.prefill_chunk(list(range(seqs)), list(range(seqs)), [prompt] * seqs, to_device(k, "bf16"),
+                            to_device(v, "bf16"), to_device(q, "bf16"), scale).double().cpu().numpy()
+    _banner("prefill 8 x 2048: oracle")
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc = oracle.new_pool(N, hkv, bs, D, synth.poison_array((), "bf16"))
+    for b in range(seqs):
+        oracle.write_kv(k[b * prompt:(b + 1) * prompt], v[b * prompt:(b + 1) * prompt],
+                        om.allocate_for_prefill(b, prompt), okc, ovc, bs)
+    _check_pool(eng, okc, ovc)
+    tabs = om.block_tables(list(range(seqs)), per, -1)
+    assert np.array_equal(eng.tables.cpu().numpy(), tabs)
+    rows = sorted({0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 129, 255, 1023, 1024, 2046, 2047} |
+                  {int(x) for x in rng.integers(0, prompt, 8)})
+    worst = 0.0
+    for b in sorted({0, seqs - 1, int(rng.integers(1, seqs - 1))}):
+        for i in rows:
+            ref = oracle.prefill_attention(q[b * prompt + i][None], [0, 1], okc, ovc, tabs[b:b + 1], [i + 1],
+                                           scale, "bf16")[0]
+            err = float(np.abs(out[b * prompt + i] - ref).max())
+            worst = max(worst, err)
+            assert err <= 2e-3, (b, i, err)
+    _banner(f"prefill 8 x 2048: max abs err {worst:.3e}")
