@@ -202,12 +202,15 @@ def measure_swap(eng, seqs: int = 8, iters: int = 5):
             "device_to_host_gbps": round(nbytes / (c_us * 1e-6) / 1e9, 1)}
 
 
-def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, seed: int = 2024):
+def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, seed: int = 2024, kv8: bool = False):
     """Full-prompt prefill attention (paged_prefill_attention) with the
     workload's head shape: ``seqs`` prompts of ``prompt`` tokens admitted and
     written through the engine, then the attention launch timed with HIP
     events around ``iters`` back-to-back launches.  Useful FLOPs: row i of a
-    prompt sees i + 1 keys, 4 * D FLOPs per key and query head (Q.K and P.V)."""
+    prompt sees i + 1 keys, 4 * D FLOPs per key and query head (Q.K and P.V).
+    ``kv8``: the same over an 8-bit pool (paged_prefill_attention_fp8: the
+    blocks' dequantisation into the 16-bit staging, then the prefill kernel,
+    both inside each timed launch)."""
     import torch
     from paged_kv_cache_128_amd.engine import PagedKVEngine
     import paged_kv_cache_128_amd as pkv
@@ -215,7 +218,7 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, see
     bs, D, hq, hkv = cfg.block_size, cfg.head_dim, cfg.num_q_heads, cfg.num_kv_heads
     per = -(-prompt // bs)
     g = torch.Generator(device="cuda").manual_seed(seed)
-    eng = PagedKVEngine(seqs * per + 8, hkv, bs, D, tdtype, seqs, per,
+    eng = PagedKVEngine(seqs * per + 8, hkv, bs, D, torch.float8_e4m3fn if kv8 else tdtype, seqs, per,
                         np.random.default_rng(seed).permutation(seqs * per + 8), num_q_heads=hq)
     T = seqs * prompt
     k = torch.randn((T, hkv, D), device="cuda", generator=g).to(tdtype)
@@ -225,22 +228,36 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, see
     out = eng.prefill_chunk(list(range(seqs)), list(range(seqs)), [prompt] * seqs, k, v, q, scale)
     qs = torch.arange(0, T + 1, prompt, dtype=torch.int32, device="cuda")
     lens = torch.full((seqs,), prompt, dtype=torch.int32, device="cuda")
+    if kv8:
+        ws = torch.empty(pkv.prefill_fp8_workspace_size(seqs, prompt, eng.key_cache, eng.value_cache),
+                         dtype=torch.uint8, device="cuda")
+
+        def launch():
+            pkv.paged_prefill_attention_fp8(q, qs, eng.key_cache, eng.value_cache, eng.key_scales,
+                                            eng.value_scales, eng.tables, lens, scale, max_q_len=prompt,
+                                            max_context_len=prompt, out=out, workspace=ws)
+    else:
+        def launch():
+            pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
+                                        max_q_len=prompt, max_context_len=prompt, out=out)
     for _ in range(2):
-        pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
-                                    max_q_len=prompt, max_context_len=prompt, out=out)
+        launch()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
-        pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
-                                    max_q_len=prompt, max_context_len=prompt, out=out)
+        launch()
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / iters
     flops = seqs * (prompt * (prompt + 1) // 2) * hq * 4 * D
     tflops = flops / (us * 1e-6) / 1e12
-    log(f"prefill: {seqs} x {prompt} tokens in {us:.1f} us per launch ({tflops:.0f} TFLOP/s)")
-    return {"kernel": f"prefill_kernel<{cfg.dtype}, D={D}>", "workload": f"{seqs} prompts of {prompt} "
-            f"tokens, H_q={hq} H_kv={hkv}, causal, full prefill", "mean_launch_us": round(us, 2),
+    log(f"prefill{' over 8-bit KV' if kv8 else ''}: {seqs} x {prompt} tokens in {us:.1f} us per launch "
+        f"({tflops:.0f} TFLOP/s)")
+    kname = (f"dequant_blocks_kernel + prefill_kernel<{cfg.dtype}, D={D}>" if kv8
+             else f"prefill_kernel<{cfg.dtype}, D={D}>")
+    return {"kernel": kname, "workload": f"{seqs} prompts of {prompt} "
+            f"tokens, H_q={hq} H_kv={hkv}, causal, full prefill" + (", 8-bit KV pool" if kv8 else ""),
+            "mean_launch_us": round(us, 2),
             "useful_flops_per_launch": flops, "achieved_tflops": round(tflops, 1),
             "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -464,9 +481,11 @@ def main():
     fp8 = None
     if not args.no_fp8 and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
         fp8 = measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s)
-    prefill = None
+    prefill = prefill8 = None
     if not args.no_prefill and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
         prefill = measure_prefill(cfg)
+        if cfg.dtype == "bf16" and not args.no_fp8:
+            prefill8 = measure_prefill(cfg, kv8=True)
 
     import paged_kv_cache_128_amd as pkv
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
@@ -528,6 +547,7 @@ def main():
         "swap_to_host": swap,
         "fp8_kv": fp8,
         "prefill": prefill,
+        "prefill_fp8": prefill8,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)

@@ -514,8 +514,8 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
  *   max_q_len    host, >= every n_b (sizes the grid)
  * Products run on the matrix cores in the cache's 16-bit type with fp32
  * accumulation; P enters P.V as a 16-bit value plus a 16-bit remainder.
- * Supported: 16-bit KV, head_dim 128, block_size a multiple of 16.
- * Errors: INVALID, UNSUPPORTED, HIP.
+ * Supported: 16-bit KV, head_dim 128, block_size a multiple of 16 (8-bit
+ * KV: paged_prefill_attention_fp8).  Errors: INVALID, UNSUPPORTED, HIP.
  */
 int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const int32_t* q_start,
                             const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
@@ -523,6 +523,31 @@ int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const i
                             const pkv_cache_layout* layout, const int32_t* block_tables,
                             int32_t block_table_stride, int32_t num_q_heads,
                             int32_t max_context_len, float scale, void* stream);
+
+/*
+ * Chunked-prefill attention over 8-bit blocks (layout->dtype ==
+ * PKV_FP8_E4M3; scale bytes as in the FP8 section below).  Computes what
+ * paged_prefill_attention computes, with every cached row read back as
+ * decode(code) * 2^(scale byte - 127) ([impl-detail] "实践建议": a block's
+ * KV quantised on its own).  The blocks the sequences hold (the first
+ * ceil(L_b / bs) table entries) are first dequantised into a bf16 staging
+ * pool and table in `workspace` (device, 256-byte aligned, at least
+ * paged_prefill_attention_fp8_workspace_size bytes, owned by the caller,
+ * overwritten), then the 16-bit kernel runs on them.  The staging holds
+ * every read-back value exactly for row scales 2^-124 .. 2^119.  q_dtype
+ * must be PKV_BF16 (bf16 queries; fp16's range cannot hold every 8-bit row:
+ * UNSUPPORTED); out_dtype PKV_F32 or PKV_BF16.  Other arguments as for
+ * paged_prefill_attention.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ */
+size_t paged_prefill_attention_fp8_workspace_size(int32_t num_seqs, int32_t max_context_len,
+                                                  const pkv_cache_layout* layout);
+int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                const int32_t* q_start, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t max_q_len, const void* key_cache, const void* value_cache,
+                                const uint8_t* key_scales, const uint8_t* value_scales,
+                                const pkv_cache_layout* layout, const int32_t* block_tables,
+                                int32_t block_table_stride, int32_t num_q_heads, int32_t max_context_len,
+                                float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------- FP8 KV */
 /*

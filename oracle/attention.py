@@ -37,7 +37,7 @@ def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         a = np.asarray(a, dtype=np.uint16)
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if dtype in ("f16", "f32"):
+    if dtype in ("f16", "f32", "f64"):
         return np.asarray(a).astype(np.float64)
     raise ValueError(dtype)
 

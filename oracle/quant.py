@@ -191,3 +191,15 @@ def decode_attention_fp8(q: np.ndarray, q_dtype: str, key_cache: np.ndarray,
         out[b] = contiguous_attention(widen(q[b], q_dtype), dequantize(kc, ks),
                                       dequantize(vc, vs), scale)
     return out
+
+
+def prefill_attention_fp8(q: np.ndarray, q_dtype: str, q_start: Sequence[int], key_cache: np.ndarray,
+                          value_cache: np.ndarray, key_scales: np.ndarray, value_scales: np.ndarray,
+                          block_tables: np.ndarray, context_lens: Sequence[int], scale: float) -> np.ndarray:
+    """Chunked-prefill attention over FP8 blocks: the causal multi-query
+    attention of attention.prefill_attention ([impl-detail] "分块注意力"),
+    with every cached row read back as decode(code) * 2^e in float64.
+    q [T, H_q, D] in ``q_dtype`` storage.  Returns float64 [T, H_q, D]."""
+    from .attention import prefill_attention, widen
+    return prefill_attention(widen(q, q_dtype), q_start, dequantize(key_cache, key_scales),
+                             dequantize(value_cache, value_scales), block_tables, context_lens, scale, "f64")

@@ -98,6 +98,10 @@ SIGNATURES = {
     "pkv_scatter_blocks": (ctypes.c_int, [_P, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
     "paged_prefill_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _I32, _I32, _P, _P,
                                                ctypes.POINTER(CacheLayout), _P, _I32, _I32, _I32, _F32, _P]),
+    "paged_prefill_attention_fp8_workspace_size": (_SZ, [_I32, _I32, ctypes.POINTER(CacheLayout)]),
+    "paged_prefill_attention_fp8": (ctypes.c_int, [_P, _I32, _P, _I32, _P, _P, _I32, _I32, _P, _P, _P, _P,
+                                                   ctypes.POINTER(CacheLayout), _P, _I32, _I32, _I32, _F32, _P,
+                                                   _SZ, _P]),
     "pkv_block_ref_count": (_I32, [_P, _I32]),
     "pkv_take_block_copies": (ctypes.c_int, [_P, _PI32, _PI32, _I32, _PI32]),
     "pkv_copy_blocks": (ctypes.c_int, [_PI32, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
@@ -567,6 +571,52 @@ def paged_prefill_attention(q, q_start, key_cache, value_cache, block_tables, co
     return out
 
 
+def prefill_fp8_workspace_size(num_seqs: int, max_context_len: int, key_cache, value_cache) -> int:
+    """Bytes of the caller-owned staging paged_prefill_attention_fp8 needs."""
+    lay = cache_layout(key_cache, value_cache)
+    return int(_lib_handle().paged_prefill_attention_fp8_workspace_size(int(num_seqs), int(max_context_len),
+                                                                        ctypes.byref(lay)))
+
+
+def paged_prefill_attention_fp8(q, q_start, key_cache, value_cache, key_scales, value_scales, block_tables,
+                                context_lens, scale: float, max_q_len: int, max_context_len: Optional[int] = None,
+                                out=None, out_dtype=None, workspace=None, stream=None):
+    """Chunked-prefill causal attention over 8-bit blocks (see
+    paged_prefill_attention_fp8 in pkv.h): bf16 q [T, H_q, D]; the other
+    tensors as for paged_prefill_attention; ``workspace`` (uint8 device
+    tensor, allocated here when None) holds the 16-bit staging."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    _check_scales(key_cache, key_scales, value_scales)
+    T, hq, d = q.shape
+    B = context_lens.shape[0]
+    if d != lay.head_dim or q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be contiguous bf16 [T, H_q, head_dim]")
+    if q_start.dtype != torch.int32 or q_start.shape != (B + 1,) or not q_start.is_contiguous():
+        raise ValueError("q_start must be contiguous int32 [B + 1]")
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [B]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] < B \
+            or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be int32 [>= B, W] with unit column stride")
+    if max_context_len is None:
+        max_context_len = block_tables.shape[1] * lay.block_size
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32 if out_dtype is None else out_dtype,
+                          device=q.device)
+    need = prefill_fp8_workspace_size(B, max_context_len, key_cache, value_cache)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = _lib_handle().paged_prefill_attention_fp8(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), q_start.data_ptr(),
+        context_lens.data_ptr(), B, int(max_q_len), key_cache.data_ptr(), value_cache.data_ptr(),
+        key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(),
+        block_tables.stride(0), hq, int(max_context_len), float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    _check(st, "paged_prefill_attention_fp8")
+    return out
+
+
 def new_pool(num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int, dtype,
              device="cuda", fill_bits: Optional[int] = None):
     """Allocate one interleaved pool [N, 2, H_kv, bs, D] and return
@@ -888,6 +938,7 @@ __all__ = [
     "copy_blocks", "gather_blocks", "scatter_blocks", "copy_blocks_fp8", "gather_blocks_fp8",
     "scatter_blocks_fp8", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
     "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention", "decode_step_fp8",
+    "paged_prefill_attention_fp8", "prefill_fp8_workspace_size",
     "cache_layout", "load_library",
     "version", "dtype_code", "PKV_F32", "PKV_F16", "PKV_BF16", "SIGNATURES",
 ]

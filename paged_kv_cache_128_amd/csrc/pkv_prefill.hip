@@ -400,13 +400,12 @@ prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
-extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void* q,
-                                       const int32_t* q_start, const int32_t* context_lens,
-                                       int32_t num_seqs, int32_t max_q_len, const void* key_cache,
-                                       const void* value_cache, const pkv_cache_layout* l,
-                                       const int32_t* block_tables, int32_t block_table_stride,
-                                       int32_t num_q_heads, int32_t max_context_len, float scale,
-                                       void* stream) {
+namespace {
+
+int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_start, const int32_t* context_lens,
+               int32_t num_seqs, int32_t max_q_len, const void* key_cache, const void* value_cache,
+               const pkv_cache_layout* l, const int32_t* block_tables, int32_t block_table_stride,
+               int32_t num_q_heads, int32_t max_context_len, float scale, void* stream) {
   if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 ||
       max_context_len < 0 || block_table_stride < 0)
     return PKV_ERR_INVALID;
@@ -466,3 +465,167 @@ extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void*
     hipLaunchKernelGGL(prefill_kernel<PKV_F16>, grid, dim3(kWave * kWavesPF), lds, s, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
+
+// 8-bit blocks for prefill: one workgroup per (sequence b, logical block j,
+// K or V, KV head) writes that head's rows of block tables[b][j], read back
+// as decode(code) * 2^(scale byte - 127), into 16-bit staging block
+// b * W + j, and workgroup (b, j, K, head 0) writes that block's id into
+// the staging table [B, W]; blocks past a sequence's length are skipped.
+struct DequantArgs {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const uint8_t* ks;
+  const uint8_t* vs;
+  const int32_t* tables;
+  const int32_t* lens;
+  uint16_t* staging;        // [B * W, 2, H, bs, D] bf16
+  int32_t* table_out;       // [B, W]
+  int64_t block_stride;     // elements (= bytes) of the code pool
+  int64_t head_stride;
+  int64_t sblock_stride;    // scale bytes
+  int64_t shead_stride;
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t heads;
+  int32_t width;            // W
+  int32_t max_len;
+};
+
+__global__ void __launch_bounds__(256)
+dequant_blocks_kernel(DequantArgs a) {
+  int64_t item = blockIdx.x;
+  const int h = static_cast<int>(item % a.heads);
+  item /= a.heads;
+  const int half = static_cast<int>(item % 2);
+  item /= 2;
+  const int j = static_cast<int>(item % a.width);
+  const int b = static_cast<int>(item / a.width);
+  const int bs = a.block_size;
+  const int Lraw = a.lens[b];
+  const int L = Lraw < 0 ? 0 : (Lraw > a.max_len ? a.max_len : Lraw);
+  if (j >= (L + bs - 1) / bs) return;
+  int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + j];
+  pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+  const int64_t dst = static_cast<int64_t>(b) * a.width + j;
+  if (half == 0 && h == 0 && threadIdx.x == 0) a.table_out[dst] = static_cast<int32_t>(dst);
+  const uint8_t* codes = (half == 0 ? a.kc : a.vc) + pb * a.block_stride + h * a.head_stride;
+  const uint8_t* scales = (half == 0 ? a.ks : a.vs) + pb * a.sblock_stride + h * a.shead_stride;
+  uint16_t* o = a.staging + ((dst * 2 + half) * a.heads + h) * static_cast<int64_t>(bs) * kD;
+  // eight codes per thread: row (8 i) / D, columns 8 i % D .. + 7
+  for (int i = threadIdx.x; i < bs * kD / 8; i += blockDim.x) {
+    const int r = (8 * i) / kD;
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + static_cast<int64_t>(r) * kD + (8 * i) % kD);
+    const int e = static_cast<int>(scales[r]) - 127;
+    // the hardware E4M3 conversion: bytes 0-1 (false) or 2-3 (true) of a word
+    const f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.x), false),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.x), true),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.y), false),
+                        __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.y), true)};
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      packed[k] = pack2<PKV_BF16>(__builtin_amdgcn_ldexpf(v[k].x, e), __builtin_amdgcn_ldexpf(v[k].y, e));
+    *reinterpret_cast<uint4*>(o + 8 * static_cast<int64_t>(i)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  }
+}
+
+// Staging size for num_seqs sequences of up to max_context_len tokens:
+// W = ceil(max_context_len / bs) blocks each (16-bit K and V of every head)
+// plus the [B, W] table.
+size_t fp8_staging_bytes(int32_t num_seqs, int32_t max_context_len, const pkv_cache_layout* l) {
+  const int64_t W = (static_cast<int64_t>(max_context_len) + l->block_size - 1) / l->block_size;
+  const int64_t blocks = static_cast<int64_t>(num_seqs) * W;
+  const int64_t block_bytes = 2LL * l->num_kv_heads * l->block_size * l->head_dim * 2;
+  const int64_t table_off = (blocks * block_bytes + 255) / 256 * 256;
+  return static_cast<size_t>(table_off + blocks * 4);
+}
+
+}  // namespace
+
+extern "C" int paged_prefill_attention(void* out, int32_t out_dtype, const void* q,
+                                       const int32_t* q_start, const int32_t* context_lens,
+                                       int32_t num_seqs, int32_t max_q_len, const void* key_cache,
+                                       const void* value_cache, const pkv_cache_layout* l,
+                                       const int32_t* block_tables, int32_t block_table_stride,
+                                       int32_t num_q_heads, int32_t max_context_len, float scale,
+                                       void* stream) {
+  if (pkv::check_layout(l) == PKV_OK && l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  return prefill_16(out, out_dtype, q, q_start, context_lens, num_seqs, max_q_len, key_cache, value_cache, l,
+                    block_tables, block_table_stride, num_q_heads, max_context_len, scale, stream);
+}
+
+extern "C" size_t paged_prefill_attention_fp8_workspace_size(int32_t num_seqs, int32_t max_context_len,
+                                                            const pkv_cache_layout* l) {
+  if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || max_context_len < 0) return 0;
+  return fp8_staging_bytes(num_seqs, max_context_len, l);
+}
+
+extern "C" int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,
+                                           const int32_t* q_start, const int32_t* context_lens, int32_t num_seqs,
+                                           int32_t max_q_len, const void* key_cache, const void* value_cache,
+                                           const uint8_t* key_scales, const uint8_t* value_scales,
+                                           const pkv_cache_layout* l, const int32_t* block_tables,
+                                           int32_t block_table_stride, int32_t num_q_heads, int32_t max_context_len,
+                                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 ||
+      max_context_len < 0 || block_table_stride < 0)
+    return PKV_ERR_INVALID;
+  if (l->dtype != PKV_FP8_E4M3 || q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (l->head_dim != kD || l->block_size % kKeys != 0) return PKV_ERR_UNSUPPORTED;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
+    return PKV_ERR_INVALID;
+  if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !key_scales || !value_scales || !context_lens ||
+      (max_context_len > 0 && !block_tables))
+    return PKV_ERR_INVALID;
+  if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) % 8) != 0 ||
+      l->head_stride % 8 != 0 || l->block_stride % 8 != 0)
+    return PKV_ERR_UNSUPPORTED;
+  const size_t need = fp8_staging_bytes(num_seqs, max_context_len, l);
+  if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return PKV_ERR_WORKSPACE;
+  const int32_t W = (max_context_len + l->block_size - 1) / l->block_size;
+  const int64_t blocks = static_cast<int64_t>(num_seqs) * W;
+  const int64_t block_elems = 2LL * l->num_kv_heads * l->block_size * l->head_dim;
+  if (blocks > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  uint16_t* staging = static_cast<uint16_t*>(workspace);
+  int32_t* table_out = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                  (blocks * block_elems * 2 + 255) / 256 * 256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (blocks > 0) {
+    DequantArgs d;
+    d.kc = static_cast<const uint8_t*>(key_cache);
+    d.vc = static_cast<const uint8_t*>(value_cache);
+    d.ks = key_scales;
+    d.vs = value_scales;
+    d.tables = block_tables;
+    d.lens = context_lens;
+    d.staging = staging;
+    d.table_out = table_out;
+    d.block_stride = l->block_stride;
+    d.head_stride = l->head_stride;
+    d.sblock_stride = l->block_stride / l->head_dim;
+    d.shead_stride = l->head_stride / l->head_dim;
+    d.table_stride = block_table_stride;
+    d.num_blocks = l->num_blocks;
+    d.block_size = l->block_size;
+    d.heads = l->num_kv_heads;
+    d.width = W;
+    d.max_len = max_context_len;
+    const int64_t grid = blocks * 2 * l->num_kv_heads;
+    if (grid > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(dequant_blocks_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s, d);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  pkv_cache_layout sl = *l;
+  sl.num_blocks = static_cast<int32_t>(blocks > 0 ? blocks : 1);
+  sl.dtype = PKV_BF16;
+  sl.block_stride = block_elems;
+  sl.head_stride = static_cast<int64_t>(l->block_size) * l->head_dim;
+  return prefill_16(out, out_dtype, q, q_start, context_lens, num_seqs, max_q_len, staging,
+                    staging + static_cast<int64_t>(l->num_kv_heads) * l->block_size * l->head_dim, &sl,
+                    table_out, W, num_q_heads, max_context_len, scale, stream);
+}
+

@@ -36,7 +36,8 @@ from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_st
                decode_write_fp8,
                gather_blocks, scatter_blocks, copy_blocks_fp8, gather_blocks_fp8, scatter_blocks_fp8,
                new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
-               paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, workspace_size)
+               paged_kv_write, paged_kv_write_fp8, paged_prefill_attention, paged_prefill_attention_fp8,
+               prefill_fp8_workspace_size, workspace_size)
 
 
 class PagedKVEngine:
@@ -70,6 +71,7 @@ class PagedKVEngine:
         self.lens = np.empty(max_rows, dtype=np.int32)       # last step's lengths (host)
         self._newb = np.empty(max_rows, dtype=np.int32)
         self._ws = None
+        self._pf_ws = None         # 16-bit staging of 8-bit prefill
         self._nq = num_q_heads
         self._sharing = False      # set once any table shares a block
 
@@ -94,9 +96,8 @@ class PagedKVEngine:
         (pkv_append_tokens); the chunks' K/V rows ([sum(chunk_lens), H_kv, D],
         concatenated in order) are written, then every chunk's query rows
         (q [sum(chunk_lens), H_q, D]) attend causally over their sequence
-        (paged_prefill_attention).  Returns out [sum(chunk_lens), H_q, D]."""
-        if self.fp8:
-            raise NotImplementedError("prefill attention reads 16-bit KV blocks")
+        (paged_prefill_attention; over an 8-bit pool paged_prefill_attention_fp8,
+        bf16 q).  Returns out [sum(chunk_lens), H_q, D]."""
         all_slots, lens = [], []
         for sid, row, n in zip(seq_ids, rows, chunk_lens):
             sid, n = int(sid), int(n)
@@ -117,9 +118,17 @@ class PagedKVEngine:
         d_qs = torch.from_numpy(q_start).to(self.device)
         d_lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(self.device)
         tables = self.tables[torch.as_tensor(list(rows), dtype=torch.long, device=self.device)]
+        max_q = int(max(chunk_lens)) if B else 0
+        max_len = int(max(lens)) if B else 0
+        if self.fp8:
+            need = prefill_fp8_workspace_size(B, max_len, self.key_cache, self.value_cache)
+            if self._pf_ws is None or self._pf_ws.numel() < need:
+                self._pf_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.device)
+            return paged_prefill_attention_fp8(q, d_qs, self.key_cache, self.value_cache, self.key_scales,
+                                               self.value_scales, tables, d_lens, scale, max_q_len=max_q,
+                                               max_context_len=max_len, out=out, workspace=self._pf_ws)
         return paged_prefill_attention(q, d_qs, self.key_cache, self.value_cache, tables, d_lens, scale,
-                                       max_q_len=int(max(chunk_lens)) if B else 0,
-                                       max_context_len=int(max(lens)) if B else 0, out=out)
+                                       max_q_len=max_q, max_context_len=max_len, out=out)
 
     def _run_copies(self):
         """Copy-on-write: the block copies the manager queued, on the stream,

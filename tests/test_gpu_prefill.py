@@ -5,6 +5,8 @@ over history written by earlier launches), ragged chunk lengths spanning
 several 64-row workgroups and a ragged tail, GQA groups 7 and 4, both 16-bit
 types and both output types; plus rows placed before the first position
 (zeros), empty chunks, and a one-row chunk against the decode kernel."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -90,3 +92,70 @@ def test_prefill_edge_cases():
                                      0.088, max_context_len=48)
     torch.cuda.synchronize()
     assert (dec[0] - out[14]).abs().max().item() <= 2e-3
+
+
+@pytest.mark.parametrize("hq,hkv,bs,out_dtype", [(28, 4, 16, None), (12, 2, 32, "bf16")])
+def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype):
+    """Chunked prefill over an 8-bit pool (paged_prefill_attention_fp8:
+    the sequences' blocks dequantised into the 16-bit staging, then the
+    prefill kernel): the quantising writes bit for bit (codes and scale
+    bytes, poison included) and the attention within 2e-3 of the oracle's
+    8-bit prefill attention, over two chunks per sequence."""
+    from oracle import quant
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    _banner(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} out={out_dtype}")
+    rng = np.random.default_rng(90 + hq)
+    D = 128
+    first = [1, 37, 64, 130, 200, 5]
+    second = [3, 64, 1, 77, 0, 150]
+    B = len(first)
+    tot = [a + b for a, b in zip(first, second)]
+    N = sum(-(-t // bs) for t in tot) + 8
+    order = rng.permutation(N)
+    width = max(-(-t // bs) for t in tot)
+    eng = PagedKVEngine(N, hkv, bs, D, torch.float8_e4m3fn, B, width, order, fill_bits=0, num_q_heads=hq)
+    om = oracle.BlockManager(N, bs, order)
+    o = quant.new_fp8_pool(N, hkv, bs, D)
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    od = None if out_dtype is None else TORCH_DTYPE[out_dtype]
+    for chunk in (first, second):
+        T = sum(chunk)
+        k = synth.normal(rng, (T, hkv, D), "bf16")
+        v = synth.normal(rng, (T, hkv, D), "bf16")
+        q = synth.normal(rng, (T, hq, D), "bf16")
+        slots = []
+        for b, n in enumerate(chunk):
+            slots += (om.append_tokens(b, n) if om.is_live(b) else om.allocate_for_prefill(b, n))
+        quant.write_kv_fp8(oracle.widen(k, "bf16").astype(np.float32), oracle.widen(v, "bf16").astype(np.float32),
+                           slots, *o, bs)
+        qs = np.concatenate([[0], np.cumsum(chunk)])
+        ref = quant.prefill_attention_fp8(q, "bf16", qs, *o, om.block_tables(list(range(B)), width, -1),
+                                          om.context_lens(list(range(B))), scale)
+        out = None if od is None else torch.empty((T, hq, D), dtype=od, device="cuda")
+        got = eng.prefill_chunk(list(range(B)), list(range(B)), chunk, to_device(k, "bf16"),
+                                to_device(v, "bf16"), to_device(q, "bf16"), scale, out=out)
+        torch.cuda.synchronize()
+        for g, w in zip((eng.key_cache, eng.value_cache, eng.key_scales, eng.value_scales), o):
+            assert np.array_equal(g.contiguous().view(torch.uint8).cpu().numpy(), w)
+        err = np.abs(got.double().cpu().numpy() - ref).max()
+        tol = 2e-3 if od is None else 2e-3 + np.abs(ref).max() * 2.0 ** -8
+        _banner(f"fp8 prefill chunk {chunk}: max abs err {err:.3e}")
+        assert err <= tol, err
+
+
+def test_fp8_prefill_refuses_f16_queries_and_small_workspace():
+    """Host-side checks of paged_prefill_attention_fp8: fp16 queries are
+    UNSUPPORTED (fp16 cannot hold every 8-bit row), a short workspace is a
+    WORKSPACE error; nothing is launched."""
+    lib = pkv.load_library()
+    N, H, bs, D = 8, 2, 16, 128
+    g = pkv.new_fp8_pool(N, H, bs, D, "cuda")
+    lay = pkv.cache_layout(g[1], g[2])
+    fake = g[0].data_ptr()
+    need = lib.paged_prefill_attention_fp8_workspace_size(2, 64, ctypes.byref(lay))
+    assert need >= 2 * 4 * 2 * H * bs * D * 2
+    args = lambda qd, ws, wsb: lib.paged_prefill_attention_fp8(
+        fake, pkv.PKV_F32, fake, qd, fake, fake, 2, 16, g[1].data_ptr(), g[2].data_ptr(), g[4].data_ptr(),
+        g[5].data_ptr(), ctypes.byref(lay), fake, 4, 4, 64, 0.1, ws, wsb, None)
+    assert args(pkv.PKV_F16, fake, need) == -5
+    assert args(pkv.PKV_BF16, fake, need - 1) == -7

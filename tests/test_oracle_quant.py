@@ -192,3 +192,55 @@ def test_fp8_swap_staging_round_trip():
     for (wk, wv), b in zip(want, dst):
         assert np.array_equal(quant.dequantize(kc[b], ks[b]), wk)
         assert np.array_equal(quant.dequantize(vc[b], vs[b]), wv)
+
+
+def _fp8_prefill_case(seed):
+    rng = np.random.default_rng(seed)
+    N, H, bs, D, hq = 24, 2, 4, 16, 6
+    kc, vc, ks, vs = quant.new_fp8_pool(N, H, bs, D)
+    order = rng.permutation(N)
+    mgr = oracle.BlockManager(N, bs, order)
+    lens = [13, 5, 9]
+    for b, L in enumerate(lens):
+        rows_k = (rng.standard_normal((L, H, D)) * 2.0 ** rng.integers(-4, 5, (L, H, 1))).astype(np.float32)
+        rows_v = (rng.standard_normal((L, H, D)) * 2.0 ** rng.integers(-4, 5, (L, H, 1))).astype(np.float32)
+        quant.write_kv_fp8(rows_k, rows_v, mgr.allocate_for_prefill(b, L), kc, vc, ks, vs, bs)
+    tables = mgr.block_tables([0, 1, 2], 4, -1)
+    return rng, (kc, vc, ks, vs), tables, lens, hq, D
+
+
+def test_fp8_prefill_one_row_chunks_equal_fp8_decode():
+    """A one-row chunk (the row at the last position sees every key) is
+    decode attention: the 8-bit prefill oracle equals the 8-bit decode
+    oracle there."""
+    rng, pool, tables, lens, hq, D = _fp8_prefill_case(21)
+    q = np.asarray(rng.standard_normal((3, hq, D)), dtype=np.float32).astype(np.float16)
+    pre = quant.prefill_attention_fp8(q, "f16", [0, 1, 2, 3], *pool, tables, lens, 0.3)
+    dec = quant.decode_attention_fp8(q, "f16", *pool, tables, lens, 0.3)
+    np.testing.assert_allclose(pre, dec, rtol=0, atol=1e-13)
+
+
+def test_fp8_prefill_equals_16bit_prefill_on_the_read_back_values():
+    """On a 16-bit pool holding exactly the read-back values (every one is a
+    bf16 number here: E4M3 codes times 2^e), the 8-bit prefill oracle equals
+    the 16-bit prefill oracle; reading K's scale bytes for V fails."""
+    rng, (kc, vc, ks, vs), tables, lens, hq, D = _fp8_prefill_case(22)
+    kd, vd = quant.dequantize(kc, ks), quant.dequantize(vc, vs)
+    written = np.isfinite(kd)
+    as_bf16 = []
+    for x in (kd, vd):
+        f = np.where(np.isfinite(x), x, 0.0).astype(np.float32)
+        assert np.array_equal(f.astype(np.float64), np.where(np.isfinite(x), x, 0.0))
+        bits = f.view(np.uint32)
+        assert not np.any(bits & 0xFFFF), "read-back values must be bf16 numbers"
+        as_bf16.append((bits >> 16).astype(np.uint16))
+    assert written.any()
+    n = [2, 5, 9]                                      # chunk rows: the last n_b positions
+    q = np.asarray(rng.standard_normal((sum(n), hq, D)), dtype=np.float32)
+    qb = (q.view(np.uint32) >> 16).astype(np.uint16)   # bf16 queries by truncation (exact values)
+    q_start = np.concatenate([[0], np.cumsum(n)])
+    got = quant.prefill_attention_fp8(qb, "bf16", q_start, kc, vc, ks, vs, tables, lens, 0.25)
+    want = oracle.prefill_attention(qb, q_start, as_bf16[0], as_bf16[1], tables, lens, 0.25, "bf16")
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+    bad = quant.prefill_attention_fp8(qb, "bf16", q_start, kc, vc, ks, ks, tables, lens, 0.25)
+    assert np.abs(bad - want).max() > 1e-3
