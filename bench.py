@@ -202,11 +202,11 @@ def measure_swap(eng, seqs: int = 8, iters: int = 5):
             "device_to_host_gbps": round(nbytes / (c_us * 1e-6) / 1e9, 1)}
 
 
-def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, seed: int = 2024, kv8: bool = False):
+def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, seed: int = 2024, kv8: bool = False):
     """Full-prompt prefill attention (paged_prefill_attention) with the
     workload's head shape: ``seqs`` prompts of ``prompt`` tokens admitted and
     written through the engine, then the attention launch timed with HIP
-    events around ``iters`` back-to-back launches.  Useful FLOPs: row i of a
+    events around ``iters`` back-to-back launches after five untimed ones.  Useful FLOPs: row i of a
     prompt sees i + 1 keys, 4 * D FLOPs per key and query head (Q.K and P.V).
     ``kv8``: the same over an 8-bit pool (paged_prefill_attention_fp8: the
     blocks' dequantisation into the 16-bit staging, then the prefill kernel,
@@ -240,7 +240,7 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 10, see
         def launch():
             pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
                                         max_q_len=prompt, max_context_len=prompt, out=out)
-    for _ in range(2):
+    for _ in range(5):                     # warm-up: the clocks settle under the matrix-core load
         launch()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
