@@ -1058,6 +1058,93 @@ __device__ __forceinline__ void acc_zero(Acc8& x) {
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Max over the lanes c16, c16 + 16, c16 + 32, c16 + 48 (every lane gets it)
+// on the vector ALU: the 16-lane row swap pairs rows (0, 1) and (2, 3), the
+// 32-lane half swap pairs the halves.
+__device__ __forceinline__ float max_over_g4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ int max_over_g4(int x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  x = max(static_cast<int>(a[0]), static_cast<int>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  return max(static_cast<int>(b[0]), static_cast<int>(b[1]));
+}
+
+// P.V of the 16-bit stream kernel on the matrix cores (false: on the vector
+// ALU with DPP broadcasts, softmax_pv above).
+constexpr bool kMfmaPV16 = true;
+
+// Two values as a packed pair of the 16-bit type (element 0 low), rounded
+// to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack16x2(float x0, float x1) {
+  if constexpr (DT == PKV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x0, x1}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)});
+}
+
+// Online softmax + P.V for one 16-bit tile with P.V on the matrix cores:
+// O^T[d][h] += V^T P^T as eight 16x16x16 MFMAs.  MFMA j maps its row index c
+// to head-dim 8 c + j, so its A operand is element j of the lane's V rows
+// 4 g4 .. 4 g4 + 3 (head-dims 8 c16 .. + 7, as loaded), and its B operand is
+// the score layout (head c16, tokens 4 g4 ..) as it leaves Q.K.  P enters as
+// a 16-bit value plus its 16-bit remainder (two MFMAs, P to about 2^-17).
+// The accumulator is the 8-bit path's (eref 0): lane (g4, c16) ends with
+// head c16's head-dims 32 g4 .. 32 g4 + 31.
+template <int DT>
+__device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128>& t, int nvalid,
+                                              float scale_log2, float& m, float& l, Acc8& acc, int lane) {
+  const int g4 = lane >> 4;
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (4 * g4 + r < nvalid) ? s[r] * scale_log2 : -INFINITY;
+  const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
+    const float m_new = fmaxf(m, bm);
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head; 0 on the first tile
+    l *= a;
+    m = m_new;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc.c[j] *= a;
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);   // masked tokens: 0
+  l += (p[0] + p[1]) + (p[2] + p[3]);
+  const uint32_t h01 = pack16x2<DT>(p[0], p[1]), h23 = pack16x2<DT>(p[2], p[3]);
+  float q0, q1, q2, q3;
+  unpack2<DT>(h01, q0, q1);
+  unpack2<DT>(h23, q2, q3);
+  const u32x2 bh = {h01, h23};
+  const u32x2 bl = {pack16x2<DT>(p[0] - q0, p[1] - q1), pack16x2<DT>(p[2] - q2, p[3] - q3)};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    const int w = j >> 1;
+    const u32x2 av = {__builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel),
+                      __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel)};
+    if constexpr (DT == PKV_BF16) {
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                           __builtin_bit_cast(i16x4, bh), acc.c[j], 0, 0, 0);
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                           __builtin_bit_cast(i16x4, bl), acc.c[j], 0, 0, 0);
+    } else {
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                       __builtin_bit_cast(f16x4, bh), acc.c[j], 0, 0, 0);
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                       __builtin_bit_cast(f16x4, bl), acc.c[j], 0, 0, 0);
+    }
+  }
+}
 
 // Online softmax + P.V for one 8-bit tile: the score of token t is the code
 // dot product times 2^ek(t) (into the exp2 argument's factor), the V row of
@@ -1078,12 +1165,8 @@ __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int 
     x[r] = valid ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
     if (valid) evm = max(evm, ev[r]);
   }
-  float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
-  evm = max(evm, __shfl_xor(evm, 16));
-  evm = max(evm, __shfl_xor(evm, 32));
-  evm = uni(evm);                                  // the same in every lane
+  const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  evm = uni(max_over_g4(evm));                     // the same in every lane
   const bool grow = bm > m + kSlack;
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
     const float m_new = fmaxf(m, bm);
@@ -1469,8 +1552,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       fetch_new(cs, cn, bc);
       int seg_lo = cs, seg_hi = cs + cn;    // tiles of the current segment
       float m = -INFINITY, l = 0.f;
-      std::conditional_t<KV8, Acc8, AccV<GP>> acc;
-      acc_zero(acc);
+      constexpr bool MPV = !KV8 && kMfmaPV16;
+      std::conditional_t<KV8 || MPV, Acc8, AccV<GP>> acc;
+      auto acc_init = [&]() {
+        acc_zero(acc);
+        if constexpr (MPV) acc.eref = 0;             // 16-bit P.V: no V scale
+      };
+      acc_init();
       // Per chunk: wait for its DMA (and its query group); scores from the K
       // rows in LDS; then the next chunk's fetch (V into `vnext`) and, when
       // that chunk is in another sequence, its query group into LDS; then
@@ -1507,6 +1595,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
           if (j < cn) {
             if constexpr (KV8)
               softmax_pv8(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
+            else if constexpr (MPV)
+              softmax_pv16m<DT>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc, lane);
             else
               softmax_pv<DT, D, GP>(scr[j], vcur[j], nvalid_at(cs + j, bc), a.scale_log2, m, l, acc.a, lane);
           }
@@ -1516,14 +1606,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
           const int slot = back ? (seg_hi == g1 ? 2 : 3) : (seg_lo == g0 ? 0 : 1);
           const int64_t orow = static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G;
           const int64_t wrow = (rng * kStreamSlots + slot) * a.hq + static_cast<int64_t>(kvh) * G;
-          if constexpr (KV8)
+          if constexpr (KV8 || MPV)
             wave_epilogue8(m, l, acc, lane, G, complete, a.out, a.out_dtype, orow, a.ws_acc, a.ws_ml, wrow);
           else
             wave_epilogue<DT, D, GP>(m, l, acc.a, lane, G, complete, a.out, a.out_dtype, orow,
                                      a.ws_acc, a.ws_ml, wrow, 1);
           m = -INFINITY;
           l = 0.f;
-          acc_zero(acc);
+          acc_init();
           seg_lo = ns;
           seg_hi = ns + nn;
         } else {
@@ -1870,8 +1960,8 @@ hipError_t launch_stream_t(const StreamArgs& a, const StreamPlan& pl, const Step
 template <int DT, bool KV8 = false>
 hipError_t launch_stream_dt(const StreamArgs& a, int gp, const StreamPlan& pl, const StepMeta* meta,
                             hipStream_t s) {
-  // the 8-bit path's P.V covers 16 heads on the matrix cores whatever G is
-  if constexpr (KV8) {
+  // P.V on the matrix cores covers 16 heads whatever G is
+  if constexpr (KV8 || kMfmaPV16) {
     return launch_stream_t<DT, 8, KV8>(a, pl, meta, s);
   } else {
     switch (gp) {
