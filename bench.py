@@ -20,6 +20,10 @@ new rows written when the write runs inside it) over its mean duration from
 HIP events recorded on the launch stream around it on every fifth timed
 step.
 
+``--config serving_trace`` runs the serving-trace workload instead (its
+own JSON line: the trace's 200 decode steps with per-step finishes and
+refills; see measure_serving).
+
     python bench.py [--steps K] [--warmup W] [--config NAME]
     python bench.py --calibrate-copy      # plain 1 GiB copy, for PMC scaling
 """
@@ -177,6 +181,7 @@ def measure_swap(eng, seqs: int = 8, iters: int = 5):
     of the blocks) and device-to-host GB/s."""
     import torch
     import paged_kv_cache_128_amd as pkv
+    seqs = min(seqs, len(eng.row_seq))
     ids = np.concatenate([np.array(eng.manager.block_table(s), dtype=np.int32) for s in range(seqs)])
     block_bytes = 2 * eng.num_kv_heads * eng.block_size * eng.head_dim * eng.pool.element_size()
     staged = pkv.gather_blocks(ids, eng.key_cache, eng.value_cache)
@@ -262,6 +267,81 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, see
             "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "prefill_tokens_per_s": round(seqs * prompt / (us * 1e-6), 1)}
+
+
+def measure_serving(cfg, args):
+    """The serving-trace workload (``--config serving_trace``): 256 rows
+    prefilled with their prompts, then the trace's decode steps, each row
+    finishing with its per-step probability and refilled at once with a
+    fresh prompt.  Every step's inputs and every refill's prompt K/V are
+    generated and placed in HBM before the timed loop.  Per step, HIP events
+    bracket the decode step (host append, the fused write + attention launch,
+    the merge) and the refills after it (release, admission, prompt write).
+    Prints one JSON line: K/V GB/s and decode tokens/s over the decode-step
+    time, and the refill time separately."""
+    import torch
+    import synth
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    tdtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cfg.dtype]
+    elem = synth.ELEM_BYTES[cfg.dtype]
+
+    def dev(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    t_gen = time.perf_counter()
+    tr = synth.serving_trace(cfg)
+    B, H, D = cfg.batch, cfg.num_kv_heads, cfg.head_dim
+    width = -(-(cfg.clip[1] + cfg.steps) // cfg.block_size)
+    eng = PagedKVEngine(cfg.num_blocks, H, cfg.block_size, D, tdtype, B, width, None, num_q_heads=cfg.num_q_heads)
+    eng.prefill_many(list(range(B)), list(range(B)), [int(x) for x in tr.prompt_lens],
+                     dev(np.concatenate(tr.hist_k)), dev(np.concatenate(tr.hist_v)))
+    steps = [(dev(st.new_k), dev(st.new_v), dev(st.q),
+              [(r.row, r.new_id, dev(r.k), dev(r.v)) for r in st.refills]) for st in tr.steps]
+    log(f"serving trace: {len(steps)} steps generated and resident in {time.perf_counter() - t_gen:.1f}s")
+    row_ids = np.arange(B, dtype=np.int64)
+    out = torch.empty((B, cfg.num_q_heads, D), dtype=torch.float32, device="cuda")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in steps]
+    kv_bytes = 0
+    n_refill = refill_tokens = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for (k, v, q, refills), ev in zip(steps, evs):
+        ev[0].record()
+        eng.decode_step(row_ids, k, v, q, cfg.scale, out=out)
+        kv_bytes += int(eng.lens[:B].astype(np.int64).sum()) * H * 2 * D * elem
+        ev[1].record()
+        for row, new_id, rk, rv in refills:
+            eng.free(int(row_ids[row]))
+            eng.prefill(new_id, row, rk, rv)
+            row_ids[row] = new_id
+            n_refill += 1
+            refill_tokens += rk.shape[0]
+        ev[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_s = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
+    ref_s = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+    tokens = B * len(steps)
+    log(f"serving trace: {1e6 * dec_s / len(steps):.1f} us per decode step, {kv_bytes / len(steps) / 1e6:.1f} MB "
+        f"K/V per step, {n_refill} refills ({refill_tokens} prompt tokens) in {1e3 * ref_s:.2f} ms")
+    print(json.dumps({
+        "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s",
+        "value": round(kv_bytes / dec_s / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": len(steps), "warmup": 0,
+        "ms_per_step": round(dec_s * 1e3 / len(steps), 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {B} rows, prompts clip(round(lognormal{tuple(cfg.lognormal)}), "
+                               f"{cfg.clip[0]}, {cfg.clip[1]}), {len(steps)} decode steps, finish probability "
+                               f"{cfg.p_finish} per row and step, refilled at once",
+                   "batch": B},
+        "pct_hbm_peak": round(100 * kv_bytes / dec_s / 1e9 / HBM_PEAK_GBPS, 1),
+        "decode_tokens_per_s": round(tokens / dec_s, 1),
+        "decode_tokens_per_s_with_refills": round(tokens / (dec_s + ref_s), 1),
+        "wall_tokens_per_s": round(tokens / wall, 1),
+        "refills": n_refill, "refill_prompt_tokens": refill_tokens, "refill_ms": round(ref_s * 1e3, 3),
+        "kernel_source_sha256_16": kernel_source_sha(),
+    }), flush=True)
 
 
 def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
@@ -377,7 +457,8 @@ def main():
 
     cfg = synth.CONFIGS[args.config]
     if cfg.steps:
-        raise SystemExit("the serving-trace workload is driven by its own test, not by bench.py")
+        measure_serving(cfg, args)
+        return
     tdtype = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[cfg.dtype]
     t_gen = time.perf_counter()
     wl = synth.decode_workload(cfg)
