@@ -532,6 +532,183 @@ __device__ __forceinline__ void wave_epilogue(float m, float l, float (&acc)[GP]
   }
 }
 
+// P.V accumulator of the 8-bit path, computed on the matrix cores:
+// O^T[d][h] += sum_t V^T[d][t] P^T[t][h], one 16x16x16 f16 MFMA per eighth
+// of the head dims.  MFMA j maps its row index c to head-dim 8 c + j, so its
+// A operand (lane (g4, c16): rows 4 g4 .. 4 g4 + 3 at head-dim 8 c16 + j) is
+// byte j of the lane's V codes, and its B operand (lane (g4, c16): head c16,
+// tokens 4 g4 ..) is the score layout as it comes out of the Q.K MFMA.
+// Lane (g4, c16) ends up with head c16's head-dims 32 g4 .. 32 g4 + 31:
+// c[j][i] is head-dim 32 g4 + 8 i + j.  The V codes enter the MFMA as exact
+// f16 values and P as f16 (round to nearest) scaled by 2^(ev(t) - eref),
+// where eref, the largest V scale exponent seen in the segment, keeps the
+// products in f16 range; c holds the accumulator times 2^-eref.
+struct Acc8 {
+  f32x4 c[8];
+  int eref;
+};
+constexpr int kNoRef = -100000;
+
+template <int GP>
+struct AccV {
+  float a[GP][8];
+};
+
+template <int GP>
+__device__ __forceinline__ void acc_zero(AccV<GP>& x) {
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x.a[h][e] = 0.f;
+}
+__device__ __forceinline__ void acc_zero(Acc8& x) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x.c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  x.eref = kNoRef;
+}
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// Max over the lanes c16, c16 + 16, c16 + 32, c16 + 48 (every lane gets it)
+// on the vector ALU: the 16-lane row swap pairs rows (0, 1) and (2, 3), the
+// 32-lane half swap pairs the halves.
+__device__ __forceinline__ float max_over_g4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ int max_over_g4(int x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  x = max(static_cast<int>(a[0]), static_cast<int>(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  return max(static_cast<int>(b[0]), static_cast<int>(b[1]));
+}
+
+// P.V of the 16-bit stream kernel on the matrix cores (false: on the vector
+// ALU with DPP broadcasts, softmax_pv above).
+constexpr bool kMfmaPV16 = true;
+
+// Two values as a packed pair of the 16-bit type (element 0 low), rounded
+// to nearest even.
+template <int DT>
+__device__ __forceinline__ uint32_t pack16x2(float x0, float x1) {
+  if constexpr (DT == PKV_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x0, x1}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)});
+}
+
+// Online softmax + P.V for one 16-bit tile with P.V on the matrix cores:
+// O^T[d][h] += V^T P^T as eight 16x16x16 MFMAs.  MFMA j maps its row index c
+// to head-dim 8 c + j, so its A operand is element j of the lane's V rows
+// 4 g4 .. 4 g4 + 3 (head-dims 8 c16 .. + 7, as loaded), and its B operand is
+// the score layout (head c16, tokens 4 g4 ..) as it leaves Q.K.  P enters as
+// a 16-bit value plus its 16-bit remainder (two MFMAs, P to about 2^-17).
+// The accumulator is the 8-bit path's (eref 0): lane (g4, c16) ends with
+// head c16's head-dims 32 g4 .. 32 g4 + 31.
+template <int DT>
+__device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128>& t, int nvalid,
+                                              float scale_log2, float& m, float& l, Acc8& acc, int lane) {
+  const int g4 = lane >> 4;
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (4 * g4 + r < nvalid) ? s[r] * scale_log2 : -INFINITY;
+  const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
+    const float m_new = fmaxf(m, bm);
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head; 0 on the first tile
+    l *= a;
+    m = m_new;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc.c[j] *= a;
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);   // masked tokens: 0
+  l += (p[0] + p[1]) + (p[2] + p[3]);
+  const uint32_t h01 = pack16x2<DT>(p[0], p[1]), h23 = pack16x2<DT>(p[2], p[3]);
+  float q0, q1, q2, q3;
+  unpack2<DT>(h01, q0, q1);
+  unpack2<DT>(h23, q2, q3);
+  const u32x2 bh = {h01, h23};
+  const u32x2 bl = {pack16x2<DT>(p[0] - q0, p[1] - q1), pack16x2<DT>(p[2] - q2, p[3] - q3)};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    const int w = j >> 1;
+    const u32x2 av = {__builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel),
+                      __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel)};
+    if constexpr (DT == PKV_BF16) {
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                           __builtin_bit_cast(i16x4, bh), acc.c[j], 0, 0, 0);
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                           __builtin_bit_cast(i16x4, bl), acc.c[j], 0, 0, 0);
+    } else {
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                       __builtin_bit_cast(f16x4, bh), acc.c[j], 0, 0, 0);
+      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                       __builtin_bit_cast(f16x4, bl), acc.c[j], 0, 0, 0);
+    }
+  }
+}
+
+// End of a segment with the MFMA P.V: lane (g4, c16) holds head c16's
+// head-dims 32 g4 .. + 31; the four token groups' sums l are added, and each
+// lane of a real head (c16 < G) writes its 32 values (normalised output, or
+// the partial with its (m, l) in workspace slot ws_row0 + c16 * ws_row_stride).
+__device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc, int lane, int G,
+                                               bool final, void* out, int out_dtype,
+                                               int64_t out_row0, float* ws_acc, float* ws_ml,
+                                               int64_t ws_row0, int64_t ws_row_stride = 1) {
+  constexpr int D = 128;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (c16 >= G) return;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i], acc.eref);
+  if (final) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const int64_t o = (out_row0 + c16) * D + 32 * g4;
+    if (out_dtype == PKV_F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        dst[k] = make_float4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
+    } else {
+      uint32_t w[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const float y0 = v[2 * k] * inv, y1 = v[2 * k + 1] * inv;
+        const uint32_t h0 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y0)
+                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y0));
+        const uint32_t h1 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y1)
+                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y1));
+        w[k] = h0 | (h1 << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+    }
+  } else {
+    const int64_t slot = ws_row0 + c16 * ws_row_stride;
+    float4* dst = reinterpret_cast<float4*>(ws_acc + slot * D + 32 * g4);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    if (g4 == 0) {
+      ws_ml[2 * slot + 0] = m;
+      ws_ml[2 * slot + 1] = l;
+    }
+  }
+}
+
 template <int DT, int D, int GP>
 __global__ void __launch_bounds__(kWave, split_waves_per_simd<DT>())
 attn_split_kernel(AttnArgs a) {
@@ -626,6 +803,16 @@ attn_split_kernel(AttnArgs a) {
   for (int h = 0; h < GP; ++h)
 #pragma unroll
     for (int e = 0; e < F::kW; ++e) acc[h][e] = 0.f;
+  // 16-bit KV with D = 128: P.V on the matrix cores (softmax_pv16m); fp32
+  // and D = 64 keep the vector-ALU P.V
+  constexpr bool MPV = F::kRowK && kMfmaPV16 && D == 128 && DT != PKV_F32;
+  Acc8 accm;
+  acc_zero(accm);
+  accm.eref = 0;
+  auto step = [&](const f32x4& sc, const VTile<DT, D>& v, int nvalid) {
+    if constexpr (MPV) softmax_pv16m<DT>(sc, v, nvalid, a.scale_log2, m, l, accm, lane);
+    else softmax_pv<DT, D, GP>(sc, v, nvalid, a.scale_log2, m, l, acc, lane);
+  };
 
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;
   const int last = ntiles - 1;
@@ -652,14 +839,14 @@ attn_split_kernel(AttnArgs a) {
         issue_k_rows<DT, D>(kc + eb, sk, nvalid_of(ib), lane);
         load_v<DT, D>(vb, vc + eb, nvalid_of(ib), lane);
       }
-      softmax_pv<DT, D, GP>(sc, va, nvalid_of(i), a.scale_log2, m, l, acc, lane);
+      step(sc, va, nvalid_of(i));
       if (i + 1 < ntiles) {
         sc = qk_mfma<DT, D>(read_k_rows<DT, D>(sk, lane), qf);
         __builtin_amdgcn_s_waitcnt(0xc07f);
         const int64_t ea = tile_addr(ia) * F::kBytes;
         issue_k_rows<DT, D>(kc + ea, sk, nvalid_of(ia), lane);
         load_v<DT, D>(va, vc + ea, nvalid_of(ia), lane);
-        softmax_pv<DT, D, GP>(sc, vb, nvalid_of(i + 1), a.scale_log2, m, l, acc, lane);
+        step(sc, vb, nvalid_of(i + 1));
       }
     }
     // the last (clamped) K fetch into LDS must land before the wave can exit
@@ -694,8 +881,12 @@ attn_split_kernel(AttnArgs a) {
     }
   }
 
-  wave_epilogue<DT, D, GP>(m, l, acc, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc,
-                           a.ws_ml, out_row0 * a.max_parts + p, a.max_parts);
+  if constexpr (MPV)
+    wave_epilogue8(m, l, accm, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc, a.ws_ml,
+                   out_row0 * a.max_parts + p, a.max_parts);
+  else
+    wave_epilogue<DT, D, GP>(m, l, acc, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc,
+                             a.ws_ml, out_row0 * a.max_parts + p, a.max_parts);
 }
 
 // Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with
@@ -1022,130 +1213,6 @@ __device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
   return r;
 }
 
-// P.V accumulator of the 8-bit path, computed on the matrix cores:
-// O^T[d][h] += sum_t V^T[d][t] P^T[t][h], one 16x16x16 f16 MFMA per eighth
-// of the head dims.  MFMA j maps its row index c to head-dim 8 c + j, so its
-// A operand (lane (g4, c16): rows 4 g4 .. 4 g4 + 3 at head-dim 8 c16 + j) is
-// byte j of the lane's V codes, and its B operand (lane (g4, c16): head c16,
-// tokens 4 g4 ..) is the score layout as it comes out of the Q.K MFMA.
-// Lane (g4, c16) ends up with head c16's head-dims 32 g4 .. 32 g4 + 31:
-// c[j][i] is head-dim 32 g4 + 8 i + j.  The V codes enter the MFMA as exact
-// f16 values and P as f16 (round to nearest) scaled by 2^(ev(t) - eref),
-// where eref, the largest V scale exponent seen in the segment, keeps the
-// products in f16 range; c holds the accumulator times 2^-eref.
-struct Acc8 {
-  f32x4 c[8];
-  int eref;
-};
-constexpr int kNoRef = -100000;
-
-template <int GP>
-struct AccV {
-  float a[GP][8];
-};
-
-template <int GP>
-__device__ __forceinline__ void acc_zero(AccV<GP>& x) {
-#pragma unroll
-  for (int h = 0; h < GP; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x.a[h][e] = 0.f;
-}
-__device__ __forceinline__ void acc_zero(Acc8& x) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) x.c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  x.eref = kNoRef;
-}
-
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// Max over the lanes c16, c16 + 16, c16 + 32, c16 + 48 (every lane gets it)
-// on the vector ALU: the 16-lane row swap pairs rows (0, 1) and (2, 3), the
-// 32-lane half swap pairs the halves.
-__device__ __forceinline__ float max_over_g4(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ int max_over_g4(int x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
-  x = max(static_cast<int>(a[0]), static_cast<int>(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
-  return max(static_cast<int>(b[0]), static_cast<int>(b[1]));
-}
-
-// P.V of the 16-bit stream kernel on the matrix cores (false: on the vector
-// ALU with DPP broadcasts, softmax_pv above).
-constexpr bool kMfmaPV16 = true;
-
-// Two values as a packed pair of the 16-bit type (element 0 low), rounded
-// to nearest even.
-template <int DT>
-__device__ __forceinline__ uint32_t pack16x2(float x0, float x1) {
-  if constexpr (DT == PKV_BF16)
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x0, x1}, bf16x2));
-  else
-    return __builtin_bit_cast(uint32_t, f16x2{static_cast<_Float16>(x0), static_cast<_Float16>(x1)});
-}
-
-// Online softmax + P.V for one 16-bit tile with P.V on the matrix cores:
-// O^T[d][h] += V^T P^T as eight 16x16x16 MFMAs.  MFMA j maps its row index c
-// to head-dim 8 c + j, so its A operand is element j of the lane's V rows
-// 4 g4 .. 4 g4 + 3 (head-dims 8 c16 .. + 7, as loaded), and its B operand is
-// the score layout (head c16, tokens 4 g4 ..) as it leaves Q.K.  P enters as
-// a 16-bit value plus its 16-bit remainder (two MFMAs, P to about 2^-17).
-// The accumulator is the 8-bit path's (eref 0): lane (g4, c16) ends with
-// head c16's head-dims 32 g4 .. 32 g4 + 31.
-template <int DT>
-__device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128>& t, int nvalid,
-                                              float scale_log2, float& m, float& l, Acc8& acc, int lane) {
-  const int g4 = lane >> 4;
-  float x[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = (4 * g4 + r < nvalid) ? s[r] * scale_log2 : -INFINITY;
-  const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
-    const float m_new = fmaxf(m, bm);
-    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head; 0 on the first tile
-    l *= a;
-    m = m_new;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc.c[j] *= a;
-  }
-  float p[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);   // masked tokens: 0
-  l += (p[0] + p[1]) + (p[2] + p[3]);
-  const uint32_t h01 = pack16x2<DT>(p[0], p[1]), h23 = pack16x2<DT>(p[2], p[3]);
-  float q0, q1, q2, q3;
-  unpack2<DT>(h01, q0, q1);
-  unpack2<DT>(h23, q2, q3);
-  const u32x2 bh = {h01, h23};
-  const u32x2 bl = {pack16x2<DT>(p[0] - q0, p[1] - q1), pack16x2<DT>(p[2] - q2, p[3] - q3)};
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-    const int w = j >> 1;
-    const u32x2 av = {__builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel),
-                      __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel)};
-    if constexpr (DT == PKV_BF16) {
-      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                           __builtin_bit_cast(i16x4, bh), acc.c[j], 0, 0, 0);
-      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                           __builtin_bit_cast(i16x4, bl), acc.c[j], 0, 0, 0);
-    } else {
-      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
-                                                       __builtin_bit_cast(f16x4, bh), acc.c[j], 0, 0, 0);
-      acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
-                                                       __builtin_bit_cast(f16x4, bl), acc.c[j], 0, 0, 0);
-    }
-  }
-}
-
 // Online softmax + P.V for one 8-bit tile: the score of token t is the code
 // dot product times 2^ek(t) (into the exp2 argument's factor), the V row of
 // t its codes times 2^ev(t) (into the probability the MFMA takes; the sum l
@@ -1214,59 +1281,6 @@ __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int 
     const u32x2 av = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1])),
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3]))};
     acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av), b, acc.c[j], 0, 0, 0);
-  }
-}
-
-// End of a segment on the 8-bit path: lane (g4, c16) holds head c16's
-// head-dims 32 g4 .. + 31; the four token groups' sums l are added, and each
-// lane of a real head (c16 < G) writes its 32 values (normalised output, or
-// the partial with its (m, l)).
-__device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc, int lane, int G,
-                                               bool final, void* out, int out_dtype,
-                                               int64_t out_row0, float* ws_acc, float* ws_ml,
-                                               int64_t ws_row0) {
-  constexpr int D = 128;
-  const int g4 = lane >> 4, c16 = lane & 15;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (c16 >= G) return;
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i], acc.eref);
-  if (final) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    const int64_t o = (out_row0 + c16) * D + 32 * g4;
-    if (out_dtype == PKV_F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + o);
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        dst[k] = make_float4(v[4 * k] * inv, v[4 * k + 1] * inv, v[4 * k + 2] * inv, v[4 * k + 3] * inv);
-    } else {
-      uint32_t w[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float y0 = v[2 * k] * inv, y1 = v[2 * k + 1] * inv;
-        const uint32_t h0 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y0)
-                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y0));
-        const uint32_t h1 = out_dtype == PKV_BF16 ? f32_to_bf16_rne(y1)
-                                                  : __builtin_bit_cast(uint16_t, static_cast<_Float16>(y1));
-        w[k] = h0 | (h1 << 16);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + o);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) dst[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
-    }
-  } else {
-    const int64_t slot = ws_row0 + c16;
-    float4* dst = reinterpret_cast<float4*>(ws_acc + slot * D + 32 * g4);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    if (g4 == 0) {
-      ws_ml[2 * slot + 0] = m;
-      ws_ml[2 * slot + 1] = l;
-    }
   }
 }
 
