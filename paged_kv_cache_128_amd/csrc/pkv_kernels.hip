@@ -1175,22 +1175,16 @@ __device__ __forceinline__ void load_v_buf8(VTile8& t, const char* vtile, const 
   t.vs = *reinterpret_cast<const uint32_t*>(vsc + 4 * g4);
 }
 
-// Four codes of a dword as float32 (hardware E4M3 conversion).
-__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float (&f)[4]) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-  f[0] = lo.x; f[1] = lo.y;
-  f[2] = hi.x; f[3] = hi.y;
-}
-
 // Two float32 of code values (exact in 16 bits) packed as the MFMA's 16-bit type.
-template <int DT>
-__device__ __forceinline__ uint32_t pack16(float a, float b) {
+// Two E4M3 codes (bytes 0-1 of w, or 2-3 when HI) as a packed pair of the
+// 16-bit type, by the hardware conversion with scale 1 (exact: every E4M3
+// value is a bf16 and an f16 number).
+template <int DT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_16(uint32_t w) {
   if constexpr (DT == PKV_BF16)
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
   else
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
 }
 
 // The staged K codes of row c16 as the MFMA operand: lane (g4, c16) takes
@@ -1205,10 +1199,8 @@ __device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
   Dw<16> r;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float f[4];
-    fp8x4_to_f32(w[i], f);
-    r.w[2 * i] = pack16<DT>(f[0], f[1]);
-    r.w[2 * i + 1] = pack16<DT>(f[2], f[3]);
+    r.w[2 * i] = fp8x2_to_16<DT, false>(w[i]);
+    r.w[2 * i + 1] = fp8x2_to_16<DT, true>(w[i]);
   }
   return r;
 }
@@ -1276,10 +1268,7 @@ __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int 
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float f[4];
-    fp8x4_to_f32(X[j], f);
-    const u32x2 av = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[0], f[1])),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f[2], f[3]))};
+    const u32x2 av = {fp8x2_to_16<PKV_F16, false>(X[j]), fp8x2_to_16<PKV_F16, true>(X[j])};
     acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av), b, acc.c[j], 0, 0, 0);
   }
 }
