@@ -73,7 +73,8 @@ class CacheLayout(ctypes.Structure):
 _LIB = None
 _P = ctypes.c_void_p
 _I32, _I64, _U32, _F32, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float, ctypes.c_size_t
-_PI32, _PI64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+# typed host arrays travel as plain addresses (see _ptr)
+_PI32 = _PI64 = _P
 
 # name -> (restype, argtypes); the complete exported C ABI
 SIGNATURES = {
@@ -181,7 +182,11 @@ def _np_i64(a) -> np.ndarray:
 
 
 def _ptr(a: np.ndarray, ty):
-    return a.ctypes.data_as(ctypes.POINTER(ty))
+    """Address of a host array's first element for a C pointer argument of
+    element type ``ty`` (the caller keeps ``a`` alive across the call).  The
+    array interface is the cheapest route to it (about half the cost of
+    ``ctypes.data_as`` per call, which the decode step pays several times)."""
+    return a.__array_interface__["data"][0]
 
 
 # --------------------------------------------------------------------------
@@ -292,6 +297,12 @@ class KVBlockManager:
             self._h, _ptr(ids, ctypes.c_int64), n, _ptr(slots, ctypes.c_int64),
             _ptr(lens, ctypes.c_int32), _ptr(newb, ctypes.c_int32)), "append_slots_for_decode")
         return slots, lens, newb
+
+    def _append_at(self, ids_addr: int, n: int, slots_addr: int, lens_addr: int, newb_addr: int) -> None:
+        """append_slots_for_decode on host buffers given by address (the
+        engine's persistent arrays, whose addresses it computes once)."""
+        _check(self._lib.pkv_append_slots_for_decode(self._h, ids_addr, n, slots_addr, lens_addr, newb_addr),
+               "append_slots_for_decode")
 
     def free_sequence(self, seq_id: int) -> None:
         _check(self._lib.pkv_free_sequence(self._h, int(seq_id)), "free_sequence")

@@ -35,7 +35,14 @@ namespace {
 struct Sequence {
   int32_t length = 0;            // tokens written == next write position
   std::vector<int32_t> table;    // logical block -> physical block id
+  uint64_t mark = 0;             // batch-call epoch that last listed it (duplicate check)
 };
+
+// Room for one more table entry, grown geometrically, so that an append
+// that opens a block cannot fail midway.
+void reserve_one(std::vector<int32_t>& t) {
+  if (t.size() == t.capacity()) t.reserve(t.size() < 8 ? 8 : 2 * t.size());
+}
 
 }  // namespace
 
@@ -51,6 +58,7 @@ struct pkv_manager {
   std::vector<int32_t> ref;                            // tables holding each block
   std::vector<std::pair<int32_t, int32_t>> copies;     // queued (source, destination)
   std::unordered_map<int64_t, int32_t> swapped;        // swapped-out sequence -> length
+  uint64_t epoch = 0;                                  // batch calls so far (Sequence::mark)
 
   int32_t free_at(int64_t i) const { return ring[(head + i) % num_blocks]; }
   int32_t pop_front() {
@@ -213,7 +221,7 @@ int pkv_append_slot_for_decode(pkv_manager* m, int64_t seq_id, int64_t* slot_out
   const bool opens = (s.length / m->block_size) == static_cast<int64_t>(s.table.size());
   if (append_takes_block(m, s, 0) && m->count == 0) return PKV_ERR_OOM;
   try {
-    if (opens) s.table.reserve(s.table.size() + 1);
+    if (opens) reserve_one(s.table);
     m->copies.reserve(m->copies.size() + 1);
   } catch (...) {
     return PKV_ERR_INVALID;
@@ -226,29 +234,46 @@ int pkv_append_slot_for_decode(pkv_manager* m, int64_t seq_id, int64_t* slot_out
 int pkv_append_slots_for_decode(pkv_manager* m, const int64_t* seq_ids, int32_t n,
                                 int64_t* slots_out, int32_t* lens_out, int32_t* new_block_out) {
   if (!m || n < 0 || (n > 0 && !seq_ids)) return PKV_ERR_INVALID;
-  std::vector<Sequence*> seqs;
+  // The ids' sequences, with the duplicate check by epoch marks (no
+  // allocation once the buffer has grown); when some id is not live, the
+  // set-based check decides which error comes first (duplicates before
+  // unknown ids).
+  thread_local std::vector<Sequence*> seqs;
+  bool all_live = true, dup = false;
   try {
-    seqs.reserve(n);
-    std::unordered_set<int64_t> seen;
-    seen.reserve(static_cast<size_t>(n) * 2);
-    for (int32_t i = 0; i < n; ++i)
-      if (!seen.insert(seq_ids[i]).second) return PKV_ERR_INVALID;
+    seqs.resize(static_cast<size_t>(n));
+    const uint64_t ep = ++m->epoch;
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = m->seqs.find(seq_ids[i]);
+      if (it == m->seqs.end()) {
+        all_live = false;
+        continue;
+      }
+      Sequence& s = it->second;
+      if (s.mark == ep) dup = true;
+      s.mark = ep;
+      seqs[i] = &s;
+    }
+    if (!all_live) {
+      std::unordered_set<int64_t> seen;
+      seen.reserve(static_cast<size_t>(n) * 2);
+      for (int32_t i = 0; i < n; ++i)
+        if (!seen.insert(seq_ids[i]).second) return PKV_ERR_INVALID;
+      return PKV_ERR_NOT_LIVE;
+    }
   } catch (...) {
     return PKV_ERR_INVALID;
   }
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = m->seqs.find(seq_ids[i]);
-    if (it == m->seqs.end()) return PKV_ERR_NOT_LIVE;
-    Sequence& s = it->second;
-    if (s.length == INT32_MAX) return PKV_ERR_INVALID;
-    seqs.push_back(&s);
-  }
+  if (dup) return PKV_ERR_INVALID;
+  for (int32_t i = 0; i < n; ++i)
+    if (seqs[i]->length == INT32_MAX) return PKV_ERR_INVALID;
   // blocks the call takes, in array order: opened blocks and copies on write
   // (a copy drops one reference from the shared block for later rows)
   int64_t need = 0;
   try {
     std::unordered_map<int32_t, int32_t> dropped;
-    for (Sequence* s : seqs) {
+    for (int32_t i = 0; i < n; ++i) {
+      Sequence* s = seqs[i];
       const int64_t lb = s->length / m->block_size;
       const bool opens = lb == static_cast<int64_t>(s->table.size());
       const int32_t pb = opens ? -1 : s->table[lb];
@@ -259,9 +284,9 @@ int pkv_append_slots_for_decode(pkv_manager* m, const int64_t* seq_ids, int32_t 
       }
     }
     if (need > m->count) return PKV_ERR_OOM;
-    for (Sequence* s : seqs)
-      if (s->length / m->block_size == static_cast<int64_t>(s->table.size()))
-        s->table.reserve(s->table.size() + 1);
+    for (int32_t i = 0; i < n; ++i)
+      if (seqs[i]->length / m->block_size == static_cast<int64_t>(seqs[i]->table.size()))
+        reserve_one(seqs[i]->table);
     m->copies.reserve(m->copies.size() + need);
   } catch (...) {
     return PKV_ERR_INVALID;

@@ -70,6 +70,9 @@ class PagedKVEngine:
         self.slots = np.empty(max_rows, dtype=np.int64)      # last step's slots (host)
         self.lens = np.empty(max_rows, dtype=np.int32)       # last step's lengths (host)
         self._newb = np.empty(max_rows, dtype=np.int32)
+        self._ids = np.empty(max_rows, dtype=np.int64)       # the step's sequence ids
+        # the persistent host arrays' addresses, for the per-step append
+        self._addr = tuple(x.__array_interface__["data"][0] for x in (self._ids, self.slots, self.lens, self._newb))
         self._ws = None
         self._pf_ws = None         # 16-bit staging of 8-bit prefill
         self._nq = num_q_heads
@@ -240,7 +243,10 @@ class PagedKVEngine:
         the merge, and after the merge.  ``fused`` = False forces the
         separate write launch."""
         n = len(seq_ids)
-        self.manager.append_slots_for_decode(seq_ids, self.slots[:n], self.lens[:n], self._newb[:n])
+        if n > self.max_rows:
+            raise ValueError("more sequences than the engine's rows")
+        self._ids[:n] = seq_ids
+        self.manager._append_at(self._addr[0], n, self._addr[1], self._addr[2], self._addr[3])
         self._run_copies()
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
