@@ -40,6 +40,39 @@ from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_st
                prefill_fp8_workspace_size, workspace_size)
 
 
+class _HostStage:
+    """Pinned host staging for the small host-to-device copies of admissions
+    (slots, table rows, chunk offsets): a bump arena whose copies are queued
+    without synchronising the stream.  When the arena wraps, the stream is
+    synchronised once, so every copy out of the previous lap has run before
+    its bytes are reused."""
+
+    def __init__(self, nbytes: int, device):
+        self.device = device
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        self.off = 0
+
+    def to_device(self, arr: np.ndarray) -> torch.Tensor:
+        arr = np.ascontiguousarray(arr)
+        n = arr.nbytes
+        if n > self.buf.numel():                     # larger than the arena: a plain copy
+            return torch.from_numpy(arr).to(self.device)
+        at = (self.off + 255) & ~255
+        if at + n > self.buf.numel():
+            torch.cuda.current_stream(self.device).synchronize()
+            at = 0
+        self.off = at + n
+        host = self.buf[at:at + n]
+        host.numpy()[:] = arr.view(np.uint8).reshape(-1)
+        return host.view(_TORCH_OF[arr.dtype]).to(self.device, non_blocking=True)
+
+    def copy_into(self, dst: torch.Tensor, arr: np.ndarray) -> None:
+        dst.copy_(self.to_device(arr), non_blocking=True)
+
+
+_TORCH_OF = {np.dtype(np.int64): torch.int64, np.dtype(np.int32): torch.int32}
+
+
 class PagedKVEngine:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                  dtype: torch.dtype, max_rows: int, max_blocks_per_seq: int,
@@ -77,6 +110,7 @@ class PagedKVEngine:
         self._pf_ws = None         # 16-bit staging of 8-bit prefill
         self._nq = num_q_heads
         self._sharing = False      # set once any table shares a block
+        self._stage = _HostStage(4 << 20, self.device)
 
     # -- admission / release ------------------------------------------------
     def prefill(self, seq_id: int, row: int, key: torch.Tensor, value: torch.Tensor,
@@ -86,7 +120,7 @@ class PagedKVEngine:
         n = key.shape[0] if num_tokens is None else num_tokens
         slots = self.manager.allocate_for_prefill(seq_id, n)
         if n > 0:
-            d_slots = torch.from_numpy(slots).to(self.device, non_blocking=False)
+            d_slots = self._stage.to_device(slots)
             self._write(key, value, d_slots)
         self._publish_row(seq_id, row)
         return slots
@@ -113,14 +147,14 @@ class PagedKVEngine:
         self._run_copies()
         slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
-            self._write(key, value, torch.from_numpy(slots).to(self.device))
+            self._write(key, value, self._stage.to_device(slots))
         for sid, row in zip(seq_ids, rows):
             self._publish_row(int(sid), int(row))
         B = len(seq_ids)
         q_start = np.concatenate([[0], np.cumsum(np.asarray(chunk_lens, dtype=np.int64))]).astype(np.int32)
-        d_qs = torch.from_numpy(q_start).to(self.device)
-        d_lens = torch.from_numpy(np.asarray(lens, dtype=np.int32)).to(self.device)
-        tables = self.tables[torch.as_tensor(list(rows), dtype=torch.long, device=self.device)]
+        d_qs = self._stage.to_device(q_start)
+        d_lens = self._stage.to_device(np.asarray(lens, dtype=np.int32))
+        tables = self.tables[self._stage.to_device(np.asarray(list(rows), dtype=np.int64))]
         max_q = int(max(chunk_lens)) if B else 0
         max_len = int(max(lens)) if B else 0
         if self.fp8:
@@ -162,7 +196,7 @@ class PagedKVEngine:
             all_slots.append(self.manager.allocate_for_prefill(int(sid), int(n)))
         slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
-            d_slots = torch.from_numpy(slots).to(self.device)
+            d_slots = self._stage.to_device(slots)
             self._write(key, value, d_slots)
         for sid, row in zip(seq_ids, rows):
             self._publish_row(int(sid), int(row))
@@ -212,7 +246,7 @@ class PagedKVEngine:
 
     def _publish_row(self, seq_id: int, row: int):
         tab = self.manager.block_tables([seq_id], self.width, -1)
-        self.tables[row].copy_(torch.from_numpy(tab[0]), non_blocking=False)
+        self._stage.copy_into(self.tables[row], tab[0])
         self.row_seq[row] = seq_id
 
     def free(self, seq_id: int) -> None:
