@@ -118,3 +118,32 @@ def test_shared_prefix_decode_matches_oracle(dtype, hq, hkv, fused):
         _banner(f"step {step}: copies {len(pairs)}, max abs err {err:.3e}")
         assert err <= TOL[dtype], (step, err)
     assert copies_seen > 0
+
+
+def test_admissions_through_a_wrapping_staging_arena():
+    """Admission copies (slots, table rows) go through the engine's pinned
+    staging arena asynchronously; with the arena shrunk to 2 KiB it wraps
+    (one stream synchronisation per lap) many times, and a prompt larger
+    than the arena takes the plain copy.  The pool equals the oracle's write
+    bit for bit and the device tables equal the manager's."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine, _HostStage
+    _banner("admissions through a 2 KiB staging arena")
+    rng = np.random.default_rng(17)
+    hkv, bs, D, dtype = 2, 16, 64, "bf16"
+    lens = [int(x) for x in rng.integers(1, 200, 40)] + [600]      # the last: 4.8 KB of slots
+    N = sum(-(-L // bs) for L in lens) + 4
+    order = rng.permutation(N)
+    width = max(-(-L // bs) for L in lens)
+    eng = PagedKVEngine(N, hkv, bs, D, torch.bfloat16, len(lens), width, order,
+                        fill_bits=synth.POISON_BITS[dtype], num_q_heads=hkv)
+    eng._stage = _HostStage(2048, eng.device)
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc = oracle.new_pool(N, hkv, bs, D, synth.poison_array((), dtype))
+    for sid, L in enumerate(lens):
+        k = synth.normal(rng, (L, hkv, D), dtype)
+        v = synth.normal(rng, (L, hkv, D), dtype)
+        oracle.write_kv(k, v, om.allocate_for_prefill(sid, L), okc, ovc, bs)
+        eng.prefill(sid, sid, to_device(k, dtype), to_device(v, dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(eng.tables.cpu().numpy(), om.block_tables(list(range(len(lens))), width, -1))
+    assert np.array_equal(bits_u(eng.key_cache), okc) and np.array_equal(bits_u(eng.value_cache), ovc)
