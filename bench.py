@@ -211,7 +211,8 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, see
     """Full-prompt prefill attention (paged_prefill_attention) with the
     workload's head shape: ``seqs`` prompts of ``prompt`` tokens admitted and
     written through the engine, then the attention launch timed with HIP
-    events around ``iters`` back-to-back launches after five untimed ones.  Useful FLOPs: row i of a
+    events around ``iters`` back-to-back launches after 0.3 s of untimed
+    ones.  Useful FLOPs: row i of a
     prompt sees i + 1 keys, 4 * D FLOPs per key and query head (Q.K and P.V).
     ``kv8``: the same over an 8-bit pool (paged_prefill_attention_fp8: the
     blocks' dequantisation into the 16-bit staging, then the prefill kernel,
@@ -245,8 +246,14 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, see
         def launch():
             pkv.paged_prefill_attention(q, qs, eng.key_cache, eng.value_cache, eng.tables, lens, scale,
                                         max_q_len=prompt, max_context_len=prompt, out=out)
-    for _ in range(5):                     # warm-up: the clocks settle under the matrix-core load
-        launch()
+    # warm-up: under the matrix-core load the clocks take a few hundred
+    # milliseconds to settle (back-to-back batches measured 490, 429 and
+    # 415 us), so launches run for 0.3 s before the timed ones
+    t_w = time.perf_counter()
+    while time.perf_counter() - t_w < 0.3:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
