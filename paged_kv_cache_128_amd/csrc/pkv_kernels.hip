@@ -1,35 +1,49 @@
 // HIP kernels of libpkv for gfx950 (MI355X) and their C-ABI launchers.
 //
-//  * kv_write_kernel     -- slot-mapping scatter of new K/V rows into the pool
-//                           ([MiniPaged-Qwen] §11 slot split, §12 cache write).
-//  * attn_split_kernel   -- decode attention over one context partition of one
-//                           (sequence, KV head): block-table walk, GQA group
-//                           sharing each K/V tile, fp32 online softmax
-//                           ([MiniPaged-Qwen] §13, §14, §17.3).
-//  * attn_reduce_kernel  -- merges the partitions' (max, sum, accumulator)
-//                           triples into the final rows (split-K).
-//  * table_update_kernel -- applies the blocks a batched decode append opened
-//                           to a device-resident block table ([MiniPaged-Qwen] §9.2).
+//  * kv_write_kernel          -- slot-mapping scatter of new K/V rows into the
+//                                pool ([MiniPaged-Qwen] §11 slot split, §12
+//                                cache write).
+//  * decode_write_kernel      -- one decode step's write with its metadata in
+//                                the kernel arguments; also publishes the
+//                                step's table entries and lengths.
+//  * table_update_kernel      -- applies the blocks a batched decode append
+//                                opened to a device-resident block table
+//                                ([MiniPaged-Qwen] §9.2).
+//  * attn_split_kernel        -- decode attention over one context partition
+//                                of one (sequence, KV head): block-table walk,
+//                                GQA group sharing each K/V tile, fp32 online
+//                                softmax ([MiniPaged-Qwen] §13, §14, §17.3).
+//  * attn_reduce_kernel       -- merges the partitions' (max, sum,
+//                                accumulator) triples into the final rows.
+//  * attn_stream_kernel,      -- stream-K decode attention: all sequences'
+//    attn_stream8_kernel         tiles laid end to end and cut into equal
+//                                ranges, one workgroup per CU (16-bit and
+//                                8-bit KV; section "stream-K attention").
+//  * attn_stream_step_kernel, -- the same, fused with the step's write (the
+//    attn_stream8_step_kernel    8-bit form quantises the new rows).
+//  * attn_stream_merge_kernel -- joins the stream kernel's partial segments.
 //
-// Work mapping of attn_split_kernel (one 64-lane wavefront per workgroup):
+// Shared work mapping of the attention kernels (64-lane wavefronts):
 //  - The K/V pool is read in tiles of 16 consecutive logical tokens (a tile
 //    never straddles a physical block because block_size % 16 == 0).
 //  - Q.K^T runs on the matrix cores: A = the K tile (16 tokens x D), B = the
 //    query group transposed (D x 16 heads, heads >= G zero), one
 //    V_MFMA_F32_16x16x32_{BF16,F16} per 32 head-dims (16x16x4 F32 for fp32).
-//    Lane l supplies token (l % 16) of the K tile straight from HBM with
-//    16-byte loads; the result S^T lands with head = l % 16 and tokens
-//    4*(l/16) .. 4*(l/16)+3 in the lane's four accumulators.
-//  - P.V runs on the vector ALUs: lane l owns head-dim chunk (l % 16) and
-//    the same four tokens 4*(l/16).., so each V tile row is read by 16 lanes
-//    as one 256-byte (bf16, D = 128) coalesced segment.  The probabilities
-//    reach the P.V lanes through a 1 KiB LDS broadcast.
+//    The result S^T lands with head = l % 16 and tokens 4*(l/16) ..
+//    4*(l/16)+3 in lane l's four accumulators.
+//  - P.V: for 16-bit KV with D = 128 it runs on the matrix cores too
+//    (softmax_pv16m: eight 16x16x16 MFMAs per tile, P as a 16-bit value plus
+//    its 16-bit remainder); otherwise (fp32, other D) on the vector ALUs,
+//    lane l owning head-dim chunk (l % 16) of tokens 4*(l/16).., the
+//    probabilities reaching it by DPP row broadcasts (softmax_pv).  8-bit KV
+//    scales the codes per row (softmax_pv8).
 //  - Softmax is online in fp32 and in log2 units (scores pre-multiplied by
 //    scale*log2(e), exponentials by v_exp_f32).  The running reference max
 //    only moves when a tile's max exceeds it by more than 8 (2^8 headroom),
 //    so the accumulator rescale is skipped on almost every tile.
-//  - The next tile's K and V are loaded before the current one is consumed
-//    (two register stages), so every wave keeps 8 KiB in flight.
+//  - Loads run ahead of use: the split kernel keeps the next tile in a
+//    second register stage, the stream kernels fetch whole chunks of tiles
+//    (K by buffer loads into LDS, V into registers) before consuming them.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
