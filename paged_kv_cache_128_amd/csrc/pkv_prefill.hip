@@ -125,6 +125,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
                                            nrows * kD * 2, kRsrcWord3);
 }
 
+// One 16-byte-per-lane LDS DMA (lane i fills bytes 16 i .. 16 i + 15 from
+// `lds`), written out so that the compiler does not track it: left to the
+// compiler, every LDS read after a DMA waits for all outstanding DMA, which
+// would hold each tile's reads until the next tile had landed and leave the
+// double buffer without overlap.  The caller orders it with explicit vmcnt
+// waits and barriers.  Nothing else in this file uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, const uint4* lds, int voff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int DT>
 __device__ __forceinline__ f32x4 mfma_k32(const u32x4& a, const u32x4& b, f32x4 c) {
   if constexpr (DT == PKV_BF16)
@@ -241,9 +256,8 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + g4;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dk + 64 * i), 16,
-                                               r * kD * 2 + ((c16 ^ r) << 4), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dv + 64 * i), 16, r * kD * 2 + (c16 << 4), 0, 0, 0);
+      dma16(rk, dk + 64 * i, r * kD * 2 + ((c16 ^ r) << 4));
+      dma16(rv, dv + 64 * i, r * kD * 2 + (c16 << 4));
     }
     asm volatile("" ::: "memory");
   };

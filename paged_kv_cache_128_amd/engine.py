@@ -43,9 +43,9 @@ from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_st
 class _HostStage:
     """Pinned host staging for the small host-to-device copies of admissions
     (slots, table rows, chunk offsets): a bump arena whose copies are queued
-    without synchronising the stream.  When the arena wraps, the stream is
+    without synchronising the stream.  When the arena wraps, the device is
     synchronised once, so every copy out of the previous lap has run before
-    its bytes are reused."""
+    its bytes are reused, whichever stream it was queued on."""
 
     def __init__(self, nbytes: int, device):
         self.device = device
@@ -59,7 +59,7 @@ class _HostStage:
             return torch.from_numpy(arr).to(self.device)
         at = (self.off + 255) & ~255
         if at + n > self.buf.numel():
-            torch.cuda.current_stream(self.device).synchronize()
+            torch.cuda.synchronize(self.device)
             at = 0
         self.off = at + n
         host = self.buf[at:at + n]
