@@ -178,7 +178,8 @@ def measure_swap(eng, seqs: int = 8, iters: int = 5):
     blocks gathered into a staging array (pkv_gather_blocks, HBM-bound) and
     copied to pinned host memory, timed separately with HIP events; the
     sequences are then swapped back in.  Reported: staging GB/s (read + write
-    of the blocks) and device-to-host GB/s."""
+    of the blocks), device-to-host GB/s, and an attention launch's time alone
+    and with the copy in flight on a side stream (as the engine queues it)."""
     import torch
     import paged_kv_cache_128_amd as pkv
     seqs = min(seqs, len(eng.row_seq))
@@ -199,12 +200,38 @@ def measure_swap(eng, seqs: int = 8, iters: int = 5):
     g_us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
     c_us = ev[1].elapsed_time(ev[2]) * 1e3 / iters
     nbytes = len(ids) * block_bytes
-    log(f"swap: {len(ids)} blocks ({nbytes / 1e6:.1f} MB): gather {g_us:.1f} us, device-to-host {c_us:.1f} us")
+    # The engine's swap_out queues the copy on a side stream: an attention
+    # launch over every row on the compute stream, alone and with that copy
+    # in flight beside it (median of a few launches each).
+    rows = len(eng.row_seq)
+    qa = torch.randn((rows, eng._nq, eng.head_dim), device="cuda").to(eng.dtype)
+    lens_d = eng.d_lens[:rows]
+    maxl = int(lens_d.max())
+    cs = torch.cuda.Stream()
+
+    def attn_us(with_copy):
+        ts = []
+        for _ in range(iters):
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if with_copy:
+                with torch.cuda.stream(cs):
+                    host.copy_(staged, non_blocking=True)
+            e0.record()
+            eng.attend(qa, lens_d, 0.088, maxl)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(ts))
+    alone, beside = attn_us(False), attn_us(True)
+    log(f"swap: {len(ids)} blocks ({nbytes / 1e6:.1f} MB): gather {g_us:.1f} us, device-to-host {c_us:.1f} us; "
+        f"attention {alone:.1f} us alone, {beside:.1f} us beside the copy")
     return {"kernel": "block_stage_kernel<gather>", "blocks": int(len(ids)), "bytes": int(nbytes),
             "gather_us": round(g_us, 2), "gather_gbps": round(2 * nbytes / (g_us * 1e-6) / 1e9, 1),
             "gather_frac_hbm": round(2 * nbytes / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "device_to_host_us": round(c_us, 2),
-            "device_to_host_gbps": round(nbytes / (c_us * 1e-6) / 1e9, 1)}
+            "device_to_host_gbps": round(nbytes / (c_us * 1e-6) / 1e9, 1),
+            "attention_us_alone": round(alone, 2), "attention_us_beside_copy": round(beside, 2)}
 
 
 def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, seed: int = 2024, kv8: bool = False):

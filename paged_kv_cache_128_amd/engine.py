@@ -111,6 +111,8 @@ class PagedKVEngine:
         self._nq = num_q_heads
         self._sharing = False      # set once any table shares a block
         self._stage = _HostStage(4 << 20, self.device)
+        self._copy_stream = None   # swap-out device-to-host copies (default priority)
+        self._swap_done: Dict[int, torch.cuda.Event] = {}
 
     # -- admission / release ------------------------------------------------
     def prefill(self, seq_id: int, row: int, key: torch.Tensor, value: torch.Tensor,
@@ -212,30 +214,51 @@ class PagedKVEngine:
 
     def swap_out(self, seq_id: int) -> torch.Tensor:
         """Move a live sequence's blocks to pinned host memory and release
-        them ([impl-detail] "异构内存支持" evict_to_cpu): gather on the device,
-        then one device-to-host copy on the current stream (the host tensor
-        holds the data once the stream has passed it).  Returns the host
-        copy, which swap_in takes back: one pinned tensor [n, 2, H_kv, bs, D],
-        or for an 8-bit pool the pair (codes, scale bytes [n, 2, H_kv, bs]).  The sequence's row is left to the
-        caller."""
+        them ([impl-detail] "异构内存支持" evict_to_cpu): gather on the device
+        (on the current stream, so it reads the blocks before any later work
+        there reuses them), then one device-to-host copy on the engine's copy
+        stream, which overlaps the decode steps queued after it.  Returns the
+        host copy, which swap_in takes back: one pinned tensor
+        [n, 2, H_kv, bs, D], or for an 8-bit pool the pair (codes, scale bytes
+        [n, 2, H_kv, bs]).  It holds the data once wait_swap(seq_id) has
+        returned; swap_in waits for the copy by itself.  The sequence's row is
+        left to the caller."""
         ids = self.manager.swap_out(seq_id)
         if self.fp8:
             staged = gather_blocks_fp8(ids, self.key_cache, self.value_cache, self.key_scales, self.value_scales)
         else:
             staged = (gather_blocks(ids, self.key_cache, self.value_cache),)
         host = tuple(torch.empty(t.shape, dtype=t.dtype, pin_memory=True) for t in staged)
-        for h, t in zip(host, staged):
-            h.copy_(t, non_blocking=True)
+        if self._copy_stream is None:
+            self._copy_stream = torch.cuda.Stream(self.device)
+        cs = self._copy_stream
+        cs.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(cs):
+            for h, t in zip(host, staged):
+                h.copy_(t, non_blocking=True)
+        for t in staged:
+            t.record_stream(cs)        # its memory is not handed out again before the copy has read it
+        self._swap_done[seq_id] = cs.record_event()
         for r, s in list(self.row_seq.items()):
             if s == seq_id:
                 del self.row_seq[r]
         return host if self.fp8 else host[0]
+
+    def wait_swap(self, seq_id: int) -> None:
+        """Blocks the host until the device-to-host copy of seq_id's last
+        swap_out has landed."""
+        ev = self._swap_done.get(seq_id)
+        if ev is not None:
+            ev.synchronize()
 
     def swap_in(self, seq_id: int, row: int, host: torch.Tensor) -> None:
         """Bring a swapped sequence back into ``row`` on fresh blocks
         ([impl-detail] "异构内存支持" prefetch_to_gpu): one host-to-device
         copy, a scatter, and the table row published."""
         ids = self.manager.swap_in(seq_id)
+        ev = self._swap_done.pop(seq_id, None)
+        if ev is not None:             # the host copy is read after it has been written
+            torch.cuda.current_stream(self.device).wait_event(ev)
         if self.fp8:
             codes, scales = (t.to(self.device, non_blocking=True) for t in host)
             scatter_blocks_fp8(codes, scales, ids, self.key_cache, self.value_cache, self.key_scales,
@@ -251,6 +274,7 @@ class PagedKVEngine:
 
     def free(self, seq_id: int) -> None:
         self.manager.free_sequence(seq_id)
+        self._swap_done.pop(seq_id, None)
         for r, s in list(self.row_seq.items()):
             if s == seq_id:
                 del self.row_seq[r]

@@ -69,3 +69,44 @@ def test_engine_swap_round_trip_is_bit_exact():
     after = eng.attend(q, d_lens, 0.088, int(lens.max()))
     torch.cuda.synchronize()
     assert torch.equal(before.view(torch.int32), after.view(torch.int32))
+
+
+def test_swap_out_copy_overlaps_later_work():
+    """swap_out's device-to-host copy runs on the engine's copy stream: work
+    queued after it on the compute stream (fresh allocations the size of the
+    staging array, filled with junk; a prompt written over the released
+    blocks; an attention launch) neither waits for it nor disturbs what it
+    copies."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    print("[gpu] swap-out copy overlapping later work", flush=True)
+    rng = np.random.default_rng(72)
+    hq, hkv, bs, D = 28, 4, 16, 128
+    lens = np.array([4096, 300, 700])
+    B = len(lens)
+    N = int(np.ceil(lens / bs).sum()) + 40
+    eng = PagedKVEngine(N, hkv, bs, D, torch.bfloat16, B + 1, N, rng.permutation(N), num_q_heads=hq)
+    k = to_device(synth.normal(rng, (int(lens.sum()), hkv, D), "bf16"), "bf16")
+    v = to_device(synth.normal(rng, (int(lens.sum()), hkv, D), "bf16"), "bf16")
+    eng.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], k, v)
+    q = to_device(synth.normal(rng, (B, hq, D), "bf16"), "bf16")
+    d_lens = torch.from_numpy(lens.astype(np.int32)).cuda()
+    before = eng.attend(q, d_lens, 0.088, int(lens.max())).clone()
+    ids = np.array(eng.manager.block_table(0), dtype=np.int32)
+    ref = pkv.gather_blocks(ids, eng.key_cache, eng.value_cache).clone()
+    host = eng.swap_out(0)
+    for _ in range(4):
+        junk = torch.empty_like(ref)
+        junk.view(torch.int16).fill_(-1)
+    n_other = eng.manager.num_free_blocks() * bs
+    eng.prefill(99, B, to_device(synth.normal(rng, (n_other, hkv, D), "bf16"), "bf16"),
+                to_device(synth.normal(rng, (n_other, hkv, D), "bf16"), "bf16"))
+    assert set(eng.manager.block_table(99)) & set(ids.tolist())
+    d_lens2 = torch.tensor([0, 300, 700], dtype=torch.int32, device="cuda")
+    eng.attend(q, d_lens2, 0.088, int(lens.max()))
+    eng.wait_swap(0)
+    assert torch.equal(host.view(torch.int16), ref.cpu().view(torch.int16))
+    eng.free(99)
+    eng.swap_in(0, 0, host)
+    after = eng.attend(q, d_lens, 0.088, int(lens.max()))
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int32), after.view(torch.int32))
