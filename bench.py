@@ -310,7 +310,8 @@ def measure_serving(cfg, args):
     fresh prompt.  Every step's inputs and every refill's prompt K/V are
     generated and placed in HBM before the timed loop.  Per step, HIP events
     bracket the decode step (host append, the fused write + attention launch,
-    the merge) and the refills after it (release, admission, prompt write).
+    the merge) and the refills after it (releases, then the step's admissions
+    as one prefill_many: allocation, one prompt write, one table update).
     Prints one JSON line: K/V GB/s and decode tokens/s over the decode-step
     time, and the refill time separately."""
     import torch
@@ -331,8 +332,12 @@ def measure_serving(cfg, args):
     eng = PagedKVEngine(cfg.num_blocks, H, cfg.block_size, D, tdtype, B, width, None, num_q_heads=cfg.num_q_heads)
     eng.prefill_many(list(range(B)), list(range(B)), [int(x) for x in tr.prompt_lens],
                      dev(np.concatenate(tr.hist_k)), dev(np.concatenate(tr.hist_v)))
+    # each step's refills as one admission: their prompts concatenated
     steps = [(dev(st.new_k), dev(st.new_v), dev(st.q),
-              [(r.row, r.new_id, dev(r.k), dev(r.v)) for r in st.refills]) for st in tr.steps]
+              ([r.row for r in st.refills], [r.new_id for r in st.refills], [r.k.shape[0] for r in st.refills],
+               dev(np.concatenate([r.k for r in st.refills])) if st.refills else None,
+               dev(np.concatenate([r.v for r in st.refills])) if st.refills else None))
+             for st in tr.steps]
     log(f"serving trace: {len(steps)} steps generated and resident in {time.perf_counter() - t_gen:.1f}s")
     row_ids = np.arange(B, dtype=np.int64)
     out = torch.empty((B, cfg.num_q_heads, D), dtype=torch.float32, device="cuda")
@@ -346,12 +351,14 @@ def measure_serving(cfg, args):
         eng.decode_step(row_ids, k, v, q, cfg.scale, out=out)
         kv_bytes += int(eng.lens[:B].astype(np.int64).sum()) * H * 2 * D * elem
         ev[1].record()
-        for row, new_id, rk, rv in refills:
-            eng.free(int(row_ids[row]))
-            eng.prefill(new_id, row, rk, rv)
-            row_ids[row] = new_id
-            n_refill += 1
-            refill_tokens += rk.shape[0]
+        rows, new_ids, plens, rk, rv = refills
+        if rows:
+            for row, new_id in zip(rows, new_ids):
+                eng.free(int(row_ids[row]))
+                row_ids[row] = new_id
+            eng.prefill_many(new_ids, rows, plens, rk, rv)
+            n_refill += len(rows)
+            refill_tokens += int(sum(plens))
         ev[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

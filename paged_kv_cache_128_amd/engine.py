@@ -192,7 +192,8 @@ class PagedKVEngine:
     def prefill_many(self, seq_ids: Sequence[int], rows: Sequence[int], lengths: Sequence[int],
                      key: torch.Tensor, value: torch.Tensor) -> np.ndarray:
         """Admit several sequences whose prompt rows are concatenated in
-        ``key``/``value`` ([sum(lengths), H_kv, D]) with one write launch."""
+        ``key``/``value`` ([sum(lengths), H_kv, D]) with one write launch and
+        one table publication (``rows`` distinct)."""
         all_slots = []
         for sid, n in zip(seq_ids, lengths):
             all_slots.append(self.manager.allocate_for_prefill(int(sid), int(n)))
@@ -200,8 +201,7 @@ class PagedKVEngine:
         if slots.size:
             d_slots = self._stage.to_device(slots)
             self._write(key, value, d_slots)
-        for sid, row in zip(seq_ids, rows):
-            self._publish_row(int(sid), int(row))
+        self._publish_rows(seq_ids, rows)
         return slots
 
     def share_prefix(self, donor_id: int, seq_id: int, row: int, num_tokens: int) -> None:
@@ -271,6 +271,20 @@ class PagedKVEngine:
         tab = self.manager.block_tables([seq_id], self.width, -1)
         self._stage.copy_into(self.tables[row], tab[0])
         self.row_seq[row] = seq_id
+
+    def _publish_rows(self, seq_ids: Sequence[int], rows: Sequence[int]):
+        """The table rows of several sequences at once (distinct rows): one
+        table read from the manager, one staged copy, one row scatter."""
+        if len(rows) == 1:
+            self._publish_row(int(seq_ids[0]), int(rows[0]))
+            return
+        if len(rows) == 0:
+            return
+        tab = self.manager.block_tables([int(x) for x in seq_ids], self.width, -1)
+        d_rows = self._stage.to_device(np.asarray(rows, dtype=np.int64))
+        self.tables.index_copy_(0, d_rows, self._stage.to_device(tab).view(len(rows), self.width))
+        for sid, row in zip(seq_ids, rows):
+            self.row_seq[int(row)] = int(sid)
 
     def free(self, seq_id: int) -> None:
         self.manager.free_sequence(seq_id)
