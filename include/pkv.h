@@ -530,14 +530,18 @@ int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const i
  * paged_prefill_attention computes, with every cached row read back as
  * decode(code) * 2^(scale byte - 127) ([impl-detail] "实践建议": a block's
  * KV quantised on its own).  The blocks the sequences hold (the first
- * ceil(L_b / bs) table entries) are first dequantised into a bf16 staging
- * pool and table in `workspace` (device, 256-byte aligned, at least
- * paged_prefill_attention_fp8_workspace_size bytes, owned by the caller,
- * overwritten), then the 16-bit kernel runs on them.  The staging holds
- * every read-back value exactly for row scales 2^-124 .. 2^119.  q_dtype
- * must be PKV_BF16 (bf16 queries; fp16's range cannot hold every 8-bit row:
- * UNSUPPORTED); out_dtype PKV_F32 or PKV_BF16.  Other arguments as for
- * paged_prefill_attention.  Errors: INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ * ceil(L_b / bs) table entries) are first dequantised into a 16-bit staging
+ * pool of the queries' type and a table in `workspace` (device, 256-byte
+ * aligned, at least paged_prefill_attention_fp8_workspace_size bytes, owned
+ * by the caller, overwritten), then the 16-bit kernel runs on them.  q_dtype
+ * PKV_BF16 or PKV_F16 (else UNSUPPORTED); out_dtype PKV_F32 or q_dtype
+ * (else INVALID).  A bf16 staging holds every read-back value exactly for
+ * row scales 2^-124 .. 2^119.  An fp16 staging holds them exactly for row
+ * scales 2^-15 .. 2^7, which covers rows quantised from fp16 tensors except
+ * those within 0.05 % of fp16's largest value; values beyond fp16's range
+ * clamp to +-65504, and rows with smaller scales keep their values to the
+ * nearest 2^-24.  Other arguments as for paged_prefill_attention.  Errors:
+ * INVALID, UNSUPPORTED, WORKSPACE, HIP.
  */
 size_t paged_prefill_attention_fp8_workspace_size(int32_t num_seqs, int32_t max_context_len,
                                                   const pkv_cache_layout* layout);

@@ -593,7 +593,7 @@ def paged_prefill_attention_fp8(q, q_start, key_cache, value_cache, key_scales, 
                                 context_lens, scale: float, max_q_len: int, max_context_len: Optional[int] = None,
                                 out=None, out_dtype=None, workspace=None, stream=None):
     """Chunked-prefill causal attention over 8-bit blocks (see
-    paged_prefill_attention_fp8 in pkv.h): bf16 q [T, H_q, D]; the other
+    paged_prefill_attention_fp8 in pkv.h): bf16 or fp16 q [T, H_q, D]; the other
     tensors as for paged_prefill_attention; ``workspace`` (uint8 device
     tensor, allocated here when None) holds the 16-bit staging."""
     torch = _torch()
@@ -601,8 +601,8 @@ def paged_prefill_attention_fp8(q, q_start, key_cache, value_cache, key_scales, 
     _check_scales(key_cache, key_scales, value_scales)
     T, hq, d = q.shape
     B = context_lens.shape[0]
-    if d != lay.head_dim or q.dtype != torch.bfloat16 or not q.is_contiguous():
-        raise ValueError("q must be contiguous bf16 [T, H_q, head_dim]")
+    if d != lay.head_dim or q.dtype not in (torch.bfloat16, torch.float16) or not q.is_contiguous():
+        raise ValueError("q must be contiguous bf16 or fp16 [T, H_q, head_dim]")
     if q_start.dtype != torch.int32 or q_start.shape != (B + 1,) or not q_start.is_contiguous():
         raise ValueError("q_start must be contiguous int32 [B + 1]")
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous():

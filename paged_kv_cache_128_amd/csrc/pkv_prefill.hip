@@ -485,6 +485,11 @@ int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_sta
 // as decode(code) * 2^(scale byte - 127), into 16-bit staging block
 // b * W + j, and workgroup (b, j, K, head 0) writes that block's id into
 // the staging table [B, W]; blocks past a sequence's length are skipped.
+// The staging type is the queries': bf16 holds every row with a scale of
+// 2^-124 .. 2^119 exactly; fp16 every row with a scale of 2^-15 .. 2^7 (the
+// rows of fp16 tensors, short of the few within 0.05 % of fp16's largest
+// value), larger values clamping to +-65504 and smaller scales keeping
+// their values to the nearest 2^-24.
 struct DequantArgs {
   const uint8_t* kc;
   const uint8_t* vc;
@@ -504,7 +509,14 @@ struct DequantArgs {
   int32_t heads;
   int32_t width;            // W
   int32_t max_len;
+  int32_t to_f16;           // staging type: fp16 (else bf16)
 };
+
+// fp16's largest finite value in place of anything larger in magnitude;
+// NaN stays NaN.
+__device__ __forceinline__ float clamp_f16(float x) {
+  return fabsf(x) > 65504.f ? copysignf(65504.f, x) : x;
+}
 
 __global__ void __launch_bounds__(256)
 dequant_blocks_kernel(DequantArgs a) {
@@ -538,8 +550,10 @@ dequant_blocks_kernel(DequantArgs a) {
                         __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w.y), true)};
     uint32_t packed[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      packed[k] = pack2<PKV_BF16>(__builtin_amdgcn_ldexpf(v[k].x, e), __builtin_amdgcn_ldexpf(v[k].y, e));
+    for (int k = 0; k < 4; ++k) {
+      const float x0 = __builtin_amdgcn_ldexpf(v[k].x, e), x1 = __builtin_amdgcn_ldexpf(v[k].y, e);
+      packed[k] = a.to_f16 ? pack2<PKV_F16>(clamp_f16(x0), clamp_f16(x1)) : pack2<PKV_BF16>(x0, x1);
+    }
     *reinterpret_cast<uint4*>(o + 8 * static_cast<int64_t>(i)) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   }
 }
@@ -585,9 +599,9 @@ extern "C" int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const v
   if (pkv::check_layout(l) != PKV_OK || num_seqs < 0 || max_q_len < 0 || num_q_heads <= 0 ||
       max_context_len < 0 || block_table_stride < 0)
     return PKV_ERR_INVALID;
-  if (l->dtype != PKV_FP8_E4M3 || q_dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (l->dtype != PKV_FP8_E4M3 || (q_dtype != PKV_BF16 && q_dtype != PKV_F16)) return PKV_ERR_UNSUPPORTED;
   if (l->head_dim != kD || l->block_size % kKeys != 0) return PKV_ERR_UNSUPPORTED;
-  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != q_dtype) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
     return PKV_ERR_INVALID;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
@@ -628,6 +642,7 @@ extern "C" int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const v
     d.heads = l->num_kv_heads;
     d.width = W;
     d.max_len = max_context_len;
+    d.to_f16 = q_dtype == PKV_F16;
     const int64_t grid = blocks * 2 * l->num_kv_heads;
     if (grid > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(dequant_blocks_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s, d);
@@ -635,7 +650,7 @@ extern "C" int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const v
   }
   pkv_cache_layout sl = *l;
   sl.num_blocks = static_cast<int32_t>(blocks > 0 ? blocks : 1);
-  sl.dtype = PKV_BF16;
+  sl.dtype = q_dtype;
   sl.block_stride = block_elems;
   sl.head_stride = static_cast<int64_t>(l->block_size) * l->head_dim;
   return prefill_16(out, out_dtype, q, q_start, context_lens, num_seqs, max_q_len, staging,

@@ -150,8 +150,7 @@ class PagedKVEngine:
         slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
             self._write(key, value, self._stage.to_device(slots))
-        for sid, row in zip(seq_ids, rows):
-            self._publish_row(int(sid), int(row))
+        self._publish_rows(seq_ids, rows)
         B = len(seq_ids)
         q_start = np.concatenate([[0], np.cumsum(np.asarray(chunk_lens, dtype=np.int64))]).astype(np.int32)
         d_qs = self._stage.to_device(q_start)

@@ -94,16 +94,18 @@ def test_prefill_edge_cases():
     assert (dec[0] - out[14]).abs().max().item() <= 2e-3
 
 
-@pytest.mark.parametrize("hq,hkv,bs,out_dtype", [(28, 4, 16, None), (12, 2, 32, "bf16")])
-def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype):
+@pytest.mark.parametrize("hq,hkv,bs,out_dtype,dt", [(28, 4, 16, None, "bf16"), (12, 2, 32, "bf16", "bf16"),
+                                                   (28, 4, 16, None, "f16"), (12, 2, 32, "f16", "f16")])
+def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype, dt):
     """Chunked prefill over an 8-bit pool (paged_prefill_attention_fp8:
-    the sequences' blocks dequantised into the 16-bit staging, then the
-    prefill kernel): the quantising writes bit for bit (codes and scale
-    bytes, poison included) and the attention within 2e-3 of the oracle's
-    8-bit prefill attention, over two chunks per sequence."""
+    the sequences' blocks dequantised into a 16-bit staging of the queries'
+    type, then the prefill kernel): the quantising writes bit for bit (codes
+    and scale bytes, poison included) and the attention within 2e-3 of the
+    oracle's 8-bit prefill attention, over two chunks per sequence, with
+    bf16 and with fp16 rows and queries."""
     from oracle import quant
     from paged_kv_cache_128_amd.engine import PagedKVEngine
-    _banner(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} out={out_dtype}")
+    _banner(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} out={out_dtype} {dt}")
     rng = np.random.default_rng(90 + hq)
     D = 128
     first = [1, 37, 64, 130, 200, 5]
@@ -120,33 +122,33 @@ def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype):
     od = None if out_dtype is None else TORCH_DTYPE[out_dtype]
     for chunk in (first, second):
         T = sum(chunk)
-        k = synth.normal(rng, (T, hkv, D), "bf16")
-        v = synth.normal(rng, (T, hkv, D), "bf16")
-        q = synth.normal(rng, (T, hq, D), "bf16")
+        k = synth.normal(rng, (T, hkv, D), dt)
+        v = synth.normal(rng, (T, hkv, D), dt)
+        q = synth.normal(rng, (T, hq, D), dt)
         slots = []
         for b, n in enumerate(chunk):
             slots += (om.append_tokens(b, n) if om.is_live(b) else om.allocate_for_prefill(b, n))
-        quant.write_kv_fp8(oracle.widen(k, "bf16").astype(np.float32), oracle.widen(v, "bf16").astype(np.float32),
+        quant.write_kv_fp8(oracle.widen(k, dt).astype(np.float32), oracle.widen(v, dt).astype(np.float32),
                            slots, *o, bs)
         qs = np.concatenate([[0], np.cumsum(chunk)])
-        ref = quant.prefill_attention_fp8(q, "bf16", qs, *o, om.block_tables(list(range(B)), width, -1),
+        ref = quant.prefill_attention_fp8(q, dt, qs, *o, om.block_tables(list(range(B)), width, -1),
                                           om.context_lens(list(range(B))), scale)
         out = None if od is None else torch.empty((T, hq, D), dtype=od, device="cuda")
-        got = eng.prefill_chunk(list(range(B)), list(range(B)), chunk, to_device(k, "bf16"),
-                                to_device(v, "bf16"), to_device(q, "bf16"), scale, out=out)
+        got = eng.prefill_chunk(list(range(B)), list(range(B)), chunk, to_device(k, dt),
+                                to_device(v, dt), to_device(q, dt), scale, out=out)
         torch.cuda.synchronize()
         for g, w in zip((eng.key_cache, eng.value_cache, eng.key_scales, eng.value_scales), o):
             assert np.array_equal(g.contiguous().view(torch.uint8).cpu().numpy(), w)
         err = np.abs(got.double().cpu().numpy() - ref).max()
-        tol = 2e-3 if od is None else 2e-3 + np.abs(ref).max() * 2.0 ** -8
+        tol = 2e-3 if od is None else 2e-3 + np.abs(ref).max() * 2.0 ** (-8 if dt == "bf16" else -11)
         _banner(f"fp8 prefill chunk {chunk}: max abs err {err:.3e}")
         assert err <= tol, err
 
 
-def test_fp8_prefill_refuses_f16_queries_and_small_workspace():
-    """Host-side checks of paged_prefill_attention_fp8: fp16 queries are
-    UNSUPPORTED (fp16 cannot hold every 8-bit row), a short workspace is a
-    WORKSPACE error; nothing is launched."""
+def test_fp8_prefill_refuses_bad_types_and_small_workspace():
+    """Host-side checks of paged_prefill_attention_fp8: fp32 queries are
+    UNSUPPORTED, an output type other than fp32 or the queries' is INVALID,
+    a short workspace is a WORKSPACE error; nothing is launched."""
     lib = pkv.load_library()
     N, H, bs, D = 8, 2, 16, 128
     g = pkv.new_fp8_pool(N, H, bs, D, "cuda")
@@ -154,8 +156,11 @@ def test_fp8_prefill_refuses_f16_queries_and_small_workspace():
     fake = g[0].data_ptr()
     need = lib.paged_prefill_attention_fp8_workspace_size(2, 64, ctypes.byref(lay))
     assert need >= 2 * 4 * 2 * H * bs * D * 2
-    args = lambda qd, ws, wsb: lib.paged_prefill_attention_fp8(
-        fake, pkv.PKV_F32, fake, qd, fake, fake, 2, 16, g[1].data_ptr(), g[2].data_ptr(), g[4].data_ptr(),
+    args = lambda qd, od, ws, wsb: lib.paged_prefill_attention_fp8(
+        fake, od, fake, qd, fake, fake, 2, 16, g[1].data_ptr(), g[2].data_ptr(), g[4].data_ptr(),
         g[5].data_ptr(), ctypes.byref(lay), fake, 4, 4, 64, 0.1, ws, wsb, None)
-    assert args(pkv.PKV_F16, fake, need) == -5
-    assert args(pkv.PKV_BF16, fake, need - 1) == -7
+    assert args(pkv.PKV_F32, pkv.PKV_F32, fake, need) == -5
+    assert args(pkv.PKV_F16, pkv.PKV_BF16, fake, need) == -1
+    assert args(pkv.PKV_BF16, pkv.PKV_F16, fake, need) == -1
+    assert args(pkv.PKV_BF16, pkv.PKV_F32, fake, need - 1) == -7
+    assert args(pkv.PKV_F16, pkv.PKV_F32, fake, need - 1) == -7
