@@ -279,6 +279,8 @@ class PagedKVEngine:
             return
         if len(rows) == 0:
             return
+        if len(set(int(r) for r in rows)) != len(rows):
+            raise ValueError("rows must be distinct")
         tab = self.manager.block_tables([int(x) for x in seq_ids], self.width, -1)
         d_rows = self._stage.to_device(np.asarray(rows, dtype=np.int64))
         self.tables.index_copy_(0, d_rows, self._stage.to_device(tab).view(len(rows), self.width))
