@@ -40,6 +40,11 @@ from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_st
                prefill_fp8_workspace_size, workspace_size)
 
 
+def _check_distinct(rows: Sequence[int]) -> None:
+    if len(set(int(r) for r in rows)) != len(rows):
+        raise ValueError("rows must be distinct")
+
+
 class _HostStage:
     """Pinned host staging for the small host-to-device copies of admissions
     (slots, table rows, chunk offsets): a bump arena whose copies are queued
@@ -136,7 +141,8 @@ class PagedKVEngine:
         concatenated in order) are written, then every chunk's query rows
         (q [sum(chunk_lens), H_q, D]) attend causally over their sequence
         (paged_prefill_attention; over an 8-bit pool paged_prefill_attention_fp8,
-        bf16 q).  Returns out [sum(chunk_lens), H_q, D]."""
+        bf16 or fp16 q); ``rows`` distinct.  Returns out [sum(chunk_lens), H_q, D]."""
+        _check_distinct(rows)
         all_slots, lens = [], []
         for sid, row, n in zip(seq_ids, rows, chunk_lens):
             sid, n = int(sid), int(n)
@@ -193,6 +199,7 @@ class PagedKVEngine:
         """Admit several sequences whose prompt rows are concatenated in
         ``key``/``value`` ([sum(lengths), H_kv, D]) with one write launch and
         one table publication (``rows`` distinct)."""
+        _check_distinct(rows)
         all_slots = []
         for sid, n in zip(seq_ids, lengths):
             all_slots.append(self.manager.allocate_for_prefill(int(sid), int(n)))
@@ -279,8 +286,6 @@ class PagedKVEngine:
             return
         if len(rows) == 0:
             return
-        if len(set(int(r) for r in rows)) != len(rows):
-            raise ValueError("rows must be distinct")
         tab = self.manager.block_tables([int(x) for x in seq_ids], self.width, -1)
         d_rows = self._stage.to_device(np.asarray(rows, dtype=np.int64))
         self.tables.index_copy_(0, d_rows, self._stage.to_device(tab).view(len(rows), self.width))
