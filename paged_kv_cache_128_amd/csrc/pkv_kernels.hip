@@ -1016,10 +1016,11 @@ constexpr int kStreamMaxHeads = 8;
 constexpr int kStreamMaxWaves = 8;
 constexpr int kStreamSlots = 4;          // partial slots per job
 // Percent of a job's chunks taken by the worker in SIMD wave slot 0 when its
-// partner is in slot 1: under this load the second slot's wave takes ~26%
-// longer per chunk (measured per wave with the real-time counter), and a
-// balanced pair splits about 56 : 44.
-constexpr int kSlot0Share = 56;
+// partner is in slot 1: under this load the second slot's wave takes longer
+// per chunk (about 26 %, measured per wave with the real-time counter, when
+// the P.V ran on the vector ALU).  With both products on the matrix cores a
+// sweep of 52 .. 66 put the kernel's time lowest at 60 : 40.
+constexpr int kSlot0Share = 60;
 
 // How many of a job's n tiles its front worker takes.  The front worker is
 // wave `job` of the workgroup, the back worker wave J + job (paired: two
