@@ -992,6 +992,7 @@ struct StreamArgs {
   int32_t range_cap;     // tiles one workgroup may hold
   int32_t num_ranges;    // W
   int32_t ranges_per_wg; // R
+  int32_t slot0_share;   // percent of a split job's tiles for its slot-0 worker
   float scale_log2;
   // decode-step form only: the step's new rows [B, H_kv, D] and where the
   // step's write goes (pool, table of table_rows rows, device lengths)
@@ -1019,20 +1020,23 @@ constexpr int kStreamSlots = 4;          // partial slots per job
 // partner is in slot 1: under this load the second slot's wave takes longer
 // per chunk (about 26 %, measured per wave with the real-time counter, when
 // the P.V ran on the vector ALU).  With both products on the matrix cores a
-// sweep of 52 .. 66 put the kernel's time lowest at 60 : 40.
+// sweep of 52 .. 66 put the kernel's time lowest at 60 : 40.  The 8-bit
+// kernel's tiles cost less per byte in flight, so it has its own share: a
+// sweep of 52 .. 64 put it lowest at 56 : 44.
 constexpr int kSlot0Share = 60;
+constexpr int kSlot0Share8 = 56;
 
 // How many of a job's n tiles its front worker takes.  The front worker is
 // wave `job` of the workgroup, the back worker wave J + job (paired: two
 // waves per job) or the wave that runs job's back after its own front
 // (J - 4 + job) mod J.  Waves 0-3 sit in SIMD wave slot 0, waves 4-7 in
-// slot 1; the slot-0 worker takes kSlot0Share percent of the tiles when
-// its partner is in slot 1, else the split is even.
-__device__ __forceinline__ int part_split(int n, int job, int J, bool paired) {
+// slot 1; the slot-0 worker takes `share` percent of the tiles when its
+// partner is in slot 1, else the split is even.
+__device__ __forceinline__ int part_split(int n, int job, int J, bool paired, int share) {
   const int fw = job;
   const int bw = paired ? J + job : (job + J - 4 % J) % J;
   if ((fw >> 2) == (bw >> 2)) return (n + 1) / 2;
-  return (fw >> 2) == 0 ? (n * kSlot0Share + 50) / 100 : (n * (100 - kSlot0Share) + 50) / 100;
+  return (fw >> 2) == 0 ? (n * share + 50) / 100 : (n * (100 - share) + 50) / 100;
 }
 constexpr int kStreamMaxRanges = 1024;   // W bound (merge kernel's piece list)
 
@@ -1388,7 +1392,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
     // The job's tiles [g0, g1) split at x: the front worker takes those
     // before, the back worker those from x on; both walk forward.
-    const int x = g0 + part_split(g1 - g0, job, J, PAIRED);
+    const int x = g0 + part_split(g1 - g0, job, J, PAIRED, a.slot0_share);
     const int p0 = back ? x : g0, p1 = back ? g1 : x;
     // the chunk from tile g of sequence b: up to CH tiles, within b and the part
     auto chunk_len = [&](int g, int b) { return min(CH, min(uni(S[b + 1]), p1) - g); };
@@ -1732,7 +1736,7 @@ attn_stream_merge_kernel(StreamArgs a) {
     if (r <= r_last) {
       const int g0 = range_start(r, total, W), g1 = range_start(r + 1, total, W);
       if (g0 < g1) {
-        const int x = g0 + part_split(g1 - g0, (r % R) * a.hkv + kvh, J, paired);
+        const int x = g0 + part_split(g1 - g0, (r % R) * a.hkv + kvh, J, paired, a.slot0_share);
         const int lo = max(g0, Sb), hi = min(g1, Se);
         if (lo < min(x, hi)) sl[n++] = r * kStreamSlots + (lo == g0 ? 0 : 1);
         if (max(x, lo) < hi) sl[n++] = r * kStreamSlots + (hi == g1 ? 2 : 3);
@@ -2239,6 +2243,7 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.range_cap = pl.range_cap;
       sa.num_ranges = pl.ranges;
       sa.ranges_per_wg = pl.ranges_per_wg;
+      sa.slot0_share = f8 ? kSlot0Share8 : kSlot0Share;
       sa.scale_log2 = scale * kLog2e;
       sa.new_k = step ? step->key : nullptr;
       sa.new_v = step ? step->value : nullptr;
