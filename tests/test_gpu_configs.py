@@ -2,7 +2,8 @@
 the long-context split-K workload and the serving trace, in the launch
 configuration bench.py times (the engine's decode step).  The cache write is
 compared bit for bit over the whole pool; attention is compared with the
-float64 oracle on sampled sequences (all query heads of each)."""
+float64 oracle on every output row (every sequence, every query head), and
+the largest error of each workload is printed."""
 import numpy as np
 import pytest
 import torch
@@ -29,15 +30,6 @@ def _check_pool(eng, kc_o, vc_o):
     assert np.array_equal(vb, vc_o.view(np.uint16)), "V pool differs from the oracle"
 
 
-def _sample(lens, k, seed):
-    order = np.argsort(lens)
-    rng = np.random.default_rng(seed)
-    pick = {int(order[0]), int(order[-1])}
-    while len(pick) < min(k, len(lens)):
-        pick.add(int(rng.integers(len(lens))))
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name,partition", [("qwen2_7b_b64", None), ("long_splitk", None),
                                             ("long_splitk", 0)])
 def test_full_size_decode_step(name, partition):
@@ -53,18 +45,20 @@ def test_full_size_decode_step(name, partition):
     assert np.array_equal(eng.tables.cpu().numpy(), st.block_tables)
     assert np.array_equal(eng.manager.context_lens(ids), st.context_lens)
     _check_pool(eng, st.key_cache, st.value_cache)
-    rows = _sample(wl.context_lens, 6, cfg.seed)
     ref = oracle.decode_attention(wl.q, st.key_cache, st.value_cache, st.block_tables,
-                                  st.context_lens, cfg.scale, cfg.dtype, seqs=rows)
-    err = np.abs(out[rows] - ref[rows]).max()
-    _banner(f"config {cfg.index}: rows {rows} max abs err {err:.3e}")
-    assert err <= 2e-3
+                                  st.context_lens, cfg.scale, cfg.dtype)
+    per_row = np.abs(out - ref).max(axis=(1, 2))
+    assert np.all(np.isfinite(per_row))
+    _banner(f"config {cfg.index} {name} partition={partition}: all {len(per_row)} rows, "
+            f"max abs err {per_row.max():.3e} (row {int(per_row.argmax())})")
+    assert per_row.max() <= 2e-3, np.flatnonzero(per_row > 2e-3)
 
 
 def test_serving_trace_200_steps():
     """256 rows, 200 decode steps with per-step finishes and refills: manager
-    slots equal the oracle's on every step, attention within 2e-3 on sampled
-    rows of sampled steps, and the whole pool bit-exact at the end."""
+    slots equal the oracle's on every step, attention within 2e-3 on all 256
+    rows of every 25th step and the last, and the whole pool bit-exact at
+    the end."""
     from paged_kv_cache_128_amd.engine import PagedKVEngine
     cfg = synth.CONFIGS["serving_trace"]
     tr_gpu = synth.serving_trace(cfg)
@@ -87,14 +81,13 @@ def test_serving_trace_200_steps():
         assert eng.slots[:B].tolist() == list(o_slots), f"slots differ at step {st_g.step}"
         if st_g.step % 25 == 0 or st_g.step == cfg.steps - 1:
             torch.cuda.synchronize()
-            rows = _sample(np.array([mgr.context_len(s) for s in o_rows]), 8, st_g.step)
-            tabs = mgr.block_tables([o_rows[r] for r in rows], width, -1)
-            lens = mgr.context_lens([o_rows[r] for r in rows])
-            ref = oracle.decode_attention(st_o.q[rows], kc, vc, tabs, lens, cfg.scale, cfg.dtype)
-            err = float(np.abs(out.double().cpu().numpy()[rows] - ref).max())
+            tabs = mgr.block_tables(list(o_rows), width, -1)
+            lens = mgr.context_lens(list(o_rows))
+            ref = oracle.decode_attention(st_o.q, kc, vc, tabs, lens, cfg.scale, cfg.dtype)
+            err = float(np.abs(out.double().cpu().numpy() - ref).max())
             worst = max(worst, err)
             checked += 1
-            _banner(f"step {st_g.step}: rows {rows} err {err:.2e}")
+            _banner(f"step {st_g.step}: all {B} rows, max abs err {err:.2e}")
             assert err <= 2e-3
         for r in st_g.refills:
             eng.free(int(row_ids[r.row]))
@@ -104,16 +97,16 @@ def test_serving_trace_200_steps():
     assert checked >= 9
     assert eng.manager.free_list() == mgr.free
     _check_pool(eng, kc, vc)
-    _banner(f"serving trace ok, worst sampled err {worst:.2e}")
+    _banner(f"serving trace ok: {checked} steps of {B} rows, max abs err {worst:.3e}")
 
 
 def test_full_size_fp8_decode_step():
     """The batch-64 workload with an 8-bit pool, in the launch configuration
     of the bench's 8-bit leg (one fused step: quantising write inside the
     attention launch, then the merge): tables and lengths as the oracle's
-    manager replay; every stored row of six sampled sequences (codes and
-    scale bytes, the step's new row included) bit for bit as the oracle's
-    quantiser; their attention within 2e-3 of the float64 oracle."""
+    manager replay; every stored row of every sequence (codes and scale
+    bytes, the step's new row included) bit for bit as the oracle's
+    quantiser; every output row within 2e-3 of the float64 oracle."""
     from paged_kv_cache_128_amd.engine import PagedKVEngine
     cfg = synth.CONFIGS["qwen2_7b_b64"]
     _banner("fp8 batch-64: generating")
@@ -136,7 +129,7 @@ def test_full_size_fp8_decode_step():
     assert np.array_equal(eng.tables.cpu().numpy(), tabs)
     assert np.array_equal(eng.d_lens[:B].cpu().numpy(), om.context_lens(list(range(B))))
     worst = 0.0
-    for b in _sample(wl.context_lens, 6, cfg.seed):
+    for b in range(B):
         L = int(wl.context_lens[b])
         nb = -(-L // bs)
         ids = torch.from_numpy(tabs[b, :nb].astype(np.int64)).cuda()
@@ -158,15 +151,15 @@ def test_full_size_fp8_decode_step():
         err = float(np.abs(out[b] - ref).max())
         worst = max(worst, err)
         assert err <= 2e-3, (b, err)
-    _banner(f"fp8 batch-64: max abs err {worst:.3e}")
+    _banner(f"fp8 batch-64: all {B} rows, max abs err {worst:.3e}")
 
 
 def test_full_size_prefill():
     """The bench's prefill launch shape: 8 prompts of 2048 tokens, H 28/4,
     bf16, each admitted as one chunk through the engine (the kernel's full
-    grid); the pool bit for bit as the oracle write; sampled rows (tile and
-    block edges, seeded picks; all query heads) within 2e-3 of the oracle's
-    prefill attention of that row over its sequence cut at the row."""
+    grid); the pool bit for bit as the oracle write; every query row of every
+    prompt (all query heads) within 2e-3 of the oracle's causal prefill
+    attention."""
     from paged_kv_cache_128_amd.engine import PagedKVEngine
     cfg = synth.CONFIGS["qwen2_7b_b64"]
     seqs, prompt = 8, 2048
@@ -194,14 +187,12 @@ def test_full_size_prefill():
     _check_pool(eng, okc, ovc)
     tabs = om.block_tables(list(range(seqs)), per, -1)
     assert np.array_equal(eng.tables.cpu().numpy(), tabs)
-    rows = sorted({0, 1, 15, 16, 31, 32, 63, 64, 127, 128, 129, 255, 1023, 1024, 2046, 2047} |
-                  {int(x) for x in rng.integers(0, prompt, 8)})
     worst = 0.0
-    for b in sorted({0, seqs - 1, int(rng.integers(1, seqs - 1))}):
-        for i in rows:
-            ref = oracle.prefill_attention(q[b * prompt + i][None], [0, 1], okc, ovc, tabs[b:b + 1], [i + 1],
-                                           scale, "bf16")[0]
-            err = float(np.abs(out[b * prompt + i] - ref).max())
-            worst = max(worst, err)
-            assert err <= 2e-3, (b, i, err)
-    _banner(f"prefill 8 x 2048: max abs err {worst:.3e}")
+    for b in range(seqs):
+        ref = oracle.prefill_attention(q[b * prompt:(b + 1) * prompt], [0, prompt], okc, ovc, tabs[b:b + 1],
+                                       [prompt], scale, "bf16")
+        err = float(np.abs(out[b * prompt:(b + 1) * prompt] - ref).max())
+        worst = max(worst, err)
+        _banner(f"prefill 8 x 2048: prompt {b}, all {prompt} rows, max abs err {err:.3e}")
+        assert err <= 2e-3, (b, err)
+    _banner(f"prefill 8 x 2048: all {seqs * prompt} rows, max abs err {worst:.3e}")

@@ -75,6 +75,39 @@ def test_swap_round_trip_restores_the_data():
     assert np.array_equal(oracle.gather_logical(vc, ids, 13), before_v)
 
 
+def test_gather_blocks_layout_pinned_to_the_written_rows():
+    """16-bit / fp32 swap staging, pinned to the rows that went in rather than
+    to scatter_blocks: entry j of the staged array is [2, H, bs, D] with
+    index 0 the K rows and index 1 the V rows of block ids[j] (the staging
+    layout the C header states), token t of the prompt at block
+    table[t // bs], row t % bs.  K and V carry different values (V = -K - 1),
+    so swapped halves, a transposed head / row axis or a wrong block order
+    all fail."""
+    N, H, bs, D, n = 6, 2, 4, 8, 10
+    m = BlockManager(N, bs, [4, 1, 5, 0, 3, 2])
+    kc, vc = oracle.new_pool(N, H, bs, D, np.array(np.nan, dtype=np.float32))
+    t_, h_, d_ = np.meshgrid(np.arange(n), np.arange(H), np.arange(D), indexing="ij")
+    k = (1000.0 * t_ + 100.0 * h_ + d_).astype(np.float32)        # [n, H, D]
+    v = -k - 1.0
+    oracle.write_kv(k, v, m.allocate_for_prefill(0, n), kc, vc, bs)
+    table = m.block_table(0)
+    assert table == [4, 1, 5]
+    ids = [5, 4, 1]
+    staged = oracle.gather_blocks(ids, kc, vc)
+    assert staged.shape == (3, 2, H, bs, D)
+    for j, blk in enumerate(ids):
+        lb = table.index(blk)
+        for off in range(bs):
+            t = lb * bs + off
+            for h in range(H):
+                if t < n:
+                    assert np.array_equal(staged[j, 0, h, off], k[t, h]), (j, off, h)
+                    assert np.array_equal(staged[j, 1, h, off], v[t, h]), (j, off, h)
+                else:                                  # block 5's unused tail: untouched poison
+                    assert np.all(np.isnan(staged[j, :, h, off]))
+    assert oracle.gather_blocks([], kc, vc).shape == (0, 2, H, bs, D)
+
+
 @pytest.mark.parametrize("seed,n_blocks,bs,sort", [(61, 30, 4, False), (62, 12, 1, True), (63, 20, 16, False)])
 def test_swap_traces_match_c_manager(seed, n_blocks, bs, sort):
     rng = np.random.default_rng(seed)
