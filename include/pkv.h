@@ -496,6 +496,31 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
                           int32_t max_context_len, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same step, with the same results bit for bit, and the same arguments
+ * except the workspace.  The split-K partials live in a device array the
+ * library owns, PKV_NOALLOC_SCRATCH_BYTES per GPU, held from the first call
+ * on that GPU until the process ends; the call allocates nothing.  Calls
+ * whose workspace (paged_decode_attention_workspace_size with
+ * partition_tokens 0) exceeds that size return PKV_ERR_WORKSPACE without
+ * doing anything; every shape the stream path takes on a 256-CU device fits.
+ * All calls on one GPU share its array, whatever their stream: calls that
+ * may overlap on one GPU race and give wrong results; the caller serialises
+ * them (one stream, or events).  The array needs no initialisation; each
+ * call overwrites what it reads.  The current device must be the one that
+ * runs `stream`.  Errors: as pkv_decode_step, WORKSPACE as above, HIP when
+ * the array's device address cannot be found.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (36u << 20)
+int pkv_decode_step_noalloc(void* out, int32_t out_dtype, const void* q, const void* key,
+                            const void* value, const int64_t* slots, const int32_t* lens,
+                            int32_t num_seqs, void* key_cache, void* value_cache,
+                            const pkv_cache_layout* layout, int32_t* block_tables,
+                            int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* stream);
+
 /* --------------------------------------------------------- prefill attention */
 /*
  * Chunked-prefill attention through block tables: sequence b holds

@@ -133,6 +133,9 @@ SIGNATURES = {
     "pkv_decode_step": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
                                        ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
                                        ctypes.c_float, _P, _SZ, _P]),
+    "pkv_decode_step_noalloc": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
+                                               ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
+                                               ctypes.c_float, _P]),
     "pkv_decode_step_partial": (ctypes.c_int, [_P, _I32, _P, _P, _P, _PI64, _PI32, _I32, _P, _P,
                                                ctypes.POINTER(CacheLayout), _P, _I32, _P, _I32, _I32,
                                                ctypes.c_float, _P, _SZ, _P]),
@@ -863,6 +866,45 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
     return out
 
 
+NOALLOC_SCRATCH_BYTES = 36 << 20     # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def decode_step_noalloc(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, value_cache,
+                        block_tables, lens_out, scale: float, max_context_len: int, out,
+                        stream=None):
+    """pkv_decode_step_noalloc: decode_step with the split-K partials in the
+    library's own per-GPU device array instead of a workspace, so the C call
+    allocates nothing (``out`` is the caller's).  Calls on one GPU must not
+    overlap (they share that array)."""
+    torch = _torch()
+    lay = cache_layout(key_cache, value_cache)
+    n, hq, d = q.shape
+    if key.shape != (n, lay.num_kv_heads, lay.head_dim) or value.shape != key.shape:
+        raise ValueError("key/value must be [num_rows, H_kv, head_dim]")
+    if not (key.is_contiguous() and value.is_contiguous() and q.is_contiguous()):
+        raise ValueError("q, key and value must be contiguous")
+    if key.dtype != key_cache.dtype or value.dtype != key_cache.dtype or q.dtype != key_cache.dtype:
+        raise ValueError("q/key/value dtype must equal the cache dtype")
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    if slots.shape != (n,) or lens.shape != (n,):
+        raise ValueError("slots and lens must have one entry per row")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.stride(1) != 1 \
+            or block_tables.shape[0] < n:
+        raise ValueError("block_tables must be int32 [>= n, W] with unit column stride")
+    if lens_out.dtype != torch.int32 or lens_out.numel() < n or not lens_out.is_contiguous():
+        raise ValueError("lens_out must be a contiguous int32 tensor of at least n entries")
+    if out.shape != (n, hq, d) or not out.is_contiguous():
+        raise ValueError("out must be contiguous [n, H_q, head_dim]")
+    st = _lib_handle().pkv_decode_step_noalloc(
+        out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
+        _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
+        value_cache.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(), block_tables.stride(0),
+        lens_out.data_ptr(), hq, int(max_context_len), float(scale), _stream_handle(stream))
+    _check(st, "pkv_decode_step_noalloc")
+    return out
+
+
 def _record(event, stream):
     if stream is None:
         event.record()
@@ -946,6 +988,7 @@ __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
     "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
+    "decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
     "copy_blocks", "gather_blocks", "scatter_blocks", "copy_blocks_fp8", "gather_blocks_fp8",
     "scatter_blocks_fp8", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",
     "paged_decode_attention_fp8", "PKV_FP8_E4M3", "paged_prefill_attention", "decode_step_fp8",

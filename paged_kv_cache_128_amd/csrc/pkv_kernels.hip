@@ -2383,6 +2383,37 @@ int paged_decode_attention_merge(void* out, int32_t out_dtype, const void* q,
                         scale, l, partition_tokens, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+// Workspace of pkv_decode_step_noalloc: a device array owned by the library,
+// one copy per GPU, alive until the process ends.  On the host its name
+// stands for the host-side shadow, not for device memory: kernels get the
+// address scratch_address() looks up, never `scratch` itself.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PKV_ERR_HIP;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
 // The decode step (append already done on the host): the write of the
 // step's new rows and the attention over the updated cache.  One launch
 // (plus the merge) when the stream path applies, at most 256 rows are
@@ -2483,6 +2514,26 @@ int pkv_decode_step_merge(void* out, int32_t out_dtype, const void* q, const voi
                           key_cache, value_cache, layout, block_tables, block_table_stride,
                           lens_out, num_q_heads, max_context_len, scale, workspace,
                           workspace_bytes, stream);
+}
+
+int pkv_decode_step_noalloc(void* out, int32_t out_dtype, const void* q, const void* key,
+                            const void* value, const int64_t* slots, const int32_t* lens,
+                            int32_t num_seqs, void* key_cache, void* value_cache,
+                            const pkv_cache_layout* layout, int32_t* block_tables,
+                            int32_t block_table_stride, int32_t* lens_out, int32_t num_q_heads,
+                            int32_t max_context_len, float scale, void* stream) {
+  if (pkv::check_layout(layout) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
+    return PKV_ERR_INVALID;
+  const size_t need = paged_decode_attention_workspace_size(num_seqs, num_q_heads, layout->num_kv_heads,
+                                                            layout->head_dim, max_context_len, 0);
+  if (need > kScratchBytes) return PKV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != PKV_OK) return st;
+  return decode_step_impl(kPhasePartial | kPhaseMerge, out, out_dtype, q, key, value, slots, lens,
+                          num_seqs, key_cache, value_cache, layout, block_tables,
+                          block_table_stride, lens_out, num_q_heads, max_context_len, scale, ws,
+                          kScratchBytes, stream);
 }
 
 int paged_decode_attention_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_dtype,

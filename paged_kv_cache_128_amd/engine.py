@@ -32,7 +32,8 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_step_fp8, decode_write,
+from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_step_fp8, decode_step_noalloc,
+               decode_write,
                decode_write_fp8,
                gather_blocks, scatter_blocks, copy_blocks_fp8, gather_blocks_fp8, scatter_blocks_fp8,
                new_fp8_pool, new_pool, paged_decode_attention, paged_decode_attention_fp8,
@@ -312,17 +313,21 @@ class PagedKVEngine:
     def decode_step(self, seq_ids: np.ndarray, new_k: torch.Tensor, new_v: torch.Tensor,
                     q: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, events=None,
-                    fused: bool = True) -> torch.Tensor:
+                    fused: bool = True, noalloc: bool = False) -> torch.Tensor:
         """One decode step for rows 0..n-1 holding ``seq_ids`` (int64).
         ``max_context_len`` defaults to the longest length after the append
         (known on the host from the manager, no device sync).  ``events``
         (three torch.cuda.Event) are recorded before the attention kernel
         (with the fused step: the write-and-attention kernel), between it and
         the merge, and after the merge.  ``fused`` = False forces the
-        separate write launch."""
+        separate write launch.  ``noalloc`` (16-bit pools, no events) runs the
+        step through pkv_decode_step_noalloc: no workspace, the library's own
+        per-GPU array instead."""
         n = len(seq_ids)
         if n > self.max_rows:
             raise ValueError("more sequences than the engine's rows")
+        if noalloc and (self.fp8 or events is not None or self.partition_tokens != 0):
+            raise ValueError("the no-allocation step covers 16-bit pools on the stream path, without events")
         self._ids[:n] = seq_ids
         self.manager._append_at(self._addr[0], n, self._addr[1], self._addr[2], self._addr[3])
         self._run_copies()
@@ -340,15 +345,21 @@ class PagedKVEngine:
             args8 = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                      self.key_scales, self.value_scales, self.tables, self.d_lens, scale, max_context_len)
             return decode_step_fp8(*args8, out=out, workspace=ws, events=events)
+        if noalloc:
+            if out is None:
+                out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+            return decode_step_noalloc(q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache,
+                                       self.value_cache, self.tables, self.d_lens, scale, max_context_len,
+                                       out=out)
         if not (fused and self.partition_tokens == 0 and n > 0):
             decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                          block_tables=self.tables, lens_out=self.d_lens)
             return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
-        ws = self.workspace(n, q.shape[1], max_context_len)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         args = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                 self.tables, self.d_lens, scale, max_context_len)
+        ws = self.workspace(n, q.shape[1], max_context_len)
         return decode_step(*args, out=out, workspace=ws, events=events)
 
     def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
