@@ -89,26 +89,74 @@ def calibrate_copy():
                       "bytes_written_per_launch": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(cfg, wl, budget_s: float, reps: int = 3):
-    """The CPU oracle, untuned, on the same workload: churned pool state and
+def _cpu_info():
+    """Cores the process may run on, the BLAS threads, and the CPU model."""
+    from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "blas_threads": blas[0] if blas else None, "cpu_model": model}
+
+
+def cpu_baseline(cfg, wl, budget_s: float, eng=None, gpu_first=None, reps: int = 3):
+    """The CPU oracle, untuned, on the same workload with the process's whole
+    affinity set (NumPy's BLAS threads as they come): churned pool state and
     history prefill (untimed), then per sequence the measured append, write
     and float64 gather-then-contiguous attention (timed).  Sequences are
     taken in order until ``budget_s`` of timed work; the whole pass is
-    repeated ``reps`` times on a fresh replay and the median pass reported."""
+    repeated ``reps`` times on a fresh replay and the median pass reported.
+    With ``gpu_first`` (the GPU output of the workload's first decode step)
+    and ``eng`` the sampled sequences are also compared with the GPU: the
+    largest attention difference, and whether every cached row of theirs
+    (positions below the first step's length, gathered through both
+    sides' tables) is bit for bit the oracle's."""
     import oracle
     from oracle.replay import replay_churn
     import synth
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):
-        passes = [_cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth) for _ in range(reps)]
+    info = _cpu_info()
+    passes = []
+    for _ in range(reps):
+        nbytes, nseq, secs, state = _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth)
+        passes.append((nbytes, nseq, secs))       # every pass computes the same state; the last is kept
     passes.sort(key=lambda p: p[0] / p[2])
     nbytes, nseq, secs = passes[len(passes) // 2]
-    log(f"cpu baseline: {nseq} sequences, {nbytes} KV bytes in {secs:.2f}s (median of {reps})")
-    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nseq} of {len(wl.context_lens)} sequences of the same workload "
-                      f"(append + write + float64 gather-then-contiguous attention), "
-                      f"{nbytes} KV bytes in {secs:.2f} s on one host thread, median of {reps} passes",
-            "decode_tokens_per_s": nseq / secs}
+    ref, mgr, kc, vc = state
+    nseq = min(nseq, int(np.count_nonzero(~np.isnan(ref[:, 0, 0]))))
+    log(f"cpu baseline: {nseq} sequences, {nbytes} KV bytes in {secs:.2f}s (median of {reps}), "
+        f"{info['affinity_cores']} cores, BLAS threads {info['blas_threads']}, {info['cpu_model']}")
+    res = {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": info["affinity_cores"], "kind": "oracle",
+           "sample": f"first {nseq} of {len(wl.context_lens)} sequences of the same workload "
+                     f"(append + write + float64 gather-then-contiguous attention), "
+                     f"{nbytes} KV bytes in {secs:.2f} s, median of {reps} passes",
+           "decode_tokens_per_s": nseq / secs, **info}
+    if gpu_first is not None and eng is not None:
+        import torch
+        err = float(np.abs(gpu_first[:nseq] - ref[:nseq]).max())
+        exact = True
+        bs, D, H = cfg.block_size, cfg.head_dim, cfg.num_kv_heads
+        for b in range(nseq):
+            L = int(mgr.context_len(b))
+            nb = -(-L // bs)
+            tab = eng.tables[b, :nb].long()
+            for half, oc in ((0, kc), (1, vc)):
+                g = eng.pool[tab, half].contiguous().cpu()                      # [nb, H, bs, D]
+                u = np.uint16 if g.element_size() == 2 else np.uint32
+                g = (g.view(torch.int16) if g.element_size() == 2 else g.view(torch.int32)).numpy().view(u)
+                g = g.transpose(1, 0, 2, 3).reshape(H, nb * bs, D)[:, :L]
+                o = np.ascontiguousarray(oracle.gather_logical(oc, mgr.block_table(b), L)).view(u)
+                exact &= bool(np.array_equal(g, o))
+        res["parity_sample"] = {"sequences": nseq, "max_abs_err": err, "tolerance": 1e-5 if cfg.dtype == "f32" else 2e-3,
+                                "cached_rows_bit_exact": exact}
+        log(f"cpu baseline parity: {nseq} sequences, max abs err {err:.3e}, cached rows bit-exact {exact}")
+    return res
 
 
 def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
@@ -117,10 +165,12 @@ def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
     fill = synth.poison_array((), cfg.dtype)
     kc, vc = oracle.new_pool(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, fill)
     elem = synth.ELEM_BYTES[cfg.dtype]
+    B = len(wl.context_lens)
+    ref = np.full((B, cfg.num_q_heads, cfg.head_dim), np.nan)
     done_bytes = 0
     done_seqs = 0
     elapsed = 0.0
-    for b in range(len(wl.context_lens)):
+    for b in range(B):
         slots = mgr.allocate_for_prefill(b, int(wl.context_lens[b]) - 1)
         oracle.write_kv(wl.hist_k[b], wl.hist_v[b], slots, kc, vc, cfg.block_size)
         t0 = time.perf_counter()
@@ -128,13 +178,13 @@ def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
         oracle.write_kv(wl.new_k[b:b + 1], wl.new_v[b:b + 1], step, kc, vc, cfg.block_size)
         L = mgr.context_len(b)
         table = np.array([mgr.block_table(b)], dtype=np.int32)
-        oracle.decode_attention(wl.q[b:b + 1], kc, vc, table, [L], cfg.scale, cfg.dtype)
+        ref[b] = oracle.decode_attention(wl.q[b:b + 1], kc, vc, table, [L], cfg.scale, cfg.dtype)[0]
         elapsed += time.perf_counter() - t0
         done_bytes += L * cfg.num_kv_heads * 2 * cfg.head_dim * elem
         done_seqs += 1
         if elapsed >= budget_s:
             break
-    return done_bytes, done_seqs, elapsed
+    return done_bytes, done_seqs, elapsed, (ref, mgr, kc, vc)
 
 
 def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
@@ -385,13 +435,15 @@ def measure_serving(cfg, args):
     }), flush=True)
 
 
-def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
+def measure_fp8(cfg, wl, args, ring, base, width, tokens_per_s_16):
     """The same workload with an 8-bit KV pool (E4M3 codes + one scale byte
-    per row; the history quantised by the prefill write): decode steps of
-    append, quantising step write and 8-bit attention + merge.  Reported
-    beside the 16-bit headline: KV bytes actually read (codes and scale
-    bytes) per second, decode tokens/s, and the 8-bit attention kernel's
-    roofline from HIP events on every --event-every-th step."""
+    per row; the history quantised by the prefill write), under the
+    headline's protocol: decode steps of append, quantising step write and
+    8-bit attention + merge, each timed step preceded by a 1 GiB device read
+    (median with p10/p90 of two-event steps), the kernel's own time from the
+    three-event steps.  Reported beside the 16-bit headline: KV bytes
+    actually read (codes and scale bytes) per second, decode tokens/s, and
+    the 8-bit step kernel's roofline."""
     import torch
     from paged_kv_cache_128_amd.engine import PagedKVEngine
     B = len(wl.context_lens)
@@ -406,6 +458,7 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
                 eng.manager.append_slots_for_decode(list(ev[1]))
         else:
             eng.manager.free_sequence(ev[1])
+
     def dev(a):
         if cfg.dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
@@ -417,39 +470,35 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
     ids = np.arange(B, dtype=np.int64)
     out = torch.empty((B, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32, device="cuda")
     row_bytes = cfg.num_kv_heads * 2 * (cfg.head_dim + 1)       # K and V codes + scale bytes per token
+    fused = not args.separate_write
 
     def kv8(step):
         return int((base + step).sum()) * row_bytes
 
     for s_ in range(args.warmup):
         k, v, q = ring[s_ % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=not args.separate_write)
-    timed = [i for i in range(args.steps) if i % max(1, args.event_every) == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        k, v, q = ring[(args.warmup + i) % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i), fused=not args.separate_write)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
-    merge_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in timed])
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=fused)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    fl = _timed_steps(eng, ring, ids, out, cfg, args.warmup, args.steps, fused, flush)
+    del flush
     step_bytes = np.array([kv8(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
-    fused = not args.separate_write
+    t_med, t10, t90 = (float(np.percentile(fl["step_us"], x)) for x in (50, 10, 90))
+    fl_bytes = float(step_bytes[fl["two_idx"]].mean())
     # the fused launch also writes the B new rows (codes and scale bytes)
-    alg = float(step_bytes[timed].mean()) + (B * row_bytes if fused else 0)
-    achieved = alg / (float(kern_ms.mean()) / 1e3) / 1e9
+    alg = float(step_bytes[fl["three_idx"]].mean()) + (B * row_bytes if fused else 0)
+    kern_us = float(fl["kern_us"].mean())
+    achieved = alg / (kern_us * 1e-6) / 1e9
     kname = "attn_stream8_step_kernel" if fused else "attn_stream8_kernel"
-    tps = B * args.steps / wall
-    log(f"fp8 KV: {wall * 1e6 / args.steps:.1f} us/step, attention kernel {kern_ms.mean() * 1e3:.1f} us, "
-        f"merge {merge_ms.mean() * 1e3:.1f} us, KV {step_bytes.mean() / 1e6:.1f} MB/step")
+    tps = B / (t_med * 1e-6)
+    log(f"fp8 KV flushed: {t_med:.1f} us median step (p10 {t10:.1f}, p90 {t90:.1f}), step kernel {kern_us:.1f} us, "
+        f"merge {fl['merge_us'].mean():.1f} us, KV {fl_bytes / 1e6:.1f} MB/step")
     return {
         "kv_dtype": "fp8_e4m3 codes + e8m0 row scales",
-        "value": round(float(step_bytes.sum()) / wall / 1e9, 2),
+        "value": round(fl_bytes / (t_med * 1e-6) / 1e9, 2),
         "unit": "GB/s",
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
-        "kv_bytes_per_step": round(float(step_bytes.mean())),
+        "ms_per_step": round(t_med / 1e3, 4),
+        "step_us_p10": round(t10, 2), "step_us_p90": round(t90, 2),
+        "kv_bytes_per_step": round(fl_bytes),
         "decode_tokens_per_s": round(tps, 1),
         "tokens_per_s_vs_16bit": round(tps / tokens_per_s_16, 3),
         "roofline": {
@@ -458,10 +507,46 @@ def measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s_16):
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": recorded_traffic(kname, cfg.name)[0],
-            "mean_launch_us": round(float(kern_ms.mean()) * 1e3, 3),
+            "mean_launch_us": round(kern_us, 3),
+            "launches_timed": len(fl["kern_us"]),
             "algorithmic_bytes_per_launch": round(alg),
+            "note": "launch time from events around the kernel in the flushed steps",
         },
     }
+
+
+def _timed_steps(eng, ring, ids, out, cfg, s0, n, fused, flush, event_every=5):
+    """n decode steps of the engine's rows, step s0 + i taking ring tensors
+    (s0 + i) mod len(ring).  With ``flush`` (a device tensor) a read of it
+    precedes every step outside its events; even steps then carry two events
+    (around the whole step) and odd steps three (before the first launch,
+    between the two launches, after the second).  Without, the steps run
+    back to back and every ``event_every``-th carries three events.  Returns
+    the wall time and the event times in microseconds."""
+    import torch
+    evs = {}
+    for i in range(n):
+        if flush is not None:
+            evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2 if i % 2 == 0 else 3)]
+        elif i % max(1, event_every) == 0:
+            evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        if flush is not None:
+            flush.sum()
+        k, v, q = ring[(s0 + i) % len(ring)]
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i), fused=fused)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    two = sorted(i for i in evs if len(evs[i]) == 2)
+    three = sorted(i for i in evs if len(evs[i]) == 3)
+    return {"wall_s": wall, "two_idx": two, "three_idx": three,
+            "step_us": np.array([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in two]),
+            "kern_us": np.array([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in three]),
+            "merge_us": np.array([evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in three])}
 
 
 def main():
@@ -469,12 +554,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-steps", type=int, default=100,
+                    help="back-to-back steps without a flush after the timed (flushed) ones")
     ap.add_argument("--config", default="qwen2_7b_b64")
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="split-K partition length (-1: the workload's own, else library default)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-iters", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--event-every", type=int, default=5,
                     help="record the kernel-timing events on every n-th timed step")
@@ -512,7 +598,7 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + args.steps + args.warm_steps
     width = int(-(-(int(wl.context_lens.max()) + total_steps) // cfg.block_size))
     part = cfg.partition_tokens if args.partition_tokens < 0 else args.partition_tokens
     eng = PagedKVEngine(cfg.num_blocks, cfg.num_kv_heads, cfg.block_size, cfg.head_dim, tdtype, B,
@@ -546,63 +632,44 @@ def main():
         return int((base + step).sum()) * cfg.num_kv_heads * 2 * cfg.head_dim * elem
 
     torch.cuda.synchronize()
+    fused = not args.separate_write
+    first_out = None
     for s in range(args.warmup):
         k, v, q = ring[s % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=not args.separate_write)
+        eng.decode_step(ids, k, v, q, cfg.scale, out=out, fused=fused)
+        if s == 0:
+            first_out = out.clone()          # the workload's own first step, for the parity sample
     torch.cuda.synchronize()
 
-    # Kernel timing: HIP events around the step's kernels on every
-    # --event-every-th timed step (each recorded event costs a few us of GPU
-    # time, so events on every step would slow the very steps being timed).
-    timed = [i for i in range(args.steps) if i % max(1, args.event_every) == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in timed}
-    if torch.distributed.is_available() and torch.distributed.is_initialized():
-        torch.distributed.barrier()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        s = args.warmup + i
-        k, v, q = ring[s % len(ring)]
-        eng.decode_step(ids, k, v, q, cfg.scale, out=out, events=evs.get(i), fused=not args.separate_write)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
-    split_ms = np.array([evs[i][0].elapsed_time(evs[i][1]) for i in timed])
-    merge_ms = np.array([evs[i][1].elapsed_time(evs[i][2]) for i in timed])
-    step_bytes = np.array([kv_bytes(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
-    timed_bytes = step_bytes[timed]
-    total_kv = float(step_bytes.sum())
-    value = total_kv / wall / 1e9
-    tokens_per_s = B * args.steps / wall
-    split_avg_s = float(split_ms.mean()) / 1e3
-    # the first launch of a step also writes the step's new K/V rows when fused
-    new_row_bytes = B * cfg.num_kv_heads * 2 * cfg.head_dim * elem
-    attn_gbps = float(timed_bytes.mean()) / (float((split_ms + merge_ms).mean()) / 1e3) / 1e9
-    log(f"timed {args.steps} steps: {wall * 1e6 / args.steps:.1f} us/step, split kernel "
-        f"{split_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us, "
-        f"KV {step_bytes.mean() / 1e6:.1f} MB/step")
-
-    # attention only, with a 1 GiB read before each launch pair (cold caches;
-    # a read leaves no dirty lines behind to be written back during the launch)
+    # Headline: flushed steps.  Before each timed step a 1 GiB device read
+    # (outside its events) evicts the 256 MB Infinity Cache and the L2s; a
+    # read leaves no dirty lines to be written back during the step.  Even
+    # steps carry two events around the whole step (the headline times),
+    # odd steps three (before the step kernel, between it and the merge,
+    # after the merge) for the kernel's own duration.
     flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
-    lens_dev = torch.from_numpy(eng.manager.context_lens(list(range(B)))).cuda()
-    maxlen = int(lens_dev.max().item())
-    cold_bytes = int(lens_dev.sum().item()) * cfg.num_kv_heads * 2 * cfg.head_dim * elem
-    q = ring[0][2]
-    cold = []
-    for _ in range(args.cold_iters):
-        flush.sum()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        eng.attend(q, lens_dev, cfg.scale, maxlen, out=out, events=e)
-        torch.cuda.synchronize()
-        cold.append((e[0].elapsed_time(e[1]), e[0].elapsed_time(e[2])))
-    cold = np.array(cold)
+    fl = _timed_steps(eng, ring, ids, out, cfg, args.warmup, args.steps, fused, flush)
+    s_warm = args.warmup + args.steps
+    # Warm steps: back to back, no flush (kernel events on every 5th step).
+    wm = _timed_steps(eng, ring, ids, out, cfg, s_warm, args.warm_steps, fused, None, args.event_every)
     del flush
+    step_bytes = np.array([kv_bytes(args.warmup + i) for i in range(args.steps)], dtype=np.float64)
+    fl_bytes = float(step_bytes[fl["two_idx"]].mean())
+    t_med, t10, t90 = (float(np.percentile(fl["step_us"], x)) for x in (50, 10, 90))
+    value = fl_bytes / (t_med * 1e-6) / 1e9
+    warm_bytes = np.array([kv_bytes(s_warm + i) for i in range(args.warm_steps)], dtype=np.float64)
+    warm_value = float(warm_bytes.sum()) / wm["wall_s"] / 1e9 if args.warm_steps else None
+    log(f"flushed {args.steps} steps: {t_med:.1f} us median (p10 {t10:.1f}, p90 {t90:.1f}), step kernel "
+        f"{fl['kern_us'].mean():.1f} us, merge {fl['merge_us'].mean():.1f} us (three-event steps); "
+        f"KV {fl_bytes / 1e6:.1f} MB/step -> {value:.0f} GB/s")
+    if args.warm_steps:
+        log(f"warm {args.warm_steps} steps: {wm['wall_s'] * 1e6 / args.warm_steps:.1f} us/step wall, step kernel "
+            f"{wm['kern_us'].mean():.1f} us, merge {wm['merge_us'].mean():.1f} us")
     block_copy = measure_block_copy(eng)
     swap = measure_swap(eng)
     fp8 = None
     if not args.no_fp8 and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
-        fp8 = measure_fp8(cfg, wl, args, ring, base, total_steps, width, tokens_per_s)
+        fp8 = measure_fp8(cfg, wl, args, ring, base, width, B / (t_med * 1e-6))
     prefill = prefill8 = None
     if not args.no_prefill and cfg.dtype in ("bf16", "f16") and cfg.head_dim == 128:
         prefill = measure_prefill(cfg)
@@ -613,12 +680,15 @@ def main():
     path = pkv.attention_path(B, cfg.num_q_heads, int(base.max()) + total_steps, eng.key_cache, part)
     # the engine's step: the write runs inside the stream launch (pkv_decode_step)
     # when the stream path applies and the batch has at most 256 rows
-    fused = path == "stream" and B <= 256 and not args.separate_write
-    kernel_name = ("attn_stream_step_kernel" if fused else
+    fused_launch = path == "stream" and B <= 256 and fused
+    kernel_name = ("attn_stream_step_kernel" if fused_launch else
                    {"stream": "attn_stream_kernel", "partition": "attn_split_kernel"}[path])
     traffic, _ = recorded_traffic(kernel_name, cfg.name)
-    alg_bytes = float(timed_bytes.mean()) + (new_row_bytes if fused else 0)
-    achieved = alg_bytes / split_avg_s / 1e9
+    # the first launch of a step also writes the step's new K/V rows when fused
+    new_row_bytes = B * cfg.num_kv_heads * 2 * cfg.head_dim * elem
+    kern_bytes = float(step_bytes[fl["three_idx"]].mean()) + (new_row_bytes if fused_launch else 0)
+    kern_us = float(fl["kern_us"].mean())
+    achieved = kern_bytes / (kern_us * 1e-6) / 1e9
     result = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s",
         "value": round(value, 2),
@@ -626,7 +696,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "ms_per_step": round(t_med / 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -637,21 +707,37 @@ def main():
                         f"H_q={cfg.num_q_heads} H_kv={cfg.num_kv_heads} D={cfg.head_dim} "
                         f"{cfg.dtype} block_size={cfg.block_size}, pool {cfg.num_blocks} blocks",
             "batch": B,
+            "seed": cfg.seed,
             "context_lens": f"U[{cfg.len_range[0]}, {cfg.len_range[1]}]" if cfg.len_range else
                             list(map(int, cfg.fixed_lens)),
             "sum_context_first_step": int(base.sum()),
             "partition_tokens": part if part else "library default",
+            "attention_path": path,
             "placement": cfg.placement,
             "adjacent_logical_neighbours_fraction": round(frag, 4),
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
-        "decode_tokens_per_s": round(tokens_per_s, 1),
-        "attention_kv_gbps": round(attn_gbps, 2),
-        "attention_cold_us": {"attention_kernel": round(float(np.median(cold[:, 0])) * 1e3, 2),
-                              "attention_plus_merge": round(float(np.median(cold[:, 1])) * 1e3, 2),
-                              "kv_bytes": cold_bytes,
-                              "kv_gbps": round(cold_bytes / (float(np.median(cold[:, 1])) / 1e3) / 1e9, 2),
-                              "note": "1 GiB device read before each launch pair"},
+        "decode_tokens_per_s": round(B / (t_med * 1e-6), 1),
+        "flushed": {
+            "what": "each timed step preceded, outside its events, by a 1 GiB device read; step = write and "
+                    "attention (one launch when fused) + merge, timed with two events around it",
+            "step_us_median": round(t_med, 2), "step_us_p10": round(t10, 2), "step_us_p90": round(t90, 2),
+            "kv_bytes_per_step": round(fl_bytes),
+            "gbps_at_p10_p90": [round(fl_bytes / (t10 * 1e-6) / 1e9, 1), round(fl_bytes / (t90 * 1e-6) / 1e9, 1)],
+            "step_kernel_us_mean": round(kern_us, 2),
+            "merge_us_mean": round(float(fl["merge_us"].mean()), 2),
+            "steps_timed": len(fl["step_us"]),
+        },
+        "warm": None if not args.warm_steps else {
+            "what": "back-to-back steps without a flush, host append included (wall clock)",
+            "steps": args.warm_steps,
+            "ms_per_step": round(wm["wall_s"] * 1e3 / args.warm_steps, 4),
+            "value": round(warm_value, 2), "unit": "GB/s",
+            "pct_hbm_peak": round(100.0 * warm_value / HBM_PEAK_GBPS, 2),
+            "decode_tokens_per_s": round(B * args.warm_steps / wm["wall_s"], 1),
+            "step_kernel_us_mean": round(float(wm["kern_us"].mean()), 2),
+            "merge_us_mean": round(float(wm["merge_us"].mean()), 2),
+        },
         "roofline": {
             "kernel": f"{kernel_name}<{cfg.dtype}, D={cfg.head_dim}, "
                       f"G={cfg.num_q_heads // cfg.num_kv_heads}>",
@@ -661,8 +747,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "mean_launch_us": round(split_avg_s * 1e6, 3),
-            "algorithmic_bytes_per_launch": round(alg_bytes),
+            "mean_launch_us": round(kern_us, 3),
+            "launches_timed": len(fl["kern_us"]),
+            "algorithmic_bytes_per_launch": round(kern_bytes),
+            "note": "launch time from events around the kernel in the flushed steps",
         },
         "kernel_source_sha256_16": kernel_source_sha(),
         "copy_on_write": block_copy,
@@ -672,7 +760,7 @@ def main():
         "prefill_fp8": prefill8,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds, eng, first_out.double().cpu().numpy())
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -500,6 +500,13 @@ def decode_step_fp8(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cach
     tail = (None if workspace is None else workspace.data_ptr(),
             0 if workspace is None else workspace.numel() * workspace.element_size(), _stream_handle(stream))
     fn = _lib_handle().pkv_decode_step_fp8
+    if events is not None and len(events) == 2:
+        if phase != "both":
+            raise ValueError("events time both phases of one call")
+        _record(events[0], stream)
+        _check(fn(*head, 3, *tail), "pkv_decode_step_fp8")
+        _record(events[1], stream)
+        return out
     if events is not None:
         if phase != "both":
             raise ValueError("events time both phases of one call")
@@ -814,9 +821,10 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
     after the append) published to lens_out (device int32 [n]) and opened
     blocks to block_tables.  ``phase`` "partial" runs only the first launch
     and "merge" (same arguments and workspace) only the second.  ``events``
-    (three torch.cuda.Event, with phase "both") are recorded on the stream
-    before the first launch, between the two and after the second; the
-    arguments are checked and marshalled once for both launches."""
+    (with phase "both") are recorded on the stream: three torch.cuda.Event
+    before the first launch, between the two and after the second, or two
+    around the whole call (no event between the launches); the arguments
+    are checked and marshalled once for both launches."""
     torch = _torch()
     lay = cache_layout(key_cache, value_cache)
     n, hq, d = q.shape
@@ -851,6 +859,13 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
             0 if workspace is None else workspace.numel() * workspace.element_size(),
             _stream_handle(stream))
     lib = _lib_handle()
+    if events is not None and len(events) == 2:
+        if phase != "both":
+            raise ValueError("events time both phases of one call")
+        _record(events[0], stream)
+        _check(lib.pkv_decode_step(*args), "pkv_decode_step")
+        _record(events[1], stream)
+        return out
     if events is not None:
         if phase != "both":
             raise ValueError("events time both phases of one call")

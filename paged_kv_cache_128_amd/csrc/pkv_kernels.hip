@@ -904,39 +904,83 @@ attn_split_kernel(AttnArgs a) {
 }
 
 // Split-K merge: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p with
-// M = max_p m_p.  One workgroup per (sequence, query head); sequences with a
-// single partition were finished by attn_split_kernel.
+// M = max_p m_p.  One workgroup of four waves per (sequence, query head);
+// sequences with a single partition were finished by attn_split_kernel.
+// Every wave reads all the (m, l) pairs, 64 partitions per load round, and
+// reduces M and the denominator across its lanes; wave w then sums the
+// weighted accumulators of partitions w, w + 4, w + 8, ... (eight loads in
+// flight per lane), and wave 0 adds the four wave sums from LDS in a fixed
+// order.  The summation order depends only on the partition count, so the
+// result is reproducible bit for bit.
+constexpr int kReduceWaves = 4;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 template <int D>
-__global__ void __launch_bounds__(kWave)
+__global__ void __launch_bounds__(kWave * kReduceWaves)
 attn_reduce_kernel(AttnArgs a) {
+  constexpr int kPer = D / kWave;
+  __shared__ float wsum[kReduceWaves][D];
   const int qh = blockIdx.x % a.hq;
   const int b = blockIdx.x / a.hq;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   int L = a.lens[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int nparts = (L + a.part_tokens - 1) / a.part_tokens;
   if (nparts <= 1) return;
   const int64_t row = static_cast<int64_t>(b) * a.hq + qh;
-  const float* ml = a.ws_ml + row * a.max_parts * 2;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml + row * a.max_parts * 2);
   const float* acc = a.ws_acc + row * a.max_parts * D;
   float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-  constexpr int kPer = D / kWave;
+  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[p].x);
+  M = wave_max(M);
+  float den = 0.f;
+  for (int p = lane; p < nparts; p += kWave) {
+    const float2 x = ml[p];
+    den = fmaf(x.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x.x - M), x.y, den);
+  }
+  den = wave_sum(den);
   float num[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) num[e] = 0.f;
-  float den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float mp = ml[2 * p];
-    const float w = (mp == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp - M);
-    den = fmaf(w, ml[2 * p + 1], den);
+  constexpr int kBatch = 8;
+  for (int p0 = wave; p0 < nparts; p0 += kReduceWaves * kBatch) {
+    float w[kBatch], v[kBatch][kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) num[e] = fmaf(w, acc[p * D + e * kWave + threadIdx.x], num[e]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int p = min(p0 + u * kReduceWaves, nparts - 1);
+      const float mp = ml[p].x;
+      w[u] = (p0 + u * kReduceWaves < nparts && mp != -INFINITY) ? __builtin_amdgcn_exp2f(mp - M) : 0.f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) v[u][e] = acc[static_cast<int64_t>(p) * D + e * kWave + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) num[e] = fmaf(w[u], v[u][e], num[e]);
   }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) wsum[wave][e * kWave + lane] = num[e];
+  __syncthreads();
+  if (wave != 0) return;
   const float inv = den > 0.f ? 1.0f / den : 0.f;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const int64_t o = row * D + e * kWave + threadIdx.x;
-    const float y = num[e] * inv;
+    const int d = e * kWave + lane;
+    float t = wsum[0][d];
+#pragma unroll
+    for (int k = 1; k < kReduceWaves; ++k) t += wsum[k][d];
+    const int64_t o = row * D + d;
+    const float y = t * inv;
     if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = y;
     else if (a.out_dtype == PKV_BF16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(y);
     else static_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
@@ -2324,8 +2368,9 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
   }
   if ((phases & kPhaseMerge) && P > 1) {
     const dim3 rgrid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
-    if (l->head_dim == 64) hipLaunchKernelGGL(attn_reduce_kernel<64>, rgrid, dim3(kWave), 0, s, a);
-    else hipLaunchKernelGGL(attn_reduce_kernel<128>, rgrid, dim3(kWave), 0, s, a);
+    const dim3 rblock(kWave * kReduceWaves);
+    if (l->head_dim == 64) hipLaunchKernelGGL(attn_reduce_kernel<64>, rgrid, rblock, 0, s, a);
+    else hipLaunchKernelGGL(attn_reduce_kernel<128>, rgrid, rblock, 0, s, a);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;

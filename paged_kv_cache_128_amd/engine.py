@@ -319,7 +319,7 @@ class PagedKVEngine:
         (known on the host from the manager, no device sync).  ``events``
         (three torch.cuda.Event) are recorded before the attention kernel
         (with the fused step: the write-and-attention kernel), between it and
-        the merge, and after the merge.  ``fused`` = False forces the
+        the merge, and after the merge; two are recorded around both.  ``fused`` = False forces the
         separate write launch.  ``noalloc`` (16-bit pools, no events) runs the
         step through pkv_decode_step_noalloc: no workspace, the library's own
         per-GPU array instead."""
@@ -375,6 +375,11 @@ class PagedKVEngine:
             kw8 = dict(out=out, max_context_len=max_context_len, workspace=ws)
             if events is None:
                 return paged_decode_attention_fp8(*args, **kw8)
+            if len(events) == 2:
+                events[0].record()
+                paged_decode_attention_fp8(*args, **kw8)
+                events[1].record()
+                return out
             events[0].record()
             paged_decode_attention_fp8(*args, phase="partial", **kw8)
             events[1].record()
@@ -383,6 +388,12 @@ class PagedKVEngine:
             return out
         kw = dict(partition_tokens=self.partition_tokens, max_context_len=max_context_len,
                   workspace=ws)
+        if events is not None and len(events) == 2:
+            events[0].record()
+            paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], lens, scale,
+                                   out=out, **kw)
+            events[1].record()
+            return out
         if events is None:
             return paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n],
                                           lens, scale, out=out, **kw)
