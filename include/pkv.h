@@ -172,6 +172,25 @@ int pkv_append_slots_for_decode(pkv_manager* mgr, const int64_t* seq_ids, int32_
  */
 int pkv_append_tokens(pkv_manager* mgr, int64_t seq_id, int32_t num_tokens, int64_t* slots_out);
 
+/*
+ * A batch of prefill chunks admitted all or nothing ([mini-vLLM BM] "Block
+ * Manager 和 Scheduler 如何协作": the scheduler admits only what the free
+ * blocks cover).  In array order, sequence seq_ids[i] receives
+ * chunk_lens[i] tokens: a sequence that is not live is created as
+ * pkv_allocate_for_prefill creates it; a live one is extended as
+ * pkv_append_tokens extends it, when `extend_live` is nonzero.  Everything
+ * is checked before anything changes: ids >= 0 and distinct, lengths >= 0,
+ * no swapped id and no live id unless extend_live (ALREADY_PREFILLED), and
+ * the blocks of the whole batch (new tables, opened blocks, a copy of each
+ * shared tail block a chunk writes into, counted in array order) against
+ * the free list (OOM).  slots_out (host, [sum of chunk_lens], nullable)
+ * receives the chunks' slots concatenated in array order; lens_out (host,
+ * [n], nullable) the lengths afterwards.  Errors: INVALID,
+ * ALREADY_PREFILLED, OOM.
+ */
+int pkv_admit_batch(pkv_manager* mgr, const int64_t* seq_ids, const int32_t* chunk_lens, int32_t n,
+                    int32_t extend_live, int64_t* slots_out, int32_t* lens_out);
+
 /* Release `seq_id`: each block of its table loses one reference, and those
  * whose count reaches 0 are appended to the free list in table order
  * ([MiniPaged-Qwen] §5.3; [mini-vLLM BM] "释放 block").  Errors: NOT_LIVE. */
@@ -675,6 +694,23 @@ int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows,
                             int32_t block_table_stride, const int32_t* rows,
                             const int32_t* lens, const int32_t* new_block, int32_t n,
                             int32_t block_size, void* stream);
+
+/*
+ * Whole rows of device block tables ([MiniPaged-Qwen] §16.5, the batch
+ * block-table tensor): for i < n, row src_rows[i] (or row i when src_rows
+ * is NULL) of `src` is copied to row dst_rows[i] (or row i) of `dst`,
+ * entries 0 .. width-1.  Used to publish the rows of admitted sequences
+ * into a device-resident table (dst_rows = their rows, src = the manager's
+ * rows staged on the device, pkv_get_block_tables) and to gather the rows
+ * of a prefill batch (src_rows = their rows).  dst, src: device int32
+ * tables with `*_stride` entries per row (>= width) and `*_num_rows` rows;
+ * dst_rows, src_rows: device int32 [n] or NULL.  Rows outside either table
+ * are skipped.  dst_rows must be distinct (two copies into one row race).
+ * Errors: INVALID, UNSUPPORTED, HIP.
+ */
+int pkv_copy_table_rows(int32_t* dst, int32_t dst_stride, int32_t dst_num_rows, const int32_t* dst_rows,
+                        const int32_t* src, int32_t src_stride, int32_t src_num_rows, const int32_t* src_rows,
+                        int32_t n, int32_t width, void* stream);
 
 /* Library version string, e.g. "pkv 0.1.0 gfx950". */
 const char* pkv_version(void);

@@ -273,6 +273,50 @@ class BlockManager:
             raise OutOfBlocks()
         return [self.append_slot_for_decode(seq_id) for _ in range(num_tokens)]
 
+    def admit_batch(self, seq_ids: Sequence[int], chunk_lens: Sequence[int],
+                    extend_live: bool = False) -> List[List[int]]:
+        """A batch of prefill chunks admitted all or nothing ([mini-vLLM BM]
+        "Block Manager 和 Scheduler 如何协作": the scheduler admits only what
+        the free blocks cover).  Sequence seq_ids[i] gets chunk_lens[i]
+        tokens, in array order: a sequence not live is created as
+        allocate_for_prefill creates it; a live one is extended as
+        append_tokens extends it, when ``extend_live``.  Everything is
+        checked before anything changes: ids >= 0 and distinct, lengths
+        >= 0, no swapped id, no live id unless ``extend_live``, and the
+        blocks of the whole batch (new tables, opened blocks, and a copy of
+        each shared tail block a chunk writes into, counting the references
+        earlier copies of the batch drop) against the free list.  Returns
+        each sequence's slots."""
+        ids = [int(x) for x in seq_ids]
+        lens = [int(x) for x in chunk_lens]
+        if len(ids) != len(lens):
+            raise InvalidArgument("one chunk length per sequence")
+        if any(x < 0 for x in ids) or any(n < 0 for n in lens):
+            raise InvalidArgument("seq_ids and chunk lengths must be >= 0")
+        if len(set(ids)) != len(ids):
+            raise InvalidArgument("duplicate sequence ids in one batch")
+        bs = self.block_size
+        need = 0
+        dropped: Dict[int, int] = {}
+        for sid, n in zip(ids, lens):
+            if sid in self.swapped or (sid in self.seqs and not extend_live):
+                raise AlreadyPrefilled(f"sequence {sid} is already live")
+            if sid not in self.seqs:
+                need += blocks_needed(n, bs)
+                continue
+            seq = self.seqs[sid]
+            L = seq.length
+            need += blocks_needed(L + n, bs) - len(seq.table)
+            if n > 0 and L // bs < len(seq.table):
+                tail = seq.table[L // bs]
+                if self.ref[tail] - dropped.get(tail, 0) > 1:
+                    need += 1
+                    dropped[tail] = dropped.get(tail, 0) + 1
+        if need > len(self.free):
+            raise OutOfBlocks()
+        return [self.append_tokens(sid, n) if sid in self.seqs else self.allocate_for_prefill(sid, n)
+                for sid, n in zip(ids, lens)]
+
     def swap_out(self, seq_id: int) -> List[int]:
         """Release the blocks of live ``seq_id`` (returned in table order, for
         the caller to copy out first) and keep its length; the sequence is

@@ -92,6 +92,7 @@ SIGNATURES = {
     "pkv_free_sequence": (ctypes.c_int, [_P, _I64]),
     "pkv_share_prefix": (ctypes.c_int, [_P, _I64, _I64, _I32]),
     "pkv_append_tokens": (ctypes.c_int, [_P, _I64, _I32, _PI64]),
+    "pkv_admit_batch": (ctypes.c_int, [_P, _PI64, _PI32, _I32, _I32, _PI64, _PI32]),
     "pkv_swap_out": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
     "pkv_swap_in": (ctypes.c_int, [_P, _I64, _PI32, _I32, _PI32]),
     "pkv_is_swapped": (ctypes.c_int, [_P, _I64]),
@@ -153,6 +154,7 @@ SIGNATURES = {
                                                     _P, _SZ, _P]),
     "paged_decode_attention_path": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(CacheLayout), _I32]),
     "pkv_update_block_tables": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _I32, _I32, _P]),
+    "pkv_copy_table_rows": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _I32, _I32, _P, _I32, _I32, _P]),
 }
 
 
@@ -317,6 +319,23 @@ class KVBlockManager:
         _check(self._lib.pkv_append_tokens(self._h, int(seq_id), int(num_tokens),
                                            _ptr(slots, ctypes.c_int64)), "append_tokens")
         return slots
+
+    def admit_batch(self, seq_ids, chunk_lens, extend_live: bool = False):
+        """All-or-nothing admission of a batch of prefill chunks (see
+        pkv_admit_batch): returns (slots int64 of every chunk concatenated,
+        lens int32 after)."""
+        ids = _np_i64(seq_ids)
+        cl = np.ascontiguousarray(chunk_lens, dtype=np.int32)
+        if cl.shape != ids.shape:
+            raise ValueError("one chunk length per sequence")
+        if np.any(cl < 0):
+            raise InvalidArgumentError(-1, "admit_batch: chunk lengths must be >= 0")
+        slots = np.empty(int(cl.sum()), dtype=np.int64)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _check(self._lib.pkv_admit_batch(self._h, _ptr(ids, ctypes.c_int64), _ptr(cl, ctypes.c_int32), len(ids),
+                                         1 if extend_live else 0, _ptr(slots, ctypes.c_int64),
+                                         _ptr(lens, ctypes.c_int32)), "admit_batch")
+        return slots, lens
 
     def swap_out(self, seq_id: int) -> np.ndarray:
         """Release a live sequence's blocks, keeping its length; returns the
@@ -999,10 +1018,30 @@ def update_block_tables(block_tables, lens, new_block, block_size: int, rows=Non
     _check(st, "update_block_tables")
 
 
+def copy_table_rows(dst, src, n: int, dst_rows=None, src_rows=None, width: Optional[int] = None,
+                    stream=None) -> None:
+    """Rows of int32 device tables (see pkv_copy_table_rows): row src_rows[i]
+    (or i) of ``src`` to row dst_rows[i] (or i) of ``dst`` for i < n; the row
+    lists are device int32 tensors or None."""
+    torch = _torch()
+    for t in (dst, src):
+        if t.dtype != torch.int32 or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError("tables must be int32 [rows, W] with unit column stride")
+    for r in (dst_rows, src_rows):
+        if r is not None and (r.dtype != torch.int32 or r.numel() < n or not r.is_contiguous()):
+            raise ValueError("row lists must be contiguous int32 tensors of at least n entries")
+    w = min(dst.shape[1], src.shape[1]) if width is None else int(width)
+    st = _lib_handle().pkv_copy_table_rows(
+        dst.data_ptr(), dst.stride(0), dst.shape[0], None if dst_rows is None else dst_rows.data_ptr(),
+        src.data_ptr(), src.stride(0), src.shape[0], None if src_rows is None else src_rows.data_ptr(),
+        int(n), w, _stream_handle(stream))
+    _check(st, "copy_table_rows")
+
+
 __all__ = [
     "KVBlockManager", "CacheLayout", "PkvError", "InvalidArgumentError", "OutOfBlocksError",
     "NotLiveError", "AlreadyPrefilledError", "paged_kv_write", "paged_decode_attention",
-    "workspace_size", "update_block_tables", "attention_path", "decode_write", "decode_step", "new_pool",
+    "workspace_size", "update_block_tables", "copy_table_rows", "attention_path", "decode_write", "decode_step", "new_pool",
     "decode_step_noalloc", "NOALLOC_SCRATCH_BYTES",
     "copy_blocks", "gather_blocks", "scatter_blocks", "copy_blocks_fp8", "gather_blocks_fp8",
     "scatter_blocks_fp8", "new_fp8_pool", "paged_kv_write_fp8", "decode_write_fp8",

@@ -327,6 +327,66 @@ int pkv_append_tokens(pkv_manager* m, int64_t seq_id, int32_t num_tokens, int64_
   return PKV_OK;
 }
 
+int pkv_admit_batch(pkv_manager* m, const int64_t* seq_ids, const int32_t* chunk_lens, int32_t n,
+                    int32_t extend_live, int64_t* slots_out, int32_t* lens_out) {
+  if (!m || n < 0 || (n > 0 && (!seq_ids || !chunk_lens))) return PKV_ERR_INVALID;
+  const int64_t bs = m->block_size;
+  int64_t need = 0;
+  try {
+    std::unordered_set<int64_t> seen;
+    seen.reserve(static_cast<size_t>(n) * 2);
+    for (int32_t i = 0; i < n; ++i) {
+      if (seq_ids[i] < 0 || chunk_lens[i] < 0) return PKV_ERR_INVALID;
+      if (!seen.insert(seq_ids[i]).second) return PKV_ERR_INVALID;
+    }
+    // the blocks the whole batch takes, in array order: new tables, opened
+    // blocks, and a copy of each shared tail block a chunk writes into (a
+    // copy drops one reference from that block for later chunks)
+    std::unordered_map<int32_t, int32_t> dropped;
+    for (int32_t i = 0; i < n; ++i) {
+      if (m->swapped.count(seq_ids[i])) return PKV_ERR_ALREADY_PREFILLED;
+      auto it = m->seqs.find(seq_ids[i]);
+      if (it == m->seqs.end()) {
+        need += m->blocks_for(chunk_lens[i]);
+        continue;
+      }
+      if (!extend_live) return PKV_ERR_ALREADY_PREFILLED;
+      const Sequence& s = it->second;
+      if (static_cast<int64_t>(s.length) + chunk_lens[i] > INT32_MAX) return PKV_ERR_INVALID;
+      need += m->blocks_for(static_cast<int64_t>(s.length) + chunk_lens[i]) - static_cast<int64_t>(s.table.size());
+      if (chunk_lens[i] > 0 && s.length / bs < static_cast<int64_t>(s.table.size())) {
+        const int32_t tail = s.table[s.length / bs];
+        const int32_t d = dropped.count(tail) ? dropped[tail] : 0;
+        if (m->ref[tail] - d > 1) {
+          ++need;
+          dropped[tail] = d + 1;
+        }
+      }
+    }
+    if (need > m->count) return PKV_ERR_OOM;
+    // room for every table entry and queued copy before anything changes
+    for (int32_t i = 0; i < n; ++i) {
+      auto it = m->seqs.find(seq_ids[i]);
+      if (it != m->seqs.end())
+        it->second.table.reserve(m->blocks_for(static_cast<int64_t>(it->second.length) + chunk_lens[i]));
+    }
+    m->seqs.reserve(m->seqs.size() + static_cast<size_t>(n));
+    m->copies.reserve(m->copies.size() + static_cast<size_t>(n));
+  } catch (...) {
+    return PKV_ERR_INVALID;
+  }
+  int64_t at = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t* dst = slots_out ? slots_out + at : nullptr;
+    const int r = m->seqs.count(seq_ids[i]) ? pkv_append_tokens(m, seq_ids[i], chunk_lens[i], dst)
+                                            : pkv_allocate_for_prefill(m, seq_ids[i], chunk_lens[i], dst);
+    if (r != PKV_OK) return PKV_ERR_INVARIANT;     // cannot happen: every check passed above
+    if (lens_out) lens_out[i] = m->seqs[seq_ids[i]].length;
+    at += chunk_lens[i];
+  }
+  return PKV_OK;
+}
+
 int pkv_swap_out(pkv_manager* m, int64_t seq_id, int32_t* ids_out, int32_t cap, int32_t* count_out) {
   if (!m || cap < 0 || !count_out || (cap > 0 && !ids_out)) return PKV_ERR_INVALID;
   auto it = m->seqs.find(seq_id);

@@ -9,6 +9,10 @@
 //  * table_update_kernel      -- applies the blocks a batched decode append
 //                                opened to a device-resident block table
 //                                ([MiniPaged-Qwen] §9.2).
+//  * table_rows_kernel        -- copies whole block-table rows between
+//                                device tables, scattered or gathered by row
+//                                lists (publishing admitted sequences' rows,
+//                                the per-sequence table of a prefill batch).
 //  * attn_split_kernel        -- decode attention over one context partition
 //                                of one (sequence, KV head): block-table walk,
 //                                GQA group sharing each K/V tile, fp32 online
@@ -208,6 +212,23 @@ table_update_kernel(int32_t* __restrict__ tables, int32_t num_rows, int32_t stri
 }
 
 // ------------------------------------------------------------ attention
+// Whole rows of int32 block tables: row i of the copy goes from source row
+// src_rows[i] (or i) to destination row dst_rows[i] (or i); one thread per
+// entry, rows outside either table skipped.
+__global__ void __launch_bounds__(256)
+table_rows_kernel(int32_t* __restrict__ dst, int32_t dst_stride, int32_t dst_num_rows,
+                  const int32_t* __restrict__ dst_rows, const int32_t* __restrict__ src,
+                  int32_t src_stride, int32_t src_num_rows, const int32_t* __restrict__ src_rows,
+                  int32_t n, int32_t width) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (e >= static_cast<int64_t>(n) * width) return;
+  const int32_t i = static_cast<int32_t>(e / width), j = static_cast<int32_t>(e - static_cast<int64_t>(i) * width);
+  const int32_t dr = dst_rows ? dst_rows[i] : i;
+  const int32_t sr = src_rows ? src_rows[i] : i;
+  if (dr < 0 || dr >= dst_num_rows || sr < 0 || sr >= src_num_rows) return;
+  dst[static_cast<int64_t>(dr) * dst_stride + j] = src[static_cast<int64_t>(sr) * src_stride + j];
+}
+
 struct AttnArgs {
   const void* q;
   const void* kc;
@@ -2609,6 +2630,21 @@ int pkv_decode_step_fp8(void* out, int32_t out_dtype, const void* q, int32_t q_d
   return decode_step_impl(phases, out, out_dtype, q, key, value, slots, lens, num_seqs, key_cache,
                           value_cache, layout, block_tables, block_table_stride, lens_out, num_q_heads,
                           max_context_len, scale, workspace, workspace_bytes, stream, &f8s);
+}
+
+int pkv_copy_table_rows(int32_t* dst, int32_t dst_stride, int32_t dst_num_rows, const int32_t* dst_rows,
+                        const int32_t* src, int32_t src_stride, int32_t src_num_rows, const int32_t* src_rows,
+                        int32_t n, int32_t width, void* stream) {
+  if (n < 0 || width < 0 || dst_stride < width || src_stride < width || dst_num_rows < 0 || src_num_rows < 0)
+    return PKV_ERR_INVALID;
+  if (n == 0 || width == 0) return PKV_OK;
+  if (!dst || !src) return PKV_ERR_INVALID;
+  const int64_t total = static_cast<int64_t>(n) * width;
+  if ((total + 255) / 256 > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(table_rows_kernel, dim3(static_cast<uint32_t>((total + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), dst, dst_stride, dst_num_rows, dst_rows, src, src_stride,
+                     src_num_rows, src_rows, n, width);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 int pkv_update_block_tables(int32_t* block_tables, int32_t num_rows, int32_t block_table_stride,

@@ -32,7 +32,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KVBlockManager, NotLiveError, copy_blocks, decode_step, decode_step_fp8, decode_step_noalloc,
+from . import (KVBlockManager, copy_blocks, copy_table_rows, decode_step, decode_step_fp8, decode_step_noalloc,
                decode_write,
                decode_write_fp8,
                gather_blocks, scatter_blocks, copy_blocks_fp8, gather_blocks_fp8, scatter_blocks_fp8,
@@ -58,11 +58,11 @@ class _HostStage:
         self.buf = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         self.off = 0
 
-    def to_device(self, arr: np.ndarray) -> torch.Tensor:
-        arr = np.ascontiguousarray(arr)
+    def _stage(self, arr: np.ndarray):
+        """The bytes of arr in the arena (None when larger than the arena)."""
         n = arr.nbytes
-        if n > self.buf.numel():                     # larger than the arena: a plain copy
-            return torch.from_numpy(arr).to(self.device)
+        if n > self.buf.numel():
+            return None
         at = (self.off + 255) & ~255
         if at + n > self.buf.numel():
             torch.cuda.synchronize(self.device)
@@ -70,10 +70,23 @@ class _HostStage:
         self.off = at + n
         host = self.buf[at:at + n]
         host.numpy()[:] = arr.view(np.uint8).reshape(-1)
-        return host.view(_TORCH_OF[arr.dtype]).to(self.device, non_blocking=True)
+        return host.view(_TORCH_OF[arr.dtype])
+
+    def to_device(self, arr: np.ndarray) -> torch.Tensor:
+        arr = np.ascontiguousarray(arr)
+        host = self._stage(arr)
+        if host is None:                             # larger than the arena: a plain copy
+            return torch.from_numpy(arr).to(self.device)
+        return host.to(self.device, non_blocking=True)
 
     def copy_into(self, dst: torch.Tensor, arr: np.ndarray) -> None:
-        dst.copy_(self.to_device(arr), non_blocking=True)
+        """arr into the contiguous device tensor dst by one host-to-device
+        copy from the arena (no device-side copy kernel)."""
+        arr = np.ascontiguousarray(arr)
+        host = self._stage(arr)
+        if host is None:
+            host = torch.from_numpy(arr)
+        dst.copy_(host.view(dst.shape), non_blocking=True)
 
 
 _TORCH_OF = {np.dtype(np.int64): torch.int64, np.dtype(np.int32): torch.int32}
@@ -142,27 +155,27 @@ class PagedKVEngine:
         concatenated in order) are written, then every chunk's query rows
         (q [sum(chunk_lens), H_q, D]) attend causally over their sequence
         (paged_prefill_attention; over an 8-bit pool paged_prefill_attention_fp8,
-        bf16 or fp16 q); ``rows`` distinct.  Returns out [sum(chunk_lens), H_q, D]."""
+        bf16 or fp16 q); ``rows`` distinct.  The allocation is all or nothing
+        (pkv_admit_batch).  Returns out [sum(chunk_lens), H_q, D]."""
         _check_distinct(rows)
-        all_slots, lens = [], []
-        for sid, row, n in zip(seq_ids, rows, chunk_lens):
-            sid, n = int(sid), int(n)
-            try:
-                self.manager.context_len(sid)
-                all_slots.append(self.manager.append_tokens(sid, n))
-            except NotLiveError:
-                all_slots.append(self.manager.allocate_for_prefill(sid, n))
-            lens.append(self.manager.context_len(sid))
+        if not (len(seq_ids) == len(rows) == len(chunk_lens)):
+            raise ValueError("one row and one chunk length per sequence")
+        # all or nothing: a batch the free list cannot hold changes nothing
+        slots, lens = self.manager.admit_batch(seq_ids, chunk_lens, extend_live=True)
         self._run_copies()
-        slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
         if slots.size:
             self._write(key, value, self._stage.to_device(slots))
         self._publish_rows(seq_ids, rows)
         B = len(seq_ids)
         q_start = np.concatenate([[0], np.cumsum(np.asarray(chunk_lens, dtype=np.int64))]).astype(np.int32)
         d_qs = self._stage.to_device(q_start)
-        d_lens = self._stage.to_device(np.asarray(lens, dtype=np.int32))
-        tables = self.tables[self._stage.to_device(np.asarray(list(rows), dtype=np.int64))]
+        d_lens = self._stage.to_device(lens)
+        rows_np = np.asarray(list(rows), dtype=np.int32)
+        if np.array_equal(rows_np, np.arange(B, dtype=np.int32)):
+            tables = self.tables[:B]                 # the rows already in batch order: a view
+        else:                                        # the batch's rows gathered in order
+            tables = torch.empty((B, self.width), dtype=torch.int32, device=self.device)
+            copy_table_rows(tables, self.tables, B, src_rows=self._stage.to_device(rows_np))
         max_q = int(max(chunk_lens)) if B else 0
         max_len = int(max(lens)) if B else 0
         if self.fp8:
@@ -199,12 +212,14 @@ class PagedKVEngine:
                      key: torch.Tensor, value: torch.Tensor) -> np.ndarray:
         """Admit several sequences whose prompt rows are concatenated in
         ``key``/``value`` ([sum(lengths), H_kv, D]) with one write launch and
-        one table publication (``rows`` distinct)."""
+        one table publication (``rows`` distinct).  The allocation is all or
+        nothing (pkv_admit_batch): when one sequence cannot be admitted, no
+        sequence is, and nothing is written or published."""
         _check_distinct(rows)
-        all_slots = []
-        for sid, n in zip(seq_ids, lengths):
-            all_slots.append(self.manager.allocate_for_prefill(int(sid), int(n)))
-        slots = np.concatenate(all_slots) if all_slots else np.empty(0, np.int64)
+        if not (len(seq_ids) == len(rows) == len(lengths)):
+            raise ValueError("one row and one length per sequence")
+        # all or nothing: a batch the free list cannot hold changes nothing
+        slots, _ = self.manager.admit_batch(seq_ids, lengths, extend_live=False)
         if slots.size:
             d_slots = self._stage.to_device(slots)
             self._write(key, value, d_slots)
@@ -281,15 +296,17 @@ class PagedKVEngine:
 
     def _publish_rows(self, seq_ids: Sequence[int], rows: Sequence[int]):
         """The table rows of several sequences at once (distinct rows): one
-        table read from the manager, one staged copy, one row scatter."""
+        table read from the manager, one staged copy, one row scatter
+        (pkv_copy_table_rows)."""
         if len(rows) == 1:
             self._publish_row(int(seq_ids[0]), int(rows[0]))
             return
         if len(rows) == 0:
             return
         tab = self.manager.block_tables([int(x) for x in seq_ids], self.width, -1)
-        d_rows = self._stage.to_device(np.asarray(rows, dtype=np.int64))
-        self.tables.index_copy_(0, d_rows, self._stage.to_device(tab).view(len(rows), self.width))
+        d_rows = self._stage.to_device(np.asarray(rows, dtype=np.int32))
+        copy_table_rows(self.tables, self._stage.to_device(tab).view(len(rows), self.width), len(rows),
+                        dst_rows=d_rows)
         for sid, row in zip(seq_ids, rows):
             self.row_seq[int(row)] = int(sid)
 

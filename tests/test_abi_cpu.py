@@ -97,6 +97,16 @@ def test_write_argument_checks_need_no_gpu():
     assert lib.pkv_update_block_tables(fake, -1, 4, None, fake, fake, 3, 16, None) == -1
 
 
+def test_table_row_copy_argument_checks_need_no_gpu():
+    lib = pkv.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pkv_copy_table_rows(fake, 8, 4, None, fake, 8, 4, None, -1, 8, None) == -1   # n < 0
+    assert lib.pkv_copy_table_rows(fake, 4, 4, None, fake, 8, 4, None, 2, 8, None) == -1    # width > dst stride
+    assert lib.pkv_copy_table_rows(fake, 8, 4, None, fake, 4, 4, None, 2, 8, None) == -1    # width > src stride
+    assert lib.pkv_copy_table_rows(None, 8, 4, None, fake, 8, 4, None, 2, 8, None) == -1    # no table
+    assert lib.pkv_copy_table_rows(fake, 8, 4, None, fake, 8, 4, None, 0, 8, None) == 0     # nothing to do
+
+
 def test_manager_create_rejects_bad_arguments():
     with pytest.raises(ValueError):
         pkv.KVBlockManager(0, 16)

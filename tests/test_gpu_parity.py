@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import synth
+import paged_kv_cache_128_amd as pkv
 from oracle.replay import decode_state
 
 from gpu_harness import bits_u, engine_for, run_step, to_device, TORCH_DTYPE
@@ -327,3 +328,27 @@ def test_fused_decode_step_equals_separate_launches(dtype, hq, hkv, B):
         assert torch.equal(engs[0].d_lens[:B], engs[1].d_lens[:B]), step
         assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), step
         assert bool(torch.isfinite(oa).all())
+
+
+def test_copy_table_rows_scatter_and_gather():
+    """pkv_copy_table_rows against numpy: rows scattered by a destination
+    list, gathered by a source list, both lists, and rows outside either
+    table skipped."""
+    rng = np.random.default_rng(31)
+    src = rng.integers(-1, 1000, (9, 7)).astype(np.int32)
+    dst0 = rng.integers(-1, 1000, (12, 10)).astype(np.int32)
+    d_src = torch.from_numpy(src).cuda()
+    for dst_rows, src_rows in (([3, 0, 11, 5], None), (None, [8, 2, 2, 0]), ([1, 7, 4], [6, 0, 3]),
+                               ([2, 12, -1, 9], [1, 4, 0, 99])):
+        n = len(dst_rows if dst_rows is not None else src_rows)
+        want = dst0.copy()
+        for i in range(n):
+            dr = dst_rows[i] if dst_rows is not None else i
+            sr = src_rows[i] if src_rows is not None else i
+            if 0 <= dr < 12 and 0 <= sr < 9:
+                want[dr, :7] = src[sr]
+        d_dst = torch.from_numpy(dst0).cuda()
+        dev = lambda r: None if r is None else torch.tensor(r, dtype=torch.int32, device="cuda")
+        pkv.copy_table_rows(d_dst, d_src, n, dst_rows=dev(dst_rows), src_rows=dev(src_rows))
+        torch.cuda.synchronize()
+        assert np.array_equal(d_dst.cpu().numpy(), want), (dst_rows, src_rows)

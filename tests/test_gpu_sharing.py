@@ -147,3 +147,64 @@ def test_admissions_through_a_wrapping_staging_arena():
     torch.cuda.synchronize()
     assert np.array_equal(eng.tables.cpu().numpy(), om.block_tables(list(range(len(lens))), width, -1))
     assert np.array_equal(bits_u(eng.key_cache), okc) and np.array_equal(bits_u(eng.value_cache), ovc)
+
+
+def test_batch_admission_is_all_or_nothing():
+    """A prefill_many / prefill_chunk batch whose k-th sequence does not fit
+    the free list raises OOM and leaves the manager (free list, tables,
+    lengths), the device tables and the whole pool as they were; a batch
+    that fits is then written bit for bit as the oracle writes it."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    _banner("all-or-nothing batch admission")
+    N, H, bs, D, hq = 12, 2, 16, 128, 4
+    rng = np.random.default_rng(77)
+    order = rng.permutation(N)
+    eng = PagedKVEngine(N, H, bs, D, torch.bfloat16, 4, 8, order, fill_bits=synth.POISON_BITS["bf16"],
+                        num_q_heads=hq)
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc = oracle.new_pool(N, H, bs, D, synth.poison_array((), "bf16"))
+
+    def rows(n):
+        return synth.normal(rng, (n, H, D), "bf16"), synth.normal(rng, (n, H, D), "bf16")
+
+    k0, v0 = rows(40)
+    eng.prefill_many([10, 11], [0, 1], [24, 16], to_device(k0, "bf16"), to_device(v0, "bf16"))
+    for sid, (a, b) in ((10, (0, 24)), (11, (24, 40))):
+        oracle.write_kv(k0[a:b], v0[a:b], om.allocate_for_prefill(sid, b - a), okc, ovc, bs)
+    torch.cuda.synchronize()
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return (eng.manager.free_list(), eng.tables.clone(), eng.pool.clone(),
+                [eng.manager.context_len(s) for s in (10, 11)])
+
+    def unchanged(before):
+        after = snapshot()
+        assert after[0] == before[0] and after[3] == before[3]
+        assert torch.equal(after[1], before[1])
+        assert torch.equal(after[2].view(torch.int16), before[2].view(torch.int16))
+        for s in (12, 13):
+            with pytest.raises(pkv.NotLiveError):
+                eng.manager.context_len(s)
+
+    before = snapshot()                                   # 3 blocks used, 9 free
+    kb, vb = rows(16 + 16 * 9)
+    with pytest.raises(pkv.OutOfBlocksError):             # 1 + 9 blocks: the second sequence does not fit
+        eng.prefill_many([12, 13], [2, 3], [16, 16 * 9], to_device(kb, "bf16"), to_device(vb, "bf16"))
+    unchanged(before)
+    q = to_device(synth.normal(rng, (16 + 16 * 9, hq, D), "bf16"), "bf16")
+    with pytest.raises(pkv.OutOfBlocksError):             # extending 10 by 16 needs 1, 13 new needs 9
+        eng.prefill_chunk([10, 13], [0, 3], [16, 16 * 9], to_device(kb, "bf16"), to_device(vb, "bf16"), q, 0.1)
+    unchanged(before)
+    with pytest.raises(pkv.AlreadyPrefilledError):        # live id in prefill_many
+        eng.prefill_many([12, 11], [2, 3], [1, 1], to_device(kb[:2], "bf16"), to_device(vb[:2], "bf16"))
+    unchanged(before)
+    # a batch that fits: everything written and published
+    kf, vf = rows(16 + 32)
+    eng.prefill_many([12, 13], [2, 3], [16, 32], to_device(kf, "bf16"), to_device(vf, "bf16"))
+    for sid, (a, b) in ((12, (0, 16)), (13, (16, 48))):
+        oracle.write_kv(kf[a:b], vf[a:b], om.allocate_for_prefill(sid, b - a), okc, ovc, bs)
+    torch.cuda.synchronize()
+    assert eng.manager.free_list() == om.free
+    assert np.array_equal(eng.tables.cpu().numpy(), om.block_tables([10, 11, 12, 13], 8, -1))
+    assert np.array_equal(bits_u(eng.pool[:, 0]), okc) and np.array_equal(bits_u(eng.pool[:, 1]), ovc)

@@ -219,3 +219,63 @@ def test_append_tokens_matches_oracle(seed, n_blocks, bs):
         kinds.add(res[0][0][0] if res[0][0][0] == "ok" else res[0][0][1])
         assert c.free_list() == o.free and c.check_invariants() and o.check_invariants() == []
     assert {"ok", "OutOfBlocks"} <= kinds
+
+
+def _admit(mgr, ids, lens, extend, impl):
+    try:
+        r = mgr.admit_batch(ids, lens, extend_live=extend)
+        if impl == "c":
+            return "ok", [int(x) for x in r[0]]
+        return "ok", [int(x) for chunk in r for x in chunk]
+    except (oracle.ManagerError, pkv.PkvError) as e:
+        for o, c in ERR.items():
+            if isinstance(e, o) or isinstance(e, c):
+                return "err", o.__name__
+        raise
+
+
+@pytest.mark.parametrize("seed,n_blocks,bs", [(21, 40, 4), (22, 12, 1), (23, 64, 16), (24, 30, 3)])
+def test_admit_batch_traces_match_oracle(seed, n_blocks, bs):
+    """All-or-nothing batch admission (pkv_admit_batch) interleaved with
+    shares, appends and frees: same slots, error kinds and state as the
+    oracle after every op; every failed batch leaves the state unchanged."""
+    rng = np.random.default_rng(seed)
+    o = oracle.BlockManager(n_blocks, bs, rng.permutation(n_blocks))
+    c = pkv.KVBlockManager(n_blocks, bs, o.free[:])
+    ids = list(range(12))
+    kinds = set()
+    for _ in range(1500):
+        u = rng.random()
+        if u < 0.45:
+            k = int(rng.integers(0, 5))
+            batch = [int(x) for x in rng.integers(0, 12, k)]
+            if rng.random() < 0.2:
+                batch.append(-1 if rng.random() < 0.5 else (batch[0] if batch else 3))
+            lens = [int(x) for x in rng.integers(0, 3 * bs + 2, len(batch))]
+            extend = bool(rng.random() < 0.6)
+            before = (o.free[:], {s: (o.context_len(s), o.block_table(s)) for s in ids if o.is_live(s)})
+            ro = _admit(o, batch, lens, extend, "o")
+            rc = _admit(c, batch, lens, extend, "c")
+            assert ro == rc, (batch, lens, extend, ro, rc)
+            if ro[0] == "err":
+                assert (o.free, {s: (o.context_len(s), o.block_table(s)) for s in ids if o.is_live(s)}) == before
+            kinds.add(("admit", ro[1] if ro[0] == "err" else "ok"))
+        elif u < 0.55:
+            donor, sid = int(rng.integers(12)), int(rng.integers(12))
+            n = int(rng.integers(0, 3 * bs))
+            for mgr in (o, c):
+                try:
+                    mgr.share_prefix(donor, sid, n)
+                except (oracle.ManagerError, pkv.PkvError):
+                    pass
+        elif u < 0.8:
+            op = ("append", int(rng.integers(12)))
+            assert _run(o, op, "o") == _run(c, op, "c")
+        else:
+            op = ("free", int(rng.integers(12)))
+            assert _run(o, op, "o") == _run(c, op, "c")
+        o.take_copies()
+        c.take_copies()
+        _same_state(o, c, ids)
+    assert {("admit", "ok"), ("admit", "OutOfBlocks"), ("admit", "AlreadyPrefilled"),
+            ("admit", "InvalidArgument")} <= kinds
