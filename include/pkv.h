@@ -609,12 +609,14 @@ int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const void* q, int
  *            [-126, 127] (0 for an all-zero row),
  *     code = E4M3(x * 2^-e), round to nearest, ties to even; a negative-zero
  *            code is stored as 0x00,
- * and the row reads back as E4M3(code) * 2^e.  Scale bytes mirror the code
+ * and the row reads back as E4M3(code) * 2^e.  The maximum runs over the
+ * row's finite elements; an infinity or a NaN is stored as the E4M3 NaN
+ * code with its sign (0x7F, 0xFF), so it reads back as NaN.  Scale bytes mirror the code
  * layout with one byte per row: the scale of row (pb, h, off) is at
  *     scales + pb * (block_stride / head_dim) + h * (head_stride / head_dim) + off
  * (an interleaved scale pool [N, 2, H_kv, bs] next to a code pool
  * [N, 2, H_kv, bs, D]: key scales = pool, value scales = pool + H_kv * bs).
- * Inputs must be finite.  The write calls accept head_dim 64 or 128; the
+ * The write calls accept head_dim 64 or 128; the
  * attention takes the stream path shapes (head_dim 128, H_kv <= 8,
  * H_q / H_kv <= 8, block_size a multiple of 16).
  */

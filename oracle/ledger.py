@@ -1,22 +1,36 @@
-"""Byte and utilisation bookkeeping (oracle, test infrastructure only)."""
+"""Byte and utilisation bookkeeping (oracle, test infrastructure only).
+
+Everything here is the KV-size formula of [MiniPaged-Qwen] §2,
+M_KV = 2 * N_layer * L * H_kv * D * bytes (K and V, every layer and KV
+head, L tokens), applied to a pool of blocks and to one block table.  The
+result keys are the names [leetcode-22]'s asserted tests check.
+"""
 from __future__ import annotations
 
 from typing import Dict
 
 
+def kv_cache_bytes(tokens: int, num_layers: int, num_kv_heads: int, head_dim: int,
+                   dtype_bytes: int) -> int:
+    """M_KV of [MiniPaged-Qwen] §2 for ``tokens`` tokens."""
+    return 2 * num_layers * tokens * num_kv_heads * head_dim * dtype_bytes
+
+
 def estimate_kv_cache_bytes(num_blocks: int, block_size: int, num_layers: int,
                             num_kv_heads: int, head_dim: int, dtype_bytes: int = 2) -> Dict[str, int]:
-    """Capacity ledger ([leetcode-22] Step 4 TODO 1; [MiniPaged-Qwen] §2's
-    M_KV = 2 * N_layer * L * H_kv * D * bytes): one token holds K and V for
-    every layer and KV head; a block holds block_size tokens; the pool holds
-    num_blocks blocks."""
-    dims = (num_blocks, block_size, num_layers, num_kv_heads, head_dim, dtype_bytes)
-    if any(x <= 0 for x in dims):
-        raise ValueError("all ledger dimensions must be positive")
-    per_token = 2 * num_layers * num_kv_heads * head_dim * dtype_bytes
-    per_block = block_size * per_token
-    return {"kv_bytes_per_token": per_token, "kv_bytes_per_block": per_block,
-            "total_cache_bytes": num_blocks * per_block}
+    """Capacity of a pool of ``num_blocks`` blocks of ``block_size`` tokens
+    ([leetcode-22] Step 4 TODO 1): M_KV of one token and of every token the
+    pool can hold."""
+    shape = dict(num_blocks=num_blocks, block_size=block_size, num_layers=num_layers,
+                 num_kv_heads=num_kv_heads, head_dim=head_dim, dtype_bytes=dtype_bytes)
+    bad = [k for k, x in shape.items() if x <= 0]
+    if bad:
+        raise ValueError(f"ledger dimensions must be positive: {', '.join(bad)}")
+    per_token = kv_cache_bytes(1, num_layers, num_kv_heads, head_dim, dtype_bytes)
+    return {"kv_bytes_per_token": per_token,
+            "kv_bytes_per_block": per_token * block_size,
+            "total_cache_bytes": kv_cache_bytes(num_blocks * block_size, num_layers, num_kv_heads, head_dim,
+                                                dtype_bytes)}
 
 
 def tail_waste(seq_len: int, block_size: int) -> int:
@@ -27,9 +41,10 @@ def tail_waste(seq_len: int, block_size: int) -> int:
 
 
 def allocation_report(num_table_blocks: int, seq_len: int, block_size: int) -> Dict[str, float]:
-    """Logical tokens, allocated tokens, unused tail and utilisation
-    ([leetcode-22] Step 4 ``allocation_report``)."""
-    allocated = num_table_blocks * block_size
-    return {"logical_tokens": seq_len, "allocated_tokens": allocated,
-            "unused_tail_tokens": allocated - seq_len,
-            "utilization": (seq_len / allocated) if allocated else 0.0}
+    """How much of a table's blocks a sequence of ``seq_len`` tokens fills
+    ([leetcode-22] Step 4 ``allocation_report``): the slots the table
+    covers, the ones past the last token, and the filled fraction."""
+    slots = num_table_blocks * block_size
+    empty = slots - seq_len
+    return {"allocated_tokens": slots, "unused_tail_tokens": empty,
+            "utilization": 1.0 - empty / slots if slots else 0.0}

@@ -13,7 +13,12 @@ block's rows never need re-quantising as the block fills:
   [-126, 127]; an all-zero row takes e = 0;
 * code = E4M3(x * 2^-e), and the row reads back as decode(code) * 2^e; a
   code of negative zero (0x80) is stored as 0x00, so stored codes never use
-  0x80, which the other 8-bit E4M3 variant (no negative zero) reads as NaN.
+  0x80, which the other 8-bit E4M3 variant (no negative zero) reads as NaN;
+* non-finite inputs (the pages say nothing of them; reading taken): the
+  scale is chosen from the row's finite elements only, and an infinity or a
+  NaN is stored as the NaN code with its sign (0x7F / 0xFF), so it reads
+  back as NaN, as a non-finite value in a 16-bit cache would poison the
+  attention that reads it.
 
 Multiplying by 2^-e is exact in float32 (the inputs are float32-widened
 16-bit or float32 values), so the only rounding is the E4M3 one.  Pins:
@@ -46,11 +51,14 @@ def e4m3_decode(code: int) -> float:
 
 def e4m3_encode(x: float) -> int:
     """Nearest E4M3 byte to the finite value x (|x| <= 448), ties to an even
-    mantissa; the sign of zero is kept."""
+    mantissa; the sign of zero is kept.  An infinity or a NaN gives the NaN
+    code with its sign."""
     x = float(x)
-    if not np.isfinite(x) or abs(x) > E4M3_MAX:
-        raise ValueError("E4M3 encode of a non-finite or out-of-range value")
     sign = 0x80 if np.signbit(x) else 0
+    if not np.isfinite(x):
+        return sign | 0x7F
+    if abs(x) > E4M3_MAX:
+        raise ValueError("E4M3 encode of an out-of-range value")
     a = abs(x)
     if a < 2.0 ** -6:
         return sign | int(np.rint(a * 2.0 ** 9))          # 0..8 (8 = smallest normal)
@@ -64,8 +72,11 @@ def e4m3_encode(x: float) -> int:
 
 
 def row_scale_exponent(row: np.ndarray) -> int:
-    """e of the row's scale 2^e: smallest with max|x| <= 448 * 2^e."""
-    amax = float(np.max(np.abs(row.astype(np.float64)))) if row.size else 0.0
+    """e of the row's scale 2^e: smallest with max|x| <= 448 * 2^e, the
+    maximum over the row's finite elements."""
+    r = row.astype(np.float64)
+    r = r[np.isfinite(r)]
+    amax = float(np.max(np.abs(r))) if r.size else 0.0
     if amax == 0.0:
         return 0
     m, k = np.frexp(amax)                                 # amax = m * 2^k, m in [0.5, 1)
@@ -95,11 +106,13 @@ def quantize_rows(rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     max, the exact power-of-two scaling, then E4M3 round to nearest even);
     returns (codes uint8 [..., D], scale bytes uint8 [...])."""
     x = rows.astype(np.float32)
-    amax = np.abs(x).max(axis=-1).astype(np.float64)
+    fin = np.isfinite(x)
+    amax = np.where(fin, np.abs(x), 0.0).max(axis=-1).astype(np.float64)
     m, k = np.frexp(amax)
     e = (k - 1) - 8 + (2.0 * m > 1.75)
     e = np.where(amax == 0.0, 0, np.clip(e, -126, 127)).astype(np.int64)
     y = (x.astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None])   # exact
+    y = np.where(fin, y, 0.0)                            # non-finite elements: NaN code below
     a = np.abs(y)
     sign = np.where(np.signbit(y), 0x80, 0)
     sub = a < 2.0 ** -6
@@ -110,6 +123,7 @@ def quantize_rows(rows: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     normal = ((E + 7) << 3) + (r - 8)
     code = np.where(sub, np.rint(a * 2.0 ** 9).astype(np.int64), normal)
     code = np.where(code == 0, 0, code | sign)
+    code = np.where(fin, code, np.where(np.signbit(x), 0xFF, 0x7F))
     return code.astype(np.uint8), (e + 127).astype(np.uint8)
 
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void quantize_store(const float (&x)[8], int lpr, int
                                                uint8_t* code_row, uint8_t* scale) {
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, pkv::finite_abs(x[i]));
   for (int o = lpr / 2; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   const int e = pkv::row_exponent(amax);
   uint32_t w0 = 0, w1 = 0;

@@ -2,7 +2,9 @@
 // the decode step that writes inside the 8-bit attention launch
 // (pkv_kernels.hip), so both produce the same bits: E4M3 codes (OCP, round
 // to nearest even, a zero code stored as +0) of x * 2^-e with e the smallest
-// integer such that max|x| <= 448 * 2^e (clamped to [-126, 127]).
+// integer such that max|x| <= 448 * 2^e (clamped to [-126, 127]), the
+// maximum taken over the row's finite elements; a non-finite element (an
+// infinity or a NaN) is stored as the E4M3 NaN code with its sign.
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -10,10 +12,19 @@
 
 namespace pkv {
 
-// E4M3 byte of a finite y with |y| <= 448, ties to an even mantissa.
+// |x| for a finite x, 0 for an infinity or a NaN: the magnitude a row's
+// scale is chosen from.
+__device__ __forceinline__ float finite_abs(float x) {
+  const float a = fabsf(x);
+  return a <= 3.4028235e38f ? a : 0.f;          // false for +inf and NaN
+}
+
+// E4M3 byte of y: for a finite y with |y| <= 448 the nearest code, ties to
+// an even mantissa; for an infinity or a NaN the NaN code S.1111.111.
 __device__ __forceinline__ uint32_t e4m3_code(float y) {
   const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
   const float a = fabsf(y);
+  if (!(a <= 3.4028235e38f)) return sign | 0x7fu;
   uint32_t c;
   if (a < 0x1p-6f) {
     c = static_cast<uint32_t>(rintf(a * 512.0f));                 // subnormal: m * 2^-9, m = 0..8

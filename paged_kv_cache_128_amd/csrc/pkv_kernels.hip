@@ -1542,8 +1542,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
         float ak = 0.f, av = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          ak = fmaxf(ak, fabsf(xk[i]));
-          av = fmaxf(av, fabsf(xv[i]));
+          ak = fmaxf(ak, pkv::finite_abs(xk[i]));
+          av = fmaxf(av, pkv::finite_abs(xv[i]));
         }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) {

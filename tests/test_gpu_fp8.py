@@ -45,6 +45,17 @@ def _special_rows(rng, D):
     return np.stack(rows)
 
 
+_NON_FINITE = {"bf16": (0x7F80, 0xFF80, 0x7FC0), "f16": (np.inf, -np.inf, np.nan),
+               "f32": (np.inf, -np.inf, np.nan)}
+
+
+def _plant_non_finite(a, dtype, t):
+    """+inf, -inf and NaN (in a's storage format) into token t's first head:
+    its row scale then comes from the finite elements, and those three take
+    the NaN code with their sign."""
+    a[t, 0, 1], a[t, 0, 4], a[t, 0, 9] = _NON_FINITE[dtype]
+
+
 @pytest.mark.parametrize("src,H,bs,D,T", [("bf16", 4, 16, 128, 200), ("f16", 2, 16, 128, 37),
                                           ("f32", 8, 32, 64, 50)])
 def test_fp8_write_bit_exact(src, H, bs, D, T):
@@ -57,6 +68,8 @@ def test_fp8_write_bit_exact(src, H, bs, D, T):
         sp = _special_rows(rng, D)
         k[:len(sp), 0] = sp
         v[:len(sp), H - 1] = -sp
+    _plant_non_finite(k, src, 5)
+    _plant_non_finite(v, src, 7)
     slots = rng.permutation(N * bs)[:T].astype(np.int64)
     slots[3] = N * bs + 5                            # outside the pool: skipped
     codes, kc, vc, scales, ks, vs = pkv.new_fp8_pool(N, H, bs, D, "cuda", poison=True)
@@ -456,3 +469,46 @@ def test_event_timed_steps_equal_plain_steps(dt):
         assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), step
         assert torch.equal(engs[0].pool.view(torch.uint8), engs[1].pool.view(torch.uint8)), step
         assert torch.equal(engs[0].tables, engs[1].tables) and torch.equal(engs[0].d_lens, engs[1].d_lens)
+
+
+@pytest.mark.parametrize("q_dtype", ["bf16", "f16"])
+def test_fused_fp8_step_codes_non_finite_new_rows_like_the_oracle(q_dtype):
+    """The 8-bit decode step quantises the new rows inside the attention
+    launch; rows holding +inf, -inf and NaN are stored exactly as the
+    oracle's quantiser stores them (NaN codes with their signs, the scale
+    from the finite elements).  Only the stored bytes are compared: the
+    attention over such rows is NaN."""
+    rng = np.random.default_rng(91)
+    N, H, hq, bs, D, B = 64, 4, 28, 16, 128, 6
+    lens = np.array([17, 1, 33, 64, 5, 48], dtype=np.int32)        # after the append
+    codes, kc, vc, scales, ks, vs = pkv.new_fp8_pool(N, H, bs, D, "cuda", poison=True)
+    width = 8
+    tabs = np.full((B, width), -1, dtype=np.int32)
+    perm = rng.permutation(N)
+    at = 0
+    for b in range(B):
+        nb = -(-int(lens[b]) // bs)
+        tabs[b, :nb] = perm[at:at + nb]
+        at += nb
+    slots = np.array([tabs[b, (lens[b] - 1) // bs] * bs + (lens[b] - 1) % bs for b in range(B)], dtype=np.int64)
+    k = synth.normal(rng, (B, H, D), q_dtype)
+    v = synth.normal(rng, (B, H, D), q_dtype)
+    for t in (0, 3):
+        _plant_non_finite(k, q_dtype, t)
+        _plant_non_finite(v, q_dtype, t)
+    q = synth.normal(rng, (B, hq, D), q_dtype)
+    tables = torch.from_numpy(tabs).cuda()
+    lens_out = torch.zeros(B, dtype=torch.int32, device="cuda")
+    assert pkv.attention_path(B, hq, int(lens.max()), kc, 0) == "stream"
+    pkv.decode_step_fp8(to_device(q, q_dtype), to_device(k, q_dtype), to_device(v, q_dtype), slots, lens, kc, vc,
+                        ks, vs, tables, lens_out, 0.088, int(lens.max()))
+    torch.cuda.synchronize()
+    okc, ovc, oks, ovs = quant.new_fp8_pool(N, H, bs, D)
+    quant.write_kv_fp8(_f32(k, q_dtype), _f32(v, q_dtype), slots, okc, ovc, oks, ovs, bs)
+    for b in range(B):
+        pb, off = divmod(int(slots[b]), bs)
+        for got, want in ((kc, okc), (vc, ovc)):
+            assert np.array_equal(_u8(got[pb, :, off]), want[pb, :, off]), b
+        for got, want in ((ks, oks), (vs, ovs)):
+            assert np.array_equal(_u8(got[pb, :, off]), want[pb, :, off]), b
+    assert _u8(kc[int(slots[0]) // bs, 0, int(slots[0]) % bs])[[1, 4, 9]].tolist() == [0x7F, 0xFF, 0x7F]

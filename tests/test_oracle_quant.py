@@ -244,3 +244,24 @@ def test_fp8_prefill_equals_16bit_prefill_on_the_read_back_values():
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
     bad = quant.prefill_attention_fp8(qb, "bf16", q_start, kc, vc, ks, ks, tables, lens, 0.25)
     assert np.abs(bad - want).max() > 1e-3
+
+
+def test_non_finite_elements_take_the_nan_code_and_leave_the_scale_to_the_finite_ones():
+    """A row holding an infinity and a NaN, worked by hand: the largest
+    finite magnitude is 2 = 2^1, so e = 1 - 8 = -7 and x * 2^7 is coded:
+    1 -> 128 = 2^7 -> (7 + 7) << 3 = 0x70; 2 -> 2^8 -> 0x78; -2 -> 0xF8;
+    0.5 -> 2^6 -> 0x68; 0 -> 0x00; -inf -> 0xFF; +inf and NaN -> 0x7F.
+    The scalar and the array encoders agree, and the NaN codes read back as
+    NaN."""
+    row = np.array([1.0, 2.0, -np.inf, np.nan, 0.5, -2.0, np.inf, 0.0], dtype=np.float32)
+    want = [0x70, 0x78, 0xFF, 0x7F, 0x68, 0xF8, 0x7F, 0x00]
+    codes, sb = quant.quantize_row(row)
+    assert list(codes) == want and sb == 127 - 7
+    c2, s2 = quant.quantize_rows(row[None])
+    assert list(c2[0]) == want and int(s2[0]) == 127 - 7
+    back = quant.dequantize(c2, s2)[0]
+    assert np.isnan(back[[2, 3, 6]]).all()
+    assert back[[0, 1, 4, 5, 7]].tolist() == [1.0, 2.0, 0.5, -2.0, 0.0]
+    # a row with no finite nonzero element takes e = 0
+    c3, s3 = quant.quantize_rows(np.array([[np.nan, -np.inf, 0.0, 0.0]], dtype=np.float32))
+    assert list(c3[0]) == [0x7F, 0xFF, 0, 0] and int(s3[0]) == 127
