@@ -556,10 +556,13 @@ int pkv_decode_step_noalloc(void* out, int32_t out_dtype, const void* q, const v
  *   q_start      device int32 [num_seqs + 1], non-decreasing from 0
  *   context_lens device int32 [num_seqs], clamped to [0, max_context_len]
  *   max_q_len    host, >= every n_b (sizes the grid)
- * Products run on the matrix cores in the cache's 16-bit type with fp32
- * accumulation; P enters P.V as a 16-bit value plus a 16-bit remainder.
- * Supported: 16-bit KV, head_dim 128, block_size a multiple of 16 (8-bit
- * KV: paged_prefill_attention_fp8).  Errors: INVALID, UNSUPPORTED, HIP.
+ * With 16-bit KV, head_dim 128 and block_size a multiple of 16 the
+ * products run on the matrix cores in the cache's 16-bit type with fp32
+ * accumulation, P entering P.V as a 16-bit value plus a 16-bit remainder;
+ * any other cache type (fp32) or shape (head_dim 64, other block sizes)
+ * takes a generic kernel, fp32 throughout.  Supported: head_dim 64 or 128,
+ * fp32, fp16 or bf16 KV (8-bit KV: paged_prefill_attention_fp8).  Errors:
+ * INVALID, UNSUPPORTED, HIP.
  */
 int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const int32_t* q_start,
                             const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len,
@@ -573,19 +576,19 @@ int paged_prefill_attention(void* out, int32_t out_dtype, const void* q, const i
  * PKV_FP8_E4M3; scale bytes as in the FP8 section below).  Computes what
  * paged_prefill_attention computes, with every cached row read back as
  * decode(code) * 2^(scale byte - 127) ([impl-detail] "实践建议": a block's
- * KV quantised on its own).  The blocks the sequences hold (the first
- * ceil(L_b / bs) table entries) are first dequantised into a 16-bit staging
- * pool of the queries' type and a table in `workspace` (device, 256-byte
- * aligned, at least paged_prefill_attention_fp8_workspace_size bytes, owned
- * by the caller, overwritten), then the 16-bit kernel runs on them.  q_dtype
- * PKV_BF16 or PKV_F16 (else UNSUPPORTED); out_dtype PKV_F32 or q_dtype
- * (else INVALID).  A bf16 staging holds every read-back value exactly for
- * row scales 2^-124 .. 2^119.  An fp16 staging holds them exactly for row
- * scales 2^-15 .. 2^7, which covers rows quantised from fp16 tensors except
- * those within 0.05 % of fp16's largest value; values beyond fp16's range
- * clamp to +-65504, and rows with smaller scales keep their values to the
- * nearest 2^-24.  Other arguments as for paged_prefill_attention.  Errors:
- * INVALID, UNSUPPORTED, WORKSPACE, HIP.
+ * KV quantised on its own).  With bf16 queries, head_dim 128 and
+ * block_size a multiple of 16, the blocks the sequences hold (the first
+ * ceil(L_b / bs) table entries) are first dequantised into a bf16 staging
+ * pool and a table in `workspace` (device, 256-byte aligned, at least
+ * paged_prefill_attention_fp8_workspace_size bytes, owned by the caller,
+ * overwritten), then the matrix-core kernel runs on them; bf16 holds every
+ * read-back value exactly for row scales 2^-124 .. 2^119.  Otherwise (fp16
+ * queries, head_dim 64, other block sizes) a generic kernel reads the codes
+ * in place, applying each row's scale in fp32, exact for every scale, and
+ * the workspace is not used.  q_dtype PKV_BF16 or PKV_F16 (else
+ * UNSUPPORTED); out_dtype PKV_F32 or q_dtype (else INVALID).  Other
+ * arguments as for paged_prefill_attention.  Errors: INVALID, UNSUPPORTED,
+ * WORKSPACE, HIP.
  */
 size_t paged_prefill_attention_fp8_workspace_size(int32_t num_seqs, int32_t max_context_len,
                                                   const pkv_cache_layout* layout);

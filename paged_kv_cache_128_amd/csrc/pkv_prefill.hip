@@ -416,6 +416,12 @@ prefill_kernel(PrefillArgs a) {
 
 namespace {
 
+int prefill_generic(void* out, int32_t out_dtype, const void* q, int32_t q_dtype, const int32_t* q_start,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len, const void* key_cache,
+                    const void* value_cache, const uint8_t* key_scales, const uint8_t* value_scales,
+                    const pkv_cache_layout* l, const int32_t* block_tables, int32_t block_table_stride,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* stream);
+
 int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_start, const int32_t* context_lens,
                int32_t num_seqs, int32_t max_q_len, const void* key_cache, const void* value_cache,
                const pkv_cache_layout* l, const int32_t* block_tables, int32_t block_table_stride,
@@ -424,8 +430,8 @@ int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_sta
       max_context_len < 0 || block_table_stride < 0)
     return PKV_ERR_INVALID;
   if (num_q_heads % l->num_kv_heads != 0 || !(scale == scale)) return PKV_ERR_INVALID;
-  if (l->dtype != PKV_BF16 && l->dtype != PKV_F16) return PKV_ERR_UNSUPPORTED;
-  if (l->head_dim != kD || l->block_size % kKeys != 0) return PKV_ERR_UNSUPPORTED;
+  if (l->dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;          // paged_prefill_attention_fp8
+  if (l->head_dim != 64 && l->head_dim != 128) return PKV_ERR_UNSUPPORTED;
   if (out_dtype != PKV_F32 && out_dtype != l->dtype) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
     return PKV_ERR_INVALID;
@@ -433,17 +439,24 @@ int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_sta
   if (!out || !q || !q_start || !context_lens || !key_cache || !value_cache ||
       (max_context_len > 0 && !block_tables))
     return PKV_ERR_INVALID;
+  // the matrix-core kernel: 16-bit KV, head_dim 128, block_size a multiple
+  // of 16, 16-byte aligned rows, the table entries within LDS; any other
+  // shape takes the generic kernel
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
                           reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache);
-  if (align % 16 != 0 || (l->head_stride * 2) % 16 != 0 || (l->block_stride * 2) % 16 != 0)
-    return PKV_ERR_UNSUPPORTED;
   const size_t lds = static_cast<size_t>(4 * kTileSlots) * 16 +
                     static_cast<size_t>((max_context_len + l->block_size - 1) / l->block_size + 1) * 4;
   int dev = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return PKV_ERR_HIP;
-  if (lds > static_cast<size_t>(lds_max)) return PKV_ERR_UNSUPPORTED;
+  const bool mfma = (l->dtype == PKV_BF16 || l->dtype == PKV_F16) && l->head_dim == kD &&
+                    l->block_size % kKeys == 0 && align % 16 == 0 && (l->head_stride * 2) % 16 == 0 &&
+                    (l->block_stride * 2) % 16 == 0 && lds <= static_cast<size_t>(lds_max);
+  if (!mfma)
+    return prefill_generic(out, out_dtype, q, l->dtype, q_start, context_lens, num_seqs, max_q_len, key_cache,
+                           value_cache, nullptr, nullptr, l, block_tables, block_table_stride, num_q_heads,
+                           max_context_len, scale, stream);
   const int64_t gx = (static_cast<int64_t>(max_q_len) + kRowsPerWG - 1) / kRowsPerWG;
   if (gx * num_q_heads * num_seqs > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
   PrefillArgs a;
@@ -478,6 +491,199 @@ int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_sta
   else
     hipLaunchKernelGGL(prefill_kernel<PKV_F16>, grid, dim3(kWave * kWavesPF), lds, s, a);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// ------------------------------------------------------------ generic prefill
+// The same causal attention for the shapes the matrix-core kernel does not
+// take (fp32 KV, head_dim 64, block sizes that are not a multiple of 16)
+// and for 8-bit blocks read in place, each row as E4M3(code) * 2^e with the
+// scale applied in fp32 (every scale exact).  One wave per (query row,
+// query head), fp32 throughout: lanes take 64 keys at a time, lane l forming
+// the score of key k0 + l from its whole K row (the query row broadcast from
+// LDS); the wave then takes the tile's max, rescales its running state
+// (online softmax, [MiniPaged-Qwen] §17.3), and adds the tile's weighted V
+// rows key by key in key order, lane l owning head-dims l and l + 64.  Keys
+// past the row's position are never read.  Every sum runs in a fixed order,
+// so the result is reproducible bit for bit.
+struct GenericArgs {
+  const void* q;             // [T, H_q, D], q_dtype
+  const int32_t* q_start;    // [B + 1]
+  const int32_t* lens;       // [B]
+  const void* kc;
+  const void* vc;
+  const uint8_t* ks;         // 8-bit KV: scale bytes
+  const uint8_t* vs;
+  const int32_t* tables;
+  void* out;                 // [T, H_q, D]
+  int64_t block_stride;      // elements
+  int64_t head_stride;
+  int64_t sblock_stride;     // scale bytes (8-bit KV)
+  int64_t shead_stride;
+  int32_t table_stride;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t hq;
+  int32_t group;
+  int32_t num_seqs;
+  int32_t max_q_len;         // rows per sequence slot of the grid
+  int32_t max_len;
+  int32_t out_dtype;
+  float scale_log2;
+};
+
+// Element i of a row of type DT, widened to fp32 (8-bit: the code's value
+// before its row scale).
+template <int DT>
+__device__ __forceinline__ float elem_f32(const void* row, int i) {
+  if constexpr (DT == PKV_F32) return static_cast<const float*>(row)[i];
+  else if constexpr (DT == PKV_BF16) return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[i]) << 16);
+  else if constexpr (DT == PKV_F16) return static_cast<float>(static_cast<const _Float16*>(row)[i]);
+  else {
+    const uint8_t c = static_cast<const uint8_t*>(row)[i];
+    return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
+  }
+}
+
+template <int KT, int QT, int D>
+__global__ void __launch_bounds__(kWave)
+prefill_generic_kernel(GenericArgs a) {
+  constexpr int kEb = KT == PKV_F32 ? 4 : (KT == PKV_FP8_E4M3 ? 1 : 2);
+  constexpr int kPer = D / kWave;
+  __shared__ float qs[D];
+  const int lane = threadIdx.x;
+  // workgroup (b, i, qh): query row i of sequence b, query head qh
+  const int qh = static_cast<int>(blockIdx.x % a.hq);
+  const int64_t t = blockIdx.x / a.hq;
+  const int i_row = static_cast<int>(t % a.max_q_len);
+  const int b = static_cast<int>(t / a.max_q_len);
+  const int r0 = a.q_start[b], n = a.q_start[b + 1] - r0;
+  if (i_row >= n) return;
+  const int64_t trow = static_cast<int64_t>(r0) + i_row;
+  const int Lraw = a.lens[b];
+  const int L = Lraw < 0 ? 0 : (Lraw > a.max_len ? a.max_len : Lraw);
+  const int pos = L - n + i_row;                            // keys 0 .. pos
+  const int64_t o = (trow * a.hq + qh) * D;
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  if (pos >= 0) {
+    for (int d = lane; d < D; d += kWave) qs[d] = elem_f32<QT>(static_cast<const char*>(a.q) + o * (QT == PKV_F32 ? 4 : 2), d);
+    __syncthreads();
+    const int kvh = qh / a.group;
+    const char* kc = static_cast<const char*>(a.kc);
+    const char* vc = static_cast<const char*>(a.vc);
+    const int bs = a.block_size;
+    for (int k0 = 0; k0 <= pos; k0 += kWave) {
+      const int k = k0 + lane;
+      const bool valid = k <= pos;
+      // this lane's key: its row offset (elements) and, for 8-bit KV, its scale bytes' offset
+      int64_t roff = 0, soff = 0;
+      if (valid) {
+        int pb = a.tables[static_cast<int64_t>(b) * a.table_stride + k / bs];
+        pb = pb < 0 ? 0 : (pb >= a.num_blocks ? a.num_blocks - 1 : pb);
+        roff = static_cast<int64_t>(pb) * a.block_stride + static_cast<int64_t>(kvh) * a.head_stride +
+               static_cast<int64_t>(k % bs) * D;
+        soff = static_cast<int64_t>(pb) * a.sblock_stride + static_cast<int64_t>(kvh) * a.shead_stride + k % bs;
+      }
+      float sc = -INFINITY;
+      if (valid) {
+        const char* krow = kc + roff * kEb;
+        float dot = 0.f;
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[d], elem_f32<KT>(krow, d), dot);
+        if constexpr (KT == PKV_FP8_E4M3) dot = __builtin_amdgcn_ldexpf(dot, static_cast<int>(a.ks[soff]) - 127);
+        sc = dot * a.scale_log2;
+      }
+      float tm = sc;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+      const float m_new = fmaxf(m, tm);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
+      const float p = valid ? __builtin_amdgcn_exp2f(sc - m_new) : 0.f;
+      float ps = p;
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
+      l = l * alpha + ps;
+      m = m_new;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] *= alpha;
+      const int nk = min(kWave, pos - k0 + 1);
+      for (int j = 0; j < nk; ++j) {
+        const float pj = __shfl(p, j);
+        const int64_t rj = __shfl(roff, j);
+        float vsc = 1.f;
+        if constexpr (KT == PKV_FP8_E4M3) vsc = __builtin_amdgcn_ldexpf(1.f, static_cast<int>(a.vs[__shfl(soff, j)]) - 127);
+        const char* vrow = vc + rj * kEb;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[e] = fmaf(pj, elem_f32<KT>(vrow, e * kWave + lane) * vsc, acc[e]);
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const float y = acc[e] * inv;
+    const int64_t i = o + e * kWave + lane;
+    if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[i] = y;
+    else if (a.out_dtype == PKV_BF16) static_cast<uint16_t*>(a.out)[i] = to16<PKV_BF16>(y);
+    else static_cast<uint16_t*>(a.out)[i] = to16<PKV_F16>(y);
+  }
+}
+
+template <int KT, int QT>
+hipError_t launch_generic(const GenericArgs& a, int D, hipStream_t s) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * a.max_q_len * a.hq));
+  if (D == 64) hipLaunchKernelGGL((prefill_generic_kernel<KT, QT, 64>), grid, dim3(kWave), 0, s, a);
+  else hipLaunchKernelGGL((prefill_generic_kernel<KT, QT, 128>), grid, dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+// Validates and launches the generic kernel: cache type l->dtype (8-bit:
+// key_scales / value_scales given), queries of type q_dtype (the cache's
+// for 16- and 32-bit KV; bf16 or fp16 for 8-bit KV).
+int prefill_generic(void* out, int32_t out_dtype, const void* q, int32_t q_dtype, const int32_t* q_start,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len, const void* key_cache,
+                    const void* value_cache, const uint8_t* key_scales, const uint8_t* value_scales,
+                    const pkv_cache_layout* l, const int32_t* block_tables, int32_t block_table_stride,
+                    int32_t num_q_heads, int32_t max_context_len, float scale, void* stream) {
+  if (l->head_dim != 64 && l->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  const int64_t waves = static_cast<int64_t>(num_seqs) * max_q_len * num_q_heads;
+  if (waves > 0x7fffffffLL) return PKV_ERR_UNSUPPORTED;
+  GenericArgs a;
+  a.q = q;
+  a.q_start = q_start;
+  a.lens = context_lens;
+  a.kc = key_cache;
+  a.vc = value_cache;
+  a.ks = key_scales;
+  a.vs = value_scales;
+  a.tables = block_tables;
+  a.out = out;
+  a.block_stride = l->block_stride;
+  a.head_stride = l->head_stride;
+  a.sblock_stride = l->block_stride / l->head_dim;
+  a.shead_stride = l->head_stride / l->head_dim;
+  a.table_stride = block_table_stride;
+  a.num_blocks = l->num_blocks;
+  a.block_size = l->block_size;
+  a.hq = num_q_heads;
+  a.group = num_q_heads / l->num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.max_q_len = max_q_len;
+  a.max_len = max_context_len;
+  a.out_dtype = out_dtype;
+  a.scale_log2 = scale * kLog2e;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (l->dtype) {
+    case PKV_F32: e = launch_generic<PKV_F32, PKV_F32>(a, l->head_dim, s); break;
+    case PKV_F16: e = launch_generic<PKV_F16, PKV_F16>(a, l->head_dim, s); break;
+    case PKV_BF16: e = launch_generic<PKV_BF16, PKV_BF16>(a, l->head_dim, s); break;
+    default:
+      e = q_dtype == PKV_BF16 ? launch_generic<PKV_FP8_E4M3, PKV_BF16>(a, l->head_dim, s)
+                              : launch_generic<PKV_FP8_E4M3, PKV_F16>(a, l->head_dim, s);
+  }
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
 // 8-bit blocks for prefill: one workgroup per (sequence b, logical block j,
@@ -600,17 +806,26 @@ extern "C" int paged_prefill_attention_fp8(void* out, int32_t out_dtype, const v
       max_context_len < 0 || block_table_stride < 0)
     return PKV_ERR_INVALID;
   if (l->dtype != PKV_FP8_E4M3 || (q_dtype != PKV_BF16 && q_dtype != PKV_F16)) return PKV_ERR_UNSUPPORTED;
-  if (l->head_dim != kD || l->block_size % kKeys != 0) return PKV_ERR_UNSUPPORTED;
+  if (l->head_dim != 64 && l->head_dim != 128) return PKV_ERR_UNSUPPORTED;
+  if (num_q_heads % l->num_kv_heads != 0 || !(scale == scale)) return PKV_ERR_INVALID;
   if (out_dtype != PKV_F32 && out_dtype != q_dtype) return PKV_ERR_INVALID;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(block_table_stride) * l->block_size)
     return PKV_ERR_INVALID;
+  if (l->head_stride % l->head_dim != 0 || l->block_stride % l->head_dim != 0) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || max_q_len == 0) return PKV_OK;
-  if (!key_cache || !value_cache || !key_scales || !value_scales || !context_lens ||
+  if (!out || !q || !q_start || !key_cache || !value_cache || !key_scales || !value_scales || !context_lens ||
       (max_context_len > 0 && !block_tables))
     return PKV_ERR_INVALID;
-  if (((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) % 8) != 0 ||
+  // bf16 queries, head_dim 128, block_size a multiple of 16: the blocks
+  // dequantised into the bf16 staging, then the matrix-core kernel; any
+  // other case (fp16 queries included, whose 16-bit type could not hold
+  // every read-back value) reads the codes in place in the generic kernel
+  if (q_dtype != PKV_BF16 || l->head_dim != kD || l->block_size % kKeys != 0 ||
+      ((reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache)) % 8) != 0 ||
       l->head_stride % 8 != 0 || l->block_stride % 8 != 0)
-    return PKV_ERR_UNSUPPORTED;
+    return prefill_generic(out, out_dtype, q, q_dtype, q_start, context_lens, num_seqs, max_q_len, key_cache,
+                           value_cache, key_scales, value_scales, l, block_tables, block_table_stride, num_q_heads,
+                           max_context_len, scale, stream);
   const size_t need = fp8_staging_bytes(num_seqs, max_context_len, l);
   if (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return PKV_ERR_WORKSPACE;

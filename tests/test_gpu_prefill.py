@@ -24,12 +24,13 @@ def _banner(msg):
     print(f"[gpu] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,out_dtype", [("bf16", 28, 4, None), ("f16", 32, 8, None),
-                                                    ("bf16", 12, 2, "bf16")])
-def test_chunked_prefill_matches_oracle(dtype, hq, hkv, out_dtype):
+@pytest.mark.parametrize("dtype,hq,hkv,out_dtype,bs,D", [
+    ("bf16", 28, 4, None, 16, 128), ("f16", 32, 8, None, 16, 128), ("bf16", 12, 2, "bf16", 16, 128),
+    # shapes the matrix-core kernel does not take: the generic kernel
+    ("f32", 4, 4, None, 16, 64), ("bf16", 8, 2, None, 8, 128), ("f16", 12, 2, "f16", 16, 64)])
+def test_chunked_prefill_matches_oracle(dtype, hq, hkv, out_dtype, bs, D):
     from paged_kv_cache_128_amd.engine import PagedKVEngine
-    rng = np.random.default_rng({"bf16": 81, "f16": 82}[dtype] + hq)
-    bs, D = 16, 128
+    rng = np.random.default_rng({"bf16": 81, "f16": 82, "f32": 83}[dtype] + hq + D + bs)
     first = [1, 37, 64, 130, 200, 5]
     second = [3, 64, 1, 77, 0, 150]
     B = len(first)
@@ -61,8 +62,8 @@ def test_chunked_prefill_matches_oracle(dtype, hq, hkv, out_dtype):
                                 to_device(v, dtype), to_device(q, dtype), scale, out=out)
         torch.cuda.synchronize()
         err = np.abs(got.double().cpu().numpy() - ref).max()
-        tol = 2e-3 if od is None else 2e-3 + np.abs(ref).max() * 2.0 ** -8
-        _banner(f"prefill {dtype} hq={hq} chunk {chunk}: max abs err {err:.3e}")
+        tol = (1e-5 if dtype == "f32" else 2e-3) if od is None else 2e-3 + np.abs(ref).max() * 2.0 ** -8
+        _banner(f"prefill {dtype} hq={hq} bs={bs} D={D} chunk {chunk}: max abs err {err:.3e}")
         assert err <= tol, err
 
 
@@ -94,20 +95,21 @@ def test_prefill_edge_cases():
     assert (dec[0] - out[14]).abs().max().item() <= 2e-3
 
 
-@pytest.mark.parametrize("hq,hkv,bs,out_dtype,dt", [(28, 4, 16, None, "bf16"), (12, 2, 32, "bf16", "bf16"),
-                                                   (28, 4, 16, None, "f16"), (12, 2, 32, "f16", "f16")])
-def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype, dt):
+@pytest.mark.parametrize("hq,hkv,bs,out_dtype,dt,D", [(28, 4, 16, None, "bf16", 128), (12, 2, 32, "bf16", "bf16", 128),
+                                                     (28, 4, 16, None, "f16", 128), (12, 2, 32, "f16", "f16", 128),
+                                                     (8, 2, 16, None, "bf16", 64), (8, 4, 8, "bf16", "bf16", 128)])
+def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype, dt, D):
     """Chunked prefill over an 8-bit pool (paged_prefill_attention_fp8:
-    the sequences' blocks dequantised into a 16-bit staging of the queries'
-    type, then the prefill kernel): the quantising writes bit for bit (codes
-    and scale bytes, poison included) and the attention within 2e-3 of the
-    oracle's 8-bit prefill attention, over two chunks per sequence, with
-    bf16 and with fp16 rows and queries."""
+    with bf16 queries, head_dim 128 and block_size a multiple of 16 the
+    blocks dequantised into a bf16 staging, then the matrix-core kernel;
+    otherwise the codes read in place by the generic kernel): the quantising
+    writes bit for bit (codes and scale bytes, poison included) and the
+    attention within 2e-3 of the oracle's 8-bit prefill attention, over two
+    chunks per sequence, with bf16 and with fp16 rows and queries."""
     from oracle import quant
     from paged_kv_cache_128_amd.engine import PagedKVEngine
-    _banner(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} out={out_dtype} {dt}")
-    rng = np.random.default_rng(90 + hq)
-    D = 128
+    _banner(f"fp8 prefill hq={hq} hkv={hkv} bs={bs} D={D} out={out_dtype} {dt}")
+    rng = np.random.default_rng(90 + hq + D + bs)
     first = [1, 37, 64, 130, 200, 5]
     second = [3, 64, 1, 77, 0, 150]
     B = len(first)
@@ -145,10 +147,45 @@ def test_fp8_chunked_prefill_matches_oracle(hq, hkv, bs, out_dtype, dt):
         assert err <= tol, err
 
 
+def test_fp8_prefill_with_fp16_queries_keeps_rows_beyond_fp16_range():
+    """8-bit rows written from fp32 tensors can carry scales no 16-bit fp16
+    value holds (V rows near 1e6, K rows near 2^-18); an fp16-query prefill
+    reads them in place with the row scale applied in fp32, so it agrees
+    with the oracle's read-back values as the 8-bit decode does."""
+    from oracle import quant
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    rng = np.random.default_rng(97)
+    hq, hkv, bs, D = 8, 2, 16, 128
+    chunk = [40, 25]
+    B, T = len(chunk), sum(chunk)
+    N = sum(-(-n // bs) for n in chunk) + 4
+    order = rng.permutation(N)
+    width = max(-(-n // bs) for n in chunk)
+    eng = PagedKVEngine(N, hkv, bs, D, torch.float8_e4m3fn, B, width, order, fill_bits=0, num_q_heads=hq)
+    k = (rng.standard_normal((T, hkv, D)) * 2.0 ** -18).astype(np.float32)
+    v = (rng.standard_normal((T, hkv, D)) * 1.0e6).astype(np.float32)
+    q = synth.normal(rng, (T, hq, D), "f16")
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    got = eng.prefill_chunk([0, 1], [0, 1], chunk, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                            to_device(q, "f16"), scale)
+    torch.cuda.synchronize()
+    om = oracle.BlockManager(N, bs, order)
+    o = quant.new_fp8_pool(N, hkv, bs, D)
+    slots = om.allocate_for_prefill(0, chunk[0]) + om.allocate_for_prefill(1, chunk[1])
+    quant.write_kv_fp8(k, v, slots, *o, bs)
+    assert int(o[2][o[2] != 0xFF].max()) - 127 < -15 and int(o[3][o[3] != 0xFF].min()) - 127 > 7
+    ref = quant.prefill_attention_fp8(q, "f16", [0, chunk[0], T], *o, om.block_tables([0, 1], width, -1),
+                                      om.context_lens([0, 1]), scale)
+    err = np.abs(got.double().cpu().numpy() - ref).max()
+    _banner(f"fp8 prefill, fp16 queries, rows beyond fp16: max abs err {err:.3e} of max |out| {np.abs(ref).max():.3e}")
+    assert err <= 2e-3 + 1e-6 * np.abs(ref).max()
+
+
 def test_fp8_prefill_refuses_bad_types_and_small_workspace():
     """Host-side checks of paged_prefill_attention_fp8: fp32 queries are
     UNSUPPORTED, an output type other than fp32 or the queries' is INVALID,
-    a short workspace is a WORKSPACE error; nothing is launched."""
+    a short workspace for the bf16 staging path is a WORKSPACE error;
+    nothing is launched."""
     lib = pkv.load_library()
     N, H, bs, D = 8, 2, 16, 128
     g = pkv.new_fp8_pool(N, H, bs, D, "cuda")
@@ -163,4 +200,5 @@ def test_fp8_prefill_refuses_bad_types_and_small_workspace():
     assert args(pkv.PKV_F16, pkv.PKV_BF16, fake, need) == -1
     assert args(pkv.PKV_BF16, pkv.PKV_F16, fake, need) == -1
     assert args(pkv.PKV_BF16, pkv.PKV_F32, fake, need - 1) == -7
-    assert args(pkv.PKV_F16, pkv.PKV_F32, fake, need - 1) == -7
+    # (fp16 queries read the codes in place and take no workspace: not called
+    # here, where the pointers are stand-ins)
