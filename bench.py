@@ -43,24 +43,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix peak
 CSRC = os.path.join(ROOT, "paged_kv_cache_128_amd", "csrc")
-# the decode attention kernels are built from this file and the headers it includes
+# the decode attention kernels are built from this file and the device headers
+# it includes; the prefill kernels from pkv_prefill.hip (the C header's comments
+# do not enter the hash)
 KERNEL_SOURCES = [os.path.join(CSRC, "pkv_kernels.hip"), os.path.join(CSRC, "pkv_internal.h"),
-                  os.path.join(CSRC, "pkv_fp8_codec.h"), os.path.join(ROOT, "include", "pkv.h")]
+                  os.path.join(CSRC, "pkv_fp8_codec.h")]
+PREFILL_SOURCES = [os.path.join(CSRC, "pkv_prefill.hip"), os.path.join(CSRC, "pkv_internal.h")]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (KERNEL_SOURCES if sources is None else sources):
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel_name: str, workload: str):
+def recorded_traffic(kernel_name: str, workload: str, sources=None):
     """HBM bytes per launch from the committed PMC summary
     profiles/<kernel>_<workload>.md, if it was taken from the current kernel
     source."""
@@ -70,7 +73,7 @@ def recorded_traffic(kernel_name: str, workload: str):
     text = open(path).read()
     sha = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     tb = re.search(r"traffic_bytes_per_launch:\s*([0-9.]+)", text)
-    if not sha or not tb or sha.group(1) != kernel_source_sha():
+    if not sha or not tb or sha.group(1) != kernel_source_sha(sources):
         return None, None
     return float(tb.group(1)), sha.group(1)
 
@@ -350,6 +353,12 @@ def measure_prefill(cfg, seqs: int = 8, prompt: int = 2048, iters: int = 20, see
             "useful_flops_per_launch": flops, "achieved_tflops": round(tflops, 1),
             "bound": "mfma", "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "matrix_flops_issued_per_launch": flops * 3 // 2,
+            "note": "useful FLOPs: row i sees i + 1 keys; the matrix cores also run P.V's remainder pass "
+                    "(1.5x the useful products)",
+            "traffic": None if kv8 else recorded_traffic("prefill_kernel", f"{cfg.name}_{seqs}x{prompt}",
+                                                          PREFILL_SOURCES)[0],
+            "kernel_source_sha256_16": kernel_source_sha(PREFILL_SOURCES),
             "prefill_tokens_per_s": round(seqs * prompt / (us * 1e-6), 1)}
 
 
