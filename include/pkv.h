@@ -271,6 +271,20 @@ int pkv_get_free_list(const pkv_manager* mgr, int32_t* out, int32_t cap, int32_t
  * Returns PKV_OK or PKV_ERR_INVARIANT. */
 int pkv_check_invariants(const pkv_manager* mgr);
 
+/* Debug check of a write's slot mapping, host only.  The pages' slot of a
+ * token is block * block_size + offset ([MiniPaged-Qwen] §11) and a
+ * manager hands each slot to one token ([mini-vLLM BM] "正确性不变量"
+ * recommends checking such ownership in debug runs); two tokens of one
+ * write with the same slot would race in the write kernels, whose result
+ * is then undefined.  `slot_mapping` is a HOST array of n int64 slots;
+ * entries outside [0, num_slots) are ignored, as the writes skip them.
+ * Returns PKV_OK when no in-range slot appears twice; PKV_ERR_INVALID when
+ * one does, with *first_repeat (optional) set to the smallest index whose
+ * slot an earlier entry already holds, and PKV_ERR_INVALID with
+ * *first_repeat = -1 for n < 0, num_slots < 0 or a NULL array with n > 0.
+ * O(n log n); nothing is kept. */
+int pkv_check_slot_mapping(const int64_t* slot_mapping, int64_t n, int64_t num_slots, int64_t* first_repeat);
+
 /* ------------------------------------------------------------- cache write */
 /*
  * Scatter the new tokens' K/V rows into the paged pool ([MiniPaged-Qwen]

@@ -63,6 +63,34 @@ def _check(status: int, what: str) -> int:
     return status
 
 
+# With PKV_DEBUG_SLOTS=1 in the environment every write entry point first
+# checks its slot mapping on the host (pkv_check_slot_mapping) and raises
+# on a slot that two rows would write; device slot tensors are copied to
+# the host for it (a synchronising copy: debug runs only).
+DEBUG_SLOTS = os.environ.get("PKV_DEBUG_SLOTS", "") == "1"
+
+
+def check_slot_mapping(slots, num_slots: int) -> None:
+    """Raise InvalidArgumentError if an in-range slot appears twice in
+    ``slots`` (host array, or a tensor copied to the host); slots outside
+    [0, num_slots) are ignored, as the writes skip them."""
+    if hasattr(slots, "detach"):
+        slots = slots.detach().cpu().numpy()
+    arr = np.ascontiguousarray(slots, dtype=np.int64).reshape(-1)
+    first = ctypes.c_int64(-1)
+    st = _lib_handle().pkv_check_slot_mapping(_ptr(arr, ctypes.c_int64), arr.size, int(num_slots),
+                                               ctypes.byref(first))
+    if st < 0 and first.value >= 0:
+        raise InvalidArgumentError(st, f"slot {int(arr[first.value])} written twice "
+                                       f"(entry {first.value} repeats an earlier one)")
+    _check(st, "pkv_check_slot_mapping")
+
+
+def _debug_slots(slots, lay) -> None:
+    if DEBUG_SLOTS:
+        check_slot_mapping(slots, int(lay.num_blocks) * int(lay.block_size))
+
+
 class CacheLayout(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32),
@@ -128,6 +156,7 @@ SIGNATURES = {
     "pkv_get_context_lens": (ctypes.c_int, [_P, _PI64, _I32, _PI32]),
     "pkv_get_free_list": (ctypes.c_int, [_P, _PI32, _I32, _PI32]),
     "pkv_check_invariants": (ctypes.c_int, [_P]),
+    "pkv_check_slot_mapping": (ctypes.c_int, [_PI64, ctypes.c_int64, ctypes.c_int64, _PI64]),
     "paged_kv_write": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(CacheLayout), _P]),
     "pkv_decode_write": (ctypes.c_int, [_P, _P, _PI64, _PI32, _I32, _P, _P, ctypes.POINTER(CacheLayout),
                                         _P, _I32, _I32, _P, _P]),
@@ -456,6 +485,7 @@ def paged_kv_write_fp8(key, value, slot_mapping, key_cache, value_cache, key_sca
         raise ValueError("key/value must be contiguous [num_tokens, H_kv, head_dim] of one dtype")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_contiguous():
         raise ValueError("slot_mapping must be contiguous int64 [num_tokens]")
+    _debug_slots(slot_mapping, lay)
     st = _lib_handle().paged_kv_write_fp8(key.data_ptr(), value.data_ptr(), dtype_code(key.dtype),
                                           slot_mapping.data_ptr(), T, key_cache.data_ptr(),
                                           value_cache.data_ptr(), key_scales.data_ptr(),
@@ -481,6 +511,7 @@ def decode_write_fp8(key, value, slots: np.ndarray, lens: np.ndarray, key_cache,
         if block_tables.dtype != torch.int32 or block_tables.stride(1) != 1:
             raise ValueError("block_tables must be int32 with unit column stride")
         tab_ptr, rows, stride = block_tables.data_ptr(), block_tables.shape[0], block_tables.stride(0)
+    _debug_slots(slots, lay)
     st = _lib_handle().pkv_decode_write_fp8(
         key.data_ptr(), value.data_ptr(), dtype_code(key.dtype), _ptr(slots, ctypes.c_int64),
         _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(), value_cache.data_ptr(),
@@ -511,6 +542,8 @@ def decode_step_fp8(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cach
         if phase != "both":
             raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if phase != "merge":
+        _debug_slots(slots, lay)
     head = (out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), dtype_code(q.dtype), key.data_ptr(),
             value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
             value_cache.data_ptr(), key_scales.data_ptr(), value_scales.data_ptr(), ctypes.byref(lay),
@@ -686,6 +719,7 @@ def paged_kv_write(key, value, slot_mapping, key_cache, value_cache, stream=None
         raise ValueError("key/value dtype must equal the cache dtype")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [num_tokens]")
+    _debug_slots(slot_mapping, lay)
     st = _lib_handle().paged_kv_write(key.data_ptr(), value.data_ptr(), slot_mapping.data_ptr(), T,
                                       key_cache.data_ptr(), value_cache.data_ptr(),
                                       ctypes.byref(lay), _stream_handle(stream))
@@ -821,6 +855,7 @@ def decode_write(key, value, slots: np.ndarray, lens: np.ndarray, key_cache, val
     if lens_out is not None and (lens_out.dtype != torch.int32 or lens_out.numel() < n
                                  or not lens_out.is_contiguous()):
         raise ValueError("lens_out must be a contiguous int32 tensor of at least n entries")
+    _debug_slots(slots, lay)
     st = _lib_handle().pkv_decode_write(
         key.data_ptr(), value.data_ptr(), _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n,
         key_cache.data_ptr(), value_cache.data_ptr(), ctypes.byref(lay),
@@ -870,6 +905,8 @@ def decode_step(q, key, value, slots: np.ndarray, lens: np.ndarray, key_cache, v
         if phase != "both":
             raise ValueError("a split-phase call needs an explicit workspace shared by both phases")
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if phase != "merge":
+        _debug_slots(slots, lay)
     args = (out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
             _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),
             value_cache.data_ptr(), ctypes.byref(lay), block_tables.data_ptr(), block_tables.stride(0),
@@ -930,6 +967,7 @@ def decode_step_noalloc(q, key, value, slots: np.ndarray, lens: np.ndarray, key_
         raise ValueError("lens_out must be a contiguous int32 tensor of at least n entries")
     if out.shape != (n, hq, d) or not out.is_contiguous():
         raise ValueError("out must be contiguous [n, H_q, head_dim]")
+    _debug_slots(slots, lay)
     st = _lib_handle().pkv_decode_step_noalloc(
         out.data_ptr(), dtype_code(out.dtype), q.data_ptr(), key.data_ptr(), value.data_ptr(),
         _ptr(slots, ctypes.c_int64), _ptr(lens, ctypes.c_int32), n, key_cache.data_ptr(),

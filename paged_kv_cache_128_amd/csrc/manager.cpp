@@ -556,4 +556,22 @@ int pkv_check_invariants(const pkv_manager* m) {
   return PKV_OK;
 }
 
+int pkv_check_slot_mapping(const int64_t* slot_mapping, int64_t n, int64_t num_slots, int64_t* first_repeat) {
+  if (first_repeat) *first_repeat = -1;
+  if (n < 0 || num_slots < 0 || (n > 0 && !slot_mapping)) return PKV_ERR_INVALID;
+  // (slot, index) pairs of the in-range entries; after sorting, equal slots
+  // sit together in index order, and each one but the first is a repeat
+  std::vector<std::pair<int64_t, int64_t>> v;
+  v.reserve(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i)
+    if (slot_mapping[i] >= 0 && slot_mapping[i] < num_slots) v.emplace_back(slot_mapping[i], i);
+  std::sort(v.begin(), v.end());
+  int64_t first = -1;
+  for (size_t k = 1; k < v.size(); ++k)
+    if (v[k].first == v[k - 1].first && (first < 0 || v[k].second < first)) first = v[k].second;
+  if (first < 0) return PKV_OK;
+  if (first_repeat) *first_repeat = first;
+  return PKV_ERR_INVALID;
+}
+
 }  // extern "C"

@@ -25,7 +25,9 @@
 //                                8-bit KV; section "stream-K attention").
 //  * attn_stream_step_kernel, -- the same, fused with the step's write (the
 //    attn_stream8_step_kernel    8-bit form quantises the new rows).
-//  * attn_stream_merge_kernel -- joins the stream kernel's partial segments.
+//  * attn_stream_merge_kernel, -- joins the stream kernel's partial
+//    attn_stream_merge_waves_kernel  segments (one wave, or four waves when
+//                                the sequences hold many pieces).
 //
 // Shared work mapping of the attention kernels (64-lane wavefronts):
 //  - The K/V pool is read in tiles of 16 consecutive logical tokens (a tile
@@ -1746,29 +1748,24 @@ attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
   stream_body<DT, GP, PAIRED, true, false>(a, &meta);
 }
 
-// Merge of the stream kernel's partials.  One 64-lane workgroup per
-// (sequence, query head).  A sequence with L = 0 gets zeros; one that a
-// single segment covered was finished already; otherwise its pieces are
-// combined as out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The
-// pieces of sequence b are, in every range that holds some of its tiles,
-// the part before the range's split tile x (front worker) and the part
-// from x on (back worker), where not empty.
-template <int D>
-__global__ void __launch_bounds__(kWave)
-attn_stream_merge_kernel(StreamArgs a) {
-  __shared__ int32_t plist[2 * kStreamMaxRanges];
-  const int lane = threadIdx.x;
-  const int qh = blockIdx.x % a.hq;
-  const int b = blockIdx.x / a.hq;
-  const int kvh = qh / a.group;
-  const int W = a.num_ranges;
-  const int R = a.ranges_per_wg;
-  const int J = R * a.hkv;
-  const bool paired = 2 * a.hkv <= kStreamMaxWaves;
-  auto len_of = [&](int j) { return clamp_len(a.lens[j], a.max_len); };
-  int before = 0, total = 0;
+// Merge of the stream kernel's partials, per (sequence, query head).  A
+// sequence with L = 0 gets zeros; one that a single segment covered was
+// finished already; otherwise its pieces are combined as
+// out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.  The pieces of
+// sequence b are, in every range that holds some of its tiles, the part
+// before the range's split tile x (front worker) and the part from x on
+// (back worker), where not empty.
+constexpr int kMergeChunk = 8;
+constexpr int kMergeWaves = 4;
+
+// Tile offset of sequence b and the launch's tile count, from the lengths
+// (one wave; every lane ends with both).
+__device__ __forceinline__ void merge_tile_counts(const StreamArgs& a, int b, int lane, int& before,
+                                                  int& total) {
+  before = 0;
+  total = 0;
   for (int j = lane; j < a.num_seqs; j += kWave) {
-    const int t = (len_of(j) + kTile - 1) / kTile;
+    const int t = (clamp_len(a.lens[j], a.max_len) + kTile - 1) / kTile;
     total += t;
     if (j < b) before += t;
   }
@@ -1777,22 +1774,19 @@ attn_stream_merge_kernel(StreamArgs a) {
     before += __shfl_xor(before, o);
     total += __shfl_xor(total, o);
   }
-  const int L = len_of(b);
-  const int64_t orow = (static_cast<int64_t>(b) * a.hq + qh) * D;
-  constexpr int kPer = D / kWave;
-  if (L == 0) {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int64_t o = orow + lane * kPer + e;
-      if (a.out_dtype == PKV_F32) static_cast<float*>(a.out)[o] = 0.f;
-      else static_cast<uint16_t*>(a.out)[o] = 0;
-    }
-    return;
-  }
-  const int Sb = before, Se = before + (L + kTile - 1) / kTile;
+}
+
+// Partial slots of the pieces of the sequence whose tiles are [Sb, Se)
+// (Se > Sb, so total >= 1) into plist, in range order; one wave.  Lane i
+// looks at ranges r_first + i, r_first + i + 64, ...  Returns their count.
+__device__ __forceinline__ int merge_piece_list(const StreamArgs& a, int kvh, int Sb, int Se, int total,
+                                                int lane, int32_t* plist) {
+  const int W = a.num_ranges;
+  const int R = a.ranges_per_wg;
+  const int J = R * a.hkv;
+  const bool paired = 2 * a.hkv <= kStreamMaxWaves;
   const int r_first = range_owner(Sb, total, W);
   const int r_last = range_owner(Se - 1, total, W);
-  // Piece list: lane i looks at ranges r_first + i, r_first + i + 64, ...
   int npieces = 0;
   for (int r0 = r_first; r0 <= r_last; r0 += kWave) {
     const int r = r0 + lane;
@@ -1818,20 +1812,22 @@ attn_stream_merge_kernel(StreamArgs a) {
     if (n > 1) plist[at + 1] = sl[1];
     npieces += __shfl(incl, kWave - 1);
   }
-  __syncthreads();
-  if (npieces <= 1) return;            // one segment covered the sequence
-  // Pieces in chunks of 8: every lane loads each piece's (m, l) and its own
-  // accumulator slice, all loads of a chunk in flight together, then folds
-  // the chunk into a running (M, den, num) with one rescale.
-  constexpr int kChunk = 8;
-  float M = -INFINITY, den = 0.f;
-  float num[kPer];
+  return npieces;
+}
+
+// Chunks j0, j0 + step, ... of kMergeChunk pieces folded into a running
+// (M, den, num): every lane loads each piece's (m, l) and its own
+// accumulator slice, all loads of a chunk in flight together, then folds
+// the chunk with one rescale.
+template <int D>
+__device__ __forceinline__ void merge_fold(const StreamArgs& a, const int32_t* plist, int npieces, int qh,
+                                           int lane, int j0, int step, float& M, float& den,
+                                           float (&num)[D / kWave]) {
+  constexpr int kPer = D / kWave;
+  for (; j0 < npieces; j0 += step) {
+    float mp[kMergeChunk], lp[kMergeChunk], v[kMergeChunk][kPer];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
-  for (int j0 = 0; j0 < npieces; j0 += kChunk) {
-    float mp[kChunk], lp[kChunk], v[kChunk][kPer];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < kMergeChunk; ++u) {
       const int j = min(j0 + u, npieces - 1);
       const int64_t sl = static_cast<int64_t>(plist[j]) * a.hq + qh;
       const float2 ml2 = *reinterpret_cast<const float2*>(a.ws_ml + 2 * sl);
@@ -1842,13 +1838,13 @@ attn_stream_merge_kernel(StreamArgs a) {
     }
     float Mc = M;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) Mc = fmaxf(Mc, mp[u]);
+    for (int u = 0; u < kMergeChunk; ++u) Mc = fmaxf(Mc, mp[u]);
     const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
     den *= r;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) num[e] *= r;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
+    for (int u = 0; u < kMergeChunk; ++u) {
       const float wt = (mp[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mp[u] - Mc);
       den = fmaf(wt, lp[u], den);
 #pragma unroll
@@ -1856,6 +1852,14 @@ attn_stream_merge_kernel(StreamArgs a) {
     }
     M = Mc;
   }
+}
+
+// Row out[b, qh] = num / den (zeros when den = 0, as for L = 0).
+template <int D>
+__device__ __forceinline__ void merge_store(const StreamArgs& a, int b, int qh, int lane, float den,
+                                            const float (&num)[D / kWave]) {
+  constexpr int kPer = D / kWave;
+  const int64_t orow = (static_cast<int64_t>(b) * a.hq + qh) * D;
   const float inv = den > 0.f ? 1.0f / den : 0.f;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -1865,6 +1869,92 @@ attn_stream_merge_kernel(StreamArgs a) {
     else if (a.out_dtype == PKV_BF16) static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(y);
     else static_cast<uint16_t*>(a.out)[o] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(y));
   }
+}
+
+// One wave per (sequence, query head): the form for launches whose
+// sequences have up to about two chunks of pieces.
+template <int D>
+__global__ void __launch_bounds__(kWave)
+attn_stream_merge_kernel(StreamArgs a) {
+  constexpr int kPer = D / kWave;
+  __shared__ int32_t plist[2 * kStreamMaxRanges];
+  const int lane = threadIdx.x;
+  const int qh = blockIdx.x % a.hq;
+  const int b = blockIdx.x / a.hq;
+  int before, total;
+  merge_tile_counts(a, b, lane, before, total);
+  const int L = clamp_len(a.lens[b], a.max_len);
+  float M = -INFINITY, den = 0.f;
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  if (L == 0) {
+    merge_store<D>(a, b, qh, lane, den, num);
+    return;
+  }
+  const int npieces = merge_piece_list(a, qh / a.group, before, before + (L + kTile - 1) / kTile, total,
+                                       lane, plist);
+  __syncthreads();
+  if (npieces <= 1) return;            // one segment covered the sequence
+  merge_fold<D>(a, plist, npieces, qh, lane, 0, kMergeChunk, M, den, num);
+  merge_store<D>(a, b, qh, lane, den, num);
+}
+
+// kMergeWaves waves per (sequence, query head), for launches whose
+// sequences have many pieces: wave w folds chunks w, w + kMergeWaves, ...
+// side by side, and wave 0 joins the waves' (M, den, num) in wave order.
+template <int D>
+__global__ void __launch_bounds__(kWave * kMergeWaves)
+attn_stream_merge_waves_kernel(StreamArgs a) {
+  constexpr int kPer = D / kWave;
+  __shared__ int32_t plist[2 * kStreamMaxRanges];
+  __shared__ int32_t s_npieces;
+  __shared__ float s_part[kMergeWaves][2 + D];     // per wave: M, den, num[D]
+  const int wave = uni(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int qh = blockIdx.x % a.hq;
+  const int b = blockIdx.x / a.hq;
+  float M = -INFINITY, den = 0.f;
+  float num[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  if (wave == 0) {
+    int before, total;
+    merge_tile_counts(a, b, lane, before, total);
+    const int L = clamp_len(a.lens[b], a.max_len);
+    const int np = L == 0 ? -1 : merge_piece_list(a, qh / a.group, before,
+                                                  before + (L + kTile - 1) / kTile, total, lane, plist);
+    if (lane == 0) s_npieces = np;
+  }
+  __syncthreads();
+  const int npieces = s_npieces;
+  if (npieces < 0) {                   // L = 0: wave 0 writes the zeros
+    if (wave == 0) merge_store<D>(a, b, qh, lane, den, num);
+    return;
+  }
+  if (npieces <= 1) return;            // one segment covered the sequence
+  merge_fold<D>(a, plist, npieces, qh, lane, wave * kMergeChunk, kMergeChunk * kMergeWaves, M, den, num);
+  if (lane == 0) {
+    s_part[wave][0] = M;
+    s_part[wave][1] = den;
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) s_part[wave][2 + lane * kPer + e] = num[e];
+  __syncthreads();
+  if (wave != 0) return;
+  const int nw = min(kMergeWaves, (npieces + kMergeChunk - 1) / kMergeChunk);
+  float Mt = s_part[0][0];
+  for (int w = 1; w < nw; ++w) Mt = fmaxf(Mt, s_part[w][0]);
+  den = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) num[e] = 0.f;
+  for (int w = 0; w < nw; ++w) {
+    const float rw = (s_part[w][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_part[w][0] - Mt);
+    den = fmaf(rw, s_part[w][1], den);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) num[e] = fmaf(rw, s_part[w][2 + lane * kPer + e], num[e]);
+  }
+  merge_store<D>(a, b, qh, lane, den, num);
 }
 
 // ------------------------------------------------------------ dispatch
@@ -2334,10 +2424,17 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
-        // lengths from device memory (for the decode step: lens_out, written by
-        // the first launch); a copy in the kernel arguments measured slower
+        // Lengths come from device memory (for the decode step: lens_out,
+        // written by the first launch); a copy in the kernel arguments
+        // measured slower.  A sequence spans about W / B ranges, two pieces each.  Beyond two
+        // chunks of pieces the waves of the multi-wave merge fold chunks
+        // side by side; below that the one-wave merge measured faster.
+        const int64_t pieces = 2 * ((pl.ranges + num_seqs - 1) / num_seqs) + 2;
         const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
-        hipLaunchKernelGGL(attn_stream_merge_kernel<128>, grid, dim3(kWave), 0, s, sa);
+        if (pieces > 2 * kMergeChunk)
+          hipLaunchKernelGGL(attn_stream_merge_waves_kernel<128>, grid, dim3(kWave * kMergeWaves), 0, s, sa);
+        else
+          hipLaunchKernelGGL(attn_stream_merge_kernel<128>, grid, dim3(kWave), 0, s, sa);
         if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
       }
       return PKV_OK;

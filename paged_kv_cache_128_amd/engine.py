@@ -336,7 +336,8 @@ class PagedKVEngine:
         (known on the host from the manager, no device sync).  ``events``
         (three torch.cuda.Event) are recorded before the attention kernel
         (with the fused step: the write-and-attention kernel), between it and
-        the merge, and after the merge; two are recorded around both.  ``fused`` = False forces the
+        the merge, and after the merge; two are recorded around the whole
+        step, a separate write launch included.  ``fused`` = False forces the
         separate write launch.  ``noalloc`` (16-bit pools, no events) runs the
         step through pkv_decode_step_noalloc: no workspace, the library's own
         per-GPU array instead."""
@@ -350,11 +351,16 @@ class PagedKVEngine:
         self._run_copies()
         if max_context_len is None:
             max_context_len = int(self.lens[:n].max()) if n else 0
+        # two events bracket the whole step, the separate write launch included
+        whole = events is not None and len(events) == 2
         if self.fp8 and not fused:
+            if whole:
+                events[0].record()
             decode_write_fp8(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache,
                              self.value_cache, self.key_scales, self.value_scales,
                              block_tables=self.tables, lens_out=self.d_lens)
-            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
+            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events,
+                               _started=whole)
         if self.fp8:
             ws = self.workspace(n, q.shape[1], max_context_len)
             if out is None:
@@ -369,9 +375,12 @@ class PagedKVEngine:
                                        self.value_cache, self.tables, self.d_lens, scale, max_context_len,
                                        out=out)
         if not (fused and self.partition_tokens == 0 and n > 0):
+            if whole:
+                events[0].record()
             decode_write(new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
                          block_tables=self.tables, lens_out=self.d_lens)
-            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events)
+            return self.attend(q, self.d_lens[:n], scale, max_context_len, out=out, events=events,
+                               _started=whole)
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
         args = (q, new_k, new_v, self.slots[:n], self.lens[:n], self.key_cache, self.value_cache,
@@ -380,8 +389,11 @@ class PagedKVEngine:
         return decode_step(*args, out=out, workspace=ws, events=events)
 
     def attend(self, q: torch.Tensor, lens: torch.Tensor, scale: float, max_context_len: int,
-               out: Optional[torch.Tensor] = None, events=None) -> torch.Tensor:
-        """Attention of rows 0..B-1 over the current cache (no append/write)."""
+               out: Optional[torch.Tensor] = None, events=None, _started: bool = False) -> torch.Tensor:
+        """Attention of rows 0..B-1 over the current cache (no append/write).
+        Two ``events`` bracket the launches, three also split them at the
+        partial / merge boundary; ``_started`` says the first of two events
+        was already recorded (before the step's write)."""
         n = q.shape[0]
         ws = self.workspace(n, q.shape[1], max_context_len)
         if out is None:
@@ -393,7 +405,8 @@ class PagedKVEngine:
             if events is None:
                 return paged_decode_attention_fp8(*args, **kw8)
             if len(events) == 2:
-                events[0].record()
+                if not _started:
+                    events[0].record()
                 paged_decode_attention_fp8(*args, **kw8)
                 events[1].record()
                 return out
@@ -406,7 +419,8 @@ class PagedKVEngine:
         kw = dict(partition_tokens=self.partition_tokens, max_context_len=max_context_len,
                   workspace=ws)
         if events is not None and len(events) == 2:
-            events[0].record()
+            if not _started:
+                events[0].record()
             paged_decode_attention(q, self.key_cache, self.value_cache, self.tables[:n], lens, scale,
                                    out=out, **kw)
             events[1].record()

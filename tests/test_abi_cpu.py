@@ -137,3 +137,50 @@ def test_block_copy_and_staging_dtype_checks_need_no_gpu():
     assert lib.pkv_copy_blocks_fp8(ids, ids, -1, fake, fake, fake, fake, ctypes.byref(l8), None) == -1
     assert lib.pkv_copy_blocks_fp8(ids, ids, 0, fake, fake, fake, fake, ctypes.byref(l8), None) == 0
     assert lib.pkv_gather_blocks_fp8(ids, 0, fake, fake, fake, fake, fake, fake, ctypes.byref(l8), None) == 0
+
+
+def test_slot_mapping_check_matches_brute_force():
+    """pkv_check_slot_mapping names the first entry whose in-range slot an
+    earlier entry holds (a write race), ignores out-of-range slots (the
+    writes skip them), and refuses bad arguments with first_repeat = -1."""
+    import numpy as np
+    lib = pkv.load_library()
+    rng = np.random.default_rng(5)
+    hits = 0
+    for _ in range(300):
+        n, N = int(rng.integers(0, 40)), int(rng.integers(1, 60))
+        sl = np.ascontiguousarray(rng.integers(-3, N + 3, n), dtype=np.int64)
+        want, seen = -1, set()
+        for i, x in enumerate(sl.tolist()):
+            if 0 <= x < N:
+                if x in seen:
+                    want = i
+                    break
+                seen.add(x)
+        first = ctypes.c_int64(-7)
+        st = lib.pkv_check_slot_mapping(sl.ctypes.data if n else None, n, N, ctypes.byref(first))
+        assert (st, first.value) == ((0, -1) if want < 0 else (-1, want)), (sl, N)
+        hits += want >= 0
+    assert 50 < hits < 250
+    first = ctypes.c_int64(-7)
+    assert lib.pkv_check_slot_mapping(None, 3, 10, ctypes.byref(first)) == -1 and first.value == -1
+    assert lib.pkv_check_slot_mapping(None, -1, 10, None) == -1
+    assert lib.pkv_check_slot_mapping(None, 0, 10, None) == 0
+
+
+def test_debug_slot_check_refuses_a_repeated_slot_before_any_launch(monkeypatch):
+    """With the debug check on, the write entry points raise on a slot two
+    rows would write, before anything is launched (CPU tensors here, so a
+    launch could not even start)."""
+    import numpy as np
+    import torch
+    pkv.check_slot_mapping(np.array([4, 1, -1, -1, 99]), 64)
+    with pytest.raises(pkv.InvalidArgumentError, match="slot 1 written twice"):
+        pkv.check_slot_mapping(np.array([4, 1, 7, 1]), 64)
+    monkeypatch.setattr(pkv, "DEBUG_SLOTS", True)
+    pool = torch.zeros(4, 2, 2, 16, 64)
+    k = torch.zeros(3, 2, 64)
+    with pytest.raises(pkv.InvalidArgumentError, match="entry 2"):
+        pkv.decode_write(k, k, np.array([5, 9, 5]), np.array([6, 10, 6], dtype=np.int32), pool[:, 0], pool[:, 1])
+    with pytest.raises(pkv.InvalidArgumentError, match="slot 17"):
+        pkv.paged_kv_write(k, k, torch.tensor([17, 3, 17]), pool[:, 0], pool[:, 1])

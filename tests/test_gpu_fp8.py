@@ -437,13 +437,16 @@ def test_fp8_engine_swap_round_trip_is_bit_exact():
     assert torch.equal(before.view(torch.int32), after.view(torch.int32))
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("dt", [torch.bfloat16, torch.float8_e4m3fn])
-def test_event_timed_steps_equal_plain_steps(dt):
-    """decode_step with timing events (the two launches issued from one
-    marshalled call, events between them) gives bit for bit the outputs,
-    cache and tables of plain decode steps, and the events measure."""
+def test_event_timed_steps_equal_plain_steps(dt, fused):
+    """decode_step with timing events (three: split at the partial / merge
+    boundary; two: around the whole step, a separate write launch included)
+    gives bit for bit the outputs, cache and tables of plain decode steps,
+    with the step's write inside the attention launch or in its own, and the
+    events measure."""
     from paged_kv_cache_128_amd.engine import PagedKVEngine
-    _banner(f"event-timed steps {dt}")
+    _banner(f"event-timed steps {dt} fused={fused}")
     rng = np.random.default_rng(91)
     B, hq, hkv, bs, D = 10, 28, 4, 16, 128
     lens = rng.integers(1, 200, B)
@@ -457,15 +460,15 @@ def test_event_timed_steps_equal_plain_steps(dt):
     for e in engs:
         e.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], k0, v0)
     ids = np.arange(B, dtype=np.int64)
-    for step in range(3):
+    for step in range(4):
         nk = to_device(synth.normal(rng, (B, hkv, D), "bf16"), "bf16")
         nv = to_device(synth.normal(rng, (B, hkv, D), "bf16"), "bf16")
         q = to_device(synth.normal(rng, (B, hq, D), "bf16"), "bf16")
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        oa = engs[0].decode_step(ids, nk, nv, q, 0.088, events=evs)
-        ob = engs[1].decode_step(ids, nk, nv, q, 0.088)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3 - step % 2)]
+        oa = engs[0].decode_step(ids, nk, nv, q, 0.088, events=evs, fused=fused)
+        ob = engs[1].decode_step(ids, nk, nv, q, 0.088, fused=fused)
         torch.cuda.synchronize()
-        assert evs[0].elapsed_time(evs[1]) > 0 and evs[1].elapsed_time(evs[2]) > 0
+        assert all(a.elapsed_time(b) > 0 for a, b in zip(evs, evs[1:]))
         assert torch.equal(oa.view(torch.int32), ob.view(torch.int32)), step
         assert torch.equal(engs[0].pool.view(torch.uint8), engs[1].pool.view(torch.uint8)), step
         assert torch.equal(engs[0].tables, engs[1].tables) and torch.equal(engs[0].d_lens, engs[1].d_lens)

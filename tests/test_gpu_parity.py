@@ -352,3 +352,44 @@ def test_copy_table_rows_scatter_and_gather():
         pkv.copy_table_rows(d_dst, d_src, n, dst_rows=dev(dst_rows), src_rows=dev(src_rows))
         torch.cuda.synchronize()
         assert np.array_equal(d_dst.cpu().numpy(), want), (dst_rows, src_rows)
+
+
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float8_e4m3fn])
+def test_debug_slot_checks_pass_on_manager_slots(dt, monkeypatch):
+    """With the debug slot check on, prefill and decode steps (fused and
+    separate writes) run as without it: the manager never hands one slot to
+    two rows, so nothing raises and pools and outputs keep their bits.  A
+    device slot mapping with a repeated slot is refused before any launch."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    _banner(f"debug slot checks {dt}")
+    rng = np.random.default_rng(77)
+    B, hq, hkv, bs, D = 12, 28, 4, 16, 128
+    lens = rng.integers(1, 300, B)
+    N = int(np.ceil((lens + 4) / bs).sum()) + 8
+    order = rng.permutation(N)
+    width = int(np.ceil((lens.max() + 4) / bs))
+    engs = [PagedKVEngine(N, hkv, bs, D, dt, B, width, order, fill_bits=0, partition_tokens=0, num_q_heads=hq)
+            for _ in range(2)]
+    k0 = torch.randn((int(lens.sum()), hkv, D), device="cuda").to(torch.bfloat16)
+    v0 = torch.randn((int(lens.sum()), hkv, D), device="cuda").to(torch.bfloat16)
+    ids = np.arange(B, dtype=np.int64)
+    for flag, e in zip((True, False), engs):
+        monkeypatch.setattr(pkv, "DEBUG_SLOTS", flag)
+        e.prefill_many(list(range(B)), list(range(B)), [int(x) for x in lens], k0, v0)
+    for step in range(4):
+        k = torch.randn((B, hkv, D), device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, hkv, D), device="cuda").to(torch.bfloat16)
+        q = torch.randn((B, hq, D), device="cuda").to(torch.bfloat16)
+        outs = []
+        for flag, e in zip((True, False), engs):
+            monkeypatch.setattr(pkv, "DEBUG_SLOTS", flag)
+            outs.append(e.decode_step(ids, k, v, q, 0.088, fused=step % 2 == 0))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32)), step
+        assert torch.equal(engs[0].pool.view(torch.uint8), engs[1].pool.view(torch.uint8)), step
+    monkeypatch.setattr(pkv, "DEBUG_SLOTS", True)
+    if dt == torch.bfloat16:
+        kk = torch.zeros((3, hkv, D), device="cuda", dtype=dt)
+        with pytest.raises(pkv.InvalidArgumentError, match="slot 40 written twice"):
+            pkv.paged_kv_write(kk, kk, torch.tensor([40, 41, 40], device="cuda"),
+                               engs[0].key_cache, engs[0].value_cache)
