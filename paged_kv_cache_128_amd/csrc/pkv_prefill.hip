@@ -23,10 +23,12 @@
 //   - adds O^T[d][row] += V^T P^T with 16x16x32 MFMAs whose k index 8 g4 + e
 //     stands for key 16 (e / 4) + 4 g4 + e % 4, so a lane's own eight
 //     probabilities are its B operand; MFMA j maps its row index c to
-//     head-dim 8 c + j, so its A operand is element j of the lane's V rows
-//     (head-dims 8 c16 .. 8 c16 + 7); P enters as a 16-bit value plus its
-//     16-bit remainder (two MFMAs; P to about 2^-17).
-// Lane (g4, c16) ends with its rows' head-dims 32 g4 .. 32 g4 + 31.  A wave
+//     head-dim 16 j + c, so its A operand (V at head-dim 16 j + c16 of keys
+//     4 g4 .. 4 g4 + 3 of each 16-key half) comes from two transposed LDS
+//     reads (ds_read_b64_tr_b16) with no lane permutes; P enters as a 16-bit
+//     value plus its 16-bit remainder (two MFMAs; P to about 2^-17).
+// Lane (g4, c16) ends with head-dims 16 j + 4 g4 .. 16 j + 4 g4 + 3 of its
+// rows, j = 0 .. 7.  A wave
 // skips the products of key ranges wholly past its rows' positions (it still
 // takes part in the staging).  Keys past L read zeros (buffer range check)
 // and are masked like every key past a row's position.  16-bit KV, head_dim
@@ -51,8 +53,14 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kSlack = 8.0f;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 constexpr int kWaitVm0 = 0x0f70;
-constexpr int kSubSlots = kKeys * kD * 2 / 16;        // 16-byte LDS slots of one K or V sub-tile
+constexpr int kSubSlots = kKeys * kD * 2 / 16;        // 16-byte LDS slots of one K sub-tile
 constexpr int kTileSlots = kSub * kSubSlots;
+// A V sub-tile is four blocks of four rows (block i: rows i, i + 4, i + 8,
+// i + 12), each block 1 KiB followed by a 32-byte pad: the four consecutive
+// rows one transposed read touches then start 32 bytes apart in the banks.
+constexpr int kVBlkSlots = 4 * kD * 2 / 16 + 2;       // 16-byte slots per V block, pad included
+constexpr int kVSubSlots = 4 * kVBlkSlots;
+constexpr int kVTileSlots = kSub * kVSubSlots;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -172,8 +180,8 @@ prefill_kernel(PrefillArgs a) {
   // dynamic LDS: [K tile x 2][V tile x 2] (16-byte slots), then the table entries
   extern __shared__ uint4 sh_pf[];
   uint4* sk = sh_pf;                                  // 2 x kTileSlots
-  uint4* sv = sh_pf + 2 * kTileSlots;                 // 2 x kTileSlots
-  int32_t* tbl = reinterpret_cast<int32_t*>(sh_pf + 4 * kTileSlots);
+  uint4* sv = sh_pf + 2 * kTileSlots;                 // 2 x kVTileSlots
+  int32_t* tbl = reinterpret_cast<int32_t*>(sh_pf + 2 * kTileSlots + 2 * kVTileSlots);
   const int wave = uni(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & (kWave - 1);
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -238,8 +246,9 @@ prefill_kernel(PrefillArgs a) {
   const char* vc = static_cast<const char*>(a.vc);
   const int64_t head_off = static_cast<int64_t>(kvh) * a.head_stride;
   // Stage tile kt into buffer kt % 2: wave w moves sub-tile w, K rows
-  // (chunk c of row r to slot c ^ r) and V rows (plain), four rows per
-  // 16-byte-per-lane DMA.  Rows past the workgroup's last key (a sub-tile
+  // (chunk c of row r to slot c ^ r; DMA i: rows 4 i .. 4 i + 3) and V rows
+  // (plain; DMA i: rows i, i + 4, i + 8, i + 12 into V block i), four rows
+  // per 16-byte-per-lane DMA.  Rows past the workgroup's last key (a sub-tile
   // wholly past it included) read zeros, so every V value that meets a zero
   // probability is finite and only staged table entries are used.
   auto stage = [&](int kt) {
@@ -251,13 +260,13 @@ prefill_kernel(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rk = rows_rsrc(kc + base, nvalid);
     const __amdgpu_buffer_rsrc_t rv = rows_rsrc(vc + base, nvalid);
     uint4* dk = sk + (kt & 1) * kTileSlots + wave * kSubSlots;
-    uint4* dv = sv + (kt & 1) * kTileSlots + wave * kSubSlots;
+    uint4* dv = sv + (kt & 1) * kVTileSlots + wave * kVSubSlots;
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + g4;
       dma16(rk, dk + 64 * i, r * kD * 2 + ((c16 ^ r) << 4));
-      dma16(rv, dv + 64 * i, r * kD * 2 + (c16 << 4));
+      dma16(rv, dv + kVBlkSlots * i, (i + 4 * g4) * kD * 2 + (c16 << 4));
     }
     asm volatile("" ::: "memory");
   };
@@ -281,7 +290,7 @@ prefill_kernel(PrefillArgs a) {
       const int key0 = (kt * kSub + sub) * kKeys;
       if (key0 > w_maxkey) break;                     // every key from here on is past this wave's rows
       const uint4* tk = sk + (kt & 1) * kTileSlots + sub * kSubSlots;
-      const uint4* tv = sv + (kt & 1) * kTileSlots + sub * kSubSlots;
+      const uint4* tv = sv + (kt & 1) * kVTileSlots + sub * kVSubSlots;
       // K operands: key c16 of half h, chunk 4 kk + g4 (slot (4 kk + g4) ^ c16)
       u32x4 kf[2][4];
 #pragma unroll
@@ -303,13 +312,21 @@ prefill_kernel(PrefillArgs a) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int c = 0; c < kBlocksPerWave; ++c) sa[h][c] = mfma_k32<DT>(kf[h][kk], qf[c][kk], sa[h][c]);
-      // V rows 4 g4 + r of each half, head-dims 8 c16 .. + 7 (read while the
-      // softmax runs)
-      uint4 vr[2][4];
+      // The P.V A operands, read while the softmax runs: transposed read
+      // (h, j) has lane i of each 16-lane group address row 4 g4 + i / 4 of
+      // half h (V block i / 4, row g4 in it), head-dims 16 j + 4 (i % 4) ..
+      // + 3, and gives lane c16 head-dim 16 j + c16 of rows 4 g4 .. 4 g4 + 3.
+      u32x2 vt[2][8];
+      {
+        const char* vb = reinterpret_cast<const char*>(tv) +
+                         ((c16 >> 2) * kVBlkSlots + g4 * (kD * 2 / 16)) * 16 + (c16 & 3) * 8;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vr[h][r] = tv[h * kSubSlots + (4 * g4 + r) * 16 + c16];
+          for (int j = 0; j < 8; ++j)
+            vt[h][j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4*)(vb + h * kVSubSlots * 16 + 32 * j)));
+      }
       // P as the B operand of the 32-key P.V: lane (g4, c16) gives row c16's
       // probabilities for k = 8 g4 + e, which stands for key 16 (e / 4) +
       // 4 g4 + e % 4 -- the lane's own scores, in order
@@ -360,20 +377,11 @@ prefill_kernel(PrefillArgs a) {
         bh[c] = u32x4{hw[0], hw[1], hw[2], hw[3]};
         bl[c] = u32x4{lw[0], lw[1], lw[2], lw[3]};
       }
-      // P.V: MFMA j maps its row index c to head-dim 8 c + j; its A operand is
-      // element j of V rows 4 g4 .. 4 g4 + 3 of half 0, then of half 1
+      // P.V: MFMA j maps its row index c to head-dim 16 j + c; its A operand is
+      // head-dim 16 j + c16 of keys 4 g4 .. 4 g4 + 3 of half 0, then of half 1
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        const int w = j >> 1;
-        uint32_t e[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            e[h][r] = w == 0 ? vr[h][r].x : w == 1 ? vr[h][r].y : w == 2 ? vr[h][r].z : vr[h][r].w;
-        const u32x4 av{__builtin_amdgcn_perm(e[0][1], e[0][0], sel), __builtin_amdgcn_perm(e[0][3], e[0][2], sel),
-                       __builtin_amdgcn_perm(e[1][1], e[1][0], sel), __builtin_amdgcn_perm(e[1][3], e[1][2], sel)};
+        const u32x4 av{vt[0][j][0], vt[0][j][1], vt[1][j][0], vt[1][j][1]};
 #pragma unroll
         for (int c = 0; c < kBlocksPerWave; ++c) {
           acc[c][j] = mfma_k32<DT>(av, bh[c], acc[c][j]);
@@ -387,27 +395,23 @@ prefill_kernel(PrefillArgs a) {
     const float lc = sum_over_g4(l[c]);
     if (!ok[c]) continue;
     const float inv = lc > 0.f ? 1.0f / lc : 0.f;
-    const int64_t o = ((static_cast<int64_t>(r0) + row[c]) * a.hq + qh) * kD + 32 * g4;
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[8 * i + j] = acc[c][j][i] * inv;
+    // head-dims 16 j + 4 g4 .. + 3 of the row: acc[c][j][i] is head-dim 16 j + 4 g4 + i
+    const int64_t o = ((static_cast<int64_t>(r0) + row[c]) * a.hq + qh) * kD + 4 * g4;
     if (a.out_dtype == PKV_F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.out) + o);
+      float* dst = static_cast<float*>(a.out) + o;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<float4*>(dst + 16 * j) =
+            make_float4(acc[c][j][0] * inv, acc[c][j][1] * inv, acc[c][j][2] * inv, acc[c][j][3] * inv);
     } else {
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + o);
+      uint16_t* dst = static_cast<uint16_t*>(a.out) + o;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e])) |
-                 (static_cast<uint32_t>(to16<DT>(v[8 * k + 2 * e + 1])) << 16);
-        dst[k] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint2*>(dst + 16 * j) =
+            make_uint2(static_cast<uint32_t>(to16<DT>(acc[c][j][0] * inv)) |
+                           (static_cast<uint32_t>(to16<DT>(acc[c][j][1] * inv)) << 16),
+                       static_cast<uint32_t>(to16<DT>(acc[c][j][2] * inv)) |
+                           (static_cast<uint32_t>(to16<DT>(acc[c][j][3] * inv)) << 16));
     }
   }
 }
@@ -444,7 +448,7 @@ int prefill_16(void* out, int32_t out_dtype, const void* q, const int32_t* q_sta
   // shape takes the generic kernel
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out) |
                           reinterpret_cast<uintptr_t>(key_cache) | reinterpret_cast<uintptr_t>(value_cache);
-  const size_t lds = static_cast<size_t>(4 * kTileSlots) * 16 +
+  const size_t lds = static_cast<size_t>(2 * kTileSlots + 2 * kVTileSlots) * 16 +
                     static_cast<size_t>((max_context_len + l->block_size - 1) / l->block_size + 1) * 4;
   int dev = 0, lds_max = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
