@@ -60,7 +60,7 @@ def test_random_traces_match_oracle(seed, n_blocks, bs, sort):
     c = pkv.KVBlockManager(n_blocks, bs, order, sort_on_release=sort)
     ids = list(range(30))
     kinds = set()
-    for op in synth.manager_op_trace(seed, 3000, max_id=30, max_prefill=50):
+    for op in synth.manager_op_trace(seed, 10_000, max_id=30, max_prefill=50):
         ro = _run(o, op, "o")
         rc = _run(c, op, "c")
         assert ro == rc, (op, ro, rc)

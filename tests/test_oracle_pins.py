@@ -242,7 +242,7 @@ def test_invariants_hold_on_random_traces(seed, n_blocks, bs):
     order = rng.permutation(n_blocks)
     m = BlockManager(n_blocks, bs, order, sort_on_release=bool(seed % 2))
     errors = {"ok": 0}
-    for op in synth.manager_op_trace(seed, 2500, max_id=30, max_prefill=40):
+    for op in synth.manager_op_trace(seed, 10_000, max_id=30, max_prefill=40):
         before = _state(m)
         try:
             if op[0] == "prefill":
