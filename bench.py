@@ -192,8 +192,8 @@ def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
 
 def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
     """Copy-on-write block copies (pkv_copy_blocks) on the workload's pool:
-    ``pairs`` allocated blocks copied into free ones per launch, timed with
-    HIP events around ``iters`` back-to-back launches.  Algorithmic bytes:
+    ``pairs`` allocated blocks copied into free ones per launch, each launch
+    timed between two HIP events (median of ``iters``).  Algorithmic bytes:
     every copied block is read once and written once."""
     import torch
     import paged_kv_cache_128_amd as pkv
@@ -208,15 +208,19 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
     for _ in range(5):
         pkv.copy_blocks(src, dst, eng.key_cache, eng.value_cache)
     torch.cuda.synchronize()
-    # back-to-back launches between one event pair, as copies arrive in a
-    # serving loop (an isolated launch would time mostly the launch itself)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
+    # each launch between two events queued behind a short device-side sleep,
+    # so that the launch is queued before the first event completes (back to
+    # back, the host's marshalling of the 256 pairs would set the pace)
+    times = []
     for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(200_000)
+        e0.record()
         pkv.copy_blocks(src, dst, eng.key_cache, eng.value_cache)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / iters
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
     moved = 2 * n * block_bytes
     gbps = moved / (us * 1e-6) / 1e9
     log(f"block copy: {n} blocks of {block_bytes} B in {us:.2f} us per launch ({gbps:.0f} GB/s)")
@@ -224,6 +228,50 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
             "algorithmic_bytes_per_launch": moved, "mean_launch_us": round(us, 3),
             "achieved_gbps": round(gbps, 2), "peak_gbps": HBM_PEAK_GBPS,
             "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def measure_write(eng, k, v, iters: int = 50):
+    """The step's write on its own: the last timed step's rows written again
+    at its slots (the same values, so the cache is unchanged), by
+    pkv_decode_write (host slots and lengths in the kernel arguments, table
+    and lengths published) and by paged_kv_write (a device slot mapping).
+    Each launch is timed alone between two HIP events queued behind a short
+    device-side sleep, so that the launch is already queued when the first
+    event completes (timed from an idle device, or back to back, the host's
+    argument marshalling would set the pace instead); the median of
+    ``iters``.  Algorithmic bytes: the new
+    K and V rows read once and written once."""
+    import torch
+    import paged_kv_cache_128_amd as pkv
+    n = k.shape[0]
+    slots, lens = eng.slots[:n].copy(), eng.lens[:n].copy()
+    d_slots = torch.from_numpy(slots).to("cuda")
+    moved = 2 * 2 * k.numel() * k.element_size()
+    res = {"rows": n, "algorithmic_bytes_per_launch": moved}
+    for name, launch in (
+            ("decode_write_kernel (pkv_decode_write)",
+             lambda: pkv.decode_write(k, v, slots, lens, eng.key_cache, eng.value_cache,
+                                      block_tables=eng.tables, lens_out=eng.d_lens)),
+            ("kv_write_kernel (paged_kv_write)",
+             lambda: pkv.paged_kv_write(k, v, d_slots, eng.key_cache, eng.value_cache))):
+        for _ in range(5):
+            launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(200_000)
+            e0.record()
+            launch()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(times))
+        res[name] = round(us, 3)
+        log(f"write: {name} {n} rows in {us:.2f} us per launch (median of {iters}, one launch per event pair)")
+    res["note"] = ("launch-bound (a few hundred KB at most); the decode step's default path writes the rows "
+                   "inside the attention launch instead")
+    return res
 
 
 def measure_swap(eng, seqs: int = 8, iters: int = 5):
@@ -627,6 +675,9 @@ def main():
     adj = sum(int(np.count_nonzero(np.diff(r[r >= 0]) == 1)) for r in tabs)
     pairs = sum(max(int((r >= 0).sum()) - 1, 0) for r in tabs)
     frag = adj / pairs if pairs else 0.0
+    # unused slots in the sequences' last blocks, and the free list, after the history prefill
+    tail_waste = int(sum(int((r >= 0).sum()) for r in tabs) * cfg.block_size - (wl.context_lens - 1).sum())
+    free_blocks = eng.manager.num_free_blocks()
     del tabs
 
     ring = [(dev(wl.new_k), dev(wl.new_v), dev(wl.q))]
@@ -674,6 +725,8 @@ def main():
     if args.warm_steps:
         log(f"warm {args.warm_steps} steps: {wm['wall_s'] * 1e6 / args.warm_steps:.1f} us/step wall, step kernel "
             f"{wm['kern_us'].mean():.1f} us, merge {wm['merge_us'].mean():.1f} us")
+    k_last, v_last, _ = ring[(total_steps - 1) % len(ring)]
+    write = measure_write(eng, k_last, v_last)
     block_copy = measure_block_copy(eng)
     swap = measure_swap(eng)
     fp8 = None
@@ -724,6 +777,8 @@ def main():
             "attention_path": path,
             "placement": cfg.placement,
             "adjacent_logical_neighbours_fraction": round(frag, 4),
+            "internal_fragmentation_tokens": tail_waste,
+            "free_blocks_after_prefill": free_blocks,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(B / (t_med * 1e-6), 1),
@@ -762,6 +817,7 @@ def main():
             "note": "launch time from events around the kernel in the flushed steps",
         },
         "kernel_source_sha256_16": kernel_source_sha(),
+        "write": write,
         "copy_on_write": block_copy,
         "swap_to_host": swap,
         "fp8_kv": fp8,
