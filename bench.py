@@ -190,6 +190,15 @@ def _cpu_pass(cfg, wl, budget_s, oracle, replay_churn, synth):
     return done_bytes, done_seqs, elapsed, (ref, mgr, kc, vc)
 
 
+def _device_sleep(cycles: int = 200_000):
+    """Keep the device busy for a moment (torch's spin kernel), so that a
+    launch queued right after an event is already waiting when the event
+    completes; without it the timing also holds the host's launch time."""
+    import torch
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(cycles)
+
+
 def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
     """Copy-on-write block copies (pkv_copy_blocks) on the workload's pool:
     ``pairs`` allocated blocks copied into free ones per launch, each launch
@@ -214,7 +223,7 @@ def measure_block_copy(eng, pairs: int = 256, iters: int = 50):
     times = []
     for _ in range(iters):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(200_000)
+        _device_sleep()
         e0.record()
         pkv.copy_blocks(src, dst, eng.key_cache, eng.value_cache)
         e1.record()
@@ -260,7 +269,7 @@ def measure_write(eng, k, v, iters: int = 50):
         times = []
         for _ in range(iters):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda._sleep(200_000)
+            _device_sleep()
             e0.record()
             launch()
             e1.record()
