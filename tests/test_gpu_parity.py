@@ -393,3 +393,54 @@ def test_debug_slot_checks_pass_on_manager_slots(dt, monkeypatch):
         with pytest.raises(pkv.InvalidArgumentError, match="slot 40 written twice"):
             pkv.paged_kv_write(kk, kk, torch.tensor([40, 41, 40], device="cuda"),
                                engs[0].key_cache, engs[0].value_cache)
+
+
+def test_layers_share_one_block_table():
+    """Per-layer pools addressed through one manager's block tables (the
+    table is shared by every layer, the K/V are per layer: [MiniPaged-Qwen]
+    §16.3): the prompt rows and one decode step of three layers, written at
+    the same slots into three pools, each pool bit for bit the oracle's
+    write of that layer's rows, and each layer's attention through the same
+    device table within 2e-3 of the oracle on that layer's cache."""
+    import paged_kv_cache_128_amd as pkv
+    _banner("three layers sharing one table")
+    rng = np.random.default_rng(71)
+    layers, N, hq, hkv, bs, D = 3, 96, 28, 4, 16, 128
+    lens = [37, 1, 160, 95, 16]
+    B = len(lens)
+    order = rng.permutation(N)
+    mgr = pkv.KVBlockManager(N, bs, order)
+    om = oracle.BlockManager(N, bs, order)
+    fill = synth.poison_array((), "bf16")
+    gpu = [pkv.new_pool(N, hkv, bs, D, torch.bfloat16, fill_bits=int(fill.view(np.uint16))) for _ in range(layers)]
+    ora = [oracle.new_pool(N, hkv, bs, D, fill) for _ in range(layers)]
+    for b, L in enumerate(lens):
+        slots = np.asarray(mgr.allocate_for_prefill(b, L), dtype=np.int64)
+        assert slots.tolist() == [int(x) for x in om.allocate_for_prefill(b, L)]
+        for (pool, kc, vc), (okc, ovc) in zip(gpu, ora):
+            k = synth.normal(rng, (L, hkv, D), "bf16")
+            v = synth.normal(rng, (L, hkv, D), "bf16")
+            pkv.paged_kv_write(to_device(k, "bf16"), to_device(v, "bf16"), torch.from_numpy(slots).cuda(), kc, vc)
+            oracle.write_kv(k, v, slots, okc, ovc, bs)
+    step = np.asarray(mgr.append_slots_for_decode(list(range(B)))[0], dtype=np.int64)
+    assert step.tolist() == [int(x) for x in om.append_slots_for_decode(list(range(B)))]
+    ctx = [L + 1 for L in lens]
+    W = -(-max(ctx) // bs)
+    tables = mgr.block_tables(list(range(B)), W)
+    assert np.array_equal(tables, np.array([om.block_table(b) + [-1] * (W - len(om.block_table(b)))
+                                            for b in range(B)], dtype=np.int32))
+    d_tab = torch.from_numpy(tables).cuda()
+    d_lens = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
+    for (pool, kc, vc), (okc, ovc) in zip(gpu, ora):
+        k = synth.normal(rng, (B, hkv, D), "bf16")
+        v = synth.normal(rng, (B, hkv, D), "bf16")
+        q = synth.normal(rng, (B, hq, D), "bf16")
+        pkv.paged_kv_write(to_device(k, "bf16"), to_device(v, "bf16"), torch.from_numpy(step).cuda(), kc, vc)
+        oracle.write_kv(k, v, step, okc, ovc, bs)
+        out = pkv.paged_decode_attention(to_device(q, "bf16"), kc, vc, d_tab, d_lens, scale,
+                                         max_context_len=max(ctx)).double().cpu().numpy()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_u(kc), okc.view(np.uint16)) and np.array_equal(bits_u(vc), ovc.view(np.uint16))
+        ref = oracle.decode_attention(q, okc, ovc, tables, ctx, scale, "bf16")
+        assert np.abs(out - ref).max() <= 2e-3
