@@ -588,12 +588,15 @@ def _timed_steps(eng, ring, ids, out, cfg, s0, n, fused, flush, event_every=5):
     (around the whole step) and odd steps three (before the first launch,
     between the two launches, after the second).  Without, the steps run
     back to back and every ``event_every``-th carries three events.  Returns
-    the wall time and the event times in microseconds."""
+    the wall time and the event times in microseconds; ``two_idx`` names the
+    steps whose whole span was timed (the two-event steps, or with none the
+    three-event ones)."""
     import torch
     evs = {}
     for i in range(n):
         if flush is not None:
-            evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2 if i % 2 == 0 else 3)]
+            # a single step carries three events (its whole span is then e0 -> e2)
+            evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(2 if i % 2 == 0 and n > 1 else 3)]
         elif i % max(1, event_every) == 0:
             evs[i] = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -609,8 +612,10 @@ def _timed_steps(eng, ring, ids, out, cfg, s0, n, fused, flush, event_every=5):
     wall = time.perf_counter() - t0
     two = sorted(i for i in evs if len(evs[i]) == 2)
     three = sorted(i for i in evs if len(evs[i]) == 3)
-    return {"wall_s": wall, "two_idx": two, "three_idx": three,
-            "step_us": np.array([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in two]),
+    whole = [(i, evs[i][0].elapsed_time(evs[i][1])) for i in two] or \
+            [(i, evs[i][0].elapsed_time(evs[i][2])) for i in three]
+    return {"wall_s": wall, "two_idx": [i for i, _ in whole], "three_idx": three,
+            "step_us": np.array([ms * 1e3 for _, ms in whole]),
             "kern_us": np.array([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in three]),
             "merge_us": np.array([evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in three])}
 
