@@ -207,6 +207,29 @@ def test_empty_context_and_half_outputs():
     assert np.all(np.abs(h[1:] - ref[1:]) <= 2e-3 + np.abs(ref[1:]) * 2.0 ** -11)
 
 
+@pytest.mark.parametrize("dtype,h_q,h_kv,d", [("bf16", 28, 4, 128), ("f32", 4, 4, 64)])
+def test_every_context_empty(dtype, h_q, h_kv, d):
+    """A batch in which no sequence holds a token: no tile for the stream
+    path to cut into ranges, no partition for the partition path; every
+    output row is exactly zero (reading: L = 0 gives zeros), on both paths
+    and whatever the stated max_context_len."""
+    import paged_kv_cache_128_amd as pkv
+    case = _small_case(dtype, h_q, h_kv, d, 16, [0, 0, 0, 0, 0], 16, seed=12)
+    for part in (0, 16):
+        got = _gpu_attend(case, partition_tokens=part).cpu().numpy()
+        assert np.all(got == 0), part
+    # lengths all zero with a nonzero max_context_len (tables unused)
+    N, hk, bs, dd = case["kc"].shape
+    pool, kc, vc = pkv.new_pool(N, hk, bs, dd, TORCH_DTYPE[dtype])
+    t = torch.from_numpy(case["tables"]).cuda()
+    lens = torch.zeros(5, dtype=torch.int32, device="cuda")
+    for part in (0, 16):
+        out = pkv.paged_decode_attention(to_device(case["q"], dtype), kc, vc, t, lens, case["scale"],
+                                         partition_tokens=part, max_context_len=16)
+        torch.cuda.synchronize()
+        assert bool((out == 0).all()), part
+
+
 def test_write_skips_out_of_range_slots():
     import paged_kv_cache_128_amd as pkv
     pool, kc, vc = pkv.new_pool(4, 2, 16, 64, torch.bfloat16, fill_bits=0x7FC5)
