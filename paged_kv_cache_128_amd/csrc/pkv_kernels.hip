@@ -577,14 +577,16 @@ __device__ __forceinline__ void wave_epilogue(float m, float l, float (&acc)[GP]
 // tokens 4 g4 ..) is the score layout as it comes out of the Q.K MFMA.
 // Lane (g4, c16) ends up with head c16's head-dims 32 g4 .. 32 g4 + 31:
 // c[j][i] is head-dim 32 g4 + 8 i + j.  The V codes enter the MFMA as exact
-// f16 values and P as f16 (round to nearest) scaled by 2^(ev(t) - eref),
-// where eref, the largest V scale exponent seen in the segment, keeps the
-// products in f16 range; c holds the accumulator times 2^-eref.
+// f16 values.  The weight of token t is its probability times its V row's
+// scale, 2^(x(t) + ev(t)), taken relative to r, a running maximum of
+// x + ev for the lane's head (log2 units): c holds the head's accumulator
+// times 2^-r.  The largest weight of a segment thus enters near 1 however
+// far apart the row scales are.  The 16-bit path keeps c relative to the
+// softmax maximum m and does not use r.
 struct Acc8 {
   f32x4 c[8];
-  int eref;
+  float r;
 };
-constexpr int kNoRef = -100000;
 
 template <int GP>
 struct AccV {
@@ -601,7 +603,7 @@ __device__ __forceinline__ void acc_zero(AccV<GP>& x) {
 __device__ __forceinline__ void acc_zero(Acc8& x) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) x.c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  x.eref = kNoRef;
+  x.r = -INFINITY;
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -645,8 +647,8 @@ __device__ __forceinline__ uint32_t pack16x2(float x0, float x1) {
 // 4 g4 .. 4 g4 + 3 (head-dims 8 c16 .. + 7, as loaded), and its B operand is
 // the score layout (head c16, tokens 4 g4 ..) as it leaves Q.K.  P enters as
 // a 16-bit value plus its 16-bit remainder (two MFMAs, P to about 2^-17).
-// The accumulator is the 8-bit path's (eref 0): lane (g4, c16) ends with
-// head c16's head-dims 32 g4 .. 32 g4 + 31.
+// The accumulator is the 8-bit path's, relative to m (r unused): lane
+// (g4, c16) ends with head c16's head-dims 32 g4 .. 32 g4 + 31.
 template <int DT>
 __device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128>& t, int nvalid,
                                               float scale_log2, float& m, float& l, Acc8& acc, int lane) {
@@ -697,6 +699,9 @@ __device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128
 // head-dims 32 g4 .. + 31; the four token groups' sums l are added, and each
 // lane of a real head (c16 < G) writes its 32 values (normalised output, or
 // the partial with its (m, l) in workspace slot ws_row0 + c16 * ws_row_stride).
+// REF: the accumulator is relative to 2^r (8-bit rows) and is brought to m
+// first, as c * 2^(r - m) = ldexp(c * 2^f, n) with r - m = n + f.
+template <bool REF>
 __device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc, int lane, int G,
                                                bool final, void* out, int out_dtype,
                                                int64_t out_row0, float* ws_acc, float* ws_ml,
@@ -707,10 +712,21 @@ __device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc
   l += __shfl_xor(l, 32);
   if (c16 >= G) return;
   float v[32];
+  if constexpr (REF) {
+    const float d = acc.r - m;
+    const float n = __builtin_rintf(d);
+    const float f = __builtin_amdgcn_exp2f(d - n);
+    const int ni = static_cast<int>(n);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i], acc.eref);
+      for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i] * f, ni);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[8 * i + j] = acc.c[j][i];
+  }
   if (final) {
     const float inv = l > 0.f ? 1.0f / l : 0.f;
     const int64_t o = (out_row0 + c16) * D + 32 * g4;
@@ -845,7 +861,6 @@ attn_split_kernel(AttnArgs a) {
   constexpr bool MPV = F::kRowK && kMfmaPV16 && D == 128 && DT != PKV_F32;
   Acc8 accm;
   acc_zero(accm);
-  accm.eref = 0;
   auto step = [&](const f32x4& sc, const VTile<DT, D>& v, int nvalid) {
     if constexpr (MPV) softmax_pv16m<DT>(sc, v, nvalid, a.scale_log2, m, l, accm, lane);
     else softmax_pv<DT, D, GP>(sc, v, nvalid, a.scale_log2, m, l, acc, lane);
@@ -919,7 +934,7 @@ attn_split_kernel(AttnArgs a) {
   }
 
   if constexpr (MPV)
-    wave_epilogue8(m, l, accm, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc, a.ws_ml,
+    wave_epilogue8<false>(m, l, accm, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc, a.ws_ml,
                    out_row0 * a.max_parts + p, a.max_parts);
   else
     wave_epilogue<DT, D, GP>(m, l, acc, lane, G, nparts == 1, a.out, a.out_dtype, out_row0, a.ws_acc,
@@ -1292,53 +1307,52 @@ __device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
 }
 
 // Online softmax + P.V for one 8-bit tile: the score of token t is the code
-// dot product times 2^ek(t) (into the exp2 argument's factor), the V row of
-// t its codes times 2^ev(t) (into the probability the MFMA takes; the sum l
-// keeps the unscaled probability).
+// dot product times 2^ek(t) (into the exp2 argument's factor), x(t) in log2
+// units.  The sum l keeps the probability p(t) = 2^(x(t) - m); the MFMA
+// takes the codes of V row t with the weight 2^(x(t) + ev(t) - r) (the
+// accumulator's reference r, a running maximum of x + ev with the same slack
+// as m), as an f16 value plus its f16 remainder (two MFMAs, the weight to
+// about 2^-22 of the segment's largest).
 __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int nvalid,
                                             float scale_log2, float& m, float& l, Acc8& acc,
                                             int lane) {
   const int g4 = lane >> 4;
-  float x[4];
-  int ev[4];
-  int evm = kNoRef;
+  float x[4], y[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool valid = 4 * g4 + r < nvalid;
     const int ek = static_cast<int>((t.ks >> (8 * r)) & 0xffu) - 127;
-    ev[r] = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
+    const int ev = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
     x[r] = valid ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
-    if (valid) evm = max(evm, ev[r]);
+    y[r] = x[r] + static_cast<float>(ev);
   }
   const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  evm = uni(max_over_g4(evm));                     // the same in every lane
-  const bool grow = bm > m + kSlack;
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+  const float by = max_over_g4(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
+  if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
     const float m_new = fmaxf(m, bm);
-    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head
-    l *= a;
+    l *= __builtin_amdgcn_exp2f(m - m_new);              // this lane's head; 0 on the first tile
     m = m_new;
+  }
+  if (__builtin_amdgcn_ballot_w64(by > acc.r + kSlack) != 0) {
+    const float r_new = fmaxf(acc.r, by);
+    const float a = __builtin_amdgcn_exp2f(acc.r - r_new);
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc.c[j] *= a;
+    acc.r = r_new;
   }
-  if (evm > acc.eref) {
-    if (acc.eref != kNoRef) {
-      const int sh = acc.eref - evm;
+  float p[4], w[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc.c[j][i] = __builtin_amdgcn_ldexpf(acc.c[j][i], sh);
-    }
-    acc.eref = evm;
+  for (int r = 0; r < 4; ++r) {
+    p[r] = __builtin_amdgcn_exp2f(x[r] - m);              // masked tokens: 0
+    w[r] = __builtin_amdgcn_exp2f(y[r] - acc.r);
   }
-  float p[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m);
   l += (p[0] + p[1]) + (p[2] + p[3]);
-  const f16x4 b = {static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[0], ev[0] - acc.eref)),
-                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[1], ev[1] - acc.eref)),
-                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[2], ev[2] - acc.eref)),
-                   static_cast<_Float16>(__builtin_amdgcn_ldexpf(p[3], ev[3] - acc.eref))};
+  const uint32_t h01 = pack16x2<PKV_F16>(w[0], w[1]), h23 = pack16x2<PKV_F16>(w[2], w[3]);
+  float q0, q1, q2, q3;
+  unpack2<PKV_F16>(h01, q0, q1);
+  unpack2<PKV_F16>(h23, q2, q3);
+  const u32x2 bh = {h01, h23};
+  const u32x2 bl = {pack16x2<PKV_F16>(w[0] - q0, w[1] - q1), pack16x2<PKV_F16>(w[2] - q2, w[3] - q3)};
   // 4x4 byte transposes: X[4 q + k] = byte k of t.w[0..3][q] (rows 0..3)
   uint32_t X[8];
 #pragma unroll
@@ -1355,7 +1369,10 @@ __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int 
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const u32x2 av = {fp8x2_to_16<PKV_F16, false>(X[j]), fp8x2_to_16<PKV_F16, true>(X[j])};
-    acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av), b, acc.c[j], 0, 0, 0);
+    acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                     __builtin_bit_cast(f16x4, bh), acc.c[j], 0, 0, 0);
+    acc.c[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, av),
+                                                     __builtin_bit_cast(f16x4, bl), acc.c[j], 0, 0, 0);
   }
 }
 
@@ -1643,10 +1660,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
       float m = -INFINITY, l = 0.f;
       constexpr bool MPV = !KV8 && kMfmaPV16;
       std::conditional_t<KV8 || MPV, Acc8, AccV<GP>> acc;
-      auto acc_init = [&]() {
-        acc_zero(acc);
-        if constexpr (MPV) acc.eref = 0;             // 16-bit P.V: no V scale
-      };
+      auto acc_init = [&]() { acc_zero(acc); };
       acc_init();
       // Per chunk: wait for its DMA (and its query group); scores from the K
       // rows in LDS; then the next chunk's fetch (V into `vnext`) and, when
@@ -1696,7 +1710,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
           const int64_t orow = static_cast<int64_t>(bc) * a.hq + static_cast<int64_t>(kvh) * G;
           const int64_t wrow = (rng * kStreamSlots + slot) * a.hq + static_cast<int64_t>(kvh) * G;
           if constexpr (KV8 || MPV)
-            wave_epilogue8(m, l, acc, lane, G, complete, a.out, a.out_dtype, orow, a.ws_acc, a.ws_ml, wrow);
+            wave_epilogue8<KV8>(m, l, acc, lane, G, complete, a.out, a.out_dtype, orow, a.ws_acc, a.ws_ml, wrow);
           else
             wave_epilogue<DT, D, GP>(m, l, acc.a, lane, G, complete, a.out, a.out_dtype, orow,
                                      a.ws_acc, a.ws_ml, wrow, 1);

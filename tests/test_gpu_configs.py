@@ -17,6 +17,13 @@ from gpu_harness import TORCH_DTYPE, bits_u, engine_for, replay_churn_device, ru
 
 pytestmark = pytest.mark.gpu
 
+# The bound the path is held to is 2e-3 (16- and 8-bit KV, fp32 outputs).
+# The kernels carry the softmax weights to about 2^-17 (a 16-bit value plus
+# its 16-bit remainder) and accumulate in fp32, and land near 1e-6 on these
+# workloads; PRECISION asserts 1e-4 as well, so that a change which loses
+# precision shows here long before it reaches the bound.
+PRECISION = 1e-4
+
 
 def _banner(msg):
     print(f"[gpu] {msg}", flush=True)
@@ -52,6 +59,7 @@ def test_full_size_decode_step(name, partition):
     _banner(f"config {cfg.index} {name} partition={partition}: all {len(per_row)} rows, "
             f"max abs err {per_row.max():.3e} (row {int(per_row.argmax())})")
     assert per_row.max() <= 2e-3, np.flatnonzero(per_row > 2e-3)
+    assert per_row.max() <= PRECISION, per_row.max()
 
 
 def test_serving_trace_200_steps():
@@ -95,6 +103,7 @@ def test_serving_trace_200_steps():
             row_ids[r.row] = r.new_id
     torch.cuda.synchronize()
     assert checked >= 9
+    assert worst <= PRECISION, worst
     assert eng.manager.free_list() == mgr.free
     _check_pool(eng, kc, vc)
     _banner(f"serving trace ok: {checked} steps of {B} rows, max abs err {worst:.3e}")
@@ -152,6 +161,7 @@ def test_full_size_fp8_decode_step():
         worst = max(worst, err)
         assert err <= 2e-3, (b, err)
     _banner(f"fp8 batch-64: all {B} rows, max abs err {worst:.3e}")
+    assert worst <= PRECISION, worst
 
 
 def test_full_size_prefill():
@@ -196,3 +206,4 @@ def test_full_size_prefill():
         _banner(f"prefill 8 x 2048: prompt {b}, all {prompt} rows, max abs err {err:.3e}")
         assert err <= 2e-3, (b, err)
     _banner(f"prefill 8 x 2048: all {seqs * prompt} rows, max abs err {worst:.3e}")
+    assert worst <= PRECISION, worst

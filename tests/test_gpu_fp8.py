@@ -515,3 +515,69 @@ def test_fused_fp8_step_codes_non_finite_new_rows_like_the_oracle(q_dtype):
         for got, want in ((ks, oks), (vs, ovs)):
             assert np.array_equal(_u8(got[pb, :, off]), want[pb, :, off]), b
     assert _u8(kc[int(slots[0]) // bs, 0, int(slots[0]) % bs])[[1, 4, 9]].tolist() == [0x7F, 0xFF, 0x7F]
+
+
+def _spread_case(pattern, q_dtype, seed):
+    """Sequences whose V rows sit at very different scales.  "outliers":
+    every 37th token (token 0 included) has its V row times 2^24 and a key
+    of -4 times the sum of its group's queries, so its weight is about
+    e^-40 and the output is of order 1 (a reference exponent taken from
+    the largest row scale alone would push every other weight below f16's
+    range); "per-sequence": sequence b's rows all times 2^e_b, e_b from
+    -40 to 40; "mixed": every row times 2^k, k uniform in [-12, 12].
+    Returns what the test needs and each sequence's tolerance."""
+    rng = np.random.default_rng(seed)
+    hq, hkv, bs, D = 28, 4, 16, 128
+    G = hq // hkv
+    lens = np.array([1, 5, 300, 2000, 4096, 17], np.int64)
+    B = len(lens)
+    q = synth.normal(rng, (B, hq, D), q_dtype)
+    qf = oracle.widen(q, q_dtype).astype(np.float32)
+    exps = np.array([-40, -20, 0, 20, 40, -8])
+    N = int(np.ceil(lens / bs).sum()) + 8
+    m = oracle.BlockManager(N, bs, rng.permutation(N))
+    okc, ovc, oks, ovs = quant.new_fp8_pool(N, hkv, bs, D)
+    codes, kc, vc, scales, ks, vs = pkv.new_fp8_pool(N, hkv, bs, D, "cuda", poison=True)
+    tol = np.full(B, 2e-3)
+    for b, L in enumerate(lens):
+        k = rng.standard_normal((L, hkv, D)).astype(np.float32)
+        v = rng.standard_normal((L, hkv, D)).astype(np.float32)
+        if pattern == "outliers":
+            out_rows = np.arange(0, L, 37)
+            v[out_rows] *= np.float32(2.0 ** 24)
+            k[out_rows] = -4.0 * qf[b].reshape(hkv, G, D).sum(axis=1)
+        elif pattern == "per-sequence":
+            v *= np.float32(2.0 ** exps[b])
+            tol[b] = 2e-3 * 2.0 ** exps[b]
+        else:
+            v *= (2.0 ** rng.integers(-12, 13, (L, 1, 1))).astype(np.float32)
+            tol[b] = 2e-3 + 2.0 ** -18 * np.abs(v).max()
+        slots = np.array(m.allocate_for_prefill(b, int(L)), np.int64)
+        quant.write_kv_fp8(k, v, slots, okc, ovc, oks, ovs, bs)
+        pkv.paged_kv_write_fp8(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(),
+                               torch.from_numpy(slots).cuda(), kc, vc, ks, vs)
+    tabs = m.block_tables(list(range(B)), int(np.ceil(lens.max() / bs)), -1)
+    return lens, tabs, q, (okc, ovc, oks, ovs), (kc, vc, ks, vs), tol
+
+
+@pytest.mark.parametrize("pattern,q_dtype", [("outliers", "bf16"), ("outliers", "f16"),
+                                             ("per-sequence", "bf16"), ("mixed", "bf16")])
+def test_fp8_attention_far_apart_row_scales(pattern, q_dtype):
+    """8-bit attention over rows whose V scales lie far apart, against the
+    float64 oracle on the read-back values: a row with a huge scale and a
+    negligible weight leaves the others' weights intact; sequences scaled
+    as a whole by 2^-40 .. 2^40 keep the 2e-3 bound scaled with them; rows
+    scaled by 2^-12 .. 2^12 stay within 2e-3 + 2^-18 of their largest
+    value.  Long sequences span several ranges, so the merge is in the
+    path."""
+    _banner(f"fp8 attention, row scales far apart: {pattern}, q={q_dtype}")
+    lens, tabs, q, o, g, tol = _spread_case(pattern, q_dtype, 4321)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    ref = quant.decode_attention_fp8(q, q_dtype, *o, tabs, lens, scale)
+    out = pkv.paged_decode_attention_fp8(to_device(q, q_dtype), *g, torch.from_numpy(tabs).cuda(),
+                                         torch.from_numpy(lens.astype(np.int32)).cuda(), scale,
+                                         max_context_len=int(lens.max())).double().cpu().numpy()
+    assert np.all(np.isfinite(out))
+    err = np.abs(out - ref).max(axis=(1, 2))
+    _banner("per sequence: " + ", ".join(f"L={L} err {e:.2e} (tol {t:.1e})" for L, e, t in zip(lens, err, tol)))
+    assert np.all(err <= tol), err / tol
