@@ -161,11 +161,24 @@ __device__ __forceinline__ f32x4 mfma_k32(const u32x4& a, const u32x4& b, f32x4 
 // Max and sum over the lanes c16, c16 + 16, c16 + 32, c16 + 48 (every lane
 // gets the result), on the vector ALU: the 16-lane row swap pairs rows
 // (0, 1) and (2, 3), the 32-lane half swap pairs the halves.
+// The score maxima use v_max3_f32 / v_max_f32 written out: fmaxf quiets
+// signalling NaNs first (the kernel runs in IEEE mode), one v_max of each
+// operand with itself, and the scores are MFMA results or -inf.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_over_g4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = vmax2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum_over_g4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -349,7 +362,7 @@ prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 4; ++i)
               x[4 * h + i] = key0 + 16 * h + 4 * g4 + i <= pos[c] ? sa[h][c][i] : -INFINITY;
         }
-        float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        float bm = vmax2(vmax3(x[0], x[1], x[2]), vmax3(x[3], x[4], vmax3(x[5], x[6], x[7])));
         bm = max_over_g4(bm) * a.scale_log2;
         if (__builtin_amdgcn_ballot_w64(bm > m[c] + kSlack) != 0) {
           const float m_new = fmaxf(m[c], bm);
