@@ -577,16 +577,19 @@ __device__ __forceinline__ void wave_epilogue(float m, float l, float (&acc)[GP]
 // tokens 4 g4 ..) is the score layout as it comes out of the Q.K MFMA.
 // Lane (g4, c16) ends up with head c16's head-dims 32 g4 .. 32 g4 + 31:
 // c[j][i] is head-dim 32 g4 + 8 i + j.  The V codes enter the MFMA as exact
-// f16 values.  The weight of token t is its probability times its V row's
-// scale, 2^(x(t) + ev(t)), taken relative to r, a running maximum of
-// x + ev for the lane's head (log2 units): c holds the head's accumulator
-// times 2^-r.  The largest weight of a segment thus enters near 1 however
-// far apart the row scales are.  The 16-bit path keeps c relative to the
-// softmax maximum m and does not use r.
+// f16 values.  The weight of token t is its probability p(t) = 2^(x(t) - m)
+// (the one the sum l takes) times its V row's scale 2^ev(t), taken relative
+// to 2^e, an integer exponent kept per head near the largest exponent of
+// those products: c holds the head's accumulator times 2^-e.  The largest
+// weight of a segment thus enters near 1 however far apart the row scales
+// are, and every change of e is an exact power-of-two rescale.  The 16-bit
+// path keeps c relative to m and does not use e.
 struct Acc8 {
   f32x4 c[8];
-  float r;
+  int e;
 };
+constexpr int kNoRef = -100000;
+constexpr int kSlackE = 8;           // allowed growth of the weights' exponent before a rescale
 
 template <int GP>
 struct AccV {
@@ -603,7 +606,7 @@ __device__ __forceinline__ void acc_zero(AccV<GP>& x) {
 __device__ __forceinline__ void acc_zero(Acc8& x) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) x.c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  x.r = -INFINITY;
+  x.e = kNoRef;
 }
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
@@ -647,7 +650,7 @@ __device__ __forceinline__ uint32_t pack16x2(float x0, float x1) {
 // 4 g4 .. 4 g4 + 3 (head-dims 8 c16 .. + 7, as loaded), and its B operand is
 // the score layout (head c16, tokens 4 g4 ..) as it leaves Q.K.  P enters as
 // a 16-bit value plus its 16-bit remainder (two MFMAs, P to about 2^-17).
-// The accumulator is the 8-bit path's, relative to m (r unused): lane
+// The accumulator is the 8-bit path's, relative to m (e unused): lane
 // (g4, c16) ends with head c16's head-dims 32 g4 .. 32 g4 + 31.
 template <int DT>
 __device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128>& t, int nvalid,
@@ -699,8 +702,7 @@ __device__ __forceinline__ void softmax_pv16m(const f32x4 s, const VTile<DT, 128
 // head-dims 32 g4 .. + 31; the four token groups' sums l are added, and each
 // lane of a real head (c16 < G) writes its 32 values (normalised output, or
 // the partial with its (m, l) in workspace slot ws_row0 + c16 * ws_row_stride).
-// REF: the accumulator is relative to 2^r (8-bit rows) and is brought to m
-// first, as c * 2^(r - m) = ldexp(c * 2^f, n) with r - m = n + f.
+// REF: the accumulator holds the partial times 2^-e (8-bit rows).
 template <bool REF>
 __device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc, int lane, int G,
                                                bool final, void* out, int out_dtype,
@@ -713,14 +715,10 @@ __device__ __forceinline__ void wave_epilogue8(float m, float l, const Acc8& acc
   if (c16 >= G) return;
   float v[32];
   if constexpr (REF) {
-    const float d = acc.r - m;
-    const float n = __builtin_rintf(d);
-    const float f = __builtin_amdgcn_exp2f(d - n);
-    const int ni = static_cast<int>(n);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i] * f, ni);
+      for (int j = 0; j < 8; ++j) v[8 * i + j] = __builtin_amdgcn_ldexpf(acc.c[j][i], acc.e);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1308,45 +1306,62 @@ __device__ __forceinline__ Dw<16> read_k_rows8(const uint4* sk, int lane) {
 
 // Online softmax + P.V for one 8-bit tile: the score of token t is the code
 // dot product times 2^ek(t) (into the exp2 argument's factor), x(t) in log2
-// units.  The sum l keeps the probability p(t) = 2^(x(t) - m); the MFMA
-// takes the codes of V row t with the weight 2^(x(t) + ev(t) - r) (the
-// accumulator's reference r, a running maximum of x + ev with the same slack
-// as m), as an f16 value plus its f16 remainder (two MFMAs, the weight to
-// about 2^-22 of the segment's largest).
+// units.  The sum l and the MFMA take the same p(t) = 2^(x(t) - m); the
+// MFMA takes it times 2^(ev(t) - e) for V row t's codes, as an f16 value
+// plus its f16 remainder (two MFMAs, the weight to about 2^-22 of the
+// segment's largest).  e follows the largest ev(t) + floor(log2 p(t)) (the
+// exponent field of p) with the slack kSlackE, and drops by the whole
+// powers of two by which a new maximum m shrinks the products, so later
+// weights keep their precision.
 __device__ __forceinline__ void softmax_pv8(const f32x4 s, const VTile8& t, int nvalid,
                                             float scale_log2, float& m, float& l, Acc8& acc,
                                             int lane) {
   const int g4 = lane >> 4;
-  float x[4], y[4];
+  float x[4];
+  int ev[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const bool valid = 4 * g4 + r < nvalid;
     const int ek = static_cast<int>((t.ks >> (8 * r)) & 0xffu) - 127;
-    const int ev = static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127;
+    // rows past nvalid: p = 0, and the smallest exponent, so they never set e
+    ev[r] = valid ? static_cast<int>((t.vs >> (8 * r)) & 0xffu) - 127 : -127;
     x[r] = valid ? s[r] * __builtin_amdgcn_ldexpf(scale_log2, ek) : -INFINITY;
-    y[r] = x[r] + static_cast<float>(ev);
   }
   const float bm = max_over_g4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-  const float by = max_over_g4(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])));
   if (__builtin_amdgcn_ballot_w64(bm > m + kSlack) != 0) {
     const float m_new = fmaxf(m, bm);
-    l *= __builtin_amdgcn_exp2f(m - m_new);              // this lane's head; 0 on the first tile
+    const float a = __builtin_amdgcn_exp2f(m - m_new);   // this lane's head; 0 on the first tile
+    // whole powers of two of the shrink, at most 512 (a is 0 beyond that)
+    const int dn = m == -INFINITY ? 0 : static_cast<int>(__builtin_floorf(fminf(m_new - m, 512.f)));
+    const float ac = __builtin_amdgcn_ldexpf(a, dn);      // in (1/2, 1], or 0
+    l *= a;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc.c[j] *= ac;
+    acc.e -= dn;
     m = m_new;
   }
-  if (__builtin_amdgcn_ballot_w64(by > acc.r + kSlack) != 0) {
-    const float r_new = fmaxf(acc.r, by);
-    const float a = __builtin_amdgcn_exp2f(acc.r - r_new);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc.c[j] *= a;
-    acc.r = r_new;
-  }
-  float p[4], w[4];
+  float p[4];
+  int et = kNoRef;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     p[r] = __builtin_amdgcn_exp2f(x[r] - m);              // masked tokens: 0
-    w[r] = __builtin_amdgcn_exp2f(y[r] - acc.r);
+    const int pe = static_cast<int>(__float_as_uint(p[r]) >> 23) - 127;   // p >= 0
+    et = max(et, ev[r] + pe);
+  }
+  et = max_over_g4(et);
+  if (__builtin_amdgcn_ballot_w64(et > acc.e + kSlackE) != 0) {
+    const int e_new = max(acc.e, et);
+    const int sh = acc.e - e_new;                           // the accumulator is 0 while e is kNoRef
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc.c[j][i] = __builtin_amdgcn_ldexpf(acc.c[j][i], sh);
+    acc.e = e_new;
   }
   l += (p[0] + p[1]) + (p[2] + p[3]);
+  float w[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) w[r] = __builtin_amdgcn_ldexpf(p[r], ev[r] - acc.e);
   const uint32_t h01 = pack16x2<PKV_F16>(w[0], w[1]), h23 = pack16x2<PKV_F16>(w[2], w[3]);
   float q0, q1, q2, q3;
   unpack2<PKV_F16>(h01, q0, q1);

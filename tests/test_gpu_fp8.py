@@ -233,14 +233,20 @@ def test_fp8_engine_decode_steps_match_oracle():
         assert err <= 2e-3, (step, err)
 
 
-@pytest.mark.parametrize("hq,hkv,B", [(28, 4, 24), (32, 8, 9), (12, 2, 40)])
-def test_fp8_fused_step_equals_separate_launches_and_oracle(hq, hkv, B):
+@pytest.mark.parametrize("hq,hkv,B,outliers", [(28, 4, 24, False), (32, 8, 9, False), (12, 2, 40, False),
+                                               (28, 4, 24, True)])
+def test_fp8_fused_step_equals_separate_launches_and_oracle(hq, hkv, B, outliers):
     """pkv_decode_step_fp8 (the quantising write inside the 8-bit attention
     launch) gives bit for bit the pool, scales, tables, lengths and outputs
     of pkv_decode_write_fp8 followed by the 8-bit attention, over three
-    steps that open blocks, and stays within 2e-3 of the oracle."""
+    steps that open blocks, and stays within 2e-3 of the oracle.  With
+    `outliers`, the last step's new row of every third sequence has its V
+    times 2^24 and a key of -4 times the sum of its group's queries (a
+    weight of about e^-40 for that step's queries): the row the fused
+    launch quantises and places itself then carries the largest V scale of
+    its segment."""
     from paged_kv_cache_128_amd.engine import PagedKVEngine
-    print(f"[gpu] fp8 fused step hq={hq} hkv={hkv} B={B}", flush=True)
+    print(f"[gpu] fp8 fused step hq={hq} hkv={hkv} B={B} outliers={outliers}", flush=True)
     rng = np.random.default_rng(40 + B)
     bs, D = 16, 128
     lens = rng.integers(1, 300, size=B)
@@ -268,6 +274,10 @@ def test_fp8_fused_step_equals_separate_launches_and_oracle(hq, hkv, B):
         nk = synth.normal(rng, (B, hkv, D), "bf16")
         nv = synth.normal(rng, (B, hkv, D), "bf16")
         q = synth.normal(rng, (B, hq, D), "bf16")
+        if outliers and step == 2:
+            qg = _f32(q, "bf16").reshape(B, hkv, hq // hkv, D).sum(axis=2)
+            nk[::3] = synth.to_storage(-4.0 * qg[::3], "bf16")
+            nv[::3] = synth.to_storage(_f32(nv[::3], "bf16") * np.float32(2.0 ** 24), "bf16")
         slots = om.append_slots_for_decode(list(range(B)))
         quant.write_kv_fp8(_f32(nk, "bf16"), _f32(nv, "bf16"), slots, okc, ovc, oks, ovs, bs)
         ref = quant.decode_attention_fp8(q, "bf16", okc, ovc, oks, ovs, om.block_tables(list(range(B)), width, -1),
