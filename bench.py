@@ -429,7 +429,10 @@ def measure_serving(cfg, args):
     the merge) and the refills after it (releases, then the step's admissions
     as one prefill_many: allocation, one prompt write, one table update).
     Prints one JSON line: K/V GB/s and decode tokens/s over the decode-step
-    time, and the refill time separately."""
+    time, and the refill time separately.  Unless --no-cpu-baseline, the
+    output of every tenth step and the last is copied aside after that
+    step's refills (outside both event pairs, inside the wall clock), and
+    the oracle replays the trace afterwards (serving_cpu_baseline)."""
     import torch
     import synth
     from paged_kv_cache_128_amd.engine import PagedKVEngine
@@ -445,7 +448,9 @@ def measure_serving(cfg, args):
     tr = synth.serving_trace(cfg)
     B, H, D = cfg.batch, cfg.num_kv_heads, cfg.head_dim
     width = -(-(cfg.clip[1] + cfg.steps) // cfg.block_size)
-    eng = PagedKVEngine(cfg.num_blocks, H, cfg.block_size, D, tdtype, B, width, None, num_q_heads=cfg.num_q_heads)
+    # the pool starts as the oracle's does (every element the poison value), so the two compare whole
+    eng = PagedKVEngine(cfg.num_blocks, H, cfg.block_size, D, tdtype, B, width, None, num_q_heads=cfg.num_q_heads,
+                        fill_bits=synth.POISON_BITS[cfg.dtype])
     eng.prefill_many(list(range(B)), list(range(B)), [int(x) for x in tr.prompt_lens],
                      dev(np.concatenate(tr.hist_k)), dev(np.concatenate(tr.hist_v)))
     # each step's refills as one admission: their prompts concatenated
@@ -460,13 +465,16 @@ def measure_serving(cfg, args):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in steps]
     kv_bytes = 0
     n_refill = refill_tokens = 0
+    sampled = set(range(0, len(steps), 10)) | {len(steps) - 1}     # steps the oracle compares
+    step_slots, kept = [], {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for (k, v, q, refills), ev in zip(steps, evs):
+    for i, ((k, v, q, refills), ev) in enumerate(zip(steps, evs)):
         ev[0].record()
         eng.decode_step(row_ids, k, v, q, cfg.scale, out=out)
         kv_bytes += int(eng.lens[:B].astype(np.int64).sum()) * H * 2 * D * elem
         ev[1].record()
+        step_slots.append(eng.slots[:B].copy())
         rows, new_ids, plens, rk, rv = refills
         if rows:
             for row, new_id in zip(rows, new_ids):
@@ -476,6 +484,8 @@ def measure_serving(cfg, args):
             n_refill += len(rows)
             refill_tokens += int(sum(plens))
         ev[2].record()
+        if i in sampled and not args.no_cpu_baseline:
+            kept[i] = out.clone()          # outside both event pairs; the refills do not touch out
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_s = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
@@ -498,7 +508,65 @@ def measure_serving(cfg, args):
         "wall_tokens_per_s": round(tokens / wall, 1),
         "refills": n_refill, "refill_prompt_tokens": refill_tokens, "refill_ms": round(ref_s * 1e3, 3),
         "kernel_source_sha256_16": kernel_source_sha(),
+        "cpu_baseline": None if args.no_cpu_baseline else serving_cpu_baseline(cfg, eng, step_slots, kept, width),
     }), flush=True)
+
+
+def serving_cpu_baseline(cfg, eng, step_slots, kept, width):
+    """The CPU oracle on the serving trace, untuned, with the process's whole
+    affinity set: the trace regenerated from its seed and replayed on the
+    oracle (oracle.replay.serving_replay: the manager's appends, writes and
+    refills on every step), with the float64 attention on the steps the GPU
+    run kept (every tenth and the last).  Reported as KV GB/s and decode
+    tokens/s over those attentions (the replay's own time beside them).
+    Compared with the GPU run: the slots of every step, the attention of
+    every row at the sampled steps, and at the end the free list and the
+    whole pool bit for bit."""
+    import torch
+    import oracle
+    import synth
+    from oracle.replay import serving_replay
+    info = _cpu_info()
+    tr = synth.serving_trace(cfg)
+    B, H, D, elem = cfg.batch, cfg.num_kv_heads, cfg.head_dim, synth.ELEM_BYTES[cfg.dtype]
+    t0 = time.perf_counter()
+    t_attn = 0.0
+    kv = 0
+    err = 0.0
+    slots_equal = True
+    mgr = kc = vc = None
+    for st, mgr, kc, vc, rows, slots in serving_replay(tr):
+        slots_equal &= bool(np.array_equal(np.asarray(slots, np.int64), step_slots[st.step]))
+        if st.step in kept:
+            t1 = time.perf_counter()
+            lens = mgr.context_lens(list(rows))
+            ref = oracle.decode_attention(st.q, kc, vc, mgr.block_tables(list(rows), width, -1), lens,
+                                          cfg.scale, cfg.dtype)
+            t_attn += time.perf_counter() - t1
+            kv += int(np.asarray(lens, np.int64).sum()) * H * 2 * D * elem
+            err = max(err, float(np.abs(kept[st.step].double().cpu().numpy() - ref).max()))
+    t_replay = time.perf_counter() - t0 - t_attn
+    free_equal = eng.manager.free_list() == mgr.free
+    pool_exact = True
+    for half, oc in ((0, kc), (1, vc)):
+        g = eng.pool[:, half].contiguous().cpu()
+        u = np.uint16 if g.element_size() == 2 else np.uint32
+        g = (g.view(torch.int16) if g.element_size() == 2 else g.view(torch.int32)).numpy().view(u)
+        pool_exact &= bool(np.array_equal(g, oc.view(u)))
+        del g
+    n = len(kept)
+    log(f"cpu baseline (serving): attention on {n} steps, {kv} KV bytes in {t_attn:.1f}s; replay (appends, "
+        f"writes, refills) {t_replay:.1f}s; max abs err {err:.3e}, slots equal {slots_equal}, free list equal "
+        f"{free_equal}, pool bit-exact {pool_exact}")
+    return {"value": kv / t_attn / 1e9, "unit": "GB/s", "cores": info["affinity_cores"], "kind": "oracle",
+            "sample": f"the serving trace replayed on the oracle over all {len(step_slots)} steps (appends, writes "
+                      f"and refills: {t_replay:.1f} s, not in value), float64 attention of all {B} rows on the {n} "
+                      f"steps the GPU run kept, every tenth and the last ({t_attn:.1f} s): value and tokens/s "
+                      f"over those attentions",
+            "decode_tokens_per_s": B * n / t_attn, "replay_s": t_replay, **info,
+            "parity": {"steps_compared": n, "rows_per_step": B, "max_abs_err": err, "tolerance": 2e-3,
+                       "slots_equal_every_step": slots_equal, "free_list_equal": free_equal,
+                       "pool_bit_exact_at_end": pool_exact}}
 
 
 def measure_fp8(cfg, wl, args, ring, base, width, tokens_per_s_16):
