@@ -591,3 +591,27 @@ def test_fp8_attention_far_apart_row_scales(pattern, q_dtype):
     err = np.abs(out - ref).max(axis=(1, 2))
     _banner("per sequence: " + ", ".join(f"L={L} err {e:.2e} (tol {t:.1e})" for L, e, t in zip(lens, err, tol)))
     assert np.all(err <= tol), err / tol
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_fp8_seeded_shape_sweep(i):
+    """8 seeded shapes of 8-bit attention (bf16 or fp16 queries, H_kv 1-8,
+    G 1-8, 2 to 40 sequences up to 2500 tokens, one of them a single token)
+    against the float64 oracle on the read-back values."""
+    rng = np.random.default_rng(9000 + i)
+    q_dtype = ["bf16", "f16"][int(rng.integers(0, 2))]
+    hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
+    hq = hkv * int(rng.integers(1, 9))
+    B = int(rng.integers(2, 41))
+    max_len = int(rng.integers(1, 2501))
+    _banner(f"fp8 sweep {i}: q={q_dtype} hq={hq} hkv={hkv} B={B} max_len={max_len}")
+    lens, tabs, q, o, g = _fp8_case(q_dtype, hq, hkv, B, max_len, 9100 + i)
+    scale = float(np.float32(1.0 / np.sqrt(128)))
+    ref = quant.decode_attention_fp8(q, q_dtype, *o, tabs, lens, scale)
+    out = pkv.paged_decode_attention_fp8(to_device(q, q_dtype), *g, torch.from_numpy(tabs).cuda(),
+                                         torch.from_numpy(lens.astype(np.int32)).cuda(), scale,
+                                         max_context_len=int(lens.max())).double().cpu().numpy()
+    assert np.all(np.isfinite(out))
+    err = float(np.abs(out - ref).max())
+    _banner(f"  max abs err {err:.3e}")
+    assert err <= 2e-3, err

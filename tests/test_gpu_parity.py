@@ -467,3 +467,43 @@ def test_layers_share_one_block_table():
         assert np.array_equal(bits_u(kc), okc.view(np.uint16)) and np.array_equal(bits_u(vc), ovc.view(np.uint16))
         ref = oracle.decode_attention(q, okc, ovc, tables, ctx, scale, "bf16")
         assert np.abs(out - ref).max() <= 2e-3
+
+
+def _sweep_shape(i):
+    """Seeded shape of sweep case i: dtype, head dim, block size, KV heads,
+    group, batch, and lengths mixing empty, one-token, whole-block and
+    ragged contexts."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+    d = 128 if rng.random() < 0.7 else 64
+    bs = [16, 32, 64][int(rng.integers(0, 3))]
+    h_kv = [1, 2, 4, 8][int(rng.integers(0, 4))]
+    g = int(rng.integers(1, 9))
+    B = int(rng.integers(1, 49))
+    lens = []
+    for _ in range(B):
+        r = rng.random()
+        lens.append(0 if r < 0.1 else 1 if r < 0.2 else bs * int(rng.integers(1, 40)) if r < 0.3
+                    else int(rng.integers(2, 2001)))
+    part = [16, 64, 256, 512][int(rng.integers(0, 4))]
+    return dtype, d, bs, h_kv, g, lens, part, int(rng.integers(0, 16))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_seeded_shape_sweep(i):
+    """24 seeded shapes (bf16 / fp16 / fp32 KV, D 64 or 128, block size 16,
+    32 or 64, H_kv 1-8, G 1-8, up to 48 sequences of 0 to 2000 tokens), each
+    through the library's default path (the stream kernel where it applies)
+    and a partition size drawn with it, against the float64 oracle."""
+    dtype, d, bs, h_kv, g, lens, part, spare = _sweep_shape(i)
+    nb = sum(-(-L // bs) for L in lens) + spare + 1
+    _banner(f"sweep {i}: {dtype} D={d} bs={bs} Hkv={h_kv} G={g} B={len(lens)} max L={max(lens)} "
+            f"partition {part}")
+    case = _small_case(dtype, h_kv * g, h_kv, d, bs, lens, nb, seed=8000 + i)
+    ref = _oracle_attend(case)
+    for p in (0, part):
+        got = _gpu_attend(case, partition_tokens=p).double().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        err = float(np.abs(got - ref).max())
+        _banner(f"  partition {p}: max abs err {err:.3e}")
+        assert err <= TOL[dtype], (p, err)
