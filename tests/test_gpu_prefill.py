@@ -202,3 +202,66 @@ def test_fp8_prefill_refuses_bad_types_and_small_workspace():
     assert args(pkv.PKV_BF16, pkv.PKV_F32, fake, need - 1) == -7
     # (fp16 queries read the codes in place and take no workspace: not called
     # here, where the pointers are stand-ins)
+
+
+def _prefill_sweep_shape(i):
+    rng = np.random.default_rng(11000 + i)
+    dtype = ["bf16", "f16", "f32"][int(rng.integers(0, 3))]
+    D = 128 if rng.random() < 0.7 else 64
+    bs = [8, 16, 32, 64][int(rng.integers(0, 4))]
+    hkv = [1, 2, 4, 8][int(rng.integers(0, 4))]
+    hq = hkv * int(rng.integers(1, 9))
+    B = int(rng.integers(1, 7))
+    rounds = [[int(rng.integers(0, 300)) if rng.random() > 0.15 else int(rng.integers(0, 2)) for _ in range(B)]
+              for _ in range(int(rng.integers(1, 4)))]
+    return dtype, D, bs, hkv, hq, rounds
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_prefill_seeded_shape_sweep(i):
+    """12 seeded prefill shapes (bf16 / fp16 / fp32 KV, D 64 or 128, block
+    size 8 to 64, H_kv 1-8, G 1-8, up to 6 sequences admitted and extended
+    over one to three rounds of chunks of 0 to 300 rows, fp32 output): the
+    pool bit for bit as the oracle's write and every query row against the
+    oracle's causal prefill, whichever kernel the shape goes to."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    dtype, D, bs, hkv, hq, rounds = _prefill_sweep_shape(i)
+    _banner(f"prefill sweep {i}: {dtype} D={D} bs={bs} hkv={hkv} hq={hq} chunks {rounds}")
+    rng = np.random.default_rng(12000 + i)
+    B = len(rounds[0])
+    tot = [sum(r[b] for r in rounds) for b in range(B)]
+    N = sum(-(-t // bs) for t in tot) + 8
+    order = rng.permutation(N)
+    width = max(1, max(-(-t // bs) for t in tot))
+    eng = PagedKVEngine(N, hkv, bs, D, TORCH_DTYPE[dtype], B, width, order,
+                        fill_bits=synth.POISON_BITS[dtype], num_q_heads=hq)
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc = oracle.new_pool(N, hkv, bs, D, synth.poison_array((), dtype))
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    for chunk in rounds:
+        T = sum(chunk)
+        k = synth.normal(rng, (T, hkv, D), dtype)
+        v = synth.normal(rng, (T, hkv, D), dtype)
+        q = synth.normal(rng, (T, hq, D), dtype)
+        slots = []
+        for b, n in enumerate(chunk):
+            slots += (om.append_tokens(b, n) if om.is_live(b) else om.allocate_for_prefill(b, n))
+        oracle.write_kv(k, v, slots, okc, ovc, bs)
+        qs = np.concatenate([[0], np.cumsum(chunk)])
+        lens = om.context_lens(list(range(B)))
+        ref = oracle.prefill_attention(q, qs, okc, ovc, om.block_tables(list(range(B)), width, -1), lens,
+                                       scale, dtype)
+        got = eng.prefill_chunk(list(range(B)), list(range(B)), chunk, to_device(k, dtype),
+                                to_device(v, dtype), to_device(q, dtype), scale)
+        torch.cuda.synchronize()
+        for half, oc in ((0, okc), (1, ovc)):
+            g = eng.pool[:, half].contiguous().cpu()
+            u = np.uint16 if g.element_size() == 2 else np.uint32
+            g = (g.view(torch.int16) if g.element_size() == 2 else g.view(torch.int32)).numpy().view(u)
+            assert np.array_equal(g, oc.view(u)), half
+        got = got.double().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        err = float(np.abs(got - ref).max()) if T else 0.0
+        _banner(f"  chunk {chunk}: max abs err {err:.3e}")
+        assert err <= tol, err
