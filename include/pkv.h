@@ -663,7 +663,10 @@ int pkv_decode_write_fp8(const void* key, const void* value, int32_t src_dtype,
 
 /*
  * paged_decode_attention over 8-bit blocks: the same quantity, with each
- * cached row read back as E4M3(code) * 2^e.  q (device, [num_seqs,
+ * cached row read back as E4M3(code) * 2^e.  Arithmetic: scores and sums in
+ * fp32; each row's weight (probability times its V scale) reaches the
+ * matrix cores to about 2^-22 of the largest weight of its segment, for any
+ * spread of the row scales.  q (device, [num_seqs,
  * num_q_heads, 128]) is q_dtype (PKV_BF16 or PKV_F16); out is PKV_F32 or
  * q_dtype.  phases: 1 = the attention kernel only, 2 = the merge only, 3 =
  * both (the pair 1 then 2 on one stream equals 3).  The workspace is that of
