@@ -389,8 +389,9 @@ int pkv_scatter_blocks_fp8(const void* staging, const uint8_t* staging_scales, c
  * partition_tokens of 0 that cannot take the stream path means 512).  Stream
  * path (partition_tokens == 0): W * 4 * num_q_heads * (head_dim + 2) * 4
  * bytes of partials, with W = CUs * max(1, 4 / num_kv_heads) tile ranges
- * (integer division; 256 CUs on MI355X).  The contents need no initialisation.  Returns 0 for invalid
- * arguments as well.
+ * (integer division; 256 CUs on MI355X), then (num_seqs + 1) * 4 bytes of
+ * per-sequence tile offsets the attention launch leaves for the merge.  The
+ * contents need no initialisation.  Returns 0 for invalid arguments as well.
  */
 size_t paged_decode_attention_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                              int32_t num_kv_heads, int32_t head_dim,

@@ -1057,6 +1057,7 @@ struct StreamArgs {
   const int32_t* lens;
   float* ws_acc;     // [W, 4, H_q, D]   (W = num_ranges)
   float* ws_ml;      // [W, 4, H_q, 2]
+  int32_t* ws_S;     // [B + 1] tile prefix sums, stored by workgroup 0 for the merge
   void* out;
   int64_t block_stride;
   int64_t head_stride;
@@ -1449,6 +1450,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& a, const StepMeta*
     }
   }
   __syncthreads();
+  // the prefix sums for the merge (the workspace outlives this launch)
+  if (blockIdx.x == 0)
+    for (int b = threadIdx.x; b <= B; b += blockDim.x) a.ws_S[b] = S[b];
   const int T = S[B];
   const int W = a.num_ranges;
   const int64_t r_base = static_cast<int64_t>(blockIdx.x) * R;
@@ -1787,23 +1791,6 @@ attn_stream_step_kernel(StreamArgs a, StepMeta meta) {
 constexpr int kMergeChunk = 8;
 constexpr int kMergeWaves = 4;
 
-// Tile offset of sequence b and the launch's tile count, from the lengths
-// (one wave; every lane ends with both).
-__device__ __forceinline__ void merge_tile_counts(const StreamArgs& a, int b, int lane, int& before,
-                                                  int& total) {
-  before = 0;
-  total = 0;
-  for (int j = lane; j < a.num_seqs; j += kWave) {
-    const int t = (clamp_len(a.lens[j], a.max_len) + kTile - 1) / kTile;
-    total += t;
-    if (j < b) before += t;
-  }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    before += __shfl_xor(before, o);
-    total += __shfl_xor(total, o);
-  }
-}
 
 // Partial slots of the pieces of the sequence whose tiles are [Sb, Se)
 // (Se > Sb, so total >= 1) into plist, in range order; one wave.  Lane i
@@ -1910,19 +1897,17 @@ attn_stream_merge_kernel(StreamArgs a) {
   const int lane = threadIdx.x;
   const int qh = blockIdx.x % a.hq;
   const int b = blockIdx.x / a.hq;
-  int before, total;
-  merge_tile_counts(a, b, lane, before, total);
-  const int L = clamp_len(a.lens[b], a.max_len);
+  // the sequence's tiles [Sb, Se) and the launch's tile count, as the attention kernel summed them
+  const int Sb = a.ws_S[b], Se = a.ws_S[b + 1], total = a.ws_S[a.num_seqs];
   float M = -INFINITY, den = 0.f;
   float num[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) num[e] = 0.f;
-  if (L == 0) {
+  if (Se == Sb) {                      // L = 0
     merge_store<D>(a, b, qh, lane, den, num);
     return;
   }
-  const int npieces = merge_piece_list(a, qh / a.group, before, before + (L + kTile - 1) / kTile, total,
-                                       lane, plist);
+  const int npieces = merge_piece_list(a, qh / a.group, Sb, Se, total, lane, plist);
   __syncthreads();
   if (npieces <= 1) return;            // one segment covered the sequence
   merge_fold<D>(a, plist, npieces, qh, lane, 0, kMergeChunk, M, den, num);
@@ -1948,11 +1933,8 @@ attn_stream_merge_waves_kernel(StreamArgs a) {
 #pragma unroll
   for (int e = 0; e < kPer; ++e) num[e] = 0.f;
   if (wave == 0) {
-    int before, total;
-    merge_tile_counts(a, b, lane, before, total);
-    const int L = clamp_len(a.lens[b], a.max_len);
-    const int np = L == 0 ? -1 : merge_piece_list(a, qh / a.group, before,
-                                                  before + (L + kTile - 1) / kTile, total, lane, plist);
+    const int Sb = a.ws_S[b], Se = a.ws_S[b + 1], total = a.ws_S[a.num_seqs];
+    const int np = Se == Sb ? -1 : merge_piece_list(a, qh / a.group, Sb, Se, total, lane, plist);
     if (lane == 0) s_npieces = np;
   }
   __syncthreads();
@@ -2027,7 +2009,7 @@ struct StreamPlan {
   int ranges = 0;         // W = wgs * R
   int range_cap = 0;
   size_t dyn_lds = 0;
-  size_t acc_floats = 0;  // workspace: accumulators, then (m, l)
+  size_t acc_floats = 0;  // workspace: accumulators, then (m, l), then the tile prefix sums
   size_t ml_floats = 0;
   size_t workspace = 0;
 };
@@ -2061,7 +2043,7 @@ StreamPlan plan_stream(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_hea
   pl.dyn_lds = dyn;
   pl.acc_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * head_dim;
   pl.ml_floats = static_cast<size_t>(ranges) * kStreamSlots * num_q_heads * 2;
-  pl.workspace = (pl.acc_floats + pl.ml_floats) * sizeof(float);
+  pl.workspace = (pl.acc_floats + pl.ml_floats) * sizeof(float) + (static_cast<size_t>(num_seqs) + 1) * sizeof(int32_t);
   return pl;
 }
 
@@ -2412,6 +2394,7 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
       sa.lens = context_lens;
       sa.ws_acc = static_cast<float*>(workspace);
       sa.ws_ml = sa.ws_acc + pl.acc_floats;
+      sa.ws_S = reinterpret_cast<int32_t*>(sa.ws_ml + pl.ml_floats);
       sa.out = out;
       sa.block_stride = l->block_stride;
       sa.head_stride = l->head_stride;
