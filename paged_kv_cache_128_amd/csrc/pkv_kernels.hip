@@ -1174,10 +1174,17 @@ struct TileOff8 {
 };
 
 // Tile ranges: range r starts at tile r*T/W; tile g lies in range owner(g).
+// Both in 32-bit unsigned arithmetic when T * W fits (every product below
+// is at most T * W), else in 64-bit: the same quotients either way.
 __device__ __forceinline__ int range_start(int64_t r, int T, int W) {
+  if (static_cast<uint64_t>(T) * static_cast<uint64_t>(W) <= 0xffffffffull)
+    return static_cast<int>(static_cast<uint32_t>(r) * static_cast<uint32_t>(T) / static_cast<uint32_t>(W));
   return static_cast<int>((r * T) / W);
 }
 __device__ __forceinline__ int range_owner(int g, int T, int W) {
+  if (static_cast<uint64_t>(T) * static_cast<uint64_t>(W) <= 0xffffffffull)
+    return static_cast<int>((static_cast<uint32_t>(g + 1) * static_cast<uint32_t>(W) - 1u) /
+                            static_cast<uint32_t>(T));
   return static_cast<int>((static_cast<int64_t>(g + 1) * W - 1) / T);
 }
 
