@@ -2443,11 +2443,11 @@ int attention_impl(int phases, void* out, int32_t out_dtype, const void* q, cons
         if (e != hipSuccess) return PKV_ERR_HIP;
       }
       if (phases & kPhaseMerge) {
-        // Lengths come from device memory (for the decode step: lens_out,
-        // written by the first launch); a copy in the kernel arguments
-        // measured slower.  A sequence spans about W / B ranges, two pieces each.  Beyond two
-        // chunks of pieces the waves of the multi-wave merge fold chunks
-        // side by side; below that the one-wave merge measured faster.
+        // The merge takes each sequence's tile range from the prefix sums the
+        // first launch left in the workspace.  A sequence spans about W / B
+        // ranges, two pieces each.  Beyond two chunks of pieces the waves of
+        // the multi-wave merge fold chunks side by side; below that the
+        // one-wave merge measured faster.
         const int64_t pieces = 2 * ((pl.ranges + num_seqs - 1) / num_seqs) + 2;
         const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads));
         if (pieces > 2 * kMergeChunk)
