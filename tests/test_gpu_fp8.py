@@ -615,3 +615,19 @@ def test_fp8_seeded_shape_sweep(i):
     err = float(np.abs(out - ref).max())
     _banner(f"  max abs err {err:.3e}")
     assert err <= 2e-3, err
+
+
+@pytest.mark.parametrize("scale", [1e-3, 4.0, 64.0])
+def test_fp8_extreme_score_ranges(scale):
+    """8-bit attention with softmax scales far from 1/sqrt(D) (near-uniform
+    weights, and score gaps beyond the rescale slack), against the oracle."""
+    lens, tabs, q, o, g = _fp8_case("bf16", 28, 4, 12, 3000, 4343)
+    s = float(np.float32(scale))
+    ref = quant.decode_attention_fp8(q, "bf16", *o, tabs, lens, s)
+    out = pkv.paged_decode_attention_fp8(to_device(q, "bf16"), *g, torch.from_numpy(tabs).cuda(),
+                                         torch.from_numpy(lens.astype(np.int32)).cuda(), s,
+                                         max_context_len=int(lens.max())).double().cpu().numpy()
+    assert np.all(np.isfinite(out))
+    err = float(np.abs(out - ref).max())
+    _banner(f"fp8 extreme scores, scale {scale}: max abs err {err:.3e}")
+    assert err <= 2e-3, err

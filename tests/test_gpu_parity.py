@@ -507,3 +507,23 @@ def test_seeded_shape_sweep(i):
         err = float(np.abs(got - ref).max())
         _banner(f"  partition {p}: max abs err {err:.3e}")
         assert err <= TOL[dtype], (p, err)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("scale", [1e-3, 4.0, 64.0])
+def test_extreme_score_ranges(dtype, scale):
+    """Softmax scales far from 1/sqrt(D): nearly uniform weights (1e-3) and
+    scores hundreds of units apart (4 and 64, where the running maximum
+    jumps by more than the rescale slack and most weights underflow), on
+    the stream path and on 64-token partitions, against the oracle."""
+    lens = [1, 2, 17, 300, 1500, 4000]
+    case = _small_case(dtype, 28, 4, 128, 16, lens, sum(-(-L // 16) for L in lens) + 4, seed=4242)
+    case["scale"] = float(np.float32(scale))
+    ref = _oracle_attend(case)
+    _banner(f"extreme scores {dtype} scale {scale}")
+    for part in (0, 64):
+        got = _gpu_attend(case, partition_tokens=part).double().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        err = float(np.abs(got - ref).max())
+        _banner(f"  partition {part}: max abs err {err:.3e}")
+        assert err <= 2e-3, (part, err)
