@@ -265,3 +265,42 @@ def test_prefill_seeded_shape_sweep(i):
         err = float(np.abs(got - ref).max()) if T else 0.0
         _banner(f"  chunk {chunk}: max abs err {err:.3e}")
         assert err <= tol, err
+
+
+@pytest.mark.parametrize("scale", [1e-3, 4.0, 64.0])
+@pytest.mark.parametrize("dtype,bs", [("bf16", 16), ("f16", 32), ("bf16", 8)])
+def test_prefill_extreme_score_ranges(scale, dtype, bs):
+    """Causal prefill with softmax scales far from 1/sqrt(D): near-uniform
+    weights, and scores hundreds of units apart (the running maximum jumping
+    past the rescale slack), on the matrix-core kernel (block sizes 16, 32)
+    and the generic one (block size 8), against the oracle."""
+    from paged_kv_cache_128_amd.engine import PagedKVEngine
+    rng = np.random.default_rng(5150 + bs)
+    hq, hkv, D = 28, 4, 128
+    chunk = [1, 45, 300, 129]
+    B = len(chunk)
+    N = sum(-(-c // bs) for c in chunk) + 4
+    order = rng.permutation(N)
+    width = max(-(-c // bs) for c in chunk)
+    eng = PagedKVEngine(N, hkv, bs, D, TORCH_DTYPE[dtype], B, width, order,
+                        fill_bits=synth.POISON_BITS[dtype], num_q_heads=hq)
+    om = oracle.BlockManager(N, bs, order)
+    okc, ovc = oracle.new_pool(N, hkv, bs, D, synth.poison_array((), dtype))
+    T = sum(chunk)
+    k = synth.normal(rng, (T, hkv, D), dtype)
+    v = synth.normal(rng, (T, hkv, D), dtype)
+    q = synth.normal(rng, (T, hq, D), dtype)
+    slots = []
+    for b, n in enumerate(chunk):
+        slots += om.allocate_for_prefill(b, n)
+    oracle.write_kv(k, v, slots, okc, ovc, bs)
+    s = float(np.float32(scale))
+    ref = oracle.prefill_attention(q, np.concatenate([[0], np.cumsum(chunk)]), okc, ovc,
+                                   om.block_tables(list(range(B)), width, -1), om.context_lens(list(range(B))),
+                                   s, dtype)
+    got = eng.prefill_chunk(list(range(B)), list(range(B)), chunk, to_device(k, dtype), to_device(v, dtype),
+                            to_device(q, dtype), s).double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = float(np.abs(got - ref).max())
+    _banner(f"prefill extreme scores {dtype} bs={bs} scale {scale}: max abs err {err:.3e}")
+    assert err <= 2e-3, err
