@@ -527,3 +527,20 @@ def test_extreme_score_ranges(dtype, scale):
         err = float(np.abs(got - ref).max())
         _banner(f"  partition {part}: max abs err {err:.3e}")
         assert err <= 2e-3, (part, err)
+
+
+@pytest.mark.parametrize("lens", [[131072], [1, 98304, 3]])
+def test_stream_very_long_contexts(lens):
+    """Contexts of 96 Ki to 128 Ki tokens (H 28/4, bf16) on the stream path:
+    one sequence spread over every range of the launch (the multi-wave
+    merge folds several hundred pieces), and a long one beside two short
+    ones; every output row against the oracle."""
+    nb = sum(-(-L // 16) for L in lens) + 4
+    case = _small_case("bf16", 28, 4, 128, 16, lens, nb, seed=777 + len(lens))
+    _banner(f"very long contexts {lens}")
+    ref = _oracle_attend(case)
+    got = _gpu_attend(case, partition_tokens=0).double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = float(np.abs(got - ref).max())
+    _banner(f"  max abs err {err:.3e}")
+    assert err <= 2e-3, err
