@@ -631,3 +631,32 @@ def test_fp8_extreme_score_ranges(scale):
     err = float(np.abs(out - ref).max())
     _banner(f"fp8 extreme scores, scale {scale}: max abs err {err:.3e}")
     assert err <= 2e-3, err
+
+
+def test_fp8_very_long_context():
+    """One 65,536-token sequence over an 8-bit pool (H 28/4, bf16 queries):
+    spread over every range of the launch, its pieces folded by the
+    multi-wave merge; against the oracle on the read-back values."""
+    rng = np.random.default_rng(8080)
+    hq, hkv, bs, D, L = 28, 4, 16, 128, 65536
+    N = L // bs + 4
+    m = oracle.BlockManager(N, bs, rng.permutation(N))
+    okc, ovc, oks, ovs = quant.new_fp8_pool(N, hkv, bs, D)
+    codes, kc, vc, scales, ks, vs = pkv.new_fp8_pool(N, hkv, bs, D, "cuda", poison=True)
+    slots = np.array(m.allocate_for_prefill(0, L), np.int64)
+    k = synth.normal(rng, (L, hkv, D), "bf16")
+    v = synth.normal(rng, (L, hkv, D), "bf16")
+    quant.write_kv_fp8(_f32(k, "bf16"), _f32(v, "bf16"), slots, okc, ovc, oks, ovs, bs)
+    pkv.paged_kv_write_fp8(to_device(k, "bf16"), to_device(v, "bf16"), torch.from_numpy(slots).cuda(),
+                           kc, vc, ks, vs)
+    tabs = m.block_tables([0], L // bs, -1)
+    lens = np.array([L], np.int64)
+    q = synth.normal(rng, (1, hq, D), "bf16")
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    ref = quant.decode_attention_fp8(q, "bf16", okc, ovc, oks, ovs, tabs, lens, scale)
+    out = pkv.paged_decode_attention_fp8(to_device(q, "bf16"), kc, vc, ks, vs, torch.from_numpy(tabs).cuda(),
+                                         torch.from_numpy(lens.astype(np.int32)).cuda(), scale,
+                                         max_context_len=L).double().cpu().numpy()
+    err = float(np.abs(out - ref).max())
+    _banner(f"fp8 65536-token context: max abs err {err:.3e}")
+    assert err <= 2e-3, err
